@@ -1,0 +1,329 @@
+"""CPU oracle for the MoE dispatch/combine path (test infrastructure only).
+
+Only tests/, the smoke check in __graft_entry__ and the CPU-baseline leg of
+bench.py may import this package.  It loads oracle/liboracle.so, built from
+oracle/oracle.c with gcc (-O2 -ffp-contract=off), and wraps its functions for
+numpy arrays.  It shares no code with the HIP library.
+
+Each wrapper names the step of the pages it follows; the C source states the
+definition.  `run_dispatch` / `run_combine` chain the steps in the pages' order
+and return every intermediate buffer, in the same flat layouts the HIP path
+exposes for checking (send rows of sender s at rows s*T*K.., receive rows of
+rank d at rows G[d]..).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+_lib = None
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-Wall",
+           "-o", LIB_PATH, SRC_PATH, "-lm"]
+    subprocess.run(cmd, check=True)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+            build()
+        _lib = ctypes.CDLL(LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_Z = ctypes.c_size_t
+
+
+def _declare(L):
+    L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    L.orc_bf16_to_f32.restype = ctypes.c_float
+    L.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+    L.orc_f32_to_bf16.restype = ctypes.c_uint16
+    L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+    L.orc_e4m3_value.restype = ctypes.c_double
+    L.orc_f32_to_e4m3.argtypes = [ctypes.c_float]
+    L.orc_f32_to_e4m3.restype = ctypes.c_uint8
+    L.orc_route_count.argtypes = [_I, _I, _I, _I, _P, _P]
+    L.orc_route_count.restype = _I
+    L.orc_send_offsets.argtypes = [_I, _I, _P, _P]
+    L.orc_positions.argtypes = [_I, _I, _I, _I, _P, _P, _P]
+    L.orc_recv_offsets.argtypes = [_I, _I, _P, _P, _P]
+    L.orc_expert_offsets.argtypes = [_I, _I, _P, _P]
+    L.orc_pack_bf16.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P]
+    L.orc_quant_row_fp8.argtypes = [_I, _P, _P, _P]
+    L.orc_pack_fp8.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P]
+    L.orc_transfer.argtypes = [_I, _I, _I, _I, _Z, _P, _P, _P, _P, _P]
+    L.orc_shuffle.argtypes = [_I, _I, _I, _I, _Z, _Z, _P, _P, _P, _P, _P,
+                              _P, _P, _P, _P, _P, _P, _P]
+    L.orc_expert_standin.argtypes = [_I, _I, _P, _P, _P, _I, _P]
+    L.orc_combine_send.argtypes = [_I, _I, _Z, _P, _P, _P, _P, _P, _P, _P]
+    L.orc_combine_transfer.argtypes = [_I, _I, _I, _I, _Z, _P, _P, _P, _P, _P]
+    L.orc_combine_recv.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P]
+    L.orc_combine_recv_f64.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P]
+    L.orc_combine_token.argtypes = [_I, _I, _P, _P, _P]
+    L.orc_f32_to_bf16_n.argtypes = [_Z, _P, _P]
+    L.orc_f32_to_e4m3_n.argtypes = [_Z, _P, _P]
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------- codecs
+
+def bf16_to_f32(b) -> float:
+    """Value of one bf16 pattern."""
+    return lib().orc_bf16_to_f32(int(b))
+
+
+def f32_to_bf16(f: np.ndarray) -> np.ndarray:
+    """fp32 array -> bf16 patterns (uint16), nearest even."""
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, dtype=np.uint16)
+    lib().orc_f32_to_bf16_n(f.size, _p(f), _p(out))
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(int(code))
+
+
+def f32_to_e4m3(f: np.ndarray) -> np.ndarray:
+    """fp32 array -> e4m3 codes (uint8), nearest even, saturating at 448."""
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, dtype=np.uint8)
+    lib().orc_f32_to_e4m3_n(f.size, _p(f), _p(out))
+    return out
+
+
+def quant_row_fp8(xrow: np.ndarray):
+    """Block-scaled e4m3 quantisation of one bf16 row -> (codes uint8[H], scales fp32[H/128])."""
+    xrow = np.ascontiguousarray(xrow, dtype=np.uint16)
+    H = xrow.shape[-1]
+    q = np.empty(H, dtype=np.uint8)
+    sc = np.empty(H // 128, dtype=np.float32)
+    lib().orc_quant_row_fp8(H, _p(xrow), _p(q), _p(sc))
+    return q, sc
+
+
+# ------------------------------------------------------------- dispatch
+
+class RoutingError(ValueError):
+    pass
+
+
+def route_count(idx: np.ndarray, E: int) -> np.ndarray:
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    N, T, K = idx.shape
+    cnt = np.empty((N, E), dtype=np.int32)
+    if lib().orc_route_count(N, T, K, E, _p(idx), _p(cnt)) != 0:
+        raise RoutingError("expert id outside [0, E)")
+    return cnt
+
+
+def send_offsets(cnt: np.ndarray) -> np.ndarray:
+    N, E = cnt.shape
+    soff = np.empty((N, E + 1), dtype=np.int32)
+    lib().orc_send_offsets(N, E, _p(cnt), _p(soff))
+    return soff
+
+
+def positions(idx: np.ndarray, soff: np.ndarray) -> np.ndarray:
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    N, T, K = idx.shape
+    E = soff.shape[1] - 1
+    pos = np.empty((N, T, K), dtype=np.int32)
+    lib().orc_positions(N, T, K, E, _p(idx), _p(soff), _p(pos))
+    return pos
+
+
+def recv_offsets(soff: np.ndarray, N: int):
+    E = soff.shape[1] - 1
+    roff = np.empty((N, N + 1), dtype=np.int32)
+    G = np.empty(N + 1, dtype=np.int32)
+    lib().orc_recv_offsets(N, E, _p(soff), _p(roff), _p(G))
+    return roff, G
+
+
+def expert_offsets(cnt: np.ndarray) -> np.ndarray:
+    N, E = cnt.shape
+    eoff = np.empty(E + 1, dtype=np.int32)
+    lib().orc_expert_offsets(N, E, _p(cnt), _p(eoff))
+    return eoff
+
+
+def plan(idx: np.ndarray, E: int) -> dict:
+    """Counts, positions and every offset table (integer part of dispatch)."""
+    N = idx.shape[0]
+    cnt = route_count(idx, E)
+    soff = send_offsets(cnt)
+    pos = positions(idx, soff)
+    roff, G = recv_offsets(soff, N)
+    eoff = expert_offsets(cnt)
+    return {"cnt": cnt, "soff": soff, "pos": pos, "roff": roff, "G": G, "eoff": eoff}
+
+
+def pack_bf16(x: np.ndarray, pos: np.ndarray):
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    N, T, H = x.shape
+    K = pos.shape[2]
+    send_x = np.zeros((N * T * K, H), dtype=np.uint16)
+    send_meta = np.zeros(N * T * K, dtype=np.int32)
+    lib().orc_pack_bf16(N, T, K, H, _p(x), _p(pos), _p(send_x), _p(send_meta))
+    return send_x, send_meta
+
+
+def pack_fp8(x: np.ndarray, pos: np.ndarray):
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    N, T, H = x.shape
+    K = pos.shape[2]
+    send_q = np.zeros((N * T * K, H), dtype=np.uint8)
+    send_scale = np.zeros((N * T * K, H // 128), dtype=np.float32)
+    send_meta = np.zeros(N * T * K, dtype=np.int32)
+    lib().orc_pack_fp8(N, T, K, H, _p(x), _p(pos), _p(send_q), _p(send_scale), _p(send_meta))
+    return send_q, send_scale, send_meta
+
+
+def transfer(send: np.ndarray, pl: dict, T: int, K: int) -> np.ndarray:
+    """Modelled network transfer of one row plane (any dtype, rows on axis 0)."""
+    send = np.ascontiguousarray(send)
+    N, E = pl["cnt"].shape
+    recv = np.zeros_like(send)
+    row_bytes = send.nbytes // max(send.shape[0], 1) if send.shape[0] else 0
+    lib().orc_transfer(N, E, T, K, row_bytes, _p(pl["soff"]), _p(pl["roff"]), _p(pl["G"]),
+                       _p(send), _p(recv))
+    return recv
+
+
+def shuffle(recv_x: np.ndarray, recv_scale, recv_meta: np.ndarray, pl: dict, T: int, K: int):
+    recv_x = np.ascontiguousarray(recv_x)
+    N, E = pl["cnt"].shape
+    R = recv_x.shape[0]
+    row_bytes = recv_x.nbytes // R if R else 0
+    expert_x = np.zeros_like(recv_x)
+    if recv_scale is not None:
+        recv_scale = np.ascontiguousarray(recv_scale)
+        expert_scale = np.zeros_like(recv_scale)
+        scale_bytes = recv_scale.nbytes // R if R else 0
+        rs, es = _p(recv_scale), _p(expert_scale)
+    else:
+        expert_scale, scale_bytes, rs, es = None, 0, None, None
+    src_rank = np.zeros(R, dtype=np.int32)
+    src_slot = np.zeros(R, dtype=np.int32)
+    recv_meta = np.ascontiguousarray(recv_meta, dtype=np.int32)
+    lib().orc_shuffle(N, E, T, K, row_bytes, scale_bytes, _p(pl["cnt"]), _p(pl["soff"]),
+                      _p(pl["roff"]), _p(pl["G"]), _p(pl["eoff"]), _p(recv_x), rs,
+                      _p(recv_meta), _p(expert_x), es, _p(src_rank), _p(src_slot))
+    return expert_x, expert_scale, src_rank, src_slot
+
+
+def expert_standin(expert_x: np.ndarray, expert_scale, eoff: np.ndarray, H: int) -> np.ndarray:
+    """Outside the path: y[r] = bf16(value * (e+1)) for row r of expert e."""
+    expert_x = np.ascontiguousarray(expert_x)
+    R = expert_x.shape[0]
+    E = eoff.shape[0] - 1
+    y = np.zeros((R, H), dtype=np.uint16)
+    fp8 = expert_scale is not None
+    sc = _p(np.ascontiguousarray(expert_scale, dtype=np.float32)) if fp8 else None
+    lib().orc_expert_standin(E, H, _p(eoff), _p(expert_x), sc, int(fp8), _p(y))
+    return y
+
+
+def run_dispatch(x: np.ndarray, idx: np.ndarray, E: int, fp8: bool = False) -> dict:
+    """Every dispatch step, in the pages' order; returns all buffers."""
+    N, T, H = x.shape
+    K = idx.shape[2]
+    pl = plan(idx, E)
+    out = dict(pl)
+    if fp8:
+        send_x, send_scale, send_meta = pack_fp8(x, pl["pos"])
+    else:
+        send_x, send_meta = pack_bf16(x, pl["pos"])
+        send_scale = None
+    recv_x = transfer(send_x, pl, T, K)
+    recv_scale = transfer(send_scale, pl, T, K) if fp8 else None
+    recv_meta = transfer(send_meta, pl, T, K)
+    expert_x, expert_scale, src_rank, src_slot = shuffle(recv_x, recv_scale, recv_meta, pl, T, K)
+    out.update(send_x=send_x, send_scale=send_scale, send_meta=send_meta, recv_x=recv_x,
+               recv_scale=recv_scale, recv_meta=recv_meta, expert_x=expert_x,
+               expert_scale=expert_scale, expert_src_rank=src_rank, expert_src_slot=src_slot)
+    return out
+
+
+def combine_send(y: np.ndarray, pl: dict) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    N, E = pl["cnt"].shape
+    R = y.shape[0]
+    comb_send = np.zeros_like(y)
+    row_bytes = y.nbytes // R if R else 0
+    lib().orc_combine_send(N, E, row_bytes, _p(pl["cnt"]), _p(pl["soff"]), _p(pl["roff"]),
+                           _p(pl["G"]), _p(pl["eoff"]), _p(y), _p(comb_send))
+    return comb_send
+
+
+def combine_transfer(comb_send: np.ndarray, pl: dict, T: int, K: int) -> np.ndarray:
+    comb_send = np.ascontiguousarray(comb_send)
+    N, E = pl["cnt"].shape
+    R = comb_send.shape[0]
+    comb_recv = np.zeros_like(comb_send)
+    row_bytes = comb_send.nbytes // R if R else 0
+    lib().orc_combine_transfer(N, E, T, K, row_bytes, _p(pl["soff"]), _p(pl["roff"]),
+                               _p(pl["G"]), _p(comb_send), _p(comb_recv))
+    return comb_recv
+
+
+def combine_recv(comb_recv: np.ndarray, pos: np.ndarray, w: np.ndarray, H: int) -> np.ndarray:
+    N, T, K = pos.shape
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    comb_recv = np.ascontiguousarray(comb_recv, dtype=np.uint16)
+    out = np.zeros((N, T, H), dtype=np.uint16)
+    lib().orc_combine_recv(N, T, K, H, _p(np.ascontiguousarray(pos)), _p(w), _p(comb_recv),
+                           _p(out))
+    return out
+
+
+def combine_recv_f64(comb_recv: np.ndarray, pos: np.ndarray, w: np.ndarray, H: int):
+    N, T, K = pos.shape
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    comb_recv = np.ascontiguousarray(comb_recv, dtype=np.uint16)
+    out = np.zeros((N, T, H), dtype=np.float64)
+    mag = np.zeros((N, T, H), dtype=np.float64)
+    lib().orc_combine_recv_f64(N, T, K, H, _p(np.ascontiguousarray(pos)), _p(w),
+                               _p(comb_recv), _p(out), _p(mag))
+    return out, mag
+
+
+def combine_token(rows: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Weighted sum of one token's K returned rows (uint16 [K][H])."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    K, H = rows.shape
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    ptrs = (ctypes.c_void_p * K)(*[rows[k].ctypes.data for k in range(K)])
+    out = np.zeros(H, dtype=np.uint16)
+    lib().orc_combine_token(K, H, ctypes.cast(ptrs, ctypes.c_void_p), _p(w), _p(out))
+    return out
+
+
+def run_combine(y: np.ndarray, w: np.ndarray, pl: dict, H: int) -> dict:
+    """Every combine step, in order; y is the expert output in expert-row order."""
+    N, T, K = pl["pos"].shape
+    comb_send = combine_send(y, pl)
+    comb_recv = combine_transfer(comb_send, pl, T, K)
+    out = combine_recv(comb_recv, pl["pos"], w, H)
+    return {"comb_send": comb_send, "comb_recv": comb_recv, "out": out}

@@ -1,0 +1,506 @@
+/*
+ * CPU oracle for the MoE dispatch/combine path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library) never calls it, includes it or shares code with it.
+ *
+ * It is the plain definition of each step, written as scalar loops in the
+ * order the pages describe, with its own bf16 and fp8-e4m3 codecs.  It is
+ * built with gcc -O2 -ffp-contract=off, so no multiply-add is fused unless
+ * fmaf() is written out.
+ *
+ * Pages cited:
+ *   [EPMC] "Efficient and portable Mixture-of-Experts communication"
+ *   [EFA]  "Enabling trillion-parameter models on AWS EFA"
+ *
+ * Notation: N logical ranks, T tokens per rank, K experts per token, E experts,
+ * L = E/N experts per rank (expert e lives on rank e / L), H hidden elements.
+ * idx[s][t][k] is the k-th expert of token t on rank s.  Row arrays are flat:
+ * the send rows of sender s are rows [s*T*K, (s+1)*T*K); the receive rows of
+ * receiver d are rows [G[d], G[d+1]) of one pooled array.
+ *
+ * Error behaviour: functions that validate their input return 0 on success and
+ * a negative value if an expert id is outside [0, E); they never abort.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ codecs */
+
+/* bf16 -> fp32: a bf16 value is the top 16 bits of the fp32 value. */
+float orc_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Value of a bf16 pattern as a double, with the all-ones exponent read as
+ * 2^128 (the value it would have with an unbounded exponent), so that rounding
+ * up past the largest finite bf16 picks infinity exactly when IEEE does. */
+static double bf16_mag_value(uint32_t mag16)
+{
+    if (mag16 == 0x7F80u)
+        return ldexp(1.0, 128);
+    return (double)orc_bf16_to_f32((uint16_t)mag16);
+}
+
+/* fp32 -> bf16, round to nearest, ties to even: pick the nearer of the two
+ * bf16 neighbours of |f| (the truncation and the next pattern up); on a tie
+ * take the one whose last mantissa bit is 0. */
+uint16_t orc_f32_to_bf16(float f)
+{
+    if (isnan(f))
+        return 0x7FC0u;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t sign = u & 0x80000000u;
+    uint32_t mag = u & 0x7FFFFFFFu;
+    if (mag >= 0x7F800000u)                /* infinity stays infinity */
+        return (uint16_t)((sign | mag) >> 16);
+    uint32_t lo = mag >> 16, hi = lo + 1;
+    double a = fabs((double)f);
+    double dlo = a - bf16_mag_value(lo);
+    double dhi = bf16_mag_value(hi) - a;
+    uint32_t pick;
+    if (dlo < dhi)
+        pick = lo;
+    else if (dhi < dlo)
+        pick = hi;
+    else
+        pick = (lo & 1u) ? hi : lo;
+    return (uint16_t)((sign >> 16) | pick);
+}
+
+/* OCP 8-bit floating point, E4M3 variant: 1 sign bit, 4 exponent bits (bias
+ * 7), 3 mantissa bits; exponent field 0 is subnormal (m * 2^-9); the pattern
+ * S.1111.111 is NaN; there is no infinity; largest finite value 448. */
+double orc_e4m3_value(uint8_t code)
+{
+    int sign = code >> 7, ex = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (ex == 15 && m == 7)
+        return NAN;
+    if (ex == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, ex - 7);
+    return sign ? -v : v;
+}
+
+/* fp32 -> e4m3, round to nearest with ties to even, saturating: |v| >= 448
+ * (infinity included) gives +-448; NaN gives the NaN pattern.  The nearest
+ * finite code is found by bisection over the increasing positive code values;
+ * a tie between two adjacent codes goes to the even code (mantissa bit 0).
+ * The sign bit is copied, so values that round to zero keep their sign. */
+uint8_t orc_f32_to_e4m3(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    /* largest code c in [0, 0x7E] with value(c) <= a */
+    int lo = 0, hi = 0x7E;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (orc_e4m3_value((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int c = lo;
+    if (orc_e4m3_value((uint8_t)c) != a) {
+        double dlo = a - orc_e4m3_value((uint8_t)c);
+        double dhi = orc_e4m3_value((uint8_t)(c + 1)) - a;
+        if (dhi < dlo || (dhi == dlo && ((c + 1) & 1) == 0))
+            c = c + 1;
+    }
+    return (uint8_t)(sign | c);
+}
+
+/* ------------------------------------------------ dispatch: count and offsets */
+
+/* Per-expert token counts of every sender ([EFA] "Dispatch and combine": the
+ * dispatch-send kernel first aggregates the routing information into token
+ * counts per expert).  cnt[s][e] = #{(t,k) : idx[s][t][k] == e}. */
+int orc_route_count(int N, int T, int K, int E, const int32_t* idx, int32_t* cnt)
+{
+    int bad = 0;
+    memset(cnt, 0, sizeof(int32_t) * (size_t)N * E);
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t)
+            for (int k = 0; k < K; ++k) {
+                int e = idx[((size_t)s * T + t) * K + k];
+                if (e < 0 || e >= E) {
+                    bad = 1;
+                    continue;
+                }
+                cnt[(size_t)s * E + e] += 1;
+            }
+    return bad ? -1 : 0;
+}
+
+/* Offsets inside each sender's contiguous send buffer ([EFA] "Dispatch and
+ * combine": the cumulative sum of the token counts gives the offsets at which
+ * tokens are packed into contiguous per-peer send buffers).
+ * soff[s][e] = sum_{e' < e} cnt[s][e'], soff[s][E] = T*K. */
+void orc_send_offsets(int N, int E, const int32_t* cnt, int32_t* soff)
+{
+    for (int s = 0; s < N; ++s) {
+        int32_t run = 0;
+        for (int e = 0; e < E; ++e) {
+            soff[(size_t)s * (E + 1) + e] = run;
+            run += cnt[(size_t)s * E + e];
+        }
+        soff[(size_t)s * (E + 1) + E] = run;
+    }
+}
+
+/* Position of each (t,k) in its sender's buffer: rows grouped by expert, and
+ * within one expert in (t,k) order -- a stable counting sort.  The pages leave
+ * the order inside an expert free (the receive order is not deterministic,
+ * [EPMC] "Dispatch"); a fixed order makes every byte checkable. */
+void orc_positions(int N, int T, int K, int E, const int32_t* idx,
+                   const int32_t* soff, int32_t* pos)
+{
+    int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    for (int s = 0; s < N; ++s) {
+        for (int e = 0; e < E; ++e)
+            cursor[e] = soff[(size_t)s * (E + 1) + e];
+        for (int t = 0; t < T; ++t)
+            for (int k = 0; k < K; ++k) {
+                size_t i = ((size_t)s * T + t) * K + k;
+                pos[i] = cursor[idx[i]]++;
+            }
+    }
+    free(cursor);
+}
+
+/* Receive-side offsets ([EFA] "Send and receive buffers": after the per-expert
+ * counts are exchanged, every rank knows where to write and from which offsets
+ * it receives).  scnt(s,d) = rows sender s sends to rank d = soff[s][(d+1)L] -
+ * soff[s][dL].  roff[d][s] = sum_{s' < s} scnt(s',d), roff[d][N] = rows d
+ * receives; G[d] = sum_{d' < d} roff[d'][N] is rank d's base in the pooled
+ * receive array, G[N] = N*T*K. */
+void orc_recv_offsets(int N, int E, const int32_t* soff, int32_t* roff, int32_t* G)
+{
+    int L = E / N;
+    for (int d = 0; d < N; ++d) {
+        int32_t run = 0;
+        for (int s = 0; s < N; ++s) {
+            roff[(size_t)d * (N + 1) + s] = run;
+            run += soff[(size_t)s * (E + 1) + (d + 1) * L] - soff[(size_t)s * (E + 1) + d * L];
+        }
+        roff[(size_t)d * (N + 1) + N] = run;
+    }
+    int32_t run = 0;
+    for (int d = 0; d < N; ++d) {
+        G[d] = run;
+        run += roff[(size_t)d * (N + 1) + N];
+    }
+    G[N] = run;
+}
+
+/* First row of every expert in the expert-contiguous grouped-GEMM input
+ * ([EPMC] "Dispatch": received tokens are laid out contiguously for the
+ * grouped GEMM).  eoff[e] = sum_{e' < e} sum_s cnt[s][e'], eoff[E] = N*T*K. */
+void orc_expert_offsets(int N, int E, const int32_t* cnt, int32_t* eoff)
+{
+    int32_t run = 0;
+    for (int e = 0; e < E; ++e) {
+        eoff[e] = run;
+        for (int s = 0; s < N; ++s)
+            run += cnt[(size_t)s * E + e];
+    }
+    eoff[E] = run;
+}
+
+/* --------------------------------------------------------------- dispatch: pack */
+
+/* Pack, bf16 payload ([EPMC] "Dispatch": activations and the token's index on
+ * the sending rank are packed into one contiguous chunk; [EFA] "Dispatch and
+ * combine": packed into contiguous per-peer send buffers).  Row pos[s][t][k] of
+ * sender s receives token t unchanged; its meta word is t*K+k. */
+void orc_pack_bf16(int N, int T, int K, int H, const uint16_t* x, const int32_t* pos,
+                   uint16_t* send_x, int32_t* send_meta)
+{
+    size_t TK = (size_t)T * K;
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t)
+            for (int k = 0; k < K; ++k) {
+                size_t row = (size_t)s * TK + pos[((size_t)s * T + t) * K + k];
+                memcpy(send_x + row * H, x + ((size_t)s * T + t) * H, sizeof(uint16_t) * H);
+                send_meta[row] = t * K + k;
+            }
+}
+
+/* Block-scaled fp8 quantisation of one token row ([EFA] "Dispatch/combine
+ * latency": block-scaled fp8 dispatch; [EPMC] "Dispatch": block scaling
+ * factors travel with the tokens).  For each block b of 128 elements:
+ * amax = max |x|; if amax > 0, inv = 448 / amax and scale = amax / 448 (each
+ * one fp32 division), else inv = 0 and scale = 1; code = e4m3(x * inv) with
+ * one fp32 multiply.  Dequantised value = e4m3 value * scale. */
+void orc_quant_row_fp8(int H, const uint16_t* xrow, uint8_t* q, float* scale)
+{
+    for (int b = 0; b < H / 128; ++b) {
+        float amax = 0.0f;
+        for (int i = 0; i < 128; ++i) {
+            float v = fabsf(orc_bf16_to_f32(xrow[b * 128 + i]));
+            if (v > amax)
+                amax = v;
+        }
+        float inv, sc;
+        if (amax > 0.0f) {
+            inv = 448.0f / amax;
+            sc = amax / 448.0f;
+        } else {
+            inv = 0.0f;
+            sc = 1.0f;
+        }
+        for (int i = 0; i < 128; ++i) {
+            float prod = orc_bf16_to_f32(xrow[b * 128 + i]) * inv;
+            q[b * 128 + i] = orc_f32_to_e4m3(prod);
+        }
+        scale[b] = sc;
+    }
+}
+
+/* Pack, fp8 payload: as orc_pack_bf16 but each token is quantised once and the
+ * K copies carry its codes and its H/128 block scales. */
+void orc_pack_fp8(int N, int T, int K, int H, const uint16_t* x, const int32_t* pos,
+                  uint8_t* send_q, float* send_scale, int32_t* send_meta)
+{
+    size_t TK = (size_t)T * K;
+    int nb = H / 128;
+    uint8_t* q = (uint8_t*)malloc((size_t)H);
+    float* sc = (float*)malloc(sizeof(float) * (size_t)nb);
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t) {
+            orc_quant_row_fp8(H, x + ((size_t)s * T + t) * H, q, sc);
+            for (int k = 0; k < K; ++k) {
+                size_t row = (size_t)s * TK + pos[((size_t)s * T + t) * K + k];
+                memcpy(send_q + row * H, q, (size_t)H);
+                memcpy(send_scale + row * nb, sc, sizeof(float) * nb);
+                send_meta[row] = t * K + k;
+            }
+        }
+    free(q);
+    free(sc);
+}
+
+/* ------------------------------------------------------ dispatch: transfer */
+
+/* The modelled network transfer ([EFA] "Dispatch and combine": the rows for
+ * one peer leave in a single write; [EFA] "Send and receive buffers"): for each
+ * sender s and receiver d, the scnt(s,d) rows starting at send row
+ * soff[s][dL] of sender s land at receive row G[d] + roff[d][s].  Rows are
+ * opaque byte strings of row_bytes bytes; the call is made once per plane
+ * (payload, scales, meta). */
+void orc_transfer(int N, int E, int T, int K, size_t row_bytes, const int32_t* soff,
+                  const int32_t* roff, const int32_t* G, const uint8_t* send, uint8_t* recv)
+{
+    int L = E / N;
+    size_t TK = (size_t)T * K;
+    for (int s = 0; s < N; ++s)
+        for (int d = 0; d < N; ++d) {
+            int32_t first = soff[(size_t)s * (E + 1) + d * L];
+            int32_t n = soff[(size_t)s * (E + 1) + (d + 1) * L] - first;
+            size_t src = (size_t)s * TK + first;
+            size_t dst = (size_t)G[d] + roff[(size_t)d * (N + 1) + s];
+            memcpy(recv + dst * row_bytes, send + src * row_bytes, row_bytes * (size_t)n);
+        }
+}
+
+/* ------------------------------------------------------ dispatch: shuffle */
+
+/* Receive shuffle into grouped-GEMM order ([EPMC] "Dispatch": the receiver
+ * copies tokens into contiguous buffers for the expert kernels and stores
+ * source rank, expert and token index separately; [EFA] "Dispatch and combine":
+ * rows are shuffled from the receive buffer into the tensor handed to the
+ * grouped GEMM).  For expert e on rank d = e/L, for s ascending, the cnt[s][e]
+ * rows of e from sender s (at receive row G[d] + roff[d][s] + soff[s][e] -
+ * soff[s][dL] onward) go to expert rows eoff[e] + sum_{s'<s} cnt[s'][e] onward.
+ * Metadata: src_rank[r] = s, src_slot[r] = the row's meta word (t*K+k).
+ * The payload plane has row_bytes bytes per row; scales (scale_bytes per row,
+ * 0 when there are none) move with it. */
+void orc_shuffle(int N, int E, int T, int K, size_t row_bytes, size_t scale_bytes,
+                 const int32_t* cnt, const int32_t* soff, const int32_t* roff,
+                 const int32_t* G, const int32_t* eoff,
+                 const uint8_t* recv_x, const uint8_t* recv_scale, const int32_t* recv_meta,
+                 uint8_t* expert_x, uint8_t* expert_scale,
+                 int32_t* src_rank, int32_t* src_slot)
+{
+    int L = E / N;
+    (void)T;
+    (void)K;
+    for (int e = 0; e < E; ++e) {
+        int d = e / L;
+        int32_t r = eoff[e];
+        for (int s = 0; s < N; ++s) {
+            int32_t n = cnt[(size_t)s * E + e];
+            int32_t q0 = G[d] + roff[(size_t)d * (N + 1) + s] +
+                         soff[(size_t)s * (E + 1) + e] - soff[(size_t)s * (E + 1) + d * L];
+            for (int32_t i = 0; i < n; ++i, ++r) {
+                size_t q = (size_t)q0 + i;
+                memcpy(expert_x + (size_t)r * row_bytes, recv_x + q * row_bytes, row_bytes);
+                if (scale_bytes)
+                    memcpy(expert_scale + (size_t)r * scale_bytes, recv_scale + q * scale_bytes,
+                           scale_bytes);
+                src_rank[r] = s;
+                src_slot[r] = recv_meta[q];
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------- the expert (not the path) */
+
+/* Stand-in for the grouped GEMM, outside the path: y[r] = bf16(v * (e+1)) where
+ * e is row r's expert and v the row's value (bf16, or e4m3 value * block scale
+ * when scales are given), one fp32 multiply per factor. */
+void orc_expert_standin(int E, int H, const int32_t* eoff, const uint8_t* expert_x,
+                        const float* expert_scale, int fp8, uint16_t* y)
+{
+    int nb = H / 128;
+    for (int e = 0; e < E; ++e)
+        for (int32_t r = eoff[e]; r < eoff[e + 1]; ++r)
+            for (int h = 0; h < H; ++h) {
+                float v;
+                if (fp8) {
+                    v = (float)orc_e4m3_value(expert_x[(size_t)r * H + h]) *
+                        expert_scale[(size_t)r * nb + h / 128];
+                } else {
+                    uint16_t b;
+                    memcpy(&b, expert_x + ((size_t)r * H + h) * 2, 2);
+                    v = orc_bf16_to_f32(b);
+                }
+                y[(size_t)r * H + h] = orc_f32_to_bf16(v * (float)(e + 1));
+            }
+}
+
+/* --------------------------------------------------------------- combine */
+
+/* Combine send ([EPMC] "Combine": senders copy the unquantised 16-bit expert
+ * outputs back toward the token's rank; [EFA] "Dispatch and combine": combine
+ * is the reverse route, one write per peer).  The inverse of orc_shuffle: the
+ * expert-order row r of expert e from sender s, i-th of its run, goes back to
+ * receive-layout row G[d] + roff[d][s] + soff[s][e] - soff[s][dL] + i. */
+void orc_combine_send(int N, int E, size_t row_bytes, const int32_t* cnt,
+                      const int32_t* soff, const int32_t* roff, const int32_t* G,
+                      const int32_t* eoff, const uint8_t* y, uint8_t* comb_send)
+{
+    int L = E / N;
+    for (int e = 0; e < E; ++e) {
+        int d = e / L;
+        int32_t r = eoff[e];
+        for (int s = 0; s < N; ++s) {
+            int32_t n = cnt[(size_t)s * E + e];
+            int32_t q0 = G[d] + roff[(size_t)d * (N + 1) + s] +
+                         soff[(size_t)s * (E + 1) + e] - soff[(size_t)s * (E + 1) + d * L];
+            for (int32_t i = 0; i < n; ++i, ++r)
+                memcpy(comb_send + ((size_t)q0 + i) * row_bytes, y + (size_t)r * row_bytes,
+                       row_bytes);
+        }
+    }
+}
+
+/* Combine transfer: the reverse of orc_transfer.  The rows rank d holds for
+ * sender s (receive rows G[d] + roff[d][s] ...) return to sender s's buffer at
+ * rows s*T*K + soff[s][dL] ..., i.e. where s packed them. */
+void orc_combine_transfer(int N, int E, int T, int K, size_t row_bytes, const int32_t* soff,
+                          const int32_t* roff, const int32_t* G, const uint8_t* comb_send,
+                          uint8_t* comb_recv)
+{
+    int L = E / N;
+    size_t TK = (size_t)T * K;
+    for (int d = 0; d < N; ++d)
+        for (int s = 0; s < N; ++s) {
+            int32_t first = soff[(size_t)s * (E + 1) + d * L];
+            int32_t n = soff[(size_t)s * (E + 1) + (d + 1) * L] - first;
+            size_t src = (size_t)G[d] + roff[(size_t)d * (N + 1) + s];
+            size_t dst = (size_t)s * TK + first;
+            memcpy(comb_recv + dst * row_bytes, comb_send + src * row_bytes, row_bytes * (size_t)n);
+        }
+}
+
+/* Combine receive: the router-weighted sum of the K expert outputs of every
+ * token ([EPMC] "Introduction": the output is the sum of the expert outputs
+ * multiplied by weights from the router distribution; [EPMC] "Combine": the
+ * receiver computes the weighted average locally into an externally allocated
+ * tensor).  Precision: fp32, k ascending, as one fused multiply-add chain
+ * from +0, rounded once to bf16 (nearest even):
+ *   acc = +0; for k: acc = fmaf(w[s][t][k], y_k[h], acc); out = bf16(acc)
+ * where y_k is the returned row at sender row pos[s][t][k]. */
+void orc_combine_recv(int N, int T, int K, int H, const int32_t* pos, const float* w,
+                      const uint16_t* comb_recv, uint16_t* out)
+{
+    size_t TK = (size_t)T * K;
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t)
+            for (int h = 0; h < H; ++h) {
+                float acc = +0.0f;
+                for (int k = 0; k < K; ++k) {
+                    size_t i = ((size_t)s * T + t) * K + k;
+                    size_t row = (size_t)s * TK + pos[i];
+                    acc = fmaf(w[i], orc_bf16_to_f32(comb_recv[row * H + h]), acc);
+                }
+                out[((size_t)s * T + t) * H + h] = orc_f32_to_bf16(acc);
+            }
+}
+
+/* The same weighted sum in double precision, unrounded (each product of a
+ * float weight and a bf16 value is exact in double; the sum of K <= 16 such
+ * terms is exact to within 2^-50 relative).  Used only to bound the fp32
+ * chain above. */
+void orc_combine_recv_f64(int N, int T, int K, int H, const int32_t* pos, const float* w,
+                          const uint16_t* comb_recv, double* out, double* abs_sum)
+{
+    size_t TK = (size_t)T * K;
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t)
+            for (int h = 0; h < H; ++h) {
+                double acc = 0.0, mag = 0.0;
+                for (int k = 0; k < K; ++k) {
+                    size_t i = ((size_t)s * T + t) * K + k;
+                    size_t row = (size_t)s * TK + pos[i];
+                    double term = (double)w[i] * (double)orc_bf16_to_f32(comb_recv[row * H + h]);
+                    acc += term;
+                    mag += fabs(term);
+                }
+                out[((size_t)s * T + t) * H + h] = acc;
+                abs_sum[((size_t)s * T + t) * H + h] = mag;
+            }
+}
+
+/* Combine receive of a single token (sampled checks at sizes where the whole
+ * output is too large for the CPU): same chain as orc_combine_recv.  rows[k]
+ * points at the k-th returned row, w at the token's K weights. */
+void orc_combine_token(int K, int H, const uint16_t* const* rows, const float* w, uint16_t* out)
+{
+    for (int h = 0; h < H; ++h) {
+        float acc = +0.0f;
+        for (int k = 0; k < K; ++k)
+            acc = fmaf(w[k], orc_bf16_to_f32(rows[k][h]), acc);
+        out[h] = orc_f32_to_bf16(acc);
+    }
+}
+
+/* ------------------------------------------------ array forms of the codecs */
+
+void orc_f32_to_bf16_n(size_t n, const float* in, uint16_t* out)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = orc_f32_to_bf16(in[i]);
+}
+
+void orc_f32_to_e4m3_n(size_t n, const float* in, uint8_t* out)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = orc_f32_to_e4m3(in[i]);
+}
