@@ -1,0 +1,227 @@
+"""Benchmark: microseconds per MoE dispatch+combine on one MI355X, and the
+achieved HBM bandwidth against the 8 TB/s peak.
+
+One step = moe_dispatch_send + moe_dispatch_recv + moe_combine_send +
+moe_combine_recv over one batch of the DeepSeek-R1-shaped decode workload
+(32 logical ranks x 128 tokens, hidden 7168 bf16, top-8 of 256 experts).  The
+expert between dispatch and combine is outside the path: its output (the
+stand-in y = x*(e+1) of the first cycle) is computed once before timing and
+reused, since the routing is the same every step.  Inputs are resident in HBM
+before the timed region.
+
+Prints one JSON line.  Per-kernel times come from HIP events the library
+records on the launch stream around each kernel during the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs per dispatch+combine and achieved HBM GB/s (% of peak), DeepSeek-R1 shape"
+HBM_PEAK_GBPS = 8000.0
+
+
+def kernel_bytes(cfg) -> dict:
+    """Algorithmic HBM bytes per launch of each kernel: every buffer the method
+    mandates is written once and read once by the next stage; inputs are read
+    once per token.  The int32 row maps the pack kernel writes for the later
+    movers (4-8 bytes per row of 7-14 KiB) are an implementation detail and not
+    counted."""
+    N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
+    R = N * T * K
+    fp8 = cfg.dtype == "fp8"
+    hb = H if fp8 else 2 * H                     # payload bytes per row
+    sb = (H // 128) * 4 if fp8 else 0            # block scales per row
+    hy = 2 * H                                   # combine row
+    tokens = N * T
+    return {
+        "route_count": R * 4 + N * E * 4 + N * (E + 1) * 4 + R * 4,
+        "offsets": N * E * 4 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4 + (E + 1) * 4 + N * E * 4,
+        "pack": tokens * H * 2 + R * 4 * 2 + R * (hb + sb + 4),
+        "transfer": 2 * R * (hb + sb + 4),
+        "shuffle": R * (hb + sb + 4) + R * (hb + sb + 8) + (E + 1) * 4,
+        "combine_pack": 2 * R * hy,
+        "transfer_back": 2 * R * hy,
+        "combine_reduce": R * hy + R * 8 + tokens * H * 2,
+    }
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_moe_dispatch_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_key: str, kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config_key}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != src_hash:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, min_seconds: float) -> dict:
+    """The oracle, unchanged and single-threaded, on the same workload: whole
+    dispatch + combine steps until min_seconds of work (at least one)."""
+    import numpy as np
+
+    import oracle
+    d0 = oracle.run_dispatch(inp["x"], inp["idx"], cfg.E, fp8=cfg.dtype == "fp8")
+    y = oracle.expert_standin(d0["expert_x"], d0["expert_scale"], d0["eoff"], cfg.H)
+    del d0
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        d = oracle.run_dispatch(inp["x"], inp["idx"], cfg.E, fp8=cfg.dtype == "fp8")
+        c = oracle.run_combine(y, inp["w"], d, cfg.H)
+        steps += 1
+        del d, c
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    assert isinstance(y, np.ndarray)
+    return {"value": round(el / steps * 1e6, 1), "unit": "us per dispatch+combine", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{steps} full dispatch+combine step(s) of the {cfg.name} workload "
+                      f"({cfg.N}x{cfg.T} tokens), single thread, {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="C")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the N logical ranks of the group all live on a "
+              f"single device; --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import combine_moe_dispatch_amd as mep
+    from workloads import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
+    R = cfg.rows
+    fp8 = cfg.dtype == "fp8"
+    print(f"[bench] {cfg.describe()} rows={R}", file=sys.stderr, flush=True)
+    inp = make_inputs(cfg)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
+    idx = torch.from_numpy(inp["idx"]).to(dev)
+    w = torch.from_numpy(inp["w"]).to(dev)
+    payload = H if fp8 else 2 * H
+    expert_x = torch.empty((R, payload), dtype=torch.uint8, device=dev)
+    expert_scale = torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+    offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    out = torch.empty((N, T, H), dtype=torch.bfloat16, device=dev)
+    g = mep.moe_group_create(N, E, K, H, T, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16)
+    stream = torch.cuda.current_stream()
+
+    # first cycle + the stand-in expert output reused by every step
+    mep.moe_dispatch_send(g, T, x, idx, stream)
+    mep.moe_dispatch_recv(g, expert_x, expert_scale, offs, stream)
+    from workloads.expert import standin_expert
+    y = standin_expert(torch, expert_x.view(-1), expert_scale.view(-1) if fp8 else None, offs,
+                       E, H, fp8).contiguous()
+    mep.moe_combine_send(g, y, stream)
+    mep.moe_combine_recv(g, w, out, stream)
+    torch.cuda.synchronize()
+    assert mep.moe_group_status(g, stream) == mep.MOE_OK
+
+    def step():
+        mep.moe_dispatch_send(g, T, x, idx, stream)
+        mep.moe_dispatch_recv(g, expert_x, expert_scale, offs, stream)
+        mep.moe_combine_send(g, y, stream)
+        mep.moe_combine_recv(g, w, out, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mep.moe_group_timing_enable(g, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    timing = mep.moe_group_timing_read(g)
+    mep.moe_group_timing_enable(g, False)
+    assert mep.moe_group_status(g, stream) == mep.MOE_OK
+    mep.moe_group_destroy(g)
+
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+    kb = kernel_bytes(cfg)
+    total_bytes = sum(kb.values())
+    kern = {}
+    for name, (ms, n) in timing.items():
+        if n:
+            avg_us = ms / n * 1e3
+            kern[name] = {"avg_us": round(avg_us, 2), "launches": n,
+                          "gbps": round(kb[name] / (avg_us * 1e-6) / 1e9, 1)}
+    dom = max(kern, key=lambda k: kern[k]["avg_us"] * kern[k]["launches"])
+    ach = kb[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = measured_traffic(args.config, dom, src_hash)
+    gbps_eff = total_bytes / (ms_per_step * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1e3, 1),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8+bf16" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.describe(), "logical_ranks": N, "tokens_per_rank": T,
+                   "hidden": H, "experts": E, "top_k": K, "rows": R,
+                   "dispatch_dtype": cfg.dtype, "combine_dtype": "bf16",
+                   "parallelism": f"ep{N} (logical ranks on one GPU)"},
+        "hbm_gbps_eff": round(gbps_eff, 1),
+        "frac_of_hbm_peak": round(gbps_eff / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": total_bytes,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "bytes_per_launch": kb[dom], "traffic": traffic},
+        "kernels": kern,
+        "source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,174 @@
+"""Python binding of libmoe_ep.so, the MI355X MoE dispatch/combine library.
+
+Argument marshalling only: every call below forwards to the C function of the
+same name in include/moe_ep.h (ctypes), passing device pointers and the HIP
+stream.  Tensors may be torch tensors (their data_ptr() is passed) or raw
+integer device addresses.  A non-zero status raises MoeError.
+
+The library is built in-tree by ``python -m combine_moe_dispatch_amd._build``;
+importing this package without it raises ImportError -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmoe_ep.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID = -1
+MOE_ERR_HIP = -2
+MOE_ERR_OOM = -3
+MOE_ERR_STATE = -4
+MOE_ERR_ROUTING = -5
+MOE_ERR_CAPACITY = -6
+
+MOE_BF16 = 0
+MOE_FP8_E4M3 = 1
+
+KERNELS = ["route_count", "offsets", "pack", "transfer", "shuffle", "combine_pack",
+           "transfer_back", "combine_reduce"]
+MOE_KERNEL_COUNT = len(KERNELS)
+
+
+class moe_group_desc(ctypes.Structure):
+    _fields_ = [("num_ranks", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("dispatch_dtype", ctypes.c_int32)]
+
+
+class moe_group_view(ctypes.Structure):
+    _fields_ = [("desc", moe_group_desc), ("num_tokens", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("payload_row_bytes", ctypes.c_int64),
+                ("combine_row_bytes", ctypes.c_int64), ("scale_blocks", ctypes.c_int32)] + [
+        (name, ctypes.c_void_p) for name in (
+            "cnt", "pos", "send_off", "recv_off", "recv_base", "expert_off", "send_x",
+            "send_scale", "send_meta", "recv_x", "recv_scale", "recv_meta",
+            "expert_src_rank", "expert_src_slot", "comb_send", "comb_recv")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {strerror(status)} ({status})")
+
+
+def _load():
+    # torch ships its own HIP runtime (soname libamdhip64.so.7); importing it
+    # first makes the library bind to that same runtime instead of loading a
+    # second one from the ROCm install.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m combine_moe_dispatch_amd._build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I32, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "moe_group_create": ([ctypes.POINTER(moe_group_desc), ctypes.POINTER(P)], I),
+        "moe_group_destroy": ([P], I),
+        "moe_dispatch_send": ([P, I32, P, P, P], I),
+        "moe_dispatch_recv": ([P, P, P, P, P], I),
+        "moe_combine_send": ([P, P, P], I),
+        "moe_combine_recv": ([P, P, P, P], I),
+        "moe_group_view_get": ([P, ctypes.POINTER(moe_group_view)], I),
+        "moe_group_status": ([P, P], I),
+        "moe_group_timing_enable": ([P, I], I),
+        "moe_group_timing_read": ([P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)], I),
+        "moe_strerror": ([I], ctypes.c_char_p),
+        "moe_kernel_name": ([I], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, call: str):
+    if status != MOE_OK:
+        raise MoeError(status, call)
+
+
+def strerror(status: int) -> str:
+    return _lib.moe_strerror(status).decode()
+
+
+def moe_group_create(num_ranks: int, num_experts: int, top_k: int, hidden: int,
+                     max_tokens: int, dispatch_dtype: int = MOE_BF16) -> int:
+    desc = moe_group_desc(num_ranks, num_experts, top_k, hidden, max_tokens, dispatch_dtype)
+    h = ctypes.c_void_p()
+    _check(_lib.moe_group_create(ctypes.byref(desc), ctypes.byref(h)), "moe_group_create")
+    return h.value
+
+
+def moe_group_destroy(g: int) -> None:
+    _check(_lib.moe_group_destroy(g), "moe_group_destroy")
+
+
+def moe_dispatch_send(g: int, num_tokens: int, x, topk_idx, stream=None) -> None:
+    _check(_lib.moe_dispatch_send(g, num_tokens, _ptr(x), _ptr(topk_idx), _stream(stream)),
+           "moe_dispatch_send")
+
+
+def moe_dispatch_recv(g: int, expert_x, expert_scale, expert_offsets, stream=None) -> None:
+    _check(_lib.moe_dispatch_recv(g, _ptr(expert_x), _ptr(expert_scale), _ptr(expert_offsets),
+                                  _stream(stream)), "moe_dispatch_recv")
+
+
+def moe_combine_send(g: int, expert_y, stream=None) -> None:
+    _check(_lib.moe_combine_send(g, _ptr(expert_y), _stream(stream)), "moe_combine_send")
+
+
+def moe_combine_recv(g: int, topk_weights, out, stream=None) -> None:
+    _check(_lib.moe_combine_recv(g, _ptr(topk_weights), _ptr(out), _stream(stream)),
+           "moe_combine_recv")
+
+
+def moe_group_view_get(g: int) -> moe_group_view:
+    v = moe_group_view()
+    _check(_lib.moe_group_view_get(g, ctypes.byref(v)), "moe_group_view_get")
+    return v
+
+
+def moe_group_status(g: int, stream=None) -> int:
+    """Synchronise and return (not raise) the device-side status."""
+    return _lib.moe_group_status(g, _stream(stream))
+
+
+def moe_group_timing_enable(g: int, enable: bool) -> None:
+    _check(_lib.moe_group_timing_enable(g, int(bool(enable))), "moe_group_timing_enable")
+
+
+def moe_group_timing_read(g: int) -> dict:
+    """{kernel: (total_ms, launches)} for the launches since the last read."""
+    ms = (ctypes.c_double * MOE_KERNEL_COUNT)()
+    n = (ctypes.c_int64 * MOE_KERNEL_COUNT)()
+    _check(_lib.moe_group_timing_read(g, ms, n), "moe_group_timing_read")
+    return {KERNELS[i]: (ms[i], n[i]) for i in range(MOE_KERNEL_COUNT)}
+
+
+def moe_kernel_name(kernel_id: int) -> str:
+    return _lib.moe_kernel_name(kernel_id).decode()

@@ -1,0 +1,480 @@
+// Host side of the C ABI declared in include/moe_ep.h: argument validation,
+// the group's memory plan, the call-order state machine, and kernel launches
+// on the caller's stream.
+//
+// Pages cited:
+//   [EPMC] "Efficient and portable Mixture-of-Experts communication"
+//   [EFA]  "Enabling trillion-parameter models on AWS EFA"
+//
+// Memory plan.  The pages size every rank's receive space for the worst case
+// (a rank receives at most N*T*max(K, E/N) rows -- [EFA] "Send and receive
+// buffers").  Here all N logical ranks share one device, and together they
+// always hold exactly N*T*K rows per stage, so the send and receive buffers are
+// each ONE pooled array of N*T_max*K rows: sender s owns rows
+// [s*T*K, (s+1)*T*K) of the send pool, receiver d owns rows
+// [rbase[d], rbase[d+1]) of the receive pool, bases computed on the device from
+// the exchanged counts.  The same two pools carry the combine rows, as the
+// pages reuse buffers between dispatch and combine ([EFA] "Dispatch and
+// combine").  Row size of a pool = max(payload row, 2H) = 2H bytes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "moe_ep.h"
+#include "moe_kernels.h"
+
+namespace {
+
+enum class State { Idle, Sent, Received, CombineSent };
+
+struct EventPair {
+    hipEvent_t start = nullptr, stop = nullptr;
+    int kernel = 0;
+};
+
+}  // namespace
+
+struct moe_group_s {
+    moe_group_desc desc{};
+    int device = 0;
+    int L = 0;
+    int64_t rows_max = 0;
+    int payload_bytes = 0;   // per row
+    int comb_bytes = 0;
+    int scale_blocks = 0;
+
+    moe::Plan plan{};
+    void* pool_send = nullptr;
+    void* pool_recv = nullptr;
+    float* send_scale = nullptr;
+    float* recv_scale = nullptr;
+    int32_t* send_meta = nullptr;
+    int32_t* recv_meta = nullptr;
+    int32_t* src_rank = nullptr;
+    int32_t* src_slot = nullptr;
+
+    State state = State::Idle;
+    int32_t T = 0;
+
+    bool timing = false;
+    std::vector<EventPair> events;
+    size_t events_used = 0;
+
+    std::vector<void*> allocations;
+};
+
+namespace {
+
+const char* const kKernelNames[MOE_KERNEL_COUNT] = {
+    "route_count_kernel", "offsets_kernel",       "pack_kernel",          "transfer_kernel",
+    "shuffle_kernel",     "combine_pack_kernel",  "transfer_back_kernel", "combine_reduce_kernel",
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int validate_desc(const moe_group_desc* d)
+{
+    if (!d)
+        return MOE_ERR_INVALID;
+    if (d->num_ranks < 1 || d->num_ranks > moe::MAX_RANKS)
+        return MOE_ERR_INVALID;
+    if (d->num_experts < d->num_ranks || d->num_experts > moe::MAX_EXPERTS ||
+        d->num_experts % d->num_ranks != 0)
+        return MOE_ERR_INVALID;
+    if (d->top_k < 1 || d->top_k > moe::MAX_TOPK)
+        return MOE_ERR_INVALID;
+    if (d->hidden < 8 || d->hidden > 65536 || d->hidden % 8 != 0)
+        return MOE_ERR_INVALID;
+    if (d->dispatch_dtype != MOE_BF16 && d->dispatch_dtype != MOE_FP8_E4M3)
+        return MOE_ERR_INVALID;
+    if (d->dispatch_dtype == MOE_FP8_E4M3 && d->hidden % 128 != 0)
+        return MOE_ERR_INVALID;
+    if (d->max_tokens < 0)
+        return MOE_ERR_INVALID;
+    const int64_t rows = (int64_t)d->num_ranks * d->max_tokens * d->top_k;
+    if (rows >= ((int64_t)1 << 31))
+        return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
+moe::Shape shape_of(const moe_group_s* g, int T)
+{
+    moe::Shape sh{};
+    sh.N = g->desc.num_ranks;
+    sh.E = g->desc.num_experts;
+    sh.K = g->desc.top_k;
+    sh.L = g->L;
+    sh.H = g->desc.hidden;
+    sh.T = T;
+    sh.fp8 = g->desc.dispatch_dtype == MOE_FP8_E4M3;
+    sh.rows = (int64_t)sh.N * T * sh.K;
+    sh.payload_vecs = g->payload_bytes / 16;
+    sh.comb_vecs = g->comb_bytes / 16;
+    sh.scale_blocks = g->scale_blocks;
+    return sh;
+}
+
+moe::Rows rows_of(const moe_group_s* g)
+{
+    moe::Rows r{};
+    r.send_x = g->pool_send;
+    r.send_scale = g->send_scale;
+    r.send_meta = g->send_meta;
+    r.recv_x = g->pool_recv;
+    r.recv_scale = g->recv_scale;
+    r.recv_meta = g->recv_meta;
+    r.src_rank = g->src_rank;
+    r.src_slot = g->src_slot;
+    r.comb_send = g->pool_send;
+    r.comb_recv = g->pool_recv;
+    return r;
+}
+
+void free_all(moe_group_s* g)
+{
+    for (void* p : g->allocations)
+        (void)hipFree(p);
+    g->allocations.clear();
+    for (auto& e : g->events) {
+        if (e.start) (void)hipEventDestroy(e.start);
+        if (e.stop) (void)hipEventDestroy(e.stop);
+    }
+    g->events.clear();
+}
+
+template <typename T>
+int alloc(moe_group_s* g, T** out, size_t count)
+{
+    void* p = nullptr;
+    const size_t bytes = std::max<size_t>(count * sizeof(T), 256);
+    const hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation ? MOE_ERR_OOM : MOE_ERR_HIP;
+    }
+    g->allocations.push_back(p);
+    *out = static_cast<T*>(p);
+    return MOE_OK;
+}
+
+// Run one kernel launch, bracketed by timing events when enabled.
+template <typename F>
+int timed_launch(moe_group_s* g, int kernel, hipStream_t st, F&& launch)
+{
+    EventPair* ev = nullptr;
+    if (g->timing) {
+        if (g->events_used == g->events.size()) {
+            EventPair e;
+            if (hipEventCreate(&e.start) != hipSuccess || hipEventCreate(&e.stop) != hipSuccess)
+                return MOE_ERR_HIP;
+            g->events.push_back(e);
+        }
+        ev = &g->events[g->events_used++];
+        ev->kernel = kernel;
+        if (hipEventRecord(ev->start, st) != hipSuccess)
+            return MOE_ERR_HIP;
+    }
+    const hipError_t e = launch();
+    if (e != hipSuccess)
+        return MOE_ERR_HIP;
+    if (ev && hipEventRecord(ev->stop, st) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int check_device(const moe_group_s* g)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MOE_ERR_HIP;
+    return dev == g->device ? MOE_OK : MOE_ERR_INVALID;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_OOM: return "out of device memory";
+    case MOE_ERR_STATE: return "call out of the dispatch/combine order";
+    case MOE_ERR_ROUTING: return "expert id outside [0, num_experts)";
+    case MOE_ERR_CAPACITY: return "receive count above the group's bound";
+    default: return "unknown status";
+    }
+}
+
+const char* moe_kernel_name(int kernel_id)
+{
+    if (kernel_id < 0 || kernel_id >= MOE_KERNEL_COUNT)
+        return "";
+    return kKernelNames[kernel_id];
+}
+
+int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
+{
+    if (!out)
+        return MOE_ERR_INVALID;
+    int rc = validate_desc(desc);
+    if (rc != MOE_OK)
+        return rc;
+    moe_group_s* g = new (std::nothrow) moe_group_s();
+    if (!g)
+        return MOE_ERR_OOM;
+    g->desc = *desc;
+    if (hipGetDevice(&g->device) != hipSuccess) {
+        delete g;
+        return MOE_ERR_HIP;
+    }
+    const int N = desc->num_ranks, E = desc->num_experts, K = desc->top_k, H = desc->hidden;
+    const int T = desc->max_tokens;
+    g->L = E / N;
+    g->rows_max = (int64_t)N * T * K;
+    const bool fp8 = desc->dispatch_dtype == MOE_FP8_E4M3;
+    g->payload_bytes = fp8 ? H : 2 * H;
+    g->comb_bytes = 2 * H;
+    g->scale_blocks = fp8 ? H / 128 : 0;
+    const size_t R = (size_t)g->rows_max;
+    const size_t pool_bytes = R * (size_t)std::max(g->payload_bytes, g->comb_bytes);
+
+    moe::Plan& p = g->plan;
+    uint8_t* pool_send = nullptr;
+    uint8_t* pool_recv = nullptr;
+    if ((rc = alloc(g, &p.err, 1)) || (rc = alloc(g, &p.cnt, (size_t)N * E)) ||
+        (rc = alloc(g, &p.pos, (size_t)N * T * K)) || (rc = alloc(g, &p.soff, (size_t)N * (E + 1))) ||
+        (rc = alloc(g, &p.roff, (size_t)N * (N + 1))) || (rc = alloc(g, &p.rbase, (size_t)N + 1)) ||
+        (rc = alloc(g, &p.eoff, (size_t)E + 1)) || (rc = alloc(g, &p.ebase, (size_t)N * E)) ||
+        (rc = alloc(g, &p.xfer_src, R)) || (rc = alloc(g, &p.shuf_map, R)) ||
+        (rc = alloc(g, &pool_send, pool_bytes)) || (rc = alloc(g, &pool_recv, pool_bytes)) ||
+        (rc = alloc(g, &g->send_meta, R)) || (rc = alloc(g, &g->recv_meta, R)) ||
+        (rc = alloc(g, &g->src_rank, R)) || (rc = alloc(g, &g->src_slot, R)) ||
+        (fp8 && ((rc = alloc(g, &g->send_scale, R * g->scale_blocks)) ||
+                 (rc = alloc(g, &g->recv_scale, R * g->scale_blocks))))) {
+        free_all(g);
+        delete g;
+        return rc;
+    }
+    g->pool_send = pool_send;
+    g->pool_recv = pool_recv;
+    // the error word starts clear; the offsets start valid for an empty cycle
+    if (hipMemset(p.err, 0, sizeof(int32_t)) != hipSuccess ||
+        hipMemset(p.eoff, 0, sizeof(int32_t) * (E + 1)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        free_all(g);
+        delete g;
+        return MOE_ERR_HIP;
+    }
+    *out = g;
+    return MOE_OK;
+}
+
+int moe_group_destroy(moe_group_t g)
+{
+    if (!g)
+        return MOE_OK;
+    int rc = MOE_OK;
+    if (hipDeviceSynchronize() != hipSuccess)
+        rc = MOE_ERR_HIP;
+    free_all(g);
+    delete g;
+    return rc;
+}
+
+int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const int32_t* topk_idx,
+                      hipStream_t stream)
+{
+    if (!g)
+        return MOE_ERR_INVALID;
+    if (g->state != State::Idle)
+        return MOE_ERR_STATE;
+    if (num_tokens < 0 || num_tokens > g->desc.max_tokens)
+        return MOE_ERR_INVALID;
+    if (num_tokens > 0 && (!x || !topk_idx || !aligned16(x) || !aligned16(topk_idx)))
+        return MOE_ERR_INVALID;
+    int rc = check_device(g);
+    if (rc != MOE_OK)
+        return rc;
+    const moe::Shape sh = shape_of(g, num_tokens);
+    const moe::Rows rows = rows_of(g);
+    if ((rc = timed_launch(g, MOE_KERNEL_ROUTE_COUNT, stream,
+                           [&] { return moe::launch_route_count(sh, topk_idx, g->plan, stream); })) ||
+        (rc = timed_launch(g, MOE_KERNEL_OFFSETS, stream,
+                           [&] { return moe::launch_offsets(sh, g->plan, stream); })) ||
+        (rc = timed_launch(g, MOE_KERNEL_PACK, stream,
+                           [&] { return moe::launch_pack(sh, x, topk_idx, g->plan, rows, stream); })) ||
+        (rc = timed_launch(g, MOE_KERNEL_TRANSFER, stream,
+                           [&] { return moe::launch_transfer(sh, g->plan, rows, stream); })))
+        return rc;
+    g->T = num_tokens;
+    g->state = State::Sent;
+    return MOE_OK;
+}
+
+int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale, int32_t* expert_offsets,
+                      hipStream_t stream)
+{
+    if (!g)
+        return MOE_ERR_INVALID;
+    if (g->state != State::Sent)
+        return MOE_ERR_STATE;
+    const bool fp8 = g->desc.dispatch_dtype == MOE_FP8_E4M3;
+    const bool any_rows = g->T > 0;
+    if (!expert_offsets || !aligned16(expert_offsets))
+        return MOE_ERR_INVALID;
+    if (any_rows && (!expert_x || !aligned16(expert_x)))
+        return MOE_ERR_INVALID;
+    if (fp8 && any_rows && (!expert_scale || !aligned16(expert_scale)))
+        return MOE_ERR_INVALID;
+    if (!fp8 && expert_scale)
+        return MOE_ERR_INVALID;
+    int rc = check_device(g);
+    if (rc != MOE_OK)
+        return rc;
+    const moe::Shape sh = shape_of(g, g->T);
+    const moe::Rows rows = rows_of(g);
+    if ((rc = timed_launch(g, MOE_KERNEL_SHUFFLE, stream, [&] {
+             return moe::launch_shuffle(sh, g->plan, rows, expert_x, expert_scale, expert_offsets,
+                                        stream);
+         })))
+        return rc;
+    g->state = State::Received;
+    return MOE_OK;
+}
+
+int moe_combine_send(moe_group_t g, const void* expert_y, hipStream_t stream)
+{
+    if (!g)
+        return MOE_ERR_INVALID;
+    if (g->state != State::Received)
+        return MOE_ERR_STATE;
+    if (g->T > 0 && (!expert_y || !aligned16(expert_y)))
+        return MOE_ERR_INVALID;
+    int rc = check_device(g);
+    if (rc != MOE_OK)
+        return rc;
+    const moe::Shape sh = shape_of(g, g->T);
+    const moe::Rows rows = rows_of(g);
+    if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_PACK, stream,
+                           [&] { return moe::launch_combine_pack(sh, g->plan, rows, expert_y, stream); })) ||
+        (rc = timed_launch(g, MOE_KERNEL_TRANSFER_BACK, stream,
+                           [&] { return moe::launch_transfer_back(sh, g->plan, rows, stream); })))
+        return rc;
+    g->state = State::CombineSent;
+    return MOE_OK;
+}
+
+int moe_combine_recv(moe_group_t g, const float* topk_weights, void* out, hipStream_t stream)
+{
+    if (!g)
+        return MOE_ERR_INVALID;
+    if (g->state != State::CombineSent)
+        return MOE_ERR_STATE;
+    if (g->T > 0 && (!topk_weights || !out || !aligned16(topk_weights) || !aligned16(out)))
+        return MOE_ERR_INVALID;
+    int rc = check_device(g);
+    if (rc != MOE_OK)
+        return rc;
+    const moe::Shape sh = shape_of(g, g->T);
+    const moe::Rows rows = rows_of(g);
+    if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_REDUCE, stream, [&] {
+             return moe::launch_combine_reduce(sh, g->plan, rows, topk_weights, out, stream);
+         })))
+        return rc;
+    g->state = State::Idle;
+    return MOE_OK;
+}
+
+int moe_group_view_get(moe_group_t g, moe_group_view* v)
+{
+    if (!g || !v)
+        return MOE_ERR_INVALID;
+    std::memset(v, 0, sizeof(*v));
+    v->desc = g->desc;
+    v->num_tokens = g->T;
+    v->rows = (int64_t)g->desc.num_ranks * g->T * g->desc.top_k;
+    v->payload_row_bytes = g->payload_bytes;
+    v->combine_row_bytes = g->comb_bytes;
+    v->scale_blocks = g->scale_blocks;
+    v->cnt = g->plan.cnt;
+    v->pos = g->plan.pos;
+    v->send_off = g->plan.soff;
+    v->recv_off = g->plan.roff;
+    v->recv_base = g->plan.rbase;
+    v->expert_off = g->plan.eoff;
+    v->send_x = g->pool_send;
+    v->send_scale = g->send_scale;
+    v->send_meta = g->send_meta;
+    v->recv_x = g->pool_recv;
+    v->recv_scale = g->recv_scale;
+    v->recv_meta = g->recv_meta;
+    v->expert_src_rank = g->src_rank;
+    v->expert_src_slot = g->src_slot;
+    v->comb_send = g->pool_send;
+    v->comb_recv = g->pool_recv;
+    return MOE_OK;
+}
+
+int moe_group_status(moe_group_t g, hipStream_t stream)
+{
+    if (!g)
+        return MOE_ERR_INVALID;
+    int rc = check_device(g);
+    if (rc != MOE_OK)
+        return rc;
+    if (hipStreamSynchronize(stream) != hipSuccess)
+        return MOE_ERR_HIP;
+    int32_t word = 0;
+    if (hipMemcpy(&word, g->plan.err, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (word != 0 && hipMemset(g->plan.err, 0, sizeof(int32_t)) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (hipDeviceSynchronize() != hipSuccess)
+        return MOE_ERR_HIP;
+    if (word & moe::ERR_BIT_ROUTING)
+        return MOE_ERR_ROUTING;
+    if (word & moe::ERR_BIT_CAPACITY)
+        return MOE_ERR_CAPACITY;
+    return MOE_OK;
+}
+
+int moe_group_timing_enable(moe_group_t g, int enable)
+{
+    if (!g)
+        return MOE_ERR_INVALID;
+    g->timing = enable != 0;
+    g->events_used = 0;
+    return MOE_OK;
+}
+
+int moe_group_timing_read(moe_group_t g, double* total_ms, int64_t* launches)
+{
+    if (!g || !total_ms || !launches)
+        return MOE_ERR_INVALID;
+    for (int k = 0; k < MOE_KERNEL_COUNT; ++k) {
+        total_ms[k] = 0.0;
+        launches[k] = 0;
+    }
+    for (size_t i = 0; i < g->events_used; ++i) {
+        const EventPair& e = g->events[i];
+        if (hipEventSynchronize(e.stop) != hipSuccess)
+            return MOE_ERR_HIP;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess)
+            return MOE_ERR_HIP;
+        total_ms[e.kernel] += ms;
+        launches[e.kernel] += 1;
+    }
+    g->events_used = 0;
+    return MOE_OK;
+}
+
+}  // extern "C"

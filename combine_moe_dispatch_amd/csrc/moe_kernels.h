@@ -1,0 +1,67 @@
+// Internal launch interface between the host planner (moe_ep.hip) and the
+// device kernels (moe_kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Bits of the device-side error word.
+constexpr int32_t ERR_BIT_ROUTING = 1;
+constexpr int32_t ERR_BIT_CAPACITY = 2;
+
+// Limits the kernels are written for (checked by the host before launch).
+constexpr int MAX_EXPERTS = 1024;
+constexpr int MAX_RANKS = 1024;
+constexpr int MAX_TOPK = 64;
+
+struct Shape {
+    int N, E, K, L, H, T;
+    int fp8;              // payload is e4m3 + fp32 block scales
+    int64_t rows;         // N*T*K
+    int payload_vecs;     // 16-byte vectors per payload row (2H/16 or H/16)
+    int comb_vecs;        // 16-byte vectors per combine row (2H/16)
+    int scale_blocks;     // H/128 (fp8) or 0
+};
+
+struct Plan {              // device pointers owned by the group
+    int32_t* err;
+    int32_t* cnt;          // [N][E]
+    int32_t* pos;          // [N][T][K]
+    int32_t* soff;         // [N][E+1]
+    int32_t* roff;         // [N][N+1]
+    int32_t* rbase;        // [N+1]
+    int32_t* eoff;         // [E+1]
+    int32_t* ebase;        // [N][E]  first expert-order row of (sender s, expert e)
+    int32_t* xfer_src;     // [rows]  receive row q <- send row xfer_src[q]
+    int2* shuf_map;        // [rows]  expert row r <- (receive row, source rank)
+};
+
+struct Rows {              // pooled row buffers
+    void* send_x;          // payload, send layout
+    float* send_scale;
+    int32_t* send_meta;
+    void* recv_x;          // payload, receive layout
+    float* recv_scale;
+    int32_t* recv_meta;
+    int32_t* src_rank;     // expert-order metadata
+    int32_t* src_slot;
+    void* comb_send;       // combine rows, receive layout (aliases send_x storage)
+    void* comb_recv;       // combine rows, send layout (aliases recv_x storage)
+};
+
+hipError_t launch_route_count(const Shape& sh, const int32_t* idx, const Plan& p, hipStream_t st);
+hipError_t launch_offsets(const Shape& sh, const Plan& p, hipStream_t st);
+hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const Plan& p,
+                       const Rows& r, hipStream_t st);
+hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, hipStream_t st);
+hipError_t launch_shuffle(const Shape& sh, const Plan& p, const Rows& r, void* expert_x,
+                          float* expert_scale, int32_t* expert_offsets, hipStream_t st);
+hipError_t launch_combine_pack(const Shape& sh, const Plan& p, const Rows& r,
+                               const void* expert_y, hipStream_t st);
+hipError_t launch_transfer_back(const Shape& sh, const Plan& p, const Rows& r, hipStream_t st);
+hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, const float* w,
+                                 void* out, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,798 @@
+// HIP kernels of the MoE dispatch/combine path for CDNA4 (gfx950, wave64).
+//
+// Pages cited:
+//   [EPMC] "Efficient and portable Mixture-of-Experts communication"
+//   [EFA]  "Enabling trillion-parameter models on AWS EFA"
+//
+// Every step is a permutation copy, a small scan, a codec or a weighted sum:
+// nothing is a dense contraction, so there is no MFMA here and the kernels are
+// bound by HBM bandwidth.  Rows move as 16-byte vectors, one wavefront per row
+// (one 14 KiB DeepSeek-shaped row = 14 vectors per lane, all loads issued
+// before the stores), so each wave keeps a whole row in flight.  Row order is
+// driven by small int32 maps that the pack kernel writes from the offsets, so
+// the transfer, shuffle and combine kernels are pure gathers or scatters.
+//
+// Every kernel after the route count checks the device error word first and
+// writes nothing once an invalid expert id has been seen.
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+// Native clang vectors (not HIP's struct wrappers) so that a value can be an
+// inline-asm register operand.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+constexpr int ROWS_PER_BLOCK = 4;          // one wave per row, 256 threads
+constexpr int COPY_THREADS = WAVE * ROWS_PER_BLOCK;
+
+__device__ inline int lane_id() { return threadIdx.x & (WAVE - 1); }
+
+// Pins loaded values in registers: an empty asm that reads and rewrites each
+// vector.  Without it the compiler sinks every load into the predicated store
+// that uses it, and the row is copied one vector at a time with a full memory
+// wait in between; with it, all U loads of a lane are in flight together.
+template <int U>
+__device__ inline void hold(v4u (&v)[U])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        asm volatile("" : "+v"(v[u]));
+}
+
+__device__ inline int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+__device__ inline float readlane_f(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Exclusive scan of one int per thread over a block of NT threads.  Returns
+// the thread's exclusive prefix; *total gets the block sum.  Contains
+// barriers: every thread of the block must call it.
+template <int NT>
+__device__ int block_exclusive_scan(int v, int* wave_sums, int* total)
+{
+    const int lane = lane_id(), wave = threadIdx.x / WAVE;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+        const int t = __shfl_up(inc, d, WAVE);
+        if (lane >= d)
+            inc += t;
+    }
+    if (lane == WAVE - 1)
+        wave_sums[wave] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < NT / WAVE; ++w) {
+            const int c = wave_sums[w];
+            wave_sums[w] = run;
+            run += c;
+        }
+        wave_sums[NT / WAVE] = run;
+    }
+    __syncthreads();
+    const int excl = wave_sums[wave] + inc - v;
+    *total = wave_sums[NT / WAVE];
+    __syncthreads();
+    return excl;
+}
+
+// ---------------------------------------------------------------------------
+// Route count + stable positions: one workgroup per logical rank.
+//
+// [EFA] "Dispatch and combine": the token counts per expert are formed by
+// atomic adds in shared memory of a single block, then summed cumulatively to
+// get the offsets inside the contiguous send buffer.  LDS atomics give the
+// counts; the order inside an expert is made stable ((t,k) ascending) with a
+// per-chunk counting sort: inside a wave, lanes with equal expert ids find
+// their rank by ballot + popcount; across the block's waves a per-expert scan
+// of the wave counts plus a running per-expert cursor gives the position.
+// ---------------------------------------------------------------------------
+constexpr int RC_NT = 512;
+constexpr int RC_WAVES = RC_NT / WAVE;
+
+__global__ __launch_bounds__(RC_NT) void route_count_kernel(const int32_t* __restrict__ idx,
+                                                            int T, int K, int E,
+                                                            int32_t* __restrict__ cnt,
+                                                            int32_t* __restrict__ soff,
+                                                            int32_t* __restrict__ pos,
+                                                            int32_t* __restrict__ err)
+{
+    extern __shared__ int32_t lds[];
+    int32_t* hist = lds;          // [E]: counts, then the running cursor
+    int32_t* wcnt = lds + E;      // [RC_WAVES][E]: wave counts, then wave bases
+    __shared__ int32_t wave_sums[RC_WAVES + 1];
+
+    const int s = blockIdx.x;
+    const int items = T * K;
+    const int32_t* my_idx = idx + (size_t)s * items;
+    int32_t* my_pos = pos + (size_t)s * items;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+
+    for (int e = tid; e < E; e += RC_NT)
+        hist[e] = 0;
+    __syncthreads();
+    int bad = 0;
+    for (int i = tid; i < items; i += RC_NT) {
+        const int e = my_idx[i];
+        if ((unsigned)e < (unsigned)E)
+            atomicAdd(&hist[e], 1);
+        else
+            bad = 1;
+    }
+    if (bad)
+        atomicOr(err, ERR_BIT_ROUTING);
+    __syncthreads();
+
+    // counts out, exclusive scan over experts -> send offsets and cursor
+    const int per = (E + RC_NT - 1) / RC_NT;
+    const int e0 = tid * per;
+    int local = 0;
+    for (int j = 0; j < per; ++j) {
+        const int e = e0 + j;
+        if (e < E) {
+            const int c = hist[e];
+            cnt[(size_t)s * E + e] = c;
+            local += c;
+        }
+    }
+    int total;
+    int run = block_exclusive_scan<RC_NT>(local, wave_sums, &total);
+    for (int j = 0; j < per; ++j) {
+        const int e = e0 + j;
+        if (e < E) {
+            const int c = hist[e];
+            soff[(size_t)s * (E + 1) + e] = run;
+            hist[e] = run;
+            run += c;
+        }
+    }
+    if (tid == 0)
+        soff[(size_t)s * (E + 1) + E] = total;
+    __syncthreads();
+
+    const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
+    for (int c0 = 0; c0 < items; c0 += RC_NT) {
+        for (int j = tid; j < RC_WAVES * E; j += RC_NT)
+            wcnt[j] = 0;
+        __syncthreads();
+        const int i = c0 + tid;
+        const int e = (i < items) ? my_idx[i] : -1;
+        const bool valid = (unsigned)e < (unsigned)E;
+        uint64_t todo = __ballot(valid);
+        int rank = 0;
+        while (todo) {
+            const int leader = __ffsll((unsigned long long)todo) - 1;
+            const int v = __shfl(e, leader, WAVE);
+            const uint64_t same = __ballot(valid && e == v);
+            if (valid && e == v) {
+                rank = __popcll(same & lanes_below);
+                if (rank == 0)
+                    wcnt[wave * E + v] = __popcll(same);
+            }
+            todo &= ~same;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += RC_NT) {
+            int r = hist[ee];
+            for (int w = 0; w < RC_WAVES; ++w) {
+                const int c = wcnt[w * E + ee];
+                wcnt[w * E + ee] = r;
+                r += c;
+            }
+            hist[ee] = r;
+        }
+        __syncthreads();
+        if (i < items)
+            my_pos[i] = valid ? wcnt[wave * E + e] + rank : -1;
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Offsets after the count exchange: one workgroup.
+//
+// [EFA] "Send and receive buffers": once the per-expert counts are exchanged,
+// each rank derives where to write and the offsets it receives from; [EFA]
+// "Dispatch and combine": the offsets for dispatch and combine are computed
+// once, off the critical path.  Outputs: receive offsets per (receiver,
+// sender), pooled receive bases, expert offsets, and the first expert-order
+// row of every (sender, expert) run.  A receive count above N*T*max(K, L) (the
+// page's bound) raises the capacity bit.
+// ---------------------------------------------------------------------------
+constexpr int OF_NT = 1024;
+
+__global__ __launch_bounds__(OF_NT) void offsets_kernel(int N, int E, int L, int64_t cap,
+                                                        const int32_t* __restrict__ cnt,
+                                                        const int32_t* __restrict__ soff,
+                                                        int32_t* __restrict__ roff,
+                                                        int32_t* __restrict__ rbase,
+                                                        int32_t* __restrict__ eoff,
+                                                        int32_t* __restrict__ ebase,
+                                                        int32_t* __restrict__ err)
+{
+    __shared__ int32_t wave_sums[OF_NT / WAVE + 1];
+    const int tid = threadIdx.x;
+
+    int recvtot = 0;
+    if (tid < N) {
+        const int d = tid;
+        int run = 0;
+        for (int s = 0; s < N; ++s) {
+            roff[(size_t)d * (N + 1) + s] = run;
+            run += soff[(size_t)s * (E + 1) + (d + 1) * L] - soff[(size_t)s * (E + 1) + d * L];
+        }
+        roff[(size_t)d * (N + 1) + N] = run;
+        recvtot = run;
+        if ((int64_t)run > cap)
+            atomicOr(err, ERR_BIT_CAPACITY);
+    }
+    int total;
+    const int base = block_exclusive_scan<OF_NT>(recvtot, wave_sums, &total);
+    if (tid < N)
+        rbase[tid] = base;
+    if (tid == 0)
+        rbase[N] = total;
+
+    int ecnt = 0;
+    if (tid < E)
+        for (int s = 0; s < N; ++s)
+            ecnt += cnt[(size_t)s * E + tid];
+    const int eb = block_exclusive_scan<OF_NT>(ecnt, wave_sums, &total);
+    if (tid < E) {
+        eoff[tid] = eb;
+        int run = eb;
+        for (int s = 0; s < N; ++s) {
+            ebase[(size_t)s * E + tid] = run;
+            run += cnt[(size_t)s * E + tid];
+        }
+    }
+    if (tid == 0)
+        eoff[E] = total;
+}
+
+// ---------------------------------------------------------------------------
+// Pack: one wave per token.
+//
+// [EPMC] "Dispatch": activations, block scales and the token's index on the
+// sending rank are packed contiguously; [EFA] "Dispatch and combine": with the
+// offsets known, rows are packed into contiguous per-peer send buffers.  The
+// token row is read once and written K times (one per routed expert).  Lanes
+// k < K also record, for row (s, t, k), where the transfer and the receive
+// shuffle will move it:
+//   receive row q  = rbase[d] + roff[d][s] + pos - soff[s][d*L]   (d = e / L)
+//   expert row r   = ebase[s][e] + pos - soff[s][e]
+// ---------------------------------------------------------------------------
+__device__ inline void record_row(const Shape& sh, const Plan& p, int32_t* __restrict__ send_meta,
+                                  int s, int t, int k, int e, int pk)
+{
+    const int64_t TK = (int64_t)sh.T * sh.K;
+    const int32_t srow = (int32_t)(s * TK + pk);
+    send_meta[srow] = t * sh.K + k;
+    const int d = e / sh.L;
+    const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
+    const int32_t q = p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + pk - so[d * sh.L];
+    p.xfer_src[q] = srow;
+    const int32_t r = p.ebase[(size_t)s * sh.E + e] + pk - so[e];
+    p.shuf_map[r] = make_int2(q, s);
+}
+
+template <int U>
+__global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan p,
+                                                                 const v4u* __restrict__ x,
+                                                                 const int32_t* __restrict__ idx,
+                                                                 v4u* __restrict__ send_x,
+                                                                 int32_t* __restrict__ send_meta)
+{
+    if (*p.err)
+        return;
+    const int lane = lane_id();
+    const int64_t tok = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    if (tok >= (int64_t)sh.N * sh.T)
+        return;
+    const int s = (int)(tok / sh.T), t = (int)(tok % sh.T);
+    const int64_t TK = (int64_t)sh.T * sh.K;
+    int my_p = 0;
+    if (lane < sh.K) {
+        const int64_t i = tok * sh.K + lane;
+        my_p = p.pos[i];
+        record_row(sh, p, send_meta, s, t, lane, idx[i], my_p);
+    }
+    const int n = sh.payload_vecs;
+    const v4u* src = x + tok * n;
+    for (int base = 0; base < n; base += WAVE * U) {
+        v4u v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = src[min(base + u * WAVE + lane, n - 1)];
+        hold(v);
+        for (int k = 0; k < sh.K; ++k) {
+            const int pk = readlane(my_p, k);
+            v4u* dst = send_x + (s * TK + pk) * n;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = base + u * WAVE + lane;
+                if (j < n)
+                    dst[j] = v[u];
+            }
+        }
+    }
+}
+
+// OCP e4m3 encode, round to nearest even, saturating at +-448; NaN -> S.1111.111.
+// Normal results round the fp32 mantissa at bit 20 (ties to even) and rebias
+// the exponent from 127 to 7; below 2^-6 the result is |v|*2^9 rounded to an
+// integer (exact scaling, then round-half-even), which also covers rounding
+// up into the smallest normal.
+__device__ inline uint32_t e4m3_encode(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u)
+        return sign | 0x7Fu;
+    if (a >= 0x43E00000u)                      // |v| >= 448
+        return sign | 0x7Eu;
+    if (a < 0x3C800000u) {                     // |v| < 2^-6
+        const float m = __uint_as_float(a) * 512.0f;
+        return sign | (uint32_t)__builtin_rintf(m);
+    }
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    uint32_t c = (r >> 20) - (120u << 3);
+    if (c > 0x7Eu)
+        c = 0x7Eu;
+    return sign | c;
+}
+
+// [EFA] "Dispatch/combine latency": block-scaled fp8 dispatch; the blocks are
+// 128 elements with one fp32 scale each.  Per block: amax = max|x| (exact from
+// bf16), inv = 448/amax and scale = amax/448 as correctly rounded fp32
+// divisions (inv = 0, scale = 1 for an all-zero block), code = e4m3(x * inv).
+// A 128-element block is 16 lanes x 8 elements; amax is reduced over the
+// 16-lane group with xor shuffles.
+template <int U>
+__global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p,
+                                                                const v4u* __restrict__ x,
+                                                                const int32_t* __restrict__ idx,
+                                                                v2u* __restrict__ send_q,
+                                                                float* __restrict__ send_scale,
+                                                                int32_t* __restrict__ send_meta)
+{
+    if (*p.err)
+        return;
+    const int lane = lane_id();
+    const int64_t tok = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    if (tok >= (int64_t)sh.N * sh.T)
+        return;
+    const int s = (int)(tok / sh.T), t = (int)(tok % sh.T);
+    const int64_t TK = (int64_t)sh.T * sh.K;
+    int my_p = 0;
+    if (lane < sh.K) {
+        const int64_t i = tok * sh.K + lane;
+        my_p = p.pos[i];
+        record_row(sh, p, send_meta, s, t, lane, idx[i], my_p);
+    }
+    const int n = sh.H / 8;                    // input vectors of 8 bf16 per row
+    const int nb = sh.scale_blocks;
+    const v4u* src = x + tok * n;
+    for (int base = 0; base < n; base += WAVE * U) {
+        // clamped loads (see copy_row); a 16-lane group lies wholly inside or
+        // wholly past the row end because n and base are multiples of 16
+        v4u v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = src[min(base + u * WAVE + lane, n - 1)];
+        hold(v);
+        v2u q[U];
+        float sc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float f[8];
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[2 * i] = __uint_as_float(w[i] << 16);
+                f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                amax = fmaxf(amax, fabsf(f[i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 8, WAVE));
+            amax = fmaxf(amax, __shfl_xor(amax, 4, WAVE));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, WAVE));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
+            float inv = 0.0f, scale = 1.0f;
+            if (amax > 0.0f) {
+                inv = 448.0f / amax;
+                scale = amax / 448.0f;
+            }
+            uint32_t c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                c[i] = e4m3_encode(f[i] * inv);
+            q[u].x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+            q[u].y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+            sc[u] = scale;
+        }
+        for (int k = 0; k < sh.K; ++k) {
+            const int64_t row = s * TK + readlane(my_p, k);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = base + u * WAVE + lane;
+                if (j < n) {
+                    send_q[row * n + j] = q[u];
+                    if ((lane & 15) == 0)
+                        send_scale[row * nb + j / 16] = sc[u];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row movers.  One wave per destination (gather) or source (scatter) row.
+// ---------------------------------------------------------------------------
+// Loads use a clamped index instead of a predicate, so all U loads of a lane
+// are issued back to back before the first wait; lanes past the row end
+// re-read its last vector (same cache line) and skip the store.
+template <int U>
+__device__ inline void copy_row(v4u* __restrict__ dst, const v4u* __restrict__ src, int n, int lane)
+{
+    for (int base = 0; base < n; base += WAVE * U) {
+        v4u v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = src[min(base + u * WAVE + lane, n - 1)];
+        hold(v);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * WAVE + lane;
+            if (j < n)
+                dst[j] = v[u];
+        }
+    }
+}
+
+// Modelled transfer ([EFA] "Dispatch and combine": each peer's rows leave as
+// one contiguous write; here rank d's receive row q takes send row
+// xfer_src[q], so every (s -> d) segment is copied contiguously).  Moves the
+// payload, the block scales (e4m3) and the meta word.
+template <int U>
+__global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p,
+                                                                const v4u* __restrict__ send_x,
+                                                                v4u* __restrict__ recv_x,
+                                                                const float* __restrict__ send_scale,
+                                                                float* __restrict__ recv_scale,
+                                                                const int32_t* __restrict__ send_meta,
+                                                                int32_t* __restrict__ recv_meta)
+{
+    if (*p.err)
+        return;
+    const int lane = lane_id();
+    const int64_t q = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    if (q >= sh.rows)
+        return;
+    const int64_t srow = p.xfer_src[q];
+    if ((uint64_t)srow >= (uint64_t)sh.rows)
+        return;
+    const int n = sh.payload_vecs;
+    copy_row<U>(recv_x + q * n, send_x + srow * n, n, lane);
+    if (sh.fp8)
+        for (int j = lane; j < sh.scale_blocks; j += WAVE)
+            recv_scale[q * sh.scale_blocks + j] = send_scale[srow * sh.scale_blocks + j];
+    if (lane == 0)
+        recv_meta[q] = send_meta[srow];
+}
+
+// Receive shuffle ([EPMC] "Dispatch": received rows are copied into the
+// contiguous grouped-GEMM input and the source rank and token index are stored
+// for combine; [EFA] "Dispatch and combine": shuffle from the receive buffer
+// into the tensor handed to the grouped GEMM).  Expert row r takes receive row
+// shuf_map[r].x; block 0 also publishes the expert offsets.
+template <int U>
+__global__ __launch_bounds__(COPY_THREADS) void shuffle_kernel(Shape sh, Plan p,
+                                                               const v4u* __restrict__ recv_x,
+                                                               const float* __restrict__ recv_scale,
+                                                               const int32_t* __restrict__ recv_meta,
+                                                               v4u* __restrict__ expert_x,
+                                                               float* __restrict__ expert_scale,
+                                                               int32_t* __restrict__ src_rank,
+                                                               int32_t* __restrict__ src_slot,
+                                                               int32_t* __restrict__ expert_offsets)
+{
+    if (*p.err)
+        return;
+    if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e <= sh.E; e += COPY_THREADS)
+            expert_offsets[e] = p.eoff[e];
+    const int lane = lane_id();
+    const int64_t r = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    if (r >= sh.rows)
+        return;
+    const int2 m = p.shuf_map[r];
+    const int64_t q = m.x;
+    if ((uint64_t)q >= (uint64_t)sh.rows)
+        return;
+    const int n = sh.payload_vecs;
+    copy_row<U>(expert_x + r * n, recv_x + q * n, n, lane);
+    if (sh.fp8)
+        for (int j = lane; j < sh.scale_blocks; j += WAVE)
+            expert_scale[r * sh.scale_blocks + j] = recv_scale[q * sh.scale_blocks + j];
+    if (lane == 0) {
+        src_rank[r] = m.y;
+        src_slot[r] = recv_meta[q];
+    }
+}
+
+// Combine send ([EPMC] "Combine": the 16-bit expert outputs go back to the
+// slot each row came from; the inverse of the receive shuffle): expert row r
+// is scattered to receive-layout row shuf_map[r].x.
+template <int U>
+__global__ __launch_bounds__(COPY_THREADS) void combine_pack_kernel(Shape sh, Plan p,
+                                                                    const v4u* __restrict__ y,
+                                                                    v4u* __restrict__ comb_send)
+{
+    if (*p.err)
+        return;
+    const int lane = lane_id();
+    const int64_t r = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    if (r >= sh.rows)
+        return;
+    const int64_t q = p.shuf_map[r].x;
+    if ((uint64_t)q >= (uint64_t)sh.rows)
+        return;
+    const int n = sh.comb_vecs;
+    copy_row<U>(comb_send + q * n, y + r * n, n, lane);
+}
+
+// Combine transfer ([EFA] "Dispatch and combine": one write per peer back to
+// the token's rank): receive-layout row q returns to send row xfer_src[q].
+template <int U>
+__global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, Plan p,
+                                                                     const v4u* __restrict__ comb_send,
+                                                                     v4u* __restrict__ comb_recv)
+{
+    if (*p.err)
+        return;
+    const int lane = lane_id();
+    const int64_t q = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    if (q >= sh.rows)
+        return;
+    const int64_t srow = p.xfer_src[q];
+    if ((uint64_t)srow >= (uint64_t)sh.rows)
+        return;
+    const int n = sh.comb_vecs;
+    copy_row<U>(comb_recv + srow * n, comb_send + q * n, n, lane);
+}
+
+// bf16 pattern of an fp32 value, round to nearest even (NaN -> 0x7FC0).
+__device__ inline uint32_t bf16_bits(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ inline void fma_row8(float (&acc)[8], float w, const v4u& v)
+{
+    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __builtin_fmaf(w, __uint_as_float(x[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(w, __uint_as_float(x[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    }
+}
+
+__device__ inline v4u pack_bf16x8(const float (&acc)[8])
+{
+    v4u o;
+    o.x = bf16_bits(acc[0]) | (bf16_bits(acc[1]) << 16);
+    o.y = bf16_bits(acc[2]) | (bf16_bits(acc[3]) << 16);
+    o.z = bf16_bits(acc[4]) | (bf16_bits(acc[5]) << 16);
+    o.w = bf16_bits(acc[6]) | (bf16_bits(acc[7]) << 16);
+    return o;
+}
+
+// Combine receive: one wave per token ([EPMC] "Introduction": the weighted
+// sum of the K expert outputs; [EPMC] "Combine": computed by the receiver
+// into the caller's tensor; accumulation only here, on the receive side --
+// [EFA] "Dispatch/combine latency").  fp32, k ascending, one fma chain from +0,
+// then bf16 round-to-nearest-even.  With K known at compile time (KT > 0) the
+// K*U row loads of a chunk are all issued before the first fma.
+template <int KT, int U>
+__global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, Plan p,
+                                                                      const v4u* __restrict__ comb_recv,
+                                                                      const float* __restrict__ w,
+                                                                      v4u* __restrict__ out)
+{
+    if (*p.err)
+        return;
+    const int lane = lane_id();
+    const int64_t tok = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    if (tok >= (int64_t)sh.N * sh.T)
+        return;
+    const int K = KT > 0 ? KT : sh.K;
+    const int64_t s = tok / sh.T;
+    const int64_t TK = (int64_t)sh.T * sh.K;
+    int my_p = 0;
+    float my_w = 0.0f;
+    if (lane < K) {
+        my_p = p.pos[tok * K + lane];
+        my_w = w[tok * K + lane];
+    }
+    const int n = sh.comb_vecs;
+    const v4u* rows = comb_recv + s * TK * n;
+    v4u* dst = out + tok * n;
+    for (int base = 0; base < n; base += WAVE * U) {
+        float acc[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[u][i] = 0.0f;
+        if constexpr (KT > 0) {
+            v4u v[KT][U];
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                const v4u* row = rows + (int64_t)readlane(my_p, k) * n;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    v[k][u] = row[min(base + u * WAVE + lane, n - 1)];
+            }
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                const float wk = readlane_f(my_w, k);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    fma_row8(acc[u], wk, v[k][u]);
+            }
+        } else {
+            for (int k = 0; k < K; ++k) {
+                const v4u* row = rows + (int64_t)readlane(my_p, k) * n;
+                const float wk = readlane_f(my_w, k);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    fma_row8(acc[u], wk, row[min(base + u * WAVE + lane, n - 1)]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * WAVE + lane;
+            if (j < n)
+                dst[j] = pack_bf16x8(acc[u]);
+        }
+    }
+}
+
+inline unsigned row_blocks(int64_t rows)
+{
+    const int64_t b = (rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    return (unsigned)(b > 0 ? b : 1);
+}
+
+// Vectors per lane needed to hold a row of n 16-byte vectors, rounded up to
+// an instantiated unroll (rows longer than 16 vectors per lane loop).
+inline int unroll_for(int n)
+{
+    const int per_lane = (n + WAVE - 1) / WAVE;
+    if (per_lane <= 1) return 1;
+    if (per_lane <= 2) return 2;
+    if (per_lane <= 4) return 4;
+    if (per_lane <= 8) return 8;
+    return 16;
+}
+
+#define MOE_DISPATCH_U(u, KERNEL, ...)                                                   \
+    switch (u) {                                                                          \
+    case 1: hipLaunchKernelGGL((KERNEL<1>), __VA_ARGS__); break;                          \
+    case 2: hipLaunchKernelGGL((KERNEL<2>), __VA_ARGS__); break;                          \
+    case 4: hipLaunchKernelGGL((KERNEL<4>), __VA_ARGS__); break;                          \
+    case 8: hipLaunchKernelGGL((KERNEL<8>), __VA_ARGS__); break;                          \
+    default: hipLaunchKernelGGL((KERNEL<16>), __VA_ARGS__); break;                        \
+    }
+
+}  // namespace
+
+hipError_t launch_route_count(const Shape& sh, const int32_t* idx, const Plan& p, hipStream_t st)
+{
+    const size_t lds = (size_t)(RC_WAVES + 1) * sh.E * sizeof(int32_t);
+    hipLaunchKernelGGL(route_count_kernel, dim3(sh.N), dim3(RC_NT), lds, st, idx, sh.T, sh.K, sh.E,
+                       p.cnt, p.soff, p.pos, p.err);
+    return hipGetLastError();
+}
+
+hipError_t launch_offsets(const Shape& sh, const Plan& p, hipStream_t st)
+{
+    const int64_t cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
+    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(OF_NT), 0, st, sh.N, sh.E, sh.L, cap, p.cnt,
+                       p.soff, p.roff, p.rbase, p.eoff, p.ebase, p.err);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const Plan& p,
+                       const Rows& r, hipStream_t st)
+{
+    const int64_t tokens = (int64_t)sh.N * sh.T;
+    if (tokens == 0)
+        return hipSuccess;
+    const dim3 grid(row_blocks(tokens)), block(COPY_THREADS);
+    if (sh.fp8) {
+        int u = unroll_for(sh.H / 8);
+        if (u > 8) u = 8;
+        MOE_DISPATCH_U(u, pack_fp8_kernel, grid, block, 0, st, sh, p, (const v4u*)x, idx,
+                       (v2u*)r.send_x, r.send_scale, r.send_meta);
+    } else {
+        MOE_DISPATCH_U(unroll_for(sh.payload_vecs), pack_bf16_kernel, grid, block, 0, st, sh, p,
+                       (const v4u*)x, idx, (v4u*)r.send_x, r.send_meta);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, hipStream_t st)
+{
+    if (sh.rows == 0)
+        return hipSuccess;
+    MOE_DISPATCH_U(unroll_for(sh.payload_vecs), transfer_kernel, dim3(row_blocks(sh.rows)),
+                   dim3(COPY_THREADS), 0, st, sh, p, (const v4u*)r.send_x, (v4u*)r.recv_x,
+                   r.send_scale, r.recv_scale, r.send_meta, r.recv_meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_shuffle(const Shape& sh, const Plan& p, const Rows& r, void* expert_x,
+                          float* expert_scale, int32_t* expert_offsets, hipStream_t st)
+{
+    MOE_DISPATCH_U(unroll_for(sh.payload_vecs), shuffle_kernel, dim3(row_blocks(sh.rows)),
+                   dim3(COPY_THREADS), 0, st, sh, p, (const v4u*)r.recv_x, r.recv_scale,
+                   r.recv_meta, (v4u*)expert_x, expert_scale, r.src_rank, r.src_slot,
+                   expert_offsets);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_pack(const Shape& sh, const Plan& p, const Rows& r, const void* y,
+                               hipStream_t st)
+{
+    if (sh.rows == 0)
+        return hipSuccess;
+    MOE_DISPATCH_U(unroll_for(sh.comb_vecs), combine_pack_kernel, dim3(row_blocks(sh.rows)),
+                   dim3(COPY_THREADS), 0, st, sh, p, (const v4u*)y, (v4u*)r.comb_send);
+    return hipGetLastError();
+}
+
+hipError_t launch_transfer_back(const Shape& sh, const Plan& p, const Rows& r, hipStream_t st)
+{
+    if (sh.rows == 0)
+        return hipSuccess;
+    MOE_DISPATCH_U(unroll_for(sh.comb_vecs), transfer_back_kernel, dim3(row_blocks(sh.rows)),
+                   dim3(COPY_THREADS), 0, st, sh, p, (const v4u*)r.comb_send,
+                   (v4u*)r.comb_recv);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, const float* w,
+                                 void* out, hipStream_t st)
+{
+    const int64_t tokens = (int64_t)sh.N * sh.T;
+    if (tokens == 0)
+        return hipSuccess;
+    const dim3 grid(row_blocks(tokens)), block(COPY_THREADS);
+    const v4u* cr = (const v4u*)r.comb_recv;
+    v4u* o = (v4u*)out;
+    switch (sh.K) {
+    case 1: hipLaunchKernelGGL((combine_reduce_kernel<1, 4>), grid, block, 0, st, sh, p, cr, w, o); break;
+    case 2: hipLaunchKernelGGL((combine_reduce_kernel<2, 4>), grid, block, 0, st, sh, p, cr, w, o); break;
+    case 4: hipLaunchKernelGGL((combine_reduce_kernel<4, 2>), grid, block, 0, st, sh, p, cr, w, o); break;
+    case 6: hipLaunchKernelGGL((combine_reduce_kernel<6, 2>), grid, block, 0, st, sh, p, cr, w, o); break;
+    case 8: hipLaunchKernelGGL((combine_reduce_kernel<8, 2>), grid, block, 0, st, sh, p, cr, w, o); break;
+    default: hipLaunchKernelGGL((combine_reduce_kernel<0, 2>), grid, block, 0, st, sh, p, cr, w, o); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,203 @@
+/*
+ * moe_ep.h -- C ABI of the MoE expert-parallel dispatch/combine library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages the calls follow:
+ *   [EPMC] "Efficient and portable Mixture-of-Experts communication" (Perplexity)
+ *   [EFA]  "Enabling trillion-parameter models on AWS EFA" (Perplexity)
+ *
+ * The group.  An expert-parallel group of N ranks, each holding T tokens of H
+ * elements and routing every token to K of E experts; rank d owns experts
+ * [d*L, (d+1)*L), L = E/N ([EPMC] "Sharding and parallelism").  All N ranks
+ * are logical: their send and receive buffers live in the one GPU's memory and
+ * the network transfer is a device-local copy.  Dispatch and combine are each
+ * split into a send half and a receive half so other work can overlap the
+ * transfer ([EPMC] "Portable kernels"; [EFA] "MoE all-to-all over EFA").
+ *
+ * Conventions for every call below.
+ *  - Return value: MOE_OK (0) or a negative moe_status.  Calls never throw and
+ *    never abort the process.
+ *  - Pointers named as device pointers are device memory of the current HIP
+ *    device, 16-byte aligned (MOE_ERR_INVALID otherwise).  Tensors are dense,
+ *    row-major, with the shapes given; bf16 data is passed as raw 16-bit
+ *    patterns.
+ *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
+ *    the caller keeps inputs unchanged and outputs unread until the call's
+ *    work completes in stream order.  The halves may run on different streams
+ *    if the caller orders them with events.
+ *  - Order: create -> (dispatch_send -> dispatch_recv -> combine_send ->
+ *    combine_recv)* -> destroy.  A call out of this order returns
+ *    MOE_ERR_STATE and enqueues nothing; combine_recv ends the cycle, like the
+ *    pages' barrier that keeps a rank from starting the next dispatch while
+ *    peers still read ([EPMC] "Portable kernels").
+ *  - Routing errors (an expert id outside [0,E)) are found on the device; the
+ *    kernels then write none of the row buffers or outputs of that cycle, and
+ *    moe_group_status() reports MOE_ERR_ROUTING.
+ *  - One host thread at a time per group.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = -1,   /* bad argument: null/misaligned pointer, size out of range */
+    MOE_ERR_HIP = -2,       /* a HIP runtime call failed */
+    MOE_ERR_OOM = -3,       /* device allocation failed at create */
+    MOE_ERR_STATE = -4,     /* call out of the dispatch/combine order */
+    MOE_ERR_ROUTING = -5,   /* device saw an expert id outside [0, E) */
+    MOE_ERR_CAPACITY = -6   /* a receive count exceeded the page's bound (never expected) */
+} moe_status;
+
+typedef enum moe_dtype {
+    MOE_BF16 = 0,           /* dispatch payload: bf16 rows, 2H bytes */
+    MOE_FP8_E4M3 = 1        /* dispatch payload: OCP e4m3 rows (H bytes) + fp32 scale per 128 elements */
+} moe_dtype;
+
+/* Sizes fixed at creation ([EPMC] "Portable kernels": the maximum number of
+ * tokens a rank may dispatch is fixed for the group, and the buffers are
+ * reused by every layer).  Limits: 1 <= num_ranks <= 1024; num_experts a
+ * multiple of num_ranks, <= 1024; 1 <= top_k <= 64; hidden a multiple of 8
+ * (of 128 for MOE_FP8_E4M3), <= 65536; 0 <= max_tokens and
+ * num_ranks*max_tokens*top_k < 2^31. */
+typedef struct moe_group_desc {
+    int32_t num_ranks;      /* N */
+    int32_t num_experts;    /* E */
+    int32_t top_k;          /* K */
+    int32_t hidden;         /* H */
+    int32_t max_tokens;     /* T_max per rank */
+    int32_t dispatch_dtype; /* moe_dtype */
+} moe_group_desc;
+
+typedef struct moe_group_s* moe_group_t;
+
+/* Create a group: validates `desc`, allocates every internal buffer on the
+ * current HIP device (two pooled row buffers of N*T_max*K rows of
+ * max(payload, 2H) bytes, used by dispatch and again by combine, as the pages
+ * reuse them between the two -- [EFA] "Dispatch and combine" -- plus counts,
+ * offsets and metadata).  On success *out owns them.  Errors: MOE_ERR_INVALID,
+ * MOE_ERR_OOM, MOE_ERR_HIP; *out is untouched on error. */
+int moe_group_create(const moe_group_desc* desc, moe_group_t* out);
+
+/* Synchronise the device, free every buffer of the group and the handle.
+ * NULL is accepted and ignored. */
+int moe_group_destroy(moe_group_t g);
+
+/* Dispatch, send half ([EFA] "Dispatch and combine": per-expert counts by
+ * atomic adds in one block, a cumulative sum for the offsets, rows packed into
+ * contiguous per-peer send buffers, then one write per peer; [EPMC] "Dispatch":
+ * activations, block scales and the token's index packed together).
+ *   num_tokens  T, 0 <= T <= max_tokens (same T on every logical rank)
+ *   x           device, bf16 [N][T][H]
+ *   topk_idx    device, int32 [N][T][K], expert ids in [0, E)
+ * Enqueues: route count + stable positions, offsets, pack (+ e4m3 encode),
+ * transfer into the receive buffers.  Reads x and topk_idx only. */
+int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x,
+                      const int32_t* topk_idx, hipStream_t stream);
+
+/* Dispatch, receive half ([EPMC] "Dispatch": received tokens are copied into
+ * contiguous buffers for the grouped GEMM and the source rank, expert and
+ * token index are stored for combine; [EFA] "Dispatch and combine": shuffle
+ * from the receive buffer into the grouped-GEMM tensor).
+ *   expert_x        device, [N*T*K] rows: bf16 [..][H] or e4m3 bytes [..][H];
+ *                   rows sorted by (expert, source rank, token, k)
+ *   expert_scale    device, fp32 [N*T*K][H/128] for MOE_FP8_E4M3, else NULL
+ *   expert_offsets  device, int32 [E+1]: expert e's rows are
+ *                   [expert_offsets[e], expert_offsets[e+1]); rank d's GEMM
+ *                   input is rows [expert_offsets[d*L], expert_offsets[(d+1)*L])
+ * The back-routing metadata stays in the group. */
+int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale,
+                      int32_t* expert_offsets, hipStream_t stream);
+
+/* Combine, send half ([EPMC] "Combine": unquantised 16-bit expert outputs are
+ * sent back, each to the rank and token slot it came from; [EFA] "Dispatch and
+ * combine": routing is already known, rows go one write per peer).
+ *   expert_y  device, bf16 [N*T*K][H], rows in the order of expert_x
+ * Enqueues: inverse shuffle into the per-peer layout, transfer back. */
+int moe_combine_send(moe_group_t g, const void* expert_y, hipStream_t stream);
+
+/* Combine, receive half ([EPMC] "Introduction": the output is the sum of the
+ * K expert outputs weighted by the router; [EPMC] "Combine": the receiver
+ * computes it locally into an externally allocated tensor).
+ *   topk_weights  device, fp32 [N][T][K]
+ *   out           device, bf16 [N][T][H]
+ * out[s][t][h] = bf16_rne(acc) with acc = +0 and, for k = 0..K-1 in order,
+ * acc = fma(w[s][t][k], y_k[h], acc) in fp32, y_k the expert output of
+ * (s,t,k). */
+int moe_combine_recv(moe_group_t g, const float* topk_weights, void* out,
+                     hipStream_t stream);
+
+/* Device pointers of the group's internal buffers, for checking only.  The
+ * pooled send buffer holds send_x during dispatch and comb_send during
+ * combine; the pooled receive buffer holds recv_x, then comb_recv.  Layouts:
+ * send rows of sender s are rows [s*T*K, (s+1)*T*K); receive rows of rank d
+ * are rows [recv_base[d], recv_base[d+1]). */
+typedef struct moe_group_view {
+    moe_group_desc desc;
+    int32_t num_tokens;          /* T of the current cycle */
+    int64_t rows;                /* N*T*K */
+    int64_t payload_row_bytes;   /* 2H (bf16) or H (e4m3) */
+    int64_t combine_row_bytes;   /* 2H */
+    int32_t scale_blocks;        /* H/128 for e4m3, else 0 */
+    int32_t* cnt;                /* [N][E]     tokens of sender s for expert e */
+    int32_t* pos;                /* [N][T][K]  row of (t,k) in its sender's rows */
+    int32_t* send_off;           /* [N][E+1]   first row of expert e in sender s's rows */
+    int32_t* recv_off;           /* [N][N+1]   first row from sender s in receiver d's rows */
+    int32_t* recv_base;          /* [N+1]      first pooled receive row of rank d */
+    int32_t* expert_off;         /* [E+1]      first expert-order row of expert e */
+    void* send_x;                /* [rows][payload_row_bytes] */
+    float* send_scale;           /* [rows][scale_blocks] or NULL */
+    int32_t* send_meta;          /* [rows] t*K+k */
+    void* recv_x;
+    float* recv_scale;
+    int32_t* recv_meta;
+    int32_t* expert_src_rank;    /* [rows] source rank of each expert-order row */
+    int32_t* expert_src_slot;    /* [rows] t*K+k on the source rank */
+    void* comb_send;             /* [rows][combine_row_bytes], receive layout */
+    void* comb_recv;             /* [rows][combine_row_bytes], send layout */
+} moe_group_view;
+
+int moe_group_view_get(moe_group_t g, moe_group_view* out);
+
+/* Synchronise `stream`, then return and clear the device-side error word:
+ * MOE_OK, MOE_ERR_ROUTING or MOE_ERR_CAPACITY. */
+int moe_group_status(moe_group_t g, hipStream_t stream);
+
+/* Per-kernel timing with HIP events recorded on the launch stream around each
+ * kernel, for measurement.  While enabled, every launch is bracketed; reading
+ * synchronises on the recorded events, returns the summed milliseconds and
+ * launch counts per kernel (arrays of MOE_KERNEL_COUNT) and resets them. */
+typedef enum moe_kernel_id {
+    MOE_KERNEL_ROUTE_COUNT = 0,
+    MOE_KERNEL_OFFSETS = 1,
+    MOE_KERNEL_PACK = 2,
+    MOE_KERNEL_TRANSFER = 3,
+    MOE_KERNEL_SHUFFLE = 4,
+    MOE_KERNEL_COMBINE_PACK = 5,
+    MOE_KERNEL_TRANSFER_BACK = 6,
+    MOE_KERNEL_COMBINE_REDUCE = 7,
+    MOE_KERNEL_COUNT = 8
+} moe_kernel_id;
+
+int moe_group_timing_enable(moe_group_t g, int enable);
+int moe_group_timing_read(moe_group_t g, double* total_ms, int64_t* launches);
+
+/* Static description of a status code; never NULL. */
+const char* moe_strerror(int status);
+
+/* Name of a kernel id (as listed in profiler traces); "" if out of range. */
+const char* moe_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

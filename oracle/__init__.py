@@ -77,6 +77,8 @@ def _declare(L):
     L.orc_combine_recv_f64.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P]
     L.orc_combine_token.argtypes = [_I, _I, _P, _P, _P]
     L.orc_f32_to_bf16_n.argtypes = [_Z, _P, _P]
+    L.orc_send_meta.argtypes = [_I, _I, _I, _P, _P]
+    L.orc_expert_rows.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
     L.orc_f32_to_e4m3_n.argtypes = [_Z, _P, _P]
 
 
@@ -177,6 +179,26 @@ def plan(idx: np.ndarray, E: int) -> dict:
     roff, G = recv_offsets(soff, N)
     eoff = expert_offsets(cnt)
     return {"cnt": cnt, "soff": soff, "pos": pos, "roff": roff, "G": G, "eoff": eoff}
+
+
+def send_meta(pos: np.ndarray) -> np.ndarray:
+    """Meta word (t*K+k) of every send row, without moving any payload."""
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    N, T, K = pos.shape
+    meta = np.zeros(N * T * K, dtype=np.int32)
+    lib().orc_send_meta(N, T, K, _p(pos), _p(meta))
+    return meta
+
+
+def expert_rows(idx: np.ndarray, pl: dict) -> np.ndarray:
+    """Expert-order row of every (s,t,k), int32 [N][T][K]."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    N, T, K = idx.shape
+    E = pl["cnt"].shape[1]
+    rows = np.zeros((N, T, K), dtype=np.int32)
+    lib().orc_expert_rows(N, T, K, E, _p(idx), _p(pl["cnt"]), _p(pl["soff"]), _p(pl["pos"]),
+                          _p(pl["eoff"]), _p(rows))
+    return rows
 
 
 def pack_bf16(x: np.ndarray, pos: np.ndarray):

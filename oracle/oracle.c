@@ -504,3 +504,34 @@ void orc_f32_to_e4m3_n(size_t n, const float* in, uint8_t* out)
     for (size_t i = 0; i < n; ++i)
         out[i] = orc_f32_to_e4m3(in[i]);
 }
+
+/* ---------------------------------------- per-row definitions for sampling */
+
+/* The meta word of every send row (the index part of the pack step, without
+ * the payload): send_meta[s*T*K + pos[s][t][k]] = t*K+k. */
+void orc_send_meta(int N, int T, int K, const int32_t* pos, int32_t* send_meta)
+{
+    size_t TK = (size_t)T * K;
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t)
+            for (int k = 0; k < K; ++k)
+                send_meta[(size_t)s * TK + pos[((size_t)s * T + t) * K + k]] = t * K + k;
+}
+
+/* The expert-order row that (s,t,k) lands in (the shuffle's destination):
+ * expert e = idx[s][t][k] starts at eoff[e]; the rows of e from senders
+ * s' < s come first; then s's own rows of e in its send order. */
+void orc_expert_rows(int N, int T, int K, int E, const int32_t* idx, const int32_t* cnt,
+                     const int32_t* soff, const int32_t* pos, const int32_t* eoff, int32_t* rows)
+{
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t)
+            for (int k = 0; k < K; ++k) {
+                size_t i = ((size_t)s * T + t) * K + k;
+                int e = idx[i];
+                int32_t before = 0;
+                for (int s2 = 0; s2 < s; ++s2)
+                    before += cnt[(size_t)s2 * E + e];
+                rows[i] = eoff[e] + before + pos[i] - soff[(size_t)s * (E + 1) + e];
+            }
+}

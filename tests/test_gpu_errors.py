@@ -1,0 +1,98 @@
+"""Error behaviour through the C ABI on the GPU: a routing error found on the
+device writes none of the cycle's outputs and is reported by the status call;
+out-of-order calls and bad arguments are rejected on the host and enqueue
+nothing."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import run_cycle, say, to_dev
+from workloads import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import combine_moe_dispatch_amd as mep  # noqa: E402
+
+
+def test_routing_error_writes_nothing_and_is_reported():
+    cfg = CONFIGS["A"]
+    say(f"[gpu] routing error {cfg.describe()}")
+    inp = make_inputs(cfg)
+    bad = inp["idx"].copy()
+    bad[1, 3, 1] = cfg.E          # one id out of range
+    bad[0, 0, 0] = -1
+    g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16)
+    try:
+        R = cfg.rows
+        x, idx, w = to_dev(torch, inp["x"]), to_dev(torch, bad), to_dev(torch, inp["w"])
+        expert_x = torch.full((R * cfg.H,), -1, dtype=torch.int16, device="cuda")
+        offs = torch.full((cfg.E + 1,), -7, dtype=torch.int32, device="cuda")
+        y = torch.zeros((R, cfg.H), dtype=torch.bfloat16, device="cuda")
+        out = torch.full((cfg.N, cfg.T, cfg.H), -1, dtype=torch.int16, device="cuda")
+        mep.moe_dispatch_send(g, cfg.T, x, idx)
+        mep.moe_dispatch_recv(g, expert_x, None, offs)
+        mep.moe_combine_send(g, y)
+        mep.moe_combine_recv(g, w, out)
+        assert mep.moe_group_status(g) == mep.MOE_ERR_ROUTING
+        assert mep.moe_group_status(g) == mep.MOE_OK          # reading clears it
+        assert torch.all(expert_x == -1).item()
+        assert torch.all(offs == -7).item()
+        assert torch.all(out == -1).item()
+        # the group is usable again with valid routing
+        from tests.test_gpu_parity import _compare_all
+        _compare_all(cfg, inp, run_cycle(torch, mep, cfg, inp, group=g))
+    finally:
+        mep.moe_group_destroy(g)
+
+
+def test_call_order_and_arguments():
+    cfg = CONFIGS["A"]
+    say(f"[gpu] call order {cfg.describe()}")
+    inp = make_inputs(cfg)
+    g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16)
+    try:
+        R = cfg.rows
+        x, idx, w = to_dev(torch, inp["x"]), to_dev(torch, inp["idx"]), to_dev(torch, inp["w"])
+        expert_x = torch.empty((R, cfg.H), dtype=torch.bfloat16, device="cuda")
+        offs = torch.empty((cfg.E + 1,), dtype=torch.int32, device="cuda")
+        out = torch.empty((cfg.N, cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+
+        def status_of(fn, *a):
+            try:
+                fn(*a)
+                return mep.MOE_OK
+            except mep.MoeError as e:
+                return e.status
+
+        assert status_of(mep.moe_dispatch_recv, g, expert_x, None, offs) == mep.MOE_ERR_STATE
+        assert status_of(mep.moe_combine_send, g, expert_x) == mep.MOE_ERR_STATE
+        assert status_of(mep.moe_combine_recv, g, w, out) == mep.MOE_ERR_STATE
+        assert status_of(mep.moe_dispatch_send, g, cfg.T + 1, x, idx) == mep.MOE_ERR_INVALID
+        assert status_of(mep.moe_dispatch_send, g, -1, x, idx) == mep.MOE_ERR_INVALID
+        assert status_of(mep.moe_dispatch_send, g, cfg.T, x.data_ptr() + 2, idx) == mep.MOE_ERR_INVALID
+        assert status_of(mep.moe_dispatch_send, g, cfg.T, None, idx) == mep.MOE_ERR_INVALID
+        mep.moe_dispatch_send(g, cfg.T, x, idx)
+        assert status_of(mep.moe_dispatch_send, g, cfg.T, x, idx) == mep.MOE_ERR_STATE
+        # bf16 groups take no scale pointer
+        assert status_of(mep.moe_dispatch_recv, g, expert_x, offs, offs) == mep.MOE_ERR_INVALID
+        mep.moe_dispatch_recv(g, expert_x, None, offs)
+        assert status_of(mep.moe_dispatch_recv, g, expert_x, None, offs) == mep.MOE_ERR_STATE
+        mep.moe_combine_send(g, expert_x)
+        mep.moe_combine_recv(g, w, out)
+        torch.cuda.synchronize()
+        assert mep.moe_group_status(g) == mep.MOE_OK
+    finally:
+        mep.moe_group_destroy(g)
+
+
+def test_create_rejects_bad_descriptors():
+    say("[gpu] create descriptors")
+    for args in [(2, 7, 2, 256, 16, 0), (0, 8, 2, 256, 16, 0), (2, 8, 0, 256, 16, 0),
+                 (2, 8, 2, 100, 16, 0), (2, 8, 2, 256, 16, 1 + 5), (2, 8, 2, 264, 16, 1),
+                 (2, 2048, 2, 256, 16, 0), (2, 8, 2, 256, -1, 0)]:
+        with pytest.raises(mep.MoeError) as ei:
+            mep.moe_group_create(*args)
+        assert ei.value.status == mep.MOE_ERR_INVALID, args

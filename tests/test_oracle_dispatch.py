@@ -64,6 +64,10 @@ def _check_against_brute(idx, E, H=4):
     for r, (s, t, k) in enumerate(b["expert_rows"]):
         assert d["expert_x"][r, 0] == s and d["expert_x"][r, 1] == t
         assert d["expert_src_rank"][r] == s and d["expert_src_slot"][r] == t * K + k
+    rows = oracle.expert_rows(idx, pl)
+    for r, (s, t, k) in enumerate(b["expert_rows"]):
+        assert rows[s, t, k] == r
+    assert np.array_equal(oracle.send_meta(pl["pos"]), d["send_meta"])
     return pl
 
 
