@@ -43,8 +43,11 @@ def kernel_bytes(cfg) -> dict:
     hy = 2 * H                                   # combine row
     tokens = N * T
     return {
-        "route_count": R * 4 + N * E * 4 + N * (E + 1) * 4 + R * 4,
-        "offsets": N * E * 4 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4 + (E + 1) * 4 + N * E * 4,
+        # idx in; counts, send offsets, positions out; then the group offsets
+        # (counts and send offsets in; receive/expert offsets and bases out)
+        "route_plan": (R * 4 + N * E * 4 + N * (E + 1) * 4 + R * 4
+                       + N * E * 4 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4
+                       + (E + 1) * 4 + N * E * 4),
         "pack": tokens * H * 2 + R * 4 * 2 + R * (hb + sb + 4),
         "transfer": 2 * R * (hb + sb + 4),
         "shuffle": R * (hb + sb + 4) + R * (hb + sb + 8) + (E + 1) * 4,

@@ -23,12 +23,13 @@ MOE_ERR_OOM = -3
 MOE_ERR_STATE = -4
 MOE_ERR_ROUTING = -5
 MOE_ERR_CAPACITY = -6
+MOE_ERR_INTERNAL = -7
 
 MOE_BF16 = 0
 MOE_FP8_E4M3 = 1
 
-KERNELS = ["route_count", "offsets", "pack", "transfer", "shuffle", "combine_pack",
-           "transfer_back", "combine_reduce"]
+KERNELS = ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
+           "combine_reduce"]
 MOE_KERNEL_COUNT = len(KERNELS)
 
 

@@ -69,8 +69,8 @@ struct moe_group_s {
 namespace {
 
 const char* const kKernelNames[MOE_KERNEL_COUNT] = {
-    "route_count_kernel", "offsets_kernel",       "pack_kernel",          "transfer_kernel",
-    "shuffle_kernel",     "combine_pack_kernel",  "transfer_back_kernel", "combine_reduce_kernel",
+    "route_plan_kernel",   "pack_kernel",          "transfer_kernel",       "shuffle_kernel",
+    "combine_pack_kernel", "transfer_back_kernel", "combine_reduce_kernel",
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -209,6 +209,7 @@ const char* moe_strerror(int status)
     case MOE_ERR_STATE: return "call out of the dispatch/combine order";
     case MOE_ERR_ROUTING: return "expert id outside [0, num_experts)";
     case MOE_ERR_CAPACITY: return "receive count above the group's bound";
+    case MOE_ERR_INTERNAL: return "device-side index check failed";
     default: return "unknown status";
     }
 }
@@ -249,7 +250,8 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
     moe::Plan& p = g->plan;
     uint8_t* pool_send = nullptr;
     uint8_t* pool_recv = nullptr;
-    if ((rc = alloc(g, &p.err, 1)) || (rc = alloc(g, &p.cnt, (size_t)N * E)) ||
+    if ((rc = alloc(g, &p.err, 1)) || (rc = alloc(g, &p.ticket, 1)) ||
+        (rc = alloc(g, &p.cnt, (size_t)N * E)) ||
         (rc = alloc(g, &p.pos, (size_t)N * T * K)) || (rc = alloc(g, &p.soff, (size_t)N * (E + 1))) ||
         (rc = alloc(g, &p.roff, (size_t)N * (N + 1))) || (rc = alloc(g, &p.rbase, (size_t)N + 1)) ||
         (rc = alloc(g, &p.eoff, (size_t)E + 1)) || (rc = alloc(g, &p.ebase, (size_t)N * E)) ||
@@ -265,8 +267,10 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
     }
     g->pool_send = pool_send;
     g->pool_recv = pool_recv;
-    // the error word starts clear; the offsets start valid for an empty cycle
+    // the error word and the ticket counter start at zero; the offsets start
+    // valid for an empty cycle
     if (hipMemset(p.err, 0, sizeof(int32_t)) != hipSuccess ||
+        hipMemset(p.ticket, 0, sizeof(int32_t)) != hipSuccess ||
         hipMemset(p.eoff, 0, sizeof(int32_t) * (E + 1)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         free_all(g);
@@ -305,10 +309,8 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const in
         return rc;
     const moe::Shape sh = shape_of(g, num_tokens);
     const moe::Rows rows = rows_of(g);
-    if ((rc = timed_launch(g, MOE_KERNEL_ROUTE_COUNT, stream,
-                           [&] { return moe::launch_route_count(sh, topk_idx, g->plan, stream); })) ||
-        (rc = timed_launch(g, MOE_KERNEL_OFFSETS, stream,
-                           [&] { return moe::launch_offsets(sh, g->plan, stream); })) ||
+    if ((rc = timed_launch(g, MOE_KERNEL_ROUTE_PLAN, stream,
+                           [&] { return moe::launch_route_plan(sh, topk_idx, g->plan, stream); })) ||
         (rc = timed_launch(g, MOE_KERNEL_PACK, stream,
                            [&] { return moe::launch_pack(sh, x, topk_idx, g->plan, rows, stream); })) ||
         (rc = timed_launch(g, MOE_KERNEL_TRANSFER, stream,
@@ -443,6 +445,8 @@ int moe_group_status(moe_group_t g, hipStream_t stream)
         return MOE_ERR_ROUTING;
     if (word & moe::ERR_BIT_CAPACITY)
         return MOE_ERR_CAPACITY;
+    if (word & moe::ERR_BIT_INTERNAL)
+        return MOE_ERR_INTERNAL;
     return MOE_OK;
 }
 

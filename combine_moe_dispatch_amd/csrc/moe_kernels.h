@@ -10,6 +10,7 @@ namespace moe {
 // Bits of the device-side error word.
 constexpr int32_t ERR_BIT_ROUTING = 1;
 constexpr int32_t ERR_BIT_CAPACITY = 2;
+constexpr int32_t ERR_BIT_INTERNAL = 4;   // a device-side index check failed
 
 // Limits the kernels are written for (checked by the host before launch).
 constexpr int MAX_EXPERTS = 1024;
@@ -27,6 +28,7 @@ struct Shape {
 
 struct Plan {              // device pointers owned by the group
     int32_t* err;
+    int32_t* ticket;       // arrival counter of the route-plan workgroups (0 between launches)
     int32_t* cnt;          // [N][E]
     int32_t* pos;          // [N][T][K]
     int32_t* soff;         // [N][E+1]
@@ -51,8 +53,7 @@ struct Rows {              // pooled row buffers
     void* comb_recv;       // combine rows, send layout (aliases recv_x storage)
 };
 
-hipError_t launch_route_count(const Shape& sh, const int32_t* idx, const Plan& p, hipStream_t st);
-hipError_t launch_offsets(const Shape& sh, const Plan& p, hipStream_t st);
+hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, hipStream_t st);
 hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const Plan& p,
                        const Rows& r, hipStream_t st);
 hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, hipStream_t st);

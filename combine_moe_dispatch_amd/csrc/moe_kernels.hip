@@ -42,6 +42,13 @@ __device__ inline void hold(v4u (&v)[U])
         asm volatile("" : "+v"(v[u]));
 }
 
+// Streaming access: every row is read once and written once per stage, so row
+// loads and stores carry the nontemporal hint and do not displace the small
+// tables (maps, offsets) from the caches.
+__device__ inline v4u ld_nt(const v4u* p) { return __builtin_nontemporal_load(p); }
+__device__ inline void st_nt(const v4u& v, v4u* p) { __builtin_nontemporal_store(v, p); }
+__device__ inline void st_nt(const v2u& v, v2u* p) { __builtin_nontemporal_store(v, p); }
+
 __device__ inline int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
 __device__ inline float readlane_f(float v, int lane)
@@ -83,42 +90,171 @@ __device__ int block_exclusive_scan(int v, int* wave_sums, int* total)
 }
 
 // ---------------------------------------------------------------------------
-// Route count + stable positions: one workgroup per logical rank.
+// Route plan: one workgroup per logical rank; the last workgroup to finish
+// also computes the offsets of the whole group.
 //
-// [EFA] "Dispatch and combine": the token counts per expert are formed by
-// atomic adds in shared memory of a single block, then summed cumulatively to
-// get the offsets inside the contiguous send buffer.  LDS atomics give the
+// Counts ([EFA] "Dispatch and combine": the token counts per expert are formed
+// by atomic adds in shared memory of a single block, then summed cumulatively
+// to get the offsets inside the contiguous send buffer).  LDS atomics give the
 // counts; the order inside an expert is made stable ((t,k) ascending) with a
 // per-chunk counting sort: inside a wave, lanes with equal expert ids find
 // their rank by ballot + popcount; across the block's waves a per-expert scan
 // of the wave counts plus a running per-expert cursor gives the position.
+//
+// Offsets ([EFA] "Send and receive buffers": once the per-expert counts are
+// exchanged, each rank derives where to write and the offsets it receives
+// from; [EFA] "Dispatch and combine": they are computed once for dispatch and
+// combine, off the critical path).  Each workgroup publishes its counts, then
+// draws a ticket from a device-wide counter (agent-scope release fence before,
+// acquire fence after); the one that draws the last ticket has every rank's
+// counts in view and computes the receive offsets per (receiver, sender), the
+// pooled receive bases, the expert offsets and the first expert-order row of
+// every (sender, expert) run, then resets the counter for the next launch.
+// A receive count above N*T*max(K, L) (the page's bound) raises the capacity
+// bit.  The loops over ranks run on one workgroup, so they issue BATCH
+// independent loads before the first use instead of one latency per rank.
 // ---------------------------------------------------------------------------
-constexpr int RC_NT = 512;
-constexpr int RC_WAVES = RC_NT / WAVE;
+constexpr int RP_NT = 512;
+constexpr int RP_WAVES = RP_NT / WAVE;
+constexpr int BATCH = 32;
+constexpr int HELD_CHUNKS = 8;      // idx chunks kept in registers between the two passes
 
-__global__ __launch_bounds__(RC_NT) void route_count_kernel(const int32_t* __restrict__ idx,
-                                                            int T, int K, int E,
-                                                            int32_t* __restrict__ cnt,
-                                                            int32_t* __restrict__ soff,
-                                                            int32_t* __restrict__ pos,
-                                                            int32_t* __restrict__ err)
+// In-place exclusive scan of n <= 2*RP_NT ints held in LDS; returns the total.
+__device__ int block_scan_lds(int32_t* a, int n, int* wave_sums)
 {
-    extern __shared__ int32_t lds[];
-    int32_t* hist = lds;          // [E]: counts, then the running cursor
-    int32_t* wcnt = lds + E;      // [RC_WAVES][E]: wave counts, then wave bases
-    __shared__ int32_t wave_sums[RC_WAVES + 1];
+    const int per = (n + RP_NT - 1) / RP_NT;
+    const int i0 = threadIdx.x * per;
+    int local = 0;
+    for (int j = 0; j < per; ++j)
+        if (i0 + j < n)
+            local += a[i0 + j];
+    int total;
+    int run = block_exclusive_scan<RP_NT>(local, wave_sums, &total);
+    for (int j = 0; j < per; ++j)
+        if (i0 + j < n) {
+            const int c = a[i0 + j];
+            a[i0 + j] = run;
+            run += c;
+        }
+    __syncthreads();
+    return total;
+}
+
+struct RouteArgs {
+    const int32_t* idx;
+    int N, T, K, E, L;
+    int chunk_waves;        // RP_WAVES, or fewer for large E (LDS budget)
+    int64_t cap;
+};
+
+__device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* lds_recv,
+                              int32_t* lds_exp, int* wave_sums)
+{
+    const int N = ra.N, E = ra.E, L = ra.L, tid = threadIdx.x;
+    const int32_t* __restrict__ soff = p.soff;
+    const int32_t* __restrict__ cnt = p.cnt;
+    for (int d = tid; d < N; d += RP_NT) {
+        int run = 0;
+        for (int s0 = 0; s0 < N; s0 += BATCH) {
+            int lo[BATCH], hi[BATCH];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) {
+                const size_t row = (size_t)min(s0 + b, N - 1) * (E + 1);
+                lo[b] = soff[row + d * L];
+                hi[b] = soff[row + (d + 1) * L];
+            }
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+                if (s0 + b < N) {
+                    p.roff[(size_t)d * (N + 1) + s0 + b] = run;
+                    run += hi[b] - lo[b];
+                }
+        }
+        p.roff[(size_t)d * (N + 1) + N] = run;
+        lds_recv[d] = run;
+        if ((int64_t)run > ra.cap)
+            atomicOr(p.err, ERR_BIT_CAPACITY);
+    }
+    // expert totals; with N <= BATCH the counts stay in registers for the
+    // per-sender bases below (e < RP_NT covers every expert of one pass when
+    // E <= RP_NT; larger E reloads)
+    int held[BATCH];
+    for (int e = tid; e < E; e += RP_NT) {
+        int sum = 0;
+        for (int s0 = 0; s0 < N; s0 += BATCH) {
+            int c[BATCH];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+                c[b] = cnt[(size_t)min(s0 + b, N - 1) * E + e];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) {
+                if (s0 + b < N)
+                    sum += c[b];
+                held[b] = c[b];
+            }
+        }
+        lds_exp[e] = sum;
+    }
+    __syncthreads();
+    const int total_recv = block_scan_lds(lds_recv, N, wave_sums);
+    const int total_exp = block_scan_lds(lds_exp, E, wave_sums);
+    for (int d = tid; d < N; d += RP_NT)
+        p.rbase[d] = lds_recv[d];
+    if (tid == 0) {
+        p.rbase[N] = total_recv;
+        p.eoff[E] = total_exp;
+    }
+    for (int e = tid; e < E; e += RP_NT) {
+        int run = lds_exp[e];
+        p.eoff[e] = run;
+        const bool reuse = N <= BATCH && E <= RP_NT;
+        for (int s0 = 0; s0 < N; s0 += BATCH) {
+            int c[BATCH];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+                c[b] = reuse ? held[b] : cnt[(size_t)min(s0 + b, N - 1) * E + e];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b)
+                if (s0 + b < N) {
+                    p.ebase[(size_t)(s0 + b) * E + e] = run;
+                    run += c[b];
+                }
+        }
+    }
+}
+
+__global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
+{
+    extern __shared__ uint64_t lds64[];
+    const int E = ra.E;
+    const int CW = ra.chunk_waves;              // waves that take items in one chunk
+    uint64_t* mask = lds64;                     // [CW][E]: lanes of a wave holding expert e
+    int32_t* hist = reinterpret_cast<int32_t*>(mask + (size_t)CW * E);   // [E] counts, then cursor
+    int32_t* lds_recv = hist + E;               // [N] (last workgroup only)
+    int32_t* lds_exp = lds_recv + ra.N;         // [E] (last workgroup only)
+    __shared__ int32_t wave_sums[RP_WAVES + 1];
+    __shared__ int32_t ticket;
 
     const int s = blockIdx.x;
-    const int items = T * K;
-    const int32_t* my_idx = idx + (size_t)s * items;
-    int32_t* my_pos = pos + (size_t)s * items;
+    const int items = ra.T * ra.K;
+    const int32_t* my_idx = ra.idx + (size_t)s * items;
+    int32_t* my_pos = p.pos + (size_t)s * items;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+    const int chunk = CW * WAVE;
 
-    for (int e = tid; e < E; e += RC_NT)
+    for (int e = tid; e < E; e += RP_NT)
         hist[e] = 0;
     __syncthreads();
+    // expert ids of the first HELD_CHUNKS chunks stay in registers for the
+    // position pass (thread tid takes item c*chunk + tid of chunk c)
+    int held_e[HELD_CHUNKS];
+#pragma unroll
+    for (int c = 0; c < HELD_CHUNKS; ++c) {
+        const int i = c * chunk + tid;
+        held_e[c] = (tid < chunk && i < items) ? my_idx[i] : -1;
+    }
     int bad = 0;
-    for (int i = tid; i < items; i += RC_NT) {
+    for (int i = tid; i < items; i += RP_NT) {
         const int e = my_idx[i];
         if ((unsigned)e < (unsigned)E)
             atomicAdd(&hist[e], 1);
@@ -126,134 +262,90 @@ __global__ __launch_bounds__(RC_NT) void route_count_kernel(const int32_t* __res
             bad = 1;
     }
     if (bad)
-        atomicOr(err, ERR_BIT_ROUTING);
+        atomicOr(p.err, ERR_BIT_ROUTING);
     __syncthreads();
 
     // counts out, exclusive scan over experts -> send offsets and cursor
-    const int per = (E + RC_NT - 1) / RC_NT;
+    const int per = (E + RP_NT - 1) / RP_NT;
     const int e0 = tid * per;
     int local = 0;
     for (int j = 0; j < per; ++j) {
         const int e = e0 + j;
         if (e < E) {
             const int c = hist[e];
-            cnt[(size_t)s * E + e] = c;
+            p.cnt[(size_t)s * E + e] = c;
             local += c;
         }
     }
     int total;
-    int run = block_exclusive_scan<RC_NT>(local, wave_sums, &total);
+    int run = block_exclusive_scan<RP_NT>(local, wave_sums, &total);
     for (int j = 0; j < per; ++j) {
         const int e = e0 + j;
         if (e < E) {
             const int c = hist[e];
-            soff[(size_t)s * (E + 1) + e] = run;
+            p.soff[(size_t)s * (E + 1) + e] = run;
             hist[e] = run;
             run += c;
         }
     }
     if (tid == 0)
-        soff[(size_t)s * (E + 1) + E] = total;
+        p.soff[(size_t)s * (E + 1) + E] = total;
     __syncthreads();
 
+    // Stable positions, one chunk of CW*64 items at a time.  Each lane sets
+    // its bit in mask[wave][e] (an LDS 64-bit OR); then its rank among equal
+    // ids of the chunk is the set bits of lower waves' masks plus the bits of
+    // its own wave's mask below its lane, and the per-expert cursor advances by
+    // the chunk's total.
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
-    for (int c0 = 0; c0 < items; c0 += RC_NT) {
-        for (int j = tid; j < RC_WAVES * E; j += RC_NT)
-            wcnt[j] = 0;
+    for (int c0 = 0, c = 0; c0 < items; c0 += chunk, ++c) {
+        for (int j = tid; j < CW * E; j += RP_NT)
+            mask[j] = 0ull;
         __syncthreads();
         const int i = c0 + tid;
-        const int e = (i < items) ? my_idx[i] : -1;
-        const bool valid = (unsigned)e < (unsigned)E;
-        uint64_t todo = __ballot(valid);
-        int rank = 0;
-        while (todo) {
-            const int leader = __ffsll((unsigned long long)todo) - 1;
-            const int v = __shfl(e, leader, WAVE);
-            const uint64_t same = __ballot(valid && e == v);
-            if (valid && e == v) {
-                rank = __popcll(same & lanes_below);
-                if (rank == 0)
-                    wcnt[wave * E + v] = __popcll(same);
-            }
-            todo &= ~same;
+        const bool mine = tid < chunk && i < items;
+        int e = -1;
+#pragma unroll
+        for (int h = 0; h < HELD_CHUNKS; ++h)
+            if (c == h)
+                e = held_e[h];
+        if (c >= HELD_CHUNKS && mine)
+            e = my_idx[i];
+        const bool valid = mine && (unsigned)e < (unsigned)E;
+        if (valid)
+            atomicOr(reinterpret_cast<unsigned long long*>(&mask[(size_t)wave * E + e]),
+                     1ull << lane);
+        __syncthreads();
+        if (valid) {
+            int before = hist[e] + __popcll(mask[(size_t)wave * E + e] & lanes_below);
+            for (int w = 0; w < wave; ++w)
+                before += __popcll(mask[(size_t)w * E + e]);
+            my_pos[i] = before;
+        } else if (mine) {
+            my_pos[i] = -1;
         }
         __syncthreads();
-        for (int ee = tid; ee < E; ee += RC_NT) {
-            int r = hist[ee];
-            for (int w = 0; w < RC_WAVES; ++w) {
-                const int c = wcnt[w * E + ee];
-                wcnt[w * E + ee] = r;
-                r += c;
-            }
-            hist[ee] = r;
+        for (int ee = tid; ee < E; ee += RP_NT) {
+            int add = 0;
+            for (int w = 0; w < CW; ++w)
+                add += __popcll(mask[(size_t)w * E + ee]);
+            hist[ee] += add;
         }
-        __syncthreads();
-        if (i < items)
-            my_pos[i] = valid ? wcnt[wave * E + e] + rank : -1;
         __syncthreads();
     }
-}
 
-// ---------------------------------------------------------------------------
-// Offsets after the count exchange: one workgroup.
-//
-// [EFA] "Send and receive buffers": once the per-expert counts are exchanged,
-// each rank derives where to write and the offsets it receives from; [EFA]
-// "Dispatch and combine": the offsets for dispatch and combine are computed
-// once, off the critical path.  Outputs: receive offsets per (receiver,
-// sender), pooled receive bases, expert offsets, and the first expert-order
-// row of every (sender, expert) run.  A receive count above N*T*max(K, L) (the
-// page's bound) raises the capacity bit.
-// ---------------------------------------------------------------------------
-constexpr int OF_NT = 1024;
-
-__global__ __launch_bounds__(OF_NT) void offsets_kernel(int N, int E, int L, int64_t cap,
-                                                        const int32_t* __restrict__ cnt,
-                                                        const int32_t* __restrict__ soff,
-                                                        int32_t* __restrict__ roff,
-                                                        int32_t* __restrict__ rbase,
-                                                        int32_t* __restrict__ eoff,
-                                                        int32_t* __restrict__ ebase,
-                                                        int32_t* __restrict__ err)
-{
-    __shared__ int32_t wave_sums[OF_NT / WAVE + 1];
-    const int tid = threadIdx.x;
-
-    int recvtot = 0;
-    if (tid < N) {
-        const int d = tid;
-        int run = 0;
-        for (int s = 0; s < N; ++s) {
-            roff[(size_t)d * (N + 1) + s] = run;
-            run += soff[(size_t)s * (E + 1) + (d + 1) * L] - soff[(size_t)s * (E + 1) + d * L];
-        }
-        roff[(size_t)d * (N + 1) + N] = run;
-        recvtot = run;
-        if ((int64_t)run > cap)
-            atomicOr(err, ERR_BIT_CAPACITY);
-    }
-    int total;
-    const int base = block_exclusive_scan<OF_NT>(recvtot, wave_sums, &total);
-    if (tid < N)
-        rbase[tid] = base;
+    // publish this rank's counts, then draw a ticket
+    __threadfence();
+    __syncthreads();
     if (tid == 0)
-        rbase[N] = total;
-
-    int ecnt = 0;
-    if (tid < E)
-        for (int s = 0; s < N; ++s)
-            ecnt += cnt[(size_t)s * E + tid];
-    const int eb = block_exclusive_scan<OF_NT>(ecnt, wave_sums, &total);
-    if (tid < E) {
-        eoff[tid] = eb;
-        int run = eb;
-        for (int s = 0; s < N; ++s) {
-            ebase[(size_t)s * E + tid] = run;
-            run += cnt[(size_t)s * E + tid];
-        }
-    }
+        ticket = atomicAdd(p.ticket, 1);
+    __syncthreads();
+    if (ticket != ra.N - 1)
+        return;
+    __threadfence();
+    group_offsets(ra, p, lds_recv, lds_exp, wave_sums);
     if (tid == 0)
-        eoff[E] = total;
+        atomicExch(p.ticket, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -273,12 +365,18 @@ __device__ inline void record_row(const Shape& sh, const Plan& p, int32_t* __res
 {
     const int64_t TK = (int64_t)sh.T * sh.K;
     const int32_t srow = (int32_t)(s * TK + pk);
-    send_meta[srow] = t * sh.K + k;
+    if ((uint64_t)pk < (uint64_t)TK)
+        send_meta[srow] = t * sh.K + k;
     const int d = e / sh.L;
     const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
     const int32_t q = p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + pk - so[d * sh.L];
-    p.xfer_src[q] = srow;
     const int32_t r = p.ebase[(size_t)s * sh.E + e] + pk - so[e];
+    if ((uint64_t)q >= (uint64_t)sh.rows || (uint64_t)r >= (uint64_t)sh.rows ||
+        (uint64_t)pk >= (uint64_t)TK) {
+        atomicOr(p.err, ERR_BIT_INTERNAL);
+        return;
+    }
+    p.xfer_src[q] = srow;
     p.shuf_map[r] = make_int2(q, s);
 }
 
@@ -306,6 +404,8 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan 
     const int n = sh.payload_vecs;
     const v4u* src = x + tok * n;
     for (int base = 0; base < n; base += WAVE * U) {
+        // the caller's tokens are read with ordinary loads (measured faster
+        // here than the streaming hint); the K copies are streamed out
         v4u v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -313,12 +413,14 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan 
         hold(v);
         for (int k = 0; k < sh.K; ++k) {
             const int pk = readlane(my_p, k);
+            if ((unsigned)pk >= (unsigned)TK)
+                continue;
             v4u* dst = send_x + (s * TK + pk) * n;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = base + u * WAVE + lane;
                 if (j < n)
-                    dst[j] = v[u];
+                    st_nt(v[u], dst + j);
             }
         }
     }
@@ -386,7 +488,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
         v4u v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            v[u] = src[min(base + u * WAVE + lane, n - 1)];
+            v[u] = ld_nt(src + min(base + u * WAVE + lane, n - 1));
         hold(v);
         v2u q[U];
         float sc[U];
@@ -421,12 +523,15 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
             sc[u] = scale;
         }
         for (int k = 0; k < sh.K; ++k) {
-            const int64_t row = s * TK + readlane(my_p, k);
+            const int pk = readlane(my_p, k);
+            if ((unsigned)pk >= (unsigned)TK)
+                continue;
+            const int64_t row = s * TK + pk;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = base + u * WAVE + lane;
                 if (j < n) {
-                    send_q[row * n + j] = q[u];
+                    st_nt(q[u], send_q + row * n + j);
                     if ((lane & 15) == 0)
                         send_scale[row * nb + j / 16] = sc[u];
                 }
@@ -448,13 +553,13 @@ __device__ inline void copy_row(v4u* __restrict__ dst, const v4u* __restrict__ s
         v4u v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            v[u] = src[min(base + u * WAVE + lane, n - 1)];
+            v[u] = ld_nt(src + min(base + u * WAVE + lane, n - 1));
         hold(v);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = base + u * WAVE + lane;
             if (j < n)
-                dst[j] = v[u];
+                st_nt(v[u], dst + j);
         }
     }
 }
@@ -627,6 +732,11 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
         my_p = p.pos[tok * K + lane];
         my_w = w[tok * K + lane];
     }
+    if (__ballot((unsigned)my_p >= (unsigned)TK) != 0) {
+        if (lane == 0)
+            atomicOr(p.err, ERR_BIT_INTERNAL);
+        return;
+    }
     const int n = sh.comb_vecs;
     const v4u* rows = comb_recv + s * TK * n;
     v4u* dst = out + tok * n;
@@ -644,7 +754,7 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
                 const v4u* row = rows + (int64_t)readlane(my_p, k) * n;
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    v[k][u] = row[min(base + u * WAVE + lane, n - 1)];
+                    v[k][u] = ld_nt(row + min(base + u * WAVE + lane, n - 1));
             }
 #pragma unroll
             for (int k = 0; k < KT; ++k) {
@@ -659,14 +769,14 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
                 const float wk = readlane_f(my_w, k);
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    fma_row8(acc[u], wk, row[min(base + u * WAVE + lane, n - 1)]);
+                    fma_row8(acc[u], wk, ld_nt(row + min(base + u * WAVE + lane, n - 1)));
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = base + u * WAVE + lane;
             if (j < n)
-                dst[j] = pack_bf16x8(acc[u]);
+                st_nt(pack_bf16x8(acc[u]), dst + j);
         }
     }
 }
@@ -700,19 +810,22 @@ inline int unroll_for(int n)
 
 }  // namespace
 
-hipError_t launch_route_count(const Shape& sh, const int32_t* idx, const Plan& p, hipStream_t st)
+hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, hipStream_t st)
 {
-    const size_t lds = (size_t)(RC_WAVES + 1) * sh.E * sizeof(int32_t);
-    hipLaunchKernelGGL(route_count_kernel, dim3(sh.N), dim3(RC_NT), lds, st, idx, sh.T, sh.K, sh.E,
-                       p.cnt, p.soff, p.pos, p.err);
-    return hipGetLastError();
-}
-
-hipError_t launch_offsets(const Shape& sh, const Plan& p, hipStream_t st)
-{
-    const int64_t cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
-    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(OF_NT), 0, st, sh.N, sh.E, sh.L, cap, p.cnt,
-                       p.soff, p.roff, p.rbase, p.eoff, p.ebase, p.err);
+    RouteArgs ra;
+    ra.idx = idx;
+    ra.N = sh.N;
+    ra.T = sh.T;
+    ra.K = sh.K;
+    ra.E = sh.E;
+    ra.L = sh.L;
+    ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
+    // lane masks take 8 bytes per (wave, expert): 8 waves up to 512 experts,
+    // 4 waves above, so the whole plan stays within 64 KiB of LDS
+    ra.chunk_waves = sh.E <= 512 ? RP_WAVES : RP_WAVES / 2;
+    const size_t lds = (size_t)ra.chunk_waves * sh.E * sizeof(uint64_t) +
+                       ((size_t)sh.E + sh.N + sh.E) * sizeof(int32_t);
+    hipLaunchKernelGGL(route_plan_kernel, dim3(sh.N), dim3(RP_NT), lds, st, ra, p);
     return hipGetLastError();
 }
 

@@ -54,7 +54,8 @@ typedef enum moe_status {
     MOE_ERR_OOM = -3,       /* device allocation failed at create */
     MOE_ERR_STATE = -4,     /* call out of the dispatch/combine order */
     MOE_ERR_ROUTING = -5,   /* device saw an expert id outside [0, E) */
-    MOE_ERR_CAPACITY = -6   /* a receive count exceeded the page's bound (never expected) */
+    MOE_ERR_CAPACITY = -6,  /* a receive count exceeded the page's bound (never expected) */
+    MOE_ERR_INTERNAL = -7   /* a device-side index check failed; the offending writes were skipped */
 } moe_status;
 
 typedef enum moe_dtype {
@@ -98,8 +99,8 @@ int moe_group_destroy(moe_group_t g);
  *   num_tokens  T, 0 <= T <= max_tokens (same T on every logical rank)
  *   x           device, bf16 [N][T][H]
  *   topk_idx    device, int32 [N][T][K], expert ids in [0, E)
- * Enqueues: route count + stable positions, offsets, pack (+ e4m3 encode),
- * transfer into the receive buffers.  Reads x and topk_idx only. */
+ * Enqueues: route plan (counts, stable positions, offsets), pack (+ e4m3
+ * encode), transfer into the receive buffers.  Reads x and topk_idx only. */
 int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x,
                       const int32_t* topk_idx, hipStream_t stream);
 
@@ -168,7 +169,8 @@ typedef struct moe_group_view {
 int moe_group_view_get(moe_group_t g, moe_group_view* out);
 
 /* Synchronise `stream`, then return and clear the device-side error word:
- * MOE_OK, MOE_ERR_ROUTING or MOE_ERR_CAPACITY. */
+ * MOE_OK, MOE_ERR_ROUTING, MOE_ERR_CAPACITY or MOE_ERR_INTERNAL (in that order
+ * of precedence when several bits are set). */
 int moe_group_status(moe_group_t g, hipStream_t stream);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around each
@@ -176,15 +178,14 @@ int moe_group_status(moe_group_t g, hipStream_t stream);
  * synchronises on the recorded events, returns the summed milliseconds and
  * launch counts per kernel (arrays of MOE_KERNEL_COUNT) and resets them. */
 typedef enum moe_kernel_id {
-    MOE_KERNEL_ROUTE_COUNT = 0,
-    MOE_KERNEL_OFFSETS = 1,
-    MOE_KERNEL_PACK = 2,
-    MOE_KERNEL_TRANSFER = 3,
-    MOE_KERNEL_SHUFFLE = 4,
-    MOE_KERNEL_COMBINE_PACK = 5,
-    MOE_KERNEL_TRANSFER_BACK = 6,
-    MOE_KERNEL_COMBINE_REDUCE = 7,
-    MOE_KERNEL_COUNT = 8
+    MOE_KERNEL_ROUTE_PLAN = 0,      /* counts, stable positions, all offsets */
+    MOE_KERNEL_PACK = 1,
+    MOE_KERNEL_TRANSFER = 2,
+    MOE_KERNEL_SHUFFLE = 3,
+    MOE_KERNEL_COMBINE_PACK = 4,
+    MOE_KERNEL_TRANSFER_BACK = 5,
+    MOE_KERNEL_COMBINE_REDUCE = 6,
+    MOE_KERNEL_COUNT = 7
 } moe_kernel_id;
 
 int moe_group_timing_enable(moe_group_t g, int enable);

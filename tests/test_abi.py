@@ -42,8 +42,9 @@ def test_strerror_and_kernel_names(lib):
     assert lib.moe_strerror(0) == b"ok"
     assert lib.moe_strerror(-5).startswith(b"expert id")
     assert lib.moe_strerror(12345) == b"unknown status"
-    assert lib.moe_kernel_name(7) == b"combine_reduce_kernel"
-    assert lib.moe_kernel_name(8) == b""
+    assert lib.moe_kernel_name(0) == b"route_plan_kernel"
+    assert lib.moe_kernel_name(6) == b"combine_reduce_kernel"
+    assert lib.moe_kernel_name(7) == b""
 
 
 def test_host_validation_without_gpu(lib):
