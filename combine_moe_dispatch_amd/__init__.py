@@ -14,7 +14,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libmoe_ep.so")
+# MOE_EP_LIBRARY selects another build of the same library (same C ABI)
+LIB_PATH = os.environ.get("MOE_EP_LIBRARY") or os.path.join(_PKG, "lib", "libmoe_ep.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID = -1

@@ -25,7 +25,7 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
-constexpr int ROWS_PER_BLOCK = 4;          // one wave per row, 256 threads
+constexpr int ROWS_PER_BLOCK = 4;          // waves per 256-thread block
 constexpr int COPY_THREADS = WAVE * ROWS_PER_BLOCK;
 
 __device__ inline int lane_id() { return threadIdx.x & (WAVE - 1); }
@@ -117,28 +117,7 @@ __device__ int block_exclusive_scan(int v, int* wave_sums, int* total)
 constexpr int RP_NT = 512;
 constexpr int RP_WAVES = RP_NT / WAVE;
 constexpr int BATCH = 32;
-constexpr int HELD_CHUNKS = 8;      // idx chunks kept in registers between the two passes
-
-// In-place exclusive scan of n <= 2*RP_NT ints held in LDS; returns the total.
-__device__ int block_scan_lds(int32_t* a, int n, int* wave_sums)
-{
-    const int per = (n + RP_NT - 1) / RP_NT;
-    const int i0 = threadIdx.x * per;
-    int local = 0;
-    for (int j = 0; j < per; ++j)
-        if (i0 + j < n)
-            local += a[i0 + j];
-    int total;
-    int run = block_exclusive_scan<RP_NT>(local, wave_sums, &total);
-    for (int j = 0; j < per; ++j)
-        if (i0 + j < n) {
-            const int c = a[i0 + j];
-            a[i0 + j] = run;
-            run += c;
-        }
-    __syncthreads();
-    return total;
-}
+constexpr int HELD_CHUNKS = 32;     // idx chunks kept in registers between the two passes
 
 struct RouteArgs {
     const int32_t* idx;
@@ -147,78 +126,86 @@ struct RouteArgs {
     int64_t cap;
 };
 
-__device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* lds_recv,
-                              int32_t* lds_exp, int* wave_sums)
+// Every group-wide table is a pass down one column of the send-offset matrix
+// soff[s][*] over the senders s, because soff[s][e] already sums sender s's
+// counts of the experts before e:
+//   eoff[e]      = sum_s soff[s][e]                 (rows of all experts < e)
+//   ebase[s][e]  = eoff[e] + sum_{s'<s} cnt[s'][e]
+//   rbase[d]     = sum_s soff[s][d*L]               (rows received by ranks < d)
+//   roff[d][s]   = sum_{s'<s} (soff[s'][(d+1)L] - soff[s'][dL])
+// so one thread takes one column (E expert columns, the total column E, then
+// N receiver columns) and walks the senders with BATCH loads in flight; no
+// scan across threads.
+__device__ void group_offsets(const RouteArgs& ra, const Plan& p)
 {
-    const int N = ra.N, E = ra.E, L = ra.L, tid = threadIdx.x;
+    const int N = ra.N, E = ra.E, L = ra.L;
     const int32_t* __restrict__ soff = p.soff;
     const int32_t* __restrict__ cnt = p.cnt;
-    for (int d = tid; d < N; d += RP_NT) {
-        int run = 0;
-        for (int s0 = 0; s0 < N; s0 += BATCH) {
-            int lo[BATCH], hi[BATCH];
-#pragma unroll
-            for (int b = 0; b < BATCH; ++b) {
-                const size_t row = (size_t)min(s0 + b, N - 1) * (E + 1);
-                lo[b] = soff[row + d * L];
-                hi[b] = soff[row + (d + 1) * L];
-            }
-#pragma unroll
-            for (int b = 0; b < BATCH; ++b)
-                if (s0 + b < N) {
-                    p.roff[(size_t)d * (N + 1) + s0 + b] = run;
-                    run += hi[b] - lo[b];
-                }
-        }
-        p.roff[(size_t)d * (N + 1) + N] = run;
-        lds_recv[d] = run;
-        if ((int64_t)run > ra.cap)
-            atomicOr(p.err, ERR_BIT_CAPACITY);
-    }
-    // expert totals; with N <= BATCH the counts stay in registers for the
-    // per-sender bases below (e < RP_NT covers every expert of one pass when
-    // E <= RP_NT; larger E reloads)
-    int held[BATCH];
-    for (int e = tid; e < E; e += RP_NT) {
-        int sum = 0;
-        for (int s0 = 0; s0 < N; s0 += BATCH) {
+    for (int col = threadIdx.x; col < E + 1 + N; col += RP_NT) {
+        if (col <= E) {
+            // expert column e (col == E: the total, which ends both tables)
+            const int e = col;
+            // the counts of the column are loaded with its offsets and, for
+            // N <= BATCH, kept in registers for the second walk
+            const int ce = min(e, E - 1);
+            int base = 0;
             int c[BATCH];
+            for (int s0 = 0; s0 < N; s0 += BATCH) {
+                int o[BATCH];
 #pragma unroll
-            for (int b = 0; b < BATCH; ++b)
-                c[b] = cnt[(size_t)min(s0 + b, N - 1) * E + e];
-#pragma unroll
-            for (int b = 0; b < BATCH; ++b) {
-                if (s0 + b < N)
-                    sum += c[b];
-                held[b] = c[b];
-            }
-        }
-        lds_exp[e] = sum;
-    }
-    __syncthreads();
-    const int total_recv = block_scan_lds(lds_recv, N, wave_sums);
-    const int total_exp = block_scan_lds(lds_exp, E, wave_sums);
-    for (int d = tid; d < N; d += RP_NT)
-        p.rbase[d] = lds_recv[d];
-    if (tid == 0) {
-        p.rbase[N] = total_recv;
-        p.eoff[E] = total_exp;
-    }
-    for (int e = tid; e < E; e += RP_NT) {
-        int run = lds_exp[e];
-        p.eoff[e] = run;
-        const bool reuse = N <= BATCH && E <= RP_NT;
-        for (int s0 = 0; s0 < N; s0 += BATCH) {
-            int c[BATCH];
-#pragma unroll
-            for (int b = 0; b < BATCH; ++b)
-                c[b] = reuse ? held[b] : cnt[(size_t)min(s0 + b, N - 1) * E + e];
-#pragma unroll
-            for (int b = 0; b < BATCH; ++b)
-                if (s0 + b < N) {
-                    p.ebase[(size_t)(s0 + b) * E + e] = run;
-                    run += c[b];
+                for (int b = 0; b < BATCH; ++b) {
+                    const int sb = min(s0 + b, N - 1);
+                    o[b] = soff[(size_t)sb * (E + 1) + e];
+                    c[b] = cnt[(size_t)sb * E + ce];
                 }
+#pragma unroll
+                for (int b = 0; b < BATCH; ++b)
+                    if (s0 + b < N)
+                        base += o[b];
+            }
+            if (e == E) {
+                p.eoff[E] = base;
+                p.rbase[N] = base;
+                continue;
+            }
+            p.eoff[e] = base;
+            int run = base;
+            for (int s0 = 0; s0 < N; s0 += BATCH) {
+                if (N > BATCH) {
+#pragma unroll
+                    for (int b = 0; b < BATCH; ++b)
+                        c[b] = cnt[(size_t)min(s0 + b, N - 1) * E + e];
+                }
+#pragma unroll
+                for (int b = 0; b < BATCH; ++b)
+                    if (s0 + b < N) {
+                        p.ebase[(size_t)(s0 + b) * E + e] = run;
+                        run += c[b];
+                    }
+            }
+        } else {
+            const int d = col - E - 1;
+            int base = 0, run = 0;
+            for (int s0 = 0; s0 < N; s0 += BATCH) {
+                int lo[BATCH], hi[BATCH];
+#pragma unroll
+                for (int b = 0; b < BATCH; ++b) {
+                    const size_t row = (size_t)min(s0 + b, N - 1) * (E + 1);
+                    lo[b] = soff[row + d * L];
+                    hi[b] = soff[row + (d + 1) * L];
+                }
+#pragma unroll
+                for (int b = 0; b < BATCH; ++b)
+                    if (s0 + b < N) {
+                        p.roff[(size_t)d * (N + 1) + s0 + b] = run;
+                        run += hi[b] - lo[b];
+                        base += lo[b];
+                    }
+            }
+            p.roff[(size_t)d * (N + 1) + N] = run;
+            p.rbase[d] = base;
+            if ((int64_t)run > ra.cap)
+                atomicOr(p.err, ERR_BIT_CAPACITY);
         }
     }
 }
@@ -228,10 +215,8 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     extern __shared__ uint64_t lds64[];
     const int E = ra.E;
     const int CW = ra.chunk_waves;              // waves that take items in one chunk
-    uint64_t* mask = lds64;                     // [CW][E]: lanes of a wave holding expert e
-    int32_t* hist = reinterpret_cast<int32_t*>(mask + (size_t)CW * E);   // [E] counts, then cursor
-    int32_t* lds_recv = hist + E;               // [N] (last workgroup only)
-    int32_t* lds_exp = lds_recv + ra.N;         // [E] (last workgroup only)
+    uint64_t* mask = lds64;                     // [2][CW][E]: lanes of a wave holding expert e
+    int32_t* cur = reinterpret_cast<int32_t*>(mask + 2 * (size_t)CW * E);  // [2][E] cursors
     __shared__ int32_t wave_sums[RP_WAVES + 1];
     __shared__ int32_t ticket;
 
@@ -241,23 +226,44 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     int32_t* my_pos = p.pos + (size_t)s * items;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
     const int chunk = CW * WAVE;
+    const int held_items = min(items, HELD_CHUNKS * chunk);
 
     for (int e = tid; e < E; e += RP_NT)
-        hist[e] = 0;
-    __syncthreads();
-    // expert ids of the first HELD_CHUNKS chunks stay in registers for the
-    // position pass (thread tid takes item c*chunk + tid of chunk c)
+        cur[e] = 0;
+    for (int j = tid; j < CW * E; j += RP_NT)
+        mask[j] = 0ull;
+    // expert ids of the first HELD_CHUNKS chunks stay in registers for both
+    // passes (thread tid takes item c*chunk + tid of chunk c); all loads are
+    // issued before the first use
     int held_e[HELD_CHUNKS];
+    if (items > 0) {
+        // clamped addresses, so the loads are unconditional and issue together
+#pragma unroll
+        for (int c = 0; c < HELD_CHUNKS; ++c)
+            held_e[c] = my_idx[min(c * chunk + tid, items - 1)];
+#pragma unroll
+        for (int c = 0; c < HELD_CHUNKS; ++c)
+            if (!(tid < chunk && c * chunk + tid < items))
+                held_e[c] = -1;
+    } else {
+#pragma unroll
+        for (int c = 0; c < HELD_CHUNKS; ++c)
+            held_e[c] = -1;
+    }
+    __syncthreads();
+    int bad = 0;
 #pragma unroll
     for (int c = 0; c < HELD_CHUNKS; ++c) {
-        const int i = c * chunk + tid;
-        held_e[c] = (tid < chunk && i < items) ? my_idx[i] : -1;
+        const int e = held_e[c];
+        if ((unsigned)e < (unsigned)E)
+            atomicAdd(&cur[e], 1);
+        else if (tid < chunk && c * chunk + tid < items)
+            bad = 1;
     }
-    int bad = 0;
-    for (int i = tid; i < items; i += RP_NT) {
+    for (int i = held_items + tid; i < items; i += RP_NT) {
         const int e = my_idx[i];
         if ((unsigned)e < (unsigned)E)
-            atomicAdd(&hist[e], 1);
+            atomicAdd(&cur[e], 1);
         else
             bad = 1;
     }
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     for (int j = 0; j < per; ++j) {
         const int e = e0 + j;
         if (e < E) {
-            const int c = hist[e];
+            const int c = cur[e];
             p.cnt[(size_t)s * E + e] = c;
             local += c;
         }
@@ -282,9 +288,9 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     for (int j = 0; j < per; ++j) {
         const int e = e0 + j;
         if (e < E) {
-            const int c = hist[e];
+            const int c = cur[e];
             p.soff[(size_t)s * (E + 1) + e] = run;
-            hist[e] = run;
+            cur[e] = run;
             run += c;
         }
     }
@@ -292,16 +298,19 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
         p.soff[(size_t)s * (E + 1) + E] = total;
     __syncthreads();
 
-    // Stable positions, one chunk of CW*64 items at a time.  Each lane sets
-    // its bit in mask[wave][e] (an LDS 64-bit OR); then its rank among equal
-    // ids of the chunk is the set bits of lower waves' masks plus the bits of
-    // its own wave's mask below its lane, and the per-expert cursor advances by
-    // the chunk's total.
+    // Stable positions, one chunk of CW*64 items at a time, two barriers per
+    // chunk (masks and cursors double-buffered by chunk parity).  Each lane
+    // sets its bit in mask[wave][e] with an LDS 64-bit OR; its rank among
+    // equal ids of the chunk is then the set bits of lower waves' masks plus
+    // the bits of its own wave's mask below its lane; the per-expert cursor
+    // advances by the chunk's total into the other buffer.
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
     for (int c0 = 0, c = 0; c0 < items; c0 += chunk, ++c) {
-        for (int j = tid; j < CW * E; j += RP_NT)
-            mask[j] = 0ull;
-        __syncthreads();
+        const int A = c & 1;
+        uint64_t* mA = mask + (size_t)A * CW * E;
+        uint64_t* mB = mask + (size_t)(A ^ 1) * CW * E;
+        int32_t* cA = cur + A * E;
+        int32_t* cB = cur + (A ^ 1) * E;
         const int i = c0 + tid;
         const bool mine = tid < chunk && i < items;
         int e = -1;
@@ -313,39 +322,70 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
             e = my_idx[i];
         const bool valid = mine && (unsigned)e < (unsigned)E;
         if (valid)
-            atomicOr(reinterpret_cast<unsigned long long*>(&mask[(size_t)wave * E + e]),
-                     1ull << lane);
+            atomicOr(reinterpret_cast<unsigned long long*>(&mA[(size_t)wave * E + e]), 1ull << lane);
+        for (int j = tid; j < CW * E; j += RP_NT)
+            mB[j] = 0ull;
         __syncthreads();
         if (valid) {
-            int before = hist[e] + __popcll(mask[(size_t)wave * E + e] & lanes_below);
+            int before = cA[e] + __popcll(mA[(size_t)wave * E + e] & lanes_below);
             for (int w = 0; w < wave; ++w)
-                before += __popcll(mask[(size_t)w * E + e]);
+                before += __popcll(mA[(size_t)w * E + e]);
             my_pos[i] = before;
         } else if (mine) {
             my_pos[i] = -1;
         }
-        __syncthreads();
         for (int ee = tid; ee < E; ee += RP_NT) {
             int add = 0;
             for (int w = 0; w < CW; ++w)
-                add += __popcll(mask[(size_t)w * E + ee]);
-            hist[ee] += add;
+                add += __popcll(mA[(size_t)w * E + ee]);
+            cB[ee] = cA[ee] + add;
         }
         __syncthreads();
     }
 
-    // publish this rank's counts, then draw a ticket
-    __threadfence();
+    // Publish this rank's counts and draw a ticket.  Every wave waits for its
+    // own stores, then one agent-scope release (an L2 write-back) covers the
+    // whole workgroup before the ticket is taken.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0)
+    if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         ticket = atomicAdd(p.ticket, 1);
+    }
     __syncthreads();
     if (ticket != ra.N - 1)
         return;
-    __threadfence();
-    group_offsets(ra, p, lds_recv, lds_exp, wave_sums);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    group_offsets(ra, p);
     if (tid == 0)
         atomicExch(p.ticket, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Work split of the row kernels.  SPLIT waves share one row, each moving a
+// contiguous part (ALIGN-vector aligned), so a 256-thread block covers
+// 4/SPLIT rows.  Long rows are split until a wave moves about 4 KiB: many
+// short waves keep more rows in flight per CU than one long wave per row
+// (measured on the 14 KiB DeepSeek-shaped rows).
+// ---------------------------------------------------------------------------
+struct RowSlot {
+    int64_t row;
+    int b0, len;      // vectors [b0, b0 + len) of the row
+    bool lead;        // part 0 also moves the row's scales and metadata
+};
+
+template <int SPLIT, int ALIGN = 1>
+__device__ inline RowSlot row_slot(int n)
+{
+    RowSlot rs;
+    const int w = threadIdx.x / WAVE;
+    rs.row = (int64_t)blockIdx.x * (ROWS_PER_BLOCK / SPLIT) + w / SPLIT;
+    const int part = w % SPLIT;
+    const int plen = ((n + SPLIT - 1) / SPLIT + ALIGN - 1) / ALIGN * ALIGN;
+    rs.b0 = min(n, part * plen);
+    rs.len = min(n, rs.b0 + plen) - rs.b0;
+    rs.lead = part == 0;
+    return rs;
 }
 
 // ---------------------------------------------------------------------------
@@ -380,7 +420,7 @@ __device__ inline void record_row(const Shape& sh, const Plan& p, int32_t* __res
     p.shuf_map[r] = make_int2(q, s);
 }
 
-template <int U>
+template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan p,
                                                                  const v4u* __restrict__ x,
                                                                  const int32_t* __restrict__ idx,
@@ -390,7 +430,9 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan 
     if (*p.err)
         return;
     const int lane = lane_id();
-    const int64_t tok = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    const int n = sh.payload_vecs;
+    const RowSlot rs = row_slot<SPLIT>(n);
+    const int64_t tok = rs.row;
     if (tok >= (int64_t)sh.N * sh.T)
         return;
     const int s = (int)(tok / sh.T), t = (int)(tok % sh.T);
@@ -399,27 +441,27 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan 
     if (lane < sh.K) {
         const int64_t i = tok * sh.K + lane;
         my_p = p.pos[i];
-        record_row(sh, p, send_meta, s, t, lane, idx[i], my_p);
+        if (rs.lead)
+            record_row(sh, p, send_meta, s, t, lane, idx[i], my_p);
     }
-    const int n = sh.payload_vecs;
-    const v4u* src = x + tok * n;
-    for (int base = 0; base < n; base += WAVE * U) {
+    const v4u* src = x + tok * n + rs.b0;
+    for (int base = 0; base < rs.len; base += WAVE * U) {
         // the caller's tokens are read with ordinary loads (measured faster
         // here than the streaming hint); the K copies are streamed out
         v4u v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            v[u] = src[min(base + u * WAVE + lane, n - 1)];
+            v[u] = src[min(base + u * WAVE + lane, rs.len - 1)];
         hold(v);
         for (int k = 0; k < sh.K; ++k) {
             const int pk = readlane(my_p, k);
             if ((unsigned)pk >= (unsigned)TK)
                 continue;
-            v4u* dst = send_x + (s * TK + pk) * n;
+            v4u* dst = send_x + (s * TK + pk) * n + rs.b0;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = base + u * WAVE + lane;
-                if (j < n)
+                if (j < rs.len)
                     st_nt(v[u], dst + j);
             }
         }
@@ -457,7 +499,7 @@ __device__ inline uint32_t e4m3_encode(float v)
 // divisions (inv = 0, scale = 1 for an all-zero block), code = e4m3(x * inv).
 // A 128-element block is 16 lanes x 8 elements; amax is reduced over the
 // 16-lane group with xor shuffles.
-template <int U>
+template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p,
                                                                 const v4u* __restrict__ x,
                                                                 const int32_t* __restrict__ idx,
@@ -468,7 +510,9 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
     if (*p.err)
         return;
     const int lane = lane_id();
-    const int64_t tok = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    const int n = sh.H / 8;                    // input vectors of 8 bf16 per row
+    const RowSlot rs = row_slot<SPLIT, 16>(n); // parts hold whole 128-element blocks
+    const int64_t tok = rs.row;
     if (tok >= (int64_t)sh.N * sh.T)
         return;
     const int s = (int)(tok / sh.T), t = (int)(tok % sh.T);
@@ -477,18 +521,20 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
     if (lane < sh.K) {
         const int64_t i = tok * sh.K + lane;
         my_p = p.pos[i];
-        record_row(sh, p, send_meta, s, t, lane, idx[i], my_p);
+        if (rs.lead)
+            record_row(sh, p, send_meta, s, t, lane, idx[i], my_p);
     }
-    const int n = sh.H / 8;                    // input vectors of 8 bf16 per row
     const int nb = sh.scale_blocks;
     const v4u* src = x + tok * n;
-    for (int base = 0; base < n; base += WAVE * U) {
+    for (int base = rs.b0; base < rs.b0 + rs.len; base += WAVE * U) {
         // clamped loads (see copy_row); a 16-lane group lies wholly inside or
-        // wholly past the row end because n and base are multiples of 16
+        // wholly past the part's end because the part bounds and base are
+        // multiples of 16
+        const int end = rs.b0 + rs.len;
         v4u v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            v[u] = ld_nt(src + min(base + u * WAVE + lane, n - 1));
+            v[u] = ld_nt(src + min(base + u * WAVE + lane, end - 1));
         hold(v);
         v2u q[U];
         float sc[U];
@@ -530,7 +576,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = base + u * WAVE + lane;
-                if (j < n) {
+                if (j < end) {
                     st_nt(q[u], send_q + row * n + j);
                     if ((lane & 15) == 0)
                         send_scale[row * nb + j / 16] = sc[u];
@@ -568,7 +614,7 @@ __device__ inline void copy_row(v4u* __restrict__ dst, const v4u* __restrict__ s
 // one contiguous write; here rank d's receive row q takes send row
 // xfer_src[q], so every (s -> d) segment is copied contiguously).  Moves the
 // payload, the block scales (e4m3) and the meta word.
-template <int U>
+template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p,
                                                                 const v4u* __restrict__ send_x,
                                                                 v4u* __restrict__ recv_x,
@@ -580,14 +626,17 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p
     if (*p.err)
         return;
     const int lane = lane_id();
-    const int64_t q = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    const int n = sh.payload_vecs;
+    const RowSlot rs = row_slot<SPLIT>(n);
+    const int64_t q = rs.row;
     if (q >= sh.rows)
         return;
     const int64_t srow = p.xfer_src[q];
     if ((uint64_t)srow >= (uint64_t)sh.rows)
         return;
-    const int n = sh.payload_vecs;
-    copy_row<U>(recv_x + q * n, send_x + srow * n, n, lane);
+    copy_row<U>(recv_x + q * n + rs.b0, send_x + srow * n + rs.b0, rs.len, lane);
+    if (!rs.lead)
+        return;
     if (sh.fp8)
         for (int j = lane; j < sh.scale_blocks; j += WAVE)
             recv_scale[q * sh.scale_blocks + j] = send_scale[srow * sh.scale_blocks + j];
@@ -600,7 +649,7 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p
 // for combine; [EFA] "Dispatch and combine": shuffle from the receive buffer
 // into the tensor handed to the grouped GEMM).  Expert row r takes receive row
 // shuf_map[r].x; block 0 also publishes the expert offsets.
-template <int U>
+template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void shuffle_kernel(Shape sh, Plan p,
                                                                const v4u* __restrict__ recv_x,
                                                                const float* __restrict__ recv_scale,
@@ -617,15 +666,18 @@ __global__ __launch_bounds__(COPY_THREADS) void shuffle_kernel(Shape sh, Plan p,
         for (int e = threadIdx.x; e <= sh.E; e += COPY_THREADS)
             expert_offsets[e] = p.eoff[e];
     const int lane = lane_id();
-    const int64_t r = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    const int n = sh.payload_vecs;
+    const RowSlot rs = row_slot<SPLIT>(n);
+    const int64_t r = rs.row;
     if (r >= sh.rows)
         return;
     const int2 m = p.shuf_map[r];
     const int64_t q = m.x;
     if ((uint64_t)q >= (uint64_t)sh.rows)
         return;
-    const int n = sh.payload_vecs;
-    copy_row<U>(expert_x + r * n, recv_x + q * n, n, lane);
+    copy_row<U>(expert_x + r * n + rs.b0, recv_x + q * n + rs.b0, rs.len, lane);
+    if (!rs.lead)
+        return;
     if (sh.fp8)
         for (int j = lane; j < sh.scale_blocks; j += WAVE)
             expert_scale[r * sh.scale_blocks + j] = recv_scale[q * sh.scale_blocks + j];
@@ -638,7 +690,7 @@ __global__ __launch_bounds__(COPY_THREADS) void shuffle_kernel(Shape sh, Plan p,
 // Combine send ([EPMC] "Combine": the 16-bit expert outputs go back to the
 // slot each row came from; the inverse of the receive shuffle): expert row r
 // is scattered to receive-layout row shuf_map[r].x.
-template <int U>
+template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void combine_pack_kernel(Shape sh, Plan p,
                                                                     const v4u* __restrict__ y,
                                                                     v4u* __restrict__ comb_send)
@@ -646,19 +698,20 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_pack_kernel(Shape sh, Pl
     if (*p.err)
         return;
     const int lane = lane_id();
-    const int64_t r = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    const int n = sh.comb_vecs;
+    const RowSlot rs = row_slot<SPLIT>(n);
+    const int64_t r = rs.row;
     if (r >= sh.rows)
         return;
     const int64_t q = p.shuf_map[r].x;
     if ((uint64_t)q >= (uint64_t)sh.rows)
         return;
-    const int n = sh.comb_vecs;
-    copy_row<U>(comb_send + q * n, y + r * n, n, lane);
+    copy_row<U>(comb_send + q * n + rs.b0, y + r * n + rs.b0, rs.len, lane);
 }
 
 // Combine transfer ([EFA] "Dispatch and combine": one write per peer back to
 // the token's rank): receive-layout row q returns to send row xfer_src[q].
-template <int U>
+template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, Plan p,
                                                                      const v4u* __restrict__ comb_send,
                                                                      v4u* __restrict__ comb_recv)
@@ -666,14 +719,15 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, P
     if (*p.err)
         return;
     const int lane = lane_id();
-    const int64_t q = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    const int n = sh.comb_vecs;
+    const RowSlot rs = row_slot<SPLIT>(n);
+    const int64_t q = rs.row;
     if (q >= sh.rows)
         return;
     const int64_t srow = p.xfer_src[q];
     if ((uint64_t)srow >= (uint64_t)sh.rows)
         return;
-    const int n = sh.comb_vecs;
-    copy_row<U>(comb_recv + srow * n, comb_send + q * n, n, lane);
+    copy_row<U>(comb_recv + srow * n + rs.b0, comb_send + q * n + rs.b0, rs.len, lane);
 }
 
 // bf16 pattern of an fp32 value, round to nearest even (NaN -> 0x7FC0).
@@ -711,7 +765,7 @@ __device__ inline v4u pack_bf16x8(const float (&acc)[8])
 // [EFA] "Dispatch/combine latency").  fp32, k ascending, one fma chain from +0,
 // then bf16 round-to-nearest-even.  With K known at compile time (KT > 0) the
 // K*U row loads of a chunk are all issued before the first fma.
-template <int KT, int U>
+template <int KT, int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, Plan p,
                                                                       const v4u* __restrict__ comb_recv,
                                                                       const float* __restrict__ w,
@@ -720,7 +774,8 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
     if (*p.err)
         return;
     const int lane = lane_id();
-    const int64_t tok = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    const RowSlot rs = row_slot<SPLIT>(sh.comb_vecs);
+    const int64_t tok = rs.row;
     if (tok >= (int64_t)sh.N * sh.T)
         return;
     const int K = KT > 0 ? KT : sh.K;
@@ -737,9 +792,10 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
             atomicOr(p.err, ERR_BIT_INTERNAL);
         return;
     }
-    const int n = sh.comb_vecs;
-    const v4u* rows = comb_recv + s * TK * n;
-    v4u* dst = out + tok * n;
+    const int n = rs.len;                      // this wave's part of the row
+    const int stride = sh.comb_vecs;
+    const v4u* rows = comb_recv + s * TK * stride + rs.b0;
+    v4u* dst = out + tok * stride + rs.b0;
     for (int base = 0; base < n; base += WAVE * U) {
         float acc[U][8];
 #pragma unroll
@@ -751,7 +807,7 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
             v4u v[KT][U];
 #pragma unroll
             for (int k = 0; k < KT; ++k) {
-                const v4u* row = rows + (int64_t)readlane(my_p, k) * n;
+                const v4u* row = rows + (int64_t)readlane(my_p, k) * stride;
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     v[k][u] = ld_nt(row + min(base + u * WAVE + lane, n - 1));
@@ -765,7 +821,7 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
             }
         } else {
             for (int k = 0; k < K; ++k) {
-                const v4u* row = rows + (int64_t)readlane(my_p, k) * n;
+                const v4u* row = rows + (int64_t)readlane(my_p, k) * stride;
                 const float wk = readlane_f(my_w, k);
 #pragma unroll
                 for (int u = 0; u < U; ++u)
@@ -781,32 +837,49 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
     }
 }
 
-inline unsigned row_blocks(int64_t rows)
+// Launch shape of a row kernel: waves per row (SPLIT) and 16-byte vectors
+// per lane per round (U), from the number of vectors in a row.
+struct RowShape {
+    int u, split;
+};
+
+inline RowShape row_shape(int n)
 {
-    const int64_t b = (rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    const int per_lane = (n + WAVE - 1) / WAVE;
+    if (per_lane <= 1) return {1, 1};
+    if (per_lane <= 2) return {2, 1};
+    if (per_lane <= 4) return {4, 1};
+    if (per_lane <= 8) return {4, 2};
+    if (per_lane <= 16) return {4, 4};
+    if (per_lane <= 32) return {8, 4};
+    return {16, 4};
+}
+
+inline unsigned row_blocks(int64_t rows, int split)
+{
+    const int64_t per_block = ROWS_PER_BLOCK / split;
+    const int64_t b = (rows + per_block - 1) / per_block;
     return (unsigned)(b > 0 ? b : 1);
 }
 
-// Vectors per lane needed to hold a row of n 16-byte vectors, rounded up to
-// an instantiated unroll (rows longer than 16 vectors per lane loop).
-inline int unroll_for(int n)
-{
-    const int per_lane = (n + WAVE - 1) / WAVE;
-    if (per_lane <= 1) return 1;
-    if (per_lane <= 2) return 2;
-    if (per_lane <= 4) return 4;
-    if (per_lane <= 8) return 8;
-    return 16;
-}
-
-#define MOE_DISPATCH_U(u, KERNEL, ...)                                                   \
-    switch (u) {                                                                          \
-    case 1: hipLaunchKernelGGL((KERNEL<1>), __VA_ARGS__); break;                          \
-    case 2: hipLaunchKernelGGL((KERNEL<2>), __VA_ARGS__); break;                          \
-    case 4: hipLaunchKernelGGL((KERNEL<4>), __VA_ARGS__); break;                          \
-    case 8: hipLaunchKernelGGL((KERNEL<8>), __VA_ARGS__); break;                          \
-    default: hipLaunchKernelGGL((KERNEL<16>), __VA_ARGS__); break;                        \
-    }
+#define MOE_DISPATCH_ROW(rsh, KERNEL, GRID_ROWS, ...)                                              \
+    do {                                                                                           \
+        const dim3 grid_(row_blocks((GRID_ROWS), (rsh).split)), block_(COPY_THREADS);              \
+        if ((rsh).split == 1 && (rsh).u == 1)                                                      \
+            hipLaunchKernelGGL((KERNEL<1, 1>), grid_, block_, 0, __VA_ARGS__);                     \
+        else if ((rsh).split == 1 && (rsh).u == 2)                                                 \
+            hipLaunchKernelGGL((KERNEL<2, 1>), grid_, block_, 0, __VA_ARGS__);                     \
+        else if ((rsh).split == 1)                                                                 \
+            hipLaunchKernelGGL((KERNEL<4, 1>), grid_, block_, 0, __VA_ARGS__);                     \
+        else if ((rsh).split == 2)                                                                 \
+            hipLaunchKernelGGL((KERNEL<4, 2>), grid_, block_, 0, __VA_ARGS__);                     \
+        else if ((rsh).u == 4)                                                                     \
+            hipLaunchKernelGGL((KERNEL<4, 4>), grid_, block_, 0, __VA_ARGS__);                     \
+        else if ((rsh).u == 8)                                                                     \
+            hipLaunchKernelGGL((KERNEL<8, 4>), grid_, block_, 0, __VA_ARGS__);                     \
+        else                                                                                       \
+            hipLaunchKernelGGL((KERNEL<16, 4>), grid_, block_, 0, __VA_ARGS__);                    \
+    } while (0)
 
 }  // namespace
 
@@ -820,11 +893,11 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     ra.E = sh.E;
     ra.L = sh.L;
     ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
-    // lane masks take 8 bytes per (wave, expert): 8 waves up to 512 experts,
-    // 4 waves above, so the whole plan stays within 64 KiB of LDS
-    ra.chunk_waves = sh.E <= 512 ? RP_WAVES : RP_WAVES / 2;
-    const size_t lds = (size_t)ra.chunk_waves * sh.E * sizeof(uint64_t) +
-                       ((size_t)sh.E + sh.N + sh.E) * sizeof(int32_t);
+    // two buffers of lane masks take 16 bytes per (wave, expert): 8 waves
+    // up to 256 experts, 4 up to 512, 2 above, within 32 KiB of LDS
+    ra.chunk_waves = sh.E <= 256 ? RP_WAVES : sh.E <= 512 ? RP_WAVES / 2 : RP_WAVES / 4;
+    const size_t lds = 2 * (size_t)ra.chunk_waves * sh.E * sizeof(uint64_t) +
+                       (size_t)2 * sh.E * sizeof(int32_t);
     hipLaunchKernelGGL(route_plan_kernel, dim3(sh.N), dim3(RP_NT), lds, st, ra, p);
     return hipGetLastError();
 }
@@ -835,15 +908,17 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
         return hipSuccess;
-    const dim3 grid(row_blocks(tokens)), block(COPY_THREADS);
     if (sh.fp8) {
-        int u = unroll_for(sh.H / 8);
-        if (u > 8) u = 8;
-        MOE_DISPATCH_U(u, pack_fp8_kernel, grid, block, 0, st, sh, p, (const v4u*)x, idx,
-                       (v2u*)r.send_x, r.send_scale, r.send_meta);
+        // input rows of H/8 vectors; each lane also holds codes and scales,
+        // so at most 8 vectors per lane per round
+        RowShape rsh = row_shape(sh.H / 8);
+        if (rsh.u > 8)
+            rsh.u = 8;
+        MOE_DISPATCH_ROW(rsh, pack_fp8_kernel, tokens, st, sh, p, (const v4u*)x, idx,
+                         (v2u*)r.send_x, r.send_scale, r.send_meta);
     } else {
-        MOE_DISPATCH_U(unroll_for(sh.payload_vecs), pack_bf16_kernel, grid, block, 0, st, sh, p,
-                       (const v4u*)x, idx, (v4u*)r.send_x, r.send_meta);
+        MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), pack_bf16_kernel, tokens, st, sh, p,
+                         (const v4u*)x, idx, (v4u*)r.send_x, r.send_meta);
     }
     return hipGetLastError();
 }
@@ -852,19 +927,19 @@ hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, hipStr
 {
     if (sh.rows == 0)
         return hipSuccess;
-    MOE_DISPATCH_U(unroll_for(sh.payload_vecs), transfer_kernel, dim3(row_blocks(sh.rows)),
-                   dim3(COPY_THREADS), 0, st, sh, p, (const v4u*)r.send_x, (v4u*)r.recv_x,
-                   r.send_scale, r.recv_scale, r.send_meta, r.recv_meta);
+    MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), transfer_kernel, sh.rows, st, sh, p,
+                     (const v4u*)r.send_x, (v4u*)r.recv_x, r.send_scale, r.recv_scale,
+                     r.send_meta, r.recv_meta);
     return hipGetLastError();
 }
 
 hipError_t launch_shuffle(const Shape& sh, const Plan& p, const Rows& r, void* expert_x,
                           float* expert_scale, int32_t* expert_offsets, hipStream_t st)
 {
-    MOE_DISPATCH_U(unroll_for(sh.payload_vecs), shuffle_kernel, dim3(row_blocks(sh.rows)),
-                   dim3(COPY_THREADS), 0, st, sh, p, (const v4u*)r.recv_x, r.recv_scale,
-                   r.recv_meta, (v4u*)expert_x, expert_scale, r.src_rank, r.src_slot,
-                   expert_offsets);
+    // launched even with no rows: block 0 publishes the expert offsets
+    MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), shuffle_kernel, sh.rows, st, sh, p,
+                     (const v4u*)r.recv_x, r.recv_scale, r.recv_meta, (v4u*)expert_x,
+                     expert_scale, r.src_rank, r.src_slot, expert_offsets);
     return hipGetLastError();
 }
 
@@ -873,8 +948,8 @@ hipError_t launch_combine_pack(const Shape& sh, const Plan& p, const Rows& r, co
 {
     if (sh.rows == 0)
         return hipSuccess;
-    MOE_DISPATCH_U(unroll_for(sh.comb_vecs), combine_pack_kernel, dim3(row_blocks(sh.rows)),
-                   dim3(COPY_THREADS), 0, st, sh, p, (const v4u*)y, (v4u*)r.comb_send);
+    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), combine_pack_kernel, sh.rows, st, sh, p,
+                     (const v4u*)y, (v4u*)r.comb_send);
     return hipGetLastError();
 }
 
@@ -882,10 +957,25 @@ hipError_t launch_transfer_back(const Shape& sh, const Plan& p, const Rows& r, h
 {
     if (sh.rows == 0)
         return hipSuccess;
-    MOE_DISPATCH_U(unroll_for(sh.comb_vecs), transfer_back_kernel, dim3(row_blocks(sh.rows)),
-                   dim3(COPY_THREADS), 0, st, sh, p, (const v4u*)r.comb_send,
-                   (v4u*)r.comb_recv);
+    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), transfer_back_kernel, sh.rows, st, sh, p,
+                     (const v4u*)r.comb_send, (v4u*)r.comb_recv);
     return hipGetLastError();
+}
+
+// The reduce keeps K*U row vectors in flight per lane: U = 4 up to K = 2,
+// else 2; rows are split across waves as for the movers.
+template <int KT, int U>
+static void launch_reduce_k(const Shape& sh, const Plan& p, const v4u* cr, const float* w, v4u* o,
+                            int64_t tokens, hipStream_t st)
+{
+    const int split = row_shape(sh.comb_vecs).split;
+    const dim3 grid(row_blocks(tokens, split)), block(COPY_THREADS);
+    if (split == 1)
+        hipLaunchKernelGGL((combine_reduce_kernel<KT, U, 1>), grid, block, 0, st, sh, p, cr, w, o);
+    else if (split == 2)
+        hipLaunchKernelGGL((combine_reduce_kernel<KT, U, 2>), grid, block, 0, st, sh, p, cr, w, o);
+    else
+        hipLaunchKernelGGL((combine_reduce_kernel<KT, U, 4>), grid, block, 0, st, sh, p, cr, w, o);
 }
 
 hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, const float* w,
@@ -894,16 +984,15 @@ hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, 
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
         return hipSuccess;
-    const dim3 grid(row_blocks(tokens)), block(COPY_THREADS);
     const v4u* cr = (const v4u*)r.comb_recv;
     v4u* o = (v4u*)out;
     switch (sh.K) {
-    case 1: hipLaunchKernelGGL((combine_reduce_kernel<1, 4>), grid, block, 0, st, sh, p, cr, w, o); break;
-    case 2: hipLaunchKernelGGL((combine_reduce_kernel<2, 4>), grid, block, 0, st, sh, p, cr, w, o); break;
-    case 4: hipLaunchKernelGGL((combine_reduce_kernel<4, 2>), grid, block, 0, st, sh, p, cr, w, o); break;
-    case 6: hipLaunchKernelGGL((combine_reduce_kernel<6, 2>), grid, block, 0, st, sh, p, cr, w, o); break;
-    case 8: hipLaunchKernelGGL((combine_reduce_kernel<8, 2>), grid, block, 0, st, sh, p, cr, w, o); break;
-    default: hipLaunchKernelGGL((combine_reduce_kernel<0, 2>), grid, block, 0, st, sh, p, cr, w, o); break;
+    case 1: launch_reduce_k<1, 4>(sh, p, cr, w, o, tokens, st); break;
+    case 2: launch_reduce_k<2, 4>(sh, p, cr, w, o, tokens, st); break;
+    case 4: launch_reduce_k<4, 2>(sh, p, cr, w, o, tokens, st); break;
+    case 6: launch_reduce_k<6, 2>(sh, p, cr, w, o, tokens, st); break;
+    case 8: launch_reduce_k<8, 2>(sh, p, cr, w, o, tokens, st); break;
+    default: launch_reduce_k<0, 2>(sh, p, cr, w, o, tokens, st); break;
     }
     return hipGetLastError();
 }
