@@ -81,6 +81,100 @@ def measured_traffic(config_key: str, kernel: str, src_hash: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+# ---------------------------------------------------------------- profiles
+
+CAL_BYTES = 469_762_048        # one plain device copy of this many bytes each way
+KERNEL_OF = [("route_plan_kernel", "route_plan"), ("pack_bf16_kernel", "pack"),
+             ("pack_fp8_kernel", "pack"), ("transfer_back_kernel", "transfer_back"),
+             ("transfer_kernel", "transfer"), ("shuffle_kernel", "shuffle"),
+             ("combine_pack_kernel", "combine_pack"),
+             ("combine_reduce_kernel", "combine_reduce")]
+
+
+def _kernel_key(name: str):
+    for sym, key in KERNEL_OF:
+        if f"::{sym}<" in name or f"::{sym}(" in name:
+            return key
+    return None
+
+
+def copy_calibration() -> int:
+    """A plain device copy of CAL_BYTES bytes, 5 times (torch's copy kernel):
+    the reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+    src.fill_(7)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": CAL_BYTES, "launches": 5}), flush=True)
+    return 0
+
+
+def _counter_by_kernel(db: str, counter: str) -> dict:
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, value from counters_collection where counter_name=?",
+                       (counter,)).fetchall()
+    acc = {}
+    for name, v in rows:
+        acc.setdefault(name, []).append(float(v))
+    return acc
+
+
+def traffic_from(cfg, fetch_db, write_db, cal_fetch_db, cal_write_db) -> dict:
+    """HBM bytes per launch of each kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the plain copy of CAL_BYTES bytes."""
+    def cal_factor(db, counter):
+        acc = _counter_by_kernel(db, counter)
+        # the calibration copy: the kernel with >= 5 dispatches and the largest reading
+        name = max((k for k, v in acc.items() if len(v) >= 5), key=lambda k: sum(acc[k]))
+        kib = sum(acc[name]) / len(acc[name])
+        return CAL_BYTES / (kib * 1024.0)
+    ff = cal_factor(cal_fetch_db, "FETCH_SIZE")
+    wf = cal_factor(cal_write_db, "WRITE_SIZE")
+    kb = kernel_bytes(cfg)
+    out = {}
+    for counter, db, f, field in (("FETCH_SIZE", fetch_db, ff, "fetch_bytes"),
+                                  ("WRITE_SIZE", write_db, wf, "write_bytes")):
+        for name, vals in _counter_by_kernel(db, counter).items():
+            key = _kernel_key(name)
+            if key is None:
+                continue
+            rec = out.setdefault(key, {"launches": len(vals)})
+            rec[field] = round(sum(vals) / len(vals) * 1024.0 * f)
+    for key, rec in out.items():
+        rec["hbm_bytes_per_launch"] = rec.get("fetch_bytes", 0) + rec.get("write_bytes", 0)
+        rec["algorithmic_bytes_per_launch"] = kb[key]
+        rec["ratio"] = round(rec["hbm_bytes_per_launch"] / kb[key], 4)
+    return {"workload": cfg.describe(), "source_hash": kernel_source_hash(),
+            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4), "kernels": out}
+
+
+def trace_summary(cfg, db: str) -> str:
+    """Markdown table of the library's kernels from a rocprofv3 kernel trace."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    acc = {}
+    for name, dur in con.execute("select name, duration from kernels"):
+        key = _kernel_key(name)
+        if key is not None:
+            acc.setdefault(key, []).append(dur / 1000.0)
+    kb = kernel_bytes(cfg)
+    lines = ["| kernel | launches | avg us | min us | max us | algorithmic GB/s |",
+             "|---|---|---|---|---|---|"]
+    for key in ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
+                "combine_reduce"]:
+        if key in acc:
+            v = acc[key]
+            avg = sum(v) / len(v)
+            lines.append(f"| {key} | {len(v)} | {avg:.2f} | {min(v):.2f} | {max(v):.2f} | "
+                         f"{kb[key] / (avg * 1e-6) / 1e9:.0f} |")
+    return "\n".join(lines)
+
+
 def cpu_baseline(cfg, inp, min_seconds: float) -> dict:
     """The oracle, unchanged and single-threaded, on the same workload: whole
     dispatch + combine steps until min_seconds of work (at least one)."""
@@ -114,7 +208,28 @@ def main() -> int:
     ap.add_argument("--config", default="C")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the plain copy used to scale HBM counters")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "CAL_FETCH_DB",
+                                                        "CAL_WRITE_DB"),
+                    help="write profiles/traffic_<config>.json from rocprofv3 --pmc databases")
+    ap.add_argument("--trace-summary", metavar="DB",
+                    help="print a table of the library's kernels from a rocprofv3 kernel trace")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
+    if args.traffic_from or args.trace_summary:
+        from workloads import CONFIGS
+        cfg = CONFIGS[args.config]
+        if args.trace_summary:
+            print(trace_summary(cfg, args.trace_summary))
+        if args.traffic_from:
+            rec = traffic_from(cfg, *args.traffic_from)
+            path = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
+            with open(path, "w") as f:
+                json.dump(rec, f, indent=1)
+            print(json.dumps(rec, indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the N logical ranks of the group all live on a "
               f"single device; --gpus {args.gpus} is not supported", file=sys.stderr)
