@@ -32,6 +32,7 @@ MOE_FP8_E4M3 = 1
 KERNELS = ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
            "combine_reduce"]
 MOE_KERNEL_COUNT = len(KERNELS)
+MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1
 
 
 class moe_group_desc(ctypes.Structure):
@@ -160,8 +161,19 @@ def moe_group_status(g: int, stream=None) -> int:
     return _lib.moe_group_status(g, _stream(stream))
 
 
-def moe_group_timing_enable(g: int, enable: bool) -> None:
-    _check(_lib.moe_group_timing_enable(g, int(bool(enable))), "moe_group_timing_enable")
+def moe_group_timing_enable(g: int, kernels=True) -> None:
+    """kernels: True (all), False (none), an int bit mask, or kernel names."""
+    if kernels is True:
+        mask = MOE_KERNEL_ALL
+    elif kernels is False or kernels is None:
+        mask = 0
+    elif isinstance(kernels, int):
+        mask = kernels
+    else:
+        mask = 0
+        for name in kernels:
+            mask |= 1 << KERNELS.index(name)
+    _check(_lib.moe_group_timing_enable(g, mask), "moe_group_timing_enable")
 
 
 def moe_group_timing_read(g: int) -> dict:

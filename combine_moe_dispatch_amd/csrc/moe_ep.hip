@@ -59,7 +59,7 @@ struct moe_group_s {
     State state = State::Idle;
     int32_t T = 0;
 
-    bool timing = false;
+    int timing_mask = 0;
     std::vector<EventPair> events;
     size_t events_used = 0;
 
@@ -162,29 +162,26 @@ int alloc(moe_group_s* g, T** out, size_t count)
     return MOE_OK;
 }
 
-// Run one kernel launch, bracketed by timing events when enabled.
+// Run one kernel launch; with timing enabled, a pair of events is attached to
+// the dispatch (recorded by the kernel's own start and end).  `launches` is
+// false when the call has nothing to do and enqueues no kernel.
 template <typename F>
-int timed_launch(moe_group_s* g, int kernel, hipStream_t st, F&& launch)
+int timed_launch(moe_group_s* g, int kernel, hipStream_t st, bool launches, F&& launch)
 {
-    EventPair* ev = nullptr;
-    if (g->timing) {
+    moe::Launch L{st, nullptr, nullptr};
+    if (((g->timing_mask >> kernel) & 1) && launches) {
         if (g->events_used == g->events.size()) {
             EventPair e;
             if (hipEventCreate(&e.start) != hipSuccess || hipEventCreate(&e.stop) != hipSuccess)
                 return MOE_ERR_HIP;
             g->events.push_back(e);
         }
-        ev = &g->events[g->events_used++];
+        EventPair* ev = &g->events[g->events_used++];
         ev->kernel = kernel;
-        if (hipEventRecord(ev->start, st) != hipSuccess)
-            return MOE_ERR_HIP;
+        L.start = ev->start;
+        L.stop = ev->stop;
     }
-    const hipError_t e = launch();
-    if (e != hipSuccess)
-        return MOE_ERR_HIP;
-    if (ev && hipEventRecord(ev->stop, st) != hipSuccess)
-        return MOE_ERR_HIP;
-    return MOE_OK;
+    return launch(L) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int check_device(const moe_group_s* g)
@@ -255,7 +252,8 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
         (rc = alloc(g, &p.pos, (size_t)N * T * K)) || (rc = alloc(g, &p.soff, (size_t)N * (E + 1))) ||
         (rc = alloc(g, &p.roff, (size_t)N * (N + 1))) || (rc = alloc(g, &p.rbase, (size_t)N + 1)) ||
         (rc = alloc(g, &p.eoff, (size_t)E + 1)) || (rc = alloc(g, &p.ebase, (size_t)N * E)) ||
-        (rc = alloc(g, &p.xfer_src, R)) || (rc = alloc(g, &p.shuf_map, R)) ||
+        (rc = alloc(g, &p.xfer_src, R)) || (rc = alloc(g, &p.xfer_dst, R)) ||
+        (rc = alloc(g, &p.shuf_map, R)) || (rc = alloc(g, &p.shuf_inv, R)) ||
         (rc = alloc(g, &pool_send, pool_bytes)) || (rc = alloc(g, &pool_recv, pool_bytes)) ||
         (rc = alloc(g, &g->send_meta, R)) || (rc = alloc(g, &g->recv_meta, R)) ||
         (rc = alloc(g, &g->src_rank, R)) || (rc = alloc(g, &g->src_slot, R)) ||
@@ -309,12 +307,17 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const in
         return rc;
     const moe::Shape sh = shape_of(g, num_tokens);
     const moe::Rows rows = rows_of(g);
-    if ((rc = timed_launch(g, MOE_KERNEL_ROUTE_PLAN, stream,
-                           [&] { return moe::launch_route_plan(sh, topk_idx, g->plan, stream); })) ||
-        (rc = timed_launch(g, MOE_KERNEL_PACK, stream,
-                           [&] { return moe::launch_pack(sh, x, topk_idx, g->plan, rows, stream); })) ||
-        (rc = timed_launch(g, MOE_KERNEL_TRANSFER, stream,
-                           [&] { return moe::launch_transfer(sh, g->plan, rows, stream); })))
+    const bool any = sh.rows > 0;
+    using moe::Launch;
+    if ((rc = timed_launch(g, MOE_KERNEL_ROUTE_PLAN, stream, true, [&](const Launch& L) {
+             return moe::launch_route_plan(sh, topk_idx, g->plan, L);
+         })) ||
+        (rc = timed_launch(g, MOE_KERNEL_PACK, stream, any, [&](const Launch& L) {
+             return moe::launch_pack(sh, x, topk_idx, g->plan, rows, L);
+         })) ||
+        (rc = timed_launch(g, MOE_KERNEL_TRANSFER, stream, any, [&](const Launch& L) {
+             return moe::launch_transfer(sh, g->plan, rows, L);
+         })))
         return rc;
     g->T = num_tokens;
     g->state = State::Sent;
@@ -343,9 +346,9 @@ int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale, int32_
         return rc;
     const moe::Shape sh = shape_of(g, g->T);
     const moe::Rows rows = rows_of(g);
-    if ((rc = timed_launch(g, MOE_KERNEL_SHUFFLE, stream, [&] {
+    if ((rc = timed_launch(g, MOE_KERNEL_SHUFFLE, stream, true, [&](const moe::Launch& L) {
              return moe::launch_shuffle(sh, g->plan, rows, expert_x, expert_scale, expert_offsets,
-                                        stream);
+                                        L);
          })))
         return rc;
     g->state = State::Received;
@@ -365,10 +368,13 @@ int moe_combine_send(moe_group_t g, const void* expert_y, hipStream_t stream)
         return rc;
     const moe::Shape sh = shape_of(g, g->T);
     const moe::Rows rows = rows_of(g);
-    if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_PACK, stream,
-                           [&] { return moe::launch_combine_pack(sh, g->plan, rows, expert_y, stream); })) ||
-        (rc = timed_launch(g, MOE_KERNEL_TRANSFER_BACK, stream,
-                           [&] { return moe::launch_transfer_back(sh, g->plan, rows, stream); })))
+    const bool any = sh.rows > 0;
+    if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_PACK, stream, any, [&](const moe::Launch& L) {
+             return moe::launch_combine_pack(sh, g->plan, rows, expert_y, L);
+         })) ||
+        (rc = timed_launch(g, MOE_KERNEL_TRANSFER_BACK, stream, any, [&](const moe::Launch& L) {
+             return moe::launch_transfer_back(sh, g->plan, rows, L);
+         })))
         return rc;
     g->state = State::CombineSent;
     return MOE_OK;
@@ -387,9 +393,11 @@ int moe_combine_recv(moe_group_t g, const float* topk_weights, void* out, hipStr
         return rc;
     const moe::Shape sh = shape_of(g, g->T);
     const moe::Rows rows = rows_of(g);
-    if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_REDUCE, stream, [&] {
-             return moe::launch_combine_reduce(sh, g->plan, rows, topk_weights, out, stream);
-         })))
+    if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_REDUCE, stream, sh.rows > 0,
+                           [&](const moe::Launch& L) {
+                               return moe::launch_combine_reduce(sh, g->plan, rows, topk_weights,
+                                                                 out, L);
+                           })))
         return rc;
     g->state = State::Idle;
     return MOE_OK;
@@ -450,11 +458,11 @@ int moe_group_status(moe_group_t g, hipStream_t stream)
     return MOE_OK;
 }
 
-int moe_group_timing_enable(moe_group_t g, int enable)
+int moe_group_timing_enable(moe_group_t g, int kernel_mask)
 {
-    if (!g)
+    if (!g || (kernel_mask & ~MOE_KERNEL_ALL) != 0)
         return MOE_ERR_INVALID;
-    g->timing = enable != 0;
+    g->timing_mask = kernel_mask;
     g->events_used = 0;
     return MOE_OK;
 }

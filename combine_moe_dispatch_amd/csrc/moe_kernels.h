@@ -37,7 +37,9 @@ struct Plan {              // device pointers owned by the group
     int32_t* eoff;         // [E+1]
     int32_t* ebase;        // [N][E]  first expert-order row of (sender s, expert e)
     int32_t* xfer_src;     // [rows]  receive row q <- send row xfer_src[q]
+    int32_t* xfer_dst;     // [rows]  send row -> its receive row (inverse of xfer_src)
     int2* shuf_map;        // [rows]  expert row r <- (receive row, source rank)
+    int32_t* shuf_inv;     // [rows]  receive row -> its expert row (inverse of shuf_map.x)
 };
 
 struct Rows {              // pooled row buffers
@@ -53,16 +55,25 @@ struct Rows {              // pooled row buffers
     void* comb_recv;       // combine rows, send layout (aliases recv_x storage)
 };
 
-hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, hipStream_t st);
+// Where and how a kernel is launched: the caller's stream, and optionally a
+// pair of events attached to the dispatch itself (they time the kernel
+// without adding packets to the stream).
+struct Launch {
+    hipStream_t stream;
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+
+hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, const Launch& L);
 hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const Plan& p,
-                       const Rows& r, hipStream_t st);
-hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, hipStream_t st);
+                       const Rows& r, const Launch& L);
+hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, const Launch& L);
 hipError_t launch_shuffle(const Shape& sh, const Plan& p, const Rows& r, void* expert_x,
-                          float* expert_scale, int32_t* expert_offsets, hipStream_t st);
+                          float* expert_scale, int32_t* expert_offsets, const Launch& L);
 hipError_t launch_combine_pack(const Shape& sh, const Plan& p, const Rows& r,
-                               const void* expert_y, hipStream_t st);
-hipError_t launch_transfer_back(const Shape& sh, const Plan& p, const Rows& r, hipStream_t st);
+                               const void* expert_y, const Launch& L);
+hipError_t launch_transfer_back(const Shape& sh, const Plan& p, const Rows& r, const Launch& L);
 hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, const float* w,
-                                 void* out, hipStream_t st);
+                                 void* out, const Launch& L);
 
 }  // namespace moe

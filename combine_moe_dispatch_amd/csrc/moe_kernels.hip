@@ -16,6 +16,8 @@
 // writes nothing once an invalid expert id has been seen.
 #include "moe_kernels.h"
 
+#include <hip/hip_ext.h>
+
 namespace moe {
 namespace {
 
@@ -29,6 +31,15 @@ constexpr int ROWS_PER_BLOCK = 4;          // waves per 256-thread block
 constexpr int COPY_THREADS = WAVE * ROWS_PER_BLOCK;
 
 __device__ inline int lane_id() { return threadIdx.x & (WAVE - 1); }
+
+// Every launch goes through here: with events set, they are attached to the
+// dispatch packet (hipExtLaunchKernelGGL) and time exactly this kernel.
+template <typename F, typename... Args>
+inline void go(F kernel, dim3 grid, dim3 block, size_t lds, const Launch& L, Args... args)
+{
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, L.stream, L.start, L.stop, 0u,
+                          args...);
+}
 
 // Pins loaded values in registers: an empty asm that reads and rewrites each
 // vector.  Without it the compiler sinks every load into the predicated store
@@ -417,7 +428,9 @@ __device__ inline void record_row(const Shape& sh, const Plan& p, int32_t* __res
         return;
     }
     p.xfer_src[q] = srow;
+    p.xfer_dst[srow] = q;
     p.shuf_map[r] = make_int2(q, s);
+    p.shuf_inv[q] = r;
 }
 
 template <int U, int SPLIT>
@@ -688,8 +701,9 @@ __global__ __launch_bounds__(COPY_THREADS) void shuffle_kernel(Shape sh, Plan p,
 }
 
 // Combine send ([EPMC] "Combine": the 16-bit expert outputs go back to the
-// slot each row came from; the inverse of the receive shuffle): expert row r
-// is scattered to receive-layout row shuf_map[r].x.
+// slot each row came from; the inverse of the receive shuffle).  Written as a
+// gather in destination order (measured faster than scattering the source
+// rows): receive-layout row q takes expert row shuf_inv[q].
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void combine_pack_kernel(Shape sh, Plan p,
                                                                     const v4u* __restrict__ y,
@@ -700,17 +714,18 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_pack_kernel(Shape sh, Pl
     const int lane = lane_id();
     const int n = sh.comb_vecs;
     const RowSlot rs = row_slot<SPLIT>(n);
-    const int64_t r = rs.row;
-    if (r >= sh.rows)
+    const int64_t q = rs.row;
+    if (q >= sh.rows)
         return;
-    const int64_t q = p.shuf_map[r].x;
-    if ((uint64_t)q >= (uint64_t)sh.rows)
+    const int64_t r = p.shuf_inv[q];
+    if ((uint64_t)r >= (uint64_t)sh.rows)
         return;
     copy_row<U>(comb_send + q * n + rs.b0, y + r * n + rs.b0, rs.len, lane);
 }
 
 // Combine transfer ([EFA] "Dispatch and combine": one write per peer back to
-// the token's rank): receive-layout row q returns to send row xfer_src[q].
+// the token's rank), the reverse of the dispatch transfer, as a gather in
+// destination order: send row srow takes receive-layout row xfer_dst[srow].
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, Plan p,
                                                                      const v4u* __restrict__ comb_send,
@@ -721,11 +736,11 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, P
     const int lane = lane_id();
     const int n = sh.comb_vecs;
     const RowSlot rs = row_slot<SPLIT>(n);
-    const int64_t q = rs.row;
-    if (q >= sh.rows)
+    const int64_t srow = rs.row;
+    if (srow >= sh.rows)
         return;
-    const int64_t srow = p.xfer_src[q];
-    if ((uint64_t)srow >= (uint64_t)sh.rows)
+    const int64_t q = p.xfer_dst[srow];
+    if ((uint64_t)q >= (uint64_t)sh.rows)
         return;
     copy_row<U>(comb_recv + srow * n + rs.b0, comb_send + q * n + rs.b0, rs.len, lane);
 }
@@ -866,24 +881,24 @@ inline unsigned row_blocks(int64_t rows, int split)
     do {                                                                                           \
         const dim3 grid_(row_blocks((GRID_ROWS), (rsh).split)), block_(COPY_THREADS);              \
         if ((rsh).split == 1 && (rsh).u == 1)                                                      \
-            hipLaunchKernelGGL((KERNEL<1, 1>), grid_, block_, 0, __VA_ARGS__);                     \
+            go((KERNEL<1, 1>), grid_, block_, 0, __VA_ARGS__);                     \
         else if ((rsh).split == 1 && (rsh).u == 2)                                                 \
-            hipLaunchKernelGGL((KERNEL<2, 1>), grid_, block_, 0, __VA_ARGS__);                     \
+            go((KERNEL<2, 1>), grid_, block_, 0, __VA_ARGS__);                     \
         else if ((rsh).split == 1)                                                                 \
-            hipLaunchKernelGGL((KERNEL<4, 1>), grid_, block_, 0, __VA_ARGS__);                     \
+            go((KERNEL<4, 1>), grid_, block_, 0, __VA_ARGS__);                     \
         else if ((rsh).split == 2)                                                                 \
-            hipLaunchKernelGGL((KERNEL<4, 2>), grid_, block_, 0, __VA_ARGS__);                     \
+            go((KERNEL<4, 2>), grid_, block_, 0, __VA_ARGS__);                     \
         else if ((rsh).u == 4)                                                                     \
-            hipLaunchKernelGGL((KERNEL<4, 4>), grid_, block_, 0, __VA_ARGS__);                     \
+            go((KERNEL<4, 4>), grid_, block_, 0, __VA_ARGS__);                     \
         else if ((rsh).u == 8)                                                                     \
-            hipLaunchKernelGGL((KERNEL<8, 4>), grid_, block_, 0, __VA_ARGS__);                     \
+            go((KERNEL<8, 4>), grid_, block_, 0, __VA_ARGS__);                     \
         else                                                                                       \
-            hipLaunchKernelGGL((KERNEL<16, 4>), grid_, block_, 0, __VA_ARGS__);                    \
+            go((KERNEL<16, 4>), grid_, block_, 0, __VA_ARGS__);                    \
     } while (0)
 
 }  // namespace
 
-hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, hipStream_t st)
+hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, const Launch& L)
 {
     RouteArgs ra;
     ra.idx = idx;
@@ -898,12 +913,12 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     ra.chunk_waves = sh.E <= 256 ? RP_WAVES : sh.E <= 512 ? RP_WAVES / 2 : RP_WAVES / 4;
     const size_t lds = 2 * (size_t)ra.chunk_waves * sh.E * sizeof(uint64_t) +
                        (size_t)2 * sh.E * sizeof(int32_t);
-    hipLaunchKernelGGL(route_plan_kernel, dim3(sh.N), dim3(RP_NT), lds, st, ra, p);
+    go(route_plan_kernel, dim3(sh.N), dim3(RP_NT), lds, L, ra, p);
     return hipGetLastError();
 }
 
 hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const Plan& p,
-                       const Rows& r, hipStream_t st)
+                       const Rows& r, const Launch& L)
 {
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
@@ -914,50 +929,50 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
         RowShape rsh = row_shape(sh.H / 8);
         if (rsh.u > 8)
             rsh.u = 8;
-        MOE_DISPATCH_ROW(rsh, pack_fp8_kernel, tokens, st, sh, p, (const v4u*)x, idx,
+        MOE_DISPATCH_ROW(rsh, pack_fp8_kernel, tokens, L, sh, p, (const v4u*)x, idx,
                          (v2u*)r.send_x, r.send_scale, r.send_meta);
     } else {
-        MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), pack_bf16_kernel, tokens, st, sh, p,
+        MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), pack_bf16_kernel, tokens, L, sh, p,
                          (const v4u*)x, idx, (v4u*)r.send_x, r.send_meta);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, hipStream_t st)
+hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, const Launch& L)
 {
     if (sh.rows == 0)
         return hipSuccess;
-    MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), transfer_kernel, sh.rows, st, sh, p,
+    MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), transfer_kernel, sh.rows, L, sh, p,
                      (const v4u*)r.send_x, (v4u*)r.recv_x, r.send_scale, r.recv_scale,
                      r.send_meta, r.recv_meta);
     return hipGetLastError();
 }
 
 hipError_t launch_shuffle(const Shape& sh, const Plan& p, const Rows& r, void* expert_x,
-                          float* expert_scale, int32_t* expert_offsets, hipStream_t st)
+                          float* expert_scale, int32_t* expert_offsets, const Launch& L)
 {
     // launched even with no rows: block 0 publishes the expert offsets
-    MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), shuffle_kernel, sh.rows, st, sh, p,
+    MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), shuffle_kernel, sh.rows, L, sh, p,
                      (const v4u*)r.recv_x, r.recv_scale, r.recv_meta, (v4u*)expert_x,
                      expert_scale, r.src_rank, r.src_slot, expert_offsets);
     return hipGetLastError();
 }
 
 hipError_t launch_combine_pack(const Shape& sh, const Plan& p, const Rows& r, const void* y,
-                               hipStream_t st)
+                               const Launch& L)
 {
     if (sh.rows == 0)
         return hipSuccess;
-    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), combine_pack_kernel, sh.rows, st, sh, p,
+    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), combine_pack_kernel, sh.rows, L, sh, p,
                      (const v4u*)y, (v4u*)r.comb_send);
     return hipGetLastError();
 }
 
-hipError_t launch_transfer_back(const Shape& sh, const Plan& p, const Rows& r, hipStream_t st)
+hipError_t launch_transfer_back(const Shape& sh, const Plan& p, const Rows& r, const Launch& L)
 {
     if (sh.rows == 0)
         return hipSuccess;
-    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), transfer_back_kernel, sh.rows, st, sh, p,
+    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), transfer_back_kernel, sh.rows, L, sh, p,
                      (const v4u*)r.comb_send, (v4u*)r.comb_recv);
     return hipGetLastError();
 }
@@ -966,20 +981,20 @@ hipError_t launch_transfer_back(const Shape& sh, const Plan& p, const Rows& r, h
 // else 2; rows are split across waves as for the movers.
 template <int KT, int U>
 static void launch_reduce_k(const Shape& sh, const Plan& p, const v4u* cr, const float* w, v4u* o,
-                            int64_t tokens, hipStream_t st)
+                            int64_t tokens, const Launch& L)
 {
     const int split = row_shape(sh.comb_vecs).split;
     const dim3 grid(row_blocks(tokens, split)), block(COPY_THREADS);
     if (split == 1)
-        hipLaunchKernelGGL((combine_reduce_kernel<KT, U, 1>), grid, block, 0, st, sh, p, cr, w, o);
+        go((combine_reduce_kernel<KT, U, 1>), grid, block, 0, L, sh, p, cr, w, o);
     else if (split == 2)
-        hipLaunchKernelGGL((combine_reduce_kernel<KT, U, 2>), grid, block, 0, st, sh, p, cr, w, o);
+        go((combine_reduce_kernel<KT, U, 2>), grid, block, 0, L, sh, p, cr, w, o);
     else
-        hipLaunchKernelGGL((combine_reduce_kernel<KT, U, 4>), grid, block, 0, st, sh, p, cr, w, o);
+        go((combine_reduce_kernel<KT, U, 4>), grid, block, 0, L, sh, p, cr, w, o);
 }
 
 hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, const float* w,
-                                 void* out, hipStream_t st)
+                                 void* out, const Launch& L)
 {
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
@@ -987,12 +1002,12 @@ hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, 
     const v4u* cr = (const v4u*)r.comb_recv;
     v4u* o = (v4u*)out;
     switch (sh.K) {
-    case 1: launch_reduce_k<1, 4>(sh, p, cr, w, o, tokens, st); break;
-    case 2: launch_reduce_k<2, 4>(sh, p, cr, w, o, tokens, st); break;
-    case 4: launch_reduce_k<4, 2>(sh, p, cr, w, o, tokens, st); break;
-    case 6: launch_reduce_k<6, 2>(sh, p, cr, w, o, tokens, st); break;
-    case 8: launch_reduce_k<8, 2>(sh, p, cr, w, o, tokens, st); break;
-    default: launch_reduce_k<0, 2>(sh, p, cr, w, o, tokens, st); break;
+    case 1: launch_reduce_k<1, 4>(sh, p, cr, w, o, tokens, L); break;
+    case 2: launch_reduce_k<2, 4>(sh, p, cr, w, o, tokens, L); break;
+    case 4: launch_reduce_k<4, 2>(sh, p, cr, w, o, tokens, L); break;
+    case 6: launch_reduce_k<6, 2>(sh, p, cr, w, o, tokens, L); break;
+    case 8: launch_reduce_k<8, 2>(sh, p, cr, w, o, tokens, L); break;
+    default: launch_reduce_k<0, 2>(sh, p, cr, w, o, tokens, L); break;
     }
     return hipGetLastError();
 }

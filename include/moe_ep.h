@@ -173,9 +173,12 @@ int moe_group_view_get(moe_group_t g, moe_group_view* out);
  * of precedence when several bits are set). */
 int moe_group_status(moe_group_t g, hipStream_t stream);
 
-/* Per-kernel timing with HIP events recorded on the launch stream around each
- * kernel, for measurement.  While enabled, every launch is bracketed; reading
- * synchronises on the recorded events, returns the summed milliseconds and
+/* Per-kernel timing, for measurement.  kernel_mask selects the kernels to
+ * time (bit k = moe_kernel_id k; 0 = off; MOE_KERNEL_ALL = every kernel).  A
+ * timed launch carries a pair of HIP events attached to its dispatch
+ * (recorded at the kernel's start and end on the launch stream); each timed
+ * kernel costs a few microseconds of extra gap, so time only what is needed.
+ * Reading synchronises on the events, returns the summed milliseconds and
  * launch counts per kernel (arrays of MOE_KERNEL_COUNT) and resets them. */
 typedef enum moe_kernel_id {
     MOE_KERNEL_ROUTE_PLAN = 0,      /* counts, stable positions, all offsets */
@@ -188,7 +191,9 @@ typedef enum moe_kernel_id {
     MOE_KERNEL_COUNT = 7
 } moe_kernel_id;
 
-int moe_group_timing_enable(moe_group_t g, int enable);
+typedef enum moe_kernel_mask { MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1 } moe_kernel_mask;
+
+int moe_group_timing_enable(moe_group_t g, int kernel_mask);
 int moe_group_timing_read(moe_group_t g, double* total_ms, int64_t* launches);
 
 /* Static description of a status code; never NULL. */

@@ -57,4 +57,6 @@ def test_host_validation_without_gpu(lib):
         assert ei.value.status == mep.MOE_ERR_INVALID
     # a null group handle is rejected by every call
     assert lib.moe_dispatch_send(None, 1, None, None, None) == mep.MOE_ERR_INVALID
+    assert lib.moe_group_timing_enable(None, 1) == mep.MOE_ERR_INVALID
+    assert lib.moe_group_status(None, None) == mep.MOE_ERR_INVALID
     assert lib.moe_group_destroy(None) == 0

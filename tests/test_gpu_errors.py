@@ -96,3 +96,26 @@ def test_create_rejects_bad_descriptors():
         with pytest.raises(mep.MoeError) as ei:
             mep.moe_group_create(*args)
         assert ei.value.status == mep.MOE_ERR_INVALID, args
+
+
+def test_kernel_timing_mask():
+    """Timing events attach only to the selected kernels; a cycle with every
+    kernel selected reports one launch of each (T > 0)."""
+    cfg = CONFIGS["A"]
+    say(f"[gpu] timing mask {cfg.describe()}")
+    inp = make_inputs(cfg)
+    g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16)
+    try:
+        mep.moe_group_timing_enable(g, True)
+        run_cycle(torch, mep, cfg, inp, group=g, want_rows=False)
+        t = mep.moe_group_timing_read(g)
+        assert all(n == 1 and ms > 0 for ms, n in t.values()), t
+        mep.moe_group_timing_enable(g, ["transfer", "combine_reduce"])
+        run_cycle(torch, mep, cfg, inp, group=g, want_rows=False)
+        t = mep.moe_group_timing_read(g)
+        assert {k for k, (ms, n) in t.items() if n} == {"transfer", "combine_reduce"}, t
+        mep.moe_group_timing_enable(g, False)
+        with pytest.raises(mep.MoeError):
+            mep.moe_group_timing_enable(g, 1 << 12)
+    finally:
+        mep.moe_group_destroy(g)
