@@ -32,7 +32,7 @@ METRIC = "µs per dispatch+combine and achieved HBM GB/s (% of peak), DeepSeek-R
 HBM_PEAK_GBPS = 8000.0
 
 
-def kernel_bytes(cfg) -> dict:
+def kernel_bytes(cfg, transport: str = "staged") -> dict:
     """Algorithmic HBM bytes per launch of each kernel: every buffer the method
     mandates is written once and read once by the next stage; inputs are read
     once per token.  The int32 row maps the pack kernel writes for the later
@@ -45,7 +45,7 @@ def kernel_bytes(cfg) -> dict:
     sb = (H // 128) * 4 if fp8 else 0            # block scales per row
     hy = 2 * H                                   # combine row
     tokens = N * T
-    return {
+    kb = {
         # idx in; counts, send offsets, positions out; then the group offsets
         # (counts and send offsets in; receive/expert offsets and bases out)
         "route_plan": (R * 4 + N * E * 4 + N * (E + 1) * 4 + R * 4
@@ -58,6 +58,13 @@ def kernel_bytes(cfg) -> dict:
         "transfer_back": 2 * R * hy,
         "combine_reduce": R * hy + R * 8 + tokens * H * 2,
     }
+    if transport == "direct":
+        # pack writes the receive rows itself and combine writes the return
+        # rows itself: no transfer passes
+        for k in ("transfer", "combine_pack", "transfer_back"):
+            del kb[k]
+        kb["combine_push"] = 2 * R * hy
+    return kb
 
 
 def kernel_source_hash() -> str:
@@ -88,6 +95,7 @@ def measured_traffic(config_key: str, kernel: str, src_hash: str):
 
 CAL_BYTES = 469_762_048        # one plain device copy of this many bytes each way
 KERNEL_OF = [("route_plan_kernel", "route_plan"), ("pack_bf16_kernel", "pack"),
+             ("combine_push_kernel", "combine_push"),
              ("pack_fp8_kernel", "pack"), ("transfer_back_kernel", "transfer_back"),
              ("transfer_kernel", "transfer"), ("shuffle_kernel", "shuffle"),
              ("combine_pack_kernel", "combine_pack"),
@@ -126,7 +134,7 @@ def _counter_by_kernel(db: str, counter: str) -> dict:
     return acc
 
 
-def traffic_from(cfg, fetch_db, write_db, cal_fetch_db, cal_write_db) -> dict:
+def traffic_from(cfg, fetch_db, write_db, cal_fetch_db, cal_write_db, transport="staged") -> dict:
     """HBM bytes per launch of each kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
     counter reads for the plain copy of CAL_BYTES bytes."""
@@ -138,7 +146,7 @@ def traffic_from(cfg, fetch_db, write_db, cal_fetch_db, cal_write_db) -> dict:
         return CAL_BYTES / (kib * 1024.0)
     ff = cal_factor(cal_fetch_db, "FETCH_SIZE")
     wf = cal_factor(cal_write_db, "WRITE_SIZE")
-    kb = kernel_bytes(cfg)
+    kb = kernel_bytes(cfg, transport)
     out = {}
     for counter, db, f, field in (("FETCH_SIZE", fetch_db, ff, "fetch_bytes"),
                                   ("WRITE_SIZE", write_db, wf, "write_bytes")):
@@ -168,8 +176,10 @@ def trace_summary(cfg, db: str) -> str:
     kb = kernel_bytes(cfg)
     lines = ["| kernel | launches | avg us | min us | max us | algorithmic GB/s |",
              "|---|---|---|---|---|---|"]
+    if "combine_push" in acc:
+        kb = kernel_bytes(cfg, "direct")
     for key in ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
-                "combine_reduce"]:
+                "combine_push", "combine_reduce"]:
         if key in acc:
             v = acc[key]
             avg = sum(v) / len(v)
@@ -209,6 +219,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C")
+    ap.add_argument("--transport", choices=["staged", "direct"], default="staged",
+                    help="staged: send buffer + modelled transfer (the measured contract); "
+                         "direct: pack/combine write the peer's rows")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -229,8 +242,9 @@ def main() -> int:
         if args.trace_summary:
             print(trace_summary(cfg, args.trace_summary))
         if args.traffic_from:
-            rec = traffic_from(cfg, *args.traffic_from)
-            path = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
+            rec = traffic_from(cfg, *args.traffic_from, transport=args.transport)
+            suffix = "" if args.transport == "staged" else "_direct"
+            path = os.path.join(ROOT, "profiles", f"traffic_{args.config}{suffix}.json")
             with open(path, "w") as f:
                 json.dump(rec, f, indent=1)
             print(json.dumps(rec, indent=1))
@@ -262,7 +276,8 @@ def main() -> int:
     expert_scale = torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None
     offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
     out = torch.empty((N, T, H), dtype=torch.bfloat16, device=dev)
-    g = mep.moe_group_create(N, E, K, H, T, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16)
+    transport = mep.MOE_TRANSPORT_DIRECT if args.transport == "direct" else mep.MOE_TRANSPORT_STAGED
+    g = mep.moe_group_create(N, E, K, H, T, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16, transport)
     stream = torch.cuda.current_stream()
 
     # first cycle + the stand-in expert output reused by every step
@@ -313,7 +328,7 @@ def main() -> int:
     mep.moe_group_destroy(g)
 
     ms_per_step = (t1 - t0) / args.steps * 1e3
-    kb = kernel_bytes(cfg)
+    kb = kernel_bytes(cfg, args.transport)
     total_bytes = sum(kb.values())
     kern = {}
     for name, (ms, n) in timing_all.items():
@@ -325,7 +340,8 @@ def main() -> int:
     dom_us = dom_ms / dom_n * 1e3
     ach = kb[dom] / (dom_us * 1e-6) / 1e9
     src_hash = kernel_source_hash()
-    traffic = measured_traffic(args.config, dom, src_hash)
+    traffic = measured_traffic(args.config + ("" if args.transport == "staged" else "_direct"),
+                               dom, src_hash)
     gbps_eff = total_bytes / (ms_per_step * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
@@ -343,6 +359,7 @@ def main() -> int:
         "config": {"workload": cfg.describe(), "logical_ranks": N, "tokens_per_rank": T,
                    "hidden": H, "experts": E, "top_k": K, "rows": R,
                    "dispatch_dtype": cfg.dtype, "combine_dtype": "bf16",
+                   "transport": args.transport,
                    "parallelism": f"ep{N} (logical ranks on one GPU)"},
         "hbm_gbps_eff": round(gbps_eff, 1),
         "frac_of_hbm_peak": round(gbps_eff / HBM_PEAK_GBPS, 4),

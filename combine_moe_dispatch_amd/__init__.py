@@ -29,8 +29,11 @@ MOE_ERR_INTERNAL = -7
 MOE_BF16 = 0
 MOE_FP8_E4M3 = 1
 
+MOE_TRANSPORT_STAGED = 0
+MOE_TRANSPORT_DIRECT = 1
+
 KERNELS = ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
-           "combine_reduce"]
+           "combine_reduce", "combine_push"]
 MOE_KERNEL_COUNT = len(KERNELS)
 MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1
 
@@ -38,7 +41,8 @@ MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1
 class moe_group_desc(ctypes.Structure):
     _fields_ = [("num_ranks", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("hidden", ctypes.c_int32),
-                ("max_tokens", ctypes.c_int32), ("dispatch_dtype", ctypes.c_int32)]
+                ("max_tokens", ctypes.c_int32), ("dispatch_dtype", ctypes.c_int32),
+                ("transport", ctypes.c_int32)]
 
 
 class moe_group_view(ctypes.Structure):
@@ -120,8 +124,10 @@ def strerror(status: int) -> str:
 
 
 def moe_group_create(num_ranks: int, num_experts: int, top_k: int, hidden: int,
-                     max_tokens: int, dispatch_dtype: int = MOE_BF16) -> int:
-    desc = moe_group_desc(num_ranks, num_experts, top_k, hidden, max_tokens, dispatch_dtype)
+                     max_tokens: int, dispatch_dtype: int = MOE_BF16,
+                     transport: int = MOE_TRANSPORT_STAGED) -> int:
+    desc = moe_group_desc(num_ranks, num_experts, top_k, hidden, max_tokens, dispatch_dtype,
+                          transport)
     h = ctypes.c_void_p()
     _check(_lib.moe_group_create(ctypes.byref(desc), ctypes.byref(h)), "moe_group_create")
     return h.value

@@ -70,7 +70,7 @@ namespace {
 
 const char* const kKernelNames[MOE_KERNEL_COUNT] = {
     "route_plan_kernel",   "pack_kernel",          "transfer_kernel",       "shuffle_kernel",
-    "combine_pack_kernel", "transfer_back_kernel", "combine_reduce_kernel",
+    "combine_pack_kernel", "transfer_back_kernel", "combine_reduce_kernel", "combine_push_kernel",
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -96,6 +96,8 @@ int validate_desc(const moe_group_desc* d)
         return MOE_ERR_INVALID;
     if (d->max_tokens < 0)
         return MOE_ERR_INVALID;
+    if (d->transport != MOE_TRANSPORT_STAGED && d->transport != MOE_TRANSPORT_DIRECT)
+        return MOE_ERR_INVALID;
     const int64_t rows = (int64_t)d->num_ranks * d->max_tokens * d->top_k;
     if (rows >= ((int64_t)1 << 31))
         return MOE_ERR_INVALID;
@@ -112,6 +114,7 @@ moe::Shape shape_of(const moe_group_s* g, int T)
     sh.H = g->desc.hidden;
     sh.T = T;
     sh.fp8 = g->desc.dispatch_dtype == MOE_FP8_E4M3;
+    sh.direct = g->desc.transport == MOE_TRANSPORT_DIRECT;
     sh.rows = (int64_t)sh.N * T * sh.K;
     sh.payload_vecs = g->payload_bytes / 16;
     sh.comb_vecs = g->comb_bytes / 16;
@@ -243,6 +246,7 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
     g->scale_blocks = fp8 ? H / 128 : 0;
     const size_t R = (size_t)g->rows_max;
     const size_t pool_bytes = R * (size_t)std::max(g->payload_bytes, g->comb_bytes);
+    const bool staged = desc->transport == MOE_TRANSPORT_STAGED;   // direct: no send buffer
 
     moe::Plan& p = g->plan;
     uint8_t* pool_send = nullptr;
@@ -254,11 +258,11 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
         (rc = alloc(g, &p.eoff, (size_t)E + 1)) || (rc = alloc(g, &p.ebase, (size_t)N * E)) ||
         (rc = alloc(g, &p.xfer_src, R)) || (rc = alloc(g, &p.xfer_dst, R)) ||
         (rc = alloc(g, &p.shuf_map, R)) || (rc = alloc(g, &p.shuf_inv, R)) ||
-        (rc = alloc(g, &pool_send, pool_bytes)) || (rc = alloc(g, &pool_recv, pool_bytes)) ||
-        (rc = alloc(g, &g->send_meta, R)) || (rc = alloc(g, &g->recv_meta, R)) ||
+        (staged && (rc = alloc(g, &pool_send, pool_bytes))) || (rc = alloc(g, &pool_recv, pool_bytes)) ||
+        (staged && (rc = alloc(g, &g->send_meta, R))) || (rc = alloc(g, &g->recv_meta, R)) ||
         (rc = alloc(g, &g->src_rank, R)) || (rc = alloc(g, &g->src_slot, R)) ||
-        (fp8 && ((rc = alloc(g, &g->send_scale, R * g->scale_blocks)) ||
-                 (rc = alloc(g, &g->recv_scale, R * g->scale_blocks))))) {
+        (fp8 && staged && (rc = alloc(g, &g->send_scale, R * g->scale_blocks))) ||
+        (fp8 && (rc = alloc(g, &g->recv_scale, R * g->scale_blocks)))) {
         free_all(g);
         delete g;
         return rc;
@@ -315,9 +319,9 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const in
         (rc = timed_launch(g, MOE_KERNEL_PACK, stream, any, [&](const Launch& L) {
              return moe::launch_pack(sh, x, topk_idx, g->plan, rows, L);
          })) ||
-        (rc = timed_launch(g, MOE_KERNEL_TRANSFER, stream, any, [&](const Launch& L) {
+        (!sh.direct && (rc = timed_launch(g, MOE_KERNEL_TRANSFER, stream, any, [&](const Launch& L) {
              return moe::launch_transfer(sh, g->plan, rows, L);
-         })))
+         }))))
         return rc;
     g->T = num_tokens;
     g->state = State::Sent;
@@ -369,13 +373,19 @@ int moe_combine_send(moe_group_t g, const void* expert_y, hipStream_t stream)
     const moe::Shape sh = shape_of(g, g->T);
     const moe::Rows rows = rows_of(g);
     const bool any = sh.rows > 0;
-    if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_PACK, stream, any, [&](const moe::Launch& L) {
-             return moe::launch_combine_pack(sh, g->plan, rows, expert_y, L);
-         })) ||
-        (rc = timed_launch(g, MOE_KERNEL_TRANSFER_BACK, stream, any, [&](const moe::Launch& L) {
-             return moe::launch_transfer_back(sh, g->plan, rows, L);
-         })))
+    if (sh.direct) {
+        if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_PUSH, stream, any, [&](const moe::Launch& L) {
+                 return moe::launch_combine_push(sh, g->plan, rows, expert_y, L);
+             })))
+            return rc;
+    } else if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_PACK, stream, any, [&](const moe::Launch& L) {
+                    return moe::launch_combine_pack(sh, g->plan, rows, expert_y, L);
+                })) ||
+               (rc = timed_launch(g, MOE_KERNEL_TRANSFER_BACK, stream, any, [&](const moe::Launch& L) {
+                    return moe::launch_transfer_back(sh, g->plan, rows, L);
+                }))) {
         return rc;
+    }
     g->state = State::CombineSent;
     return MOE_OK;
 }

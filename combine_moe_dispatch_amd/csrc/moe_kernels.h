@@ -20,6 +20,7 @@ constexpr int MAX_TOPK = 64;
 struct Shape {
     int N, E, K, L, H, T;
     int fp8;              // payload is e4m3 + fp32 block scales
+    int direct;           // direct transport: pack and combine write the peer's rows
     int64_t rows;         // N*T*K
     int payload_vecs;     // 16-byte vectors per payload row (2H/16 or H/16)
     int comb_vecs;        // 16-byte vectors per combine row (2H/16)
@@ -73,6 +74,8 @@ hipError_t launch_shuffle(const Shape& sh, const Plan& p, const Rows& r, void* e
 hipError_t launch_combine_pack(const Shape& sh, const Plan& p, const Rows& r,
                                const void* expert_y, const Launch& L);
 hipError_t launch_transfer_back(const Shape& sh, const Plan& p, const Rows& r, const Launch& L);
+hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r,
+                               const void* expert_y, const Launch& L);
 hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, const float* w,
                                  void* out, const Launch& L);
 

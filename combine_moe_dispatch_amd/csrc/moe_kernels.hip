@@ -400,45 +400,80 @@ __device__ inline RowSlot row_slot(int n)
 }
 
 // ---------------------------------------------------------------------------
-// Pack: one wave per token.
+// Pack: one token per wave (or per SPLIT waves).
 //
 // [EPMC] "Dispatch": activations, block scales and the token's index on the
 // sending rank are packed contiguously; [EFA] "Dispatch and combine": with the
 // offsets known, rows are packed into contiguous per-peer send buffers.  The
-// token row is read once and written K times (one per routed expert).  Lanes
-// k < K also record, for row (s, t, k), where the transfer and the receive
-// shuffle will move it:
-//   receive row q  = rbase[d] + roff[d][s] + pos - soff[s][d*L]   (d = e / L)
-//   expert row r   = ebase[s][e] + pos - soff[s][e]
+// token row is read once and written K times (one per routed expert).  For
+// row (s, t, k) lanes k < K work out where it goes:
+//   send row       srow = s*T*K + pos
+//   receive row    q    = rbase[d] + roff[d][s] + pos - soff[s][d*L]   (d = e / L)
+//   expert row     r    = ebase[s][e] + pos - soff[s][e]
+// and the lead wave records the row maps the movers follow.  With the staged
+// transport the rows go to the send buffer (row srow) and the transfer kernel
+// moves them; with the direct transport they are pushed straight into the
+// receive buffer (row q), as the pages push intra-node tokens into peers'
+// buffers ([EFA] "Dispatch and combine").
 // ---------------------------------------------------------------------------
-__device__ inline void record_row(const Shape& sh, const Plan& p, int32_t* __restrict__ send_meta,
-                                  int s, int t, int k, int e, int pk)
+struct RowDest {
+    int32_t srow, q, r;
+    bool ok;
+};
+
+__device__ inline RowDest row_dest(const Shape& sh, const Plan& p, int s, int e, int pk)
 {
     const int64_t TK = (int64_t)sh.T * sh.K;
-    const int32_t srow = (int32_t)(s * TK + pk);
-    if ((uint64_t)pk < (uint64_t)TK)
-        send_meta[srow] = t * sh.K + k;
+    RowDest rd;
+    rd.srow = (int32_t)(s * TK + pk);
     const int d = e / sh.L;
     const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
-    const int32_t q = p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + pk - so[d * sh.L];
-    const int32_t r = p.ebase[(size_t)s * sh.E + e] + pk - so[e];
-    if ((uint64_t)q >= (uint64_t)sh.rows || (uint64_t)r >= (uint64_t)sh.rows ||
-        (uint64_t)pk >= (uint64_t)TK) {
-        atomicOr(p.err, ERR_BIT_INTERNAL);
-        return;
+    rd.q = p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + pk - so[d * sh.L];
+    rd.r = p.ebase[(size_t)s * sh.E + e] + pk - so[e];
+    rd.ok = (uint64_t)rd.q < (uint64_t)sh.rows && (uint64_t)rd.r < (uint64_t)sh.rows &&
+            (uint64_t)pk < (uint64_t)TK;
+    return rd;
+}
+
+__device__ inline void record_maps(const Plan& p, const RowDest& rd, int s)
+{
+    p.xfer_src[rd.q] = rd.srow;
+    p.xfer_dst[rd.srow] = rd.q;
+    p.shuf_map[rd.r] = make_int2(rd.q, s);
+    p.shuf_inv[rd.q] = rd.r;
+}
+
+// Lanes k < K: the destination row of (token, k) in the buffer pack writes
+// (send row, or receive row when direct), -1 if an index check failed; the
+// lead wave also writes the maps and the meta word t*K+k.
+__device__ inline int pack_dest(const Shape& sh, const Plan& p, const int32_t* __restrict__ idx,
+                                int32_t* __restrict__ dst_meta, int64_t tok, int s, int t,
+                                bool lead)
+{
+    const int lane = lane_id();
+    int row = -1;
+    if (lane < sh.K) {
+        const int64_t i = tok * sh.K + lane;
+        const RowDest rd = row_dest(sh, p, s, idx[i], p.pos[i]);
+        if (rd.ok) {
+            row = sh.direct ? rd.q : rd.srow;
+            if (lead) {
+                record_maps(p, rd, s);
+                dst_meta[row] = t * sh.K + lane;
+            }
+        } else if (lead) {
+            atomicOr(p.err, ERR_BIT_INTERNAL);
+        }
     }
-    p.xfer_src[q] = srow;
-    p.xfer_dst[srow] = q;
-    p.shuf_map[r] = make_int2(q, s);
-    p.shuf_inv[q] = r;
+    return row;
 }
 
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan p,
                                                                  const v4u* __restrict__ x,
                                                                  const int32_t* __restrict__ idx,
-                                                                 v4u* __restrict__ send_x,
-                                                                 int32_t* __restrict__ send_meta)
+                                                                 v4u* __restrict__ dst_x,
+                                                                 int32_t* __restrict__ dst_meta)
 {
     if (*p.err)
         return;
@@ -449,14 +484,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan 
     if (tok >= (int64_t)sh.N * sh.T)
         return;
     const int s = (int)(tok / sh.T), t = (int)(tok % sh.T);
-    const int64_t TK = (int64_t)sh.T * sh.K;
-    int my_p = 0;
-    if (lane < sh.K) {
-        const int64_t i = tok * sh.K + lane;
-        my_p = p.pos[i];
-        if (rs.lead)
-            record_row(sh, p, send_meta, s, t, lane, idx[i], my_p);
-    }
+    const int my_row = pack_dest(sh, p, idx, dst_meta, tok, s, t, rs.lead);
     const v4u* src = x + tok * n + rs.b0;
     for (int base = 0; base < rs.len; base += WAVE * U) {
         // the caller's tokens are read with ordinary loads (measured faster
@@ -467,10 +495,10 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan 
             v[u] = src[min(base + u * WAVE + lane, rs.len - 1)];
         hold(v);
         for (int k = 0; k < sh.K; ++k) {
-            const int pk = readlane(my_p, k);
-            if ((unsigned)pk >= (unsigned)TK)
+            const int row = readlane(my_row, k);
+            if ((uint64_t)row >= (uint64_t)sh.rows)
                 continue;
-            v4u* dst = send_x + (s * TK + pk) * n + rs.b0;
+            v4u* dst = dst_x + (int64_t)row * n + rs.b0;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = base + u * WAVE + lane;
@@ -516,9 +544,9 @@ template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p,
                                                                 const v4u* __restrict__ x,
                                                                 const int32_t* __restrict__ idx,
-                                                                v2u* __restrict__ send_q,
-                                                                float* __restrict__ send_scale,
-                                                                int32_t* __restrict__ send_meta)
+                                                                v2u* __restrict__ dst_q,
+                                                                float* __restrict__ dst_scale,
+                                                                int32_t* __restrict__ dst_meta)
 {
     if (*p.err)
         return;
@@ -529,14 +557,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
     if (tok >= (int64_t)sh.N * sh.T)
         return;
     const int s = (int)(tok / sh.T), t = (int)(tok % sh.T);
-    const int64_t TK = (int64_t)sh.T * sh.K;
-    int my_p = 0;
-    if (lane < sh.K) {
-        const int64_t i = tok * sh.K + lane;
-        my_p = p.pos[i];
-        if (rs.lead)
-            record_row(sh, p, send_meta, s, t, lane, idx[i], my_p);
-    }
+    const int my_row = pack_dest(sh, p, idx, dst_meta, tok, s, t, rs.lead);
     const int nb = sh.scale_blocks;
     const v4u* src = x + tok * n;
     for (int base = rs.b0; base < rs.b0 + rs.len; base += WAVE * U) {
@@ -582,17 +603,17 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
             sc[u] = scale;
         }
         for (int k = 0; k < sh.K; ++k) {
-            const int pk = readlane(my_p, k);
-            if ((unsigned)pk >= (unsigned)TK)
+            const int row32 = readlane(my_row, k);
+            if ((uint64_t)row32 >= (uint64_t)sh.rows)
                 continue;
-            const int64_t row = s * TK + pk;
+            const int64_t row = row32;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = base + u * WAVE + lane;
                 if (j < end) {
-                    st_nt(q[u], send_q + row * n + j);
+                    st_nt(q[u], dst_q + row * n + j);
                     if ((lane & 15) == 0)
-                        send_scale[row * nb + j / 16] = sc[u];
+                        dst_scale[row * nb + j / 16] = sc[u];
                 }
             }
         }
@@ -743,6 +764,32 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, P
     if ((uint64_t)q >= (uint64_t)sh.rows)
         return;
     copy_row<U>(comb_recv + srow * n + rs.b0, comb_send + q * n + rs.b0, rs.len, lane);
+}
+
+// Combine with the direct transport: the expert output goes straight back
+// into the token owner's return rows (send layout), the inverse of the direct
+// pack.  Gather in destination order: send row srow takes expert row
+// shuf_inv[xfer_dst[srow]].
+template <int U, int SPLIT>
+__global__ __launch_bounds__(COPY_THREADS) void combine_push_kernel(Shape sh, Plan p,
+                                                                    const v4u* __restrict__ y,
+                                                                    v4u* __restrict__ comb_recv)
+{
+    if (*p.err)
+        return;
+    const int lane = lane_id();
+    const int n = sh.comb_vecs;
+    const RowSlot rs = row_slot<SPLIT>(n);
+    const int64_t srow = rs.row;
+    if (srow >= sh.rows)
+        return;
+    const int64_t q = p.xfer_dst[srow];
+    if ((uint64_t)q >= (uint64_t)sh.rows)
+        return;
+    const int64_t r = p.shuf_inv[q];
+    if ((uint64_t)r >= (uint64_t)sh.rows)
+        return;
+    copy_row<U>(comb_recv + srow * n + rs.b0, y + r * n + rs.b0, rs.len, lane);
 }
 
 // bf16 pattern of an fp32 value, round to nearest even (NaN -> 0x7FC0).
@@ -930,10 +977,13 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
         if (rsh.u > 8)
             rsh.u = 8;
         MOE_DISPATCH_ROW(rsh, pack_fp8_kernel, tokens, L, sh, p, (const v4u*)x, idx,
-                         (v2u*)r.send_x, r.send_scale, r.send_meta);
+                         (v2u*)(sh.direct ? r.recv_x : r.send_x),
+                         sh.direct ? r.recv_scale : r.send_scale,
+                         sh.direct ? r.recv_meta : r.send_meta);
     } else {
         MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), pack_bf16_kernel, tokens, L, sh, p,
-                         (const v4u*)x, idx, (v4u*)r.send_x, r.send_meta);
+                         (const v4u*)x, idx, (v4u*)(sh.direct ? r.recv_x : r.send_x),
+                         sh.direct ? r.recv_meta : r.send_meta);
     }
     return hipGetLastError();
 }
@@ -974,6 +1024,16 @@ hipError_t launch_transfer_back(const Shape& sh, const Plan& p, const Rows& r, c
         return hipSuccess;
     MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), transfer_back_kernel, sh.rows, L, sh, p,
                      (const v4u*)r.comb_send, (v4u*)r.comb_recv);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r, const void* y,
+                               const Launch& L)
+{
+    if (sh.rows == 0)
+        return hipSuccess;
+    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), combine_push_kernel, sh.rows, L, sh, p,
+                     (const v4u*)y, (v4u*)r.comb_recv);
     return hipGetLastError();
 }
 

@@ -63,6 +63,26 @@ typedef enum moe_dtype {
     MOE_FP8_E4M3 = 1        /* dispatch payload: OCP e4m3 rows (H bytes) + fp32 scale per 128 elements */
 } moe_dtype;
 
+/* How rows reach the peer (same four calls and results either way, as the
+ * pages keep one interface across transports -- [EFA] "MoE all-to-all over
+ * EFA"):
+ *   MOE_TRANSPORT_STAGED  pack into a contiguous per-peer send buffer, then a
+ *                         transfer copies each (sender -> receiver) segment
+ *                         into the receive buffer; combine mirrors it.  This
+ *                         is the network model: one write per peer from a
+ *                         send buffer ([EFA] "Dispatch and combine").
+ *   MOE_TRANSPORT_DIRECT  pack writes each row straight into the receiver's
+ *                         receive region and combine writes each expert
+ *                         output straight back into the token owner's return
+ *                         rows, like the pages' intra-node push into peers'
+ *                         buffers ([EFA] "Dispatch and combine") and their
+ *                         shared-buffer idea ([EPMC] "Further improvements").
+ *                         No send buffer: two fewer row passes per stage. */
+typedef enum moe_transport {
+    MOE_TRANSPORT_STAGED = 0,
+    MOE_TRANSPORT_DIRECT = 1
+} moe_transport;
+
 /* Sizes fixed at creation ([EPMC] "Portable kernels": the maximum number of
  * tokens a rank may dispatch is fixed for the group, and the buffers are
  * reused by every layer).  Limits: 1 <= num_ranks <= 1024; num_experts a
@@ -76,6 +96,7 @@ typedef struct moe_group_desc {
     int32_t hidden;         /* H */
     int32_t max_tokens;     /* T_max per rank */
     int32_t dispatch_dtype; /* moe_dtype */
+    int32_t transport;      /* moe_transport */
 } moe_group_desc;
 
 typedef struct moe_group_s* moe_group_t;
@@ -100,7 +121,8 @@ int moe_group_destroy(moe_group_t g);
  *   x           device, bf16 [N][T][H]
  *   topk_idx    device, int32 [N][T][K], expert ids in [0, E)
  * Enqueues: route plan (counts, stable positions, offsets), pack (+ e4m3
- * encode), transfer into the receive buffers.  Reads x and topk_idx only. */
+ * encode) and, with the staged transport, the transfer into the receive
+ * buffers.  Reads x and topk_idx only. */
 int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x,
                       const int32_t* topk_idx, hipStream_t stream);
 
@@ -122,7 +144,8 @@ int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale,
  * sent back, each to the rank and token slot it came from; [EFA] "Dispatch and
  * combine": routing is already known, rows go one write per peer).
  *   expert_y  device, bf16 [N*T*K][H], rows in the order of expert_x
- * Enqueues: inverse shuffle into the per-peer layout, transfer back. */
+ * Enqueues (staged): inverse shuffle into the per-peer layout, transfer back;
+ * (direct): one kernel writing each output into its return row. */
 int moe_combine_send(moe_group_t g, const void* expert_y, hipStream_t stream);
 
 /* Combine, receive half ([EPMC] "Introduction": the output is the sum of the
@@ -140,7 +163,8 @@ int moe_combine_recv(moe_group_t g, const float* topk_weights, void* out,
  * pooled send buffer holds send_x during dispatch and comb_send during
  * combine; the pooled receive buffer holds recv_x, then comb_recv.  Layouts:
  * send rows of sender s are rows [s*T*K, (s+1)*T*K); receive rows of rank d
- * are rows [recv_base[d], recv_base[d+1]). */
+ * are rows [recv_base[d], recv_base[d+1]).  With the direct transport there
+ * is no send buffer: send_x, send_scale, send_meta and comb_send are NULL. */
 typedef struct moe_group_view {
     moe_group_desc desc;
     int32_t num_tokens;          /* T of the current cycle */
@@ -188,7 +212,8 @@ typedef enum moe_kernel_id {
     MOE_KERNEL_COMBINE_PACK = 4,
     MOE_KERNEL_TRANSFER_BACK = 5,
     MOE_KERNEL_COMBINE_REDUCE = 6,
-    MOE_KERNEL_COUNT = 7
+    MOE_KERNEL_COMBINE_PUSH = 7,    /* direct transport: replaces combine pack + transfer back */
+    MOE_KERNEL_COUNT = 8
 } moe_kernel_id;
 
 typedef enum moe_kernel_mask { MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1 } moe_kernel_mask;

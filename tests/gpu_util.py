@@ -56,15 +56,17 @@ def to_dev(torch, a: np.ndarray):
     return t.to("cuda")
 
 
-def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, want_rows=True):
+def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, want_rows=True,
+              transport=0):
     """One full dispatch + stand-in expert + combine cycle on the GPU.
-    Returns a dict of host copies of every buffer (rows only if want_rows)."""
+    Returns a dict of host copies of every buffer (rows only if want_rows;
+    the send-side buffers only with the staged transport)."""
     N, T, K, E, H = cfg.N, inp["idx"].shape[1], cfg.K, cfg.E, cfg.H
     fp8 = cfg.dtype == "fp8"
     T_max = T if T_max is None else T_max
     own = group is None
     g = group if group is not None else mep.moe_group_create(
-        N, E, K, H, T_max, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16)
+        N, E, K, H, T_max, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16, transport)
     try:
         R = N * T * K
         x = to_dev(torch, inp["x"])
@@ -89,18 +91,22 @@ def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, w
         res["G"] = d2h(v.recv_base, (N + 1,), np.int32)
         res["eoff"] = d2h(v.expert_off, (E + 1,), np.int32)
         res["expert_offsets"] = expert_offsets.cpu().numpy()
-        res["send_meta"] = d2h(v.send_meta, (R,), np.int32)
+        staged = bool(v.send_x)
+        if staged:
+            res["send_meta"] = d2h(v.send_meta, (R,), np.int32)
         res["recv_meta"] = d2h(v.recv_meta, (R,), np.int32)
         res["expert_src_rank"] = d2h(v.expert_src_rank, (R,), np.int32)
         res["expert_src_slot"] = d2h(v.expert_src_slot, (R,), np.int32)
         pdt = np.uint8 if fp8 else np.uint16
         if want_rows:
-            res["send_x"] = d2h(v.send_x, (R, H), pdt)
+            if staged:
+                res["send_x"] = d2h(v.send_x, (R, H), pdt)
             res["recv_x"] = d2h(v.recv_x, (R, H), pdt)
             res["expert_x"] = expert_x[:R * payload].cpu().numpy().view(pdt).reshape(R, H)
             if fp8:
                 nb = H // 128
-                res["send_scale"] = d2h(v.send_scale, (R, nb), np.float32)
+                if staged:
+                    res["send_scale"] = d2h(v.send_scale, (R, nb), np.float32)
                 res["recv_scale"] = d2h(v.recv_scale, (R, nb), np.float32)
                 res["expert_scale"] = expert_scale[:R * nb].cpu().numpy().reshape(R, nb)
         if identity:
@@ -117,7 +123,8 @@ def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, w
         v = mep.moe_group_view_get(g)
         if want_rows:
             res["y"] = y.view(torch.int16).cpu().numpy().view(np.uint16)
-            res["comb_send"] = d2h(v.comb_send, (R, H), np.uint16)
+            if staged:
+                res["comb_send"] = d2h(v.comb_send, (R, H), np.uint16)
             res["comb_recv"] = d2h(v.comb_recv, (R, H), np.uint16)
         res["y_dev"] = y
         res["out"] = out[:, :T].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
