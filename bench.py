@@ -18,6 +18,7 @@ adds a few microseconds of gap to the step.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -188,6 +189,150 @@ def trace_summary(cfg, db: str) -> str:
     return "\n".join(lines)
 
 
+def _hip_runtime():
+    """The HIP runtime already loaded by torch (found by soname, not loaded again)."""
+    import torch  # noqa: F401  (loads the runtime)
+    mode = getattr(os, "RTLD_NOLOAD", 4) | os.RTLD_LAZY
+    for name in ("libamdhip64.so.7", "libamdhip64.so"):
+        try:
+            lib = ctypes.CDLL(name, mode=mode)
+            break
+        except OSError:
+            lib = None
+    assert lib is not None, "HIP runtime not loaded"
+    lib.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    lib.hipExtStreamCreateWithCUMask.restype = ctypes.c_int
+    lib.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    lib.hipStreamDestroy.restype = ctypes.c_int
+    return lib
+
+
+def overlap_demo(cfg, args) -> dict:
+    """Send/recv split in use: a bf16 GEMM standing in for the shared expert
+    ([N*T, H] x [H, 2048]) runs on its own stream while dispatch-send runs;
+    compared with running the two back to back on one stream."""
+    import numpy as np
+    import torch
+
+    import combine_moe_dispatch_amd as mep
+    from workloads import make_inputs
+    inp = make_inputs(cfg)
+    N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
+    R = cfg.rows
+    transport = mep.MOE_TRANSPORT_DIRECT if args.transport == "direct" else mep.MOE_TRANSPORT_STAGED
+    x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
+    idx = torch.from_numpy(inp["idx"]).cuda()
+    expert_x = torch.empty((R, 2 * H), dtype=torch.uint8, device="cuda")
+    offs = torch.empty((E + 1,), dtype=torch.int32, device="cuda")
+    a = torch.randn((N * T, H), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((H, 2048), dtype=torch.bfloat16, device="cuda")
+    g = mep.moe_group_create(N, E, K, H, T, mep.MOE_BF16, transport)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    # a dispatch cycle must be completed before the next send; the combine
+    # halves are run (untimed) with a fixed expert output
+    y = torch.zeros((R, H), dtype=torch.bfloat16, device="cuda")
+    w = torch.from_numpy(inp["w"]).cuda()
+    out = torch.empty((N, T, H), dtype=torch.bfloat16, device="cuda")
+
+    def finish(stream):
+        mep.moe_combine_send(g, y, stream)
+        mep.moe_combine_recv(g, w, out, stream)
+
+    def timed(fn, iters):
+        ts = []
+        for _ in range(iters):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+            finish(s1)
+        torch.cuda.synchronize()
+        return float(np.median(ts)) * 1e6
+
+    def gemm_only():
+        with torch.cuda.stream(s2):
+            torch.matmul(a, b)
+
+    def dispatch_only():
+        mep.moe_dispatch_send(g, T, x, idx, s1)
+        mep.moe_dispatch_recv(g, expert_x, None, offs, s1)
+
+    def serial():
+        mep.moe_dispatch_send(g, T, x, idx, s1)
+        with torch.cuda.stream(s1):
+            torch.matmul(a, b)
+        mep.moe_dispatch_recv(g, expert_x, None, offs, s1)
+
+    def overlapped():
+        ev = torch.cuda.Event()
+        with torch.cuda.stream(s2):
+            torch.matmul(a, b)
+            ev.record(s2)
+        mep.moe_dispatch_send(g, T, x, idx, s1)
+        mep.moe_dispatch_recv(g, expert_x, None, offs, s1)
+        s1.wait_event(ev)
+
+    # CU-partitioned streams: the movers on one set of CUs, the GEMM on the
+    # rest (hipExtStreamCreateWithCUMask), so neither starves the other of
+    # wave slots
+    hip = _hip_runtime()
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def cu_stream(first, count):
+        words = (ncu + 31) // 32
+        mask = (ctypes.c_uint32 * words)()
+        for c in range(first, first + count):
+            mask[c // 32] |= 1 << (c % 32)
+        handle = ctypes.c_void_p()
+        rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), words, mask)
+        assert rc == 0, rc
+        return torch.cuda.ExternalStream(handle.value), handle
+
+    def overlapped_partitioned(split):
+        sa, ha = cu_stream(0, split)
+        sb, hb = cu_stream(split, ncu - split)
+
+        def run():
+            ev = torch.cuda.Event()
+            with torch.cuda.stream(sb):
+                torch.matmul(a, b)
+                ev.record(sb)
+            mep.moe_dispatch_send(g, T, x, idx, sa)
+            mep.moe_dispatch_recv(g, expert_x, None, offs, sa)
+            sa.wait_event(ev)
+        timed(run, 3)
+        t = timed(run, 30)
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy(ha)
+        hip.hipStreamDestroy(hb)
+        return t
+
+    for fn in (dispatch_only, serial, overlapped):      # warm up
+        timed(fn, 3)
+    res = {"dispatch_us": timed(dispatch_only, 30), "serial_us": timed(serial, 30),
+           "overlapped_us": timed(overlapped, 30)}
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(30):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gemm_only()
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    res["gemm_us"] = float(np.median(ts)) * 1e6
+    for split in (ncu // 2, 3 * ncu // 4):
+        res[f"overlapped_cu_split_{split}_{ncu - split}_us"] = overlapped_partitioned(split)
+    mep.moe_group_destroy(g)
+    res = {k: round(v, 1) for k, v in res.items()}
+    best = min(v for k, v in res.items() if k.startswith("overlapped"))
+    res["hidden_fraction_of_gemm"] = round((res["serial_us"] - best) / res["gemm_us"], 3)
+    res["workload"] = cfg.describe() + f" transport={args.transport}"
+    res["other_work"] = f"bf16 GEMM [{N * T} x {H}] x [{H} x 2048] on its own stream"
+    return res
+
+
 def cpu_baseline(cfg, inp, min_seconds: float) -> dict:
     """The oracle, unchanged and single-threaded, on the same workload: whole
     dispatch + combine steps until min_seconds of work (at least one)."""
@@ -231,11 +376,17 @@ def main() -> int:
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "CAL_FETCH_DB",
                                                         "CAL_WRITE_DB"),
                     help="write profiles/traffic_<config>.json from rocprofv3 --pmc databases")
+    ap.add_argument("--overlap", action="store_true",
+                    help="measure the send/recv split hiding a concurrent GEMM (prints one JSON line)")
     ap.add_argument("--trace-summary", metavar="DB",
                     help="print a table of the library's kernels from a rocprofv3 kernel trace")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration()
+    if args.overlap:
+        from workloads import CONFIGS
+        print(json.dumps(overlap_demo(CONFIGS[args.config], args)), flush=True)
+        return 0
     if args.traffic_from or args.trace_summary:
         from workloads import CONFIGS
         cfg = CONFIGS[args.config]
