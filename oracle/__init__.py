@@ -78,6 +78,11 @@ def _declare(L):
     L.orc_combine_token.argtypes = [_I, _I, _P, _P, _P]
     L.orc_f32_to_bf16_n.argtypes = [_Z, _P, _P]
     L.orc_send_meta.argtypes = [_I, _I, _I, _P, _P]
+    L.orc_partial_counts.argtypes = [_I, _I, _I, _I, _P, _P]
+    L.orc_partial_rows.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P]
+    L.orc_partial_send.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+    L.orc_partial_transfer.argtypes = [_I, _I, _I, _P, _P, _P, _P]
+    L.orc_partial_recv.argtypes = [_I, _I, _I, _P, _P, _P]
     L.orc_expert_rows.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
     L.orc_f32_to_e4m3_n.argtypes = [_Z, _P, _P]
 
@@ -349,3 +354,40 @@ def run_combine(y: np.ndarray, w: np.ndarray, pl: dict, H: int) -> dict:
     comb_recv = combine_transfer(comb_send, pl, T, K)
     out = combine_recv(comb_recv, pl["pos"], w, H)
     return {"comb_send": comb_send, "comb_recv": comb_recv, "out": out}
+
+
+# ------------------------------------------ combine with sender-side partial sums
+
+def partial_plan(idx: np.ndarray, E: int) -> dict:
+    """Partial-row counts pc[s][d] and the owner-side / token-owner-side row of
+    every visited (s,t,d) ([N][T][N], -1 where token (s,t) has no expert on d)."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    N, T, K = idx.shape
+    pc = np.zeros((N, N), dtype=np.int32)
+    lib().orc_partial_counts(N, T, K, E, _p(idx), _p(pc))
+    owner_row = np.zeros((N, T, N), dtype=np.int32)
+    token_row = np.zeros((N, T, N), dtype=np.int32)
+    lib().orc_partial_rows(N, T, K, E, _p(idx), _p(pc), _p(owner_row), _p(token_row))
+    return {"pc": pc, "owner_row": owner_row, "token_row": token_row, "P": int(pc.sum())}
+
+
+def run_partial_combine(y: np.ndarray, w: np.ndarray, idx: np.ndarray, pl: dict, H: int) -> dict:
+    """Combine with sender-side partial sums; y in expert-row order, pl from plan()."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    N, T, K = idx.shape
+    E = pl["cnt"].shape[1]
+    pp = partial_plan(idx, E)
+    rows = expert_rows(idx, pl)
+    P = pp["P"]
+    psend = np.zeros((P, H), dtype=np.uint16)
+    precv = np.zeros((P, H), dtype=np.uint16)
+    out = np.zeros((N, T, H), dtype=np.uint16)
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    lib().orc_partial_send(N, T, K, E, H, _p(idx), _p(w), _p(rows), _p(y), _p(pp["owner_row"]),
+                           _p(psend))
+    lib().orc_partial_transfer(N, T, H, _p(pp["owner_row"]), _p(pp["token_row"]), _p(psend),
+                               _p(precv))
+    lib().orc_partial_recv(N, T, H, _p(pp["token_row"]), _p(precv), _p(out))
+    pp.update(psend=psend, precv=precv, out=out)
+    return pp

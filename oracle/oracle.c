@@ -535,3 +535,133 @@ void orc_expert_rows(int N, int T, int K, int E, const int32_t* idx, const int32
                 rows[i] = eoff[e] + before + pos[i] - soff[(size_t)s * (E + 1) + e];
             }
 }
+
+/* ------------------------------------- combine with sender-side partial sums */
+/*
+ * [EFA] "Dispatch/combine latency": accumulating on the send side of combine
+ * cuts the bytes moved, at some cost in precision.  Reading taken here: the
+ * rank d owning some of token (s,t)'s experts sums their weighted outputs
+ * (fp32, k ascending, fma chain from +0), rounds the partial once to bf16 and
+ * returns ONE row per (token, destination rank); the token's owner adds the
+ * partials in fp32, destination rank ascending, from +0, and rounds to bf16.
+ *
+ * visits(s,t,d) = some k has idx[s][t][k] / L == d.
+ * pc[s][d]      = #{t : visits(s,t,d)}          (partial rows from d back to s)
+ * prank(s,t,d)  = #{t' < t : visits(s,t',d)}
+ * Owner-side rows ("partial send", like the receive layout): owner d's rows
+ * start at sum_{d'<d} sum_s pc[s][d']; inside, sender s ascending, then t.
+ * Token-owner rows ("partial receive", like the send layout): sender s's rows
+ * start at sum_{s'<s} sum_d pc[s'][d]; inside, d ascending, then t.
+ */
+void orc_partial_counts(int N, int T, int K, int E, const int32_t* idx, int32_t* pc)
+{
+    int L = E / N;
+    memset(pc, 0, sizeof(int32_t) * (size_t)N * N);
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t)
+            for (int d = 0; d < N; ++d) {
+                int v = 0;
+                for (int k = 0; k < K; ++k)
+                    if (idx[((size_t)s * T + t) * K + k] / L == d)
+                        v = 1;
+                pc[(size_t)s * N + d] += v;
+            }
+}
+
+/* Row of partial (s,t,d) in the owner-side and token-owner-side layouts, for
+ * every (s,t,d) visited (-1 elsewhere); arrays [N][T][N]. */
+void orc_partial_rows(int N, int T, int K, int E, const int32_t* idx, const int32_t* pc,
+                      int32_t* owner_row, int32_t* token_row)
+{
+    int L = E / N;
+    int32_t* rank = (int32_t*)calloc((size_t)N * N, sizeof(int32_t));   /* [s][d] running prank */
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t)
+            for (int d = 0; d < N; ++d) {
+                size_t o = ((size_t)s * T + t) * N + d;
+                int v = 0;
+                for (int k = 0; k < K; ++k)
+                    if (idx[((size_t)s * T + t) * K + k] / L == d)
+                        v = 1;
+                if (!v) {
+                    owner_row[o] = -1;
+                    token_row[o] = -1;
+                    continue;
+                }
+                int32_t ob = 0, tb = 0;
+                for (int d2 = 0; d2 < d; ++d2)
+                    for (int s2 = 0; s2 < N; ++s2)
+                        ob += pc[(size_t)s2 * N + d2];
+                for (int s2 = 0; s2 < s; ++s2)
+                    ob += pc[(size_t)s2 * N + d];
+                for (int s2 = 0; s2 < s; ++s2)
+                    for (int d2 = 0; d2 < N; ++d2)
+                        tb += pc[(size_t)s2 * N + d2];
+                for (int d2 = 0; d2 < d; ++d2)
+                    tb += pc[(size_t)s * N + d2];
+                int32_t pr = rank[(size_t)s * N + d]++;
+                owner_row[o] = ob + pr;
+                token_row[o] = tb + pr;
+            }
+    free(rank);
+}
+
+/* The owner's partial sums: for every visited (s,t,d), the fp32 fma chain over
+ * the token's k (ascending) whose expert lives on d, of w[s][t][k] times the
+ * expert output row y[expert_rows[s][t][k]], rounded to bf16, written to the
+ * owner-side row. */
+void orc_partial_send(int N, int T, int K, int E, int H, const int32_t* idx, const float* w,
+                      const int32_t* expert_rows, const uint16_t* y, const int32_t* owner_row,
+                      uint16_t* psend)
+{
+    int L = E / N;
+    float* acc = (float*)malloc(sizeof(float) * (size_t)H);
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t)
+            for (int d = 0; d < N; ++d) {
+                int32_t row = owner_row[((size_t)s * T + t) * N + d];
+                if (row < 0)
+                    continue;
+                for (int h = 0; h < H; ++h)
+                    acc[h] = +0.0f;
+                for (int k = 0; k < K; ++k) {
+                    size_t i = ((size_t)s * T + t) * K + k;
+                    if (idx[i] / L != d)
+                        continue;
+                    const uint16_t* yr = y + (size_t)expert_rows[i] * H;
+                    for (int h = 0; h < H; ++h)
+                        acc[h] = fmaf(w[i], orc_bf16_to_f32(yr[h]), acc[h]);
+                }
+                for (int h = 0; h < H; ++h)
+                    psend[(size_t)row * H + h] = orc_f32_to_bf16(acc[h]);
+            }
+    free(acc);
+}
+
+/* The transfer of the partial rows back to each token's owner. */
+void orc_partial_transfer(int N, int T, int H, const int32_t* owner_row, const int32_t* token_row,
+                          const uint16_t* psend, uint16_t* precv)
+{
+    for (size_t o = 0; o < (size_t)N * T * N; ++o)
+        if (owner_row[o] >= 0)
+            memcpy(precv + (size_t)token_row[o] * H, psend + (size_t)owner_row[o] * H,
+                   sizeof(uint16_t) * H);
+}
+
+/* The token owner's sum of its partial rows: fp32, destination rank
+ * ascending, from +0, rounded once to bf16. */
+void orc_partial_recv(int N, int T, int H, const int32_t* token_row, const uint16_t* precv,
+                      uint16_t* out)
+{
+    for (int s = 0; s < N; ++s)
+        for (int t = 0; t < T; ++t)
+            for (int h = 0; h < H; ++h) {
+                float acc = +0.0f;
+                for (int d = 0; d < N; ++d) {
+                    int32_t row = token_row[((size_t)s * T + t) * N + d];
+                    if (row >= 0)
+                        acc = acc + orc_bf16_to_f32(precv[(size_t)row * H + h]);
+                }
+                out[((size_t)s * T + t) * H + h] = orc_f32_to_bf16(acc);
+            }
+}

@@ -1,0 +1,116 @@
+"""Pins of the oracle's combine with sender-side partial sums (each expert
+owner returns one pre-summed row per (token, destination rank)): layouts
+against sorted brute-force lists, reduction to the receiver-side combine when
+every expert of a token lives on one rank, one-hot weights reading back exact
+rows, and the rounding bound against an exact double-precision sum."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.brute import brute_plan
+from workloads import CONFIGS, Config, f32_from_bf16_bits, make_inputs, renormalised
+
+
+def _dispatch(cfg, inp):
+    d = oracle.run_dispatch(inp["x"], inp["idx"], cfg.E)
+    y = oracle.expert_standin(d["expert_x"], None, d["eoff"], cfg.H)
+    return d, y
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_partial_layout_matches_sorted_lists(seed):
+    g = np.random.default_rng(300 + seed)
+    N = int(g.choice([1, 2, 3, 4, 8]))
+    L = int(g.integers(1, 5))
+    E, K, T = N * L, int(g.integers(1, 9)), int(g.integers(0, 7))
+    idx = g.integers(0, E, size=(N, T, K)).astype(np.int32)
+    pp = oracle.partial_plan(idx, E)
+    visits = sorted({(s, t, int(idx[s, t, k]) // L) for s in range(N) for t in range(T)
+                     for k in range(K)})
+    assert pp["P"] == len(visits)
+    for s in range(N):
+        for d in range(N):
+            assert pp["pc"][s, d] == sum(1 for (a, _, b) in visits if a == s and b == d)
+    owner_order = sorted(visits, key=lambda v: (v[2], v[0], v[1]))     # (d, s, t)
+    token_order = sorted(visits, key=lambda v: (v[0], v[2], v[1]))
+    for row, (s, t, d) in enumerate(owner_order):
+        assert pp["owner_row"][s, t, d] == row
+    for row, (s, t, d) in enumerate(token_order):
+        assert pp["token_row"][s, t, d] == row
+    unvisited = np.ones((N, T, N), dtype=bool)
+    for (s, t, d) in visits:
+        unvisited[s, t, d] = False
+    assert np.all(pp["owner_row"][unvisited] == -1) and np.all(pp["token_row"][unvisited] == -1)
+
+
+def test_single_rank_equals_receiver_combine():
+    """With one rank every token has one partial, bf16(full chain), and the
+    final sum of one bf16 value rounds back to itself: bit-identical to the
+    receiver-side combine."""
+    cfg = CONFIGS["A"].with_(N=1, E=8, K=4, routing="uniform")
+    inp = make_inputs(cfg)
+    d, y = _dispatch(cfg, inp)
+    ref = oracle.run_combine(y, inp["w"], d, cfg.H)["out"]
+    got = oracle.run_partial_combine(y, inp["w"], inp["idx"], d, cfg.H)["out"]
+    assert np.array_equal(got, ref)
+
+
+def test_identity_when_all_experts_of_a_token_share_a_rank():
+    """Identity experts, weights summing to one, every expert of a token on
+    one rank: the one partial is bf16(x * sum w) = x, so out == x (-0 -> +0)."""
+    cfg = Config("P", "same-rank", 4, 16, 256, 16, 3, "bf16", "uniform", 9)
+    inp = make_inputs(cfg)
+    g = np.random.default_rng(9)
+    L = cfg.L
+    ranks = g.integers(0, cfg.N, size=(cfg.N, cfg.T))
+    inp["idx"] = (ranks[..., None] * L + g.integers(0, L, size=(cfg.N, cfg.T, cfg.K))).astype(np.int32)
+    w = renormalised(inp["w"])
+    d = oracle.run_dispatch(inp["x"], inp["idx"], cfg.E)
+    got = oracle.run_partial_combine(d["expert_x"], w, inp["idx"], d, cfg.H)["out"]
+    assert np.array_equal(got, np.where(inp["x"] == 0x8000, np.uint16(0), inp["x"]))
+
+
+def test_one_hot_weights_read_back_each_slot():
+    cfg = CONFIGS["A"].with_(routing="uniform", K=3)
+    inp = make_inputs(cfg)
+    N, T, K, H, E = cfg.N, cfg.T, cfg.K, cfg.H, cfg.E
+    d = oracle.run_dispatch(inp["x"], inp["idx"], E)
+    b = brute_plan(inp["idx"].tolist(), E)
+    where = {stk: r for r, stk in enumerate(b["expert_rows"])}
+    y = np.random.default_rng(4).integers(0, 0x7F00, size=(cfg.rows, H)).astype(np.uint16)
+    for k in range(K):
+        w = np.zeros((N, T, K), dtype=np.float32)
+        w[:, :, k] = 1.0
+        out = oracle.run_partial_combine(y, w, inp["idx"], d, H)["out"]
+        for s in range(N):
+            for t in range(T):
+                assert np.array_equal(out[s, t], y[where[(s, t, k)]])
+
+
+@pytest.mark.parametrize("key", ["A", "B", "Ep"])
+def test_partial_sums_within_rounding_bound(key):
+    """|out - exact| <= sum over partials of (chain error + half a bf16 ulp)
+    + the fp32 sum's error + half a bf16 ulp of the result."""
+    cfg = CONFIGS[key]
+    if key == "Ep":
+        cfg = cfg.with_(N=8, E=48, T=16, H=512)        # same routing rule, small
+    inp = make_inputs(cfg)
+    d, y = _dispatch(cfg, inp)
+    res = oracle.run_partial_combine(y, inp["w"], inp["idx"], d, cfg.H)
+    rows = oracle.expert_rows(inp["idx"], d)
+    yv = f32_from_bf16_bits(y).astype(np.float64)
+    terms = inp["w"].astype(np.float64)[..., None] * yv[rows]          # [N][T][K][H]
+    exact = terms.sum(axis=2)
+    mag = np.abs(terms).sum(axis=2)
+    got = f32_from_bf16_bits(res["out"]).astype(np.float64)
+    u = 2.0 ** -24
+    K, Nd = cfg.K, cfg.N
+    bound = (K * u * 1.01 * mag                     # fp32 chains inside the partials
+             + 2.0 ** -8 * mag * (1 + 2 * K * u)    # bf16 rounding of every partial
+             + Nd * u * 1.01 * mag * (1 + 2.0 ** -7)   # fp32 sum of the partials
+             + 2.0 ** -8 * np.abs(got) + 2.0 ** -133)  # final bf16 rounding
+    assert np.all(np.abs(got - exact) <= bound)
+    # the bytes saved: one row per (token, destination rank)
+    assert res["P"] <= cfg.rows
+    if key == "Ep":
+        assert res["P"] < 0.5 * cfg.rows           # 6 of 8 experts share rank 0
