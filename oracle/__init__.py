@@ -76,6 +76,7 @@ def _declare(L):
     L.orc_combine_recv.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P]
     L.orc_combine_recv_f64.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P]
     L.orc_combine_token.argtypes = [_I, _I, _P, _P, _P]
+    L.orc_partial_token.argtypes = [_I, _I, _P, _P, _P, _P]
     L.orc_f32_to_bf16_n.argtypes = [_Z, _P, _P]
     L.orc_send_meta.argtypes = [_I, _I, _I, _P, _P]
     L.orc_partial_counts.argtypes = [_I, _I, _I, _I, _P, _P]
@@ -344,6 +345,19 @@ def combine_token(rows: np.ndarray, w: np.ndarray) -> np.ndarray:
     ptrs = (ctypes.c_void_p * K)(*[rows[k].ctypes.data for k in range(K)])
     out = np.zeros(H, dtype=np.uint16)
     lib().orc_combine_token(K, H, ctypes.cast(ptrs, ctypes.c_void_p), _p(w), _p(out))
+    return out
+
+
+def partial_token(rows: np.ndarray, w: np.ndarray, rank: np.ndarray) -> np.ndarray:
+    """One token of the combine with sender-side partial sums: its K returned
+    rows (uint16 [K][H]), weights and destination ranks."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    K, H = rows.shape
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rank = np.ascontiguousarray(rank, dtype=np.int32)
+    ptrs = (ctypes.c_void_p * K)(*[rows[k].ctypes.data for k in range(K)])
+    out = np.zeros(H, dtype=np.uint16)
+    lib().orc_partial_token(K, H, ctypes.cast(ptrs, ctypes.c_void_p), _p(w), _p(rank), _p(out))
     return out
 
 

@@ -665,3 +665,34 @@ void orc_partial_recv(int N, int T, int H, const int32_t* token_row, const uint1
                 out[((size_t)s * T + t) * H + h] = orc_f32_to_bf16(acc);
             }
 }
+
+/* One token of the same combine, for checking single tokens of workloads too
+ * large for the whole-batch functions: rows[k] is the expert output of item
+ * k, rank[k] its destination rank.  Ranks ascending: the partial of rank d is
+ * the fp32 fma chain from +0 over the k with rank[k] == d, k ascending,
+ * rounded to bf16; the partials are added in fp32 from +0 and the sum is
+ * rounded to bf16. */
+void orc_partial_token(int K, int H, const uint16_t* const* rows, const float* w,
+                       const int32_t* rank, uint16_t* out)
+{
+    for (int h = 0; h < H; ++h) {
+        float acc = +0.0f;
+        int32_t prev = -1;
+        for (;;) {
+            /* the smallest rank above the previous one */
+            int32_t d = -1;
+            for (int k = 0; k < K; ++k)
+                if (rank[k] > prev && (d < 0 || rank[k] < d))
+                    d = rank[k];
+            if (d < 0)
+                break;
+            float part = +0.0f;
+            for (int k = 0; k < K; ++k)
+                if (rank[k] == d)
+                    part = fmaf(w[k], orc_bf16_to_f32(rows[k][h]), part);
+            acc = acc + orc_bf16_to_f32(orc_f32_to_bf16(part));
+            prev = d;
+        }
+        out[h] = orc_f32_to_bf16(acc);
+    }
+}

@@ -114,3 +114,27 @@ def test_partial_sums_within_rounding_bound(key):
     assert res["P"] <= cfg.rows
     if key == "Ep":
         assert res["P"] < 0.5 * cfg.rows           # 6 of 8 experts share rank 0
+
+
+@pytest.mark.parametrize("key", ["A", "B"])
+def test_single_token_form_matches_the_batch(key):
+    """The one-token form gives every token's output of the whole-batch
+    form (pinned above)."""
+    cfg = CONFIGS[key].with_(T=24)
+    inp = make_inputs(cfg)
+    d, y = _dispatch(cfg, inp)
+    out = oracle.run_partial_combine(y, inp["w"], inp["idx"], d, cfg.H)["out"]
+    rows = oracle.expert_rows(inp["idx"], d)
+    for s in range(cfg.N):
+        for t in range(cfg.T):
+            got = oracle.partial_token(y[rows[s, t]], inp["w"][s, t], inp["idx"][s, t] // cfg.L)
+            assert np.array_equal(got, out[s, t]), (s, t)
+
+
+def test_single_token_form_reduces_to_receiver_combine_on_one_rank():
+    """All items on one rank: one partial, rounded twice to the same bf16."""
+    g = np.random.default_rng(8)
+    rows = g.integers(0, 0x7F00, size=(5, 64)).astype(np.uint16)
+    w = g.random(5).astype(np.float32)
+    got = oracle.partial_token(rows, w, np.full(5, 3, dtype=np.int32))
+    assert np.array_equal(got, oracle.combine_token(rows, w))
