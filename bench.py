@@ -33,12 +33,23 @@ METRIC = "µs per dispatch+combine and achieved HBM GB/s (% of peak), DeepSeek-R
 HBM_PEAK_GBPS = 8000.0
 
 
-def kernel_bytes(cfg, transport: str = "staged") -> dict:
+def partial_rows(cfg, idx) -> int:
+    """P: the number of distinct (token, destination rank) pairs, i.e. the rows
+    the expert-side partial combine returns."""
+    import numpy as np
+    N, T = cfg.N, cfg.T
+    d = np.asarray(idx, dtype=np.int64) // cfg.L                    # [N][T][K]
+    tok = np.arange(N * T, dtype=np.int64).reshape(N, T, 1)
+    return int(np.unique(tok * N + d).size)
+
+
+def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: int = 0) -> dict:
     """Algorithmic HBM bytes per launch of each kernel: every buffer the method
     mandates is written once and read once by the next stage; inputs are read
     once per token.  The int32 row maps the pack kernel writes for the later
     movers (4-8 bytes per row of 7-14 KiB) are an implementation detail and not
-    counted."""
+    counted.  With the partial combine (P partial rows), the router weights
+    travel with the dispatched rows and combine moves P rows instead of R."""
     N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
     R = N * T * K
     fp8 = cfg.dtype == "fp8"
@@ -65,6 +76,21 @@ def kernel_bytes(cfg, transport: str = "staged") -> dict:
         for k in ("transfer", "combine_pack", "transfer_back"):
             del kb[k]
         kb["combine_push"] = 2 * R * hy
+    if combine == "partial":
+        # second route-plan pass: rank and position of every item; weights
+        # (4 bytes a row) through pack and transfer
+        kb["route_plan"] += 2 * R * 4 + 3 * N * (N + 1) * 4 + 2 * (N + 1) * 4
+        kb["pack"] += 2 * R * 4
+        if "transfer" in kb:
+            kb["transfer"] += 2 * R * 4
+        for k in ("combine_pack", "transfer_back", "combine_push", "combine_reduce"):
+            kb.pop(k, None)
+        # expert rows in (+ per item: position, rank, partial position, row
+        # pair, weight), partial rows out
+        kb["partial_send"] = R * hy + R * 24 + P * hy
+        if transport == "staged":
+            kb["partial_transfer"] = 2 * P * hy
+        kb["partial_reduce"] = P * hy + R * 8 + tokens * H * 2
     return kb
 
 
@@ -100,7 +126,10 @@ KERNEL_OF = [("route_plan_kernel", "route_plan"), ("pack_bf16_kernel", "pack"),
              ("pack_fp8_kernel", "pack"), ("transfer_back_kernel", "transfer_back"),
              ("transfer_kernel", "transfer"), ("shuffle_kernel", "shuffle"),
              ("combine_pack_kernel", "combine_pack"),
-             ("combine_reduce_kernel", "combine_reduce")]
+             ("combine_reduce_kernel", "combine_reduce"),
+             ("partial_send_kernel", "partial_send"),
+             ("partial_transfer_kernel", "partial_transfer"),
+             ("partial_reduce_kernel", "partial_reduce")]
 
 
 def _kernel_key(name: str):
@@ -135,7 +164,8 @@ def _counter_by_kernel(db: str, counter: str) -> dict:
     return acc
 
 
-def traffic_from(cfg, fetch_db, write_db, cal_fetch_db, cal_write_db, transport="staged") -> dict:
+def traffic_from(cfg, fetch_db, write_db, cal_fetch_db, cal_write_db, transport="staged",
+                 combine="receiver") -> dict:
     """HBM bytes per launch of each kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
     counter reads for the plain copy of CAL_BYTES bytes."""
@@ -147,7 +177,7 @@ def traffic_from(cfg, fetch_db, write_db, cal_fetch_db, cal_write_db, transport=
         return CAL_BYTES / (kib * 1024.0)
     ff = cal_factor(cal_fetch_db, "FETCH_SIZE")
     wf = cal_factor(cal_write_db, "WRITE_SIZE")
-    kb = kernel_bytes(cfg, transport)
+    kb = kernel_bytes(cfg, transport, combine, _partial_rows_of(cfg, combine))
     out = {}
     for counter, db, f, field in (("FETCH_SIZE", fetch_db, ff, "fetch_bytes"),
                                   ("WRITE_SIZE", write_db, wf, "write_bytes")):
@@ -165,6 +195,13 @@ def traffic_from(cfg, fetch_db, write_db, cal_fetch_db, cal_write_db, transport=
             "fetch_factor": round(ff, 4), "write_factor": round(wf, 4), "kernels": out}
 
 
+def _partial_rows_of(cfg, combine: str) -> int:
+    if combine != "partial":
+        return 0
+    from workloads import make_routing
+    return partial_rows(cfg, make_routing(cfg)[0])
+
+
 def trace_summary(cfg, db: str) -> str:
     """Markdown table of the library's kernels from a rocprofv3 kernel trace."""
     import sqlite3
@@ -174,13 +211,14 @@ def trace_summary(cfg, db: str) -> str:
         key = _kernel_key(name)
         if key is not None:
             acc.setdefault(key, []).append(dur / 1000.0)
-    kb = kernel_bytes(cfg)
     lines = ["| kernel | launches | avg us | min us | max us | algorithmic GB/s |",
              "|---|---|---|---|---|---|"]
-    if "combine_push" in acc:
-        kb = kernel_bytes(cfg, "direct")
+    transport = "staged" if "transfer" in acc else "direct"
+    combine = "partial" if "partial_send" in acc else "receiver"
+    kb = kernel_bytes(cfg, transport, combine, _partial_rows_of(cfg, combine))
     for key in ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
-                "combine_push", "combine_reduce"]:
+                "combine_push", "combine_reduce", "partial_send", "partial_transfer",
+                "partial_reduce"]:
         if key in acc:
             v = acc[key]
             avg = sum(v) / len(v)
@@ -236,8 +274,8 @@ def overlap_demo(cfg, args) -> dict:
     out = torch.empty((N, T, H), dtype=torch.bfloat16, device="cuda")
 
     def finish(stream):
-        mep.moe_combine_send(g, y, stream)
-        mep.moe_combine_recv(g, w, out, stream)
+        mep.moe_combine_send(g, y, stream=stream)
+        mep.moe_combine_recv(g, w, out, stream=stream)
 
     def timed(fn, iters):
         ts = []
@@ -256,22 +294,22 @@ def overlap_demo(cfg, args) -> dict:
             torch.matmul(a, b)
 
     def dispatch_only():
-        mep.moe_dispatch_send(g, T, x, idx, s1)
-        mep.moe_dispatch_recv(g, expert_x, None, offs, s1)
+        mep.moe_dispatch_send(g, T, x, idx, stream=s1)
+        mep.moe_dispatch_recv(g, expert_x, None, offs, stream=s1)
 
     def serial():
-        mep.moe_dispatch_send(g, T, x, idx, s1)
+        mep.moe_dispatch_send(g, T, x, idx, stream=s1)
         with torch.cuda.stream(s1):
             torch.matmul(a, b)
-        mep.moe_dispatch_recv(g, expert_x, None, offs, s1)
+        mep.moe_dispatch_recv(g, expert_x, None, offs, stream=s1)
 
     def overlapped():
         ev = torch.cuda.Event()
         with torch.cuda.stream(s2):
             torch.matmul(a, b)
             ev.record(s2)
-        mep.moe_dispatch_send(g, T, x, idx, s1)
-        mep.moe_dispatch_recv(g, expert_x, None, offs, s1)
+        mep.moe_dispatch_send(g, T, x, idx, stream=s1)
+        mep.moe_dispatch_recv(g, expert_x, None, offs, stream=s1)
         s1.wait_event(ev)
 
     # CU-partitioned streams: the movers on one set of CUs, the GEMM on the
@@ -299,8 +337,8 @@ def overlap_demo(cfg, args) -> dict:
             with torch.cuda.stream(sb):
                 torch.matmul(a, b)
                 ev.record(sb)
-            mep.moe_dispatch_send(g, T, x, idx, sa)
-            mep.moe_dispatch_recv(g, expert_x, None, offs, sa)
+            mep.moe_dispatch_send(g, T, x, idx, stream=sa)
+            mep.moe_dispatch_recv(g, expert_x, None, offs, stream=sa)
             sa.wait_event(ev)
         timed(run, 3)
         t = timed(run, 30)
@@ -333,7 +371,7 @@ def overlap_demo(cfg, args) -> dict:
     return res
 
 
-def cpu_baseline(cfg, inp, min_seconds: float) -> dict:
+def cpu_baseline(cfg, inp, min_seconds: float, combine: str = "receiver") -> dict:
     """The oracle, unchanged and single-threaded, on the same workload: whole
     dispatch + combine steps until min_seconds of work (at least one)."""
     import numpy as np
@@ -345,7 +383,10 @@ def cpu_baseline(cfg, inp, min_seconds: float) -> dict:
     steps, t0 = 0, time.perf_counter()
     while True:
         d = oracle.run_dispatch(inp["x"], inp["idx"], cfg.E, fp8=cfg.dtype == "fp8")
-        c = oracle.run_combine(y, inp["w"], d, cfg.H)
+        if combine == "partial":
+            c = oracle.run_partial_combine(y, inp["w"], inp["idx"], d, cfg.H)
+        else:
+            c = oracle.run_combine(y, inp["w"], d, cfg.H)
         steps += 1
         del d, c
         el = time.perf_counter() - t0
@@ -355,7 +396,7 @@ def cpu_baseline(cfg, inp, min_seconds: float) -> dict:
     return {"value": round(el / steps * 1e6, 1), "unit": "us per dispatch+combine", "cores": 1,
             "kind": "oracle",
             "sample": f"{steps} full dispatch+combine step(s) of the {cfg.name} workload "
-                      f"({cfg.N}x{cfg.T} tokens), single thread, {el:.1f} s"}
+                      f"({cfg.N}x{cfg.T} tokens, {combine} combine), single thread, {el:.1f} s"}
 
 
 def main() -> int:
@@ -367,6 +408,9 @@ def main() -> int:
     ap.add_argument("--transport", choices=["staged", "direct"], default="staged",
                     help="staged: send buffer + modelled transfer (the measured contract); "
                          "direct: pack/combine write the peer's rows")
+    ap.add_argument("--combine", choices=["receiver", "partial"], default="receiver",
+                    help="receiver: the token owner sums all K expert rows; partial: each "
+                         "expert owner returns one pre-summed row per (token, rank)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -393,8 +437,10 @@ def main() -> int:
         if args.trace_summary:
             print(trace_summary(cfg, args.trace_summary))
         if args.traffic_from:
-            rec = traffic_from(cfg, *args.traffic_from, transport=args.transport)
-            suffix = "" if args.transport == "staged" else "_direct"
+            rec = traffic_from(cfg, *args.traffic_from, transport=args.transport,
+                               combine=args.combine)
+            suffix = ("" if args.transport == "staged" else "_direct") + \
+                ("_partial" if args.combine == "partial" else "")
             path = os.path.join(ROOT, "profiles", f"traffic_{args.config}{suffix}.json")
             with open(path, "w") as f:
                 json.dump(rec, f, indent=1)
@@ -428,25 +474,28 @@ def main() -> int:
     offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
     out = torch.empty((N, T, H), dtype=torch.bfloat16, device=dev)
     transport = mep.MOE_TRANSPORT_DIRECT if args.transport == "direct" else mep.MOE_TRANSPORT_STAGED
-    g = mep.moe_group_create(N, E, K, H, T, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16, transport)
+    partial = args.combine == "partial"
+    g = mep.moe_group_create(N, E, K, H, T, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16, transport,
+                             mep.MOE_COMBINE_PARTIAL if partial else mep.MOE_COMBINE_RECEIVER)
     stream = torch.cuda.current_stream()
+    w_send = w if partial else None          # partial combine: weights go with dispatch
 
     # first cycle + the stand-in expert output reused by every step
-    mep.moe_dispatch_send(g, T, x, idx, stream)
-    mep.moe_dispatch_recv(g, expert_x, expert_scale, offs, stream)
+    mep.moe_dispatch_send(g, T, x, idx, w_send, stream=stream)
+    mep.moe_dispatch_recv(g, expert_x, expert_scale, offs, stream=stream)
     from workloads.expert import standin_expert
     y = standin_expert(torch, expert_x.view(-1), expert_scale.view(-1) if fp8 else None, offs,
                        E, H, fp8).contiguous()
-    mep.moe_combine_send(g, y, stream)
-    mep.moe_combine_recv(g, w, out, stream)
+    mep.moe_combine_send(g, y, stream=stream)
+    mep.moe_combine_recv(g, w, out, stream=stream)
     torch.cuda.synchronize()
     assert mep.moe_group_status(g, stream) == mep.MOE_OK
 
     def step():
-        mep.moe_dispatch_send(g, T, x, idx, stream)
-        mep.moe_dispatch_recv(g, expert_x, expert_scale, offs, stream)
-        mep.moe_combine_send(g, y, stream)
-        mep.moe_combine_recv(g, w, out, stream)
+        mep.moe_dispatch_send(g, T, x, idx, w_send, stream=stream)
+        mep.moe_dispatch_recv(g, expert_x, expert_scale, offs, stream=stream)
+        mep.moe_combine_send(g, y, stream=stream)
+        mep.moe_combine_recv(g, w, out, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -479,7 +528,8 @@ def main() -> int:
     mep.moe_group_destroy(g)
 
     ms_per_step = (t1 - t0) / args.steps * 1e3
-    kb = kernel_bytes(cfg, args.transport)
+    P = partial_rows(cfg, inp["idx"]) if partial else 0
+    kb = kernel_bytes(cfg, args.transport, args.combine, P)
     total_bytes = sum(kb.values())
     kern = {}
     for name, (ms, n) in timing_all.items():
@@ -491,8 +541,8 @@ def main() -> int:
     dom_us = dom_ms / dom_n * 1e3
     ach = kb[dom] / (dom_us * 1e-6) / 1e9
     src_hash = kernel_source_hash()
-    traffic = measured_traffic(args.config + ("" if args.transport == "staged" else "_direct"),
-                               dom, src_hash)
+    traffic = measured_traffic(args.config + ("" if args.transport == "staged" else "_direct")
+                               + ("_partial" if partial else ""), dom, src_hash)
     gbps_eff = total_bytes / (ms_per_step * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
@@ -510,7 +560,8 @@ def main() -> int:
         "config": {"workload": cfg.describe(), "logical_ranks": N, "tokens_per_rank": T,
                    "hidden": H, "experts": E, "top_k": K, "rows": R,
                    "dispatch_dtype": cfg.dtype, "combine_dtype": "bf16",
-                   "transport": args.transport,
+                   "transport": args.transport, "combine": args.combine,
+                   **({"partial_rows": P} if partial else {}),
                    "parallelism": f"ep{N} (logical ranks on one GPU)"},
         "hbm_gbps_eff": round(gbps_eff, 1),
         "frac_of_hbm_peak": round(gbps_eff / HBM_PEAK_GBPS, 4),
@@ -524,7 +575,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.combine)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -32,8 +32,12 @@ MOE_FP8_E4M3 = 1
 MOE_TRANSPORT_STAGED = 0
 MOE_TRANSPORT_DIRECT = 1
 
+MOE_COMBINE_RECEIVER = 0
+MOE_COMBINE_PARTIAL = 1
+
 KERNELS = ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
-           "combine_reduce", "combine_push"]
+           "combine_reduce", "combine_push", "partial_send", "partial_transfer",
+           "partial_reduce"]
 MOE_KERNEL_COUNT = len(KERNELS)
 MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1
 
@@ -42,7 +46,7 @@ class moe_group_desc(ctypes.Structure):
     _fields_ = [("num_ranks", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("dispatch_dtype", ctypes.c_int32),
-                ("transport", ctypes.c_int32)]
+                ("transport", ctypes.c_int32), ("combine_mode", ctypes.c_int32)]
 
 
 class moe_group_view(ctypes.Structure):
@@ -52,7 +56,8 @@ class moe_group_view(ctypes.Structure):
         (name, ctypes.c_void_p) for name in (
             "cnt", "pos", "send_off", "recv_off", "recv_base", "expert_off", "send_x",
             "send_scale", "send_meta", "recv_x", "recv_scale", "recv_meta",
-            "expert_src_rank", "expert_src_slot", "comb_send", "comb_recv")]
+            "expert_src_rank", "expert_src_slot", "comb_send", "comb_recv", "send_w", "recv_w",
+            "part_dst", "part_pos", "part_send_off", "part_base", "part_owner_base")]
 
 
 class MoeError(RuntimeError):
@@ -76,7 +81,7 @@ def _load():
     sig = {
         "moe_group_create": ([ctypes.POINTER(moe_group_desc), ctypes.POINTER(P)], I),
         "moe_group_destroy": ([P], I),
-        "moe_dispatch_send": ([P, I32, P, P, P], I),
+        "moe_dispatch_send": ([P, I32, P, P, P, P], I),
         "moe_dispatch_recv": ([P, P, P, P, P], I),
         "moe_combine_send": ([P, P, P], I),
         "moe_combine_recv": ([P, P, P, P], I),
@@ -125,9 +130,10 @@ def strerror(status: int) -> str:
 
 def moe_group_create(num_ranks: int, num_experts: int, top_k: int, hidden: int,
                      max_tokens: int, dispatch_dtype: int = MOE_BF16,
-                     transport: int = MOE_TRANSPORT_STAGED) -> int:
+                     transport: int = MOE_TRANSPORT_STAGED,
+                     combine_mode: int = MOE_COMBINE_RECEIVER) -> int:
     desc = moe_group_desc(num_ranks, num_experts, top_k, hidden, max_tokens, dispatch_dtype,
-                          transport)
+                          transport, combine_mode)
     h = ctypes.c_void_p()
     _check(_lib.moe_group_create(ctypes.byref(desc), ctypes.byref(h)), "moe_group_create")
     return h.value
@@ -137,9 +143,10 @@ def moe_group_destroy(g: int) -> None:
     _check(_lib.moe_group_destroy(g), "moe_group_destroy")
 
 
-def moe_dispatch_send(g: int, num_tokens: int, x, topk_idx, stream=None) -> None:
-    _check(_lib.moe_dispatch_send(g, num_tokens, _ptr(x), _ptr(topk_idx), _stream(stream)),
-           "moe_dispatch_send")
+def moe_dispatch_send(g: int, num_tokens: int, x, topk_idx, topk_weights=None,
+                      stream=None) -> None:
+    _check(_lib.moe_dispatch_send(g, num_tokens, _ptr(x), _ptr(topk_idx), _ptr(topk_weights),
+                                  _stream(stream)), "moe_dispatch_send")
 
 
 def moe_dispatch_recv(g: int, expert_x, expert_scale, expert_offsets, stream=None) -> None:

@@ -55,6 +55,8 @@ struct moe_group_s {
     int32_t* recv_meta = nullptr;
     int32_t* src_rank = nullptr;
     int32_t* src_slot = nullptr;
+    float* send_w = nullptr;     // partial combine: router weights beside the rows
+    float* recv_w = nullptr;
 
     State state = State::Idle;
     int32_t T = 0;
@@ -71,6 +73,7 @@ namespace {
 const char* const kKernelNames[MOE_KERNEL_COUNT] = {
     "route_plan_kernel",   "pack_kernel",          "transfer_kernel",       "shuffle_kernel",
     "combine_pack_kernel", "transfer_back_kernel", "combine_reduce_kernel", "combine_push_kernel",
+    "partial_send_kernel", "partial_transfer_kernel", "partial_reduce_kernel",
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -98,6 +101,8 @@ int validate_desc(const moe_group_desc* d)
         return MOE_ERR_INVALID;
     if (d->transport != MOE_TRANSPORT_STAGED && d->transport != MOE_TRANSPORT_DIRECT)
         return MOE_ERR_INVALID;
+    if (d->combine_mode != MOE_COMBINE_RECEIVER && d->combine_mode != MOE_COMBINE_PARTIAL)
+        return MOE_ERR_INVALID;
     const int64_t rows = (int64_t)d->num_ranks * d->max_tokens * d->top_k;
     if (rows >= ((int64_t)1 << 31))
         return MOE_ERR_INVALID;
@@ -115,6 +120,7 @@ moe::Shape shape_of(const moe_group_s* g, int T)
     sh.T = T;
     sh.fp8 = g->desc.dispatch_dtype == MOE_FP8_E4M3;
     sh.direct = g->desc.transport == MOE_TRANSPORT_DIRECT;
+    sh.partial = g->desc.combine_mode == MOE_COMBINE_PARTIAL;
     sh.rows = (int64_t)sh.N * T * sh.K;
     sh.payload_vecs = g->payload_bytes / 16;
     sh.comb_vecs = g->comb_bytes / 16;
@@ -135,6 +141,8 @@ moe::Rows rows_of(const moe_group_s* g)
     r.src_slot = g->src_slot;
     r.comb_send = g->pool_send;
     r.comb_recv = g->pool_recv;
+    r.send_w = g->send_w;
+    r.recv_w = g->recv_w;
     return r;
 }
 
@@ -247,6 +255,7 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
     const size_t R = (size_t)g->rows_max;
     const size_t pool_bytes = R * (size_t)std::max(g->payload_bytes, g->comb_bytes);
     const bool staged = desc->transport == MOE_TRANSPORT_STAGED;   // direct: no send buffer
+    const bool partial = desc->combine_mode == MOE_COMBINE_PARTIAL;
 
     moe::Plan& p = g->plan;
     uint8_t* pool_send = nullptr;
@@ -262,7 +271,14 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
         (staged && (rc = alloc(g, &g->send_meta, R))) || (rc = alloc(g, &g->recv_meta, R)) ||
         (rc = alloc(g, &g->src_rank, R)) || (rc = alloc(g, &g->src_slot, R)) ||
         (fp8 && staged && (rc = alloc(g, &g->send_scale, R * g->scale_blocks))) ||
-        (fp8 && (rc = alloc(g, &g->recv_scale, R * g->scale_blocks)))) {
+        (fp8 && (rc = alloc(g, &g->recv_scale, R * g->scale_blocks))) ||
+        (partial && ((rc = alloc(g, &p.pdst, R)) || (rc = alloc(g, &p.ppos, R)) ||
+                     (rc = alloc(g, &p.psoff, (size_t)N * (N + 1))) ||
+                     (rc = alloc(g, &p.qoff, (size_t)N * (N + 1))) ||
+                     (rc = alloc(g, &p.qbase, (size_t)N + 1)) ||
+                     (rc = alloc(g, &p.pbase, (size_t)N + 1)) ||
+                     (rc = alloc(g, &g->recv_w, R)) ||
+                     (staged && ((rc = alloc(g, &p.pmap, R)) || (rc = alloc(g, &g->send_w, R))))))) {
         free_all(g);
         delete g;
         return rc;
@@ -296,7 +312,7 @@ int moe_group_destroy(moe_group_t g)
 }
 
 int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const int32_t* topk_idx,
-                      hipStream_t stream)
+                      const float* topk_weights, hipStream_t stream)
 {
     if (!g)
         return MOE_ERR_INVALID;
@@ -305,6 +321,9 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const in
     if (num_tokens < 0 || num_tokens > g->desc.max_tokens)
         return MOE_ERR_INVALID;
     if (num_tokens > 0 && (!x || !topk_idx || !aligned16(x) || !aligned16(topk_idx)))
+        return MOE_ERR_INVALID;
+    const bool partial = g->desc.combine_mode == MOE_COMBINE_PARTIAL;
+    if (partial && num_tokens > 0 && (!topk_weights || !aligned16(topk_weights)))
         return MOE_ERR_INVALID;
     int rc = check_device(g);
     if (rc != MOE_OK)
@@ -317,7 +336,8 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const in
              return moe::launch_route_plan(sh, topk_idx, g->plan, L);
          })) ||
         (rc = timed_launch(g, MOE_KERNEL_PACK, stream, any, [&](const Launch& L) {
-             return moe::launch_pack(sh, x, topk_idx, g->plan, rows, L);
+             return moe::launch_pack(sh, x, topk_idx, partial ? topk_weights : nullptr, g->plan,
+                                     rows, L);
          })) ||
         (!sh.direct && (rc = timed_launch(g, MOE_KERNEL_TRANSFER, stream, any, [&](const Launch& L) {
              return moe::launch_transfer(sh, g->plan, rows, L);
@@ -373,7 +393,16 @@ int moe_combine_send(moe_group_t g, const void* expert_y, hipStream_t stream)
     const moe::Shape sh = shape_of(g, g->T);
     const moe::Rows rows = rows_of(g);
     const bool any = sh.rows > 0;
-    if (sh.direct) {
+    if (sh.partial) {
+        if ((rc = timed_launch(g, MOE_KERNEL_PARTIAL_SEND, stream, any, [&](const moe::Launch& L) {
+                 return moe::launch_partial_send(sh, g->plan, rows, expert_y, L);
+             })) ||
+            (!sh.direct &&
+             (rc = timed_launch(g, MOE_KERNEL_PARTIAL_TRANSFER, stream, any, [&](const moe::Launch& L) {
+                  return moe::launch_partial_transfer(sh, g->plan, rows, L);
+              }))))
+            return rc;
+    } else if (sh.direct) {
         if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_PUSH, stream, any, [&](const moe::Launch& L) {
                  return moe::launch_combine_push(sh, g->plan, rows, expert_y, L);
              })))
@@ -396,19 +425,30 @@ int moe_combine_recv(moe_group_t g, const float* topk_weights, void* out, hipStr
         return MOE_ERR_INVALID;
     if (g->state != State::CombineSent)
         return MOE_ERR_STATE;
-    if (g->T > 0 && (!topk_weights || !out || !aligned16(topk_weights) || !aligned16(out)))
+    // with the partial combine the weights were applied on the expert side
+    const bool partial = g->desc.combine_mode == MOE_COMBINE_PARTIAL;
+    if (g->T > 0 && (!out || !aligned16(out)))
+        return MOE_ERR_INVALID;
+    if (!partial && g->T > 0 && (!topk_weights || !aligned16(topk_weights)))
         return MOE_ERR_INVALID;
     int rc = check_device(g);
     if (rc != MOE_OK)
         return rc;
     const moe::Shape sh = shape_of(g, g->T);
     const moe::Rows rows = rows_of(g);
-    if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_REDUCE, stream, sh.rows > 0,
-                           [&](const moe::Launch& L) {
-                               return moe::launch_combine_reduce(sh, g->plan, rows, topk_weights,
-                                                                 out, L);
-                           })))
+    if (partial) {
+        if ((rc = timed_launch(g, MOE_KERNEL_PARTIAL_REDUCE, stream, sh.rows > 0,
+                               [&](const moe::Launch& L) {
+                                   return moe::launch_partial_reduce(sh, g->plan, rows, out, L);
+                               })))
+            return rc;
+    } else if ((rc = timed_launch(g, MOE_KERNEL_COMBINE_REDUCE, stream, sh.rows > 0,
+                                  [&](const moe::Launch& L) {
+                                      return moe::launch_combine_reduce(sh, g->plan, rows,
+                                                                        topk_weights, out, L);
+                                  }))) {
         return rc;
+    }
     g->state = State::Idle;
     return MOE_OK;
 }
@@ -440,6 +480,13 @@ int moe_group_view_get(moe_group_t g, moe_group_view* v)
     v->expert_src_slot = g->src_slot;
     v->comb_send = g->pool_send;
     v->comb_recv = g->pool_recv;
+    v->send_w = g->send_w;
+    v->recv_w = g->recv_w;
+    v->part_dst = g->plan.pdst;
+    v->part_pos = g->plan.ppos;
+    v->part_send_off = g->plan.psoff;
+    v->part_base = g->plan.pbase;
+    v->part_owner_base = g->plan.qbase;
     return MOE_OK;
 }
 

@@ -21,6 +21,7 @@ struct Shape {
     int N, E, K, L, H, T;
     int fp8;              // payload is e4m3 + fp32 block scales
     int direct;           // direct transport: pack and combine write the peer's rows
+    int partial;          // combine sums on the expert side, one row per (token, rank)
     int64_t rows;         // N*T*K
     int payload_vecs;     // 16-byte vectors per payload row (2H/16 or H/16)
     int comb_vecs;        // 16-byte vectors per combine row (2H/16)
@@ -41,6 +42,15 @@ struct Plan {              // device pointers owned by the group
     int2* xfer_dst;        // [rows]  send row -> (its receive row, its expert row)
     int2* shuf_map;        // [rows]  expert row r <- (receive row, source rank)
     int32_t* shuf_inv;     // [rows]  receive row -> its expert row (inverse of shuf_map.x)
+    // combine with expert-side partial sums (null unless Shape::partial)
+    int32_t* pdst;         // [N][T][K]  destination rank of item (s,t,k)
+    int32_t* ppos;         // [N][T][K]  first k of its rank in the token: row among sender
+                           //            s's partial rows (rank-major, then t); else -1
+    int32_t* psoff;        // [N][N+1]   first partial row of (sender s, rank d) among s's
+    int32_t* qoff;         // [N][N+1]   first owner-layout row of sender s among rank d's
+    int32_t* qbase;        // [N+1]      first owner-layout row of rank d (qbase[N] = P)
+    int32_t* pbase;        // [N+1]      first token-layout row of sender s (pbase[N] = P)
+    int32_t* pmap;         // [rows]     token-layout row -> owner-layout row (staged)
 };
 
 struct Rows {              // pooled row buffers
@@ -54,6 +64,8 @@ struct Rows {              // pooled row buffers
     int32_t* src_slot;
     void* comb_send;       // combine rows, receive layout (aliases send_x storage)
     void* comb_recv;       // combine rows, send layout (aliases recv_x storage)
+    float* send_w;         // router weight of each send row (partial combine, staged)
+    float* recv_w;         // router weight of each receive row (partial combine)
 };
 
 // Where and how a kernel is launched: the caller's stream, and optionally a
@@ -66,8 +78,8 @@ struct Launch {
 };
 
 hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, const Launch& L);
-hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const Plan& p,
-                       const Rows& r, const Launch& L);
+hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const float* w,
+                       const Plan& p, const Rows& r, const Launch& L);
 hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, const Launch& L);
 hipError_t launch_shuffle(const Shape& sh, const Plan& p, const Rows& r, void* expert_x,
                           float* expert_scale, int32_t* expert_offsets, const Launch& L);
@@ -78,5 +90,10 @@ hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r,
                                const void* expert_y, const Launch& L);
 hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, const float* w,
                                  void* out, const Launch& L);
+hipError_t launch_partial_send(const Shape& sh, const Plan& p, const Rows& r, const void* expert_y,
+                               const Launch& L);
+hipError_t launch_partial_transfer(const Shape& sh, const Plan& p, const Rows& r, const Launch& L);
+hipError_t launch_partial_reduce(const Shape& sh, const Plan& p, const Rows& r, void* out,
+                                 const Launch& L);
 
 }  // namespace moe

@@ -134,8 +134,38 @@ struct RouteArgs {
     const int32_t* idx;
     int N, T, K, E, L;
     int chunk_waves;        // RP_WAVES, or fewer for large E (LDS budget)
+    int partial;            // also plan the expert-side partial rows
     int64_t cap;
 };
+
+// One column of an [N][stride] offset table, walked down the senders with
+// BATCH loads in flight: .x = sum_s lo[s], and run_out[s] (when given) =
+// sum_{s'<s} (hi - lo)[s'], run_out[N] = .y = the column's total span.
+__device__ int2 walk_column(const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
+                            size_t stride, int N, int32_t* __restrict__ run_out)
+{
+    int base = 0, run = 0;
+    for (int s0 = 0; s0 < N; s0 += BATCH) {
+        int a[BATCH], b[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const size_t row = (size_t)min(s0 + j, N - 1) * stride;
+            a[j] = lo[row];
+            b[j] = hi[row];
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j)
+            if (s0 + j < N) {
+                if (run_out)
+                    run_out[s0 + j] = run;
+                run += b[j] - a[j];
+                base += a[j];
+            }
+    }
+    if (run_out)
+        run_out[N] = run;
+    return make_int2(base, run);
+}
 
 // Every group-wide table is a pass down one column of the send-offset matrix
 // soff[s][*] over the senders s, because soff[s][e] already sums sender s's
@@ -144,15 +174,21 @@ struct RouteArgs {
 //   ebase[s][e]  = eoff[e] + sum_{s'<s} cnt[s'][e]
 //   rbase[d]     = sum_s soff[s][d*L]               (rows received by ranks < d)
 //   roff[d][s]   = sum_{s'<s} (soff[s'][(d+1)L] - soff[s'][dL])
-// so one thread takes one column (E expert columns, the total column E, then
-// N receiver columns) and walks the senders with BATCH loads in flight; no
-// scan across threads.
+// and the partial-row tables are the same walks over psoff[s][*] (one bucket
+// per rank instead of per expert):
+//   qbase[d]     = sum_s psoff[s][d]                (partial rows of ranks < d)
+//   qoff[d][s]   = sum_{s'<s} (psoff[s'][d+1] - psoff[s'][d])
+//   pbase[s]     = sum_{s'<s} psoff[s'][N]          (partial rows of senders < s)
+// so one thread takes one column (E expert columns, the total column E, N
+// receiver columns, then N + 1 partial columns) and walks the senders; no scan
+// across threads.
 __device__ void group_offsets(const RouteArgs& ra, const Plan& p)
 {
     const int N = ra.N, E = ra.E, L = ra.L;
     const int32_t* __restrict__ soff = p.soff;
     const int32_t* __restrict__ cnt = p.cnt;
-    for (int col = threadIdx.x; col < E + 1 + N; col += RP_NT) {
+    const int cols = E + 1 + N + (ra.partial ? N + 1 : 0);
+    for (int col = threadIdx.x; col < cols; col += RP_NT) {
         if (col <= E) {
             // expert column e (col == E: the total, which ends both tables)
             const int e = col;
@@ -194,31 +230,143 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p)
                         run += c[b];
                     }
             }
-        } else {
+        } else if (col <= E + N) {
             const int d = col - E - 1;
-            int base = 0, run = 0;
-            for (int s0 = 0; s0 < N; s0 += BATCH) {
-                int lo[BATCH], hi[BATCH];
-#pragma unroll
-                for (int b = 0; b < BATCH; ++b) {
-                    const size_t row = (size_t)min(s0 + b, N - 1) * (E + 1);
-                    lo[b] = soff[row + d * L];
-                    hi[b] = soff[row + (d + 1) * L];
-                }
-#pragma unroll
-                for (int b = 0; b < BATCH; ++b)
-                    if (s0 + b < N) {
-                        p.roff[(size_t)d * (N + 1) + s0 + b] = run;
-                        run += hi[b] - lo[b];
-                        base += lo[b];
-                    }
-            }
-            p.roff[(size_t)d * (N + 1) + N] = run;
-            p.rbase[d] = base;
-            if ((int64_t)run > ra.cap)
+            const int2 br = walk_column(soff + d * L, soff + (d + 1) * L, E + 1, N,
+                                        p.roff + (size_t)d * (N + 1));
+            p.rbase[d] = br.x;
+            if ((int64_t)br.y > ra.cap)
                 atomicOr(p.err, ERR_BIT_CAPACITY);
+        } else if (col <= E + 2 * N) {
+            const int d = col - E - 1 - N;
+            const int2 br = walk_column(p.psoff + d, p.psoff + d + 1, N + 1, N,
+                                        p.qoff + (size_t)d * (N + 1));
+            p.qbase[d] = br.x;
+        } else {
+            // psoff[s][0] is 0, so this walk is the running sum of the totals
+            const int2 br = walk_column(p.psoff, p.psoff + N, N + 1, N, p.pbase);
+            p.qbase[N] = br.y;
         }
     }
+}
+
+// The counts of one rank's keys sit in cur[0, nkeys): write them out
+// (cnt_out may be null), scan them into off_out[0, nkeys] and leave the
+// exclusive offsets in cur as the cursors of the ranking pass.
+__device__ __forceinline__ void publish_counts(int32_t* cur, int nkeys, int32_t* __restrict__ cnt_out,
+                                               int32_t* __restrict__ off_out, int* wave_sums)
+{
+    const int tid = threadIdx.x;
+    const int per = (nkeys + RP_NT - 1) / RP_NT;
+    const int k0 = tid * per;
+    int local = 0;
+    for (int j = 0; j < per; ++j) {
+        const int k = k0 + j;
+        if (k < nkeys) {
+            const int c = cur[k];
+            if (cnt_out)
+                cnt_out[k] = c;
+            local += c;
+        }
+    }
+    int total;
+    int run = block_exclusive_scan<RP_NT>(local, wave_sums, &total);
+    for (int j = 0; j < per; ++j) {
+        const int k = k0 + j;
+        if (k < nkeys) {
+            const int c = cur[k];
+            off_out[k] = run;
+            cur[k] = run;
+            run += c;
+        }
+    }
+    if (tid == 0)
+        off_out[nkeys] = total;
+    __syncthreads();
+}
+
+// Stable positions, one chunk of CW*64 items at a time (thread tid takes item
+// c*CW*64 + tid of chunk c), two barriers per chunk (masks and cursors
+// double-buffered by chunk parity).  Each lane sets its bit in
+// mask[wave][key] with an LDS 64-bit OR; its rank among equal keys of the
+// chunk is then the set bits of lower waves' masks plus the bits of its own
+// wave's mask below its lane; the per-key cursor advances by the chunk's
+// total into the other buffer.  Keys of the first HELD_CHUNKS chunks come from
+// registers, later ones from key_at(i, mine), which every thread calls.
+// out[i] = the item's position, -1 for an item without a valid key.
+template <typename KeyAt>
+__device__ __forceinline__ void stable_ranks(int items, int nkeys, int CW, uint64_t* mask,
+                                             int32_t* cur, const int (&held)[HELD_CHUNKS],
+                                             KeyAt key_at, int32_t* __restrict__ out)
+{
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+    const int chunk = CW * WAVE;
+    const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
+    for (int c0 = 0, c = 0; c0 < items; c0 += chunk, ++c) {
+        const int A = c & 1;
+        uint64_t* mA = mask + (size_t)A * CW * nkeys;
+        uint64_t* mB = mask + (size_t)(A ^ 1) * CW * nkeys;
+        int32_t* cA = cur + A * nkeys;
+        int32_t* cB = cur + (A ^ 1) * nkeys;
+        const int i = c0 + tid;
+        const bool mine = tid < chunk && i < items;
+        int key = -1;
+#pragma unroll
+        for (int h = 0; h < HELD_CHUNKS; ++h)
+            if (c == h)
+                key = held[h];
+        if (c >= HELD_CHUNKS)
+            key = key_at(i, mine);
+        const bool valid = mine && (unsigned)key < (unsigned)nkeys;
+        if (valid)
+            atomicOr(reinterpret_cast<unsigned long long*>(&mA[(size_t)wave * nkeys + key]),
+                     1ull << lane);
+        for (int j = tid; j < CW * nkeys; j += RP_NT)
+            mB[j] = 0ull;
+        __syncthreads();
+        if (valid) {
+            int before = cA[key] + __popcll(mA[(size_t)wave * nkeys + key] & lanes_below);
+            for (int w = 0; w < wave; ++w)
+                before += __popcll(mA[(size_t)w * nkeys + key]);
+            out[i] = before;
+        } else if (mine) {
+            out[i] = -1;
+        }
+        for (int kk = tid; kk < nkeys; kk += RP_NT) {
+            int add = 0;
+            for (int w = 0; w < CW; ++w)
+                add += __popcll(mA[(size_t)w * nkeys + kk]);
+            cB[kk] = cA[kk] + add;
+        }
+        __syncthreads();
+    }
+}
+
+// Destination rank d = e / L of item i (expert id e; -1 when invalid or not
+// this thread's) and whether it is the first item of its token with that
+// rank.  A token's K items are consecutive and so are a wave's, so its
+// earlier items come from lower lanes by shuffle, or from memory for those
+// before the wave.  Every lane of the wave must call it.
+__device__ __forceinline__ int rank_of_item(const RouteArgs& ra, const int32_t* __restrict__ my_idx,
+                                            int e, int i, bool mine, bool* first)
+{
+    const int lane = lane_id();
+    const int d = (mine && (unsigned)e < (unsigned)ra.E) ? e / ra.L : -1;
+    const int k = i % ra.K;
+    bool f = d >= 0;
+    for (int j = 1; j < ra.K; ++j) {
+        int dj = __shfl(d, max(lane - j, 0), WAVE);
+        if (mine && j <= k) {
+            if (lane < j) {
+                const int ej = my_idx[i - j];
+                dj = (unsigned)ej < (unsigned)ra.E ? ej / ra.L : -1;
+            }
+            if (dj == d)
+                f = false;
+        }
+    }
+    *first = f;
+    return d;
 }
 
 __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
@@ -234,8 +382,7 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     const int s = blockIdx.x;
     const int items = ra.T * ra.K;
     const int32_t* my_idx = ra.idx + (size_t)s * items;
-    int32_t* my_pos = p.pos + (size_t)s * items;
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+    const int tid = threadIdx.x;
     const int chunk = CW * WAVE;
     const int held_items = min(items, HELD_CHUNKS * chunk);
 
@@ -282,76 +429,61 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
         atomicOr(p.err, ERR_BIT_ROUTING);
     __syncthreads();
 
-    // counts out, exclusive scan over experts -> send offsets and cursor
-    const int per = (E + RP_NT - 1) / RP_NT;
-    const int e0 = tid * per;
-    int local = 0;
-    for (int j = 0; j < per; ++j) {
-        const int e = e0 + j;
-        if (e < E) {
-            const int c = cur[e];
-            p.cnt[(size_t)s * E + e] = c;
-            local += c;
-        }
-    }
-    int total;
-    int run = block_exclusive_scan<RP_NT>(local, wave_sums, &total);
-    for (int j = 0; j < per; ++j) {
-        const int e = e0 + j;
-        if (e < E) {
-            const int c = cur[e];
-            p.soff[(size_t)s * (E + 1) + e] = run;
-            cur[e] = run;
-            run += c;
-        }
-    }
-    if (tid == 0)
-        p.soff[(size_t)s * (E + 1) + E] = total;
-    __syncthreads();
+    // counts out, exclusive scan over experts -> send offsets and cursors,
+    // then the stable position of every item inside its expert's rows
+    publish_counts(cur, E, p.cnt + (size_t)s * E, p.soff + (size_t)s * (E + 1), wave_sums);
+    stable_ranks(items, E, CW, mask, cur, held_e,
+                 [&](int i, bool mine) { return mine ? my_idx[i] : -1; },
+                 p.pos + (size_t)s * items);
 
-    // Stable positions, one chunk of CW*64 items at a time, two barriers per
-    // chunk (masks and cursors double-buffered by chunk parity).  Each lane
-    // sets its bit in mask[wave][e] with an LDS 64-bit OR; its rank among
-    // equal ids of the chunk is then the set bits of lower waves' masks plus
-    // the bits of its own wave's mask below its lane; the per-expert cursor
-    // advances by the chunk's total into the other buffer.
-    const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
-    for (int c0 = 0, c = 0; c0 < items; c0 += chunk, ++c) {
-        const int A = c & 1;
-        uint64_t* mA = mask + (size_t)A * CW * E;
-        uint64_t* mB = mask + (size_t)(A ^ 1) * CW * E;
-        int32_t* cA = cur + A * E;
-        int32_t* cB = cur + (A ^ 1) * E;
-        const int i = c0 + tid;
-        const bool mine = tid < chunk && i < items;
-        int e = -1;
+    if (ra.partial) {
+        // Second pass over the same items for the expert-side partial rows:
+        // the key of an item is its destination rank when it is the first of
+        // its token with that rank (one partial row per (token, rank)), none
+        // otherwise.  Counting, scanning and ranking these keys gives each
+        // (token, rank) its row among the sender's partial rows, ordered by
+        // rank, then token.
+        const int N = ra.N;
+        int32_t* my_pdst = p.pdst + (size_t)s * items;
+        for (int d = tid; d < N; d += RP_NT)
+            cur[d] = 0;
+        for (int j = tid; j < CW * N; j += RP_NT)
+            mask[j] = 0ull;
+        __syncthreads();
 #pragma unroll
-        for (int h = 0; h < HELD_CHUNKS; ++h)
-            if (c == h)
-                e = held_e[h];
-        if (c >= HELD_CHUNKS && mine)
-            e = my_idx[i];
-        const bool valid = mine && (unsigned)e < (unsigned)E;
-        if (valid)
-            atomicOr(reinterpret_cast<unsigned long long*>(&mA[(size_t)wave * E + e]), 1ull << lane);
-        for (int j = tid; j < CW * E; j += RP_NT)
-            mB[j] = 0ull;
-        __syncthreads();
-        if (valid) {
-            int before = cA[e] + __popcll(mA[(size_t)wave * E + e] & lanes_below);
-            for (int w = 0; w < wave; ++w)
-                before += __popcll(mA[(size_t)w * E + e]);
-            my_pos[i] = before;
-        } else if (mine) {
-            my_pos[i] = -1;
+        for (int c = 0; c < HELD_CHUNKS; ++c) {
+            if (c * chunk >= items)
+                break;
+            const int i = c * chunk + tid;
+            const bool mine = tid < chunk && i < items;
+            bool first;
+            const int d = rank_of_item(ra, my_idx, held_e[c], i, mine, &first);
+            if (mine)
+                my_pdst[i] = d;
+            held_e[c] = first ? d : -1;
+            if (first)
+                atomicAdd(&cur[d], 1);
         }
-        for (int ee = tid; ee < E; ee += RP_NT) {
-            int add = 0;
-            for (int w = 0; w < CW; ++w)
-                add += __popcll(mA[(size_t)w * E + ee]);
-            cB[ee] = cA[ee] + add;
+        for (int c0 = HELD_CHUNKS * chunk; c0 < items; c0 += chunk) {
+            const int i = c0 + tid;
+            const bool mine = tid < chunk && i < items;
+            bool first;
+            const int d = rank_of_item(ra, my_idx, mine ? my_idx[i] : -1, i, mine, &first);
+            if (mine)
+                my_pdst[i] = d;
+            if (first)
+                atomicAdd(&cur[d], 1);
         }
         __syncthreads();
+        publish_counts(cur, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums);
+        stable_ranks(items, N, CW, mask, cur, held_e,
+                     [&](int i, bool mine) {
+                         bool first;
+                         const int d = rank_of_item(ra, my_idx, mine ? my_idx[i] : -1, i, mine,
+                                                    &first);
+                         return first ? d : -1;
+                     },
+                     p.ppos + (size_t)s * items);
     }
 
     // Publish this rank's counts and draw a ticket.  Every wave waits for its
@@ -445,10 +577,11 @@ __device__ inline void record_maps(const Plan& p, const RowDest& rd, int s)
 
 // Lanes k < K: the destination row of (token, k) in the buffer pack writes
 // (send row, or receive row when direct), -1 if an index check failed; the
-// lead wave also writes the maps and the meta word t*K+k.
+// lead wave also writes the maps, the meta word t*K+k and, for the
+// expert-side partial combine, the router weight (dst_w non-null).
 __device__ inline int pack_dest(const Shape& sh, const Plan& p, const int32_t* __restrict__ idx,
-                                int32_t* __restrict__ dst_meta, int64_t tok, int s, int t,
-                                bool lead)
+                                const float* __restrict__ w, int32_t* __restrict__ dst_meta,
+                                float* __restrict__ dst_w, int64_t tok, int s, int t, bool lead)
 {
     const int lane = lane_id();
     int row = -1;
@@ -460,6 +593,8 @@ __device__ inline int pack_dest(const Shape& sh, const Plan& p, const int32_t* _
             if (lead) {
                 record_maps(p, rd, s);
                 dst_meta[row] = t * sh.K + lane;
+                if (dst_w)
+                    dst_w[row] = w[i];
             }
         } else if (lead) {
             atomicOr(p.err, ERR_BIT_INTERNAL);
@@ -472,8 +607,10 @@ template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan p,
                                                                  const v4u* __restrict__ x,
                                                                  const int32_t* __restrict__ idx,
+                                                                 const float* __restrict__ w,
                                                                  v4u* __restrict__ dst_x,
-                                                                 int32_t* __restrict__ dst_meta)
+                                                                 int32_t* __restrict__ dst_meta,
+                                                                 float* __restrict__ dst_w)
 {
     if (*p.err)
         return;
@@ -484,7 +621,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan 
     if (tok >= (int64_t)sh.N * sh.T)
         return;
     const int s = (int)(tok / sh.T), t = (int)(tok % sh.T);
-    const int my_row = pack_dest(sh, p, idx, dst_meta, tok, s, t, rs.lead);
+    const int my_row = pack_dest(sh, p, idx, w, dst_meta, dst_w, tok, s, t, rs.lead);
     const v4u* src = x + tok * n + rs.b0;
     for (int base = 0; base < rs.len; base += WAVE * U) {
         // the caller's tokens are read with ordinary loads (measured faster
@@ -544,9 +681,11 @@ template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p,
                                                                 const v4u* __restrict__ x,
                                                                 const int32_t* __restrict__ idx,
+                                                                const float* __restrict__ w,
                                                                 v2u* __restrict__ dst_q,
                                                                 float* __restrict__ dst_scale,
-                                                                int32_t* __restrict__ dst_meta)
+                                                                int32_t* __restrict__ dst_meta,
+                                                                float* __restrict__ dst_w)
 {
     if (*p.err)
         return;
@@ -557,7 +696,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
     if (tok >= (int64_t)sh.N * sh.T)
         return;
     const int s = (int)(tok / sh.T), t = (int)(tok % sh.T);
-    const int my_row = pack_dest(sh, p, idx, dst_meta, tok, s, t, rs.lead);
+    const int my_row = pack_dest(sh, p, idx, w, dst_meta, dst_w, tok, s, t, rs.lead);
     const int nb = sh.scale_blocks;
     const v4u* src = x + tok * n;
     for (int base = rs.b0; base < rs.b0 + rs.len; base += WAVE * U) {
@@ -647,7 +786,8 @@ __device__ inline void copy_row(v4u* __restrict__ dst, const v4u* __restrict__ s
 // Modelled transfer ([EFA] "Dispatch and combine": each peer's rows leave as
 // one contiguous write; here rank d's receive row q takes send row
 // xfer_src[q], so every (s -> d) segment is copied contiguously).  Moves the
-// payload, the block scales (e4m3) and the meta word.
+// payload, the block scales (e4m3), the meta word and, for the expert-side
+// partial combine, the router weight.
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p,
                                                                 const v4u* __restrict__ send_x,
@@ -655,7 +795,9 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p
                                                                 const float* __restrict__ send_scale,
                                                                 float* __restrict__ recv_scale,
                                                                 const int32_t* __restrict__ send_meta,
-                                                                int32_t* __restrict__ recv_meta)
+                                                                int32_t* __restrict__ recv_meta,
+                                                                const float* __restrict__ send_w,
+                                                                float* __restrict__ recv_w)
 {
     if (*p.err)
         return;
@@ -674,8 +816,11 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p
     if (sh.fp8)
         for (int j = lane; j < sh.scale_blocks; j += WAVE)
             recv_scale[q * sh.scale_blocks + j] = send_scale[srow * sh.scale_blocks + j];
-    if (lane == 0)
+    if (lane == 0) {
         recv_meta[q] = send_meta[srow];
+        if (send_w)
+            recv_w[q] = send_w[srow];
+    }
 }
 
 // Receive shuffle ([EPMC] "Dispatch": received rows are copied into the
@@ -896,6 +1041,287 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Combine with expert-side partial sums ([EFA] "Dispatch/combine latency":
+// summing on the send side of combine cuts the bytes moved, at some cost in
+// precision).  Reading taken here: the expert owner d sums, for each token
+// routed to it, the weighted outputs of that token's experts held by d (fp32
+// fma chain, k ascending, from +0), rounds the partial once to bf16 and
+// returns one row per (token, rank); the token's owner adds its partials in
+// fp32, rank ascending, from +0, and rounds to bf16.  The router weights
+// travel with the dispatched rows (pack and transfer carry them).
+//
+// Row layouts of the P partial rows (P = pbase[N]):
+//   owner layout  (rank d, sender s, token t): row qbase[d] + qoff[d][s] + rank
+//   token layout  (sender s, rank d, token t): row pbase[s] + ppos
+// where ppos is the route plan's position of the token's first item on d.
+// ---------------------------------------------------------------------------
+
+// One wave group per token (s, t).  Each lane k < K holds the expert row,
+// weight and destination rank of item k; every expert row is loaded once,
+// then each head item (first k of its rank) sums the items of its rank and
+// stores one bf16 row: to the owner layout (staged; the transfer moves it) or
+// straight to the token layout (direct).  The staged lead wave also records
+// pmap[token row] = owner row for the transfer.
+template <int KT, int U, int SPLIT>
+__global__ __launch_bounds__(COPY_THREADS) void partial_send_kernel(Shape sh, Plan p,
+                                                                    const v4u* __restrict__ y,
+                                                                    const float* __restrict__ recv_w,
+                                                                    v4u* __restrict__ dst)
+{
+    if (*p.err)
+        return;
+    const int lane = lane_id();
+    const RowSlot rs = row_slot<SPLIT>(sh.comb_vecs);
+    const int64_t tok = rs.row;
+    if (tok >= (int64_t)sh.N * sh.T)
+        return;
+    const int K = KT > 0 ? KT : sh.K;
+    const int N = sh.N;
+    const int64_t s = tok / sh.T;
+    const int64_t TK = (int64_t)sh.T * sh.K;
+    int my_d = -1, my_row = 0, my_dst = 0;
+    float my_w = 0.0f;
+    bool head = false, bad = false;
+    if (lane < K) {
+        const int64_t i = tok * K + lane;
+        const int pk = p.pos[i];
+        const int pp = p.ppos[i];
+        my_d = p.pdst[i];
+        bad = (uint64_t)pk >= (uint64_t)TK || (unsigned)my_d >= (unsigned)N;
+        if (!bad) {
+            const int2 xd = p.xfer_dst[s * TK + pk];
+            bad = (uint64_t)xd.x >= (uint64_t)sh.rows || (uint64_t)xd.y >= (uint64_t)sh.rows;
+            if (!bad) {
+                my_row = xd.y;
+                my_w = recv_w[xd.x];
+            }
+        }
+        if (!bad && pp >= 0) {
+            head = true;
+            const int P = p.pbase[N];
+            const int tr = p.pbase[s] + pp;
+            const int orow = p.qbase[my_d] + p.qoff[(size_t)my_d * (N + 1) + s] + pp -
+                             p.psoff[(size_t)s * (N + 1) + my_d];
+            bad = (unsigned)tr >= (unsigned)P || (unsigned)orow >= (unsigned)P;
+            my_dst = sh.direct ? tr : orow;
+            if (!bad && rs.lead && !sh.direct)
+                p.pmap[tr] = orow;
+        }
+    }
+    if (__ballot(bad) != 0) {
+        if (lane == 0)
+            atomicOr(p.err, ERR_BIT_INTERNAL);
+        return;
+    }
+    const uint64_t heads = __ballot(head);
+    const int n = rs.len;
+    const int stride = sh.comb_vecs;
+    const v4u* ysrc = y + rs.b0;
+    v4u* out = dst + rs.b0;
+    for (int base = 0; base < n; base += WAVE * U) {
+        if constexpr (KT > 0) {
+            v4u v[KT][U];
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                const v4u* row = ysrc + (int64_t)readlane(my_row, k) * stride;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    v[k][u] = ld_nt(row + min(base + u * WAVE + lane, n - 1));
+            }
+            // keep the raw rows: otherwise each row is widened to fp32 right
+            // after its load, which serialises the loads
+#pragma unroll
+            for (int k = 0; k < KT; ++k)
+                hold(v[k]);
+            for (uint64_t hm = heads; hm != 0; hm &= hm - 1) {
+                const int f = __builtin_ctzll(hm);
+                const int df = readlane(my_d, f);
+                // the rows stay packed until the rank that uses them: pinned
+                // here, the widening to fp32 is not hoisted out of this loop
+                // (which would hold every row as fp32 and halve occupancy)
+#pragma unroll
+                for (int k = 0; k < KT; ++k)
+                    hold(v[k]);
+                float acc[U][8];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[u][e] = 0.0f;
+#pragma unroll
+                for (int k = 0; k < KT; ++k)
+                    if (readlane(my_d, k) == df) {
+                        const float wk = readlane_f(my_w, k);
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+                            fma_row8(acc[u], wk, v[k][u]);
+                    }
+                v4u* o = out + (int64_t)readlane(my_dst, f) * stride;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int j = base + u * WAVE + lane;
+                    if (j < n)
+                        st_nt(pack_bf16x8(acc[u]), o + j);
+                }
+            }
+        } else {
+            for (uint64_t hm = heads; hm != 0; hm &= hm - 1) {
+                const int f = __builtin_ctzll(hm);
+                const int df = readlane(my_d, f);
+                float acc[U][8];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[u][e] = 0.0f;
+                for (int k = f; k < K; ++k)
+                    if (readlane(my_d, k) == df) {
+                        const v4u* row = ysrc + (int64_t)readlane(my_row, k) * stride;
+                        const float wk = readlane_f(my_w, k);
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+                            fma_row8(acc[u], wk, ld_nt(row + min(base + u * WAVE + lane, n - 1)));
+                    }
+                v4u* o = out + (int64_t)readlane(my_dst, f) * stride;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int j = base + u * WAVE + lane;
+                    if (j < n)
+                        st_nt(pack_bf16x8(acc[u]), o + j);
+                }
+            }
+        }
+    }
+}
+
+// Staged transport: the partial rows go back to the token owners, one
+// contiguous segment per (rank -> token owner) pair, as a gather in
+// destination order: token-layout row j takes owner-layout row pmap[j].  The
+// grid covers the largest possible P; rows past the cycle's P exit.
+template <int U, int SPLIT>
+__global__ __launch_bounds__(COPY_THREADS) void partial_transfer_kernel(Shape sh, Plan p,
+                                                                        const v4u* __restrict__ psend,
+                                                                        v4u* __restrict__ precv)
+{
+    if (*p.err)
+        return;
+    const int lane = lane_id();
+    const int n = sh.comb_vecs;
+    const RowSlot rs = row_slot<SPLIT>(n);
+    const int64_t j = rs.row;
+    const int P = p.pbase[sh.N];
+    if (j >= P)
+        return;
+    const int64_t o = p.pmap[j];
+    if ((uint64_t)o >= (uint64_t)P)
+        return;
+    copy_row<U>(precv + j * n + rs.b0, psend + o * n + rs.b0, rs.len, lane);
+}
+
+__device__ inline void add_row8(float (&acc)[8], const v4u& v)
+{
+    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = acc[2 * i] + __uint_as_float(x[i] << 16);
+        acc[2 * i + 1] = acc[2 * i + 1] + __uint_as_float(x[i] & 0xFFFF0000u);
+    }
+}
+
+// The token owner's sum: one wave group per token.  The head lanes (one per
+// rank the token visited) are put in rank order, lane j then holds the row of
+// the j-th partial; the m <= K rows are loaded together (with KT known, the
+// loads past m repeat the last row and are not added) and added in fp32 from
+// +0, then rounded to bf16.
+template <int KT, int U, int SPLIT>
+__global__ __launch_bounds__(COPY_THREADS) void partial_reduce_kernel(Shape sh, Plan p,
+                                                                      const v4u* __restrict__ precv,
+                                                                      v4u* __restrict__ out)
+{
+    if (*p.err)
+        return;
+    const int lane = lane_id();
+    const RowSlot rs = row_slot<SPLIT>(sh.comb_vecs);
+    const int64_t tok = rs.row;
+    if (tok >= (int64_t)sh.N * sh.T)
+        return;
+    const int K = KT > 0 ? KT : sh.K;
+    const int N = sh.N;
+    const int64_t s = tok / sh.T;
+    int my_d = 0, my_row = 0;
+    bool head = false, bad = false;
+    if (lane < K) {
+        const int64_t i = tok * K + lane;
+        const int pp = p.ppos[i];
+        if (pp >= 0) {
+            head = true;
+            my_d = p.pdst[i];
+            my_row = p.pbase[s] + pp;
+            bad = (unsigned)my_d >= (unsigned)N || (unsigned)my_row >= (unsigned)p.pbase[N];
+        }
+    }
+    const uint64_t heads = __ballot(head);
+    if (__ballot(bad) != 0 || heads == 0) {
+        if (lane == 0)
+            atomicOr(p.err, ERR_BIT_INTERNAL);
+        return;
+    }
+    // a token's heads have distinct ranks: order = number of heads below
+    int order = 0;
+    for (uint64_t hm = heads; hm != 0; hm &= hm - 1)
+        if (readlane(my_d, __builtin_ctzll(hm)) < my_d)
+            ++order;
+    int term_row = 0;
+    for (uint64_t hm = heads; hm != 0; hm &= hm - 1) {
+        const int f = __builtin_ctzll(hm);
+        if (lane == readlane(order, f))
+            term_row = readlane(my_row, f);
+    }
+    const int m = __popcll(heads);
+    const int n = rs.len;
+    const int stride = sh.comb_vecs;
+    const v4u* src = precv + rs.b0;
+    v4u* dst = out + tok * stride + rs.b0;
+    for (int base = 0; base < n; base += WAVE * U) {
+        float acc[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc[u][e] = 0.0f;
+        if constexpr (KT > 0) {
+            v4u v[KT][U];
+#pragma unroll
+            for (int j = 0; j < KT; ++j) {
+                const v4u* row = src + (int64_t)readlane(term_row, min(j, m - 1)) * stride;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    v[j][u] = ld_nt(row + min(base + u * WAVE + lane, n - 1));
+            }
+#pragma unroll
+            for (int j = 0; j < KT; ++j)
+                if (j < m)
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        add_row8(acc[u], v[j][u]);
+        } else {
+            for (int j = 0; j < m; ++j) {
+                const v4u* row = src + (int64_t)readlane(term_row, j) * stride;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    add_row8(acc[u], ld_nt(row + min(base + u * WAVE + lane, n - 1)));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * WAVE + lane;
+            if (j < n)
+                st_nt(pack_bf16x8(acc[u]), dst + j);
+        }
+    }
+}
+
 // Launch shape of a row kernel: waves per row (SPLIT) and 16-byte vectors
 // per lane per round (U), from the number of vectors in a row.
 struct RowShape {
@@ -951,6 +1377,7 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     ra.K = sh.K;
     ra.E = sh.E;
     ra.L = sh.L;
+    ra.partial = sh.partial;
     ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
     // two buffers of lane masks take 16 bytes per (wave, expert): 8 waves
     // up to 256 experts, 4 up to 512, 2 above, within 32 KiB of LDS
@@ -961,9 +1388,10 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const Plan& p,
-                       const Rows& r, const Launch& L)
+hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const float* w,
+                       const Plan& p, const Rows& r, const Launch& L)
 {
+    float* dst_w = sh.partial ? (sh.direct ? r.recv_w : r.send_w) : nullptr;
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
         return hipSuccess;
@@ -973,14 +1401,14 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
         RowShape rsh = row_shape(sh.H / 8);
         if (rsh.u > 8)
             rsh.u = 8;
-        MOE_DISPATCH_ROW(rsh, pack_fp8_kernel, tokens, L, sh, p, (const v4u*)x, idx,
+        MOE_DISPATCH_ROW(rsh, pack_fp8_kernel, tokens, L, sh, p, (const v4u*)x, idx, w,
                          (v2u*)(sh.direct ? r.recv_x : r.send_x),
                          sh.direct ? r.recv_scale : r.send_scale,
-                         sh.direct ? r.recv_meta : r.send_meta);
+                         sh.direct ? r.recv_meta : r.send_meta, dst_w);
     } else {
         MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), pack_bf16_kernel, tokens, L, sh, p,
-                         (const v4u*)x, idx, (v4u*)(sh.direct ? r.recv_x : r.send_x),
-                         sh.direct ? r.recv_meta : r.send_meta);
+                         (const v4u*)x, idx, w, (v4u*)(sh.direct ? r.recv_x : r.send_x),
+                         sh.direct ? r.recv_meta : r.send_meta, dst_w);
     }
     return hipGetLastError();
 }
@@ -991,7 +1419,7 @@ hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, const 
         return hipSuccess;
     MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), transfer_kernel, sh.rows, L, sh, p,
                      (const v4u*)r.send_x, (v4u*)r.recv_x, r.send_scale, r.recv_scale,
-                     r.send_meta, r.recv_meta);
+                     r.send_meta, r.recv_meta, sh.partial ? r.send_w : nullptr, r.recv_w);
     return hipGetLastError();
 }
 
@@ -1034,22 +1462,34 @@ hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r, co
     return hipGetLastError();
 }
 
-// The reduce keeps K*U row vectors in flight per lane: U = 4 for the K it is
-// compiled for (measured ~3% faster than U = 2 at K = 8), 2 for any other K;
-// rows are split across waves as for the movers.
-template <int KT, int U>
-static void launch_reduce_k(const Shape& sh, const Plan& p, const v4u* cr, const float* w, v4u* o,
-                            int64_t tokens, const Launch& L)
-{
-    const int split = row_shape(sh.comb_vecs).split;
-    const dim3 grid(row_blocks(tokens, split)), block(COPY_THREADS);
-    if (split == 1)
-        go((combine_reduce_kernel<KT, U, 1>), grid, block, 0, L, sh, p, cr, w, o);
-    else if (split == 2)
-        go((combine_reduce_kernel<KT, U, 2>), grid, block, 0, L, sh, p, cr, w, o);
-    else
-        go((combine_reduce_kernel<KT, U, 4>), grid, block, 0, L, sh, p, cr, w, o);
-}
+// Token kernels (one wave group per token, all K expert rows in flight) are
+// compiled for the common K with UK = 4 vectors per lane per row (the reduce:
+// measured ~3% faster than 2 at K = 8; the partial send: ~2% faster than 2,
+// at 180 VGPRs against 100) and for any other K with U = 2; rows are split
+// across waves as for the movers.
+#define MOE_TOKEN_SPLIT(KERNEL, KT, U, split, grid, block, L, ...)                                  \
+    do {                                                                                           \
+        if ((split) == 1)                                                                          \
+            go((KERNEL<KT, U, 1>), grid, block, 0, L, __VA_ARGS__);                                \
+        else if ((split) == 2)                                                                     \
+            go((KERNEL<KT, U, 2>), grid, block, 0, L, __VA_ARGS__);                                \
+        else                                                                                       \
+            go((KERNEL<KT, U, 4>), grid, block, 0, L, __VA_ARGS__);                                \
+    } while (0)
+
+#define MOE_DISPATCH_TOKEN(sh, KERNEL, UK, tokens, L, ...)                                         \
+    do {                                                                                           \
+        const int split_ = row_shape((sh).comb_vecs).split;                                        \
+        const dim3 grid_(row_blocks((tokens), split_)), block_(COPY_THREADS);                      \
+        switch ((sh).K) {                                                                          \
+        case 1: MOE_TOKEN_SPLIT(KERNEL, 1, UK, split_, grid_, block_, L, __VA_ARGS__); break;      \
+        case 2: MOE_TOKEN_SPLIT(KERNEL, 2, UK, split_, grid_, block_, L, __VA_ARGS__); break;      \
+        case 4: MOE_TOKEN_SPLIT(KERNEL, 4, UK, split_, grid_, block_, L, __VA_ARGS__); break;      \
+        case 6: MOE_TOKEN_SPLIT(KERNEL, 6, UK, split_, grid_, block_, L, __VA_ARGS__); break;      \
+        case 8: MOE_TOKEN_SPLIT(KERNEL, 8, UK, split_, grid_, block_, L, __VA_ARGS__); break;      \
+        default: MOE_TOKEN_SPLIT(KERNEL, 0, 2, split_, grid_, block_, L, __VA_ARGS__); break;      \
+        }                                                                                          \
+    } while (0)
 
 hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, const float* w,
                                  void* out, const Launch& L)
@@ -1057,16 +1497,41 @@ hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, 
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
         return hipSuccess;
-    const v4u* cr = (const v4u*)r.comb_recv;
-    v4u* o = (v4u*)out;
-    switch (sh.K) {
-    case 1: launch_reduce_k<1, 4>(sh, p, cr, w, o, tokens, L); break;
-    case 2: launch_reduce_k<2, 4>(sh, p, cr, w, o, tokens, L); break;
-    case 4: launch_reduce_k<4, 4>(sh, p, cr, w, o, tokens, L); break;
-    case 6: launch_reduce_k<6, 4>(sh, p, cr, w, o, tokens, L); break;
-    case 8: launch_reduce_k<8, 4>(sh, p, cr, w, o, tokens, L); break;
-    default: launch_reduce_k<0, 2>(sh, p, cr, w, o, tokens, L); break;
-    }
+    MOE_DISPATCH_TOKEN(sh, combine_reduce_kernel, 4, tokens, L, sh, p, (const v4u*)r.comb_recv, w,
+                       (v4u*)out);
+    return hipGetLastError();
+}
+
+hipError_t launch_partial_send(const Shape& sh, const Plan& p, const Rows& r, const void* y,
+                               const Launch& L)
+{
+    const int64_t tokens = (int64_t)sh.N * sh.T;
+    if (tokens == 0)
+        return hipSuccess;
+    MOE_DISPATCH_TOKEN(sh, partial_send_kernel, 4, tokens, L, sh, p, (const v4u*)y, r.recv_w,
+                       (v4u*)(sh.direct ? r.comb_recv : r.comb_send));
+    return hipGetLastError();
+}
+
+hipError_t launch_partial_transfer(const Shape& sh, const Plan& p, const Rows& r, const Launch& L)
+{
+    // at most one partial row per (token, rank), and at most K ranks per token
+    const int64_t p_max = (int64_t)sh.N * sh.T * (sh.K < sh.N ? sh.K : sh.N);
+    if (p_max == 0)
+        return hipSuccess;
+    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), partial_transfer_kernel, p_max, L, sh, p,
+                     (const v4u*)r.comb_send, (v4u*)r.comb_recv);
+    return hipGetLastError();
+}
+
+hipError_t launch_partial_reduce(const Shape& sh, const Plan& p, const Rows& r, void* out,
+                                 const Launch& L)
+{
+    const int64_t tokens = (int64_t)sh.N * sh.T;
+    if (tokens == 0)
+        return hipSuccess;
+    MOE_DISPATCH_TOKEN(sh, partial_reduce_kernel, 4, tokens, L, sh, p, (const v4u*)r.comb_recv,
+                       (v4u*)out);
     return hipGetLastError();
 }
 

@@ -83,6 +83,26 @@ typedef enum moe_transport {
     MOE_TRANSPORT_DIRECT = 1
 } moe_transport;
 
+/* Where combine sums the weighted expert outputs:
+ *   MOE_COMBINE_RECEIVER  every expert output returns to the token's owner,
+ *                         which forms the weighted sum of its K rows ([EPMC]
+ *                         "Combine": the receiver computes the weighted
+ *                         average locally).  One fp32 fma chain per token.
+ *   MOE_COMBINE_PARTIAL   each expert owner first sums the outputs of the
+ *                         token's experts it holds and returns one row per
+ *                         (token, rank), fewer bytes at some cost in
+ *                         precision ([EFA] "Dispatch/combine latency": the
+ *                         send-side accumulation of prefill kernels).  The
+ *                         router weights are then given to dispatch_send and
+ *                         travel with the rows.  Rounding: a bf16 partial per
+ *                         (token, rank) (fp32 fma chain, k ascending, from
+ *                         +0), then an fp32 sum of the partials, rank
+ *                         ascending, from +0, rounded to bf16. */
+typedef enum moe_combine_mode {
+    MOE_COMBINE_RECEIVER = 0,
+    MOE_COMBINE_PARTIAL = 1
+} moe_combine_mode;
+
 /* Sizes fixed at creation ([EPMC] "Portable kernels": the maximum number of
  * tokens a rank may dispatch is fixed for the group, and the buffers are
  * reused by every layer).  Limits: 1 <= num_ranks <= 1024; num_experts a
@@ -97,6 +117,7 @@ typedef struct moe_group_desc {
     int32_t max_tokens;     /* T_max per rank */
     int32_t dispatch_dtype; /* moe_dtype */
     int32_t transport;      /* moe_transport */
+    int32_t combine_mode;   /* moe_combine_mode */
 } moe_group_desc;
 
 typedef struct moe_group_s* moe_group_t;
@@ -117,14 +138,19 @@ int moe_group_destroy(moe_group_t g);
  * atomic adds in one block, a cumulative sum for the offsets, rows packed into
  * contiguous per-peer send buffers, then one write per peer; [EPMC] "Dispatch":
  * activations, block scales and the token's index packed together).
- *   num_tokens  T, 0 <= T <= max_tokens (same T on every logical rank)
- *   x           device, bf16 [N][T][H]
- *   topk_idx    device, int32 [N][T][K], expert ids in [0, E)
- * Enqueues: route plan (counts, stable positions, offsets), pack (+ e4m3
- * encode) and, with the staged transport, the transfer into the receive
- * buffers.  Reads x and topk_idx only. */
+ *   num_tokens    T, 0 <= T <= max_tokens (same T on every logical rank)
+ *   x             device, bf16 [N][T][H]
+ *   topk_idx      device, int32 [N][T][K], expert ids in [0, E)
+ *   topk_weights  device, fp32 [N][T][K] with MOE_COMBINE_PARTIAL (carried
+ *                 to the expert owners with the rows); ignored, may be
+ *                 NULL, with MOE_COMBINE_RECEIVER
+ * Enqueues: route plan (counts, stable positions, offsets; with
+ * MOE_COMBINE_PARTIAL also the partial-row plan), pack (+ e4m3 encode) and,
+ * with the staged transport, the transfer into the receive buffers.  Reads
+ * x, topk_idx and topk_weights only. */
 int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x,
-                      const int32_t* topk_idx, hipStream_t stream);
+                      const int32_t* topk_idx, const float* topk_weights,
+                      hipStream_t stream);
 
 /* Dispatch, receive half ([EPMC] "Dispatch": received tokens are copied into
  * contiguous buffers for the grouped GEMM and the source rank, expert and
@@ -145,17 +171,26 @@ int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale,
  * combine": routing is already known, rows go one write per peer).
  *   expert_y  device, bf16 [N*T*K][H], rows in the order of expert_x
  * Enqueues (staged): inverse shuffle into the per-peer layout, transfer back;
- * (direct): one kernel writing each output into its return row. */
+ * (direct): one kernel writing each output into its return row.  With
+ * MOE_COMBINE_PARTIAL: one kernel forming the bf16 partial row of every
+ * (token, rank) from the expert outputs and the carried weights, into the
+ * ranks' return rows (staged) or straight into the token owner's rows
+ * (direct); staged adds the transfer of the partial rows. */
 int moe_combine_send(moe_group_t g, const void* expert_y, hipStream_t stream);
 
 /* Combine, receive half ([EPMC] "Introduction": the output is the sum of the
  * K expert outputs weighted by the router; [EPMC] "Combine": the receiver
  * computes it locally into an externally allocated tensor).
- *   topk_weights  device, fp32 [N][T][K]
+ *   topk_weights  device, fp32 [N][T][K] (MOE_COMBINE_RECEIVER); ignored,
+ *                 may be NULL, with MOE_COMBINE_PARTIAL
  *   out           device, bf16 [N][T][H]
- * out[s][t][h] = bf16_rne(acc) with acc = +0 and, for k = 0..K-1 in order,
- * acc = fma(w[s][t][k], y_k[h], acc) in fp32, y_k the expert output of
- * (s,t,k). */
+ * MOE_COMBINE_RECEIVER: out[s][t][h] = bf16_rne(acc) with acc = +0 and, for
+ * k = 0..K-1 in order, acc = fma(w[s][t][k], y_k[h], acc) in fp32, y_k the
+ * expert output of (s,t,k).
+ * MOE_COMBINE_PARTIAL: out[s][t][h] = bf16_rne(sum over the ranks d the
+ * token visited, d ascending, from +0, in fp32, of its partial row's value);
+ * partial(s,t,d) = bf16_rne(fp32 fma chain from +0 over the k with
+ * topk_idx / L == d, k ascending, of w * y_k). */
 int moe_combine_recv(moe_group_t g, const float* topk_weights, void* out,
                      hipStream_t stream);
 
@@ -164,7 +199,13 @@ int moe_combine_recv(moe_group_t g, const float* topk_weights, void* out,
  * combine; the pooled receive buffer holds recv_x, then comb_recv.  Layouts:
  * send rows of sender s are rows [s*T*K, (s+1)*T*K); receive rows of rank d
  * are rows [recv_base[d], recv_base[d+1]).  With the direct transport there
- * is no send buffer: send_x, send_scale, send_meta and comb_send are NULL. */
+ * is no send buffer: send_x, send_scale, send_meta and comb_send are NULL.
+ * With MOE_COMBINE_PARTIAL the first P = part_base[N] rows of comb_send hold
+ * the partial rows in owner layout (rank d, then sender s, then token t; rank
+ * d's rows start at part_owner_base[d]) and those of comb_recv in token layout
+ * (sender s, then rank d, then token t; row part_base[s] + part_pos[s][t][k]
+ * for the first k of the token on rank d).  The part_* fields and the weight
+ * planes are NULL with MOE_COMBINE_RECEIVER (send_w also with direct). */
 typedef struct moe_group_view {
     moe_group_desc desc;
     int32_t num_tokens;          /* T of the current cycle */
@@ -188,6 +229,14 @@ typedef struct moe_group_view {
     int32_t* expert_src_slot;    /* [rows] t*K+k on the source rank */
     void* comb_send;             /* [rows][combine_row_bytes], receive layout */
     void* comb_recv;             /* [rows][combine_row_bytes], send layout */
+    float* send_w;               /* [rows] router weight of each send row */
+    float* recv_w;               /* [rows] router weight of each receive row */
+    int32_t* part_dst;           /* [N][T][K]  destination rank of item (s,t,k) */
+    int32_t* part_pos;           /* [N][T][K]  row of (s,t,rank) among sender s's partial
+                                    rows for the rank's first k of the token, else -1 */
+    int32_t* part_send_off;      /* [N][N+1]   first partial row of rank d among sender s's */
+    int32_t* part_base;          /* [N+1]      first token-layout partial row of sender s */
+    int32_t* part_owner_base;    /* [N+1]      first owner-layout partial row of rank d */
 } moe_group_view;
 
 int moe_group_view_get(moe_group_t g, moe_group_view* out);
@@ -213,7 +262,10 @@ typedef enum moe_kernel_id {
     MOE_KERNEL_TRANSFER_BACK = 5,
     MOE_KERNEL_COMBINE_REDUCE = 6,
     MOE_KERNEL_COMBINE_PUSH = 7,    /* direct transport: replaces combine pack + transfer back */
-    MOE_KERNEL_COUNT = 8
+    MOE_KERNEL_PARTIAL_SEND = 8,    /* MOE_COMBINE_PARTIAL: the expert-side partial sums */
+    MOE_KERNEL_PARTIAL_TRANSFER = 9,
+    MOE_KERNEL_PARTIAL_REDUCE = 10,
+    MOE_KERNEL_COUNT = 11
 } moe_kernel_id;
 
 typedef enum moe_kernel_mask { MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1 } moe_kernel_mask;

@@ -57,16 +57,18 @@ def to_dev(torch, a: np.ndarray):
 
 
 def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, want_rows=True,
-              transport=0):
+              transport=0, combine_mode=0):
     """One full dispatch + stand-in expert + combine cycle on the GPU.
     Returns a dict of host copies of every buffer (rows only if want_rows;
-    the send-side buffers only with the staged transport)."""
+    the send-side buffers only with the staged transport).  With the partial
+    combine the weights go to dispatch_send, combine_recv gets none, and the
+    partial-row plan and rows are returned too."""
     N, T, K, E, H = cfg.N, inp["idx"].shape[1], cfg.K, cfg.E, cfg.H
     fp8 = cfg.dtype == "fp8"
     T_max = T if T_max is None else T_max
     own = group is None
     g = group if group is not None else mep.moe_group_create(
-        N, E, K, H, T_max, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16, transport)
+        N, E, K, H, T_max, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16, transport, combine_mode)
     try:
         R = N * T * K
         x = to_dev(torch, inp["x"])
@@ -78,7 +80,8 @@ def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, w
                                    device="cuda") if fp8 else None
         expert_offsets = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
         out = torch.empty((N, max(T, 1), H), dtype=torch.bfloat16, device="cuda")
-        mep.moe_dispatch_send(g, T, x, idx)
+        partial = combine_mode == mep.MOE_COMBINE_PARTIAL
+        mep.moe_dispatch_send(g, T, x, idx, w if partial else None)
         mep.moe_dispatch_recv(g, expert_x, expert_scale, expert_offsets)
         torch.cuda.synchronize()
         assert mep.moe_group_status(g) == mep.MOE_OK
@@ -117,12 +120,24 @@ def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, w
                 torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
         y = y.contiguous()
         mep.moe_combine_send(g, y)
-        mep.moe_combine_recv(g, w, out)
+        mep.moe_combine_recv(g, None if partial else w, out)
         torch.cuda.synchronize()
         assert mep.moe_group_status(g) == mep.MOE_OK
         v = mep.moe_group_view_get(g)
-        if want_rows:
-            res["y"] = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        res["y"] = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        if partial:
+            res["part_dst"] = d2h(v.part_dst, (N, T, K), np.int32)
+            res["part_pos"] = d2h(v.part_pos, (N, T, K), np.int32)
+            res["part_send_off"] = d2h(v.part_send_off, (N, N + 1), np.int32)
+            res["part_base"] = d2h(v.part_base, (N + 1,), np.int32)
+            res["part_owner_base"] = d2h(v.part_owner_base, (N + 1,), np.int32)
+            P = int(res["part_base"][N])
+            res["P"] = P
+            if want_rows:
+                if staged:
+                    res["psend"] = d2h(v.comb_send, (P, H), np.uint16)
+                res["precv"] = d2h(v.comb_recv, (P, H), np.uint16)
+        elif want_rows:
             if staged:
                 res["comb_send"] = d2h(v.comb_send, (R, H), np.uint16)
             res["comb_recv"] = d2h(v.comb_recv, (R, H), np.uint16)

@@ -45,19 +45,22 @@ def test_strerror_and_kernel_names(lib):
     assert lib.moe_kernel_name(0) == b"route_plan_kernel"
     assert lib.moe_kernel_name(6) == b"combine_reduce_kernel"
     assert lib.moe_kernel_name(7) == b"combine_push_kernel"
-    assert lib.moe_kernel_name(8) == b""
+    assert lib.moe_kernel_name(8) == b"partial_send_kernel"
+    assert lib.moe_kernel_name(10) == b"partial_reduce_kernel"
+    assert lib.moe_kernel_name(11) == b""
 
 
 def test_host_validation_without_gpu(lib):
     import combine_moe_dispatch_amd as mep
     # descriptor checks happen before any HIP call
     for args in [(2, 7, 2, 256, 16, 0), (0, 8, 2, 256, 16, 0), (2, 8, 2, 100, 16, 0),
-                 (2, 8, 2, 264, 16, 1), (2, 8, 65, 256, 16, 0), (2, 8, 2, 256, 16, 0, 2)]:
+                 (2, 8, 2, 264, 16, 1), (2, 8, 65, 256, 16, 0), (2, 8, 2, 256, 16, 0, 2),
+                 (2, 8, 2, 256, 16, 0, 0, 2)]:
         with pytest.raises(mep.MoeError) as ei:
             mep.moe_group_create(*args)
         assert ei.value.status == mep.MOE_ERR_INVALID
     # a null group handle is rejected by every call
-    assert lib.moe_dispatch_send(None, 1, None, None, None) == mep.MOE_ERR_INVALID
+    assert lib.moe_dispatch_send(None, 1, None, None, None, None) == mep.MOE_ERR_INVALID
     assert lib.moe_group_timing_enable(None, 1) == mep.MOE_ERR_INVALID
     assert lib.moe_group_status(None, None) == mep.MOE_ERR_INVALID
     assert lib.moe_group_destroy(None) == 0

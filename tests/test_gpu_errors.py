@@ -17,14 +17,17 @@ if not torch.cuda.is_available():
 import combine_moe_dispatch_amd as mep  # noqa: E402
 
 
-def test_routing_error_writes_nothing_and_is_reported():
+@pytest.mark.parametrize("combine_mode", [0, 1])
+def test_routing_error_writes_nothing_and_is_reported(combine_mode):
     cfg = CONFIGS["A"]
-    say(f"[gpu] routing error {cfg.describe()}")
+    say(f"[gpu] routing error {cfg.describe()} combine_mode={combine_mode}")
+    partial = combine_mode == mep.MOE_COMBINE_PARTIAL
     inp = make_inputs(cfg)
     bad = inp["idx"].copy()
     bad[1, 3, 1] = cfg.E          # one id out of range
     bad[0, 0, 0] = -1
-    g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16)
+    g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16,
+                             mep.MOE_TRANSPORT_STAGED, combine_mode)
     try:
         R = cfg.rows
         x, idx, w = to_dev(torch, inp["x"]), to_dev(torch, bad), to_dev(torch, inp["w"])
@@ -32,18 +35,23 @@ def test_routing_error_writes_nothing_and_is_reported():
         offs = torch.full((cfg.E + 1,), -7, dtype=torch.int32, device="cuda")
         y = torch.zeros((R, cfg.H), dtype=torch.bfloat16, device="cuda")
         out = torch.full((cfg.N, cfg.T, cfg.H), -1, dtype=torch.int16, device="cuda")
-        mep.moe_dispatch_send(g, cfg.T, x, idx)
+        mep.moe_dispatch_send(g, cfg.T, x, idx, w if partial else None)
         mep.moe_dispatch_recv(g, expert_x, None, offs)
         mep.moe_combine_send(g, y)
-        mep.moe_combine_recv(g, w, out)
+        mep.moe_combine_recv(g, None if partial else w, out)
         assert mep.moe_group_status(g) == mep.MOE_ERR_ROUTING
         assert mep.moe_group_status(g) == mep.MOE_OK          # reading clears it
         assert torch.all(expert_x == -1).item()
         assert torch.all(offs == -7).item()
         assert torch.all(out == -1).item()
         # the group is usable again with valid routing
-        from tests.test_gpu_parity import _compare_all
-        _compare_all(cfg, inp, run_cycle(torch, mep, cfg, inp, group=g))
+        gpu = run_cycle(torch, mep, cfg, inp, group=g, combine_mode=combine_mode)
+        if partial:
+            from tests.test_gpu_partial import _check
+            _check(cfg, inp, gpu)
+        else:
+            from tests.test_gpu_parity import _compare_all
+            _compare_all(cfg, inp, gpu)
     finally:
         mep.moe_group_destroy(g)
 
@@ -109,9 +117,11 @@ def test_kernel_timing_mask():
         mep.moe_group_timing_enable(g, True)
         run_cycle(torch, mep, cfg, inp, group=g, want_rows=False)
         t = mep.moe_group_timing_read(g)
-        # the staged transport runs every kernel but the direct combine push
-        assert all(n == 1 and ms > 0 for k, (ms, n) in t.items() if k != "combine_push"), t
-        assert t["combine_push"][1] == 0
+        # the staged receiver-side combine runs every kernel but the direct
+        # combine push and the partial-combine kernels
+        unused = {"combine_push", "partial_send", "partial_transfer", "partial_reduce"}
+        assert all(n == 1 and ms > 0 for k, (ms, n) in t.items() if k not in unused), t
+        assert all(t[k][1] == 0 for k in unused), t
         mep.moe_group_timing_enable(g, ["transfer", "combine_reduce"])
         run_cycle(torch, mep, cfg, inp, group=g, want_rows=False)
         t = mep.moe_group_timing_read(g)
@@ -119,5 +129,19 @@ def test_kernel_timing_mask():
         mep.moe_group_timing_enable(g, False)
         with pytest.raises(mep.MoeError):
             mep.moe_group_timing_enable(g, 1 << 12)
+    finally:
+        mep.moe_group_destroy(g)
+    # the partial combine: its three kernels replace the combine pack,
+    # transfer back and reduce
+    g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16,
+                             mep.MOE_TRANSPORT_STAGED, mep.MOE_COMBINE_PARTIAL)
+    try:
+        mep.moe_group_timing_enable(g, True)
+        run_cycle(torch, mep, cfg, inp, group=g, want_rows=False,
+                  combine_mode=mep.MOE_COMBINE_PARTIAL)
+        t = mep.moe_group_timing_read(g)
+        ran = {k for k, (ms, n) in t.items() if n}
+        assert ran == {"route_plan", "pack", "transfer", "shuffle", "partial_send",
+                       "partial_transfer", "partial_reduce"}, t
     finally:
         mep.moe_group_destroy(g)

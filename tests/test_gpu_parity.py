@@ -44,8 +44,11 @@ def _compare_all(cfg, inp, gpu, *, identity=False):
             g, o = g.view(np.uint32), o.view(np.uint32)
         bad = np.argwhere(g != o)
         assert bad.size == 0, (k, bad[:5])
-    # combine from the GPU's own expert output (the stand-in is outside the path)
-    c = oracle.run_combine(gpu["y"], inp["w"], d, cfg.H)
+    # combine from the oracle's stand-in expert output, which the GPU's (torch,
+    # outside the path) must equal, given the equal expert rows above
+    y = oracle.expert_standin(d["expert_x"], d["expert_scale"] if fp8 else None, d["eoff"], cfg.H)
+    assert np.array_equal(gpu["y"], y)
+    c = oracle.run_combine(y, inp["w"], d, cfg.H)
     if "comb_send" in gpu:
         assert np.array_equal(gpu["comb_send"], c["comb_send"])
     assert np.array_equal(gpu["comb_recv"], c["comb_recv"])

@@ -1,8 +1,9 @@
 """The DeepSeek-R1 prefill shape with fp8 dispatch at full size (64 ranks x
 2048 tokens x 7168, top-8 of 256 experts: 1 048 576 rows): the integer plan and
-all metadata are compared in full with the oracle; payload rows, block scales
-and combined tokens are compared on a seeded sample, each computed by the
-oracle one at a time."""
+all metadata (and, for the combine with sender-side partial sums, the
+partial-row plan) are compared in full with the oracle; payload rows, block
+scales and combined tokens are compared on a seeded sample, each computed by
+the oracle one at a time."""
 import numpy as np
 import pytest
 
@@ -19,12 +20,15 @@ if not torch.cuda.is_available():
 import combine_moe_dispatch_amd as mep  # noqa: E402
 
 
+@pytest.mark.parametrize("combine_mode", [0, 1])
 @pytest.mark.parametrize("transport", [0, 1])
-def test_prefill_fp8_full_size_sampled(transport):
+def test_prefill_fp8_full_size_sampled(transport, combine_mode):
     cfg = CONFIGS["D"]
+    partial = combine_mode == mep.MOE_COMBINE_PARTIAL
     N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
     R = cfg.rows
-    say(f"[gpu] prefill full size {cfg.describe()} rows={R} transport={transport}")
+    say(f"[gpu] prefill full size {cfg.describe()} rows={R} transport={transport} "
+        f"combine_mode={combine_mode}")
     idx, w = make_routing(cfg)
     x = torch.empty((N, T, H), dtype=torch.int16, device="cuda")
     for s in range(N):
@@ -35,9 +39,9 @@ def test_prefill_fp8_full_size_sampled(transport):
     expert_scale = torch.empty((R, H // 128), dtype=torch.float32, device="cuda")
     offs = torch.empty((E + 1,), dtype=torch.int32, device="cuda")
     out = torch.empty((N, T, H), dtype=torch.bfloat16, device="cuda")
-    g = mep.moe_group_create(N, E, K, H, T, mep.MOE_FP8_E4M3, transport)
+    g = mep.moe_group_create(N, E, K, H, T, mep.MOE_FP8_E4M3, transport, combine_mode)
     try:
-        mep.moe_dispatch_send(g, T, x, d_idx)
+        mep.moe_dispatch_send(g, T, x, d_idx, d_w if partial else None)
         mep.moe_dispatch_recv(g, expert_x, expert_scale, offs)
         torch.cuda.synchronize()
         assert mep.moe_group_status(g) == mep.MOE_OK
@@ -86,14 +90,32 @@ def test_prefill_fp8_full_size_sampled(transport):
             v8 = lut[expert_x[a:b].long()] * expert_scale[a:b].repeat_interleave(128, dim=1)
             y[a:b] = (v8 * (e_of_row + 1).float()[:, None]).to(torch.bfloat16)
         mep.moe_combine_send(g, y)
-        mep.moe_combine_recv(g, d_w, out)
+        mep.moe_combine_recv(g, None if partial else d_w, out)
         torch.cuda.synchronize()
         assert mep.moe_group_status(g) == mep.MOE_OK
+        if partial:
+            say("[gpu] prefill: partial-row plan")
+            v = mep.moe_group_view_get(g)
+            pp = oracle.partial_plan(idx, E)
+            ranks = idx // cfg.L
+            assert np.array_equal(d2h(v.part_dst, (N, T, K), np.int32), ranks)
+            base = d2h(v.part_base, (N + 1,), np.int32)
+            assert base[N] == pp["P"] < R
+            ppos = d2h(v.part_pos, (N, T, K), np.int32)
+            head = ppos >= 0
+            s_i, t_i, _ = np.indices(idx.shape)
+            assert np.array_equal(base[s_i[head]] + ppos[head],
+                                  pp["token_row"][s_i[head], t_i[head], ranks[head]])
+            assert head.sum() == pp["P"]
         rows_of = oracle.expert_rows(idx, pl)
         for _ in range(64):
             s, t = int(gsm.integers(N)), int(gsm.integers(T))
             yk = y[torch.from_numpy(rows_of[s, t].astype(np.int64)).cuda()].view(torch.int16)
-            ref = oracle.combine_token(yk.cpu().numpy().view(np.uint16), w[s, t])
+            yk = yk.cpu().numpy().view(np.uint16)
+            if partial:
+                ref = oracle.partial_token(yk, w[s, t], idx[s, t] // cfg.L)
+            else:
+                ref = oracle.combine_token(yk, w[s, t])
             got = out[s, t].view(torch.int16).cpu().numpy().view(np.uint16)
             assert ulp_dist_bf16(got, ref).max() == 0, (s, t)
     finally:

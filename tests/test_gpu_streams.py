@@ -41,20 +41,20 @@ def test_halves_on_separate_streams_with_concurrent_gemm(transport):
         sent, received, combined = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
         with torch.cuda.stream(other_s):
             gemm = torch.matmul(a, b)                       # runs beside the send half
-        mep.moe_dispatch_send(g, T, x, idx, send_s)
+        mep.moe_dispatch_send(g, T, x, idx, stream=send_s)
         sent.record(send_s)
         recv_s.wait_event(sent)
-        mep.moe_dispatch_recv(g, expert_x, None, offs, recv_s)
+        mep.moe_dispatch_recv(g, expert_x, None, offs, stream=recv_s)
         with torch.cuda.stream(recv_s):
             y = standin_expert(torch, expert_x.view(torch.uint8), None, offs, E, H, False)
         received.record(recv_s)
         send_s.wait_event(received)
         with torch.cuda.stream(other_s):
             gemm2 = torch.matmul(a, b)                      # runs beside the combine send
-        mep.moe_combine_send(g, y, send_s)
+        mep.moe_combine_send(g, y, stream=send_s)
         combined.record(send_s)
         recv_s.wait_event(combined)
-        mep.moe_combine_recv(g, w, out, recv_s)
+        mep.moe_combine_recv(g, w, out, stream=recv_s)
         torch.cuda.synchronize()
         assert mep.moe_group_status(g) == mep.MOE_OK
         d = oracle.run_dispatch(inp["x"], inp["idx"], E)
