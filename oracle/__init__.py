@@ -86,6 +86,11 @@ def _declare(L):
     L.orc_partial_recv.argtypes = [_I, _I, _I, _P, _P, _P]
     L.orc_expert_rows.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
     L.orc_f32_to_e4m3_n.argtypes = [_Z, _P, _P]
+    L.orc_slot_capacity_ok.argtypes = [_I, _I, _I, _P]
+    L.orc_slot_capacity_ok.restype = _I
+    L.orc_slot_rows.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P]
+    L.orc_transfer_slots.argtypes = [_I, _I, _I, _Z, _P, _P, _P, _P]
+    L.orc_shuffle_slots.argtypes = [_I, _I, _I, _Z, _Z, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 
 
 def _p(a: np.ndarray):
@@ -271,6 +276,91 @@ def expert_standin(expert_x: np.ndarray, expert_scale, eoff: np.ndarray, H: int)
     sc = _p(np.ascontiguousarray(expert_scale, dtype=np.float32)) if fp8 else None
     lib().orc_expert_standin(E, H, _p(eoff), _p(expert_x), sc, int(fp8), _p(y))
     return y
+
+
+# ------------------------------------------------- fixed-slot receive layout
+
+def slot_capacity_ok(cnt: np.ndarray, T_max: int) -> bool:
+    """Every (sender, expert) count fits its T_max slots."""
+    cnt = np.ascontiguousarray(cnt, dtype=np.int32)
+    N, E = cnt.shape
+    return bool(lib().orc_slot_capacity_ok(N, E, T_max, _p(cnt)))
+
+
+def slot_rows(idx: np.ndarray, pl: dict, T_max: int) -> np.ndarray:
+    """Slot row of every (s,t,k) in the fixed-slot receive layout, int64 [N][T][K]."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    N, T, K = idx.shape
+    E = pl["cnt"].shape[1]
+    slot = np.zeros((N, T, K), dtype=np.int64)
+    lib().orc_slot_rows(N, T, K, E, T_max, _p(idx), _p(pl["soff"]), _p(pl["pos"]), _p(slot))
+    return slot
+
+
+def transfer_slots(send: np.ndarray, pl: dict, slot: np.ndarray, n_slots: int,
+                   fill: int = 0) -> np.ndarray:
+    """Transfer of one row plane into the fixed-slot receive layout (n_slots
+    rows; slots no row names hold `fill`)."""
+    send = np.ascontiguousarray(send)
+    N, T, K = slot.shape
+    recv = np.full((n_slots,) + send.shape[1:], fill, dtype=send.dtype)
+    row_bytes = send.nbytes // send.shape[0] if send.shape[0] else 0
+    lib().orc_transfer_slots(N, T, K, row_bytes, _p(np.ascontiguousarray(pl["pos"])),
+                             _p(np.ascontiguousarray(slot)), _p(send), _p(recv))
+    return recv
+
+
+def shuffle_slots(recv_x: np.ndarray, recv_scale, recv_meta: np.ndarray, pl: dict, T_max: int,
+                  R: int):
+    """Receive shuffle out of the fixed-slot layout into R expert-order rows."""
+    recv_x = np.ascontiguousarray(recv_x)
+    N, E = pl["cnt"].shape
+    row_bytes = recv_x.nbytes // recv_x.shape[0] if recv_x.shape[0] else 0
+    expert_x = np.zeros((R,) + recv_x.shape[1:], dtype=recv_x.dtype)
+    if recv_scale is not None:
+        recv_scale = np.ascontiguousarray(recv_scale)
+        expert_scale = np.zeros((R,) + recv_scale.shape[1:], dtype=recv_scale.dtype)
+        scale_bytes = recv_scale.nbytes // recv_scale.shape[0]
+        rs, es = _p(recv_scale), _p(expert_scale)
+    else:
+        expert_scale, scale_bytes, rs, es = None, 0, None, None
+    src_rank = np.zeros(R, dtype=np.int32)
+    src_slot = np.zeros(R, dtype=np.int32)
+    lib().orc_shuffle_slots(N, E, T_max, row_bytes, scale_bytes, _p(pl["cnt"]), _p(pl["eoff"]),
+                            _p(recv_x), rs, _p(np.ascontiguousarray(recv_meta, dtype=np.int32)),
+                            _p(expert_x), es, _p(src_rank), _p(src_slot))
+    return expert_x, expert_scale, src_rank, src_slot
+
+
+def run_dispatch_fixed(x: np.ndarray, idx: np.ndarray, E: int, T_max: int,
+                       fp8: bool = False) -> dict:
+    """Every dispatch step with the fixed-slot receive layout: the receive
+    planes have N*E*T_max rows (-1 meta words and zero payload where no row
+    arrived)."""
+    N, T, H = x.shape
+    K = idx.shape[2]
+    pl = plan(idx, E)
+    out = dict(pl)
+    out["capacity_ok"] = slot_capacity_ok(pl["cnt"], T_max)
+    if not out["capacity_ok"]:
+        return out
+    if fp8:
+        send_x, send_scale, send_meta = pack_fp8(x, pl["pos"])
+    else:
+        send_x, send_meta = pack_bf16(x, pl["pos"])
+        send_scale = None
+    slot = slot_rows(idx, pl, T_max)
+    n_slots = N * E * T_max
+    recv_x = transfer_slots(send_x, pl, slot, n_slots)
+    recv_scale = transfer_slots(send_scale, pl, slot, n_slots) if fp8 else None
+    recv_meta = transfer_slots(send_meta, pl, slot, n_slots, fill=-1)
+    R = N * T * K
+    expert_x, expert_scale, src_rank, src_slot = shuffle_slots(recv_x, recv_scale, recv_meta, pl,
+                                                               T_max, R)
+    out.update(slot=slot, send_x=send_x, send_scale=send_scale, send_meta=send_meta,
+               recv_x=recv_x, recv_scale=recv_scale, recv_meta=recv_meta, expert_x=expert_x,
+               expert_scale=expert_scale, expert_src_rank=src_rank, expert_src_slot=src_slot)
+    return out
 
 
 def run_dispatch(x: np.ndarray, idx: np.ndarray, E: int, fp8: bool = False) -> dict:
