@@ -408,6 +408,9 @@ def main() -> int:
     ap.add_argument("--transport", choices=["staged", "direct"], default="staged",
                     help="staged: send buffer + modelled transfer (the measured contract); "
                          "direct: pack/combine write the peer's rows")
+    ap.add_argument("--layout", choices=["packed", "fixed"], default="packed",
+                    help="receive layout: packed at exchanged offsets, or fixed slots per "
+                         "(source, local expert)")
     ap.add_argument("--combine", choices=["receiver", "partial"], default="receiver",
                     help="receiver: the token owner sums all K expert rows; partial: each "
                          "expert owner returns one pre-summed row per (token, rank)")
@@ -476,7 +479,9 @@ def main() -> int:
     transport = mep.MOE_TRANSPORT_DIRECT if args.transport == "direct" else mep.MOE_TRANSPORT_STAGED
     partial = args.combine == "partial"
     g = mep.moe_group_create(N, E, K, H, T, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16, transport,
-                             mep.MOE_COMBINE_PARTIAL if partial else mep.MOE_COMBINE_RECEIVER)
+                             mep.MOE_COMBINE_PARTIAL if partial else mep.MOE_COMBINE_RECEIVER,
+                             mep.MOE_LAYOUT_FIXED_SLOT if args.layout == "fixed"
+                             else mep.MOE_LAYOUT_PACKED)
     stream = torch.cuda.current_stream()
     w_send = w if partial else None          # partial combine: weights go with dispatch
 
@@ -560,7 +565,7 @@ def main() -> int:
         "config": {"workload": cfg.describe(), "logical_ranks": N, "tokens_per_rank": T,
                    "hidden": H, "experts": E, "top_k": K, "rows": R,
                    "dispatch_dtype": cfg.dtype, "combine_dtype": "bf16",
-                   "transport": args.transport, "combine": args.combine,
+                   "transport": args.transport, "combine": args.combine, "layout": args.layout,
                    **({"partial_rows": P} if partial else {}),
                    "parallelism": f"ep{N} (logical ranks on one GPU)"},
         "hbm_gbps_eff": round(gbps_eff, 1),

@@ -35,6 +35,9 @@ MOE_TRANSPORT_DIRECT = 1
 MOE_COMBINE_RECEIVER = 0
 MOE_COMBINE_PARTIAL = 1
 
+MOE_LAYOUT_PACKED = 0
+MOE_LAYOUT_FIXED_SLOT = 1
+
 KERNELS = ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
            "combine_reduce", "combine_push", "partial_send", "partial_transfer",
            "partial_reduce"]
@@ -46,7 +49,8 @@ class moe_group_desc(ctypes.Structure):
     _fields_ = [("num_ranks", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("dispatch_dtype", ctypes.c_int32),
-                ("transport", ctypes.c_int32), ("combine_mode", ctypes.c_int32)]
+                ("transport", ctypes.c_int32), ("combine_mode", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 class moe_group_view(ctypes.Structure):
@@ -57,7 +61,8 @@ class moe_group_view(ctypes.Structure):
             "cnt", "pos", "send_off", "recv_off", "recv_base", "expert_off", "send_x",
             "send_scale", "send_meta", "recv_x", "recv_scale", "recv_meta",
             "expert_src_rank", "expert_src_slot", "comb_send", "comb_recv", "send_w", "recv_w",
-            "part_dst", "part_pos", "part_send_off", "part_base", "part_owner_base")]
+            "part_dst", "part_pos", "part_send_off", "part_base", "part_owner_base")] + [
+        ("recv_rows", ctypes.c_int64)]
 
 
 class MoeError(RuntimeError):
@@ -131,9 +136,10 @@ def strerror(status: int) -> str:
 def moe_group_create(num_ranks: int, num_experts: int, top_k: int, hidden: int,
                      max_tokens: int, dispatch_dtype: int = MOE_BF16,
                      transport: int = MOE_TRANSPORT_STAGED,
-                     combine_mode: int = MOE_COMBINE_RECEIVER) -> int:
+                     combine_mode: int = MOE_COMBINE_RECEIVER,
+                     layout: int = MOE_LAYOUT_PACKED) -> int:
     desc = moe_group_desc(num_ranks, num_experts, top_k, hidden, max_tokens, dispatch_dtype,
-                          transport, combine_mode)
+                          transport, combine_mode, layout)
     h = ctypes.c_void_p()
     _check(_lib.moe_group_create(ctypes.byref(desc), ctypes.byref(h)), "moe_group_create")
     return h.value

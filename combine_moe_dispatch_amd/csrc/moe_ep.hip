@@ -16,6 +16,11 @@
 // the exchanged counts.  The same two pools carry the combine rows, as the
 // pages reuse buffers between dispatch and combine ([EFA] "Dispatch and
 // combine").  Row size of a pool = max(payload row, 2H) = 2H bytes.
+//
+// With the fixed-slot layout ([EPMC] "Portable kernels") the receive pool and
+// its planes instead hold one region of T_max slots per (receiver, source,
+// local expert): N*E*T_max rows.  The direct transport has no send pool; the
+// partial combine's rows (at most N*T*K) reuse whichever pools combine uses.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -42,6 +47,7 @@ struct moe_group_s {
     int device = 0;
     int L = 0;
     int64_t rows_max = 0;
+    int64_t recv_rows_max = 0;  // rows of the receive planes
     int payload_bytes = 0;   // per row
     int comb_bytes = 0;
     int scale_blocks = 0;
@@ -103,8 +109,13 @@ int validate_desc(const moe_group_desc* d)
         return MOE_ERR_INVALID;
     if (d->combine_mode != MOE_COMBINE_RECEIVER && d->combine_mode != MOE_COMBINE_PARTIAL)
         return MOE_ERR_INVALID;
+    if (d->layout != MOE_LAYOUT_PACKED && d->layout != MOE_LAYOUT_FIXED_SLOT)
+        return MOE_ERR_INVALID;
     const int64_t rows = (int64_t)d->num_ranks * d->max_tokens * d->top_k;
     if (rows >= ((int64_t)1 << 31))
+        return MOE_ERR_INVALID;
+    const int64_t slots = (int64_t)d->num_ranks * d->num_experts * d->max_tokens;
+    if (d->layout == MOE_LAYOUT_FIXED_SLOT && slots >= ((int64_t)1 << 31))
         return MOE_ERR_INVALID;
     return MOE_OK;
 }
@@ -121,7 +132,10 @@ moe::Shape shape_of(const moe_group_s* g, int T)
     sh.fp8 = g->desc.dispatch_dtype == MOE_FP8_E4M3;
     sh.direct = g->desc.transport == MOE_TRANSPORT_DIRECT;
     sh.partial = g->desc.combine_mode == MOE_COMBINE_PARTIAL;
+    sh.fixed = g->desc.layout == MOE_LAYOUT_FIXED_SLOT;
+    sh.slots = g->desc.max_tokens;
     sh.rows = (int64_t)sh.N * T * sh.K;
+    sh.recv_rows = sh.fixed ? g->recv_rows_max : sh.rows;
     sh.payload_vecs = g->payload_bytes / 16;
     sh.comb_vecs = g->comb_bytes / 16;
     sh.scale_blocks = g->scale_blocks;
@@ -139,8 +153,13 @@ moe::Rows rows_of(const moe_group_s* g)
     r.recv_meta = g->recv_meta;
     r.src_rank = g->src_rank;
     r.src_slot = g->src_slot;
-    r.comb_send = g->pool_send;
-    r.comb_recv = g->pool_recv;
+    // combine rows: the receive layout in the send pool and the send layout
+    // in the receive pool; the fixed-slot receive layout is larger than the
+    // send pool, so with it the two swap (direct push has no send pool)
+    const bool swap = g->desc.layout == MOE_LAYOUT_FIXED_SLOT &&
+                      g->desc.transport == MOE_TRANSPORT_STAGED;
+    r.comb_send = swap ? g->pool_recv : g->pool_send;
+    r.comb_recv = swap ? g->pool_send : g->pool_recv;
     r.send_w = g->send_w;
     r.recv_w = g->recv_w;
     return r;
@@ -248,12 +267,17 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
     const int T = desc->max_tokens;
     g->L = E / N;
     g->rows_max = (int64_t)N * T * K;
+    const bool fixed = desc->layout == MOE_LAYOUT_FIXED_SLOT;
+    // the receive pool also takes combine's send-layout rows (direct push),
+    // and N*E*T_max < N*T_max*K when K > E
+    g->recv_rows_max = fixed ? std::max((int64_t)N * E * T, g->rows_max) : g->rows_max;
     const bool fp8 = desc->dispatch_dtype == MOE_FP8_E4M3;
     g->payload_bytes = fp8 ? H : 2 * H;
     g->comb_bytes = 2 * H;
     g->scale_blocks = fp8 ? H / 128 : 0;
     const size_t R = (size_t)g->rows_max;
-    const size_t pool_bytes = R * (size_t)std::max(g->payload_bytes, g->comb_bytes);
+    const size_t RQ = (size_t)g->recv_rows_max;
+    const size_t row_bytes = (size_t)std::max(g->payload_bytes, g->comb_bytes);
     const bool staged = desc->transport == MOE_TRANSPORT_STAGED;   // direct: no send buffer
     const bool partial = desc->combine_mode == MOE_COMBINE_PARTIAL;
 
@@ -267,17 +291,19 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
         (rc = alloc(g, &p.eoff, (size_t)E + 1)) || (rc = alloc(g, &p.ebase, (size_t)N * E)) ||
         (rc = alloc(g, &p.xfer_src, R)) || (rc = alloc(g, &p.xfer_dst, R)) ||
         (rc = alloc(g, &p.shuf_map, R)) || (rc = alloc(g, &p.shuf_inv, R)) ||
-        (staged && (rc = alloc(g, &pool_send, pool_bytes))) || (rc = alloc(g, &pool_recv, pool_bytes)) ||
-        (staged && (rc = alloc(g, &g->send_meta, R))) || (rc = alloc(g, &g->recv_meta, R)) ||
+        (staged && (rc = alloc(g, &pool_send, R * row_bytes))) ||
+        (rc = alloc(g, &pool_recv, RQ * row_bytes)) ||
+        (staged && (rc = alloc(g, &g->send_meta, R))) || (rc = alloc(g, &g->recv_meta, RQ)) ||
         (rc = alloc(g, &g->src_rank, R)) || (rc = alloc(g, &g->src_slot, R)) ||
         (fp8 && staged && (rc = alloc(g, &g->send_scale, R * g->scale_blocks))) ||
-        (fp8 && (rc = alloc(g, &g->recv_scale, R * g->scale_blocks))) ||
+        (fp8 && (rc = alloc(g, &g->recv_scale, RQ * g->scale_blocks))) ||
+        (fixed && (rc = alloc(g, &p.slot_of, R))) ||
         (partial && ((rc = alloc(g, &p.pdst, R)) || (rc = alloc(g, &p.ppos, R)) ||
                      (rc = alloc(g, &p.psoff, (size_t)N * (N + 1))) ||
                      (rc = alloc(g, &p.qoff, (size_t)N * (N + 1))) ||
                      (rc = alloc(g, &p.qbase, (size_t)N + 1)) ||
                      (rc = alloc(g, &p.pbase, (size_t)N + 1)) ||
-                     (rc = alloc(g, &g->recv_w, R)) ||
+                     (rc = alloc(g, &g->recv_w, RQ)) ||
                      (staged && ((rc = alloc(g, &p.pmap, R)) || (rc = alloc(g, &g->send_w, R))))))) {
         free_all(g);
         delete g;
@@ -478,8 +504,10 @@ int moe_group_view_get(moe_group_t g, moe_group_view* v)
     v->recv_meta = g->recv_meta;
     v->expert_src_rank = g->src_rank;
     v->expert_src_slot = g->src_slot;
-    v->comb_send = g->pool_send;
-    v->comb_recv = g->pool_recv;
+    const moe::Rows r = rows_of(g);
+    v->comb_send = r.comb_send;
+    v->comb_recv = r.comb_recv;
+    v->recv_rows = g->recv_rows_max;
     v->send_w = g->send_w;
     v->recv_w = g->recv_w;
     v->part_dst = g->plan.pdst;

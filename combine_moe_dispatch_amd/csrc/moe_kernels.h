@@ -22,6 +22,10 @@ struct Shape {
     int fp8;              // payload is e4m3 + fp32 block scales
     int direct;           // direct transport: pack and combine write the peer's rows
     int partial;          // combine sums on the expert side, one row per (token, rank)
+    int fixed;            // fixed-slot receive layout: one region of `slots` rows per
+                          // (receiver, source, local expert)
+    int slots;            // T_max (fixed-slot layout)
+    int64_t recv_rows;    // rows of the receive planes: rows, or N*E*slots (fixed-slot)
     int64_t rows;         // N*T*K
     int payload_vecs;     // 16-byte vectors per payload row (2H/16 or H/16)
     int comb_vecs;        // 16-byte vectors per combine row (2H/16)
@@ -38,10 +42,13 @@ struct Plan {              // device pointers owned by the group
     int32_t* rbase;        // [N+1]
     int32_t* eoff;         // [E+1]
     int32_t* ebase;        // [N][E]  first expert-order row of (sender s, expert e)
-    int32_t* xfer_src;     // [rows]  receive row q <- send row xfer_src[q]
-    int2* xfer_dst;        // [rows]  send row -> (its receive row, its expert row)
-    int2* shuf_map;        // [rows]  expert row r <- (receive row, source rank)
-    int32_t* shuf_inv;     // [rows]  receive row -> its expert row (inverse of shuf_map.x)
+    // Receive rows are numbered in the packed order q (rank, source, expert,
+    // t, k); with the fixed-slot layout a row's place in the receive planes
+    // is slot_of[q], otherwise q itself.
+    int32_t* xfer_src;     // [rows]  packed receive row q <- send row xfer_src[q]
+    int2* xfer_dst;        // [rows]  send row -> (its receive-plane row, its expert row)
+    int2* shuf_map;        // [rows]  expert row r <- (receive-plane row, source rank)
+    int32_t* shuf_inv;     // [rows]  packed receive row -> its expert row
     // combine with expert-side partial sums (null unless Shape::partial)
     int32_t* pdst;         // [N][T][K]  destination rank of item (s,t,k)
     int32_t* ppos;         // [N][T][K]  first k of its rank in the token: row among sender
@@ -51,6 +58,7 @@ struct Plan {              // device pointers owned by the group
     int32_t* qbase;        // [N+1]      first owner-layout row of rank d (qbase[N] = P)
     int32_t* pbase;        // [N+1]      first token-layout row of sender s (pbase[N] = P)
     int32_t* pmap;         // [rows]     token-layout row -> owner-layout row (staged)
+    int32_t* slot_of;      // [rows]     packed receive row -> its slot (fixed-slot layout)
 };
 
 struct Rows {              // pooled row buffers

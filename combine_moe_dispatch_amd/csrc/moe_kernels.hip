@@ -135,6 +135,7 @@ struct RouteArgs {
     int N, T, K, E, L;
     int chunk_waves;        // RP_WAVES, or fewer for large E (LDS budget)
     int partial;            // also plan the expert-side partial rows
+    int slot_cap;           // fixed-slot layout: most rows per (sender, expert); -1: none
     int64_t cap;
 };
 
@@ -252,9 +253,11 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p)
 
 // The counts of one rank's keys sit in cur[0, nkeys): write them out
 // (cnt_out may be null), scan them into off_out[0, nkeys] and leave the
-// exclusive offsets in cur as the cursors of the ranking pass.
+// exclusive offsets in cur as the cursors of the ranking pass.  A count above
+// cap (when cap >= 0) raises the capacity bit.
 __device__ __forceinline__ void publish_counts(int32_t* cur, int nkeys, int32_t* __restrict__ cnt_out,
-                                               int32_t* __restrict__ off_out, int* wave_sums)
+                                               int32_t* __restrict__ off_out, int* wave_sums,
+                                               int cap, int32_t* err)
 {
     const int tid = threadIdx.x;
     const int per = (nkeys + RP_NT - 1) / RP_NT;
@@ -266,6 +269,8 @@ __device__ __forceinline__ void publish_counts(int32_t* cur, int nkeys, int32_t*
             const int c = cur[k];
             if (cnt_out)
                 cnt_out[k] = c;
+            if (cap >= 0 && c > cap)
+                atomicOr(err, ERR_BIT_CAPACITY);
             local += c;
         }
     }
@@ -431,7 +436,8 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
 
     // counts out, exclusive scan over experts -> send offsets and cursors,
     // then the stable position of every item inside its expert's rows
-    publish_counts(cur, E, p.cnt + (size_t)s * E, p.soff + (size_t)s * (E + 1), wave_sums);
+    publish_counts(cur, E, p.cnt + (size_t)s * E, p.soff + (size_t)s * (E + 1), wave_sums,
+                   ra.slot_cap, p.err);
     stable_ranks(items, E, CW, mask, cur, held_e,
                  [&](int i, bool mine) { return mine ? my_idx[i] : -1; },
                  p.pos + (size_t)s * items);
@@ -475,7 +481,7 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
                 atomicAdd(&cur[d], 1);
         }
         __syncthreads();
-        publish_counts(cur, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums);
+        publish_counts(cur, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums, -1, p.err);
         stable_ranks(items, N, CW, mask, cur, held_e,
                      [&](int i, bool mine) {
                          bool first;
@@ -549,10 +555,13 @@ __device__ inline RowSlot row_slot(int n)
 // buffers ([EFA] "Dispatch and combine").
 // ---------------------------------------------------------------------------
 struct RowDest {
-    int32_t srow, q, r;
+    int32_t srow, q, qd, r;   // send row, packed receive row, receive-plane row, expert row
     bool ok;
 };
 
+// With the fixed-slot layout ([EPMC] "Portable kernels") the receive-plane
+// row needs only the sender's own offsets: slot pk - soff[s][e] of region
+// (d, s, e - d*L).
 __device__ inline RowDest row_dest(const Shape& sh, const Plan& p, int s, int e, int pk)
 {
     const int64_t TK = (int64_t)sh.T * sh.K;
@@ -562,17 +571,23 @@ __device__ inline RowDest row_dest(const Shape& sh, const Plan& p, int s, int e,
     const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
     rd.q = p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + pk - so[d * sh.L];
     rd.r = p.ebase[(size_t)s * sh.E + e] + pk - so[e];
+    const int i = pk - so[e];
+    const int64_t slot = (((int64_t)d * sh.N + s) * sh.L + (e - d * sh.L)) * sh.slots + i;
+    rd.qd = sh.fixed ? (int32_t)slot : rd.q;
     rd.ok = (uint64_t)rd.q < (uint64_t)sh.rows && (uint64_t)rd.r < (uint64_t)sh.rows &&
-            (uint64_t)pk < (uint64_t)TK;
+            (uint64_t)pk < (uint64_t)TK &&
+            (!sh.fixed || ((uint32_t)i < (uint32_t)sh.slots && (uint64_t)slot < (uint64_t)sh.recv_rows));
     return rd;
 }
 
-__device__ inline void record_maps(const Plan& p, const RowDest& rd, int s)
+__device__ inline void record_maps(const Shape& sh, const Plan& p, const RowDest& rd, int s)
 {
     p.xfer_src[rd.q] = rd.srow;
-    p.xfer_dst[rd.srow] = make_int2(rd.q, rd.r);
-    p.shuf_map[rd.r] = make_int2(rd.q, s);
+    p.xfer_dst[rd.srow] = make_int2(rd.qd, rd.r);
+    p.shuf_map[rd.r] = make_int2(rd.qd, s);
     p.shuf_inv[rd.q] = rd.r;
+    if (sh.fixed)
+        p.slot_of[rd.q] = rd.qd;
 }
 
 // Lanes k < K: the destination row of (token, k) in the buffer pack writes
@@ -589,9 +604,9 @@ __device__ inline int pack_dest(const Shape& sh, const Plan& p, const int32_t* _
         const int64_t i = tok * sh.K + lane;
         const RowDest rd = row_dest(sh, p, s, idx[i], p.pos[i]);
         if (rd.ok) {
-            row = sh.direct ? rd.q : rd.srow;
+            row = sh.direct ? rd.qd : rd.srow;
             if (lead) {
-                record_maps(p, rd, s);
+                record_maps(sh, p, rd, s);
                 dst_meta[row] = t * sh.K + lane;
                 if (dst_w)
                     dst_w[row] = w[i];
@@ -633,7 +648,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan 
         hold(v);
         for (int k = 0; k < sh.K; ++k) {
             const int row = readlane(my_row, k);
-            if ((uint64_t)row >= (uint64_t)sh.rows)
+            if ((uint64_t)row >= (uint64_t)(sh.direct ? sh.recv_rows : sh.rows))
                 continue;
             v4u* dst = dst_x + (int64_t)row * n + rs.b0;
 #pragma unroll
@@ -743,7 +758,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
         }
         for (int k = 0; k < sh.K; ++k) {
             const int row32 = readlane(my_row, k);
-            if ((uint64_t)row32 >= (uint64_t)sh.rows)
+            if ((uint64_t)row32 >= (uint64_t)(sh.direct ? sh.recv_rows : sh.rows))
                 continue;
             const int64_t row = row32;
 #pragma unroll
@@ -804,11 +819,12 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p
     const int lane = lane_id();
     const int n = sh.payload_vecs;
     const RowSlot rs = row_slot<SPLIT>(n);
-    const int64_t q = rs.row;
-    if (q >= sh.rows)
+    const int64_t qp = rs.row;
+    if (qp >= sh.rows)
         return;
-    const int64_t srow = p.xfer_src[q];
-    if ((uint64_t)srow >= (uint64_t)sh.rows)
+    const int64_t srow = p.xfer_src[qp];
+    const int64_t q = sh.fixed ? (int64_t)p.slot_of[qp] : qp;
+    if ((uint64_t)srow >= (uint64_t)sh.rows || (uint64_t)q >= (uint64_t)sh.recv_rows)
         return;
     copy_row<U>(recv_x + q * n + rs.b0, send_x + srow * n + rs.b0, rs.len, lane);
     if (!rs.lead)
@@ -852,7 +868,7 @@ __global__ __launch_bounds__(COPY_THREADS) void shuffle_kernel(Shape sh, Plan p,
         return;
     const int2 m = p.shuf_map[r];
     const int64_t q = m.x;
-    if ((uint64_t)q >= (uint64_t)sh.rows)
+    if ((uint64_t)q >= (uint64_t)sh.recv_rows)
         return;
     copy_row<U>(expert_x + r * n + rs.b0, recv_x + q * n + rs.b0, rs.len, lane);
     if (!rs.lead)
@@ -880,11 +896,12 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_pack_kernel(Shape sh, Pl
     const int lane = lane_id();
     const int n = sh.comb_vecs;
     const RowSlot rs = row_slot<SPLIT>(n);
-    const int64_t q = rs.row;
-    if (q >= sh.rows)
+    const int64_t qp = rs.row;
+    if (qp >= sh.rows)
         return;
-    const int64_t r = p.shuf_inv[q];
-    if ((uint64_t)r >= (uint64_t)sh.rows)
+    const int64_t r = p.shuf_inv[qp];
+    const int64_t q = sh.fixed ? (int64_t)p.slot_of[qp] : qp;
+    if ((uint64_t)r >= (uint64_t)sh.rows || (uint64_t)q >= (uint64_t)sh.recv_rows)
         return;
     copy_row<U>(comb_send + q * n + rs.b0, y + r * n + rs.b0, rs.len, lane);
 }
@@ -906,7 +923,7 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, P
     if (srow >= sh.rows)
         return;
     const int64_t q = p.xfer_dst[srow].x;
-    if ((uint64_t)q >= (uint64_t)sh.rows)
+    if ((uint64_t)q >= (uint64_t)sh.recv_rows)
         return;
     copy_row<U>(comb_recv + srow * n + rs.b0, comb_send + q * n + rs.b0, rs.len, lane);
 }
@@ -1091,7 +1108,7 @@ __global__ __launch_bounds__(COPY_THREADS) void partial_send_kernel(Shape sh, Pl
         bad = (uint64_t)pk >= (uint64_t)TK || (unsigned)my_d >= (unsigned)N;
         if (!bad) {
             const int2 xd = p.xfer_dst[s * TK + pk];
-            bad = (uint64_t)xd.x >= (uint64_t)sh.rows || (uint64_t)xd.y >= (uint64_t)sh.rows;
+            bad = (uint64_t)xd.x >= (uint64_t)sh.recv_rows || (uint64_t)xd.y >= (uint64_t)sh.rows;
             if (!bad) {
                 my_row = xd.y;
                 my_w = recv_w[xd.x];
@@ -1378,6 +1395,7 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     ra.E = sh.E;
     ra.L = sh.L;
     ra.partial = sh.partial;
+    ra.slot_cap = sh.fixed ? sh.slots : -1;
     ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
     // two buffers of lane masks take 16 bytes per (wave, expert): 8 waves
     // up to 256 experts, 4 up to 512, 2 above, within 32 KiB of LDS

@@ -103,12 +103,35 @@ typedef enum moe_combine_mode {
     MOE_COMBINE_PARTIAL = 1
 } moe_combine_mode;
 
+/* Layout of the receive buffers:
+ *   MOE_LAYOUT_PACKED      rank d's receive rows are contiguous at bases
+ *                          computed from the exchanged counts, sources
+ *                          ascending ([EFA] "Send and receive buffers").
+ *   MOE_LAYOUT_FIXED_SLOT  rank d holds one region of max_tokens slots per
+ *                          (source rank, local expert), at row
+ *                          ((d*N + s)*L + j)*max_tokens; a sender writes its
+ *                          i-th row for expert e = d*L + j to slot i, an
+ *                          address it knows from its own counts ([EPMC]
+ *                          "Portable kernels": the fixed token maximum bounds
+ *                          each (source, local expert) share).  The receive
+ *                          buffers then have N*E*max_tokens rows.  A sender
+ *                          with more than max_tokens rows for one expert
+ *                          (only possible when a token names an expert twice)
+ *                          raises MOE_ERR_CAPACITY and the cycle writes
+ *                          nothing.  dispatch_recv's outputs are the same as
+ *                          with MOE_LAYOUT_PACKED. */
+typedef enum moe_layout {
+    MOE_LAYOUT_PACKED = 0,
+    MOE_LAYOUT_FIXED_SLOT = 1
+} moe_layout;
+
 /* Sizes fixed at creation ([EPMC] "Portable kernels": the maximum number of
  * tokens a rank may dispatch is fixed for the group, and the buffers are
  * reused by every layer).  Limits: 1 <= num_ranks <= 1024; num_experts a
  * multiple of num_ranks, <= 1024; 1 <= top_k <= 64; hidden a multiple of 8
  * (of 128 for MOE_FP8_E4M3), <= 65536; 0 <= max_tokens and
- * num_ranks*max_tokens*top_k < 2^31. */
+ * num_ranks*max_tokens*top_k < 2^31 (with MOE_LAYOUT_FIXED_SLOT also
+ * num_ranks*num_experts*max_tokens < 2^31). */
 typedef struct moe_group_desc {
     int32_t num_ranks;      /* N */
     int32_t num_experts;    /* E */
@@ -118,15 +141,17 @@ typedef struct moe_group_desc {
     int32_t dispatch_dtype; /* moe_dtype */
     int32_t transport;      /* moe_transport */
     int32_t combine_mode;   /* moe_combine_mode */
+    int32_t layout;         /* moe_layout */
 } moe_group_desc;
 
 typedef struct moe_group_s* moe_group_t;
 
 /* Create a group: validates `desc`, allocates every internal buffer on the
  * current HIP device (two pooled row buffers of N*T_max*K rows of
- * max(payload, 2H) bytes, used by dispatch and again by combine, as the pages
- * reuse them between the two -- [EFA] "Dispatch and combine" -- plus counts,
- * offsets and metadata).  On success *out owns them.  Errors: MOE_ERR_INVALID,
+ * max(payload, 2H) bytes -- the receive one N*E*T_max rows with
+ * MOE_LAYOUT_FIXED_SLOT -- used by dispatch and again by combine, as the
+ * pages reuse them between the two -- [EFA] "Dispatch and combine" -- plus
+ * counts, offsets and metadata).  On success *out owns them.  Errors: MOE_ERR_INVALID,
  * MOE_ERR_OOM, MOE_ERR_HIP; *out is untouched on error. */
 int moe_group_create(const moe_group_desc* desc, moe_group_t* out);
 
@@ -200,6 +225,11 @@ int moe_combine_recv(moe_group_t g, const float* topk_weights, void* out,
  * send rows of sender s are rows [s*T*K, (s+1)*T*K); receive rows of rank d
  * are rows [recv_base[d], recv_base[d+1]).  With the direct transport there
  * is no send buffer: send_x, send_scale, send_meta and comb_send are NULL.
+ * With MOE_LAYOUT_FIXED_SLOT the receive planes have recv_rows rows, the
+ * slots first (slots no row names hold stale data), recv_off and recv_base still
+ * give the packed order the kernels walk, and with the staged transport the
+ * two pools swap roles in combine: comb_send (slot layout) is in the
+ * receive pool, comb_recv (send layout) in the send pool.
  * With MOE_COMBINE_PARTIAL the first P = part_base[N] rows of comb_send hold
  * the partial rows in owner layout (rank d, then sender s, then token t; rank
  * d's rows start at part_owner_base[d]) and those of comb_recv in token layout
@@ -237,6 +267,8 @@ typedef struct moe_group_view {
     int32_t* part_send_off;      /* [N][N+1]   first partial row of rank d among sender s's */
     int32_t* part_base;          /* [N+1]      first token-layout partial row of sender s */
     int32_t* part_owner_base;    /* [N+1]      first owner-layout partial row of rank d */
+    int64_t recv_rows;           /* rows of the receive planes: N*T_max*K, or with
+                                    MOE_LAYOUT_FIXED_SLOT max(N*E*T_max, N*T_max*K) */
 } moe_group_view;
 
 int moe_group_view_get(moe_group_t g, moe_group_view* out);

@@ -44,6 +44,26 @@ def d2h(ptr: int, shape, dtype) -> np.ndarray:
     return out
 
 
+def d2h_rows(ptr: int, rows: np.ndarray, row_shape, dtype) -> np.ndarray:
+    """Copy the listed rows of a device row buffer (raw address) to the host,
+    one copy per run of consecutive rows."""
+    global _HIP
+    if _HIP is None:
+        _HIP = hip()
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    out = np.empty((rows.size,) + tuple(row_shape), dtype=dtype)
+    rb = out[0].nbytes if rows.size else 0
+    i = 0
+    while i < rows.size:
+        j = i + 1
+        while j < rows.size and rows[j] == rows[j - 1] + 1:
+            j += 1
+        rc = _HIP.hipMemcpy(out[i:j].ctypes.data, ptr + int(rows[i]) * rb, rb * (j - i), 2)
+        assert rc == 0, f"hipMemcpy failed: {rc}"
+        i = j
+    return out
+
+
 def say(msg: str):
     print(msg, flush=True)
     sys.stdout.flush()
@@ -57,18 +77,21 @@ def to_dev(torch, a: np.ndarray):
 
 
 def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, want_rows=True,
-              transport=0, combine_mode=0):
+              transport=0, combine_mode=0, layout=0, recv_gather=None):
     """One full dispatch + stand-in expert + combine cycle on the GPU.
     Returns a dict of host copies of every buffer (rows only if want_rows;
     the send-side buffers only with the staged transport).  With the partial
     combine the weights go to dispatch_send, combine_recv gets none, and the
-    partial-row plan and rows are returned too."""
+    partial-row plan and rows are returned too.  With the fixed-slot layout the
+    receive-layout rows (receive planes, combine send rows) are read only at
+    the slot rows listed in recv_gather, in that order."""
     N, T, K, E, H = cfg.N, inp["idx"].shape[1], cfg.K, cfg.E, cfg.H
     fp8 = cfg.dtype == "fp8"
     T_max = T if T_max is None else T_max
     own = group is None
     g = group if group is not None else mep.moe_group_create(
-        N, E, K, H, T_max, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16, transport, combine_mode)
+        N, E, K, H, T_max, mep.MOE_FP8_E4M3 if fp8 else mep.MOE_BF16, transport, combine_mode,
+        layout)
     try:
         R = N * T * K
         x = to_dev(torch, inp["x"])
@@ -95,22 +118,29 @@ def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, w
         res["eoff"] = d2h(v.expert_off, (E + 1,), np.int32)
         res["expert_offsets"] = expert_offsets.cpu().numpy()
         staged = bool(v.send_x)
+        fixed = v.desc.layout == mep.MOE_LAYOUT_FIXED_SLOT
+
+        def recv_plane(ptr, row_shape, dtype):
+            if fixed:
+                return None if recv_gather is None else d2h_rows(ptr, recv_gather, row_shape, dtype)
+            return d2h(ptr, (R,) + tuple(row_shape), dtype)
+
         if staged:
             res["send_meta"] = d2h(v.send_meta, (R,), np.int32)
-        res["recv_meta"] = d2h(v.recv_meta, (R,), np.int32)
+        res["recv_meta"] = recv_plane(v.recv_meta, (), np.int32)
         res["expert_src_rank"] = d2h(v.expert_src_rank, (R,), np.int32)
         res["expert_src_slot"] = d2h(v.expert_src_slot, (R,), np.int32)
         pdt = np.uint8 if fp8 else np.uint16
         if want_rows:
             if staged:
                 res["send_x"] = d2h(v.send_x, (R, H), pdt)
-            res["recv_x"] = d2h(v.recv_x, (R, H), pdt)
+            res["recv_x"] = recv_plane(v.recv_x, (H,), pdt)
             res["expert_x"] = expert_x[:R * payload].cpu().numpy().view(pdt).reshape(R, H)
             if fp8:
                 nb = H // 128
                 if staged:
                     res["send_scale"] = d2h(v.send_scale, (R, nb), np.float32)
-                res["recv_scale"] = d2h(v.recv_scale, (R, nb), np.float32)
+                res["recv_scale"] = recv_plane(v.recv_scale, (nb,), np.float32)
                 res["expert_scale"] = expert_scale[:R * nb].cpu().numpy().reshape(R, nb)
         if identity:
             y = expert_x[:R * payload].view(torch.bfloat16).reshape(R, H) if R else \
@@ -139,7 +169,7 @@ def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, w
                 res["precv"] = d2h(v.comb_recv, (P, H), np.uint16)
         elif want_rows:
             if staged:
-                res["comb_send"] = d2h(v.comb_send, (R, H), np.uint16)
+                res["comb_send"] = recv_plane(v.comb_send, (H,), np.uint16)
             res["comb_recv"] = d2h(v.comb_recv, (R, H), np.uint16)
         res["y_dev"] = y
         res["out"] = out[:, :T].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
