@@ -423,6 +423,8 @@ def main() -> int:
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "CAL_FETCH_DB",
                                                         "CAL_WRITE_DB"),
                     help="write profiles/traffic_<config>.json from rocprofv3 --pmc databases")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once as a HIP graph and replayed")
     ap.add_argument("--overlap", action="store_true",
                     help="measure the send/recv split hiding a concurrent GEMM (prints one JSON line)")
     ap.add_argument("--trace-summary", metavar="DB",
@@ -529,6 +531,29 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"us_per_step_without_events": round((time.perf_counter() - t2) / args.steps * 1e6, 1)}),
               file=sys.stderr, flush=True)
+    graph_rec = None
+    if args.graph:
+        # the four calls of one step captured as a HIP graph, then replayed:
+        # the same kernels without the per-launch host work
+        cap = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                mep.moe_dispatch_send(g, T, x, idx, w_send, stream=cap)
+                mep.moe_dispatch_recv(g, expert_x, expert_scale, offs, stream=cap)
+                mep.moe_combine_send(g, y, stream=cap)
+                mep.moe_combine_recv(g, w, out, stream=cap)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_rec = {"us_per_step": round((time.perf_counter() - t2) / args.steps * 1e6, 1),
+                     "replays": args.steps}
+        del graph
     assert mep.moe_group_status(g, stream) == mep.MOE_OK
     mep.moe_group_destroy(g)
 
@@ -578,6 +603,8 @@ def main() -> int:
         "kernels": kern,
         "source_hash": src_hash,
     }
+    if graph_rec is not None:
+        rec["graph"] = graph_rec
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.combine)
