@@ -651,12 +651,30 @@ void orc_partial_counts(int N, int T, int K, int E, const int32_t* idx, int32_t*
 }
 
 /* Row of partial (s,t,d) in the owner-side and token-owner-side layouts, for
- * every (s,t,d) visited (-1 elsewhere); arrays [N][T][N]. */
+ * every (s,t,d) visited (-1 elsewhere); arrays [N][T][N].  The owner-side
+ * rows are ordered by (d, s, t): the rows before (d, s) are a running count of
+ * pc taken in (d, s) order.  The token-side rows are ordered by (s, d, t):
+ * a running count of pc in (s, d) order.  Inside a (d, s) pair, tokens in
+ * order (the running rank of the pair). */
 void orc_partial_rows(int N, int T, int K, int E, const int32_t* idx, const int32_t* pc,
                       int32_t* owner_row, int32_t* token_row)
 {
     int L = E / N;
-    int32_t* rank = (int32_t*)calloc((size_t)N * N, sizeof(int32_t));   /* [s][d] running prank */
+    int32_t* obase = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * N);  /* [d][s] */
+    int32_t* tbase = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * N);  /* [s][d] */
+    int32_t* rank = (int32_t*)calloc((size_t)N * N, sizeof(int32_t));    /* [s][d] running prank */
+    int32_t run = 0;
+    for (int d = 0; d < N; ++d)
+        for (int s = 0; s < N; ++s) {
+            obase[(size_t)d * N + s] = run;
+            run += pc[(size_t)s * N + d];
+        }
+    run = 0;
+    for (int s = 0; s < N; ++s)
+        for (int d = 0; d < N; ++d) {
+            tbase[(size_t)s * N + d] = run;
+            run += pc[(size_t)s * N + d];
+        }
     for (int s = 0; s < N; ++s)
         for (int t = 0; t < T; ++t)
             for (int d = 0; d < N; ++d) {
@@ -670,21 +688,12 @@ void orc_partial_rows(int N, int T, int K, int E, const int32_t* idx, const int3
                     token_row[o] = -1;
                     continue;
                 }
-                int32_t ob = 0, tb = 0;
-                for (int d2 = 0; d2 < d; ++d2)
-                    for (int s2 = 0; s2 < N; ++s2)
-                        ob += pc[(size_t)s2 * N + d2];
-                for (int s2 = 0; s2 < s; ++s2)
-                    ob += pc[(size_t)s2 * N + d];
-                for (int s2 = 0; s2 < s; ++s2)
-                    for (int d2 = 0; d2 < N; ++d2)
-                        tb += pc[(size_t)s2 * N + d2];
-                for (int d2 = 0; d2 < d; ++d2)
-                    tb += pc[(size_t)s * N + d2];
                 int32_t pr = rank[(size_t)s * N + d]++;
-                owner_row[o] = ob + pr;
-                token_row[o] = tb + pr;
+                owner_row[o] = obase[(size_t)d * N + s] + pr;
+                token_row[o] = tbase[(size_t)s * N + d] + pr;
             }
+    free(obase);
+    free(tbase);
     free(rank);
 }
 
