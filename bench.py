@@ -393,8 +393,17 @@ def cpu_baseline(cfg, inp, min_seconds: float, combine: str = "receiver") -> dic
         if el >= min_seconds:
             break
     assert isinstance(y, np.ndarray)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(el / steps * 1e6, 1), "unit": "us per dispatch+combine", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": f"{steps} full dispatch+combine step(s) of the {cfg.name} workload "
                       f"({cfg.N}x{cfg.T} tokens, {combine} combine), single thread, {el:.1f} s"}
 
