@@ -141,11 +141,13 @@ struct RouteArgs {
 
 // One column of an [N][stride] offset table, walked down the senders with
 // BATCH loads in flight: .x = sum_s lo[s], and run_out[s] (when given) =
-// sum_{s'<s} (hi - lo)[s'], run_out[N] = .y = the column's total span.
+// sum_{s'<s} (hi - lo)[s'], run_out[N] = .y = the column's total span;
+// hi_run_out[s] (when given) = sum_{s'<s} hi[s'], hi_run_out[N] = sum of hi.
 __device__ int2 walk_column(const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
-                            size_t stride, int N, int32_t* __restrict__ run_out)
+                            size_t stride, int N, int32_t* __restrict__ run_out,
+                            int32_t* __restrict__ hi_run_out)
 {
-    int base = 0, run = 0;
+    int base = 0, run = 0, hrun = 0;
     for (int s0 = 0; s0 < N; s0 += BATCH) {
         int a[BATCH], b[BATCH];
 #pragma unroll
@@ -159,12 +161,17 @@ __device__ int2 walk_column(const int32_t* __restrict__ lo, const int32_t* __res
             if (s0 + j < N) {
                 if (run_out)
                     run_out[s0 + j] = run;
+                if (hi_run_out)
+                    hi_run_out[s0 + j] = hrun;
                 run += b[j] - a[j];
+                hrun += b[j];
                 base += a[j];
             }
     }
     if (run_out)
         run_out[N] = run;
+    if (hi_run_out)
+        hi_run_out[N] = hrun;
     return make_int2(base, run);
 }
 
@@ -180,22 +187,22 @@ __device__ int2 walk_column(const int32_t* __restrict__ lo, const int32_t* __res
 //   qbase[d]     = sum_s psoff[s][d]                (partial rows of ranks < d)
 //   qoff[d][s]   = sum_{s'<s} (psoff[s'][d+1] - psoff[s'][d])
 //   pbase[s]     = sum_{s'<s} psoff[s'][N]          (partial rows of senders < s)
-// so one thread takes one column (E expert columns, the total column E, N
-// receiver columns, then N + 1 partial columns) and walks the senders; no scan
-// across threads.
+// so one thread takes one column (E expert columns, N receiver columns, then
+// N partial columns) and walks the senders; no scan across threads.  The
+// totals need no column of their own: the last expert column's running sum
+// ends at eoff[E] = rbase[N], and the last partial column's upper bounds
+// psoff[s][N] are the per-sender totals whose running sum is pbase.
 __device__ void group_offsets(const RouteArgs& ra, const Plan& p)
 {
     const int N = ra.N, E = ra.E, L = ra.L;
     const int32_t* __restrict__ soff = p.soff;
     const int32_t* __restrict__ cnt = p.cnt;
-    const int cols = E + 1 + N + (ra.partial ? N + 1 : 0);
+    const int cols = E + N + (ra.partial ? N : 0);
     for (int col = threadIdx.x; col < cols; col += RP_NT) {
-        if (col <= E) {
-            // expert column e (col == E: the total, which ends both tables)
+        if (col < E) {
+            // expert column e; its counts are loaded with its offsets and,
+            // for N <= BATCH, kept in registers for the second walk
             const int e = col;
-            // the counts of the column are loaded with its offsets and, for
-            // N <= BATCH, kept in registers for the second walk
-            const int ce = min(e, E - 1);
             int base = 0;
             int c[BATCH];
             for (int s0 = 0; s0 < N; s0 += BATCH) {
@@ -204,17 +211,12 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p)
                 for (int b = 0; b < BATCH; ++b) {
                     const int sb = min(s0 + b, N - 1);
                     o[b] = soff[(size_t)sb * (E + 1) + e];
-                    c[b] = cnt[(size_t)sb * E + ce];
+                    c[b] = cnt[(size_t)sb * E + e];
                 }
 #pragma unroll
                 for (int b = 0; b < BATCH; ++b)
                     if (s0 + b < N)
                         base += o[b];
-            }
-            if (e == E) {
-                p.eoff[E] = base;
-                p.rbase[N] = base;
-                continue;
             }
             p.eoff[e] = base;
             int run = base;
@@ -231,22 +233,25 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p)
                         run += c[b];
                     }
             }
-        } else if (col <= E + N) {
-            const int d = col - E - 1;
+            if (e == E - 1) {
+                p.eoff[E] = run;
+                p.rbase[N] = run;
+            }
+        } else if (col < E + N) {
+            const int d = col - E;
             const int2 br = walk_column(soff + d * L, soff + (d + 1) * L, E + 1, N,
-                                        p.roff + (size_t)d * (N + 1));
+                                        p.roff + (size_t)d * (N + 1), nullptr);
             p.rbase[d] = br.x;
             if ((int64_t)br.y > ra.cap)
                 atomicOr(p.err, ERR_BIT_CAPACITY);
-        } else if (col <= E + 2 * N) {
-            const int d = col - E - 1 - N;
-            const int2 br = walk_column(p.psoff + d, p.psoff + d + 1, N + 1, N,
-                                        p.qoff + (size_t)d * (N + 1));
-            p.qbase[d] = br.x;
         } else {
-            // psoff[s][0] is 0, so this walk is the running sum of the totals
-            const int2 br = walk_column(p.psoff, p.psoff + N, N + 1, N, p.pbase);
-            p.qbase[N] = br.y;
+            const int d = col - E - N;
+            const bool last = d == N - 1;
+            const int2 br = walk_column(p.psoff + d, p.psoff + d + 1, N + 1, N,
+                                        p.qoff + (size_t)d * (N + 1), last ? p.pbase : nullptr);
+            p.qbase[d] = br.x;
+            if (last)
+                p.qbase[N] = br.x + br.y;
         }
     }
 }
@@ -1397,9 +1402,10 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     ra.partial = sh.partial;
     ra.slot_cap = sh.fixed ? sh.slots : -1;
     ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
-    // two buffers of lane masks take 16 bytes per (wave, expert): 8 waves
-    // up to 256 experts, 4 up to 512, 2 above, within 32 KiB of LDS
-    ra.chunk_waves = sh.E <= 256 ? RP_WAVES : sh.E <= 512 ? RP_WAVES / 2 : RP_WAVES / 4;
+    // two buffers of lane masks take 16 bytes per (wave, expert) and the
+    // cursors 8 bytes per expert: (16*CW + 8)*E bytes, kept within 64 KiB:
+    // 8 waves up to 481 experts, 4 up to 910, 2 above
+    ra.chunk_waves = sh.E <= 481 ? RP_WAVES : sh.E <= 910 ? RP_WAVES / 2 : RP_WAVES / 4;
     const size_t lds = 2 * (size_t)ra.chunk_waves * sh.E * sizeof(uint64_t) +
                        (size_t)2 * sh.E * sizeof(int32_t);
     go(route_plan_kernel, dim3(sh.N), dim3(RP_NT), lds, L, ra, p);
