@@ -295,19 +295,31 @@ __device__ __forceinline__ void publish_counts(int32_t* cur, int nkeys, int32_t*
     __syncthreads();
 }
 
+// Two keys can be packed into one int: the low 16 bits the first, the high 16
+// bits the second, NO_KEY for none (keys stay below 2048 here).
+constexpr int NO_KEY = 0xFFFF;
+
+__device__ inline int pack_keys(int k1, int k2)
+{
+    return (k1 < 0 ? NO_KEY : k1) | ((k2 < 0 ? NO_KEY : k2) << 16);
+}
+
 // Stable positions, one chunk of CW*64 items at a time (thread tid takes item
 // c*CW*64 + tid of chunk c), two barriers per chunk (masks and cursors
 // double-buffered by chunk parity).  Each lane sets its bit in
 // mask[wave][key] with an LDS 64-bit OR; its rank among equal keys of the
 // chunk is then the set bits of lower waves' masks plus the bits of its own
 // wave's mask below its lane; the per-key cursor advances by the chunk's
-// total into the other buffer.  Keys of the first HELD_CHUNKS chunks come from
-// registers, later ones from key_at(i, mine), which every thread calls.
-// out[i] = the item's position, -1 for an item without a valid key.
-template <typename KeyAt>
+// total into the other buffer.  With TWO, every item carries two keys (packed,
+// see pack_keys) from disjoint key ranges, ranked in the same pass.  Keys of
+// the first HELD_CHUNKS chunks come from registers, later ones from
+// key_at(i, mine), which every thread calls.  out1[i] (out2[i]) = the item's
+// position for its first (second) key, -1 for an item without one.
+template <bool TWO, typename KeyAt>
 __device__ __forceinline__ void stable_ranks(int items, int nkeys, int CW, uint64_t* mask,
                                              int32_t* cur, const int (&held)[HELD_CHUNKS],
-                                             KeyAt key_at, int32_t* __restrict__ out)
+                                             KeyAt key_at, int32_t* __restrict__ out1,
+                                             int32_t* __restrict__ out2)
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
     const int chunk = CW * WAVE;
@@ -320,27 +332,43 @@ __device__ __forceinline__ void stable_ranks(int items, int nkeys, int CW, uint6
         int32_t* cB = cur + (A ^ 1) * nkeys;
         const int i = c0 + tid;
         const bool mine = tid < chunk && i < items;
-        int key = -1;
+        int key = TWO ? pack_keys(-1, -1) : -1;
 #pragma unroll
         for (int h = 0; h < HELD_CHUNKS; ++h)
             if (c == h)
                 key = held[h];
         if (c >= HELD_CHUNKS)
             key = key_at(i, mine);
-        const bool valid = mine && (unsigned)key < (unsigned)nkeys;
-        if (valid)
-            atomicOr(reinterpret_cast<unsigned long long*>(&mA[(size_t)wave * nkeys + key]),
+        const int k1 = TWO ? key & 0xFFFF : key;
+        const int k2 = TWO ? (key >> 16) & 0xFFFF : NO_KEY;
+        const bool v1 = mine && (unsigned)k1 < (unsigned)nkeys;
+        const bool v2 = TWO && mine && (unsigned)k2 < (unsigned)nkeys;
+        if (v1)
+            atomicOr(reinterpret_cast<unsigned long long*>(&mA[(size_t)wave * nkeys + k1]),
+                     1ull << lane);
+        if (v2)
+            atomicOr(reinterpret_cast<unsigned long long*>(&mA[(size_t)wave * nkeys + k2]),
                      1ull << lane);
         for (int j = tid; j < CW * nkeys; j += RP_NT)
             mB[j] = 0ull;
         __syncthreads();
-        if (valid) {
-            int before = cA[key] + __popcll(mA[(size_t)wave * nkeys + key] & lanes_below);
+        if (v1) {
+            int before = cA[k1] + __popcll(mA[(size_t)wave * nkeys + k1] & lanes_below);
             for (int w = 0; w < wave; ++w)
-                before += __popcll(mA[(size_t)w * nkeys + key]);
-            out[i] = before;
+                before += __popcll(mA[(size_t)w * nkeys + k1]);
+            out1[i] = before;
         } else if (mine) {
-            out[i] = -1;
+            out1[i] = -1;
+        }
+        if (TWO) {
+            if (v2) {
+                int before = cA[k2] + __popcll(mA[(size_t)wave * nkeys + k2] & lanes_below);
+                for (int w = 0; w < wave; ++w)
+                    before += __popcll(mA[(size_t)w * nkeys + k2]);
+                out2[i] = before;
+            } else if (mine) {
+                out2[i] = -1;
+            }
         }
         for (int kk = tid; kk < nkeys; kk += RP_NT) {
             int add = 0;
@@ -382,27 +410,31 @@ __device__ __forceinline__ int rank_of_item(const RouteArgs& ra, const int32_t* 
 __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
 {
     extern __shared__ uint64_t lds64[];
-    const int E = ra.E;
+    const int E = ra.E, N = ra.N;
+    // keys: experts [0, E) and, for the partial combine, destination ranks
+    // [E, E + N) for the first item of each (token, rank)
+    const int NK = ra.partial ? E + N : E;
     const int CW = ra.chunk_waves;              // waves that take items in one chunk
-    uint64_t* mask = lds64;                     // [2][CW][E]: lanes of a wave holding expert e
-    int32_t* cur = reinterpret_cast<int32_t*>(mask + 2 * (size_t)CW * E);  // [2][E] cursors
+    uint64_t* mask = lds64;                     // [2][CW][NK]: lanes of a wave holding a key
+    int32_t* cur = reinterpret_cast<int32_t*>(mask + 2 * (size_t)CW * NK);  // [2][NK] cursors
     __shared__ int32_t wave_sums[RP_WAVES + 1];
     __shared__ int32_t ticket;
 
     const int s = blockIdx.x;
     const int items = ra.T * ra.K;
     const int32_t* my_idx = ra.idx + (size_t)s * items;
+    int32_t* my_pdst = ra.partial ? p.pdst + (size_t)s * items : nullptr;
     const int tid = threadIdx.x;
     const int chunk = CW * WAVE;
     const int held_items = min(items, HELD_CHUNKS * chunk);
 
-    for (int e = tid; e < E; e += RP_NT)
-        cur[e] = 0;
-    for (int j = tid; j < CW * E; j += RP_NT)
+    for (int k = tid; k < NK; k += RP_NT)
+        cur[k] = 0;
+    for (int j = tid; j < CW * NK; j += RP_NT)
         mask[j] = 0ull;
     // expert ids of the first HELD_CHUNKS chunks stay in registers for both
-    // passes (thread tid takes item c*chunk + tid of chunk c); all loads are
-    // issued before the first use
+    // the counting and the ranking (thread tid takes item c*chunk + tid of
+    // chunk c); all loads are issued before the first use
     int held_e[HELD_CHUNKS];
     if (items > 0) {
         // clamped addresses, so the loads are unconditional and issue together
@@ -420,81 +452,87 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     }
     __syncthreads();
     int bad = 0;
+    if (!ra.partial) {
 #pragma unroll
-    for (int c = 0; c < HELD_CHUNKS; ++c) {
-        const int e = held_e[c];
-        if ((unsigned)e < (unsigned)E)
-            atomicAdd(&cur[e], 1);
-        else if (tid < chunk && c * chunk + tid < items)
-            bad = 1;
-    }
-    for (int i = held_items + tid; i < items; i += RP_NT) {
-        const int e = my_idx[i];
-        if ((unsigned)e < (unsigned)E)
-            atomicAdd(&cur[e], 1);
-        else
-            bad = 1;
-    }
-    if (bad)
-        atomicOr(p.err, ERR_BIT_ROUTING);
-    __syncthreads();
-
-    // counts out, exclusive scan over experts -> send offsets and cursors,
-    // then the stable position of every item inside its expert's rows
-    publish_counts(cur, E, p.cnt + (size_t)s * E, p.soff + (size_t)s * (E + 1), wave_sums,
-                   ra.slot_cap, p.err);
-    stable_ranks(items, E, CW, mask, cur, held_e,
-                 [&](int i, bool mine) { return mine ? my_idx[i] : -1; },
-                 p.pos + (size_t)s * items);
-
-    if (ra.partial) {
-        // Second pass over the same items for the expert-side partial rows:
-        // the key of an item is its destination rank when it is the first of
-        // its token with that rank (one partial row per (token, rank)), none
-        // otherwise.  Counting, scanning and ranking these keys gives each
-        // (token, rank) its row among the sender's partial rows, ordered by
-        // rank, then token.
-        const int N = ra.N;
-        int32_t* my_pdst = p.pdst + (size_t)s * items;
-        for (int d = tid; d < N; d += RP_NT)
-            cur[d] = 0;
-        for (int j = tid; j < CW * N; j += RP_NT)
-            mask[j] = 0ull;
-        __syncthreads();
+        for (int c = 0; c < HELD_CHUNKS; ++c) {
+            const int e = held_e[c];
+            if ((unsigned)e < (unsigned)E)
+                atomicAdd(&cur[e], 1);
+            else if (tid < chunk && c * chunk + tid < items)
+                bad = 1;
+        }
+        for (int i = held_items + tid; i < items; i += RP_NT) {
+            const int e = my_idx[i];
+            if ((unsigned)e < (unsigned)E)
+                atomicAdd(&cur[e], 1);
+            else
+                bad = 1;
+        }
+    } else {
+        // Each item also gets its rank key when it is the first of its token
+        // on that rank (one partial row per (token, rank)); the held ids are
+        // replaced by the packed key pair.
 #pragma unroll
         for (int c = 0; c < HELD_CHUNKS; ++c) {
             if (c * chunk >= items)
                 break;
             const int i = c * chunk + tid;
             const bool mine = tid < chunk && i < items;
+            const int e = held_e[c];
+            const bool ok = (unsigned)e < (unsigned)E;
+            if (ok)
+                atomicAdd(&cur[e], 1);
+            else if (mine)
+                bad = 1;
             bool first;
-            const int d = rank_of_item(ra, my_idx, held_e[c], i, mine, &first);
-            if (mine)
-                my_pdst[i] = d;
-            held_e[c] = first ? d : -1;
-            if (first)
-                atomicAdd(&cur[d], 1);
-        }
-        for (int c0 = HELD_CHUNKS * chunk; c0 < items; c0 += chunk) {
-            const int i = c0 + tid;
-            const bool mine = tid < chunk && i < items;
-            bool first;
-            const int d = rank_of_item(ra, my_idx, mine ? my_idx[i] : -1, i, mine, &first);
+            const int d = rank_of_item(ra, my_idx, e, i, mine, &first);
             if (mine)
                 my_pdst[i] = d;
             if (first)
-                atomicAdd(&cur[d], 1);
+                atomicAdd(&cur[E + d], 1);
+            held_e[c] = pack_keys(ok ? e : -1, first ? E + d : -1);
         }
-        __syncthreads();
-        publish_counts(cur, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums, -1, p.err);
-        stable_ranks(items, N, CW, mask, cur, held_e,
-                     [&](int i, bool mine) {
-                         bool first;
-                         const int d = rank_of_item(ra, my_idx, mine ? my_idx[i] : -1, i, mine,
-                                                    &first);
-                         return first ? d : -1;
-                     },
-                     p.ppos + (size_t)s * items);
+        for (int i0 = held_items; i0 < items; i0 += RP_NT) {
+            const int i = i0 + tid;
+            const bool mine = i < items;
+            const int e = mine ? my_idx[i] : -1;
+            if ((unsigned)e < (unsigned)E)
+                atomicAdd(&cur[e], 1);
+            else if (mine)
+                bad = 1;
+            bool first;
+            const int d = rank_of_item(ra, my_idx, e, i, mine, &first);
+            if (mine)
+                my_pdst[i] = d;
+            if (first)
+                atomicAdd(&cur[E + d], 1);
+        }
+    }
+    if (bad)
+        atomicOr(p.err, ERR_BIT_ROUTING);
+    __syncthreads();
+
+    // counts out, exclusive scans -> send offsets (and the partial rows'
+    // offsets per rank) and the cursors, then the stable position of every
+    // item inside its expert's rows (and of every first item of a rank among
+    // the sender's partial rows, ordered by rank, then token)
+    publish_counts(cur, E, p.cnt + (size_t)s * E, p.soff + (size_t)s * (E + 1), wave_sums,
+                   ra.slot_cap, p.err);
+    if (!ra.partial) {
+        stable_ranks<false>(items, NK, CW, mask, cur, held_e,
+                            [&](int i, bool mine) { return mine ? my_idx[i] : -1; },
+                            p.pos + (size_t)s * items, nullptr);
+    } else {
+        publish_counts(cur + E, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums, -1, p.err);
+        stable_ranks<true>(items, NK, CW, mask, cur, held_e,
+                           [&](int i, bool mine) {
+                               const int e = mine ? my_idx[i] : -1;
+                               bool first;
+                               const int d = rank_of_item(ra, my_idx, e, i, mine, &first);
+                               return pack_keys((unsigned)e < (unsigned)E ? e : -1,
+                                                first ? E + d : -1);
+                           },
+                           p.pos + (size_t)s * items, p.ppos + (size_t)s * items);
     }
 
     // Publish this rank's counts and draw a ticket.  Every wave waits for its
@@ -1402,12 +1440,15 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     ra.partial = sh.partial;
     ra.slot_cap = sh.fixed ? sh.slots : -1;
     ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
-    // two buffers of lane masks take 16 bytes per (wave, expert) and the
-    // cursors 8 bytes per expert: (16*CW + 8)*E bytes, kept within 64 KiB:
-    // 8 waves up to 481 experts, 4 up to 910, 2 above
-    ra.chunk_waves = sh.E <= 481 ? RP_WAVES : sh.E <= 910 ? RP_WAVES / 2 : RP_WAVES / 4;
-    const size_t lds = 2 * (size_t)ra.chunk_waves * sh.E * sizeof(uint64_t) +
-                       (size_t)2 * sh.E * sizeof(int32_t);
+    // keys: E experts, plus N ranks for the partial combine.  Two buffers of
+    // lane masks take 16 bytes per (wave, key) and the cursors 8 bytes per
+    // key: (16*CW + 8)*NK bytes, kept within 64 KiB: 8 waves up to 481 keys,
+    // 4 up to 910, 2 up to 1638, 1 above
+    const int nk = sh.E + (sh.partial ? sh.N : 0);
+    ra.chunk_waves = nk <= 481 ? RP_WAVES : nk <= 910 ? RP_WAVES / 2 : nk <= 1638 ? RP_WAVES / 4
+                                                                                   : RP_WAVES / 8;
+    const size_t lds = 2 * (size_t)ra.chunk_waves * nk * sizeof(uint64_t) +
+                       (size_t)2 * nk * sizeof(int32_t);
     go(route_plan_kernel, dim3(sh.N), dim3(RP_NT), lds, L, ra, p);
     return hipGetLastError();
 }
