@@ -371,6 +371,58 @@ def overlap_demo(cfg, args) -> dict:
     return res
 
 
+def hbm_ceiling(torch, mep, nbytes: int = 1 << 30, iters: int = 10) -> dict:
+    """What HBM delivers to the library's streaming probes (16-byte
+    nontemporal vectors, the movers' access style) on buffers of nbytes: a
+    copy, a pure read and a pure write.  The rate depends on the footprint
+    against the 256 MB MALL, so it is measured at the dominant kernel's own
+    footprint and at 1 GiB."""
+    nbytes -= nbytes % 16
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, kind, moved in (("copy", mep.MOE_PROBE_COPY, 2), ("read", mep.MOE_PROBE_READ, 1),
+                              ("write", mep.MOE_PROBE_WRITE, 1)):
+        for _ in range(2):
+            mep.moe_hbm_probe(kind, dst, src, nbytes)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            mep.moe_hbm_probe(kind, dst, src, nbytes)
+        b.record()
+        b.synchronize()
+        ms = a.elapsed_time(b) / iters
+        res[f"{name}_gbps"] = round(nbytes * moved / (ms * 1e-3) / 1e9, 1)
+    res["bytes"] = nbytes
+    del src, dst
+    return res
+
+
+def step_distribution(torch, step, stream, n: int, flush_bytes: int = 0) -> dict:
+    """Per-step times from an event pair around each step (p10 / p50 / p90, µs);
+    with flush_bytes, a scratch buffer that size is written before every step
+    so the step starts with the MALL holding none of its data."""
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if scratch is not None:
+            with torch.cuda.stream(stream):
+                scratch.fill_(0)
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+    def q(p):
+        return round(ts[min(len(ts) - 1, int(p * len(ts)))], 1)
+    return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "n": n}
+
+
 def cpu_baseline(cfg, inp, min_seconds: float, combine: str = "receiver") -> dict:
     """The oracle, unchanged and single-threaded, on the same workload: whole
     dispatch + combine steps until min_seconds of work (at least one)."""
@@ -540,6 +592,10 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"us_per_step_without_events": round((time.perf_counter() - t2) / args.steps * 1e6, 1)}),
               file=sys.stderr, flush=True)
+    # per-step distribution, warm and with the MALL flushed before each step
+    dist = {"warm": step_distribution(torch, step, stream, args.steps),
+            "cold": step_distribution(torch, step, stream, args.steps, flush_bytes=512 << 20),
+            "flush_bytes": 512 << 20}
     graph_rec = None
     if args.graph:
         # the four calls of one step captured as a HIP graph, then replayed:
@@ -565,6 +621,12 @@ def main() -> int:
         del graph
     assert mep.moe_group_status(g, stream) == mep.MOE_OK
     mep.moe_group_destroy(g)
+    # the probe's source and destination each the size of one side of the
+    # dominant kernel's traffic
+    kb_dom = kernel_bytes(cfg, args.transport, args.combine,
+                          partial_rows(cfg, inp["idx"]) if partial else 0)[dom]
+    ceiling = {"at_kernel_footprint": hbm_ceiling(torch, mep, kb_dom // 2),
+               "at_1gib": hbm_ceiling(torch, mep, 1 << 30)}
 
     ms_per_step = (t1 - t0) / args.steps * 1e3
     P = partial_rows(cfg, inp["idx"]) if partial else 0
@@ -608,7 +670,11 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "bytes_per_launch": kb[dom], "avg_us": round(dom_us, 2),
-                     "launches_timed": dom_n, "traffic": traffic},
+                     "launches_timed": dom_n, "traffic": traffic,
+                     "frac_of_copy_ceiling": round(
+                         ach / ceiling["at_kernel_footprint"]["copy_gbps"], 4)},
+        "hbm_ceiling": ceiling,
+        "step_us": dist,
         "kernels": kern,
         "source_hash": src_hash,
     }

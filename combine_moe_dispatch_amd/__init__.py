@@ -5,7 +5,7 @@ same name in include/moe_ep.h (ctypes), passing device pointers and the HIP
 stream.  Tensors may be torch tensors (their data_ptr() is passed) or raw
 integer device addresses.  A non-zero status raises MoeError.
 
-The library is built in-tree by ``python -m combine_moe_dispatch_amd._build``;
+The library is built in-tree by ``python combine_moe_dispatch_amd/_build.py``;
 importing this package without it raises ImportError -- there is no fallback.
 """
 from __future__ import annotations
@@ -37,6 +37,10 @@ MOE_COMBINE_PARTIAL = 1
 
 MOE_LAYOUT_PACKED = 0
 MOE_LAYOUT_FIXED_SLOT = 1
+
+MOE_PROBE_COPY = 0
+MOE_PROBE_READ = 1
+MOE_PROBE_WRITE = 2
 
 KERNELS = ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
            "combine_reduce", "combine_push", "partial_send", "partial_transfer",
@@ -80,7 +84,7 @@ def _load():
     except ImportError:
         pass
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run python -m combine_moe_dispatch_amd._build")
+        raise ImportError(f"{LIB_PATH} is not built; run python combine_moe_dispatch_amd/_build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, I32, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64
     sig = {
@@ -96,6 +100,7 @@ def _load():
         "moe_group_timing_read": ([P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)], I),
         "moe_strerror": ([I], ctypes.c_char_p),
         "moe_kernel_name": ([I], ctypes.c_char_p),
+        "moe_hbm_probe": ([I, P, P, ctypes.c_size_t, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -205,3 +210,9 @@ def moe_group_timing_read(g: int) -> dict:
 
 def moe_kernel_name(kernel_id: int) -> str:
     return _lib.moe_kernel_name(kernel_id).decode()
+
+
+def moe_hbm_probe(kind: int, dst, src, nbytes: int, stream=None) -> None:
+    """Measurement aid: one streaming copy / read / write kernel of nbytes."""
+    _check(_lib.moe_hbm_probe(kind, _ptr(dst), _ptr(src), nbytes, _stream(stream)),
+           "moe_hbm_probe")

@@ -1,6 +1,9 @@
 """Build libmoe_ep.so (the C-ABI HIP library) in-tree with hipcc for gfx950.
 
-    python -m combine_moe_dispatch_amd._build
+    python combine_moe_dispatch_amd/_build.py
+
+(run as a file, not as a module of the package: importing the package loads
+the library this script builds)
 
 Flags: -O3; packed fp32 instructions disabled (-packed-fp32-ops); fp32 divide
 correctly rounded (the fp8 block scales depend on it); no fast-math.

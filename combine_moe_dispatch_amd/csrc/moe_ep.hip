@@ -543,6 +543,18 @@ int moe_group_status(moe_group_t g, hipStream_t stream)
     return MOE_OK;
 }
 
+int moe_hbm_probe(int kind, void* dst, const void* src, size_t bytes, hipStream_t stream)
+{
+    if (kind < MOE_PROBE_COPY || kind > MOE_PROBE_WRITE || bytes == 0 || bytes % 16 != 0)
+        return MOE_ERR_INVALID;
+    if (bytes / 16 >= ((size_t)1 << 40))
+        return MOE_ERR_INVALID;
+    const bool reads = kind != MOE_PROBE_WRITE;
+    if (!dst || !aligned16(dst) || (reads && (!src || !aligned16(src))))
+        return MOE_ERR_INVALID;
+    return from_hip(moe::launch_hbm_probe(kind, dst, src, (int64_t)(bytes / 16), stream));
+}
+
 int moe_group_timing_enable(moe_group_t g, int kernel_mask)
 {
     if (!g || (kernel_mask & ~MOE_KERNEL_ALL) != 0)

@@ -103,5 +103,7 @@ hipError_t launch_partial_send(const Shape& sh, const Plan& p, const Rows& r, co
 hipError_t launch_partial_transfer(const Shape& sh, const Plan& p, const Rows& r, const Launch& L);
 hipError_t launch_partial_reduce(const Shape& sh, const Plan& p, const Rows& r, void* out,
                                  const Launch& L);
+// Streaming probes (kind: 0 copy, 1 read, 2 write) over `vecs` 16-byte vectors.
+hipError_t launch_hbm_probe(int kind, void* dst, const void* src, int64_t vecs, hipStream_t stream);
 
 }  // namespace moe

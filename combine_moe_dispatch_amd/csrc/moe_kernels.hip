@@ -1382,6 +1382,65 @@ __global__ __launch_bounds__(COPY_THREADS) void partial_reduce_kernel(Shape sh, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming probes: what HBM delivers to 16-byte nontemporal streams (a
+// measurement aid beside the kernels above, not a step of the method).  Each
+// 256-thread block moves 4 vectors per lane, all loads issued before the
+// stores; the read probe folds its loads into one word that is stored only
+// for a value the data never holds, so the loads cannot be dropped.
+// ---------------------------------------------------------------------------
+constexpr int PROBE_U = 4;
+constexpr int PROBE_NT = 256;
+
+__global__ __launch_bounds__(PROBE_NT) void probe_copy_kernel(const v4u* __restrict__ src,
+                                                              v4u* __restrict__ dst, int64_t nv)
+{
+    const int64_t base = (int64_t)blockIdx.x * PROBE_U * PROBE_NT + threadIdx.x;
+    v4u v[PROBE_U];
+#pragma unroll
+    for (int u = 0; u < PROBE_U; ++u) {
+        const int64_t j = base + (int64_t)u * PROBE_NT;
+        v[u] = ld_nt(src + (j < nv ? j : nv - 1));
+    }
+    hold(v);
+#pragma unroll
+    for (int u = 0; u < PROBE_U; ++u) {
+        const int64_t j = base + (int64_t)u * PROBE_NT;
+        if (j < nv)
+            st_nt(v[u], dst + j);
+    }
+}
+
+__global__ __launch_bounds__(PROBE_NT) void probe_read_kernel(const v4u* __restrict__ src,
+                                                              uint32_t* __restrict__ word, int64_t nv)
+{
+    const int64_t base = (int64_t)blockIdx.x * PROBE_U * PROBE_NT + threadIdx.x;
+    v4u v[PROBE_U];
+#pragma unroll
+    for (int u = 0; u < PROBE_U; ++u) {
+        const int64_t j = base + (int64_t)u * PROBE_NT;
+        v[u] = ld_nt(src + (j < nv ? j : nv - 1));
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int u = 0; u < PROBE_U; ++u)
+        acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    if (acc == 0x9E3779B9u)
+        word[0] = acc;
+}
+
+__global__ __launch_bounds__(PROBE_NT) void probe_write_kernel(v4u* __restrict__ dst, int64_t nv)
+{
+    const int64_t base = (int64_t)blockIdx.x * PROBE_U * PROBE_NT + threadIdx.x;
+    const v4u v = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, (uint32_t)blockIdx.x};
+#pragma unroll
+    for (int u = 0; u < PROBE_U; ++u) {
+        const int64_t j = base + (int64_t)u * PROBE_NT;
+        if (j < nv)
+            st_nt(v, dst + j);
+    }
+}
+
 // Launch shape of a row kernel: waves per row (SPLIT) and 16-byte vectors
 // per lane per round (U), from the number of vectors in a row.
 struct RowShape {
@@ -1597,6 +1656,20 @@ hipError_t launch_partial_reduce(const Shape& sh, const Plan& p, const Rows& r, 
         return hipSuccess;
     MOE_DISPATCH_TOKEN(sh, partial_reduce_kernel, 4, tokens, L, sh, p, (const v4u*)r.comb_recv,
                        (v4u*)out);
+    return hipGetLastError();
+}
+
+hipError_t launch_hbm_probe(int kind, void* dst, const void* src, int64_t vecs, hipStream_t stream)
+{
+    const int64_t per_block = (int64_t)PROBE_U * PROBE_NT;
+    const dim3 grid((unsigned)((vecs + per_block - 1) / per_block)), block(PROBE_NT);
+    const Launch L{stream, nullptr, nullptr};
+    if (kind == 0)
+        go(probe_copy_kernel, grid, block, 0, L, (const v4u*)src, (v4u*)dst, vecs);
+    else if (kind == 1)
+        go(probe_read_kernel, grid, block, 0, L, (const v4u*)src, (uint32_t*)dst, vecs);
+    else
+        go(probe_write_kernel, grid, block, 0, L, (v4u*)dst, vecs);
     return hipGetLastError();
 }
 

@@ -305,6 +305,21 @@ typedef enum moe_kernel_mask { MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1 } mo
 int moe_group_timing_enable(moe_group_t g, int kernel_mask);
 int moe_group_timing_read(moe_group_t g, double* total_ms, int64_t* launches);
 
+/* Measurement aid, not part of the method: streaming kernels with the row
+ * movers' access style (16-byte nontemporal vectors, all loads of a lane in
+ * flight before its stores), to measure what HBM delivers for each traffic
+ * mix on this device.  kind: MOE_PROBE_COPY (read src, write dst),
+ * MOE_PROBE_READ (read src; dst receives at most one 4-byte word),
+ * MOE_PROBE_WRITE (write dst).  bytes: a multiple of 16, > 0; device
+ * pointers 16-byte aligned.  Errors: MOE_ERR_INVALID, MOE_ERR_HIP. */
+typedef enum moe_probe_kind {
+    MOE_PROBE_COPY = 0,
+    MOE_PROBE_READ = 1,
+    MOE_PROBE_WRITE = 2
+} moe_probe_kind;
+
+int moe_hbm_probe(int kind, void* dst, const void* src, size_t bytes, hipStream_t stream);
+
 /* Static description of a status code; never NULL. */
 const char* moe_strerror(int status);
 

@@ -363,8 +363,14 @@ def run_dispatch_fixed(x: np.ndarray, idx: np.ndarray, E: int, T_max: int,
     return out
 
 
+def _assert_finite_bf16(a: np.ndarray, what: str):
+    """The inputs are finite: every bf16 pattern has an exponent below 0xFF."""
+    assert not np.any((np.asarray(a, dtype=np.uint16) & 0x7F80) == 0x7F80), f"non-finite {what}"
+
+
 def run_dispatch(x: np.ndarray, idx: np.ndarray, E: int, fp8: bool = False) -> dict:
     """Every dispatch step, in the pages' order; returns all buffers."""
+    _assert_finite_bf16(x, "tokens")
     N, T, H = x.shape
     K = idx.shape[2]
     pl = plan(idx, E)
@@ -453,6 +459,8 @@ def partial_token(rows: np.ndarray, w: np.ndarray, rank: np.ndarray) -> np.ndarr
 
 def run_combine(y: np.ndarray, w: np.ndarray, pl: dict, H: int) -> dict:
     """Every combine step, in order; y is the expert output in expert-row order."""
+    _assert_finite_bf16(y, "expert outputs")
+    assert np.all(np.isfinite(w)), "non-finite weights"
     N, T, K = pl["pos"].shape
     comb_send = combine_send(y, pl)
     comb_recv = combine_transfer(comb_send, pl, T, K)
@@ -477,6 +485,8 @@ def partial_plan(idx: np.ndarray, E: int) -> dict:
 
 def run_partial_combine(y: np.ndarray, w: np.ndarray, idx: np.ndarray, pl: dict, H: int) -> dict:
     """Combine with sender-side partial sums; y in expert-row order, pl from plan()."""
+    _assert_finite_bf16(y, "expert outputs")
+    assert np.all(np.isfinite(w)), "non-finite weights"
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     N, T, K = idx.shape
     E = pl["cnt"].shape[1]

@@ -64,3 +64,13 @@ def test_host_validation_without_gpu(lib):
     assert lib.moe_group_timing_enable(None, 1) == mep.MOE_ERR_INVALID
     assert lib.moe_group_status(None, None) == mep.MOE_ERR_INVALID
     assert lib.moe_group_destroy(None) == 0
+
+
+def test_probe_validation_without_gpu(lib):
+    """The measurement probes reject bad arguments before any HIP call."""
+    import combine_moe_dispatch_amd as mep
+    P = ctypes.c_void_p
+    lib.moe_hbm_probe.argtypes = [ctypes.c_int, P, P, ctypes.c_size_t, P]
+    for kind, dst, src, n in [(3, 16, 16, 16), (0, 16, 16, 0), (0, 16, 16, 24), (0, 0, 16, 16),
+                              (0, 16, 0, 16), (1, 16, 8, 16), (2, 8, 0, 16), (-1, 16, 16, 16)]:
+        assert lib.moe_hbm_probe(kind, dst, src, n, None) == mep.MOE_ERR_INVALID, (kind, dst, src, n)
