@@ -6,14 +6,16 @@
 //
 // Every step is a permutation copy, a small scan, a codec or a weighted sum:
 // nothing is a dense contraction, so there is no MFMA here and the kernels are
-// bound by HBM bandwidth.  Rows move as 16-byte vectors, one wavefront per row
-// (one 14 KiB DeepSeek-shaped row = 14 vectors per lane, all loads issued
-// before the stores), so each wave keeps a whole row in flight.  Row order is
-// driven by small int32 maps that the pack kernel writes from the offsets, so
-// the transfer, shuffle and combine kernels are pure gathers or scatters.
+// bound by HBM bandwidth.  Rows move as 16-byte vectors; a row is shared by
+// one to four waves (a 14 KiB DeepSeek-shaped row: four waves of 3.5 KiB,
+// 4 vectors per lane), and every lane issues all its loads before its first
+// store.  Row order is driven by small int32 maps that the pack kernel writes
+// from the offsets, so the transfer, shuffle and combine kernels are pure
+// gathers in destination order.
 //
-// Every kernel after the route count checks the device error word first and
-// writes nothing once an invalid expert id has been seen.
+// Every kernel after the route plan checks the device error word first and
+// writes nothing once an invalid expert id (or a capacity overflow) has been
+// seen.
 #include "moe_kernels.h"
 
 #include <hip/hip_ext.h>
@@ -108,9 +110,13 @@ __device__ int block_exclusive_scan(int v, int* wave_sums, int* total)
 // by atomic adds in shared memory of a single block, then summed cumulatively
 // to get the offsets inside the contiguous send buffer).  LDS atomics give the
 // counts; the order inside an expert is made stable ((t,k) ascending) with a
-// per-chunk counting sort: inside a wave, lanes with equal expert ids find
-// their rank by ballot + popcount; across the block's waves a per-expert scan
-// of the wave counts plus a running per-expert cursor gives the position.
+// per-chunk counting sort: each lane sets its bit in a 64-bit lane mask per
+// (wave, key) in LDS, and its position is a running per-key cursor plus the
+// set bits of lower waves' masks and of its own wave's mask below its lane.
+// With the partial combine every item carries a second key (its destination
+// rank, when it is the first item of its token there), ranked in the same
+// pass.  With the fixed-slot layout a (sender, expert) count above the slot
+// count raises the capacity bit.
 //
 // Offsets ([EFA] "Send and receive buffers": once the per-expert counts are
 // exchanged, each rank derives where to write and the offsets it receives
@@ -818,7 +824,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
 }
 
 // ---------------------------------------------------------------------------
-// Row movers.  One wave per destination (gather) or source (scatter) row.
+// Row movers: gathers in destination order, a row per one to four waves.
 // ---------------------------------------------------------------------------
 // Loads use a clamped index instead of a predicate, so all U loads of a lane
 // are issued back to back before the first wait; lanes past the row end
