@@ -55,7 +55,9 @@ def test_host_validation_without_gpu(lib):
     # descriptor checks happen before any HIP call
     for args in [(2, 7, 2, 256, 16, 0), (0, 8, 2, 256, 16, 0), (2, 8, 2, 100, 16, 0),
                  (2, 8, 2, 264, 16, 1), (2, 8, 65, 256, 16, 0), (2, 8, 2, 256, 16, 0, 2),
-                 (2, 8, 2, 256, 16, 0, 0, 2)]:
+                 (2, 8, 2, 256, 16, 0, 0, 2), (2, 8, 2, 256, 16, 0, 0, 0, 2),
+                 # fixed-slot layout: N*E*T_max slots must stay below 2^31
+                 (1024, 1024, 1, 8, 2048, 0, 0, 0, 1)]:
         with pytest.raises(mep.MoeError) as ei:
             mep.moe_group_create(*args)
         assert ei.value.status == mep.MOE_ERR_INVALID
