@@ -1302,11 +1302,39 @@ __device__ inline void add_row8(float (&acc)[8], const v4u& v)
     }
 }
 
+// Adds the m partial rows of a token (lane j of term_row holds the row of the
+// j-th one) into acc in order j = 0..m-1.  m is the same on every lane of the
+// wave; the rows are loaded together, exactly m of them (a token visits
+// between 1 and min(K, N) ranks, often far fewer than K).
+template <int M, int U>
+__device__ inline void sum_partials(int m, float (&acc)[U][8], const v4u* src, int term_row,
+                                    int stride, int base, int n, int lane)
+{
+    if constexpr (M > 1) {
+        if (m < M) {
+            sum_partials<M - 1, U>(m, acc, src, term_row, stride, base, n, lane);
+            return;
+        }
+    }
+    v4u v[M][U];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        const v4u* row = src + (int64_t)readlane(term_row, j) * stride;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[j][u] = ld_nt(row + min(base + u * WAVE + lane, n - 1));
+    }
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            add_row8(acc[u], v[j][u]);
+}
+
 // The token owner's sum: one wave group per token.  The head lanes (one per
 // rank the token visited) are put in rank order, lane j then holds the row of
-// the j-th partial; the m <= K rows are loaded together (with KT known, the
-// loads past m repeat the last row and are not added) and added in fp32 from
-// +0, then rounded to bf16.
+// the j-th partial; the m <= K rows are added in fp32 from +0, then rounded
+// to bf16.
 template <int KT, int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void partial_reduce_kernel(Shape sh, Plan p,
                                                                       const v4u* __restrict__ precv,
@@ -1364,20 +1392,7 @@ __global__ __launch_bounds__(COPY_THREADS) void partial_reduce_kernel(Shape sh, 
             for (int e = 0; e < 8; ++e)
                 acc[u][e] = 0.0f;
         if constexpr (KT > 0) {
-            v4u v[KT][U];
-#pragma unroll
-            for (int j = 0; j < KT; ++j) {
-                const v4u* row = src + (int64_t)readlane(term_row, min(j, m - 1)) * stride;
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    v[j][u] = ld_nt(row + min(base + u * WAVE + lane, n - 1));
-            }
-#pragma unroll
-            for (int j = 0; j < KT; ++j)
-                if (j < m)
-#pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        add_row8(acc[u], v[j][u]);
+            sum_partials<KT, U>(m, acc, src, term_row, stride, base, n, lane);
         } else {
             for (int j = 0; j < m; ++j) {
                 const v4u* row = src + (int64_t)readlane(term_row, j) * stride;
