@@ -576,9 +576,10 @@ template <int SPLIT, int ALIGN = 1>
 __device__ inline RowSlot row_slot(int n)
 {
     RowSlot rs;
-    const int w = threadIdx.x / WAVE;
-    rs.row = (int64_t)blockIdx.x * (ROWS_PER_BLOCK / SPLIT) + w / SPLIT;
-    const int part = w % SPLIT;
+    // waves are numbered across blocks, so a row may span two blocks (SPLIT 8)
+    const int64_t w = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    rs.row = w / SPLIT;
+    const int part = (int)(w % SPLIT);
     const int plen = ((n + SPLIT - 1) / SPLIT + ALIGN - 1) / ALIGN * ALIGN;
     rs.b0 = min(n, part * plen);
     rs.len = min(n, rs.b0 + plen) - rs.b0;
@@ -1489,8 +1490,7 @@ inline RowShape row_shape(int n)
 
 inline unsigned row_blocks(int64_t rows, int split)
 {
-    const int64_t per_block = ROWS_PER_BLOCK / split;
-    const int64_t b = (rows + per_block - 1) / per_block;
+    const int64_t b = (rows * split + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
     return (unsigned)(b > 0 ? b : 1);
 }
 
@@ -1621,19 +1621,31 @@ hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r, co
 // measured ~3% faster than 2 at K = 8; the partial send: ~2% faster than 2,
 // at 180 VGPRs against 100) and for any other K with U = 2; rows are split
 // across waves as for the movers.
+// The token kernels hold K rows' vectors at once.  Rows of 9-16 vectors per
+// lane (over 4 waves) go to 8 waves with half as many vectors per lane: the
+// rows then take ~64 VGPRs and the kernel runs at twice the occupancy
+// (measured: partial send 172 -> 165 us on DeepSeek-R1 decode).
+inline int token_split(int n)
+{
+    const int per_lane = (n + WAVE - 1) / WAVE;
+    return per_lane > 8 && per_lane <= 16 ? 8 : row_shape(n).split;
+}
+
 #define MOE_TOKEN_SPLIT(KERNEL, KT, U, split, grid, block, L, ...)                                  \
     do {                                                                                           \
         if ((split) == 1)                                                                          \
             go((KERNEL<KT, U, 1>), grid, block, 0, L, __VA_ARGS__);                                \
         else if ((split) == 2)                                                                     \
             go((KERNEL<KT, U, 2>), grid, block, 0, L, __VA_ARGS__);                                \
-        else                                                                                       \
+        else if ((split) == 4)                                                                     \
             go((KERNEL<KT, U, 4>), grid, block, 0, L, __VA_ARGS__);                                \
+        else                                                                                       \
+            go((KERNEL<KT, (U + 1) / 2, 8>), grid, block, 0, L, __VA_ARGS__);                      \
     } while (0)
 
 #define MOE_DISPATCH_TOKEN(sh, KERNEL, UK, tokens, L, ...)                                         \
     do {                                                                                           \
-        const int split_ = row_shape((sh).comb_vecs).split;                                        \
+        const int split_ = token_split((sh).comb_vecs);                                            \
         const dim3 grid_(row_blocks((tokens), split_)), block_(COPY_THREADS);                      \
         switch ((sh).K) {                                                                          \
         case 1: MOE_TOKEN_SPLIT(KERNEL, 1, UK, split_, grid_, block_, L, __VA_ARGS__); break;      \
