@@ -496,6 +496,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="tokens per rank (default: the workload's own)")
     ap.add_argument("--transport", choices=["staged", "direct"], default="staged",
                     help="staged: send buffer + modelled transfer (the measured contract); "
                          "direct: pack/combine write the peer's rows")
@@ -554,6 +556,8 @@ def main() -> int:
     from workloads import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.config]
+    if args.tokens is not None:
+        cfg = cfg.with_(T=args.tokens)
     N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
     R = cfg.rows
     fp8 = cfg.dtype == "fp8"
