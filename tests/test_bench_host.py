@@ -1,0 +1,146 @@
+"""Host logic of bench.py on the CPU: the algorithmic byte model against the
+closed-form totals of the method (every mandated buffer written once and read
+once by the next stage), the partial-row count against brute force, the
+counter scaling and trace tables on small synthetic profiler databases, the
+source hash's indifference to comments, and the one-GPU guard."""
+import os
+import sqlite3
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from workloads import CONFIGS, make_routing
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _closed_form(cfg, transport="staged"):
+    """Row-payload bytes of one dispatch+combine: x read once per token; each
+    dispatch row written by pack, read+written by the transfer, read+written by
+    the shuffle (5 row passes; 3 when pack writes the receive rows itself);
+    each expert output row read by combine-send and written to the return
+    buffer, read+written by the transfer back, read by the reduce (5 passes;
+    3 when combine-send writes the return rows itself); one x-sized output."""
+    N, T, K, H = cfg.N, cfg.T, cfg.K, cfg.H
+    R = N * T * K
+    hb = (H + 4 * (H // 128)) if cfg.dtype == "fp8" else 2 * H
+    passes_d, passes_c = (5, 5) if transport == "staged" else (3, 3)
+    return N * T * H * 2 + passes_d * R * hb + passes_c * R * 2 * H + N * T * H * 2
+
+
+@pytest.mark.parametrize("key", ["A", "B", "C", "D", "E"])
+@pytest.mark.parametrize("transport", ["staged", "direct"])
+def test_byte_model_matches_closed_form(key, transport):
+    cfg = CONFIGS[key]
+    kb = bench.kernel_bytes(cfg, transport)
+    total = sum(kb.values())
+    main = _closed_form(cfg, transport)
+    # the rest is metadata: a few int32 per row and the per-rank tables
+    R, N, E = cfg.rows, cfg.N, cfg.E
+    small = 64 * R + 64 * N * E + 16 * N * (N + 1) + 64 * E
+    assert main <= total <= main + small, (total, main)
+
+
+def test_headline_totals():
+    """The DeepSeek-R1 decode totals: 4.817 GB staged (602 us at 8 TB/s),
+    2.937 GB with direct push (367 us)."""
+    c = CONFIGS["C"]
+    assert sum(bench.kernel_bytes(c).values()) == 4_816_804_364
+    assert sum(bench.kernel_bytes(c, "direct").values()) == 2_937_494_028
+
+
+def test_partial_byte_model_moves_p_rows():
+    """With the partial combine the combine passes carry P rows instead of R."""
+    cfg = CONFIGS["C"]
+    P = 29_804
+    kb = bench.kernel_bytes(cfg, "staged", "partial", P)
+    hy = 2 * cfg.H
+    assert kb["partial_transfer"] == 2 * P * hy
+    assert kb["partial_send"] - P * hy == cfg.rows * (hy + 24)
+    assert kb["partial_reduce"] - P * hy == cfg.rows * 8 + cfg.N * cfg.T * cfg.H * 2
+    assert "combine_reduce" not in kb and "transfer_back" not in kb
+
+
+@pytest.mark.parametrize("key", ["A", "B", "E"])
+def test_partial_rows_brute_force(key):
+    cfg = CONFIGS[key].with_(T=min(CONFIGS[key].T, 24))
+    idx = make_routing(cfg)[0]
+    pairs = set()
+    for s in range(cfg.N):
+        for t in range(cfg.T):
+            for k in range(cfg.K):
+                pairs.add((s, t, int(idx[s, t, k]) // cfg.L))
+    assert bench.partial_rows(cfg, idx) == len(pairs)
+
+
+def test_code_only_ignores_comments_keeps_strings():
+    a = 'int x = 1; // note\n/* block\n comment */ const char* s = "// not a comment";\n'
+    b = 'int x = 1;\nconst char* s = "// not a comment";'
+    assert bench._code_only(a) == bench._code_only(b)
+    assert '"// not a comment"' in bench._code_only(a)
+    assert bench._code_only("a  b\n\tc") == "a b c"
+    assert bench._code_only("x = 1; // a") != bench._code_only("x = 2; // a")
+
+
+def _counters_db(path, rows):
+    con = sqlite3.connect(path)
+    con.execute("create table counters_collection (kernel_name text, counter_name text, value real)")
+    con.executemany("insert into counters_collection values (?, ?, ?)", rows)
+    con.commit()
+    con.close()
+
+
+def test_traffic_scaling_from_counters(tmp_path):
+    """Each counter is scaled by CAL_BYTES / (its reading on the calibration
+    copy): a kernel that reads what the copy read moves CAL_BYTES."""
+    cfg = CONFIGS["C"]
+    cal = bench.CAL_BYTES
+    copy_name = "void at::native::elementwise_kernel<128, 4>(int, Func)"
+    tr = "void moe::(anonymous namespace)::transfer_kernel<4, 4>(moe::Shape, ...)"
+    # the counters see half the fetched bytes and all the written bytes
+    _counters_db(tmp_path / "cal_f.db", [(copy_name, "FETCH_SIZE", cal / 2048.0)] * 5)
+    _counters_db(tmp_path / "cal_w.db", [(copy_name, "WRITE_SIZE", cal / 1024.0)] * 5)
+    kb = bench.kernel_bytes(cfg)["transfer"]
+    half = kb / 2
+    _counters_db(tmp_path / "f.db", [(tr, "FETCH_SIZE", half / 2048.0)] * 3)
+    _counters_db(tmp_path / "w.db", [(tr, "WRITE_SIZE", half / 1024.0)] * 3)
+    rec = bench.traffic_from(cfg, str(tmp_path / "f.db"), str(tmp_path / "w.db"),
+                             str(tmp_path / "cal_f.db"), str(tmp_path / "cal_w.db"))
+    assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
+    t = rec["kernels"]["transfer"]
+    assert t["launches"] == 3
+    assert abs(t["hbm_bytes_per_launch"] - kb) <= 2
+    assert t["ratio"] == 1.0
+    assert rec["source_hash"] == bench.kernel_source_hash()
+
+
+def test_trace_summary_table(tmp_path):
+    cfg = CONFIGS["C"]
+    db = tmp_path / "trace.db"
+    con = sqlite3.connect(db)
+    con.execute("create table kernels (name text, duration integer)")
+    rows = [("void moe::(anonymous namespace)::transfer_kernel<4, 4>(...)", d)
+            for d in (150_000, 160_000, 170_000)]
+    rows += [("void moe::(anonymous namespace)::route_plan_kernel(moe::RouteArgs, moe::Plan)", 12_000)]
+    rows += [("void at::native::vectorized_elementwise_kernel<4>(...)", 5_000)]
+    con.executemany("insert into kernels values (?, ?)", rows)
+    con.commit()
+    con.close()
+    table = bench.trace_summary(cfg, str(db)).splitlines()
+    assert table[0].startswith("| kernel | launches | avg us")
+    body = {line.split("|")[1].strip(): line for line in table[2:]}
+    assert set(body) == {"route_plan", "transfer"}
+    cells = [c.strip() for c in body["transfer"].split("|")[1:-1]]
+    assert cells[1:5] == ["3", "160.00", "150.00", "170.00"]
+    kb = bench.kernel_bytes(cfg)["transfer"]
+    assert int(cells[5]) == round(kb / 160e-6 / 1e9)
+
+
+def test_several_gpus_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
