@@ -561,10 +561,10 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
 
 // ---------------------------------------------------------------------------
 // Work split of the row kernels.  SPLIT waves share one row, each moving a
-// contiguous part (ALIGN-vector aligned), so a 256-thread block covers
-// 4/SPLIT rows.  Long rows are split until a wave moves about 4 KiB: many
-// short waves keep more rows in flight per CU than one long wave per row
-// (measured on the 14 KiB DeepSeek-shaped rows).
+// contiguous part (ALIGN-vector aligned); waves are numbered across blocks,
+// so with SPLIT 8 a row spans two 256-thread blocks.  Long rows are split
+// until each lane moves about 2 vectors: many short waves keep more rows in
+// flight per CU than a few long ones (measured on 7-14 KiB rows).
 // ---------------------------------------------------------------------------
 struct RowSlot {
     int64_t row;
@@ -576,7 +576,6 @@ template <int SPLIT, int ALIGN = 1>
 __device__ inline RowSlot row_slot(int n)
 {
     RowSlot rs;
-    // waves are numbered across blocks, so a row may span two blocks (SPLIT 8)
     const int64_t w = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
     rs.row = w / SPLIT;
     const int part = (int)(w % SPLIT);
@@ -1478,13 +1477,17 @@ struct RowShape {
 
 inline RowShape row_shape(int n)
 {
+    // measured against 4 vectors per lane over up to 4 waves: DeepSeek-R1
+    // decode step 820 -> 802 us (14 KiB rows, 8 waves of 2), fp8 prefill
+    // 21.4 -> 20.6 ms (7 KiB payload rows, 4 waves of 2); 16 waves of 1 lost
+    // 8%
     const int per_lane = (n + WAVE - 1) / WAVE;
     if (per_lane <= 1) return {1, 1};
     if (per_lane <= 2) return {2, 1};
-    if (per_lane <= 4) return {4, 1};
-    if (per_lane <= 8) return {4, 2};
-    if (per_lane <= 16) return {4, 4};
-    if (per_lane <= 32) return {8, 4};
+    if (per_lane <= 4) return {2, 2};
+    if (per_lane <= 8) return {2, 4};
+    if (per_lane <= 16) return {2, 8};
+    if (per_lane <= 32) return {4, 8};
     return {16, 4};
 }
 
@@ -1498,19 +1501,21 @@ inline unsigned row_blocks(int64_t rows, int split)
     do {                                                                                           \
         const dim3 grid_(row_blocks((GRID_ROWS), (rsh).split)), block_(COPY_THREADS);              \
         if ((rsh).split == 1 && (rsh).u == 1)                                                      \
-            go((KERNEL<1, 1>), grid_, block_, 0, __VA_ARGS__);                     \
-        else if ((rsh).split == 1 && (rsh).u == 2)                                                 \
-            go((KERNEL<2, 1>), grid_, block_, 0, __VA_ARGS__);                     \
+            go((KERNEL<1, 1>), grid_, block_, 0, __VA_ARGS__);                                     \
         else if ((rsh).split == 1)                                                                 \
-            go((KERNEL<4, 1>), grid_, block_, 0, __VA_ARGS__);                     \
+            go((KERNEL<2, 1>), grid_, block_, 0, __VA_ARGS__);                                     \
         else if ((rsh).split == 2)                                                                 \
-            go((KERNEL<4, 2>), grid_, block_, 0, __VA_ARGS__);                     \
-        else if ((rsh).u == 4)                                                                     \
-            go((KERNEL<4, 4>), grid_, block_, 0, __VA_ARGS__);                     \
-        else if ((rsh).u == 8)                                                                     \
-            go((KERNEL<8, 4>), grid_, block_, 0, __VA_ARGS__);                     \
+            go((KERNEL<2, 2>), grid_, block_, 0, __VA_ARGS__);                                     \
+        else if ((rsh).split == 4 && (rsh).u == 2)                                                 \
+            go((KERNEL<2, 4>), grid_, block_, 0, __VA_ARGS__);                                     \
+        else if ((rsh).split == 4 && (rsh).u == 4)                                                 \
+            go((KERNEL<4, 4>), grid_, block_, 0, __VA_ARGS__);                                     \
+        else if ((rsh).split == 4)                                                                 \
+            go((KERNEL<16, 4>), grid_, block_, 0, __VA_ARGS__);                                    \
+        else if ((rsh).u == 2)                                                                     \
+            go((KERNEL<2, 8>), grid_, block_, 0, __VA_ARGS__);                                     \
         else                                                                                       \
-            go((KERNEL<16, 4>), grid_, block_, 0, __VA_ARGS__);                    \
+            go((KERNEL<4, 8>), grid_, block_, 0, __VA_ARGS__);                                     \
     } while (0)
 
 }  // namespace
@@ -1621,16 +1626,6 @@ hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r, co
 // measured ~3% faster than 2 at K = 8; the partial send: ~2% faster than 2,
 // at 180 VGPRs against 100) and for any other K with U = 2; rows are split
 // across waves as for the movers.
-// The token kernels hold K rows' vectors at once.  Rows of 9-16 vectors per
-// lane (over 4 waves) go to 8 waves with half as many vectors per lane: the
-// rows then take ~64 VGPRs and the kernel runs at twice the occupancy
-// (measured: partial send 172 -> 165 us on DeepSeek-R1 decode).
-inline int token_split(int n)
-{
-    const int per_lane = (n + WAVE - 1) / WAVE;
-    return per_lane > 8 && per_lane <= 16 ? 8 : row_shape(n).split;
-}
-
 #define MOE_TOKEN_SPLIT(KERNEL, KT, U, split, grid, block, L, ...)                                  \
     do {                                                                                           \
         if ((split) == 1)                                                                          \
@@ -1640,12 +1635,16 @@ inline int token_split(int n)
         else if ((split) == 4)                                                                     \
             go((KERNEL<KT, U, 4>), grid, block, 0, L, __VA_ARGS__);                                \
         else                                                                                       \
-            go((KERNEL<KT, (U + 1) / 2, 8>), grid, block, 0, L, __VA_ARGS__);                      \
+            go((KERNEL<KT, U, 8>), grid, block, 0, L, __VA_ARGS__);                                \
     } while (0)
 
+// The token kernels hold all K rows' vectors of a token at once: with the
+// movers' split and 2 vectors per lane per row, K = 8 rows take 64 VGPRs
+// (4 waves per SIMD); at 4 vectors per lane over 4 waves they took 160-180
+// VGPRs and ran at 2 (partial send 172 -> 165 us on DeepSeek-R1 decode).
 #define MOE_DISPATCH_TOKEN(sh, KERNEL, UK, tokens, L, ...)                                         \
     do {                                                                                           \
-        const int split_ = token_split((sh).comb_vecs);                                            \
+        const int split_ = row_shape((sh).comb_vecs).split;                                        \
         const dim3 grid_(row_blocks((tokens), split_)), block_(COPY_THREADS);                      \
         switch ((sh).K) {                                                                          \
         case 1: MOE_TOKEN_SPLIT(KERNEL, 1, UK, split_, grid_, block_, L, __VA_ARGS__); break;      \
@@ -1653,7 +1652,7 @@ inline int token_split(int n)
         case 4: MOE_TOKEN_SPLIT(KERNEL, 4, UK, split_, grid_, block_, L, __VA_ARGS__); break;      \
         case 6: MOE_TOKEN_SPLIT(KERNEL, 6, UK, split_, grid_, block_, L, __VA_ARGS__); break;      \
         case 8: MOE_TOKEN_SPLIT(KERNEL, 8, UK, split_, grid_, block_, L, __VA_ARGS__); break;      \
-        default: MOE_TOKEN_SPLIT(KERNEL, 0, 2, split_, grid_, block_, L, __VA_ARGS__); break;      \
+        default: MOE_TOKEN_SPLIT(KERNEL, 0, UK, split_, grid_, block_, L, __VA_ARGS__); break;     \
         }                                                                                          \
     } while (0)
 
@@ -1663,7 +1662,7 @@ hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, 
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
         return hipSuccess;
-    MOE_DISPATCH_TOKEN(sh, combine_reduce_kernel, 4, tokens, L, sh, p, (const v4u*)r.comb_recv, w,
+    MOE_DISPATCH_TOKEN(sh, combine_reduce_kernel, 2, tokens, L, sh, p, (const v4u*)r.comb_recv, w,
                        (v4u*)out);
     return hipGetLastError();
 }
@@ -1674,7 +1673,7 @@ hipError_t launch_partial_send(const Shape& sh, const Plan& p, const Rows& r, co
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
         return hipSuccess;
-    MOE_DISPATCH_TOKEN(sh, partial_send_kernel, 4, tokens, L, sh, p, (const v4u*)y, r.recv_w,
+    MOE_DISPATCH_TOKEN(sh, partial_send_kernel, 2, tokens, L, sh, p, (const v4u*)y, r.recv_w,
                        (v4u*)(sh.direct ? r.comb_recv : r.comb_send));
     return hipGetLastError();
 }
@@ -1696,7 +1695,7 @@ hipError_t launch_partial_reduce(const Shape& sh, const Plan& p, const Rows& r, 
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
         return hipSuccess;
-    MOE_DISPATCH_TOKEN(sh, partial_reduce_kernel, 4, tokens, L, sh, p, (const v4u*)r.comb_recv,
+    MOE_DISPATCH_TOKEN(sh, partial_reduce_kernel, 2, tokens, L, sh, p, (const v4u*)r.comb_recv,
                        (v4u*)out);
     return hipGetLastError();
 }
