@@ -7,9 +7,9 @@
 // Every step is a permutation copy, a small scan, a codec or a weighted sum:
 // nothing is a dense contraction, so there is no MFMA here and the kernels are
 // bound by HBM bandwidth.  Rows move as 16-byte vectors; a row is shared by
-// one to four waves (a 14 KiB DeepSeek-shaped row: four waves of 3.5 KiB,
-// 4 vectors per lane), and every lane issues all its loads before its first
-// store.  Row order is driven by small int32 maps that the pack kernel writes
+// up to eight waves with about 2 vectors per lane (a 14 KiB DeepSeek-shaped
+// row: eight waves of 1.75 KiB), and every lane issues all its loads before
+// its first store.  Row order is driven by small int32 maps that the pack kernel writes
 // from the offsets, so the transfer, shuffle and combine kernels are pure
 // gathers in destination order.
 //
@@ -831,7 +831,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
 }
 
 // ---------------------------------------------------------------------------
-// Row movers: gathers in destination order, a row per one to four waves.
+// Row movers: gathers in destination order, a row per one to eight waves.
 // ---------------------------------------------------------------------------
 // Loads use a clamped index instead of a predicate, so all U loads of a lane
 // are issued back to back before the first wait; lanes past the row end
@@ -1413,11 +1413,12 @@ __global__ __launch_bounds__(COPY_THREADS) void partial_reduce_kernel(Shape sh, 
 // ---------------------------------------------------------------------------
 // Streaming probes: what HBM delivers to 16-byte nontemporal streams (a
 // measurement aid beside the kernels above, not a step of the method).  Each
-// 256-thread block moves 4 vectors per lane, all loads issued before the
-// stores; the read probe folds its loads into one word that is stored only
-// for a value the data never holds, so the loads cannot be dropped.
+// 256-thread block moves one vector per lane, the fastest of 1, 2, 4 and 8
+// measured (copy 6.6 TB/s against 6.35 with 4; write 6.8 against 5.95); the
+// read probe folds its loads into one word that is stored only for a value
+// the data never holds, so the loads cannot be dropped.
 // ---------------------------------------------------------------------------
-constexpr int PROBE_U = 4;
+constexpr int PROBE_U = 1;
 constexpr int PROBE_NT = 256;
 
 __global__ __launch_bounds__(PROBE_NT) void probe_copy_kernel(const v4u* __restrict__ src,
@@ -1622,10 +1623,8 @@ hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r, co
 }
 
 // Token kernels (one wave group per token, all K expert rows in flight) are
-// compiled for the common K with UK = 4 vectors per lane per row (the reduce:
-// measured ~3% faster than 2 at K = 8; the partial send: ~2% faster than 2,
-// at 180 VGPRs against 100) and for any other K with U = 2; rows are split
-// across waves as for the movers.
+// compiled for the common K (1, 2, 4, 6, 8) and for any other K, with UK
+// vectors per lane per row; rows are split across waves as for the movers.
 #define MOE_TOKEN_SPLIT(KERNEL, KT, U, split, grid, block, L, ...)                                  \
     do {                                                                                           \
         if ((split) == 1)                                                                          \
