@@ -18,8 +18,8 @@
 // combine").  Row size of a pool = max(payload row, 2H) = 2H bytes.
 //
 // With the fixed-slot layout ([EPMC] "Portable kernels") the receive pool and
-// its planes instead hold one region of T_max slots per (receiver, source,
-// local expert): N*E*T_max rows.  The direct transport has no send pool; the
+// its planes instead hold T_max slots per (source, expert), each expert's
+// area slot-major (row (e*T_max + i)*N + s): N*E*T_max rows.  The direct transport has no send pool; the
 // partial combine's rows (at most N*T*K) reuse whichever pools combine uses.
 #include <hip/hip_runtime.h>
 

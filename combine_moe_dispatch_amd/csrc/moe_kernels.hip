@@ -609,8 +609,9 @@ struct RowDest {
 };
 
 // With the fixed-slot layout ([EPMC] "Portable kernels") the receive-plane
-// row needs only the sender's own offsets: slot pk - soff[s][e] of region
-// (d, s, e - d*L).
+// row needs only the sender's own offsets: slot i = pk - soff[s][e] of the
+// pair (s, e) is row (e*T_max + i)*N + s (each expert's area slot-major, so
+// the filled slots of all senders sit together at its start).
 __device__ inline RowDest row_dest(const Shape& sh, const Plan& p, int s, int e, int pk)
 {
     const int64_t TK = (int64_t)sh.T * sh.K;
@@ -621,7 +622,7 @@ __device__ inline RowDest row_dest(const Shape& sh, const Plan& p, int s, int e,
     rd.q = p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + pk - so[d * sh.L];
     rd.r = p.ebase[(size_t)s * sh.E + e] + pk - so[e];
     const int i = pk - so[e];
-    const int64_t slot = (((int64_t)d * sh.N + s) * sh.L + (e - d * sh.L)) * sh.slots + i;
+    const int64_t slot = ((int64_t)e * sh.slots + i) * sh.N + s;
     rd.qd = sh.fixed ? (int32_t)slot : rd.q;
     rd.ok = (uint64_t)rd.q < (uint64_t)sh.rows && (uint64_t)rd.r < (uint64_t)sh.rows &&
             (uint64_t)pk < (uint64_t)TK &&

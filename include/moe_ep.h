@@ -107,11 +107,11 @@ typedef enum moe_combine_mode {
  *   MOE_LAYOUT_PACKED      rank d's receive rows are contiguous at bases
  *                          computed from the exchanged counts, sources
  *                          ascending ([EFA] "Send and receive buffers").
- *   MOE_LAYOUT_FIXED_SLOT  rank d holds one region of max_tokens slots per
- *                          (source rank, local expert), at row
- *                          ((d*N + s)*L + j)*max_tokens; a sender writes its
- *                          i-th row for expert e = d*L + j to slot i, an
- *                          address it knows from its own counts ([EPMC]
+ *   MOE_LAYOUT_FIXED_SLOT  rank d holds, for each of its experts
+ *                          e = d*L + j, an area of max_tokens slot planes of
+ *                          N rows; a sender s writes its i-th row for expert
+ *                          e to row (e*max_tokens + i)*N + s, an address it
+ *                          knows from its own counts ([EPMC]
  *                          "Portable kernels": the fixed token maximum bounds
  *                          each (source, local expert) share).  The receive
  *                          buffers then have N*E*max_tokens rows.  A sender

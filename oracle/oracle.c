@@ -542,12 +542,14 @@ void orc_expert_rows(int N, int T, int K, int E, const int32_t* idx, const int32
  * for the group, and that also bounds what a rank can receive from each
  * source rank for each of its local experts, so a sender can work out a
  * unique address on the receiver without synchronising with other ranks.
- * Reading taken here: receiver d holds, for every source rank s and local
- * expert j, a region of T_max slots starting at row ((d*N + s)*L + j)*T_max
- * of the pooled receive array (N*E*T_max rows in all); sender s's i-th row for
- * expert e = d*L + j (i = its rank among s's rows for e, (t,k) order) goes to
- * slot i of that region.  A (sender, expert) count above T_max -- possible
- * only when a token names an expert more than once -- does not fit.
+ * Reading taken here: receiver d holds the areas of its experts e = d*L + j,
+ * each T_max*N rows of the pooled receive array (N*E*T_max rows in all), slot
+ * index major and source rank minor: sender s's i-th row for expert e (i = its
+ * rank among s's rows for e, (t,k) order) goes to row (e*T_max + i)*N + s.
+ * Each (source, expert) pair so owns T_max slots (every N-th row of the
+ * expert's area), and the filled slots, i < count, gather at the start of
+ * each expert's area.  A (sender, expert) count above T_max -- possible only
+ * when a token names an expert more than once -- does not fit.
  */
 
 /* 1 when every (sender, expert) count fits its T_max slots, else 0. */
@@ -559,20 +561,18 @@ int orc_slot_capacity_ok(int N, int E, int T_max, const int32_t* cnt)
     return 1;
 }
 
-/* Slot row of every (s,t,k): the region of (d, s, j) plus the item's rank
+/* Slot row of every (s,t,k): (e*T_max + i)*N + s, with i the item's rank
  * among sender s's rows for its expert (pos - soff[s][e]). */
 void orc_slot_rows(int N, int T, int K, int E, int T_max, const int32_t* idx, const int32_t* soff,
                    const int32_t* pos, int64_t* slot)
 {
-    int L = E / N;
     for (int s = 0; s < N; ++s)
         for (int t = 0; t < T; ++t)
             for (int k = 0; k < K; ++k) {
-                size_t i = ((size_t)s * T + t) * K + k;
-                int e = idx[i];
-                int d = e / L, j = e % L;
-                int64_t region = (((int64_t)d * N + s) * L + j) * T_max;
-                slot[i] = region + (pos[i] - soff[(size_t)s * (E + 1) + e]);
+                size_t it = ((size_t)s * T + t) * K + k;
+                int e = idx[it];
+                int64_t i = pos[it] - soff[(size_t)s * (E + 1) + e];
+                slot[it] = ((int64_t)e * T_max + i) * N + s;
             }
 }
 
@@ -590,23 +590,20 @@ void orc_transfer_slots(int N, int T, int K, size_t row_bytes, const int32_t* po
         }
 }
 
-/* The receive shuffle out of the slots, from the layout alone: expert e =
- * d*L + j takes, for s ascending, the first cnt[s][e] slots of region
- * (d, s, j), in slot order, into expert rows eoff[e] onward; metadata as in
- * orc_shuffle. */
+/* The receive shuffle out of the slots, from the layout alone: expert e
+ * takes, for s ascending, source s's first cnt[s][e] slots, in slot order
+ * (rows (e*T_max + i)*N + s, i = 0, 1, ...), into expert rows eoff[e]
+ * onward; metadata as in orc_shuffle. */
 void orc_shuffle_slots(int N, int E, int T_max, size_t row_bytes, size_t scale_bytes,
                        const int32_t* cnt, const int32_t* eoff, const uint8_t* recv_x,
                        const uint8_t* recv_scale, const int32_t* recv_meta, uint8_t* expert_x,
                        uint8_t* expert_scale, int32_t* src_rank, int32_t* src_slot)
 {
-    int L = E / N;
     for (int e = 0; e < E; ++e) {
-        int d = e / L, j = e % L;
         int32_t r = eoff[e];
         for (int s = 0; s < N; ++s) {
-            size_t q0 = (((size_t)d * N + s) * L + j) * (size_t)T_max;
             for (int32_t i = 0; i < cnt[(size_t)s * E + e]; ++i, ++r) {
-                size_t q = q0 + (size_t)i;
+                size_t q = ((size_t)e * T_max + (size_t)i) * N + s;
                 memcpy(expert_x + (size_t)r * row_bytes, recv_x + q * row_bytes, row_bytes);
                 if (scale_bytes)
                     memcpy(expert_scale + (size_t)r * scale_bytes, recv_scale + q * scale_bytes,

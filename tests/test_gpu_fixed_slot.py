@@ -1,5 +1,5 @@
-"""GPU parity of the fixed-slot receive layout (one region of T_max slots per
-(receiver, source rank, local expert)) against the oracle: the plan, the
+"""GPU parity of the fixed-slot receive layout (T_max slots per (source rank,
+expert), each expert's area slot-major) against the oracle: the plan, the
 receive planes read at the oracle's slot rows, the combine rows, the
 dispatch outputs and the combined tokens, all bit-exact, both transports;
 the capacity error when a sender has more rows for one expert than T_max."""

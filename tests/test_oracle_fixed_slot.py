@@ -1,7 +1,8 @@
-"""Pins of the oracle's fixed-slot receive layout (one region of T_max slots per
-(receiver, source rank, local expert)): slot rows against a brute-force walk
-of the routing, slot contents against identity-carrying tokens, the dispatch
-result against the packed layout's (pinned elsewhere), and the capacity rule."""
+"""Pins of the oracle's fixed-slot receive layout (T_max slots per (source
+rank, expert), slot index major and source minor within each expert's area):
+slot rows against a brute-force walk of the routing, slot contents against
+identity-carrying tokens, the dispatch result against the packed layout's
+(pinned elsewhere), and the capacity rule."""
 import numpy as np
 import pytest
 
@@ -11,9 +12,8 @@ from workloads import CONFIGS, Config, make_inputs
 
 def _brute_slots(idx, E, T_max):
     """Walk the items of each sender in (t,k) order; the i-th item of (s, e)
-    takes slot i of region (e // L, s, e % L)."""
+    takes slot i of that pair: row s of slot plane i of expert e's area."""
     N, T, K = idx.shape
-    L = E // N
     seen = {}
     slot = np.zeros(idx.shape, dtype=np.int64)
     for s in range(N):
@@ -22,8 +22,8 @@ def _brute_slots(idx, E, T_max):
                 e = int(idx[s, t, k])
                 i = seen.get((s, e), 0)
                 seen[(s, e)] = i + 1
-                d, j = divmod(e, L)
-                slot[s, t, k] = ((d * N + s) * L + j) * T_max + i
+                area = e * T_max * N                  # expert e's T_max planes of N rows
+                slot[s, t, k] = area + i * N + s
     return slot, seen
 
 
@@ -87,10 +87,11 @@ def test_fixed_layout_gives_the_packed_dispatch_result(seed, fp8):
 
 
 def test_slot_contents_carry_their_tokens():
-    """Identity-carrying tokens (element 0 = s, element 1 = t): region
-    (d, s, j) holds in its first cnt slots the tokens of sender s routed to
-    expert d*L + j, t ascending, with their meta words; every other slot is
-    empty."""
+    """Identity-carrying tokens (element 0 = s, element 1 = t): the first cnt
+    slots of (source s, expert e) -- row s of slot planes 0, 1, ... of e's
+    area -- hold the tokens of sender s routed to e, t ascending, with their
+    meta words; every other slot is empty, and receiver d's rows are the areas
+    of its experts d*L .. d*L + L - 1."""
     cfg = CONFIGS["A"].with_(N=4, E=8, K=2, T=6, H=16, routing="uniform")
     T_max = 9
     inp = make_inputs(cfg)
@@ -106,10 +107,10 @@ def test_slot_contents_carry_their_tokens():
             for j in range(L):
                 e = d * L + j
                 items = [(t, k) for t in range(T) for k in range(K) if inp["idx"][s, t, k] == e]
-                base = ((d * N + s) * L + j) * T_max
                 for i, (t, k) in enumerate(items):
-                    row = res["recv_x"][base + i]
+                    q = d * L * T_max * N + (j * T_max + i) * N + s
+                    row = res["recv_x"][q]
                     assert (row[0], row[1]) == (s, t)
-                    assert meta[base + i] == t * K + k
-                    filled[base + i] = True
+                    assert meta[q] == t * K + k
+                    filled[q] = True
     assert np.all(meta[~filled] == -1)
