@@ -106,6 +106,31 @@ def test_create_rejects_bad_descriptors():
         assert ei.value.status == mep.MOE_ERR_INVALID, args
 
 
+def test_group_larger_than_the_device_reports_oom():
+    """The DeepSeek-R1 prefill shape with the fixed-slot layout needs
+    64 x 256 x 2048 slots of 14 KiB (~480 GB, more than the device holds):
+    create reports MOE_ERR_OOM, frees what it had allocated, and a group that
+    fits is created and runs afterwards."""
+    say("[gpu] oversized fixed-slot group")
+    free, total = torch.cuda.mem_get_info()
+    slots_bytes = 64 * 256 * 2048 * 7168 * 2
+    assert slots_bytes > total
+    with pytest.raises(mep.MoeError) as ei:
+        mep.moe_group_create(64, 256, 8, 7168, 2048, mep.MOE_FP8_E4M3, mep.MOE_TRANSPORT_STAGED,
+                             mep.MOE_COMBINE_RECEIVER, mep.MOE_LAYOUT_FIXED_SLOT)
+    assert ei.value.status == mep.MOE_ERR_OOM
+    free_after, _ = torch.cuda.mem_get_info()
+    assert free_after >= free - (64 << 20)
+    cfg = CONFIGS["A"]
+    inp = make_inputs(cfg)
+    g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16)
+    try:
+        run_cycle(torch, mep, cfg, inp, group=g, want_rows=False)
+        assert mep.moe_group_status(g) == mep.MOE_OK
+    finally:
+        mep.moe_group_destroy(g)
+
+
 def test_kernel_timing_mask():
     """Timing events attach only to the selected kernels; a cycle with every
     kernel selected reports one launch of each (T > 0)."""
