@@ -85,9 +85,9 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
             kb["transfer"] += 2 * R * 4
         for k in ("combine_pack", "transfer_back", "combine_push", "combine_reduce"):
             kb.pop(k, None)
-        # expert rows in (+ per item: position, rank, partial position, row
-        # pair, weight), partial rows out
-        kb["partial_send"] = R * hy + R * 24 + P * hy
+        # expert rows in (+ per item: its expert/receive row pair and weight;
+        # per partial row: its 16-byte record), partial rows out
+        kb["partial_send"] = R * hy + R * 12 + P * 16 + P * hy
         if transport == "staged":
             kb["partial_transfer"] = 2 * P * hy
         kb["partial_reduce"] = P * hy + R * 8 + tokens * H * 2

@@ -664,21 +664,65 @@ __device__ inline void record_maps(const Shape& sh, const Plan& p, const RowDest
         p.slot_of[rd.q] = rd.qd;
 }
 
+// Records of the expert-side partial combine, made by the lead wave of a
+// token (all lanes call it; lane k < K holds item k's expert rank d, or -1
+// if its indices failed, and its receive-plane and expert rows).  Each item
+// gets its (expert row, receive-plane row); each head item (the first of its
+// rank in the token) gets the token and the mask of the token's items on its
+// rank, at the partial row it heads in the layout the expert side writes
+// (owner layout when staged, token layout when direct), and, staged, the
+// owner row of its token-layout row for the transfer back.
+__device__ inline void record_partial(const Shape& sh, const Plan& p, int64_t tok, int s, int d,
+                                      const RowDest& rd)
+{
+    const int lane = lane_id();
+    const int N = sh.N;
+    int pp = -1;
+    if (lane < sh.K && d >= 0) {
+        const int64_t i = tok * sh.K + lane;
+        p.pitem[i] = make_int2(rd.r, rd.qd);
+        pp = p.ppos[i];
+    }
+    const uint64_t heads = __ballot(pp >= 0);
+    for (uint64_t hm = heads; hm != 0; hm &= hm - 1) {
+        const int f = __builtin_ctzll(hm);
+        const uint64_t mask = __ballot(d >= 0 && d == readlane(d, f));
+        if (lane == f) {
+            const int P = p.pbase[N];
+            const int tr = p.pbase[s] + pp;
+            const int orow = p.qbase[d] + p.qoff[(size_t)d * (N + 1) + s] + pp -
+                             p.psoff[(size_t)s * (N + 1) + d];
+            if ((unsigned)tr >= (unsigned)P || (unsigned)orow >= (unsigned)P) {
+                atomicOr(p.err, ERR_BIT_INTERNAL);
+            } else {
+                p.phead[sh.direct ? tr : orow] =
+                    make_int4((int)tok, 0, (int)(uint32_t)mask, (int)(uint32_t)(mask >> 32));
+                if (!sh.direct)
+                    p.pmap[tr] = orow;
+            }
+        }
+    }
+}
+
 // Lanes k < K: the destination row of (token, k) in the buffer pack writes
 // (send row, or receive row when direct), -1 if an index check failed; the
 // lead wave also writes the maps, the meta word t*K+k and, for the
-// expert-side partial combine, the router weight (dst_w non-null).
+// expert-side partial combine, the router weight (dst_w non-null) and the
+// partial-row records.
 __device__ inline int pack_dest(const Shape& sh, const Plan& p, const int32_t* __restrict__ idx,
                                 const float* __restrict__ w, int32_t* __restrict__ dst_meta,
                                 float* __restrict__ dst_w, int64_t tok, int s, int t, bool lead)
 {
     const int lane = lane_id();
-    int row = -1;
+    int row = -1, d = -1;
+    RowDest rd{};
     if (lane < sh.K) {
         const int64_t i = tok * sh.K + lane;
-        const RowDest rd = row_dest(sh, p, s, idx[i], p.pos[i]);
+        const int e = idx[i];
+        rd = row_dest(sh, p, s, e, p.pos[i]);
         if (rd.ok) {
             row = sh.direct ? rd.qd : rd.srow;
+            d = e / sh.L;
             if (lead) {
                 record_maps(sh, p, rd, s);
                 dst_meta[row] = t * sh.K + lane;
@@ -689,6 +733,8 @@ __device__ inline int pack_dest(const Shape& sh, const Plan& p, const int32_t* _
             atomicOr(p.err, ERR_BIT_INTERNAL);
         }
     }
+    if (sh.partial && lead)
+        record_partial(sh, p, tok, s, d, rd);
     return row;
 }
 
@@ -1157,140 +1203,120 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
 // where ppos is the route plan's position of the token's first item on d.
 // ---------------------------------------------------------------------------
 
-// One wave group per token (s, t).  Each lane k < K holds the expert row,
-// weight and destination rank of item k; every expert row is loaded once,
-// then each head item (first k of its rank) sums the items of its rank and
-// stores one bf16 row: to the owner layout (staged; the transfer moves it) or
-// straight to the token layout (direct).  The staged lead wave also records
-// pmap[token row] = owner row for the transfer.
-template <int KT, int U, int SPLIT>
+// Adds the terms of up to M set bits of `bits` (lowest first) into acc as an
+// fp32 fma chain in bit order, and clears them from `bits`.  Lane k of
+// my_row / my_w holds the expert row and router weight of item k.  The rows
+// are loaded together; the weights are read only after the row loads are
+// issued.  `bits` is the same on every lane.
+template <int M, int U>
+__device__ inline void fma_terms(uint64_t& bits, float (&acc)[U][8], const v4u* src, int my_row,
+                                 float my_w, int stride, int base, int n, int lane)
+{
+    if constexpr (M > 1) {
+        if (__popcll(bits) < M) {
+            fma_terms<M - 1, U>(bits, acc, src, my_row, my_w, stride, base, n, lane);
+            return;
+        }
+    }
+    int f[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        f[j] = __builtin_ctzll(bits);
+        bits &= bits - 1;
+    }
+    v4u v[M][U];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        const v4u* row = src + (int64_t)readlane(my_row, f[j]) * stride;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[j][u] = ld_nt(row + min(base + u * WAVE + lane, n - 1));
+    }
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+        hold(v[j]);
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        const float wj = readlane_f(my_w, f[j]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            fma_row8(acc[u], wj, v[j][u]);
+    }
+}
+
+// Terms loaded together per round: 2 rows of 2 vectors per lane keep the
+// kernel within 64 VGPRs, 8 waves per SIMD like the movers (most partials
+// have one term: a token seldom sends two of its K items to one rank).
+constexpr int PARTIAL_TERMS = 2;
+
+// One wave group per partial row, in the order of the layout the expert side
+// writes (owner layout (rank, sender, token) when staged, token layout
+// (sender, rank, token) when direct): a gather like the movers, so each wave
+// stores one row part and reads only the expert rows of its own terms.  The
+// row's record (written by pack) names its token and the mask of the token's
+// items held by this rank; lane k of the mask holds item k's expert row and
+// router weight, and the partial is the fp32 fma chain over the items in k
+// order from +0, rounded once to bf16.  Two dependent index loads (record,
+// then items) precede the row loads.  Iterating the owner layout in direct
+// mode too (so consecutive rows read one rank's expert rows) and scattering
+// the stores to the token layout was slower: DeepSeek-R1 decode 167 -> 167
+// us, Kimi-K2 Zipf 269 -> 293, all-to-rank-0 221 -> 258.  The grid covers the
+// largest possible P; rows past the cycle's P exit.
+template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void partial_send_kernel(Shape sh, Plan p,
                                                                     const v4u* __restrict__ y,
                                                                     const float* __restrict__ recv_w,
                                                                     v4u* __restrict__ dst)
 {
-    if (*p.err)
-        return;
     const int lane = lane_id();
     const RowSlot rs = row_slot<SPLIT>(sh.comb_vecs);
-    const int64_t tok = rs.row;
-    if (tok >= (int64_t)sh.N * sh.T)
+    const int64_t j = rs.row;
+    // at most one partial row per (token, rank): below the rows phead holds,
+    // so the record is read together with the error word and the cycle's P
+    // (pinned before the branch, or the compiler sinks its load after it)
+    if (j >= (int64_t)sh.N * sh.T * min(sh.K, sh.N))
         return;
-    const int K = KT > 0 ? KT : sh.K;
-    const int N = sh.N;
-    const int64_t s = tok / sh.T;
-    const int64_t TK = (int64_t)sh.T * sh.K;
-    int my_d = -1, my_row = 0, my_dst = 0;
-    float my_w = 0.0f;
-    bool head = false, bad = false;
-    if (lane < K) {
-        const int64_t i = tok * K + lane;
-        const int pk = p.pos[i];
-        const int pp = p.ppos[i];
-        my_d = p.pdst[i];
-        bad = (uint64_t)pk >= (uint64_t)TK || (unsigned)my_d >= (unsigned)N;
-        if (!bad) {
-            const int2 xd = p.xfer_dst[s * TK + pk];
-            bad = (uint64_t)xd.x >= (uint64_t)sh.recv_rows || (uint64_t)xd.y >= (uint64_t)sh.rows;
-            if (!bad) {
-                my_row = xd.y;
-                my_w = recv_w[xd.x];
-            }
-        }
-        if (!bad && pp >= 0) {
-            head = true;
-            const int P = p.pbase[N];
-            const int tr = p.pbase[s] + pp;
-            const int orow = p.qbase[my_d] + p.qoff[(size_t)my_d * (N + 1) + s] + pp -
-                             p.psoff[(size_t)s * (N + 1) + my_d];
-            bad = (unsigned)tr >= (unsigned)P || (unsigned)orow >= (unsigned)P;
-            my_dst = sh.direct ? tr : orow;
-            if (!bad && rs.lead && !sh.direct)
-                p.pmap[tr] = orow;
-        }
+    const int err = *p.err;
+    const int P = p.pbase[sh.N];
+    int4 h = p.phead[j];
+    asm volatile("" : "+v"(h.x), "+v"(h.y), "+v"(h.z), "+v"(h.w));
+    if (err != 0 || j >= P)
+        return;
+    const int K = sh.K;
+    const uint64_t mask = (uint64_t)(uint32_t)h.z | ((uint64_t)(uint32_t)h.w << 32);
+    const uint64_t kmask = K >= 64 ? ~0ull : (1ull << K) - 1;
+    int my_row = 0, my_q = 0;
+    bool bad = (uint64_t)h.x >= (uint64_t)sh.N * sh.T || mask == 0 || (mask & ~kmask) != 0;
+    if (!bad && lane < K && ((mask >> lane) & 1)) {
+        const int2 it = p.pitem[(int64_t)h.x * K + lane];
+        bad = (uint64_t)it.x >= (uint64_t)sh.rows || (uint64_t)it.y >= (uint64_t)sh.recv_rows;
+        my_row = it.x;
+        my_q = it.y;
     }
     if (__ballot(bad) != 0) {
         if (lane == 0)
             atomicOr(p.err, ERR_BIT_INTERNAL);
         return;
     }
-    const uint64_t heads = __ballot(head);
+    const float my_w = recv_w[my_q];
     const int n = rs.len;
     const int stride = sh.comb_vecs;
-    const v4u* ysrc = y + rs.b0;
-    v4u* out = dst + rs.b0;
+    const v4u* src = y + rs.b0;
+    v4u* o = dst + j * stride + rs.b0;
     for (int base = 0; base < n; base += WAVE * U) {
-        if constexpr (KT > 0) {
-            v4u v[KT][U];
+        float acc[U][8];
 #pragma unroll
-            for (int k = 0; k < KT; ++k) {
-                const v4u* row = ysrc + (int64_t)readlane(my_row, k) * stride;
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    v[k][u] = ld_nt(row + min(base + u * WAVE + lane, n - 1));
-            }
-            // keep the raw rows: otherwise each row is widened to fp32 right
-            // after its load, which serialises the loads
+            for (int e = 0; e < 8; ++e)
+                acc[u][e] = 0.0f;
+        for (uint64_t bits = mask; bits != 0;)
+            fma_terms<PARTIAL_TERMS, U>(bits, acc, src, my_row, my_w, stride, base, n, lane);
 #pragma unroll
-            for (int k = 0; k < KT; ++k)
-                hold(v[k]);
-            for (uint64_t hm = heads; hm != 0; hm &= hm - 1) {
-                const int f = __builtin_ctzll(hm);
-                const int df = readlane(my_d, f);
-                // the rows stay packed until the rank that uses them: pinned
-                // here, the widening to fp32 is not hoisted out of this loop
-                // (which would hold every row as fp32 and halve occupancy)
-#pragma unroll
-                for (int k = 0; k < KT; ++k)
-                    hold(v[k]);
-                float acc[U][8];
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[u][e] = 0.0f;
-#pragma unroll
-                for (int k = 0; k < KT; ++k)
-                    if (readlane(my_d, k) == df) {
-                        const float wk = readlane_f(my_w, k);
-#pragma unroll
-                        for (int u = 0; u < U; ++u)
-                            fma_row8(acc[u], wk, v[k][u]);
-                    }
-                v4u* o = out + (int64_t)readlane(my_dst, f) * stride;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int j = base + u * WAVE + lane;
-                    if (j < n)
-                        st_nt(pack_bf16x8(acc[u]), o + j);
-                }
-            }
-        } else {
-            for (uint64_t hm = heads; hm != 0; hm &= hm - 1) {
-                const int f = __builtin_ctzll(hm);
-                const int df = readlane(my_d, f);
-                float acc[U][8];
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[u][e] = 0.0f;
-                for (int k = f; k < K; ++k)
-                    if (readlane(my_d, k) == df) {
-                        const v4u* row = ysrc + (int64_t)readlane(my_row, k) * stride;
-                        const float wk = readlane_f(my_w, k);
-#pragma unroll
-                        for (int u = 0; u < U; ++u)
-                            fma_row8(acc[u], wk, ld_nt(row + min(base + u * WAVE + lane, n - 1)));
-                    }
-                v4u* o = out + (int64_t)readlane(my_dst, f) * stride;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int j = base + u * WAVE + lane;
-                    if (j < n)
-                        st_nt(pack_bf16x8(acc[u]), o + j);
-                }
-            }
+        for (int u = 0; u < U; ++u) {
+            const int jj = base + u * WAVE + lane;
+            if (jj < n)
+                st_nt(pack_bf16x8(acc[u]), o + jj);
         }
     }
 }
@@ -1713,11 +1739,24 @@ hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, 
 hipError_t launch_partial_send(const Shape& sh, const Plan& p, const Rows& r, const void* y,
                                const Launch& L)
 {
-    const int64_t tokens = (int64_t)sh.N * sh.T;
-    if (tokens == 0)
+    // at most one partial row per (token, rank), and at most K ranks per token
+    const int64_t p_max = (int64_t)sh.N * sh.T * (sh.K < sh.N ? sh.K : sh.N);
+    if (p_max == 0)
         return hipSuccess;
-    MOE_DISPATCH_TOKEN(sh, partial_send_kernel, 2, tokens, L, sh, p, (const v4u*)y, r.recv_w,
-                       (v4u*)(sh.direct ? r.comb_recv : r.comb_send));
+    // 2 vectors per lane per row and round whatever the row length (a round
+    // holds up to PARTIAL_TERMS rows and an fp32 accumulator); the movers' split
+    const int split = row_shape(sh.comb_vecs).split;
+    const dim3 grid(row_blocks(p_max, split)), block(COPY_THREADS);
+    const v4u* ysrc = (const v4u*)y;
+    v4u* dst = (v4u*)(sh.direct ? r.comb_recv : r.comb_send);
+    if (split == 1)
+        go(partial_send_kernel<2, 1>, grid, block, 0, L, sh, p, ysrc, r.recv_w, dst);
+    else if (split == 2)
+        go(partial_send_kernel<2, 2>, grid, block, 0, L, sh, p, ysrc, r.recv_w, dst);
+    else if (split == 4)
+        go(partial_send_kernel<2, 4>, grid, block, 0, L, sh, p, ysrc, r.recv_w, dst);
+    else
+        go(partial_send_kernel<2, 8>, grid, block, 0, L, sh, p, ysrc, r.recv_w, dst);
     return hipGetLastError();
 }
 
