@@ -587,14 +587,17 @@ __device__ inline RowSlot row_slot(int n, int64_t block = blockIdx.x)
 }
 
 // The hardware places blocks round-robin over the chip's 8 XCDs (block b on
-// XCD b mod 8), so consecutive rows run on different XCDs.  For the two
-// transfers, whose rows come in (sender -> receiver) segments of contiguous
-// source rows, the block index is remapped so that each XCD takes runs of
-// `run` consecutive blocks (one average segment): an XCD's CUs then stay in
-// one segment's source pages.  Measured, with run = one segment: DeepSeek-R1
-// decode (64 blocks a segment) transfers 155 -> 148-150 us; fp8 prefill (256
+// XCD b mod 8), so consecutive rows run on different XCDs.  The movers remap
+// the block index so that each XCD takes runs of `run` consecutive blocks: an
+// XCD's CUs (its L2 and its address translation) then stay in fewer source
+// pages at a time.  The transfers, whose rows come in (sender -> receiver)
+// segments of contiguous source rows, take one average segment per run:
+// DeepSeek-R1 decode (64 blocks a segment) 155 -> 148-150 us; fp8 prefill (256
 // and 512) 2610 -> 2460 and 5284 -> 4760 us, where round-robin placement took
-// one UTCL1 translation miss per row.  A ragged last tile keeps its order.
+// one UTCL1 translation miss per row.  The shuffle, the combine pack, the
+// combine push and the combine reduce take fixed runs (host side,
+// RUN_ROWS_BLOCKS and RUN_TOKEN_BLOCKS).  A ragged last tile keeps its order; run = 1 is plain
+// order.
 constexpr int XCDS = 8;
 
 __device__ inline int64_t xcd_run_block(uint32_t run)
@@ -981,7 +984,8 @@ __global__ __launch_bounds__(COPY_THREADS) void shuffle_kernel(Shape sh, Plan p,
                                                                float* __restrict__ expert_scale,
                                                                int32_t* __restrict__ src_rank,
                                                                int32_t* __restrict__ src_slot,
-                                                               int32_t* __restrict__ expert_offsets)
+                                                               int32_t* __restrict__ expert_offsets,
+                                                               uint32_t xrun)
 {
     if (*p.err)
         return;
@@ -990,7 +994,7 @@ __global__ __launch_bounds__(COPY_THREADS) void shuffle_kernel(Shape sh, Plan p,
             expert_offsets[e] = p.eoff[e];
     const int lane = lane_id();
     const int n = sh.payload_vecs;
-    const RowSlot rs = row_slot<SPLIT>(n);
+    const RowSlot rs = row_slot<SPLIT>(n, xcd_run_block(xrun));
     const int64_t r = rs.row;
     if (r >= sh.rows)
         return;
@@ -1017,13 +1021,14 @@ __global__ __launch_bounds__(COPY_THREADS) void shuffle_kernel(Shape sh, Plan p,
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void combine_pack_kernel(Shape sh, Plan p,
                                                                     const v4u* __restrict__ y,
-                                                                    v4u* __restrict__ comb_send)
+                                                                    v4u* __restrict__ comb_send,
+                                                                    uint32_t xrun)
 {
     if (*p.err)
         return;
     const int lane = lane_id();
     const int n = sh.comb_vecs;
-    const RowSlot rs = row_slot<SPLIT>(n);
+    const RowSlot rs = row_slot<SPLIT>(n, xcd_run_block(xrun));
     const int64_t qp = rs.row;
     if (qp >= sh.rows)
         return;
@@ -1064,13 +1069,14 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_back_kernel(Shape sh, P
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void combine_push_kernel(Shape sh, Plan p,
                                                                     const v4u* __restrict__ y,
-                                                                    v4u* __restrict__ comb_recv)
+                                                                    v4u* __restrict__ comb_recv,
+                                                                    uint32_t xrun)
 {
     if (*p.err)
         return;
     const int lane = lane_id();
     const int n = sh.comb_vecs;
-    const RowSlot rs = row_slot<SPLIT>(n);
+    const RowSlot rs = row_slot<SPLIT>(n, xcd_run_block(xrun));
     const int64_t srow = rs.row;
     if (srow >= sh.rows)
         return;
@@ -1119,12 +1125,13 @@ template <int KT, int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, Plan p,
                                                                       const v4u* __restrict__ comb_recv,
                                                                       const float* __restrict__ w,
-                                                                      v4u* __restrict__ out)
+                                                                      v4u* __restrict__ out,
+                                                                      uint32_t xrun)
 {
     if (*p.err)
         return;
     const int lane = lane_id();
-    const RowSlot rs = row_slot<SPLIT>(sh.comb_vecs);
+    const RowSlot rs = row_slot<SPLIT>(sh.comb_vecs, xcd_run_block(xrun));
     const int64_t tok = rs.row;
     if (tok >= (int64_t)sh.N * sh.T)
         return;
@@ -1632,6 +1639,25 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
 // with runs), since there is then no later block to keep in the same pages.
 constexpr int64_t XCD_RUN_MIN_BLOCKS = 8192;
 
+// Fixed XCD runs for the shuffle, the combine pack and the direct combine
+// push (RUN_ROWS_BLOCKS: 128 blocks move about 1 MiB of destination rows) and
+// for the combine reduce (RUN_TOKEN_BLOCKS), measured per kernel on
+// DeepSeek-R1 decode, Kimi-K2 Zipf decode and the fp8 prefill against runs of
+// 1 to 512 blocks: shuffle 149 -> 144, 310 -> 292, 2578 -> 2430 us; combine
+// pack 147 -> 146, 302 -> 297, 4993 -> 4769 us; combine push 156 -> 150,
+// 308 -> 304, 5036 -> 4750 us; combine reduce flat on the decode shapes,
+// 2923 -> 2836 us on the prefill; runs of 256 and more lost up to 10% on the
+// decode shapes.  The pack and partial-send kernels gained nothing from runs
+// (partial send lost 3-6%); the partial transfer and reduce gained on the
+// prefill and lost on the all-to-rank-0 decode, and keep plain order.
+constexpr uint32_t RUN_ROWS_BLOCKS = 128;
+constexpr uint32_t RUN_TOKEN_BLOCKS = 32;
+
+inline uint32_t fixed_run(int64_t blocks, uint32_t run)
+{
+    return blocks < XCD_RUN_MIN_BLOCKS ? 1u : run;
+}
+
 inline uint32_t segment_blocks(const Shape& sh, const RowShape& rsh)
 {
     if ((int64_t)row_blocks(sh.rows, rsh.split) < XCD_RUN_MIN_BLOCKS)
@@ -1656,9 +1682,10 @@ hipError_t launch_shuffle(const Shape& sh, const Plan& p, const Rows& r, void* e
                           float* expert_scale, int32_t* expert_offsets, const Launch& L)
 {
     // launched even with no rows: block 0 publishes the expert offsets
-    MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), shuffle_kernel, sh.rows, L, sh, p,
-                     (const v4u*)r.recv_x, r.recv_scale, r.recv_meta, (v4u*)expert_x,
-                     expert_scale, r.src_rank, r.src_slot, expert_offsets);
+    const RowShape rsh = row_shape(sh.payload_vecs);
+    MOE_DISPATCH_ROW(rsh, shuffle_kernel, sh.rows, L, sh, p, (const v4u*)r.recv_x, r.recv_scale,
+                     r.recv_meta, (v4u*)expert_x, expert_scale, r.src_rank, r.src_slot,
+                     expert_offsets, fixed_run(row_blocks(sh.rows, rsh.split), RUN_ROWS_BLOCKS));
     return hipGetLastError();
 }
 
@@ -1667,8 +1694,10 @@ hipError_t launch_combine_pack(const Shape& sh, const Plan& p, const Rows& r, co
 {
     if (sh.rows == 0)
         return hipSuccess;
-    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), combine_pack_kernel, sh.rows, L, sh, p,
-                     (const v4u*)y, (v4u*)r.comb_send);
+    const RowShape rsh = row_shape(sh.comb_vecs);
+    MOE_DISPATCH_ROW(rsh, combine_pack_kernel, sh.rows, L, sh, p, (const v4u*)y,
+                     (v4u*)r.comb_send,
+                     fixed_run(row_blocks(sh.rows, rsh.split), RUN_ROWS_BLOCKS));
     return hipGetLastError();
 }
 
@@ -1687,8 +1716,10 @@ hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r, co
 {
     if (sh.rows == 0)
         return hipSuccess;
-    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), combine_push_kernel, sh.rows, L, sh, p,
-                     (const v4u*)y, (v4u*)r.comb_recv);
+    const RowShape rsh = row_shape(sh.comb_vecs);
+    MOE_DISPATCH_ROW(rsh, combine_push_kernel, sh.rows, L, sh, p, (const v4u*)y,
+                     (v4u*)r.comb_recv,
+                     fixed_run(row_blocks(sh.rows, rsh.split), RUN_ROWS_BLOCKS));
     return hipGetLastError();
 }
 
@@ -1731,8 +1762,10 @@ hipError_t launch_combine_reduce(const Shape& sh, const Plan& p, const Rows& r, 
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
         return hipSuccess;
+    const uint32_t run =
+        fixed_run(row_blocks(tokens, row_shape(sh.comb_vecs).split), RUN_TOKEN_BLOCKS);
     MOE_DISPATCH_TOKEN(sh, combine_reduce_kernel, 2, tokens, L, sh, p, (const v4u*)r.comb_recv, w,
-                       (v4u*)out);
+                       (v4u*)out, run);
     return hipGetLastError();
 }
 
