@@ -304,7 +304,7 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
                      (rc = alloc(g, &p.qbase, (size_t)N + 1)) ||
                      (rc = alloc(g, &p.pbase, (size_t)N + 1)) ||
                      (rc = alloc(g, &g->recv_w, RQ)) ||
-                     (rc = alloc(g, &p.phead, R)) || (rc = alloc(g, &p.pitem, R)) ||
+                     (rc = alloc(g, &p.phead, 2 * R)) || (rc = alloc(g, &p.pitem, R)) ||
                      (staged && ((rc = alloc(g, &p.pmap, R)) || (rc = alloc(g, &g->send_w, R))))))) {
         free_all(g);
         delete g;

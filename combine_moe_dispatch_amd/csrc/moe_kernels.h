@@ -58,9 +58,11 @@ struct Plan {              // device pointers owned by the group
     int32_t* qbase;        // [N+1]      first owner-layout row of rank d (qbase[N] = P)
     int32_t* pbase;        // [N+1]      first token-layout row of sender s (pbase[N] = P)
     int32_t* pmap;         // [rows]     token-layout row -> owner-layout row (staged)
-    int4* phead;           // [rows]     partial row the expert side writes (owner layout when
-                           //            staged, token layout when direct) -> (token, 0, mask
-                           //            of the token's items on that rank: low, high word)
+    int4* phead;           // [rows][2]  partial row the expert side writes (owner layout when
+                           //            staged, token layout when direct) -> (expert row,
+                           //            receive-plane row of its first item, the same of its
+                           //            second), (token, item count, mask of the token's
+                           //            items on that rank: low word, high word)
     int2* pitem;           // [N][T][K]  item (s,t,k) -> (its expert row, its receive-plane row)
     int32_t* slot_of;      // [rows]     packed receive row -> its slot (fixed-slot layout)
 };

@@ -671,10 +671,11 @@ __device__ inline void record_maps(const Shape& sh, const Plan& p, const RowDest
 // token (all lanes call it; lane k < K holds item k's expert rank d, or -1
 // if its indices failed, and its receive-plane and expert rows).  Each item
 // gets its (expert row, receive-plane row); each head item (the first of its
-// rank in the token) gets the token and the mask of the token's items on its
-// rank, at the partial row it heads in the layout the expert side writes
-// (owner layout when staged, token layout when direct), and, staged, the
-// owner row of its token-layout row for the transfer back.
+// rank in the token) writes the record of the partial row it heads, in the
+// layout the expert side writes (owner layout when staged, token layout when
+// direct): the (expert row, receive-plane row) of its first two items, the
+// token, the item count and the mask of the token's items on its rank; and,
+// staged, the owner row of its token-layout row for the transfer back.
 __device__ inline void record_partial(const Shape& sh, const Plan& p, int64_t tok, int s, int d,
                                       const RowDest& rd)
 {
@@ -690,6 +691,9 @@ __device__ inline void record_partial(const Shape& sh, const Plan& p, int64_t to
     for (uint64_t hm = heads; hm != 0; hm &= hm - 1) {
         const int f = __builtin_ctzll(hm);
         const uint64_t mask = __ballot(d >= 0 && d == readlane(d, f));
+        const uint64_t rest = mask & (mask - 1);
+        const int f1 = rest ? __builtin_ctzll(rest) : f;
+        const int r1 = readlane(rd.r, f1), q1 = readlane(rd.qd, f1);
         if (lane == f) {
             const int P = p.pbase[N];
             const int tr = p.pbase[s] + pp;
@@ -698,8 +702,10 @@ __device__ inline void record_partial(const Shape& sh, const Plan& p, int64_t to
             if ((unsigned)tr >= (unsigned)P || (unsigned)orow >= (unsigned)P) {
                 atomicOr(p.err, ERR_BIT_INTERNAL);
             } else {
-                p.phead[sh.direct ? tr : orow] =
-                    make_int4((int)tok, 0, (int)(uint32_t)mask, (int)(uint32_t)(mask >> 32));
+                int4* rec = p.phead + 2 * (int64_t)(sh.direct ? tr : orow);
+                rec[0] = make_int4(rd.r, rd.qd, r1, q1);
+                rec[1] = make_int4((int)tok, __popcll(mask), (int)(uint32_t)mask,
+                                   (int)(uint32_t)(mask >> 32));
                 if (!sh.direct)
                     p.pmap[tr] = orow;
             }
@@ -1260,15 +1266,17 @@ constexpr int PARTIAL_TERMS = 2;
 // writes (owner layout (rank, sender, token) when staged, token layout
 // (sender, rank, token) when direct): a gather like the movers, so each wave
 // stores one row part and reads only the expert rows of its own terms.  The
-// row's record (written by pack) names its token and the mask of the token's
-// items held by this rank; lane k of the mask holds item k's expert row and
-// router weight, and the partial is the fp32 fma chain over the items in k
-// order from +0, rounded once to bf16.  Two dependent index loads (record,
-// then items) precede the row loads.  Iterating the owner layout in direct
-// mode too (so consecutive rows read one rank's expert rows) and scattering
-// the stores to the token layout was slower: DeepSeek-R1 decode 167 -> 167
-// us, Kimi-K2 Zipf 269 -> 293, all-to-rank-0 221 -> 258.  The grid covers the
-// largest possible P; rows past the cycle's P exit.
+// partial is the fp32 fma chain over the token's items held by this rank, in
+// k order from +0, rounded once to bf16.  The row's record (written by pack)
+// holds the expert and receive-plane rows of its first two items, so a
+// partial of one or two items (most of them: a token seldom sends more than
+// two of its K items to one rank) needs no index load beyond the record; a
+// larger one reads its items' rows from the item table (lane k of the mask
+// holds item k's).  Iterating the owner layout in direct mode too (so
+// consecutive rows read one rank's expert rows) and scattering the stores to
+// the token layout was slower: DeepSeek-R1 decode 167 -> 167 us, Kimi-K2 Zipf
+// 269 -> 293, all-to-rank-0 221 -> 258.  The grid covers the largest possible
+// P; rows past the cycle's P exit.
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void partial_send_kernel(Shape sh, Plan p,
                                                                     const v4u* __restrict__ y,
@@ -1285,16 +1293,22 @@ __global__ __launch_bounds__(COPY_THREADS) void partial_send_kernel(Shape sh, Pl
         return;
     const int err = *p.err;
     const int P = p.pbase[sh.N];
-    int4 h = p.phead[j];
+    int4 a = p.phead[2 * j];
+    int4 h = p.phead[2 * j + 1];
+    asm volatile("" : "+v"(a.x), "+v"(a.y), "+v"(a.z), "+v"(a.w));
     asm volatile("" : "+v"(h.x), "+v"(h.y), "+v"(h.z), "+v"(h.w));
     if (err != 0 || j >= P)
         return;
     const int K = sh.K;
     const uint64_t mask = (uint64_t)(uint32_t)h.z | ((uint64_t)(uint32_t)h.w << 32);
     const uint64_t kmask = K >= 64 ? ~0ull : (1ull << K) - 1;
+    const int m = h.y;
+    bool bad = (uint64_t)h.x >= (uint64_t)sh.N * sh.T || mask == 0 || (mask & ~kmask) != 0 ||
+               m != __popcll(mask) ||
+               (uint64_t)a.x >= (uint64_t)sh.rows || (uint64_t)a.y >= (uint64_t)sh.recv_rows ||
+               (uint64_t)a.z >= (uint64_t)sh.rows || (uint64_t)a.w >= (uint64_t)sh.recv_rows;
     int my_row = 0, my_q = 0;
-    bool bad = (uint64_t)h.x >= (uint64_t)sh.N * sh.T || mask == 0 || (mask & ~kmask) != 0;
-    if (!bad && lane < K && ((mask >> lane) & 1)) {
+    if (m > 2 && !bad && lane < K && ((mask >> lane) & 1)) {
         const int2 it = p.pitem[(int64_t)h.x * K + lane];
         bad = (uint64_t)it.x >= (uint64_t)sh.rows || (uint64_t)it.y >= (uint64_t)sh.recv_rows;
         my_row = it.x;
@@ -1305,11 +1319,57 @@ __global__ __launch_bounds__(COPY_THREADS) void partial_send_kernel(Shape sh, Pl
             atomicOr(p.err, ERR_BIT_INTERNAL);
         return;
     }
-    const float my_w = recv_w[my_q];
     const int n = rs.len;
     const int stride = sh.comb_vecs;
     const v4u* src = y + rs.b0;
     v4u* o = dst + j * stride + rs.b0;
+    if (m <= 2) {
+        // the record's values are the same on every lane
+        const int r0 = __builtin_amdgcn_readfirstlane(a.x);
+        const int r1 = __builtin_amdgcn_readfirstlane(a.z);
+        const int q0 = __builtin_amdgcn_readfirstlane(a.y);
+        const int q1 = __builtin_amdgcn_readfirstlane(a.w);
+        const v4u* row0 = src + (int64_t)r0 * stride;
+        const v4u* row1 = src + (int64_t)r1 * stride;
+        for (int base = 0; base < n; base += WAVE * U) {
+            v4u v0[U], v1[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int jj = min(base + u * WAVE + lane, n - 1);
+                v0[u] = ld_nt(row0 + jj);
+                if (m == 2)
+                    v1[u] = ld_nt(row1 + jj);
+            }
+            // the weights are loaded once the row loads are issued, before
+            // the rows are waited for
+            const float w0 = recv_w[q0];
+            const float w1 = m == 2 ? recv_w[q1] : 0.0f;
+            hold(v0);
+            if (m == 2)
+                hold(v1);
+            float acc[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[u][e] = 0.0f;
+                fma_row8(acc[u], w0, v0[u]);
+            }
+            if (m == 2) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    fma_row8(acc[u], w1, v1[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int jj = base + u * WAVE + lane;
+                if (jj < n)
+                    st_nt(pack_bf16x8(acc[u]), o + jj);
+            }
+        }
+        return;
+    }
+    const float my_w = recv_w[my_q];
     for (int base = 0; base < n; base += WAVE * U) {
         float acc[U][8];
 #pragma unroll
