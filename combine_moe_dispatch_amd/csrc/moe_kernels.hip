@@ -1676,8 +1676,9 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
     if (sh.fp8) {
         // a row is H/16 groups of 16 elements (16 codes out per lane); each
         // lane holds two input vectors per group, so at most 4 groups per
-        // lane per round (4 groups on 2 waves per DeepSeek-shaped row
-        // measured 1.6% faster than 2 groups on 4 waves)
+        // lane per round.  A DeepSeek-shaped row takes 4 waves of 112 groups;
+        // 2 or 8 waves, or 4 groups per lane, were equal or up to 6% slower
+        // on the fp8 prefill
         RowShape rsh = row_shape(sh.H / 16);
         if (rsh.u > 4)
             rsh.u = 4;
