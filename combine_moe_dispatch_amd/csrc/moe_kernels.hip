@@ -687,6 +687,20 @@ __device__ inline void record_partial(const Shape& sh, const Plan& p, int64_t to
         p.pitem[i] = make_int2(rd.r, rd.qd);
         pp = p.ppos[i];
     }
+    // every head lane finds its partial rows at once
+    int tr = 0, orow = 0;
+    bool ok = false;
+    if (pp >= 0) {
+        const int P = p.pbase[N];
+        tr = p.pbase[s] + pp;
+        orow = p.qbase[d] + p.qoff[(size_t)d * (N + 1) + s] + pp - p.psoff[(size_t)s * (N + 1) + d];
+        ok = (unsigned)tr < (unsigned)P && (unsigned)orow < (unsigned)P;
+        if (!ok)
+            atomicOr(p.err, ERR_BIT_INTERNAL);
+    }
+    // then the masks and second items, head by head (no memory access)
+    uint64_t my_mask = 0;
+    int my_r1 = 0, my_q1 = 0;
     const uint64_t heads = __ballot(pp >= 0);
     for (uint64_t hm = heads; hm != 0; hm &= hm - 1) {
         const int f = __builtin_ctzll(hm);
@@ -695,21 +709,18 @@ __device__ inline void record_partial(const Shape& sh, const Plan& p, int64_t to
         const int f1 = rest ? __builtin_ctzll(rest) : f;
         const int r1 = readlane(rd.r, f1), q1 = readlane(rd.qd, f1);
         if (lane == f) {
-            const int P = p.pbase[N];
-            const int tr = p.pbase[s] + pp;
-            const int orow = p.qbase[d] + p.qoff[(size_t)d * (N + 1) + s] + pp -
-                             p.psoff[(size_t)s * (N + 1) + d];
-            if ((unsigned)tr >= (unsigned)P || (unsigned)orow >= (unsigned)P) {
-                atomicOr(p.err, ERR_BIT_INTERNAL);
-            } else {
-                int4* rec = p.phead + 2 * (int64_t)(sh.direct ? tr : orow);
-                rec[0] = make_int4(rd.r, rd.qd, r1, q1);
-                rec[1] = make_int4((int)tok, __popcll(mask), (int)(uint32_t)mask,
-                                   (int)(uint32_t)(mask >> 32));
-                if (!sh.direct)
-                    p.pmap[tr] = orow;
-            }
+            my_mask = mask;
+            my_r1 = r1;
+            my_q1 = q1;
         }
+    }
+    if (ok) {
+        int4* rec = p.phead + 2 * (int64_t)(sh.direct ? tr : orow);
+        rec[0] = make_int4(rd.r, rd.qd, my_r1, my_q1);
+        rec[1] = make_int4((int)tok, __popcll(my_mask), (int)(uint32_t)my_mask,
+                           (int)(uint32_t)(my_mask >> 32));
+        if (!sh.direct)
+            p.pmap[tr] = orow;
     }
 }
 
