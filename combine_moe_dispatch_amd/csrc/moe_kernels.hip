@@ -1795,7 +1795,7 @@ hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r, co
     return hipGetLastError();
 }
 
-// Token kernels (one wave group per token, all K expert rows in flight) are
+// Token kernels (one wave group per token, all K rows in flight) are
 // compiled for the common K (1, 2, 4, 6, 8) and for any other K, with UK
 // vectors per lane per row; rows are split across waves as for the movers.
 #define MOE_TOKEN_SPLIT(KERNEL, KT, U, split, grid, block, L, ...)                                  \
@@ -1810,10 +1810,11 @@ hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r, co
             go((KERNEL<KT, U, 8>), grid, block, 0, L, __VA_ARGS__);                                \
     } while (0)
 
-// The token kernels hold all K rows' vectors of a token at once: with the
-// movers' split and 2 vectors per lane per row, K = 8 rows take 64 VGPRs
-// (4 waves per SIMD); at 4 vectors per lane over 4 waves they took 160-180
-// VGPRs and ran at 2 (partial send 172 -> 165 us on DeepSeek-R1 decode).
+// The token kernels (combine reduce, partial reduce) hold all K rows' vectors
+// of a token at once: with the movers' split and 2 vectors per lane per row,
+// K = 8 rows take 64 VGPRs of data (94 in all, 5 waves per SIMD); at 4
+// vectors per lane over 4 waves such kernels took 160-180 VGPRs and ran at 2
+// (an earlier per-token partial send: 172 -> 165 us on DeepSeek-R1 decode).
 #define MOE_DISPATCH_TOKEN(sh, KERNEL, UK, tokens, L, ...)                                         \
     do {                                                                                           \
         const int split_ = row_shape((sh).comb_vecs).split;                                        \
