@@ -841,13 +841,15 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
                                                                 v4u* __restrict__ dst_q,
                                                                 float* __restrict__ dst_scale,
                                                                 int32_t* __restrict__ dst_meta,
-                                                                float* __restrict__ dst_w)
+                                                                float* __restrict__ dst_w,
+                                                                uint32_t xrun)
 {
     if (*p.err)
         return;
     const int lane = lane_id();
     const int n2 = sh.H / 16;                  // 16-element groups per row (= 16-byte code vectors)
-    const RowSlot rs = row_slot<SPLIT, 8>(n2); // parts hold whole 128-element blocks
+    // parts hold whole 128-element blocks
+    const RowSlot rs = row_slot<SPLIT, 8>(n2, xcd_run_block(xrun));
     const int64_t tok = rs.row;
     if (tok >= (int64_t)sh.N * sh.T)
         return;
@@ -859,13 +861,16 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
     for (int base = rs.b0; base < end; base += WAVE * U) {
         // clamped loads (see copy_row); an 8-lane group lies wholly inside or
         // wholly past the part's end because the part bounds and base are
-        // multiples of 8
+        // multiples of 8.  Ordinary loads, as in the bf16 pack: the
+        // nontemporal hint cost 2.5% on the fp8 prefill (each lane's two
+        // vectors are interleaved with its neighbours', so each 16-byte load
+        // touches lines that its partner load reads again)
         v4u va[U], vb[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = min(base + u * WAVE + lane, end - 1);
-            va[u] = ld_nt(src + 2 * j);
-            vb[u] = ld_nt(src + 2 * j + 1);
+            va[u] = src[2 * j];
+            vb[u] = src[2 * j + 1];
         }
         hold(va);
         hold(vb);
@@ -1677,6 +1682,33 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     return hipGetLastError();
 }
 
+// Grids below this many blocks keep round-robin placement: they are resident
+// at once, so there is no later block to keep in the same pages (Mixtral
+// decode, 2048 blocks: 61.2 -> 63.0 us with runs in the transfers).
+constexpr int64_t XCD_RUN_MIN_BLOCKS = 8192;
+
+// Fixed XCD runs for the shuffle, the combine pack and the direct combine
+// push (RUN_ROWS_BLOCKS: 128 blocks move about 1 MiB of destination rows) and
+// for the combine reduce (RUN_TOKEN_BLOCKS), measured per kernel on
+// DeepSeek-R1 decode, Kimi-K2 Zipf decode and the fp8 prefill against runs of
+// 1 to 512 blocks: shuffle 149 -> 144, 310 -> 292, 2578 -> 2430 us; combine
+// pack 147 -> 146, 302 -> 297, 4993 -> 4769 us; combine push 156 -> 150,
+// 308 -> 304, 5036 -> 4750 us; combine reduce flat on the decode shapes,
+// 2923 -> 2836 us on the prefill; runs of 256 and more lost up to 10% on the
+// decode shapes.  The bf16 pack and partial send gained nothing from runs
+// (partial send lost 3-6%); the partial transfer and reduce gained on the
+// prefill and lost on the all-to-rank-0 decode, and keep plain order.
+constexpr uint32_t RUN_ROWS_BLOCKS = 128;
+constexpr uint32_t RUN_TOKEN_BLOCKS = 32;
+// The fp8 pack: runs of 256 blocks (256 tokens of one sender per run) on the
+// prefill 1859-1868 -> 1821-1823 us; 64 and 1024 gained less.
+constexpr uint32_t RUN_FP8_PACK_BLOCKS = 256;
+
+inline uint32_t fixed_run(int64_t blocks, uint32_t run)
+{
+    return blocks < XCD_RUN_MIN_BLOCKS ? 1u : run;
+}
+
 hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const float* w,
                        const Plan& p, const Rows& r, const Launch& L)
 {
@@ -1696,7 +1728,8 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
         MOE_DISPATCH_ROW(rsh, pack_fp8_kernel, tokens, L, sh, p, (const v4u*)x, idx, w,
                          (v4u*)(sh.direct ? r.recv_x : r.send_x),
                          sh.direct ? r.recv_scale : r.send_scale,
-                         sh.direct ? r.recv_meta : r.send_meta, dst_w);
+                         sh.direct ? r.recv_meta : r.send_meta, dst_w,
+                         fixed_run(row_blocks(tokens, rsh.split), RUN_FP8_PACK_BLOCKS));
     } else {
         MOE_DISPATCH_ROW(row_shape(sh.payload_vecs), pack_bf16_kernel, tokens, L, sh, p,
                          (const v4u*)x, idx, w, (v4u*)(sh.direct ? r.recv_x : r.send_x),
@@ -1705,31 +1738,8 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
     return hipGetLastError();
 }
 
-// Blocks of an average (sender -> receiver) segment, R / N^2 rows, for the
-// transfers' XCD runs; 1 (round-robin placement kept) when the grid is small
-// enough to be resident at once (Mixtral decode, 2048 blocks: 61.2 -> 63.0 us
-// with runs), since there is then no later block to keep in the same pages.
-constexpr int64_t XCD_RUN_MIN_BLOCKS = 8192;
-
-// Fixed XCD runs for the shuffle, the combine pack and the direct combine
-// push (RUN_ROWS_BLOCKS: 128 blocks move about 1 MiB of destination rows) and
-// for the combine reduce (RUN_TOKEN_BLOCKS), measured per kernel on
-// DeepSeek-R1 decode, Kimi-K2 Zipf decode and the fp8 prefill against runs of
-// 1 to 512 blocks: shuffle 149 -> 144, 310 -> 292, 2578 -> 2430 us; combine
-// pack 147 -> 146, 302 -> 297, 4993 -> 4769 us; combine push 156 -> 150,
-// 308 -> 304, 5036 -> 4750 us; combine reduce flat on the decode shapes,
-// 2923 -> 2836 us on the prefill; runs of 256 and more lost up to 10% on the
-// decode shapes.  The pack and partial-send kernels gained nothing from runs
-// (partial send lost 3-6%); the partial transfer and reduce gained on the
-// prefill and lost on the all-to-rank-0 decode, and keep plain order.
-constexpr uint32_t RUN_ROWS_BLOCKS = 128;
-constexpr uint32_t RUN_TOKEN_BLOCKS = 32;
-
-inline uint32_t fixed_run(int64_t blocks, uint32_t run)
-{
-    return blocks < XCD_RUN_MIN_BLOCKS ? 1u : run;
-}
-
+// Blocks of an average (sender -> receiver) segment, R / N^2 rows: the
+// transfers' XCD runs.
 inline uint32_t segment_blocks(const Shape& sh, const RowShape& rsh)
 {
     if ((int64_t)row_blocks(sh.rows, rsh.split) < XCD_RUN_MIN_BLOCKS)
