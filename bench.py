@@ -493,8 +493,9 @@ def cpu_baseline(cfg, inp, min_seconds: float, combine: str = "receiver") -> dic
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the timing protocol: 20 warmup steps, 200 timed (20 on the prefill shape)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="C")
     ap.add_argument("--tokens", type=int, default=None,
                     help="tokens per rank (default: the workload's own)")
@@ -523,6 +524,8 @@ def main() -> int:
     ap.add_argument("--trace-summary", metavar="DB",
                     help="print a table of the library's kernels from a rocprofv3 kernel trace")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 20 if args.config == "D" else 200
     if args.copy_calibration:
         return copy_calibration()
     if args.overlap:
