@@ -34,8 +34,12 @@ MODES = [
     (mep.MOE_TRANSPORT_STAGED, mep.MOE_COMBINE_PARTIAL, mep.MOE_LAYOUT_PACKED),
     (mep.MOE_TRANSPORT_DIRECT, mep.MOE_COMBINE_PARTIAL, mep.MOE_LAYOUT_FIXED_SLOT),
     (mep.MOE_TRANSPORT_STAGED, mep.MOE_COMBINE_RECEIVER, mep.MOE_LAYOUT_FIXED_SLOT),
+    (mep.MOE_TRANSPORT_DIRECT, mep.MOE_COMBINE_PARTIAL, mep.MOE_LAYOUT_PACKED),
+    (mep.MOE_TRANSPORT_DIRECT, mep.MOE_COMBINE_RECEIVER, mep.MOE_LAYOUT_FIXED_SLOT),
+    (mep.MOE_TRANSPORT_STAGED, mep.MOE_COMBINE_PARTIAL, mep.MOE_LAYOUT_FIXED_SLOT),
 ]
-MODE_IDS = ["staged", "direct", "staged-partial", "direct-partial-fixed", "staged-fixed"]
+MODE_IDS = ["staged", "direct", "staged-partial", "direct-partial-fixed", "staged-fixed",
+            "direct-partial", "direct-fixed", "staged-partial-fixed"]
 
 
 def _cases(K):
