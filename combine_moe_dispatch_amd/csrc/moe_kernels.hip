@@ -1411,13 +1411,14 @@ __global__ __launch_bounds__(COPY_THREADS) void partial_send_kernel(Shape sh, Pl
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void partial_transfer_kernel(Shape sh, Plan p,
                                                                         const v4u* __restrict__ psend,
-                                                                        v4u* __restrict__ precv)
+                                                                        v4u* __restrict__ precv,
+                                                                        uint32_t xrun)
 {
     if (*p.err)
         return;
     const int lane = lane_id();
     const int n = sh.comb_vecs;
-    const RowSlot rs = row_slot<SPLIT>(n);
+    const RowSlot rs = row_slot<SPLIT>(n, xcd_run_block(xrun));
     const int64_t j = rs.row;
     const int P = p.pbase[sh.N];
     if (j >= P)
@@ -1696,13 +1697,15 @@ constexpr int64_t XCD_RUN_MIN_BLOCKS = 8192;
 // 308 -> 304, 5036 -> 4750 us; combine reduce flat on the decode shapes,
 // 2923 -> 2836 us on the prefill; runs of 256 and more lost up to 10% on the
 // decode shapes.  The bf16 pack and partial send gained nothing from runs
-// (partial send lost 3-6%); the partial transfer and reduce gained on the
-// prefill and lost on the all-to-rank-0 decode, and keep plain order.
+// (partial send lost 3-6%); the partial reduce gained on the prefill and lost
+// on the all-to-rank-0 decode, and keeps plain order; the partial transfer
+// takes segment runs where segments are long (launch_partial_transfer).
 constexpr uint32_t RUN_ROWS_BLOCKS = 128;
 constexpr uint32_t RUN_TOKEN_BLOCKS = 32;
 // The fp8 pack: runs of 256 blocks (256 tokens of one sender per run) on the
 // prefill 1859-1868 -> 1821-1823 us; 64 and 1024 gained less.
 constexpr uint32_t RUN_FP8_PACK_BLOCKS = 256;
+constexpr int64_t PARTIAL_RUN_MIN_BLOCKS = 64;
 
 inline uint32_t fixed_run(int64_t blocks, uint32_t run)
 {
@@ -1882,8 +1885,20 @@ hipError_t launch_partial_transfer(const Shape& sh, const Plan& p, const Rows& r
     const int64_t p_max = (int64_t)sh.N * sh.T * (sh.K < sh.N ? sh.K : sh.N);
     if (p_max == 0)
         return hipSuccess;
-    MOE_DISPATCH_ROW(row_shape(sh.comb_vecs), partial_transfer_kernel, p_max, L, sh, p,
-                     (const v4u*)r.comb_send, (v4u*)r.comb_recv);
+    // XCD runs of one (rank -> token owner) segment of the largest P, only
+    // where a segment spans PARTIAL_RUN_MIN_BLOCKS blocks: runs of 64 blocks
+    // on DeepSeek-R1 decode 139 -> 134 us, of 512 on the fp8 prefill
+    // 5033 -> 4642 us; on the Kimi-K2 decode shapes (32-block segments, the
+    // partial rows piled on few ranks) runs of 32 lost 2-6%
+    const RowShape rsh = row_shape(sh.comb_vecs);
+    const int64_t seg_rows = std::max<int64_t>(1, p_max / ((int64_t)sh.N * sh.N));
+    const int64_t seg = (seg_rows * rsh.split + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    const uint32_t run = seg >= PARTIAL_RUN_MIN_BLOCKS
+                             ? fixed_run(row_blocks(p_max, rsh.split),
+                                         (uint32_t)std::min<int64_t>(seg, (int64_t)1 << 24))
+                             : 1u;
+    MOE_DISPATCH_ROW(rsh, partial_transfer_kernel, p_max, L, sh, p, (const v4u*)r.comb_send,
+                     (v4u*)r.comb_recv, run);
     return hipGetLastError();
 }
 
