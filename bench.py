@@ -85,9 +85,11 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
             kb["transfer"] += 2 * R * 4
         for k in ("combine_pack", "transfer_back", "combine_push", "combine_reduce"):
             kb.pop(k, None)
-        # expert rows in (+ per item: its expert/receive row pair and weight;
-        # per partial row: its 16-byte record), partial rows out
-        kb["partial_send"] = R * hy + R * 12 + P * 16 + P * hy
+        # expert rows in (+ per item its weight; per partial row its 32-byte
+        # record, which names the rows of its first two items: the item-table
+        # reads of larger partials are not counted, like the row maps),
+        # partial rows out
+        kb["partial_send"] = R * hy + R * 4 + P * 32 + P * hy
         if transport == "staged":
             kb["partial_transfer"] = 2 * P * hy
         kb["partial_reduce"] = P * hy + R * 8 + tokens * H * 2

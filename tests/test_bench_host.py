@@ -58,9 +58,9 @@ def test_partial_byte_model_moves_p_rows():
     kb = bench.kernel_bytes(cfg, "staged", "partial", P)
     hy = 2 * cfg.H
     assert kb["partial_transfer"] == 2 * P * hy
-    # every expert row read once with its row pair and weight (12 bytes), one
-    # 16-byte record per partial row
-    assert kb["partial_send"] - P * hy == cfg.rows * (hy + 12) + P * 16
+    # every expert row read once with its weight, one 32-byte record per
+    # partial row
+    assert kb["partial_send"] - P * hy == cfg.rows * (hy + 4) + P * 32
     assert kb["partial_reduce"] - P * hy == cfg.rows * 8 + cfg.N * cfg.T * cfg.H * 2
     assert "combine_reduce" not in kb and "transfer_back" not in kb
 
