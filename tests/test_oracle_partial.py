@@ -138,3 +138,32 @@ def test_single_token_form_reduces_to_receiver_combine_on_one_rank():
     w = g.random(5).astype(np.float32)
     got = oracle.partial_token(rows, w, np.full(5, 3, dtype=np.int32))
     assert np.array_equal(got, oracle.combine_token(rows, w))
+
+
+def test_hand_worked_partial_example():
+    """The partial-row layouts, partial rows and outputs of the hand-worked
+    2-rank example (tests/golden/tiny_hand_example.json, "partial"), derived
+    on paper from the definitions."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "tiny_hand_example.json")))
+    gp = g["partial"]
+    idx = np.array(g["idx"], dtype=np.int32)
+    N, T, K, E = g["N"], g["T"], g["K"], g["E"]
+    H = 4
+    pp = oracle.partial_plan(idx, E)
+    assert pp["pc"].tolist() == gp["pc"]
+    assert pp["P"] == gp["P"]
+    assert pp["token_row"].tolist() == gp["token_row"]
+    assert pp["owner_row"].tolist() == gp["owner_row"]
+    pl = oracle.plan(idx, E)
+    # expert row r holds r + 1 in every element (exact in bf16)
+    R = N * T * K
+    y = oracle.f32_to_bf16(np.repeat(np.arange(1, R + 1, dtype=np.float32)[:, None], H, axis=1))
+    w = np.array(gp["w"], dtype=np.float32)
+    res = oracle.run_partial_combine(y, w, idx, pl, H)
+    f = lambda a: f32_from_bf16_bits(a)[:, 0].tolist()  # noqa: E731
+    assert f(res["psend"]) == gp["owner_layout_values"]
+    assert f(res["precv"]) == gp["token_layout_values"]
+    assert f32_from_bf16_bits(res["out"])[:, :, 0].tolist() == gp["out"]
