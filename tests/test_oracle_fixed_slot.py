@@ -114,3 +114,16 @@ def test_slot_contents_carry_their_tokens():
                     assert meta[q] == t * K + k
                     filled[q] = True
     assert np.all(meta[~filled] == -1)
+
+
+def test_hand_worked_slot_rows():
+    """Slot rows of the hand-worked 2-rank example (tests/golden/
+    tiny_hand_example.json, "fixed_slot"), derived on paper."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "tiny_hand_example.json")))
+    idx = np.array(g["idx"], dtype=np.int32)
+    pl = oracle.plan(idx, g["E"])
+    slot = oracle.slot_rows(idx, pl, g["fixed_slot"]["T_max"])
+    assert slot.tolist() == g["fixed_slot"]["slot_row"]
