@@ -146,3 +146,21 @@ def test_quant_row_fp8_definition(seed):
         bound = (np.maximum(np.abs(blk) * 2.0 ** -4, 2.0 ** -10 * float(sc[b])) * (1 + 2.0 ** -16)
                  + 2.0 ** -21 * np.abs(blk))
         assert np.all(err <= bound), (b, err.max())
+
+
+def test_hand_worked_fp8_block():
+    """The block-scaled e4m3 row of the hand-worked example
+    (tests/golden/tiny_hand_example.json, "fp8_block"), derived on paper."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "tiny_hand_example.json")))["fp8_block"]
+    x = np.zeros(g["H"], dtype=np.uint16)
+    for i, v in g["x_nonzero_bf16"].items():
+        x[int(i)] = v
+    codes, scales = oracle.quant_row_fp8(x)
+    want = np.zeros(g["H"], dtype=np.uint8)
+    for i, v in g["codes_nonzero"].items():
+        want[int(i)] = v
+    assert codes.tolist() == want.tolist()
+    assert scales.view(np.uint32).tolist() == g["scale_bits"]
