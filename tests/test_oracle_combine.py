@@ -115,3 +115,22 @@ def test_ulp_distance_helper():
     a = np.array([0x3F80, 0x0000, 0x8000, 0x0001, 0x8001], dtype=np.uint16)
     b = np.array([0x3F81, 0x8000, 0x0001, 0x8001, 0x0001], dtype=np.uint16)
     assert _ulp_dist_bf16(a, b).tolist() == [1, 0, 1, 2, 2]
+
+
+def test_hand_worked_combine():
+    """The receiver-side combine of the hand-worked 2-rank example
+    (tests/golden/tiny_hand_example.json, "combine"), derived on paper."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "tiny_hand_example.json")))
+    idx = np.array(g["idx"], dtype=np.int32)
+    N, T, K, E = g["N"], g["T"], g["K"], g["E"]
+    H = 4
+    pl = oracle.plan(idx, E)
+    y = oracle.f32_to_bf16(np.repeat(np.arange(1, N * T * K + 1, dtype=np.float32)[:, None], H,
+                                     axis=1))
+    w = np.array(g["partial"]["w"], dtype=np.float32)
+    out = oracle.run_combine(y, w, pl, H)["out"]
+    got = (out.astype(np.uint32) << 16).view(np.float32)[:, :, 0]
+    assert got.tolist() == g["combine"]["out"]
