@@ -498,7 +498,8 @@ def main() -> int:
     # the timing protocol: 20 warmup steps, 200 timed (20 on the prefill shape)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="C")
+    ap.add_argument("--config", default="C",
+                    help="workload: key (A, B, C, D, E, Ep) or name (e.g. deepseek-r1-decode)")
     ap.add_argument("--tokens", type=int, default=None,
                     help="tokens per rank (default: the workload's own)")
     ap.add_argument("--transport", choices=["staged", "direct"], default="staged",
@@ -526,6 +527,15 @@ def main() -> int:
     ap.add_argument("--trace-summary", metavar="DB",
                     help="print a table of the library's kernels from a rocprofv3 kernel trace")
     args = ap.parse_args()
+    from workloads import CONFIGS as _configs
+    if args.config not in _configs:
+        # a workload may also be named by its name ("deepseek-r1-decode", ...)
+        by_name = {c.name: k for k, c in _configs.items()}
+        if args.config not in by_name:
+            print(f"unknown workload {args.config!r}; known: "
+                  + ", ".join(f"{k} ({c.name})" for k, c in _configs.items()), file=sys.stderr)
+            return 2
+        args.config = by_name[args.config]
     if args.steps is None:
         args.steps = 20 if args.config == "D" else 200
     if args.copy_calibration:

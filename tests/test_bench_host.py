@@ -146,3 +146,14 @@ def test_several_gpus_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_workload_named_or_unknown():
+    """--config takes a workload's key or its name; an unknown one is refused."""
+    bench_py = os.path.join(ROOT, "bench.py")
+    r = subprocess.run([sys.executable, bench_py, "--config", "deepseek-r1-decode", "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr       # the name resolved
+    r = subprocess.run([sys.executable, bench_py, "--config", "no-such-workload"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "unknown workload" in r.stderr and r.stdout == ""
