@@ -130,6 +130,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def traffic_key(args) -> str:
+    """Name of the counter summary of a workload and mode: the workload key,
+    then _direct, _partial and _fixed for the non-default choices (each mode
+    moves different rows, so each has its own summary)."""
+    return (args.config + ("" if args.transport == "staged" else "_direct")
+            + ("_partial" if args.combine == "partial" else "")
+            + ("_fixed" if getattr(args, "layout", "packed") == "fixed" else ""))
+
+
 def measured_traffic(config_key: str, kernel: str, src_hash: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
@@ -552,9 +561,7 @@ def main() -> int:
         if args.traffic_from:
             rec = traffic_from(cfg, *args.traffic_from, transport=args.transport,
                                combine=args.combine)
-            suffix = ("" if args.transport == "staged" else "_direct") + \
-                ("_partial" if args.combine == "partial" else "")
-            path = os.path.join(ROOT, "profiles", f"traffic_{args.config}{suffix}.json")
+            path = os.path.join(ROOT, "profiles", f"traffic_{traffic_key(args)}.json")
             with open(path, "w") as f:
                 json.dump(rec, f, indent=1)
             print(json.dumps(rec, indent=1))
@@ -691,8 +698,7 @@ def main() -> int:
     dom_us = dom_ms / dom_n * 1e3
     ach = kb[dom] / (dom_us * 1e-6) / 1e9
     src_hash = kernel_source_hash()
-    traffic = measured_traffic(args.config + ("" if args.transport == "staged" else "_direct")
-                               + ("_partial" if partial else ""), dom, src_hash)
+    traffic = measured_traffic(traffic_key(args), dom, src_hash)
     gbps_eff = total_bytes / (ms_per_step * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
