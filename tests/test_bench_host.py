@@ -157,3 +157,16 @@ def test_workload_named_or_unknown():
     r = subprocess.run([sys.executable, bench_py, "--config", "no-such-workload"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "unknown workload" in r.stderr and r.stdout == ""
+
+
+def test_traffic_summary_names():
+    """Each workload and mode has its own counter summary; the fixed-slot
+    layout does not read the packed layout's."""
+    import argparse
+    key = lambda **kw: bench.traffic_key(argparse.Namespace(**kw))  # noqa: E731
+    assert key(config="C", transport="staged", combine="receiver", layout="packed") == "C"
+    assert key(config="C", transport="direct", combine="partial", layout="packed") == \
+        "C_direct_partial"
+    assert key(config="D", transport="staged", combine="receiver", layout="fixed") == "D_fixed"
+    h = bench.kernel_source_hash()
+    assert bench.measured_traffic("C_fixed", "transfer", h) is None
