@@ -242,12 +242,21 @@ void orc_pack_bf16(int N, int T, int K, int H, const uint16_t* x, const int32_t*
 
 /* Block-scaled fp8 quantisation of one token row ([EFA] "Dispatch/combine
  * latency": block-scaled fp8 dispatch; [EPMC] "Dispatch": block scaling
- * factors travel with the tokens).  For each block b of 128 elements:
- * amax = max |x|; if amax > 0, inv = 448 / amax and scale = amax / 448 (each
- * one fp32 division), else inv = 0 and scale = 1; code = e4m3(x * inv) with
- * one fp32 multiply.  Dequantised value = e4m3 value * scale. */
+ * factors travel with the tokens).  For each block b of 128 elements, with
+ * amax = max |x| and m = the smallest normal fp32 number, 2^-126:
+ *   amax >= 448*m:    inv = 448 / amax and scale = amax / 448 (each one fp32
+ *                     division; scale >= m, a normal number);
+ *   0 < amax < 448*m: scale = m and inv = 1/m = 2^126 (the scale is kept
+ *                     normal: amax / 448 would be an fp32 subnormal with few
+ *                     significant bits, and 448 / amax can overflow to
+ *                     infinity);
+ *   amax == 0:        inv = 0 and scale = 1.
+ * code = e4m3(x * inv) with one fp32 multiply.  Dequantised value = e4m3
+ * value * scale.  Every finite input gives a finite code and a finite,
+ * normal scale. */
 void orc_quant_row_fp8(int H, const uint16_t* xrow, uint8_t* q, float* scale)
 {
+    const float m = ldexpf(1.0f, -126);
     for (int b = 0; b < H / 128; ++b) {
         float amax = 0.0f;
         for (int i = 0; i < 128; ++i) {
@@ -256,9 +265,12 @@ void orc_quant_row_fp8(int H, const uint16_t* xrow, uint8_t* q, float* scale)
                 amax = v;
         }
         float inv, sc;
-        if (amax > 0.0f) {
+        if (amax >= 448.0f * m) {
             inv = 448.0f / amax;
             sc = amax / 448.0f;
+        } else if (amax > 0.0f) {
+            inv = 1.0f / m;
+            sc = m;
         } else {
             inv = 0.0f;
             sc = 1.0f;

@@ -164,3 +164,43 @@ def test_hand_worked_fp8_block():
         want[int(i)] = v
     assert codes.tolist() == want.tolist()
     assert scales.view(np.uint32).tolist() == g["scale_bits"]
+
+
+def test_quant_row_fp8_total_over_every_bf16_exponent():
+    """Blocks whose largest magnitude walks every bf16 exponent, subnormal
+    bf16 values included, with and without +-0 elements: no NaN code, a
+    finite normal scale, codes equal to torch's e4m3 rounding of x * inv
+    under the block rule (the scale held at 2^-126 below amax = 448 * 2^-126),
+    and the dequantisation bound (tests/fp8_checks.py, which uses no oracle
+    code)."""
+    from tests.fp8_checks import CLAMP_BELOW, check_blocks
+    from workloads import f32_from_bf16_bits, fp8_exponent_sweep
+    blocks = fp8_exponent_sweep()
+    q, sc = oracle.quant_row_fp8(blocks.reshape(-1))
+    check_blocks(blocks, q.reshape(-1, 128), sc, "oracle")
+    amax = np.abs(f32_from_bf16_bits(blocks)).max(axis=1)
+    # both regimes are reached, the clamped one from many exponents
+    assert (amax < CLAMP_BELOW).sum() >= 2 * 3 * 10 and (amax >= CLAMP_BELOW).sum() > 1000
+
+
+def test_quant_row_fp8_small_amax_regime_by_hand():
+    """Blocks below amax = 448 * 2^-126, worked by hand: the scale is
+    2^-126 and each code is the e4m3 value of x * 2^126 (exact).  A block with
+    largest magnitude 2^-120 (x * 2^126 = 64 = 2^6: exponent field 6 + 7 = 13,
+    code 0x68; 2^-121 -> 32: field 12, code 0x60; -0 -> 0x80) and one of
+    subnormal bf16 values (pattern 0x0001 = 2^-133 -> 2^-7 = 4 * 2^-9, an e4m3
+    subnormal: code 0x04; -2^-133 -> 0x84; pattern 0x0003 = 3 * 2^-133 ->
+    3 * 2^-7 = 1.5 * 2^-6: field 1, mantissa 4, code 0x0C)."""
+    x = np.zeros(256, dtype=np.uint16)
+    x[0] = 0x0380            # 2^-120: exponent field 7 -> 2^(7-127)
+    x[1] = 0x0300            # 2^-121
+    x[2] = 0x8000            # -0
+    x[128 + 0] = 0x0001
+    x[128 + 1] = 0x8001
+    x[128 + 2] = 0x0003
+    q, sc = oracle.quant_row_fp8(x)
+    assert sc.view(np.uint32).tolist() == [0x00800000, 0x00800000]     # 2^-126 both
+    assert q[:3].tolist() == [0x68, 0x60, 0x80]
+    assert np.all(q[3:128] == 0)
+    assert q[128:131].tolist() == [0x04, 0x84, 0x0C]
+    assert np.all(q[131:] == 0)

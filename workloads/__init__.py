@@ -29,7 +29,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "make_tokens", "make_routing", "make_inputs",
-           "bf16_bits_from_f32", "f32_from_bf16_bits"]
+           "bf16_bits_from_f32", "f32_from_bf16_bits", "fp8_exponent_sweep"]
 
 _STREAM_X = 0
 _STREAM_ROUTE = 1
@@ -186,3 +186,31 @@ def make_inputs(cfg: Config, T: int | None = None) -> dict:
         np.zeros((cfg.N, 0, cfg.H), dtype=np.uint16)
     idx, w = make_routing(cfg, T)
     return {"x": x, "idx": idx, "w": w}
+
+
+def fp8_exponent_sweep(seed: int = 3) -> np.ndarray:
+    """Blocks of 128 bf16 values (uint16 patterns, [n][128]) whose largest
+    magnitude walks every bf16 exponent: for each biased exponent 0..254 and
+    mantissas {0, 1, 0x40, 0x7F} (no zero pattern), two blocks with that
+    largest magnitude at a random place and random sign, the other elements
+    random patterns of no larger magnitude with random signs -- one block
+    with no zeros, one with a quarter of its elements +0 or -0.  Inputs for
+    the block-scaled e4m3 codec from the subnormal bf16 range to the largest
+    finite value."""
+    g = _rng(seed, 0, 2)
+    blocks = []
+    for ex in range(255):
+        for mant in (0, 1, 0x40, 0x7F):
+            top = (ex << 7) | mant
+            if top == 0:
+                continue
+            for zeros in (False, True):
+                mag = g.integers(1, top + 1, size=128, dtype=np.int64)
+                if zeros:
+                    z = g.choice(128, size=32, replace=False)
+                    mag[z] = 0
+                j = int(g.integers(128))
+                mag[j] = top
+                sign = g.integers(0, 2, size=128, dtype=np.int64) << 15
+                blocks.append((mag | sign).astype(np.uint16))
+    return np.stack(blocks)
