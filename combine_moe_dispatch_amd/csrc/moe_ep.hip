@@ -284,7 +284,8 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
     moe::Plan& p = g->plan;
     uint8_t* pool_send = nullptr;
     uint8_t* pool_recv = nullptr;
-    if ((rc = alloc(g, &p.err, 1)) || (rc = alloc(g, &p.ticket, 1)) ||
+    if ((rc = alloc(g, &p.err, 1)) || (rc = alloc(g, &p.err_sticky, 1)) ||
+        (rc = alloc(g, &p.err_rank, (size_t)N)) || (rc = alloc(g, &p.ticket, 1)) ||
         (rc = alloc(g, &p.cnt, (size_t)N * E)) ||
         (rc = alloc(g, &p.pos, (size_t)N * T * K)) || (rc = alloc(g, &p.soff, (size_t)N * (E + 1))) ||
         (rc = alloc(g, &p.roff, (size_t)N * (N + 1))) || (rc = alloc(g, &p.rbase, (size_t)N + 1)) ||
@@ -312,9 +313,10 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
     }
     g->pool_send = pool_send;
     g->pool_recv = pool_recv;
-    // the error word and the ticket counter start at zero; the offsets start
+    // the error words and the ticket counter start at zero; the offsets start
     // valid for an empty cycle
     if (hipMemset(p.err, 0, sizeof(int32_t)) != hipSuccess ||
+        hipMemset(p.err_sticky, 0, sizeof(int32_t)) != hipSuccess ||
         hipMemset(p.ticket, 0, sizeof(int32_t)) != hipSuccess ||
         hipMemset(p.eoff, 0, sizeof(int32_t) * (E + 1)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
@@ -528,10 +530,12 @@ int moe_group_status(moe_group_t g, hipStream_t stream)
         return rc;
     if (hipStreamSynchronize(stream) != hipSuccess)
         return MOE_ERR_HIP;
+    // the sticky word holds the bits of every cycle since the last status
+    // call; the cycle word is left alone (the next route plan overwrites it)
     int32_t word = 0;
-    if (hipMemcpy(&word, g->plan.err, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+    if (hipMemcpy(&word, g->plan.err_sticky, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
         return MOE_ERR_HIP;
-    if (word != 0 && hipMemset(g->plan.err, 0, sizeof(int32_t)) != hipSuccess)
+    if (word != 0 && hipMemset(g->plan.err_sticky, 0, sizeof(int32_t)) != hipSuccess)
         return MOE_ERR_HIP;
     if (hipDeviceSynchronize() != hipSuccess)
         return MOE_ERR_HIP;

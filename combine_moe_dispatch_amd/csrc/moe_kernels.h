@@ -33,7 +33,14 @@ struct Shape {
 };
 
 struct Plan {              // device pointers owned by the group
+    // Errors.  err is the current cycle's word: the route plan's last
+    // workgroup overwrites it with the OR of err_rank[] and its own checks,
+    // and every later kernel of the cycle writes nothing while it is set.
+    // err_sticky collects every cycle's bits until moe_group_status reads and
+    // clears it.
     int32_t* err;
+    int32_t* err_rank;     // [N]  routing/capacity bits of each sender, this cycle
+    int32_t* err_sticky;
     int32_t* ticket;       // arrival counter of the route-plan workgroups (0 between launches)
     int32_t* cnt;          // [N][E]
     int32_t* pos;          // [N][T][K]

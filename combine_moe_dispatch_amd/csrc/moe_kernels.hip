@@ -13,9 +13,10 @@
 // from the offsets, so the transfer, shuffle and combine kernels are pure
 // gathers in destination order.
 //
-// Every kernel after the route plan checks the device error word first and
+// Every kernel after the route plan checks the cycle's error word first and
 // writes nothing once an invalid expert id (or a capacity overflow) has been
-// seen.
+// seen in that cycle; the next cycle's route plan overwrites the word, and a
+// sticky copy keeps every cycle's bits for the status call.
 #include "moe_kernels.h"
 
 #include <hip/hip_ext.h>
@@ -67,6 +68,14 @@ __device__ inline int readlane(int v, int lane) { return __builtin_amdgcn_readla
 __device__ inline float readlane_f(float v, int lane)
 {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// A failed device-side check after the route plan: the cycle's word stops
+// the kernels that follow, the sticky word keeps it for moe_group_status.
+__device__ inline void raise_err(const Plan& p, int32_t bit)
+{
+    atomicOr(p.err, bit);
+    atomicOr(p.err_sticky, bit);
 }
 
 // Exclusive scan of one int per thread over a block of NT threads.  Returns
@@ -198,7 +207,7 @@ __device__ int2 walk_column(const int32_t* __restrict__ lo, const int32_t* __res
 // totals need no column of their own: the last expert column's running sum
 // ends at eoff[E] = rbase[N], and the last partial column's upper bounds
 // psoff[s][N] are the per-sender totals whose running sum is pbase.
-__device__ void group_offsets(const RouteArgs& ra, const Plan& p)
+__device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* wg_err)
 {
     const int N = ra.N, E = ra.E, L = ra.L;
     const int32_t* __restrict__ soff = p.soff;
@@ -249,7 +258,7 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p)
                                         p.roff + (size_t)d * (N + 1), nullptr);
             p.rbase[d] = br.x;
             if ((int64_t)br.y > ra.cap)
-                atomicOr(p.err, ERR_BIT_CAPACITY);
+                atomicOr(wg_err, ERR_BIT_CAPACITY);
         } else {
             const int d = col - E - N;
             const bool last = d == N - 1;
@@ -425,6 +434,7 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     int32_t* cur = reinterpret_cast<int32_t*>(mask + 2 * (size_t)CW * NK);  // [2][NK] cursors
     __shared__ int32_t wave_sums[RP_WAVES + 1];
     __shared__ int32_t ticket;
+    __shared__ int32_t wg_err;             // this workgroup's error bits
 
     const int s = blockIdx.x;
     const int items = ra.T * ra.K;
@@ -438,6 +448,8 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
         cur[k] = 0;
     for (int j = tid; j < CW * NK; j += RP_NT)
         mask[j] = 0ull;
+    if (tid == 0)
+        wg_err = 0;
     // expert ids of the first HELD_CHUNKS chunks stay in registers for both
     // the counting and the ranking (thread tid takes item c*chunk + tid of
     // chunk c); all loads are issued before the first use
@@ -515,7 +527,7 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
         }
     }
     if (bad)
-        atomicOr(p.err, ERR_BIT_ROUTING);
+        atomicOr(&wg_err, ERR_BIT_ROUTING);
     __syncthreads();
 
     // counts out, exclusive scans -> send offsets (and the partial rows'
@@ -523,13 +535,13 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     // item inside its expert's rows (and of every first item of a rank among
     // the sender's partial rows, ordered by rank, then token)
     publish_counts(cur, E, p.cnt + (size_t)s * E, p.soff + (size_t)s * (E + 1), wave_sums,
-                   ra.slot_cap, p.err);
+                   ra.slot_cap, &wg_err);
     if (!ra.partial) {
         stable_ranks<false>(items, NK, CW, mask, cur, held_e,
                             [&](int i, bool mine) { return mine ? my_idx[i] : -1; },
                             p.pos + (size_t)s * items, nullptr);
     } else {
-        publish_counts(cur + E, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums, -1, p.err);
+        publish_counts(cur + E, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums, -1, &wg_err);
         stable_ranks<true>(items, NK, CW, mask, cur, held_e,
                            [&](int i, bool mine) {
                                const int e = mine ? my_idx[i] : -1;
@@ -541,9 +553,12 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
                            p.pos + (size_t)s * items, p.ppos + (size_t)s * items);
     }
 
-    // Publish this rank's counts and draw a ticket.  Every wave waits for its
-    // own stores, then one agent-scope release (an L2 write-back) covers the
-    // whole workgroup before the ticket is taken.
+    // Publish this rank's counts and error bits and draw a ticket.  Every
+    // wave waits for its own stores, then one agent-scope release (an L2
+    // write-back) covers the whole workgroup before the ticket is taken.
+    __syncthreads();
+    if (tid == 0)
+        p.err_rank[s] = wg_err;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
@@ -554,9 +569,23 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     if (ticket != ra.N - 1)
         return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    group_offsets(ra, p);
-    if (tid == 0)
+    group_offsets(ra, p, &wg_err);
+    // the cycle's error word: every sender's bits and the offsets' checks.
+    // It overwrites the last cycle's word, so an error stops only the kernels
+    // of its own cycle; the sticky word keeps it for the status call.
+    int e = 0;
+    for (int j = tid; j < N; j += RP_NT)
+        e |= p.err_rank[j];
+    if (e)
+        atomicOr(&wg_err, e);
+    __syncthreads();
+    if (tid == 0) {
+        const int32_t cyc = wg_err;
+        *p.err = cyc;
+        if (cyc)
+            atomicOr(p.err_sticky, cyc);
         atomicExch(p.ticket, 0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -696,7 +725,7 @@ __device__ inline void record_partial(const Shape& sh, const Plan& p, int64_t to
         orow = p.qbase[d] + p.qoff[(size_t)d * (N + 1) + s] + pp - p.psoff[(size_t)s * (N + 1) + d];
         ok = (unsigned)tr < (unsigned)P && (unsigned)orow < (unsigned)P;
         if (!ok)
-            atomicOr(p.err, ERR_BIT_INTERNAL);
+            raise_err(p, ERR_BIT_INTERNAL);
     }
     // then the masks and second items, head by head (no memory access)
     uint64_t my_mask = 0;
@@ -750,7 +779,7 @@ __device__ inline int pack_dest(const Shape& sh, const Plan& p, const int32_t* _
                     dst_w[row] = w[i];
             }
         } else if (lead) {
-            atomicOr(p.err, ERR_BIT_INTERNAL);
+            raise_err(p, ERR_BIT_INTERNAL);
         }
     }
     if (sh.partial && lead)
@@ -828,8 +857,11 @@ __device__ inline uint32_t e4m3_encode(float v)
 
 // [EFA] "Dispatch/combine latency": block-scaled fp8 dispatch; the blocks are
 // 128 elements with one fp32 scale each.  Per block: amax = max|x| (exact from
-// bf16), inv = 448/amax and scale = amax/448 as correctly rounded fp32
-// divisions (inv = 0, scale = 1 for an all-zero block), code = e4m3(x * inv).
+// bf16); for amax >= 448 * 2^-126, inv = 448/amax and scale = amax/448 as
+// correctly rounded fp32 divisions; for a smaller nonzero amax the scale is
+// held at the smallest normal fp32 value, scale = 2^-126 and inv = 2^126 (so
+// the scale never loses bits to an fp32 subnormal and inv never overflows);
+// inv = 0, scale = 1 for an all-zero block; code = e4m3(x * inv).
 // Each lane encodes 16 consecutive elements (two 16-byte input vectors) into
 // one 16-byte store of codes; a 128-element block is 8 lanes, and amax is
 // reduced over the 8-lane group with xor shuffles.
@@ -894,9 +926,12 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
             amax = fmaxf(amax, __shfl_xor(amax, 2, WAVE));
             amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
             float inv = 0.0f, scale = 1.0f;
-            if (amax > 0.0f) {
+            if (amax >= 0x1.cp-118f) {         // 448 * 2^-126
                 inv = 448.0f / amax;
                 scale = amax / 448.0f;
+            } else if (amax > 0.0f) {
+                inv = 0x1p126f;
+                scale = 0x1p-126f;
             }
             uint32_t c[16];
 #pragma unroll
@@ -1168,7 +1203,7 @@ __global__ __launch_bounds__(COPY_THREADS) void combine_reduce_kernel(Shape sh, 
     }
     if (__ballot((unsigned)my_p >= (unsigned)TK) != 0) {
         if (lane == 0)
-            atomicOr(p.err, ERR_BIT_INTERNAL);
+            raise_err(p, ERR_BIT_INTERNAL);
         return;
     }
     const int n = rs.len;                      // this wave's part of the row
@@ -1332,7 +1367,7 @@ __global__ __launch_bounds__(COPY_THREADS) void partial_send_kernel(Shape sh, Pl
     }
     if (__ballot(bad) != 0) {
         if (lane == 0)
-            atomicOr(p.err, ERR_BIT_INTERNAL);
+            raise_err(p, ERR_BIT_INTERNAL);
         return;
     }
     const int n = rs.len;
@@ -1502,7 +1537,7 @@ __global__ __launch_bounds__(COPY_THREADS) void partial_reduce_kernel(Shape sh, 
     const uint64_t heads = __ballot(head);
     if (__ballot(bad) != 0 || heads == 0) {
         if (lane == 0)
-            atomicOr(p.err, ERR_BIT_INTERNAL);
+            raise_err(p, ERR_BIT_INTERNAL);
         return;
     }
     // a token's heads have distinct ranks: order = number of heads below

@@ -31,8 +31,11 @@
  *    pages' barrier that keeps a rank from starting the next dispatch while
  *    peers still read ([EPMC] "Portable kernels").
  *  - Routing errors (an expert id outside [0,E)) are found on the device; the
- *    kernels then write none of the row buffers or outputs of that cycle, and
- *    moe_group_status() reports MOE_ERR_ROUTING.
+ *    kernels then write none of the row buffers or outputs of that cycle
+ *    (only that cycle: the next dispatch_send starts with a clean cycle
+ *    word), and moe_group_status() reports MOE_ERR_ROUTING.  The four calls
+ *    never synchronise with the device, so they cannot return an error the
+ *    device finds later; the status call is where device errors surface.
  *  - One host thread at a time per group.
  */
 #ifndef MOE_EP_H
@@ -273,9 +276,13 @@ typedef struct moe_group_view {
 
 int moe_group_view_get(moe_group_t g, moe_group_view* out);
 
-/* Synchronise `stream`, then return and clear the device-side error word:
- * MOE_OK, MOE_ERR_ROUTING, MOE_ERR_CAPACITY or MOE_ERR_INTERNAL (in that order
- * of precedence when several bits are set). */
+/* Synchronise `stream`, then return and clear the device-side errors of
+ * every cycle since the previous status call: MOE_OK, MOE_ERR_ROUTING,
+ * MOE_ERR_CAPACITY or MOE_ERR_INTERNAL (in that order of precedence when
+ * several bits are set).  Only `stream` is synchronised: when the group's
+ * calls ran on several streams, synchronise the others first (or pass the
+ * stream that was ordered after them), or a bit set by work still running on
+ * another stream can be missed. */
 int moe_group_status(moe_group_t g, hipStream_t stream);
 
 /* Per-kernel timing, for measurement.  kernel_mask selects the kernels to

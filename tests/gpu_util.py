@@ -77,14 +77,15 @@ def to_dev(torch, a: np.ndarray):
 
 
 def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, want_rows=True,
-              transport=0, combine_mode=0, layout=0, recv_gather=None):
+              transport=0, combine_mode=0, layout=0, recv_gather=None, check_status=True):
     """One full dispatch + stand-in expert + combine cycle on the GPU.
     Returns a dict of host copies of every buffer (rows only if want_rows;
     the send-side buffers only with the staged transport).  With the partial
     combine the weights go to dispatch_send, combine_recv gets none, and the
     partial-row plan and rows are returned too.  With the fixed-slot layout the
     receive-layout rows (receive planes, combine send rows) are read only at
-    the slot rows listed in recv_gather, in that order."""
+    the slot rows listed in recv_gather, in that order.  With
+    check_status=False the group's status is not read (nor cleared)."""
     N, T, K, E, H = cfg.N, inp["idx"].shape[1], cfg.K, cfg.E, cfg.H
     fp8 = cfg.dtype == "fp8"
     T_max = T if T_max is None else T_max
@@ -107,7 +108,8 @@ def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, w
         mep.moe_dispatch_send(g, T, x, idx, w if partial else None)
         mep.moe_dispatch_recv(g, expert_x, expert_scale, expert_offsets)
         torch.cuda.synchronize()
-        assert mep.moe_group_status(g) == mep.MOE_OK
+        if check_status:
+            assert mep.moe_group_status(g) == mep.MOE_OK
         res = {}
         v = mep.moe_group_view_get(g)
         res["cnt"] = d2h(v.cnt, (N, E), np.int32)
@@ -152,7 +154,8 @@ def run_cycle(torch, mep, cfg, inp, *, T_max=None, identity=False, group=None, w
         mep.moe_combine_send(g, y)
         mep.moe_combine_recv(g, None if partial else w, out)
         torch.cuda.synchronize()
-        assert mep.moe_group_status(g) == mep.MOE_OK
+        if check_status:
+            assert mep.moe_group_status(g) == mep.MOE_OK
         v = mep.moe_group_view_get(g)
         res["y"] = y.view(torch.int16).cpu().numpy().view(np.uint16)
         if partial:

@@ -56,6 +56,45 @@ def test_routing_error_writes_nothing_and_is_reported(combine_mode):
         mep.moe_group_destroy(g)
 
 
+@pytest.mark.parametrize("combine_mode", [0, 1])
+def test_routing_error_stops_only_its_own_cycle(combine_mode):
+    """A cycle with an invalid expert id, then a valid cycle on the same group
+    with no status read in between: the valid cycle runs in full (its outputs
+    equal the oracle's), and the status call afterwards still reports the
+    earlier cycle's routing error, once."""
+    cfg = CONFIGS["A"]
+    say(f"[gpu] routing error then a valid cycle {cfg.describe()} combine_mode={combine_mode}")
+    partial = combine_mode == mep.MOE_COMBINE_PARTIAL
+    inp = make_inputs(cfg)
+    bad = inp["idx"].copy()
+    bad[0, 5, 1] = cfg.E + 3
+    g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16,
+                             mep.MOE_TRANSPORT_STAGED, combine_mode)
+    try:
+        R = cfg.rows
+        x, idx, w = to_dev(torch, inp["x"]), to_dev(torch, bad), to_dev(torch, inp["w"])
+        expert_x = torch.empty((R * cfg.H,), dtype=torch.int16, device="cuda")
+        offs = torch.empty((cfg.E + 1,), dtype=torch.int32, device="cuda")
+        y = torch.zeros((R, cfg.H), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((cfg.N, cfg.T, cfg.H), dtype=torch.int16, device="cuda")
+        mep.moe_dispatch_send(g, cfg.T, x, idx, w if partial else None)
+        mep.moe_dispatch_recv(g, expert_x, None, offs)
+        mep.moe_combine_send(g, y)
+        mep.moe_combine_recv(g, None if partial else w, out)
+        gpu = run_cycle(torch, mep, cfg, inp, group=g, combine_mode=combine_mode,
+                        check_status=False)
+        if partial:
+            from tests.test_gpu_partial import _check
+            _check(cfg, inp, gpu)
+        else:
+            from tests.test_gpu_parity import _compare_all
+            _compare_all(cfg, inp, gpu)
+        assert mep.moe_group_status(g) == mep.MOE_ERR_ROUTING
+        assert mep.moe_group_status(g) == mep.MOE_OK
+    finally:
+        mep.moe_group_destroy(g)
+
+
 def test_call_order_and_arguments():
     cfg = CONFIGS["A"]
     say(f"[gpu] call order {cfg.describe()}")

@@ -1,13 +1,18 @@
 """fp8-e4m3 dispatch on the GPU against the oracle's codec on crafted rows:
 every bf16 value of magnitude <= 448 quantised with scale 1 (so every e4m3
 code, every midpoint and every tie), blocks with awkward scales, all-zero and
-signed-zero blocks, and blocks whose largest magnitude is tiny."""
+signed-zero blocks, blocks whose largest magnitude is tiny, and blocks whose
+largest magnitude walks every bf16 exponent.  Besides equality with the
+oracle, every block is held to the codec's own properties (tests/fp8_checks.py:
+no NaN code, a normal scale, torch's e4m3 rounding of x * inv, the
+dequantisation bound)."""
 import numpy as np
 import pytest
 
 import oracle
+from tests.fp8_checks import check_blocks
 from tests.gpu_util import run_cycle, say
-from workloads import Config, bf16_bits_from_f32
+from workloads import Config, bf16_bits_from_f32, fp8_exponent_sweep
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +49,7 @@ def _crafted_rows() -> np.ndarray:
     tiny[3] = 0x0001                                                  # amax subnormal
     tiny[9] = 0x8001
     blocks.append(tiny)
+    blocks.extend(fp8_exponent_sweep())
     rows = np.concatenate(blocks)
     n_rows = -(-rows.size // H)
     pad = np.zeros(n_rows * H - rows.size, dtype=np.uint16)
@@ -64,3 +70,5 @@ def test_fp8_encode_exhaustive_on_crafted_rows():
         bad = np.nonzero(gpu["expert_x"][t] != q)[0]
         assert bad.size == 0, (t, bad[:5], rows[t][bad[:5]], gpu["expert_x"][t][bad[:5]], q[bad[:5]])
         assert np.array_equal(gpu["expert_scale"][t].view(np.uint32), sc.view(np.uint32)), t
+    check_blocks(rows.reshape(-1, BLK), gpu["expert_x"].reshape(-1, BLK),
+                 gpu["expert_scale"].reshape(-1), "gpu")
