@@ -77,6 +77,9 @@ def _declare(L):
     L.orc_combine_recv_f64.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P]
     L.orc_combine_token.argtypes = [_I, _I, _P, _P, _P]
     L.orc_partial_token.argtypes = [_I, _I, _P, _P, _P, _P]
+    L.orc_combine_tokens.argtypes = [ctypes.c_int64, _I, _I, _P, _P, _P, _P]
+    L.orc_partial_tokens.argtypes = [ctypes.c_int64, _I, _I, _P, _P, _P, _P, _P]
+    L.orc_quant_rows_fp8.argtypes = [ctypes.c_int64, _I, _P, _P, _P]
     L.orc_f32_to_bf16_n.argtypes = [_Z, _P, _P]
     L.orc_send_meta.argtypes = [_I, _I, _I, _P, _P]
     L.orc_partial_counts.argtypes = [_I, _I, _I, _I, _P, _P]
@@ -91,6 +94,17 @@ def _declare(L):
     L.orc_slot_rows.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P]
     L.orc_transfer_slots.argtypes = [_I, _I, _I, _Z, _P, _P, _P, _P]
     L.orc_shuffle_slots.argtypes = [_I, _I, _I, _Z, _Z, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    L.orc_transfer_range.argtypes = [_I, _I, _I, _I, _Z, _P, _P, _P, _P, _P, _I, _I]
+    L.orc_shuffle_range.argtypes = [_I, _I, _I, _I, _Z, _Z, _P, _P, _P, _P, _P,
+                                    _P, _P, _P, _P, _P, _P, _P, _I, _I]
+    L.orc_combine_send_range.argtypes = [_I, _I, _Z, _P, _P, _P, _P, _P, _P, _P, _I, _I]
+    L.orc_combine_transfer_range.argtypes = [_I, _I, _I, _I, _Z, _P, _P, _P, _P, _P, _I, _I]
+    L.orc_expert_rows_range.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I]
+    L.orc_partial_counts_range.argtypes = [_I, _I, _I, _I, _P, _P, _I, _I]
+    L.orc_partial_rows_range.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _I, _I]
+    L.orc_partial_send_range.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I]
+    L.orc_partial_transfer_range.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I, _I]
+    L.orc_partial_recv_range.argtypes = [_I, _I, _I, _P, _P, _P, _I, _I]
 
 
 def _p(a: np.ndarray):
@@ -132,6 +146,18 @@ def quant_row_fp8(xrow: np.ndarray):
     q = np.empty(H, dtype=np.uint8)
     sc = np.empty(H // 128, dtype=np.float32)
     lib().orc_quant_row_fp8(H, _p(xrow), _p(q), _p(sc))
+    return q, sc
+
+
+def quant_rows_fp8(x: np.ndarray, q: np.ndarray = None, sc: np.ndarray = None):
+    """quant_row_fp8 of every row of x (uint16 [n][H]) -> (codes uint8 [n][H],
+    scales fp32 [n][H/128]); q and sc may be given to be filled in place."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    n, H = x.shape
+    q = np.empty((n, H), dtype=np.uint8) if q is None else q
+    sc = np.empty((n, H // 128), dtype=np.float32) if sc is None else sc
+    assert q.shape == (n, H) and sc.shape == (n, H // 128)
+    lib().orc_quant_rows_fp8(n, H, _p(x), _p(q), _p(sc))
     return q, sc
 
 
@@ -457,6 +483,36 @@ def partial_token(rows: np.ndarray, w: np.ndarray, rank: np.ndarray) -> np.ndarr
     return out
 
 
+def combine_tokens(y: np.ndarray, rows: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """combine_token of many tokens: rows int64 [n][K] index the returned rows
+    in y (uint16 [*][H]), w fp32 [n][K] -> out uint16 [n][H]."""
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, K = rows.shape
+    H = y.shape[1]
+    assert w.shape == (n, K) and (n == 0 or (rows.min() >= 0 and rows.max() < y.shape[0]))
+    out = np.empty((n, H), dtype=np.uint16)
+    lib().orc_combine_tokens(n, K, H, _p(rows), _p(w), _p(y), _p(out))
+    return out
+
+
+def partial_tokens(y: np.ndarray, rows: np.ndarray, w: np.ndarray, rank: np.ndarray) -> np.ndarray:
+    """partial_token of many tokens (rows int64 [n][K] into y, w fp32 [n][K],
+    destination ranks int32 [n][K]) -> out uint16 [n][H]."""
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rank = np.ascontiguousarray(rank, dtype=np.int32)
+    n, K = rows.shape
+    H = y.shape[1]
+    assert w.shape == (n, K) and rank.shape == (n, K)
+    assert n == 0 or (rows.min() >= 0 and rows.max() < y.shape[0])
+    out = np.empty((n, H), dtype=np.uint16)
+    lib().orc_partial_tokens(n, K, H, _p(rows), _p(w), _p(rank), _p(y), _p(out))
+    return out
+
+
 def run_combine(y: np.ndarray, w: np.ndarray, pl: dict, H: int) -> dict:
     """Every combine step, in order; y is the expert output in expert-row order."""
     _assert_finite_bf16(y, "expert outputs")
@@ -505,3 +561,184 @@ def run_partial_combine(y: np.ndarray, w: np.ndarray, idx: np.ndarray, pl: dict,
     lib().orc_partial_recv(N, T, H, _p(pp["token_row"]), _p(precv), _p(out))
     pp.update(psend=psend, precv=precv, out=out)
     return pp
+
+
+# ------------------------------------------- threaded forms (P-thread timing)
+#
+# The same steps with each stage's outer loop (over sender ranks, receiver
+# ranks or experts) split into `threads` contiguous ranges, one per thread,
+# and a join between stages.  Stages whose loop runs over senders alone are
+# called on row slices of their arrays; the cross-rank stages take the
+# range of their outer loop.  The arithmetic is the functions' own, so the
+# results equal the single-thread forms bit for bit (checked by the tests).
+# Used to time the oracle on several host cores.
+
+def _ranges(n: int, parts: int):
+    parts = max(1, min(parts, n)) if n > 0 else 1
+    step, extra = divmod(n, parts)
+    out, a = [], 0
+    for i in range(parts):
+        b = a + step + (1 if i < extra else 0)
+        out.append((a, b))
+        a = b
+    return out
+
+
+def _par(pool, n: int, threads: int, fn):
+    """fn(a, b) over a split of [0, n) into `threads` ranges; returns the results."""
+    return list(pool.map(lambda ab: fn(*ab), _ranges(n, threads)))
+
+
+def run_dispatch_threads(x: np.ndarray, idx: np.ndarray, E: int, threads: int,
+                         fp8: bool = False, pool=None) -> dict:
+    """run_dispatch with every stage split over `threads` threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    own = pool is None
+    pool = ThreadPoolExecutor(threads) if own else pool
+    try:
+        return _run_dispatch_threads(x, idx, E, threads, fp8, pool)
+    finally:
+        if own:
+            pool.shutdown()
+
+
+def _run_dispatch_threads(x, idx, E, P, fp8, pool):
+    _assert_finite_bf16(x, "tokens")
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    N, T, H = x.shape
+    K = idx.shape[2]
+    TK = T * K
+    L_ = lib()
+    cnt = np.empty((N, E), dtype=np.int32)
+    soff = np.empty((N, E + 1), dtype=np.int32)
+    pos = np.empty((N, T, K), dtype=np.int32)
+    bad = _par(pool, N, P, lambda a, b: L_.orc_route_count(b - a, T, K, E, _p(idx[a:b]),
+                                                            _p(cnt[a:b])))
+    if any(r != 0 for r in bad):
+        raise RoutingError("expert id outside [0, E)")
+    _par(pool, N, P, lambda a, b: L_.orc_send_offsets(b - a, E, _p(cnt[a:b]), _p(soff[a:b])))
+    _par(pool, N, P, lambda a, b: L_.orc_positions(b - a, T, K, E, _p(idx[a:b]), _p(soff[a:b]),
+                                                    _p(pos[a:b])))
+    roff, G = recv_offsets(soff, N)
+    eoff = expert_offsets(cnt)
+    R = N * TK
+    send_meta = np.zeros(R, dtype=np.int32)
+    if fp8:
+        send_x = np.zeros((R, H), dtype=np.uint8)
+        send_scale = np.zeros((R, H // 128), dtype=np.float32)
+        _par(pool, N, P, lambda a, b: L_.orc_pack_fp8(
+            b - a, T, K, H, _p(x[a:b]), _p(pos[a:b]), _p(send_x[a * TK:b * TK]),
+            _p(send_scale[a * TK:b * TK]), _p(send_meta[a * TK:b * TK])))
+    else:
+        send_x = np.zeros((R, H), dtype=np.uint16)
+        send_scale = None
+        _par(pool, N, P, lambda a, b: L_.orc_pack_bf16(
+            b - a, T, K, H, _p(x[a:b]), _p(pos[a:b]), _p(send_x[a * TK:b * TK]),
+            _p(send_meta[a * TK:b * TK])))
+
+    def xfer(plane):
+        recv = np.zeros_like(plane)
+        rb = plane.nbytes // R if R else 0
+        _par(pool, N, P, lambda a, b: L_.orc_transfer_range(
+            N, E, T, K, rb, _p(soff), _p(roff), _p(G), _p(plane), _p(recv), a, b))
+        return recv
+    recv_x = xfer(send_x)
+    recv_scale = xfer(send_scale) if fp8 else None
+    recv_meta = xfer(send_meta)
+    expert_x = np.zeros_like(recv_x)
+    expert_scale = np.zeros_like(recv_scale) if fp8 else None
+    src_rank = np.zeros(R, dtype=np.int32)
+    src_slot = np.zeros(R, dtype=np.int32)
+    rb = recv_x.nbytes // R if R else 0
+    sb = recv_scale.nbytes // R if (fp8 and R) else 0
+    _par(pool, E, P, lambda a, b: L_.orc_shuffle_range(
+        N, E, T, K, rb, sb, _p(cnt), _p(soff), _p(roff), _p(G), _p(eoff), _p(recv_x),
+        _p(recv_scale) if fp8 else None, _p(recv_meta), _p(expert_x),
+        _p(expert_scale) if fp8 else None, _p(src_rank), _p(src_slot), a, b))
+    return {"cnt": cnt, "soff": soff, "pos": pos, "roff": roff, "G": G, "eoff": eoff,
+            "send_x": send_x, "send_scale": send_scale, "send_meta": send_meta,
+            "recv_x": recv_x, "recv_scale": recv_scale, "recv_meta": recv_meta,
+            "expert_x": expert_x, "expert_scale": expert_scale, "expert_src_rank": src_rank,
+            "expert_src_slot": src_slot}
+
+
+def run_combine_threads(y: np.ndarray, w: np.ndarray, pl: dict, H: int, threads: int,
+                        pool=None) -> dict:
+    """run_combine with every stage split over `threads` threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    own = pool is None
+    pool = ThreadPoolExecutor(threads) if own else pool
+    try:
+        _assert_finite_bf16(y, "expert outputs")
+        assert np.all(np.isfinite(w)), "non-finite weights"
+        P = threads
+        L_ = lib()
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        N, T, K = pl["pos"].shape
+        E = pl["cnt"].shape[1]
+        TK = T * K
+        R = y.shape[0]
+        rb = y.nbytes // R if R else 0
+        comb_send = np.zeros_like(y)
+        _par(pool, E, P, lambda a, b: L_.orc_combine_send_range(
+            N, E, rb, _p(pl["cnt"]), _p(pl["soff"]), _p(pl["roff"]), _p(pl["G"]),
+            _p(pl["eoff"]), _p(y), _p(comb_send), a, b))
+        comb_recv = np.zeros_like(y)
+        _par(pool, N, P, lambda a, b: L_.orc_combine_transfer_range(
+            N, E, T, K, rb, _p(pl["soff"]), _p(pl["roff"]), _p(pl["G"]), _p(comb_send),
+            _p(comb_recv), a, b))
+        out = np.zeros((N, T, H), dtype=np.uint16)
+        pos = np.ascontiguousarray(pl["pos"])
+        _par(pool, N, P, lambda a, b: L_.orc_combine_recv(
+            b - a, T, K, H, _p(pos[a:b]), _p(w[a:b]), _p(comb_recv[a * TK:b * TK]),
+            _p(out[a:b])))
+        return {"comb_send": comb_send, "comb_recv": comb_recv, "out": out}
+    finally:
+        if own:
+            pool.shutdown()
+
+
+def run_partial_combine_threads(y: np.ndarray, w: np.ndarray, idx: np.ndarray, pl: dict, H: int,
+                                threads: int, pool=None) -> dict:
+    """run_partial_combine with every stage split over `threads` threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    own = pool is None
+    pool = ThreadPoolExecutor(threads) if own else pool
+    try:
+        _assert_finite_bf16(y, "expert outputs")
+        assert np.all(np.isfinite(w)), "non-finite weights"
+        P = threads
+        L_ = lib()
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        N, T, K = idx.shape
+        E = pl["cnt"].shape[1]
+        pc = np.zeros((N, N), dtype=np.int32)
+        _par(pool, N, P, lambda a, b: L_.orc_partial_counts_range(N, T, K, E, _p(idx), _p(pc),
+                                                                   a, b))
+        owner_row = np.zeros((N, T, N), dtype=np.int32)
+        token_row = np.zeros((N, T, N), dtype=np.int32)
+        _par(pool, N, P, lambda a, b: L_.orc_partial_rows_range(
+            N, T, K, E, _p(idx), _p(pc), _p(owner_row), _p(token_row), a, b))
+        rows = np.zeros((N, T, K), dtype=np.int32)
+        _par(pool, N, P, lambda a, b: L_.orc_expert_rows_range(
+            N, T, K, E, _p(idx), _p(pl["cnt"]), _p(pl["soff"]), _p(pl["pos"]), _p(pl["eoff"]),
+            _p(rows), a, b))
+        Pn = int(pc.sum())
+        psend = np.zeros((Pn, H), dtype=np.uint16)
+        precv = np.zeros((Pn, H), dtype=np.uint16)
+        out = np.zeros((N, T, H), dtype=np.uint16)
+        _par(pool, N, P, lambda a, b: L_.orc_partial_send_range(
+            N, T, K, E, H, _p(idx), _p(w), _p(rows), _p(y), _p(owner_row), _p(psend), a, b))
+        _par(pool, N, P, lambda a, b: L_.orc_partial_transfer_range(
+            N, T, H, _p(owner_row), _p(token_row), _p(psend), _p(precv), a, b))
+        _par(pool, N, P, lambda a, b: L_.orc_partial_recv_range(
+            N, T, H, _p(token_row), _p(precv), _p(out), a, b))
+        return {"pc": pc, "owner_row": owner_row, "token_row": token_row, "P": Pn,
+                "psend": psend, "precv": precv, "out": out}
+    finally:
+        if own:
+            pool.shutdown()

@@ -283,6 +283,13 @@ void orc_quant_row_fp8(int H, const uint16_t* xrow, uint8_t* q, float* scale)
     }
 }
 
+/* orc_quant_row_fp8 of n consecutive rows of H elements. */
+void orc_quant_rows_fp8(int64_t n, int H, const uint16_t* x, uint8_t* q, float* scale)
+{
+    for (int64_t i = 0; i < n; ++i)
+        orc_quant_row_fp8(H, x + (size_t)i * H, q + (size_t)i * H, scale + (size_t)i * (H / 128));
+}
+
 /* Pack, fp8 payload: as orc_pack_bf16 but each token is quantised once and the
  * K copies carry its codes and its H/128 block scales. */
 void orc_pack_fp8(int N, int T, int K, int H, const uint16_t* x, const int32_t* pos,
@@ -314,12 +321,13 @@ void orc_pack_fp8(int N, int T, int K, int H, const uint16_t* x, const int32_t* 
  * soff[s][dL] of sender s land at receive row G[d] + roff[d][s].  Rows are
  * opaque byte strings of row_bytes bytes; the call is made once per plane
  * (payload, scales, meta). */
-void orc_transfer(int N, int E, int T, int K, size_t row_bytes, const int32_t* soff,
-                  const int32_t* roff, const int32_t* G, const uint8_t* send, uint8_t* recv)
+void orc_transfer_range(int N, int E, int T, int K, size_t row_bytes, const int32_t* soff,
+                        const int32_t* roff, const int32_t* G, const uint8_t* send,
+                        uint8_t* recv, int s0, int s1)
 {
     int L = E / N;
     size_t TK = (size_t)T * K;
-    for (int s = 0; s < N; ++s)
+    for (int s = s0; s < s1; ++s)
         for (int d = 0; d < N; ++d) {
             int32_t first = soff[(size_t)s * (E + 1) + d * L];
             int32_t n = soff[(size_t)s * (E + 1) + (d + 1) * L] - first;
@@ -327,6 +335,12 @@ void orc_transfer(int N, int E, int T, int K, size_t row_bytes, const int32_t* s
             size_t dst = (size_t)G[d] + roff[(size_t)d * (N + 1) + s];
             memcpy(recv + dst * row_bytes, send + src * row_bytes, row_bytes * (size_t)n);
         }
+}
+
+void orc_transfer(int N, int E, int T, int K, size_t row_bytes, const int32_t* soff,
+                  const int32_t* roff, const int32_t* G, const uint8_t* send, uint8_t* recv)
+{
+    orc_transfer_range(N, E, T, K, row_bytes, soff, roff, G, send, recv, 0, N);
 }
 
 /* ------------------------------------------------------ dispatch: shuffle */
@@ -341,17 +355,17 @@ void orc_transfer(int N, int E, int T, int K, size_t row_bytes, const int32_t* s
  * Metadata: src_rank[r] = s, src_slot[r] = the row's meta word (t*K+k).
  * The payload plane has row_bytes bytes per row; scales (scale_bytes per row,
  * 0 when there are none) move with it. */
-void orc_shuffle(int N, int E, int T, int K, size_t row_bytes, size_t scale_bytes,
-                 const int32_t* cnt, const int32_t* soff, const int32_t* roff,
-                 const int32_t* G, const int32_t* eoff,
-                 const uint8_t* recv_x, const uint8_t* recv_scale, const int32_t* recv_meta,
-                 uint8_t* expert_x, uint8_t* expert_scale,
-                 int32_t* src_rank, int32_t* src_slot)
+void orc_shuffle_range(int N, int E, int T, int K, size_t row_bytes, size_t scale_bytes,
+                       const int32_t* cnt, const int32_t* soff, const int32_t* roff,
+                       const int32_t* G, const int32_t* eoff,
+                       const uint8_t* recv_x, const uint8_t* recv_scale, const int32_t* recv_meta,
+                       uint8_t* expert_x, uint8_t* expert_scale,
+                       int32_t* src_rank, int32_t* src_slot, int e0, int e1)
 {
     int L = E / N;
     (void)T;
     (void)K;
-    for (int e = 0; e < E; ++e) {
+    for (int e = e0; e < e1; ++e) {
         int d = e / L;
         int32_t r = eoff[e];
         for (int s = 0; s < N; ++s) {
@@ -369,6 +383,17 @@ void orc_shuffle(int N, int E, int T, int K, size_t row_bytes, size_t scale_byte
             }
         }
     }
+}
+
+void orc_shuffle(int N, int E, int T, int K, size_t row_bytes, size_t scale_bytes,
+                 const int32_t* cnt, const int32_t* soff, const int32_t* roff,
+                 const int32_t* G, const int32_t* eoff,
+                 const uint8_t* recv_x, const uint8_t* recv_scale, const int32_t* recv_meta,
+                 uint8_t* expert_x, uint8_t* expert_scale,
+                 int32_t* src_rank, int32_t* src_slot)
+{
+    orc_shuffle_range(N, E, T, K, row_bytes, scale_bytes, cnt, soff, roff, G, eoff, recv_x,
+                      recv_scale, recv_meta, expert_x, expert_scale, src_rank, src_slot, 0, E);
 }
 
 /* ------------------------------------------------- the expert (not the path) */
@@ -403,12 +428,13 @@ void orc_expert_standin(int E, int H, const int32_t* eoff, const uint8_t* expert
  * is the reverse route, one write per peer).  The inverse of orc_shuffle: the
  * expert-order row r of expert e from sender s, i-th of its run, goes back to
  * receive-layout row G[d] + roff[d][s] + soff[s][e] - soff[s][dL] + i. */
-void orc_combine_send(int N, int E, size_t row_bytes, const int32_t* cnt,
-                      const int32_t* soff, const int32_t* roff, const int32_t* G,
-                      const int32_t* eoff, const uint8_t* y, uint8_t* comb_send)
+void orc_combine_send_range(int N, int E, size_t row_bytes, const int32_t* cnt,
+                            const int32_t* soff, const int32_t* roff, const int32_t* G,
+                            const int32_t* eoff, const uint8_t* y, uint8_t* comb_send,
+                            int e0, int e1)
 {
     int L = E / N;
-    for (int e = 0; e < E; ++e) {
+    for (int e = e0; e < e1; ++e) {
         int d = e / L;
         int32_t r = eoff[e];
         for (int s = 0; s < N; ++s) {
@@ -422,16 +448,23 @@ void orc_combine_send(int N, int E, size_t row_bytes, const int32_t* cnt,
     }
 }
 
+void orc_combine_send(int N, int E, size_t row_bytes, const int32_t* cnt,
+                      const int32_t* soff, const int32_t* roff, const int32_t* G,
+                      const int32_t* eoff, const uint8_t* y, uint8_t* comb_send)
+{
+    orc_combine_send_range(N, E, row_bytes, cnt, soff, roff, G, eoff, y, comb_send, 0, E);
+}
+
 /* Combine transfer: the reverse of orc_transfer.  The rows rank d holds for
  * sender s (receive rows G[d] + roff[d][s] ...) return to sender s's buffer at
  * rows s*T*K + soff[s][dL] ..., i.e. where s packed them. */
-void orc_combine_transfer(int N, int E, int T, int K, size_t row_bytes, const int32_t* soff,
-                          const int32_t* roff, const int32_t* G, const uint8_t* comb_send,
-                          uint8_t* comb_recv)
+void orc_combine_transfer_range(int N, int E, int T, int K, size_t row_bytes,
+                                const int32_t* soff, const int32_t* roff, const int32_t* G,
+                                const uint8_t* comb_send, uint8_t* comb_recv, int d0, int d1)
 {
     int L = E / N;
     size_t TK = (size_t)T * K;
-    for (int d = 0; d < N; ++d)
+    for (int d = d0; d < d1; ++d)
         for (int s = 0; s < N; ++s) {
             int32_t first = soff[(size_t)s * (E + 1) + d * L];
             int32_t n = soff[(size_t)s * (E + 1) + (d + 1) * L] - first;
@@ -439,6 +472,13 @@ void orc_combine_transfer(int N, int E, int T, int K, size_t row_bytes, const in
             size_t dst = (size_t)s * TK + first;
             memcpy(comb_recv + dst * row_bytes, comb_send + src * row_bytes, row_bytes * (size_t)n);
         }
+}
+
+void orc_combine_transfer(int N, int E, int T, int K, size_t row_bytes, const int32_t* soff,
+                          const int32_t* roff, const int32_t* G, const uint8_t* comb_send,
+                          uint8_t* comb_recv)
+{
+    orc_combine_transfer_range(N, E, T, K, row_bytes, soff, roff, G, comb_send, comb_recv, 0, N);
 }
 
 /* Combine receive: the router-weighted sum of the K expert outputs of every
@@ -503,6 +543,22 @@ void orc_combine_token(int K, int H, const uint16_t* const* rows, const float* w
     }
 }
 
+/* Many tokens of the same combine, for whole-workload checks where the
+ * returned rows sit in one array: token i's k-th returned row is row
+ * rows[i*K + k] of y ([*][H]), its weights w[i*K ...]; out[i] is
+ * orc_combine_token of those rows. */
+void orc_combine_tokens(int64_t n, int K, int H, const int64_t* rows, const float* w,
+                        const uint16_t* y, uint16_t* out)
+{
+    const uint16_t** r = (const uint16_t**)malloc(sizeof(*r) * (size_t)K);
+    for (int64_t i = 0; i < n; ++i) {
+        for (int k = 0; k < K; ++k)
+            r[k] = y + (size_t)rows[i * K + k] * H;
+        orc_combine_token(K, H, r, w + i * K, out + (size_t)i * H);
+    }
+    free(r);
+}
+
 /* ------------------------------------------------ array forms of the codecs */
 
 void orc_f32_to_bf16_n(size_t n, const float* in, uint16_t* out)
@@ -533,10 +589,12 @@ void orc_send_meta(int N, int T, int K, const int32_t* pos, int32_t* send_meta)
 /* The expert-order row that (s,t,k) lands in (the shuffle's destination):
  * expert e = idx[s][t][k] starts at eoff[e]; the rows of e from senders
  * s' < s come first; then s's own rows of e in its send order. */
-void orc_expert_rows(int N, int T, int K, int E, const int32_t* idx, const int32_t* cnt,
-                     const int32_t* soff, const int32_t* pos, const int32_t* eoff, int32_t* rows)
+void orc_expert_rows_range(int N, int T, int K, int E, const int32_t* idx, const int32_t* cnt,
+                           const int32_t* soff, const int32_t* pos, const int32_t* eoff,
+                           int32_t* rows, int s0, int s1)
 {
-    for (int s = 0; s < N; ++s)
+    (void)N;
+    for (int s = s0; s < s1; ++s)
         for (int t = 0; t < T; ++t)
             for (int k = 0; k < K; ++k) {
                 size_t i = ((size_t)s * T + t) * K + k;
@@ -546,6 +604,12 @@ void orc_expert_rows(int N, int T, int K, int E, const int32_t* idx, const int32
                     before += cnt[(size_t)s2 * E + e];
                 rows[i] = eoff[e] + before + pos[i] - soff[(size_t)s * (E + 1) + e];
             }
+}
+
+void orc_expert_rows(int N, int T, int K, int E, const int32_t* idx, const int32_t* cnt,
+                     const int32_t* soff, const int32_t* pos, const int32_t* eoff, int32_t* rows)
+{
+    orc_expert_rows_range(N, T, K, E, idx, cnt, soff, pos, eoff, rows, 0, N);
 }
 
 /* ------------------------------------------------ fixed-slot receive layout */
@@ -644,11 +708,12 @@ void orc_shuffle_slots(int N, int E, int T_max, size_t row_bytes, size_t scale_b
  * Token-owner rows ("partial receive", like the send layout): sender s's rows
  * start at sum_{s'<s} sum_d pc[s'][d]; inside, d ascending, then t.
  */
-void orc_partial_counts(int N, int T, int K, int E, const int32_t* idx, int32_t* pc)
+void orc_partial_counts_range(int N, int T, int K, int E, const int32_t* idx, int32_t* pc,
+                              int s0, int s1)
 {
     int L = E / N;
-    memset(pc, 0, sizeof(int32_t) * (size_t)N * N);
-    for (int s = 0; s < N; ++s)
+    memset(pc + (size_t)s0 * N, 0, sizeof(int32_t) * (size_t)(s1 - s0) * N);
+    for (int s = s0; s < s1; ++s)
         for (int t = 0; t < T; ++t)
             for (int d = 0; d < N; ++d) {
                 int v = 0;
@@ -659,14 +724,19 @@ void orc_partial_counts(int N, int T, int K, int E, const int32_t* idx, int32_t*
             }
 }
 
+void orc_partial_counts(int N, int T, int K, int E, const int32_t* idx, int32_t* pc)
+{
+    orc_partial_counts_range(N, T, K, E, idx, pc, 0, N);
+}
+
 /* Row of partial (s,t,d) in the owner-side and token-owner-side layouts, for
  * every (s,t,d) visited (-1 elsewhere); arrays [N][T][N].  The owner-side
  * rows are ordered by (d, s, t): the rows before (d, s) are a running count of
  * pc taken in (d, s) order.  The token-side rows are ordered by (s, d, t):
  * a running count of pc in (s, d) order.  Inside a (d, s) pair, tokens in
  * order (the running rank of the pair). */
-void orc_partial_rows(int N, int T, int K, int E, const int32_t* idx, const int32_t* pc,
-                      int32_t* owner_row, int32_t* token_row)
+void orc_partial_rows_range(int N, int T, int K, int E, const int32_t* idx, const int32_t* pc,
+                            int32_t* owner_row, int32_t* token_row, int s0, int s1)
 {
     int L = E / N;
     int32_t* obase = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * N);  /* [d][s] */
@@ -684,7 +754,7 @@ void orc_partial_rows(int N, int T, int K, int E, const int32_t* idx, const int3
             tbase[(size_t)s * N + d] = run;
             run += pc[(size_t)s * N + d];
         }
-    for (int s = 0; s < N; ++s)
+    for (int s = s0; s < s1; ++s)
         for (int t = 0; t < T; ++t)
             for (int d = 0; d < N; ++d) {
                 size_t o = ((size_t)s * T + t) * N + d;
@@ -706,17 +776,23 @@ void orc_partial_rows(int N, int T, int K, int E, const int32_t* idx, const int3
     free(rank);
 }
 
+void orc_partial_rows(int N, int T, int K, int E, const int32_t* idx, const int32_t* pc,
+                      int32_t* owner_row, int32_t* token_row)
+{
+    orc_partial_rows_range(N, T, K, E, idx, pc, owner_row, token_row, 0, N);
+}
+
 /* The owner's partial sums: for every visited (s,t,d), the fp32 fma chain over
  * the token's k (ascending) whose expert lives on d, of w[s][t][k] times the
  * expert output row y[expert_rows[s][t][k]], rounded to bf16, written to the
  * owner-side row. */
-void orc_partial_send(int N, int T, int K, int E, int H, const int32_t* idx, const float* w,
-                      const int32_t* expert_rows, const uint16_t* y, const int32_t* owner_row,
-                      uint16_t* psend)
+void orc_partial_send_range(int N, int T, int K, int E, int H, const int32_t* idx,
+                            const float* w, const int32_t* expert_rows, const uint16_t* y,
+                            const int32_t* owner_row, uint16_t* psend, int s0, int s1)
 {
     int L = E / N;
     float* acc = (float*)malloc(sizeof(float) * (size_t)H);
-    for (int s = 0; s < N; ++s)
+    for (int s = s0; s < s1; ++s)
         for (int t = 0; t < T; ++t)
             for (int d = 0; d < N; ++d) {
                 int32_t row = owner_row[((size_t)s * T + t) * N + d];
@@ -738,22 +814,36 @@ void orc_partial_send(int N, int T, int K, int E, int H, const int32_t* idx, con
     free(acc);
 }
 
-/* The transfer of the partial rows back to each token's owner. */
-void orc_partial_transfer(int N, int T, int H, const int32_t* owner_row, const int32_t* token_row,
-                          const uint16_t* psend, uint16_t* precv)
+void orc_partial_send(int N, int T, int K, int E, int H, const int32_t* idx, const float* w,
+                      const int32_t* expert_rows, const uint16_t* y, const int32_t* owner_row,
+                      uint16_t* psend)
 {
-    for (size_t o = 0; o < (size_t)N * T * N; ++o)
+    orc_partial_send_range(N, T, K, E, H, idx, w, expert_rows, y, owner_row, psend, 0, N);
+}
+
+/* The transfer of the partial rows back to each token's owner. */
+void orc_partial_transfer_range(int N, int T, int H, const int32_t* owner_row,
+                                const int32_t* token_row, const uint16_t* psend,
+                                uint16_t* precv, int s0, int s1)
+{
+    for (size_t o = (size_t)s0 * T * N; o < (size_t)s1 * T * N; ++o)
         if (owner_row[o] >= 0)
             memcpy(precv + (size_t)token_row[o] * H, psend + (size_t)owner_row[o] * H,
                    sizeof(uint16_t) * H);
 }
 
+void orc_partial_transfer(int N, int T, int H, const int32_t* owner_row, const int32_t* token_row,
+                          const uint16_t* psend, uint16_t* precv)
+{
+    orc_partial_transfer_range(N, T, H, owner_row, token_row, psend, precv, 0, N);
+}
+
 /* The token owner's sum of its partial rows: fp32, destination rank
  * ascending, from +0, rounded once to bf16. */
-void orc_partial_recv(int N, int T, int H, const int32_t* token_row, const uint16_t* precv,
-                      uint16_t* out)
+void orc_partial_recv_range(int N, int T, int H, const int32_t* token_row,
+                            const uint16_t* precv, uint16_t* out, int s0, int s1)
 {
-    for (int s = 0; s < N; ++s)
+    for (int s = s0; s < s1; ++s)
         for (int t = 0; t < T; ++t)
             for (int h = 0; h < H; ++h) {
                 float acc = +0.0f;
@@ -764,6 +854,12 @@ void orc_partial_recv(int N, int T, int H, const int32_t* token_row, const uint1
                 }
                 out[((size_t)s * T + t) * H + h] = orc_f32_to_bf16(acc);
             }
+}
+
+void orc_partial_recv(int N, int T, int H, const int32_t* token_row, const uint16_t* precv,
+                      uint16_t* out)
+{
+    orc_partial_recv_range(N, T, H, token_row, precv, out, 0, N);
 }
 
 /* One token of the same combine, for checking single tokens of workloads too
@@ -795,4 +891,19 @@ void orc_partial_token(int K, int H, const uint16_t* const* rows, const float* w
         }
         out[h] = orc_f32_to_bf16(acc);
     }
+}
+
+/* orc_partial_token of many tokens: token i's k-th returned row is row
+ * rows[i*K + k] of y ([*][H]), its weight w[i*K + k] and destination rank
+ * rank[i*K + k]. */
+void orc_partial_tokens(int64_t n, int K, int H, const int64_t* rows, const float* w,
+                        const int32_t* rank, const uint16_t* y, uint16_t* out)
+{
+    const uint16_t** r = (const uint16_t**)malloc(sizeof(*r) * (size_t)K);
+    for (int64_t i = 0; i < n; ++i) {
+        for (int k = 0; k < K; ++k)
+            r[k] = y + (size_t)rows[i * K + k] * H;
+        orc_partial_token(K, H, r, w + i * K, rank + i * K, out + (size_t)i * H);
+    }
+    free(r);
 }

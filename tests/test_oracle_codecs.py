@@ -204,3 +204,12 @@ def test_quant_row_fp8_small_amax_regime_by_hand():
     assert np.all(q[3:128] == 0)
     assert q[128:131].tolist() == [0x04, 0x84, 0x0C]
     assert np.all(q[131:] == 0)
+
+
+def test_quant_rows_fp8_is_the_row_form_per_row():
+    from workloads import fp8_exponent_sweep
+    x = fp8_exponent_sweep()[:448].reshape(8, 7168)
+    q, sc = oracle.quant_rows_fp8(x)
+    for i in range(8):
+        q1, s1 = oracle.quant_row_fp8(x[i])
+        assert np.array_equal(q[i], q1) and np.array_equal(sc[i].view(np.uint32), s1.view(np.uint32))

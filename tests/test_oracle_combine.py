@@ -134,3 +134,17 @@ def test_hand_worked_combine():
     out = oracle.run_combine(y, w, pl, H)["out"]
     got = (out.astype(np.uint32) << 16).view(np.float32)[:, :, 0]
     assert got.tolist() == g["combine"]["out"]
+
+
+@pytest.mark.parametrize("key", ["A", "B"])
+def test_combine_tokens_matches_full_combine(key):
+    """The many-token form (returned rows indexed in the expert-order output
+    y) gives every token of the whole-batch combine (pinned above)."""
+    cfg = CONFIGS[key].with_(T=24)
+    inp = make_inputs(cfg)
+    d = oracle.run_dispatch(inp["x"], inp["idx"], cfg.E)
+    y = oracle.expert_standin(d["expert_x"], None, d["eoff"], cfg.H)
+    c = oracle.run_combine(y, inp["w"], d, cfg.H)
+    rows = oracle.expert_rows(inp["idx"], d).reshape(-1, cfg.K)
+    got = oracle.combine_tokens(y, rows, inp["w"].reshape(-1, cfg.K))
+    assert np.array_equal(got, c["out"].reshape(-1, cfg.H))

@@ -167,3 +167,17 @@ def test_hand_worked_partial_example():
     assert f(res["psend"]) == gp["owner_layout_values"]
     assert f(res["precv"]) == gp["token_layout_values"]
     assert f32_from_bf16_bits(res["out"])[:, :, 0].tolist() == gp["out"]
+
+
+@pytest.mark.parametrize("key", ["A", "C"])
+def test_partial_tokens_matches_the_batch(key):
+    """The many-token form gives every token of the whole-batch partial
+    combine (pinned above)."""
+    cfg = CONFIGS[key].with_(T=12)
+    inp = make_inputs(cfg)
+    d, y = _dispatch(cfg, inp)
+    out = oracle.run_partial_combine(y, inp["w"], inp["idx"], d, cfg.H)["out"]
+    rows = oracle.expert_rows(inp["idx"], d).reshape(-1, cfg.K)
+    got = oracle.partial_tokens(y, rows, inp["w"].reshape(-1, cfg.K),
+                                (inp["idx"] // cfg.L).reshape(-1, cfg.K))
+    assert np.array_equal(got, out.reshape(-1, cfg.H))
