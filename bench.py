@@ -9,11 +9,18 @@ stand-in y = x*(e+1) of the first cycle) is computed once before timing and
 reused, since the routing is the same every step.  Inputs are resident in HBM
 before the timed region.
 
+Timing protocol: `warmup` untimed steps; then `steps` steps back to back
+under a wall clock (the warm figure, reported beside the headline); then the
+timed region, `steps` steps each started with the MALL flushed (a 512 MB
+buffer written first) and bracketed by events: `value` is the median of those
+per-step times (µs), with p10 / p90 beside it.
+
 Prints one JSON line.  Kernel durations come from HIP events the library
 attaches to the kernel dispatches: every kernel in an untimed pass (the
 `kernels` table, which picks the dominant kernel), then only the dominant
 kernel during the timed steps (its `roofline` entry), since each timed kernel
-adds a few microseconds of gap to the step.
+adds a few microseconds of gap to the step.  The CPU baseline is the oracle
+on the same workload, single-threaded and split over the host's cores.
 """
 from __future__ import annotations
 
@@ -464,41 +471,90 @@ def step_distribution(torch, step, stream, n: int, flush_bytes: int = 0) -> dict
     return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "n": n}
 
 
-def cpu_baseline(cfg, inp, min_seconds: float, combine: str = "receiver") -> dict:
-    """The oracle, unchanged and single-threaded, on the same workload: whole
-    dispatch + combine steps until min_seconds of work (at least one)."""
-    import numpy as np
+def host_cpu() -> dict:
+    """The host's CPU as lscpu and the scheduler report it."""
+    import subprocess
+    info = {"logical_cpus": os.cpu_count(), "cpus_in_affinity": len(os.sched_getaffinity(0))}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k in ("Model name", "Vendor ID", "CPU family", "Model", "Socket(s)",
+                     "Core(s) per socket", "Thread(s) per core", "CPU max MHz", "L3 cache"):
+                info[k.lower().replace("(s)", "s").replace(" ", "_")] = v
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if "model_name" not in info:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        info["model_name"] = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    return info
+
+
+# host threads for the oracle's threaded leg: the cores this process may use,
+# at most 16 (one GPU's share of the host)
+CPU_THREADS_MAX = 16
+
+
+def cpu_baseline(cfg, inp, min_seconds: float, combine: str, step_bytes: int) -> dict:
+    """The oracle, unchanged, on the same workload: whole dispatch + combine
+    steps until min_seconds of work (at least one), single-threaded, then the
+    same with each stage split over P threads by logical rank (or expert)
+    ranges, P = the cores this process may use, at most 16.  Both legs report
+    µs per step and the effective GB/s of the step's algorithmic bytes."""
+    from concurrent.futures import ThreadPoolExecutor
 
     import oracle
-    d0 = oracle.run_dispatch(inp["x"], inp["idx"], cfg.E, fp8=cfg.dtype == "fp8")
+    fp8 = cfg.dtype == "fp8"
+    d0 = oracle.run_dispatch(inp["x"], inp["idx"], cfg.E, fp8=fp8)
     y = oracle.expert_standin(d0["expert_x"], d0["expert_scale"], d0["eoff"], cfg.H)
     del d0
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        d = oracle.run_dispatch(inp["x"], inp["idx"], cfg.E, fp8=cfg.dtype == "fp8")
+
+    def one(dispatch, combine_fn, partial_fn):
+        d = dispatch()
         if combine == "partial":
-            c = oracle.run_partial_combine(y, inp["w"], inp["idx"], d, cfg.H)
+            partial_fn(d)
         else:
-            c = oracle.run_combine(y, inp["w"], d, cfg.H)
-        steps += 1
-        del d, c
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
-    assert isinstance(y, np.ndarray)
-    model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {"value": round(el / steps * 1e6, 1), "unit": "us per dispatch+combine", "cores": 1,
-            "kind": "oracle", "cpu_model": model,
-            "sample": f"{steps} full dispatch+combine step(s) of the {cfg.name} workload "
-                      f"({cfg.N}x{cfg.T} tokens, {combine} combine), single thread, {el:.1f} s"}
+            combine_fn(d)
+
+    def timed(run, budget):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            run()
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return steps, el
+
+    n1, el1 = timed(lambda: one(
+        lambda: oracle.run_dispatch(inp["x"], inp["idx"], cfg.E, fp8=fp8),
+        lambda d: oracle.run_combine(y, inp["w"], d, cfg.H),
+        lambda d: oracle.run_partial_combine(y, inp["w"], inp["idx"], d, cfg.H)), min_seconds)
+    P = max(1, min(CPU_THREADS_MAX, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(P) as pool:
+        nP, elP = timed(lambda: one(
+            lambda: oracle.run_dispatch_threads(inp["x"], inp["idx"], cfg.E, P, fp8=fp8,
+                                                pool=pool),
+            lambda d: oracle.run_combine_threads(y, inp["w"], d, cfg.H, P, pool=pool),
+            lambda d: oracle.run_partial_combine_threads(y, inp["w"], inp["idx"], d, cfg.H, P,
+                                                         pool=pool)), min_seconds / 2)
+    us1, usP = el1 / n1 * 1e6, elP / nP * 1e6
+    cpu = host_cpu()
+    return {"value": round(us1, 1), "unit": "us per dispatch+combine", "cores": 1,
+            "kind": "oracle", "gbps_eff": round(step_bytes / (us1 * 1e-6) / 1e9, 3),
+            "cpu_model": cpu.get("model_name", "unknown"), "host": cpu,
+            "sample": f"{n1} full dispatch+combine step(s) of the {cfg.name} workload "
+                      f"({cfg.N}x{cfg.T} tokens, {combine} combine), single thread, {el1:.1f} s",
+            "threaded": {"value": round(usP, 1), "unit": "us per dispatch+combine", "cores": P,
+                         "gbps_eff": round(step_bytes / (usP * 1e-6) / 1e9, 3),
+                         "sample": f"{nP} step(s), each stage split over {P} threads by "
+                                   f"logical-rank (or expert) ranges, {elP:.1f} s"}}
 
 
 def main() -> int:
@@ -629,29 +685,40 @@ def main() -> int:
     for _ in range(max(10, args.warmup)):
         step()
     timing_all = mep.moe_group_timing_read(g)
+    mep.moe_group_timing_enable(g, False)
     dom = max((k for k in timing_all if timing_all[k][1]), key=lambda k: timing_all[k][0])
-    # timed region: only the dominant kernel carries events (a few us per timed
-    # kernel), so its duration is measured live over exactly these steps
-    mep.moe_group_timing_enable(g, [dom])
+    # warm leg, beside the headline: the steps back to back, wall clock, no
+    # kernel carrying events
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    # timed region (the headline): each step starts with the MALL flushed (a
+    # 512 MB buffer written first) and is bracketed by events; value = the
+    # median step.  Only the dominant kernel carries its own events (a few us
+    # per timed kernel), so its duration is measured live over exactly these
+    # steps
+    flush = 512 << 20
+    mep.moe_group_timing_enable(g, [dom])
+    torch.cuda.synchronize()
     t1 = time.perf_counter()
+    cold = step_distribution(torch, step, stream, args.steps, flush_bytes=flush)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
     timing_dom = mep.moe_group_timing_read(g)
     mep.moe_group_timing_enable(g, False)
     if args.no_kernel_timing:
-        t2 = time.perf_counter()
+        t3 = time.perf_counter()
         for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
-        print(json.dumps({"us_per_step_without_events": round((time.perf_counter() - t2) / args.steps * 1e6, 1)}),
+        print(json.dumps({"us_per_step_without_events": round((time.perf_counter() - t3) / args.steps * 1e6, 1)}),
               file=sys.stderr, flush=True)
-    # per-step distribution, warm and with the MALL flushed before each step
-    dist = {"warm": step_distribution(torch, step, stream, args.steps),
-            "cold": step_distribution(torch, step, stream, args.steps, flush_bytes=512 << 20),
-            "flush_bytes": 512 << 20}
+    dist = {"cold": cold, "warm": step_distribution(torch, step, stream, args.steps),
+            "flush_bytes": flush,
+            "cold_wall_ms_per_step_with_flush": round((t2 - t1) / args.steps * 1e3, 4)}
     graph_rec = None
     if args.graph:
         # the four calls of one step captured as a HIP graph, then replayed:
@@ -684,7 +751,7 @@ def main() -> int:
     ceiling = {"at_kernel_footprint": hbm_ceiling(torch, mep, kb_dom // 2),
                "at_1gib": hbm_ceiling(torch, mep, 1 << 30)}
 
-    ms_per_step = (t1 - t0) / args.steps * 1e3
+    ms_per_step = cold["p50"] * 1e-3
     P = partial_rows(cfg, inp["idx"]) if partial else 0
     kb = kernel_bytes(cfg, args.transport, args.combine, P)
     total_bytes = sum(kb.values())
@@ -719,8 +786,13 @@ def main() -> int:
                    "transport": args.transport, "combine": args.combine, "layout": args.layout,
                    **({"partial_rows": P} if partial else {}),
                    "parallelism": f"ep{N} (logical ranks on one GPU)"},
+        "timing": "value = median of the timed steps, each started with the MALL flushed",
         "hbm_gbps_eff": round(gbps_eff, 1),
         "frac_of_hbm_peak": round(gbps_eff / HBM_PEAK_GBPS, 4),
+        "warm": {"us_per_step": round(warm_ms * 1e3, 1),
+                 "hbm_gbps_eff": round(total_bytes / (warm_ms * 1e-3) / 1e9, 1),
+                 "frac_of_hbm_peak": round(total_bytes / (warm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                 "how": "wall clock over the same number of steps back to back, no flush"},
         "algorithmic_bytes_per_step": total_bytes,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
@@ -737,7 +809,7 @@ def main() -> int:
         rec["graph"] = graph_rec
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.combine)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, args.combine, total_bytes)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -121,7 +121,7 @@ def test_parity_edge_shapes(transport):
     assert gpu["expert_offsets"].tolist() == [0] * (cfg.E + 1)
 
 
-@pytest.mark.parametrize("key", ["A", "B", "C"])
+@pytest.mark.parametrize("key", ["A", "B", "C", "E", "Ep"])
 def test_identity_experts_return_input(key):
     cfg = CONFIGS[key]
     say(f"[gpu] identity {cfg.describe()}")
