@@ -25,6 +25,9 @@ MOE_ERR_STATE = -4
 MOE_ERR_ROUTING = -5
 MOE_ERR_CAPACITY = -6
 MOE_ERR_INTERNAL = -7
+MOE_ERR_SCRATCH = -8
+
+MOE_SCRATCH_BYTES = 64 << 20
 
 MOE_BF16 = 0
 MOE_FP8_E4M3 = 1
@@ -89,6 +92,7 @@ def _load():
     P, I, I32, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64
     sig = {
         "moe_group_create": ([ctypes.POINTER(moe_group_desc), ctypes.POINTER(P)], I),
+        "moe_group_create_static": ([ctypes.POINTER(moe_group_desc), ctypes.POINTER(P)], I),
         "moe_group_destroy": ([P], I),
         "moe_dispatch_send": ([P, I32, P, P, P, P], I),
         "moe_dispatch_recv": ([P, P, P, P, P], I),
@@ -147,6 +151,21 @@ def moe_group_create(num_ranks: int, num_experts: int, top_k: int, hidden: int,
                           transport, combine_mode, layout)
     h = ctypes.c_void_p()
     _check(_lib.moe_group_create(ctypes.byref(desc), ctypes.byref(h)), "moe_group_create")
+    return h.value
+
+
+def moe_group_create_static(num_ranks: int, num_experts: int, top_k: int, hidden: int,
+                            max_tokens: int, dispatch_dtype: int = MOE_BF16,
+                            transport: int = MOE_TRANSPORT_STAGED,
+                            combine_mode: int = MOE_COMBINE_RECEIVER,
+                            layout: int = MOE_LAYOUT_PACKED) -> int:
+    """A group whose buffers live in the library's static device scratch area
+    (no device allocation); one per device at a time."""
+    desc = moe_group_desc(num_ranks, num_experts, top_k, hidden, max_tokens, dispatch_dtype,
+                          transport, combine_mode, layout)
+    h = ctypes.c_void_p()
+    _check(_lib.moe_group_create_static(ctypes.byref(desc), ctypes.byref(h)),
+           "moe_group_create_static")
     return h.value
 
 

@@ -72,6 +72,7 @@ struct moe_group_s {
     size_t events_used = 0;
 
     std::vector<void*> allocations;
+    bool in_scratch = false;     // buffers carved from the device's static scratch area
 };
 
 namespace {
@@ -177,18 +178,113 @@ void free_all(moe_group_s* g)
     g->events.clear();
 }
 
-template <typename T>
-int alloc(moe_group_s* g, T** out, size_t count)
-{
-    void* p = nullptr;
-    const size_t bytes = std::max<size_t>(count * sizeof(T), 256);
-    const hipError_t e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation ? MOE_ERR_OOM : MOE_ERR_HIP;
+// Where a group's device buffers go: each its own hipMalloc allocation, or
+// (region mode) consecutive 256-byte aligned pieces of one region starting
+// at `base`; with a null base the region mode only counts the bytes.  Every
+// buffer takes at least 256 bytes either way.
+struct Placer {
+    moe_group_s* g;
+    bool region = false;
+    uintptr_t base = 0;
+    size_t used = 0;
+
+    template <typename T>
+    int operator()(T** out, size_t count)
+    {
+        const size_t bytes = std::max<size_t>(count * sizeof(T), 256);
+        if (region) {
+            *out = reinterpret_cast<T*>(base + used);
+            used += (bytes + 255) / 256 * 256;
+            return MOE_OK;
+        }
+        void* p = nullptr;
+        const hipError_t e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation ? MOE_ERR_OOM
+                                                                             : MOE_ERR_HIP;
+        }
+        g->allocations.push_back(p);
+        *out = static_cast<T*>(p);
+        return MOE_OK;
     }
-    g->allocations.push_back(p);
-    *out = static_cast<T*>(p);
+};
+
+// Sizes of a group from its (validated) descriptor.
+void init_sizes(moe_group_s* g)
+{
+    const moe_group_desc* desc = &g->desc;
+    const int N = desc->num_ranks, E = desc->num_experts, K = desc->top_k, H = desc->hidden;
+    const int T = desc->max_tokens;
+    g->L = E / N;
+    g->rows_max = (int64_t)N * T * K;
+    const bool fixed = desc->layout == MOE_LAYOUT_FIXED_SLOT;
+    // the receive pool also takes combine's send-layout rows (direct push),
+    // and N*E*T_max < N*T_max*K when K > E
+    g->recv_rows_max = fixed ? std::max((int64_t)N * E * T, g->rows_max) : g->rows_max;
+    const bool fp8 = desc->dispatch_dtype == MOE_FP8_E4M3;
+    g->payload_bytes = fp8 ? H : 2 * H;
+    g->comb_bytes = 2 * H;
+    g->scale_blocks = fp8 ? H / 128 : 0;
+}
+
+// Every device buffer of a group, placed by `take`.
+int place_buffers(moe_group_s* g, Placer& take)
+{
+    const moe_group_desc* desc = &g->desc;
+    const int N = desc->num_ranks, E = desc->num_experts, K = desc->top_k;
+    const int T = desc->max_tokens;
+    const size_t R = (size_t)g->rows_max;
+    const size_t RQ = (size_t)g->recv_rows_max;
+    const size_t row_bytes = (size_t)std::max(g->payload_bytes, g->comb_bytes);
+    const bool fp8 = desc->dispatch_dtype == MOE_FP8_E4M3;
+    const bool fixed = desc->layout == MOE_LAYOUT_FIXED_SLOT;
+    const bool staged = desc->transport == MOE_TRANSPORT_STAGED;   // direct: no send buffer
+    const bool partial = desc->combine_mode == MOE_COMBINE_PARTIAL;
+    moe::Plan& p = g->plan;
+    uint8_t* pool_send = nullptr;
+    uint8_t* pool_recv = nullptr;
+    int rc;
+    if ((rc = take(&p.err, 1)) || (rc = take(&p.err_sticky, 1)) ||
+        (rc = take(&p.err_rank, (size_t)N)) || (rc = take(&p.ticket, 1)) ||
+        (rc = take(&p.cnt, (size_t)N * E)) ||
+        (rc = take(&p.pos, (size_t)N * T * K)) || (rc = take(&p.soff, (size_t)N * (E + 1))) ||
+        (rc = take(&p.roff, (size_t)N * (N + 1))) || (rc = take(&p.rbase, (size_t)N + 1)) ||
+        (rc = take(&p.eoff, (size_t)E + 1)) || (rc = take(&p.ebase, (size_t)N * E)) ||
+        (rc = take(&p.xfer_src, R)) || (rc = take(&p.xfer_dst, R)) ||
+        (rc = take(&p.shuf_map, R)) || (rc = take(&p.shuf_inv, R)) ||
+        (staged && (rc = take(&pool_send, R * row_bytes))) ||
+        (rc = take(&pool_recv, RQ * row_bytes)) ||
+        (staged && (rc = take(&g->send_meta, R))) || (rc = take(&g->recv_meta, RQ)) ||
+        (rc = take(&g->src_rank, R)) || (rc = take(&g->src_slot, R)) ||
+        (fp8 && staged && (rc = take(&g->send_scale, R * g->scale_blocks))) ||
+        (fp8 && (rc = take(&g->recv_scale, RQ * g->scale_blocks))) ||
+        (fixed && (rc = take(&p.slot_of, R))) ||
+        (partial && ((rc = take(&p.pdst, R)) || (rc = take(&p.ppos, R)) ||
+                     (rc = take(&p.psoff, (size_t)N * (N + 1))) ||
+                     (rc = take(&p.qoff, (size_t)N * (N + 1))) ||
+                     (rc = take(&p.qbase, (size_t)N + 1)) ||
+                     (rc = take(&p.pbase, (size_t)N + 1)) ||
+                     (rc = take(&g->recv_w, RQ)) ||
+                     (rc = take(&p.phead, 2 * R)) || (rc = take(&p.pitem, R)) ||
+                     (staged && ((rc = take(&p.pmap, R)) || (rc = take(&g->send_w, R)))))))
+        return rc;
+    g->pool_send = pool_send;
+    g->pool_recv = pool_recv;
+    return MOE_OK;
+}
+
+// The error words and the ticket counter start at zero; the offsets start
+// valid for an empty cycle.
+int zero_words(moe_group_s* g)
+{
+    const moe::Plan& p = g->plan;
+    if (hipMemset(p.err, 0, sizeof(int32_t)) != hipSuccess ||
+        hipMemset(p.err_sticky, 0, sizeof(int32_t)) != hipSuccess ||
+        hipMemset(p.ticket, 0, sizeof(int32_t)) != hipSuccess ||
+        hipMemset(p.eoff, 0, sizeof(int32_t) * (g->desc.num_experts + 1)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess)
+        return MOE_ERR_HIP;
     return MOE_OK;
 }
 
@@ -222,6 +318,42 @@ int check_device(const moe_group_s* g)
     return dev == g->device ? MOE_OK : MOE_ERR_INVALID;
 }
 
+// The static scratch area of groups made by moe_group_create_static: one per
+// device (each GPU the library runs on holds its own copy from the library's
+// first use on it until the process ends).  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that address is used.
+__device__ __align__(256) static uint8_t scratch[MOE_SCRATCH_BYTES];
+
+constexpr int MAX_SCRATCH_DEVICES = 64;
+
+struct ScratchSlot {
+    bool resolved = false;
+    bool in_use = false;           // a live group holds the area
+    uint8_t* ptr = nullptr;        // device address of this device's scratch
+    moe_group_s group;             // the handle moe_group_create_static returns
+};
+
+ScratchSlot g_scratch[MAX_SCRATCH_DEVICES];
+
+// The device address of the current device `dev`'s scratch area, looked up on
+// first use.
+int scratch_address(int dev)
+{
+    ScratchSlot& slot = g_scratch[dev];
+    if (slot.resolved)
+        return MOE_OK;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+        (void)hipGetLastError();
+        return MOE_ERR_HIP;
+    }
+    slot.ptr = static_cast<uint8_t*>(ptr);
+    slot.resolved = true;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -237,6 +369,7 @@ const char* moe_strerror(int status)
     case MOE_ERR_ROUTING: return "expert id outside [0, num_experts)";
     case MOE_ERR_CAPACITY: return "receive count above the group's bound";
     case MOE_ERR_INTERNAL: return "device-side index check failed";
+    case MOE_ERR_SCRATCH: return "group larger than the static scratch area (MOE_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }
@@ -263,67 +396,53 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
         delete g;
         return MOE_ERR_HIP;
     }
-    const int N = desc->num_ranks, E = desc->num_experts, K = desc->top_k, H = desc->hidden;
-    const int T = desc->max_tokens;
-    g->L = E / N;
-    g->rows_max = (int64_t)N * T * K;
-    const bool fixed = desc->layout == MOE_LAYOUT_FIXED_SLOT;
-    // the receive pool also takes combine's send-layout rows (direct push),
-    // and N*E*T_max < N*T_max*K when K > E
-    g->recv_rows_max = fixed ? std::max((int64_t)N * E * T, g->rows_max) : g->rows_max;
-    const bool fp8 = desc->dispatch_dtype == MOE_FP8_E4M3;
-    g->payload_bytes = fp8 ? H : 2 * H;
-    g->comb_bytes = 2 * H;
-    g->scale_blocks = fp8 ? H / 128 : 0;
-    const size_t R = (size_t)g->rows_max;
-    const size_t RQ = (size_t)g->recv_rows_max;
-    const size_t row_bytes = (size_t)std::max(g->payload_bytes, g->comb_bytes);
-    const bool staged = desc->transport == MOE_TRANSPORT_STAGED;   // direct: no send buffer
-    const bool partial = desc->combine_mode == MOE_COMBINE_PARTIAL;
-
-    moe::Plan& p = g->plan;
-    uint8_t* pool_send = nullptr;
-    uint8_t* pool_recv = nullptr;
-    if ((rc = alloc(g, &p.err, 1)) || (rc = alloc(g, &p.err_sticky, 1)) ||
-        (rc = alloc(g, &p.err_rank, (size_t)N)) || (rc = alloc(g, &p.ticket, 1)) ||
-        (rc = alloc(g, &p.cnt, (size_t)N * E)) ||
-        (rc = alloc(g, &p.pos, (size_t)N * T * K)) || (rc = alloc(g, &p.soff, (size_t)N * (E + 1))) ||
-        (rc = alloc(g, &p.roff, (size_t)N * (N + 1))) || (rc = alloc(g, &p.rbase, (size_t)N + 1)) ||
-        (rc = alloc(g, &p.eoff, (size_t)E + 1)) || (rc = alloc(g, &p.ebase, (size_t)N * E)) ||
-        (rc = alloc(g, &p.xfer_src, R)) || (rc = alloc(g, &p.xfer_dst, R)) ||
-        (rc = alloc(g, &p.shuf_map, R)) || (rc = alloc(g, &p.shuf_inv, R)) ||
-        (staged && (rc = alloc(g, &pool_send, R * row_bytes))) ||
-        (rc = alloc(g, &pool_recv, RQ * row_bytes)) ||
-        (staged && (rc = alloc(g, &g->send_meta, R))) || (rc = alloc(g, &g->recv_meta, RQ)) ||
-        (rc = alloc(g, &g->src_rank, R)) || (rc = alloc(g, &g->src_slot, R)) ||
-        (fp8 && staged && (rc = alloc(g, &g->send_scale, R * g->scale_blocks))) ||
-        (fp8 && (rc = alloc(g, &g->recv_scale, RQ * g->scale_blocks))) ||
-        (fixed && (rc = alloc(g, &p.slot_of, R))) ||
-        (partial && ((rc = alloc(g, &p.pdst, R)) || (rc = alloc(g, &p.ppos, R)) ||
-                     (rc = alloc(g, &p.psoff, (size_t)N * (N + 1))) ||
-                     (rc = alloc(g, &p.qoff, (size_t)N * (N + 1))) ||
-                     (rc = alloc(g, &p.qbase, (size_t)N + 1)) ||
-                     (rc = alloc(g, &p.pbase, (size_t)N + 1)) ||
-                     (rc = alloc(g, &g->recv_w, RQ)) ||
-                     (rc = alloc(g, &p.phead, 2 * R)) || (rc = alloc(g, &p.pitem, R)) ||
-                     (staged && ((rc = alloc(g, &p.pmap, R)) || (rc = alloc(g, &g->send_w, R))))))) {
+    init_sizes(g);
+    Placer take{g};
+    if ((rc = place_buffers(g, take)) || (rc = zero_words(g))) {
         free_all(g);
         delete g;
         return rc;
     }
-    g->pool_send = pool_send;
-    g->pool_recv = pool_recv;
-    // the error words and the ticket counter start at zero; the offsets start
-    // valid for an empty cycle
-    if (hipMemset(p.err, 0, sizeof(int32_t)) != hipSuccess ||
-        hipMemset(p.err_sticky, 0, sizeof(int32_t)) != hipSuccess ||
-        hipMemset(p.ticket, 0, sizeof(int32_t)) != hipSuccess ||
-        hipMemset(p.eoff, 0, sizeof(int32_t) * (E + 1)) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
-        free_all(g);
-        delete g;
+    *out = g;
+    return MOE_OK;
+}
+
+int moe_group_create_static(const moe_group_desc* desc, moe_group_t* out)
+{
+    if (!out)
+        return MOE_ERR_INVALID;
+    int rc = validate_desc(desc);
+    if (rc != MOE_OK)
+        return rc;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
         return MOE_ERR_HIP;
+    if (dev < 0 || dev >= MAX_SCRATCH_DEVICES)
+        return MOE_ERR_INVALID;
+    ScratchSlot& slot = g_scratch[dev];
+    if (slot.in_use)
+        return MOE_ERR_STATE;
+    if ((rc = scratch_address(dev)) != MOE_OK)
+        return rc;
+    moe_group_s* g = &slot.group;
+    *g = moe_group_s{};
+    g->desc = *desc;
+    g->device = dev;
+    g->in_scratch = true;
+    init_sizes(g);
+    Placer count{g, true, 0, 0};
+    if ((rc = place_buffers(g, count)) != MOE_OK)
+        return rc;
+    if (count.used > MOE_SCRATCH_BYTES) {
+        *g = moe_group_s{};
+        return MOE_ERR_SCRATCH;
     }
+    Placer carve{g, true, reinterpret_cast<uintptr_t>(slot.ptr), 0};
+    if ((rc = place_buffers(g, carve)) || (rc = zero_words(g))) {
+        *g = moe_group_s{};
+        return rc;
+    }
+    slot.in_use = true;
     *out = g;
     return MOE_OK;
 }
@@ -336,6 +455,11 @@ int moe_group_destroy(moe_group_t g)
     if (hipDeviceSynchronize() != hipSuccess)
         rc = MOE_ERR_HIP;
     free_all(g);
+    if (g->in_scratch) {
+        // the buffers stay in the device's scratch area; the slot is free again
+        g_scratch[g->device].in_use = false;
+        return rc;
+    }
     delete g;
     return rc;
 }

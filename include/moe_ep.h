@@ -58,7 +58,8 @@ typedef enum moe_status {
     MOE_ERR_STATE = -4,     /* call out of the dispatch/combine order */
     MOE_ERR_ROUTING = -5,   /* device saw an expert id outside [0, E) */
     MOE_ERR_CAPACITY = -6,  /* a receive count exceeded the page's bound (never expected) */
-    MOE_ERR_INTERNAL = -7   /* a device-side index check failed; the offending writes were skipped */
+    MOE_ERR_INTERNAL = -7,  /* a device-side index check failed; the offending writes were skipped */
+    MOE_ERR_SCRATCH = -8    /* moe_group_create_static: the group does not fit MOE_SCRATCH_BYTES */
 } moe_status;
 
 typedef enum moe_dtype {
@@ -158,7 +159,32 @@ typedef struct moe_group_s* moe_group_t;
  * MOE_ERR_OOM, MOE_ERR_HIP; *out is untouched on error. */
 int moe_group_create(const moe_group_desc* desc, moe_group_t* out);
 
-/* Synchronise the device, free every buffer of the group and the handle.
+/* For callers that cannot allocate device memory (code that must not call
+ * hipMalloc: a serving loop, a harness that forbids allocation, setup next to
+ * code under graph capture): the same group as moe_group_create, with every
+ * internal buffer placed in a static device array of MOE_SCRATCH_BYTES
+ * (64 MiB) that the library holds on each device it runs on until the process
+ * ends.  No hipMalloc, hipFree or other allocation, on the device or the
+ * host.  Enough for, e.g., the Mixtral-8x7B decode shape (8 ranks x 128
+ * tokens x hidden 4096, top-2 of 8; ~35 MB); not for the DeepSeek-R1 shapes.
+ *  - One such group per device at a time: while one is live (until
+ *    moe_group_destroy), another returns MOE_ERR_STATE.  The area keeps the
+ *    last group's contents; creation clears what must start at zero (error
+ *    words, counters, offsets).  Not safe to call from two host threads at
+ *    once; two groups' calls cannot overlap on one device since only one
+ *    exists, and the four calls of that group race with each other only as
+ *    any group's do (order them on one stream, or with events).
+ *  - Errors: MOE_ERR_INVALID (bad desc, or a device index >= 64),
+ *    MOE_ERR_SCRATCH (the group needs more than MOE_SCRATCH_BYTES),
+ *    MOE_ERR_STATE, MOE_ERR_HIP.  *out is untouched on error.
+ *  - It synchronises the device once (clearing the words); call it outside
+ *    graph capture.  The group's four calls enqueue kernels only, as for any
+ *    group; moe_group_destroy releases the area (it frees nothing). */
+#define MOE_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_group_create_static(const moe_group_desc* desc, moe_group_t* out);
+
+/* Synchronise the device, free every buffer of the group and the handle (a
+ * group of moe_group_create_static releases the static area instead).
  * NULL is accepted and ignored. */
 int moe_group_destroy(moe_group_t g);
 
