@@ -6,7 +6,8 @@
 the library this script builds)
 
 Flags: -O3; packed fp32 instructions disabled (-packed-fp32-ops); fp32 divide
-correctly rounded (the fp8 block scales depend on it); no fast-math.
+correctly rounded (the fp8 block scales depend on it); no fast-math.  Links
+the ROCTX library of the ROCm install (ranges around the four calls).
 """
 from __future__ import annotations
 
@@ -24,9 +25,12 @@ SOURCES = [os.path.join(CSRC, "moe_ep.hip"), os.path.join(CSRC, "moe_kernels.hip
 ARCH = "gfx950"
 
 
+def rocm() -> str:
+    return os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
 def hipcc() -> str:
-    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
-    cand = os.path.join(rocm, "bin", "hipcc")
+    cand = os.path.join(rocm(), "bin", "hipcc")
     return cand if os.path.exists(cand) else "hipcc"
 
 
@@ -37,7 +41,10 @@ def build(verbose: bool = False) -> str:
            "-Wall", "-Wno-unused-result",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
-           "-I", INCLUDE, "-I", CSRC, "-o", tmp] + SOURCES
+           "-I", INCLUDE, "-I", CSRC, "-o", tmp] + SOURCES + [
+           # ROCTX ranges around the four calls (rocprofv3 --marker-trace)
+           "-L", os.path.join(rocm(), "lib"), "-lrocprofiler-sdk-roctx",
+           "-Wl,-rpath," + os.path.join(rocm(), "lib")]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -23,7 +23,10 @@
 // partial combine's rows (at most N*T*K) reuse whichever pools combine uses.
 #include <hip/hip_runtime.h>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -73,6 +76,7 @@ struct moe_group_s {
 
     std::vector<void*> allocations;
     bool in_scratch = false;     // buffers carved from the device's static scratch area
+    bool debug = false;          // MOE_EP_DEBUG: poison what each call must rewrite
 };
 
 namespace {
@@ -310,6 +314,60 @@ int timed_launch(moe_group_s* g, int kernel, hipStream_t st, bool launches, F&& 
     return launch(L) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// A ROCTX range around one call of the C ABI (shown by rocprofv3
+// --marker-trace; a few tens of nanoseconds when no tool listens).
+struct CallRange {
+    explicit CallRange(const char* name) { roctxRangePushA(name); }
+    ~CallRange() { roctxRangePop(); }
+    CallRange(const CallRange&) = delete;
+    CallRange& operator=(const CallRange&) = delete;
+};
+
+bool debug_from_env()
+{
+    const char* v = std::getenv("MOE_EP_DEBUG");
+    return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+
+// Debug mode: fill a buffer with 0xFF bytes (bf16 NaN, int32 -1) on the
+// call's stream, so a kernel reading a row or entry its call did not write
+// sees NaN or an out-of-range index instead of last cycle's value.
+int poison(hipStream_t st, const void* p, size_t bytes)
+{
+    if (!p || bytes < 4)
+        return MOE_OK;
+    return from_hip(moe::launch_fill(const_cast<void*>(p), bytes, 0xFFFFFFFFu, st));
+}
+
+// Everything dispatch_send's kernels write: the row pools and planes, the
+// plan tables and the row maps (not the error words or the ticket counter).
+int poison_dispatch_send(const moe_group_s* g, hipStream_t st)
+{
+    const moe::Plan& p = g->plan;
+    const size_t N = g->desc.num_ranks, E = g->desc.num_experts;
+    const size_t R = (size_t)g->rows_max, RQ = (size_t)g->recv_rows_max;
+    const size_t row = (size_t)std::max(g->payload_bytes, g->comb_bytes);
+    const size_t sb = (size_t)g->scale_blocks * 4;
+    int rc;
+    if ((rc = poison(st, g->pool_send, R * row)) || (rc = poison(st, g->pool_recv, RQ * row)) ||
+        (rc = poison(st, g->send_scale, R * sb)) || (rc = poison(st, g->recv_scale, RQ * sb)) ||
+        (rc = poison(st, g->send_meta, R * 4)) || (rc = poison(st, g->recv_meta, RQ * 4)) ||
+        (rc = poison(st, g->send_w, R * 4)) || (rc = poison(st, g->recv_w, RQ * 4)) ||
+        (rc = poison(st, p.cnt, N * E * 4)) || (rc = poison(st, p.pos, R * 4)) ||
+        (rc = poison(st, p.soff, N * (E + 1) * 4)) || (rc = poison(st, p.roff, N * (N + 1) * 4)) ||
+        (rc = poison(st, p.rbase, (N + 1) * 4)) || (rc = poison(st, p.eoff, (E + 1) * 4)) ||
+        (rc = poison(st, p.ebase, N * E * 4)) || (rc = poison(st, p.xfer_src, R * 4)) ||
+        (rc = poison(st, p.xfer_dst, R * 8)) || (rc = poison(st, p.shuf_map, R * 8)) ||
+        (rc = poison(st, p.shuf_inv, R * 4)) || (rc = poison(st, p.slot_of, R * 4)) ||
+        (rc = poison(st, p.pdst, R * 4)) || (rc = poison(st, p.ppos, R * 4)) ||
+        (rc = poison(st, p.psoff, N * (N + 1) * 4)) || (rc = poison(st, p.qoff, N * (N + 1) * 4)) ||
+        (rc = poison(st, p.qbase, (N + 1) * 4)) || (rc = poison(st, p.pbase, (N + 1) * 4)) ||
+        (rc = poison(st, p.pmap, R * 4)) || (rc = poison(st, p.phead, 2 * R * 16)) ||
+        (rc = poison(st, p.pitem, R * 8)))
+        return rc;
+    return MOE_OK;
+}
+
 int check_device(const moe_group_s* g)
 {
     int dev = -1;
@@ -397,6 +455,7 @@ int moe_group_create(const moe_group_desc* desc, moe_group_t* out)
         return MOE_ERR_HIP;
     }
     init_sizes(g);
+    g->debug = debug_from_env();
     Placer take{g};
     if ((rc = place_buffers(g, take)) || (rc = zero_words(g))) {
         free_all(g);
@@ -430,6 +489,7 @@ int moe_group_create_static(const moe_group_desc* desc, moe_group_t* out)
     g->device = dev;
     g->in_scratch = true;
     init_sizes(g);
+    g->debug = debug_from_env();
     Placer count{g, true, 0, 0};
     if ((rc = place_buffers(g, count)) != MOE_OK)
         return rc;
@@ -467,6 +527,7 @@ int moe_group_destroy(moe_group_t g)
 int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const int32_t* topk_idx,
                       const float* topk_weights, hipStream_t stream)
 {
+    CallRange range("moe_dispatch_send");
     if (!g)
         return MOE_ERR_INVALID;
     if (g->state != State::Idle)
@@ -485,6 +546,8 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const in
     const moe::Rows rows = rows_of(g);
     const bool any = sh.rows > 0;
     using moe::Launch;
+    if (g->debug && (rc = poison_dispatch_send(g, stream)))
+        return rc;
     if ((rc = timed_launch(g, MOE_KERNEL_ROUTE_PLAN, stream, true, [&](const Launch& L) {
              return moe::launch_route_plan(sh, topk_idx, g->plan, L);
          })) ||
@@ -504,6 +567,7 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const in
 int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale, int32_t* expert_offsets,
                       hipStream_t stream)
 {
+    CallRange range("moe_dispatch_recv");
     if (!g)
         return MOE_ERR_INVALID;
     if (g->state != State::Sent)
@@ -523,6 +587,15 @@ int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale, int32_
         return rc;
     const moe::Shape sh = shape_of(g, g->T);
     const moe::Rows rows = rows_of(g);
+    // debug: the expert-order metadata and the caller's outputs, all of which
+    // the shuffle must write
+    if (g->debug &&
+        ((rc = poison(stream, g->src_rank, (size_t)g->rows_max * 4)) ||
+         (rc = poison(stream, g->src_slot, (size_t)g->rows_max * 4)) ||
+         (rc = poison(stream, expert_x, (size_t)sh.rows * g->payload_bytes)) ||
+         (rc = poison(stream, expert_scale, (size_t)sh.rows * g->scale_blocks * 4)) ||
+         (rc = poison(stream, expert_offsets, (size_t)(sh.E + 1) * 4))))
+        return rc;
     if ((rc = timed_launch(g, MOE_KERNEL_SHUFFLE, stream, true, [&](const moe::Launch& L) {
              return moe::launch_shuffle(sh, g->plan, rows, expert_x, expert_scale, expert_offsets,
                                         L);
@@ -534,6 +607,7 @@ int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale, int32_
 
 int moe_combine_send(moe_group_t g, const void* expert_y, hipStream_t stream)
 {
+    CallRange range("moe_combine_send");
     if (!g)
         return MOE_ERR_INVALID;
     if (g->state != State::Received)
@@ -546,6 +620,14 @@ int moe_combine_send(moe_group_t g, const void* expert_y, hipStream_t stream)
     const moe::Shape sh = shape_of(g, g->T);
     const moe::Rows rows = rows_of(g);
     const bool any = sh.rows > 0;
+    // debug: both row pools (their dispatch rows are consumed; combine's
+    // kernels rewrite every row they later read)
+    if (g->debug &&
+        ((rc = poison(stream, g->pool_send,
+                      (size_t)g->rows_max * std::max(g->payload_bytes, g->comb_bytes))) ||
+         (rc = poison(stream, g->pool_recv,
+                      (size_t)g->recv_rows_max * std::max(g->payload_bytes, g->comb_bytes)))))
+        return rc;
     if (sh.partial) {
         if ((rc = timed_launch(g, MOE_KERNEL_PARTIAL_SEND, stream, any, [&](const moe::Launch& L) {
                  return moe::launch_partial_send(sh, g->plan, rows, expert_y, L);
@@ -574,6 +656,7 @@ int moe_combine_send(moe_group_t g, const void* expert_y, hipStream_t stream)
 
 int moe_combine_recv(moe_group_t g, const float* topk_weights, void* out, hipStream_t stream)
 {
+    CallRange range("moe_combine_recv");
     if (!g)
         return MOE_ERR_INVALID;
     if (g->state != State::CombineSent)
@@ -589,6 +672,8 @@ int moe_combine_recv(moe_group_t g, const float* topk_weights, void* out, hipStr
         return rc;
     const moe::Shape sh = shape_of(g, g->T);
     const moe::Rows rows = rows_of(g);
+    if (g->debug && (rc = poison(stream, out, (size_t)sh.N * sh.T * sh.H * 2)))
+        return rc;
     if (partial) {
         if ((rc = timed_launch(g, MOE_KERNEL_PARTIAL_REDUCE, stream, sh.rows > 0,
                                [&](const moe::Launch& L) {

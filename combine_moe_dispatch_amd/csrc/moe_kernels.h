@@ -116,6 +116,9 @@ hipError_t launch_partial_send(const Shape& sh, const Plan& p, const Rows& r, co
 hipError_t launch_partial_transfer(const Shape& sh, const Plan& p, const Rows& r, const Launch& L);
 hipError_t launch_partial_reduce(const Shape& sh, const Plan& p, const Rows& r, void* out,
                                  const Launch& L);
+// Fill `bytes` bytes (a multiple of 4, p 16-byte aligned) with a repeated
+// 32-bit pattern: the debug mode's poisoning of buffers a call must rewrite.
+hipError_t launch_fill(void* p, size_t bytes, uint32_t pattern, hipStream_t stream);
 // Streaming probes (kind: 0 copy, 1 read, 2 write) over `vecs` 16-byte vectors.
 hipError_t launch_hbm_probe(int kind, void* dst, const void* src, int64_t vecs, hipStream_t stream);
 

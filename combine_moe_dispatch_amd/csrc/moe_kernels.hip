@@ -1642,6 +1642,21 @@ __global__ __launch_bounds__(PROBE_NT) void probe_write_kernel(v4u* __restrict__
     }
 }
 
+// Debug poisoning: 16-byte stores over the vector part, then the 4-byte tail.
+constexpr int FILL_NT = 256;
+
+__global__ __launch_bounds__(FILL_NT) void fill_kernel(v4u* __restrict__ p, int64_t nvec,
+                                                      uint32_t* __restrict__ tail, int ntail,
+                                                      uint32_t pattern)
+{
+    const v4u v = {pattern, pattern, pattern, pattern};
+    const int64_t stride = (int64_t)gridDim.x * FILL_NT;
+    for (int64_t i = (int64_t)blockIdx.x * FILL_NT + threadIdx.x; i < nvec; i += stride)
+        p[i] = v;
+    if (blockIdx.x == 0 && (int)threadIdx.x < ntail)
+        tail[threadIdx.x] = pattern;
+}
+
 // Launch shape of a row kernel: waves per row (SPLIT) and 16-byte vectors
 // per lane per round (U), from the number of vectors in a row.
 struct RowShape {
@@ -1945,6 +1960,20 @@ hipError_t launch_partial_reduce(const Shape& sh, const Plan& p, const Rows& r, 
         return hipSuccess;
     MOE_DISPATCH_TOKEN(sh, partial_reduce_kernel, 2, tokens, L, sh, p, (const v4u*)r.comb_recv,
                        (v4u*)out);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill(void* p, size_t bytes, uint32_t pattern, hipStream_t stream)
+{
+    if (bytes < 4)
+        return hipSuccess;
+    const int64_t nvec = (int64_t)(bytes / 16);
+    const int ntail = (int)((bytes % 16) / 4);
+    const int64_t blocks = std::min<int64_t>(std::max<int64_t>((nvec + FILL_NT - 1) / FILL_NT, 1),
+                                             (int64_t)1 << 16);
+    const Launch L{stream, nullptr, nullptr};
+    go(fill_kernel, dim3((unsigned)blocks), dim3(FILL_NT), 0, L, (v4u*)p, nvec,
+       (uint32_t*)((uint8_t*)p + nvec * 16), ntail, pattern);
     return hipGetLastError();
 }
 

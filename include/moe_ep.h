@@ -37,6 +37,17 @@
  *    never synchronise with the device, so they cannot return an error the
  *    device finds later; the status call is where device errors surface.
  *  - One host thread at a time per group.
+ *  - Tracing: each of the four calls is a ROCTX range named after it
+ *    (rocprofv3 --marker-trace shows them).
+ *  - Debug mode: with MOE_EP_DEBUG=1 in the environment when a group is
+ *    created, every call first fills (on its stream, with a kernel) each
+ *    buffer its kernels must rewrite with 0xFF bytes -- bf16 NaN, int32 -1:
+ *    dispatch_send the group's row pools, planes, plan tables and row maps;
+ *    dispatch_recv the expert-order metadata and the caller's expert rows,
+ *    scales and offsets of this cycle; combine_send both row pools;
+ *    combine_recv the caller's output of this cycle -- so a stale or unwritten
+ *    read shows as NaN or as an index error.  Outputs are unchanged; each
+ *    call costs a few extra passes over its buffers.
  */
 #ifndef MOE_EP_H
 #define MOE_EP_H

@@ -20,7 +20,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY selects another build of oracle.c (the sanitizer test's)
+_OVERRIDE = os.environ.get("ORACLE_LIBRARY")
+LIB_PATH = _OVERRIDE or os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "oracle.c")
 
 _lib = None
@@ -37,7 +39,8 @@ def build() -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+        if not _OVERRIDE and (not os.path.exists(LIB_PATH)
+                              or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH)):
             build()
         _lib = ctypes.CDLL(LIB_PATH)
         _declare(_lib)
