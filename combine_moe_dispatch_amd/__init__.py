@@ -3,7 +3,11 @@
 Argument marshalling only: every call below forwards to the C function of the
 same name in include/moe_ep.h (ctypes), passing device pointers and the HIP
 stream.  Tensors may be torch tensors (their data_ptr() is passed) or raw
-integer device addresses.  A non-zero status raises MoeError.
+integer device addresses.  A non-zero status raises MoeError.  Torch tensors
+are checked before their address is passed (on the group's device, dense,
+the expected dtype where one is fixed, at least as many bytes as the call
+reads or writes) and a failed check raises MoeError(MOE_ERR_INVALID); raw
+addresses are passed unchecked.
 
 The library is built in-tree by ``python combine_moe_dispatch_amd/_build.py``;
 importing this package without it raises ImportError -- there is no fallback.
@@ -124,6 +128,49 @@ def _ptr(a):
     return a.data_ptr()
 
 
+# group handle -> (desc, device index), for checking tensor arguments
+_groups: dict = {}
+_DT_I32, _DT_F32 = "int32", "float32"
+
+
+def _arg(a, call: str, name: str, nbytes: int, g: int, dtype: str = None):
+    """The address of a tensor argument after checking it; raw addresses and
+    None pass through."""
+    if a is None or isinstance(a, int):
+        return _ptr(a)
+    info = _groups.get(g)
+    bad = None
+    if not a.is_cuda:
+        bad = "not a device tensor"
+    elif info is not None and a.device.index != info[1]:
+        bad = f"on device {a.device.index}, the group is on device {info[1]}"
+    elif not a.is_contiguous():
+        bad = "not contiguous"
+    elif dtype is not None and str(a.dtype).rsplit(".", 1)[-1] != dtype:
+        bad = f"dtype {a.dtype}, expected {dtype}"
+    elif a.numel() * a.element_size() < nbytes:
+        bad = f"{a.numel() * a.element_size()} bytes, the call needs {nbytes}"
+    if bad is not None:
+        raise MoeError(MOE_ERR_INVALID, f"{call}: {name} {bad}")
+    return a.data_ptr()
+
+
+def _shape(g: int):
+    """(N, E, K, H, payload bytes per row, scale blocks per row) of a group
+    this binding created, else None."""
+    info = _groups.get(g)
+    if info is None:
+        return None
+    d = info[0]
+    fp8 = d.dispatch_dtype == MOE_FP8_E4M3
+    return (d.num_ranks, d.num_experts, d.top_k, d.hidden, d.hidden * (1 if fp8 else 2),
+            d.hidden // 128 if fp8 else 0)
+
+
+def _cur_tokens(g: int) -> int:
+    return moe_group_view_get(g).num_tokens if g in _groups else 0
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -151,6 +198,7 @@ def moe_group_create(num_ranks: int, num_experts: int, top_k: int, hidden: int,
                           transport, combine_mode, layout)
     h = ctypes.c_void_p()
     _check(_lib.moe_group_create(ctypes.byref(desc), ctypes.byref(h)), "moe_group_create")
+    _groups[h.value] = (desc, _current_device())
     return h.value
 
 
@@ -166,31 +214,59 @@ def moe_group_create_static(num_ranks: int, num_experts: int, top_k: int, hidden
     h = ctypes.c_void_p()
     _check(_lib.moe_group_create_static(ctypes.byref(desc), ctypes.byref(h)),
            "moe_group_create_static")
+    _groups[h.value] = (desc, _current_device())
     return h.value
 
 
+def _current_device() -> int:
+    import torch
+    return torch.cuda.current_device()
+
+
 def moe_group_destroy(g: int) -> None:
+    _groups.pop(g, None)
     _check(_lib.moe_group_destroy(g), "moe_group_destroy")
 
 
 def moe_dispatch_send(g: int, num_tokens: int, x, topk_idx, topk_weights=None,
                       stream=None) -> None:
-    _check(_lib.moe_dispatch_send(g, num_tokens, _ptr(x), _ptr(topk_idx), _ptr(topk_weights),
-                                  _stream(stream)), "moe_dispatch_send")
+    c = "moe_dispatch_send"
+    sh = _shape(g)
+    N, E, K, H = sh[:4] if sh else (0, 0, 0, 0)
+    T = max(int(num_tokens), 0)
+    px = _arg(x, c, "x", N * T * H * 2, g)
+    pi = _arg(topk_idx, c, "topk_idx", N * T * K * 4, g, _DT_I32)
+    pw = _arg(topk_weights, c, "topk_weights", N * T * K * 4, g, _DT_F32)
+    _check(_lib.moe_dispatch_send(g, num_tokens, px, pi, pw, _stream(stream)), c)
 
 
 def moe_dispatch_recv(g: int, expert_x, expert_scale, expert_offsets, stream=None) -> None:
-    _check(_lib.moe_dispatch_recv(g, _ptr(expert_x), _ptr(expert_scale), _ptr(expert_offsets),
-                                  _stream(stream)), "moe_dispatch_recv")
+    c = "moe_dispatch_recv"
+    sh = _shape(g)
+    N, E, K, H, pb, nb = sh if sh else (0, 0, 0, 0, 0, 0)
+    R = N * _cur_tokens(g) * K
+    px = _arg(expert_x, c, "expert_x", R * pb, g)
+    ps = _arg(expert_scale, c, "expert_scale", R * nb * 4, g, _DT_F32)
+    po = _arg(expert_offsets, c, "expert_offsets", (E + 1) * 4 if sh else 0, g, _DT_I32)
+    _check(_lib.moe_dispatch_recv(g, px, ps, po, _stream(stream)), c)
 
 
 def moe_combine_send(g: int, expert_y, stream=None) -> None:
-    _check(_lib.moe_combine_send(g, _ptr(expert_y), _stream(stream)), "moe_combine_send")
+    c = "moe_combine_send"
+    sh = _shape(g)
+    N, E, K, H = sh[:4] if sh else (0, 0, 0, 0)
+    py = _arg(expert_y, c, "expert_y", N * _cur_tokens(g) * K * H * 2, g)
+    _check(_lib.moe_combine_send(g, py, _stream(stream)), c)
 
 
 def moe_combine_recv(g: int, topk_weights, out, stream=None) -> None:
-    _check(_lib.moe_combine_recv(g, _ptr(topk_weights), _ptr(out), _stream(stream)),
-           "moe_combine_recv")
+    c = "moe_combine_recv"
+    sh = _shape(g)
+    N, E, K, H = sh[:4] if sh else (0, 0, 0, 0)
+    T = _cur_tokens(g)
+    pw = _arg(topk_weights, c, "topk_weights", N * T * K * 4, g, _DT_F32)
+    po = _arg(out, c, "out", N * T * H * 2, g)
+    _check(_lib.moe_combine_recv(g, pw, po, _stream(stream)), c)
 
 
 def moe_group_view_get(g: int) -> moe_group_view:

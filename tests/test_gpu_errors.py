@@ -209,3 +209,49 @@ def test_kernel_timing_mask():
                        "partial_transfer", "partial_reduce"}, t
     finally:
         mep.moe_group_destroy(g)
+
+
+def test_binding_rejects_bad_tensors():
+    """The Python binding checks torch tensors before passing their address:
+    on the device, dense, the fixed dtypes (int32 ids and offsets, fp32
+    weights and scales), and large enough for the call; a failed check raises
+    MOE_ERR_INVALID and enqueues nothing, and the cycle then runs normally."""
+    cfg = CONFIGS["A"]
+    say(f"[gpu] binding tensor checks {cfg.describe()}")
+    inp = make_inputs(cfg)
+    g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16)
+    try:
+        R = cfg.rows
+        x, idx, w = to_dev(torch, inp["x"]), to_dev(torch, inp["idx"]), to_dev(torch, inp["w"])
+
+        def status_of(fn, *a):
+            try:
+                fn(*a)
+                return mep.MOE_OK
+            except mep.MoeError as e:
+                return e.status
+
+        assert status_of(mep.moe_dispatch_send, g, cfg.T, x.cpu(), idx) == mep.MOE_ERR_INVALID
+        assert status_of(mep.moe_dispatch_send, g, cfg.T, x, idx.long()) == mep.MOE_ERR_INVALID
+        assert status_of(mep.moe_dispatch_send, g, cfg.T, x[:, :cfg.T - 1], idx) == mep.MOE_ERR_INVALID
+        xt = torch.empty((cfg.N, cfg.H, cfg.T), dtype=torch.int16, device="cuda").transpose(1, 2)
+        assert status_of(mep.moe_dispatch_send, g, cfg.T, xt, idx) == mep.MOE_ERR_INVALID
+        mep.moe_dispatch_send(g, cfg.T, x, idx)
+        offs = torch.empty((cfg.E + 1,), dtype=torch.int32, device="cuda")
+        small = torch.empty((R - 1, cfg.H), dtype=torch.bfloat16, device="cuda")
+        assert status_of(mep.moe_dispatch_recv, g, small, None, offs) == mep.MOE_ERR_INVALID
+        assert status_of(mep.moe_dispatch_recv, g, torch.empty((R, cfg.H), dtype=torch.bfloat16,
+                                                                device="cuda"),
+                         None, offs[:cfg.E]) == mep.MOE_ERR_INVALID
+        expert_x = torch.empty((R, cfg.H), dtype=torch.bfloat16, device="cuda")
+        mep.moe_dispatch_recv(g, expert_x, None, offs)
+        assert status_of(mep.moe_combine_send, g, expert_x[:R - 1]) == mep.MOE_ERR_INVALID
+        mep.moe_combine_send(g, expert_x)
+        out = torch.empty((cfg.N, cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+        assert status_of(mep.moe_combine_recv, g, w.double(), out) == mep.MOE_ERR_INVALID
+        assert status_of(mep.moe_combine_recv, g, w, out[:, 1:]) == mep.MOE_ERR_INVALID
+        mep.moe_combine_recv(g, w, out)
+        torch.cuda.synchronize()
+        assert mep.moe_group_status(g) == mep.MOE_OK
+    finally:
+        mep.moe_group_destroy(g)
