@@ -50,13 +50,17 @@ def partial_rows(cfg, idx) -> int:
     return int(np.unique(tok * N + d).size)
 
 
-def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: int = 0) -> dict:
+def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: int = 0,
+                 layout: str = "packed") -> dict:
     """Algorithmic HBM bytes per launch of each kernel: every buffer the method
     mandates is written once and read once by the next stage; inputs are read
     once per token.  The int32 row maps the pack kernel writes for the later
     movers (4-8 bytes per row of 7-14 KiB) are an implementation detail and not
     counted.  With the partial combine (P partial rows), the router weights
-    travel with the dispatched rows and combine moves P rows instead of R."""
+    travel with the dispatched rows and combine moves P rows instead of R.
+    The receiver's map kernel reads the counts and offsets (its maps, like the
+    pack's, are not counted); with fixed slots and the receiver-side combine
+    the group offsets move from the route plan to their own kernel."""
     N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
     R = N * T * K
     fp8 = cfg.dtype == "fp8"
@@ -76,7 +80,13 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
         "combine_pack": 2 * R * hy,
         "transfer_back": 2 * R * hy,
         "combine_reduce": R * hy + R * 8 + tokens * H * 2,
+        "recv_map": N * E * 4 * 2 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4,
     }
+    if layout == "fixed" and combine == "receiver":
+        offs = (N * E * 4 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4 + (E + 1) * 4
+                + N * E * 4)
+        kb["route_plan"] -= offs
+        kb["offsets"] = offs
     if transport == "direct":
         # pack writes the receive rows itself and combine writes the return
         # rows itself: no transfer passes
@@ -172,7 +182,8 @@ KERNEL_OF = [("route_plan_kernel", "route_plan"), ("pack_bf16_kernel", "pack"),
              ("combine_reduce_kernel", "combine_reduce"),
              ("partial_send_kernel", "partial_send"),
              ("partial_transfer_kernel", "partial_transfer"),
-             ("partial_reduce_kernel", "partial_reduce")]
+             ("partial_reduce_kernel", "partial_reduce"),
+             ("recv_map_kernel", "recv_map"), ("offsets_kernel", "offsets")]
 
 
 def _kernel_key(name: str):
@@ -258,10 +269,11 @@ def trace_summary(cfg, db: str) -> str:
              "|---|---|---|---|---|---|"]
     transport = "staged" if "transfer" in acc else "direct"
     combine = "partial" if "partial_send" in acc else "receiver"
-    kb = kernel_bytes(cfg, transport, combine, _partial_rows_of(cfg, combine))
-    for key in ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
-                "combine_push", "combine_reduce", "partial_send", "partial_transfer",
-                "partial_reduce"]:
+    layout = "fixed" if "offsets" in acc else "packed"
+    kb = kernel_bytes(cfg, transport, combine, _partial_rows_of(cfg, combine), layout)
+    for key in ["route_plan", "pack", "transfer", "recv_map", "offsets", "shuffle",
+                "combine_pack", "transfer_back", "combine_push", "combine_reduce",
+                "partial_send", "partial_transfer", "partial_reduce"]:
         if key in acc:
             v = acc[key]
             avg = sum(v) / len(v)
@@ -747,13 +759,13 @@ def main() -> int:
     # the probe's source and destination each the size of one side of the
     # dominant kernel's traffic
     kb_dom = kernel_bytes(cfg, args.transport, args.combine,
-                          partial_rows(cfg, inp["idx"]) if partial else 0)[dom]
+                          partial_rows(cfg, inp["idx"]) if partial else 0, args.layout)[dom]
     ceiling = {"at_kernel_footprint": hbm_ceiling(torch, mep, kb_dom // 2),
                "at_1gib": hbm_ceiling(torch, mep, 1 << 30)}
 
     ms_per_step = cold["p50"] * 1e-3
     P = partial_rows(cfg, inp["idx"]) if partial else 0
-    kb = kernel_bytes(cfg, args.transport, args.combine, P)
+    kb = kernel_bytes(cfg, args.transport, args.combine, P, args.layout)
     total_bytes = sum(kb.values())
     kern = {}
     for name, (ms, n) in timing_all.items():

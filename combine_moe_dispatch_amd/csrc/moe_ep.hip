@@ -85,6 +85,7 @@ const char* const kKernelNames[MOE_KERNEL_COUNT] = {
     "route_plan_kernel",   "pack_kernel",          "transfer_kernel",       "shuffle_kernel",
     "combine_pack_kernel", "transfer_back_kernel", "combine_reduce_kernel", "combine_push_kernel",
     "partial_send_kernel", "partial_transfer_kernel", "partial_reduce_kernel",
+    "recv_map_kernel",     "offsets_kernel",
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -138,6 +139,7 @@ moe::Shape shape_of(const moe_group_s* g, int T)
     sh.direct = g->desc.transport == MOE_TRANSPORT_DIRECT;
     sh.partial = g->desc.combine_mode == MOE_COMBINE_PARTIAL;
     sh.fixed = g->desc.layout == MOE_LAYOUT_FIXED_SLOT;
+    sh.sender_only = sh.fixed && !sh.partial;
     sh.slots = g->desc.max_tokens;
     sh.rows = (int64_t)sh.N * T * sh.K;
     sh.recv_rows = sh.fixed ? g->recv_rows_max : sh.rows;
@@ -263,7 +265,7 @@ int place_buffers(moe_group_s* g, Placer& take)
         (rc = take(&g->src_rank, R)) || (rc = take(&g->src_slot, R)) ||
         (fp8 && staged && (rc = take(&g->send_scale, R * g->scale_blocks))) ||
         (fp8 && (rc = take(&g->recv_scale, RQ * g->scale_blocks))) ||
-        (fixed && (rc = take(&p.slot_of, R))) ||
+        (fixed && ((rc = take(&p.slot_of, R)) || (rc = take(&p.send_slot, R)))) ||
         (partial && ((rc = take(&p.pdst, R)) || (rc = take(&p.ppos, R)) ||
                      (rc = take(&p.psoff, (size_t)N * (N + 1))) ||
                      (rc = take(&p.qoff, (size_t)N * (N + 1))) ||
@@ -359,6 +361,7 @@ int poison_dispatch_send(const moe_group_s* g, hipStream_t st)
         (rc = poison(st, p.ebase, N * E * 4)) || (rc = poison(st, p.xfer_src, R * 4)) ||
         (rc = poison(st, p.xfer_dst, R * 8)) || (rc = poison(st, p.shuf_map, R * 8)) ||
         (rc = poison(st, p.shuf_inv, R * 4)) || (rc = poison(st, p.slot_of, R * 4)) ||
+        (rc = poison(st, p.send_slot, R * 4)) ||
         (rc = poison(st, p.pdst, R * 4)) || (rc = poison(st, p.ppos, R * 4)) ||
         (rc = poison(st, p.psoff, N * (N + 1) * 4)) || (rc = poison(st, p.qoff, N * (N + 1) * 4)) ||
         (rc = poison(st, p.qbase, (N + 1) * 4)) || (rc = poison(st, p.pbase, (N + 1) * 4)) ||
@@ -596,7 +599,17 @@ int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale, int32_
          (rc = poison(stream, expert_scale, (size_t)sh.rows * g->scale_blocks * 4)) ||
          (rc = poison(stream, expert_offsets, (size_t)(sh.E + 1) * 4))))
         return rc;
-    if ((rc = timed_launch(g, MOE_KERNEL_SHUFFLE, stream, true, [&](const moe::Launch& L) {
+    // the receiver's side of the plan: with sender-only addressing (fixed
+    // slots, receiver-side combine) first the group offsets from the exchanged
+    // counts; then the row maps; then the shuffle
+    if ((sh.sender_only &&
+         (rc = timed_launch(g, MOE_KERNEL_OFFSETS, stream, true, [&](const moe::Launch& L) {
+              return moe::launch_offsets(sh, g->plan, L);
+          }))) ||
+        (rc = timed_launch(g, MOE_KERNEL_RECV_MAP, stream, sh.rows > 0, [&](const moe::Launch& L) {
+             return moe::launch_recv_map(sh, g->plan, L);
+         })) ||
+        (rc = timed_launch(g, MOE_KERNEL_SHUFFLE, stream, true, [&](const moe::Launch& L) {
              return moe::launch_shuffle(sh, g->plan, rows, expert_x, expert_scale, expert_offsets,
                                         L);
          })))

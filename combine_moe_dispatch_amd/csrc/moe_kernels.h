@@ -22,8 +22,11 @@ struct Shape {
     int fp8;              // payload is e4m3 + fp32 block scales
     int direct;           // direct transport: pack and combine write the peer's rows
     int partial;          // combine sums on the expert side, one row per (token, rank)
-    int fixed;            // fixed-slot receive layout: one region of `slots` rows per
-                          // (receiver, source, local expert)
+    int fixed;            // fixed-slot receive layout: T_max slots per (source, expert),
+                          // each expert's area slot-major
+    int sender_only;      // fixed slots with the receiver-side combine: dispatch_send's
+                          // kernels use only each sender's own plan, and the group
+                          // offsets are computed in dispatch_recv
     int slots;            // T_max (fixed-slot layout)
     int64_t recv_rows;    // rows of the receive planes: rows, or N*E*slots (fixed-slot)
     int64_t rows;         // N*T*K
@@ -51,8 +54,11 @@ struct Plan {              // device pointers owned by the group
     int32_t* ebase;        // [N][E]  first expert-order row of (sender s, expert e)
     // Receive rows are numbered in the packed order q (rank, source, expert,
     // t, k); with the fixed-slot layout a row's place in the receive planes
-    // is slot_of[q], otherwise q itself.
-    int32_t* xfer_src;     // [rows]  packed receive row q <- send row xfer_src[q]
+    // is slot_of[q], otherwise q itself.  The sender's pack writes the maps its
+    // own transfer follows (xfer_src, send_slot); the receiver's map kernel
+    // writes the rest from the exchanged counts and offsets.
+    int32_t* xfer_src;     // [rows]  packed receive row q <- send row xfer_src[q] (sender)
+    int32_t* send_slot;    // [rows]  send row -> its slot (fixed-slot layout; sender)
     int2* xfer_dst;        // [rows]  send row -> (its receive-plane row, its expert row)
     int2* shuf_map;        // [rows]  expert row r <- (receive-plane row, source rank)
     int32_t* shuf_inv;     // [rows]  packed receive row -> its expert row
@@ -102,6 +108,11 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
 hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const float* w,
                        const Plan& p, const Rows& r, const Launch& L);
 hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, const Launch& L);
+// The group offsets and the cycle's error word alone (one workgroup), for
+// plans whose route plan left them out (Shape::sender_only).
+hipError_t launch_offsets(const Shape& sh, const Plan& p, const Launch& L);
+// The receiver's row maps from the exchanged counts and offsets.
+hipError_t launch_recv_map(const Shape& sh, const Plan& p, const Launch& L);
 hipError_t launch_shuffle(const Shape& sh, const Plan& p, const Rows& r, void* expert_x,
                           float* expert_scale, int32_t* expert_offsets, const Launch& L);
 hipError_t launch_combine_pack(const Shape& sh, const Plan& p, const Rows& r,

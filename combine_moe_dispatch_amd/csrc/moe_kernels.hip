@@ -151,6 +151,7 @@ struct RouteArgs {
     int chunk_waves;        // RP_WAVES, or fewer for large E (LDS budget)
     int partial;            // also plan the expert-side partial rows
     int slot_cap;           // fixed-slot layout: most rows per (sender, expert); -1: none
+    int offsets;            // the last workgroup computes the group offsets
     int64_t cap;
 };
 
@@ -268,6 +269,29 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* wg_er
             if (last)
                 p.qbase[N] = br.x + br.y;
         }
+    }
+}
+
+// The end of the plan, once every sender's counts are in view: the group
+// offsets, then the cycle's error word -- every sender's bits and the
+// offsets' checks.  It overwrites the last cycle's word, so an error stops
+// only the kernels of its own cycle; the sticky word keeps it for the status
+// call.  Every thread of the workgroup calls it; wg_err (LDS) holds the
+// workgroup's own bits.
+__device__ void close_plan(const RouteArgs& ra, const Plan& p, int32_t* wg_err)
+{
+    group_offsets(ra, p, wg_err);
+    int e = 0;
+    for (int j = threadIdx.x; j < ra.N; j += RP_NT)
+        e |= p.err_rank[j];
+    if (e)
+        atomicOr(wg_err, e);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int32_t cyc = *wg_err;
+        *p.err = cyc;
+        if (cyc)
+            atomicOr(p.err_sticky, cyc);
     }
 }
 
@@ -557,8 +581,15 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     // wave waits for its own stores, then one agent-scope release (an L2
     // write-back) covers the whole workgroup before the ticket is taken.
     __syncthreads();
-    if (tid == 0)
+    if (tid == 0) {
         p.err_rank[s] = wg_err;
+        // without the offsets tail the cycle word is made in dispatch_recv;
+        // the sticky word gets the sender's bits now
+        if (!ra.offsets && wg_err)
+            atomicOr(p.err_sticky, wg_err);
+    }
+    if (!ra.offsets)
+        return;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
@@ -569,23 +600,24 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     if (ticket != ra.N - 1)
         return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    group_offsets(ra, p, &wg_err);
-    // the cycle's error word: every sender's bits and the offsets' checks.
-    // It overwrites the last cycle's word, so an error stops only the kernels
-    // of its own cycle; the sticky word keeps it for the status call.
-    int e = 0;
-    for (int j = tid; j < N; j += RP_NT)
-        e |= p.err_rank[j];
-    if (e)
-        atomicOr(&wg_err, e);
-    __syncthreads();
-    if (tid == 0) {
-        const int32_t cyc = wg_err;
-        *p.err = cyc;
-        if (cyc)
-            atomicOr(p.err_sticky, cyc);
+    close_plan(ra, p, &wg_err);
+    if (tid == 0)
         atomicExch(p.ticket, 0);
-    }
+}
+
+// The group offsets and the cycle's error word in a launch of their own (one
+// workgroup), for the fixed-slot layout with the receiver-side combine: there
+// the senders address their slots from their own counts ([EPMC] "Portable
+// kernels": no synchronisation with other ranks before writing), so the
+// offsets the receivers need are formed at dispatch_recv from the exchanged
+// counts, after the senders' kernels.
+__global__ __launch_bounds__(RP_NT) void offsets_kernel(RouteArgs ra, Plan p)
+{
+    __shared__ int32_t wg_err;
+    if (threadIdx.x == 0)
+        wg_err = 0;
+    __syncthreads();
+    close_plan(ra, p, &wg_err);
 }
 
 // ---------------------------------------------------------------------------
@@ -668,32 +700,52 @@ struct RowDest {
 // row needs only the sender's own offsets: slot i = pk - soff[s][e] of the
 // pair (s, e) is row (e*T_max + i)*N + s (each expert's area slot-major, so
 // the filled slots of all senders sit together at its start).
+// With Shape::sender_only the group offsets are not formed yet: only the
+// send row and the slot are computed (q and r stay 0, unused).
 __device__ inline RowDest row_dest(const Shape& sh, const Plan& p, int s, int e, int pk)
 {
     const int64_t TK = (int64_t)sh.T * sh.K;
     RowDest rd;
     rd.srow = (int32_t)(s * TK + pk);
-    const int d = e / sh.L;
     const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
-    rd.q = p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + pk - so[d * sh.L];
-    rd.r = p.ebase[(size_t)s * sh.E + e] + pk - so[e];
     const int i = pk - so[e];
+    bool ok = (uint64_t)pk < (uint64_t)TK;
+    rd.q = 0;
+    rd.r = 0;
+    if (!sh.sender_only) {
+        const int d = e / sh.L;
+        rd.q = p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + pk - so[d * sh.L];
+        rd.r = p.ebase[(size_t)s * sh.E + e] + i;
+        ok = ok && (uint64_t)rd.q < (uint64_t)sh.rows && (uint64_t)rd.r < (uint64_t)sh.rows;
+    }
     const int64_t slot = ((int64_t)e * sh.slots + i) * sh.N + s;
     rd.qd = sh.fixed ? (int32_t)slot : rd.q;
-    rd.ok = (uint64_t)rd.q < (uint64_t)sh.rows && (uint64_t)rd.r < (uint64_t)sh.rows &&
-            (uint64_t)pk < (uint64_t)TK &&
-            (!sh.fixed || ((uint32_t)i < (uint32_t)sh.slots && (uint64_t)slot < (uint64_t)sh.recv_rows));
+    if (sh.fixed)
+        ok = ok && (uint32_t)i < (uint32_t)sh.slots && (uint64_t)slot < (uint64_t)sh.recv_rows;
+    rd.ok = ok;
     return rd;
 }
 
-__device__ inline void record_maps(const Shape& sh, const Plan& p, const RowDest& rd, int s)
+// The map the sender's own transfer follows (the receiver's maps are made by
+// recv_map_kernel): for the packed layout the send row of each receive row,
+// for the fixed-slot layout the slot of each send row.  The direct transport
+// has no transfer.
+__device__ inline void record_maps(const Shape& sh, const Plan& p, const RowDest& rd)
 {
-    p.xfer_src[rd.q] = rd.srow;
-    p.xfer_dst[rd.srow] = make_int2(rd.qd, rd.r);
-    p.shuf_map[rd.r] = make_int2(rd.qd, s);
-    p.shuf_inv[rd.q] = rd.r;
+    if (sh.direct)
+        return;
     if (sh.fixed)
-        p.slot_of[rd.q] = rd.qd;
+        p.send_slot[rd.srow] = rd.qd;
+    else
+        p.xfer_src[rd.q] = rd.srow;
+}
+
+// Whether sender s's rows are to be dropped this cycle: the cycle's error
+// word, or with Shape::sender_only (where that word is made later, at
+// dispatch_recv) the sender's own bits from this cycle's route plan.
+__device__ inline bool sender_failed(const Shape& sh, const Plan& p, int s)
+{
+    return sh.sender_only ? p.err_rank[s] != 0 : *p.err != 0;
 }
 
 // Records of the expert-side partial combine, made by the lead wave of a
@@ -773,7 +825,7 @@ __device__ inline int pack_dest(const Shape& sh, const Plan& p, const int32_t* _
             row = sh.direct ? rd.qd : rd.srow;
             d = e / sh.L;
             if (lead) {
-                record_maps(sh, p, rd, s);
+                record_maps(sh, p, rd);
                 dst_meta[row] = t * sh.K + lane;
                 if (dst_w)
                     dst_w[row] = w[i];
@@ -796,8 +848,6 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan 
                                                                  int32_t* __restrict__ dst_meta,
                                                                  float* __restrict__ dst_w)
 {
-    if (*p.err)
-        return;
     const int lane = lane_id();
     const int n = sh.payload_vecs;
     const RowSlot rs = row_slot<SPLIT>(n);
@@ -805,6 +855,8 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_bf16_kernel(Shape sh, Plan 
     if (tok >= (int64_t)sh.N * sh.T)
         return;
     const int s = (int)(tok / sh.T), t = (int)(tok % sh.T);
+    if (sender_failed(sh, p, s))
+        return;
     const int my_row = pack_dest(sh, p, idx, w, dst_meta, dst_w, tok, s, t, rs.lead);
     const v4u* src = x + tok * n + rs.b0;
     for (int base = 0; base < rs.len; base += WAVE * U) {
@@ -876,8 +928,6 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
                                                                 float* __restrict__ dst_w,
                                                                 uint32_t xrun)
 {
-    if (*p.err)
-        return;
     const int lane = lane_id();
     const int n2 = sh.H / 16;                  // 16-element groups per row (= 16-byte code vectors)
     // parts hold whole 128-element blocks
@@ -886,6 +936,8 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
     if (tok >= (int64_t)sh.N * sh.T)
         return;
     const int s = (int)(tok / sh.T), t = (int)(tok % sh.T);
+    if (sender_failed(sh, p, s))
+        return;
     const int my_row = pack_dest(sh, p, idx, w, dst_meta, dst_w, tok, s, t, rs.lead);
     const int nb = sh.scale_blocks;
     const v4u* src = x + tok * (2 * n2);
@@ -987,9 +1039,12 @@ __device__ inline void copy_row(v4u* __restrict__ dst, const v4u* __restrict__ s
 
 // Modelled transfer ([EFA] "Dispatch and combine": each peer's rows leave as
 // one contiguous write; here rank d's receive row q takes send row
-// xfer_src[q], so every (s -> d) segment is copied contiguously).  Moves the
-// payload, the block scales (e4m3), the meta word and, for the expert-side
-// partial combine, the router weight.
+// xfer_src[q], so every (s -> d) segment is copied contiguously).  With the
+// fixed-slot layout the copy runs in send order instead: send row srow goes
+// to slot send_slot[srow], an address its sender formed from its own counts
+// ([EPMC] "Portable kernels").  Moves the payload, the block scales (e4m3),
+// the meta word and, for the expert-side partial combine, the router
+// weight.
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p,
                                                                 const v4u* __restrict__ send_x,
@@ -1002,16 +1057,21 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p
                                                                 float* __restrict__ recv_w,
                                                                 uint32_t xrun)
 {
-    if (*p.err)
-        return;
     const int lane = lane_id();
     const int n = sh.payload_vecs;
     const RowSlot rs = row_slot<SPLIT>(n, xcd_run_block(xrun));
-    const int64_t qp = rs.row;
-    if (qp >= sh.rows)
-        return;
-    const int64_t srow = p.xfer_src[qp];
-    const int64_t q = sh.fixed ? (int64_t)p.slot_of[qp] : qp;
+    int64_t srow, q;
+    if (sh.fixed) {
+        srow = rs.row;
+        if (srow >= sh.rows || sender_failed(sh, p, (int)(srow / ((int64_t)sh.T * sh.K))))
+            return;
+        q = p.send_slot[srow];
+    } else {
+        q = rs.row;
+        if (q >= sh.rows || *p.err)
+            return;
+        srow = p.xfer_src[q];
+    }
     if ((uint64_t)srow >= (uint64_t)sh.rows || (uint64_t)q >= (uint64_t)sh.recv_rows)
         return;
     copy_row<U>(recv_x + q * n + rs.b0, send_x + srow * n + rs.b0, rs.len, lane);
@@ -1024,6 +1084,52 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p
         recv_meta[q] = send_meta[srow];
         if (send_w)
             recv_w[q] = send_w[srow];
+    }
+}
+
+// The receiver's row maps, formed at dispatch_recv from the exchanged counts
+// and offsets alone ([EFA] "Send and receive buffers": once the counts are
+// exchanged, each rank knows where its rows come from).  One wave per
+// (expert e, sender s) pair, pairs in expert order so consecutive waves
+// write consecutive expert rows; lane i < cnt[s][e] takes the pair's i-th
+// row:
+//   expert row        r    = ebase[s][e] + i
+//   packed receive row q    = rbase[d] + roff[d][s] + soff[s][e] - soff[s][d*L] + i
+//   receive-plane row qd   = q, or the slot (e*T_max + i)*N + s
+//   send row          srow = s*T*K + soff[s][e] + i   (its place on the way back)
+// and writes shuf_map[r] (the shuffle's gather), shuf_inv[q] and slot_of[q]
+// (the combine pack's) and xfer_dst[srow] (the return transfer's and the
+// direct combine push's).
+__global__ __launch_bounds__(COPY_THREADS) void recv_map_kernel(Shape sh, Plan p)
+{
+    if (*p.err)
+        return;
+    const int64_t w = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    if (w >= (int64_t)sh.E * sh.N)
+        return;
+    const int e = (int)(w / sh.N), s = (int)(w % sh.N);
+    const int c = p.cnt[(size_t)s * sh.E + e];
+    if (c <= 0)
+        return;
+    const int d = e / sh.L;
+    const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
+    const int64_t srow0 = (int64_t)s * sh.T * sh.K + so[e];
+    const int64_t q0 = (int64_t)p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + so[e] - so[d * sh.L];
+    const int64_t r0 = p.ebase[(size_t)s * sh.E + e];
+    for (int i = lane_id(); i < c; i += WAVE) {
+        const int64_t q = q0 + i, r = r0 + i, srow = srow0 + i;
+        const int64_t qd = sh.fixed ? ((int64_t)e * sh.slots + i) * sh.N + s : q;
+        if ((uint64_t)q >= (uint64_t)sh.rows || (uint64_t)r >= (uint64_t)sh.rows ||
+            (uint64_t)srow >= (uint64_t)sh.rows || (uint64_t)qd >= (uint64_t)sh.recv_rows ||
+            (sh.fixed && i >= sh.slots)) {
+            raise_err(p, ERR_BIT_INTERNAL);
+            continue;
+        }
+        p.shuf_map[r] = make_int2((int)qd, s);
+        p.shuf_inv[q] = (int32_t)r;
+        p.xfer_dst[srow] = make_int2((int)qd, (int)r);
+        if (sh.fixed)
+            p.slot_of[q] = (int32_t)qd;
     }
 }
 
@@ -1719,6 +1825,7 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     ra.L = sh.L;
     ra.partial = sh.partial;
     ra.slot_cap = sh.fixed ? sh.slots : -1;
+    ra.offsets = !sh.sender_only;
     ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
     // keys: E experts, plus N ranks for the partial combine.  Two buffers of
     // lane masks take 16 bytes per (wave, key) and the cursors 8 bytes per
@@ -1730,6 +1837,29 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     const size_t lds = 2 * (size_t)ra.chunk_waves * nk * sizeof(uint64_t) +
                        (size_t)2 * nk * sizeof(int32_t);
     go(route_plan_kernel, dim3(sh.N), dim3(RP_NT), lds, L, ra, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_offsets(const Shape& sh, const Plan& p, const Launch& L)
+{
+    RouteArgs ra{};
+    ra.N = sh.N;
+    ra.T = sh.T;
+    ra.K = sh.K;
+    ra.E = sh.E;
+    ra.L = sh.L;
+    ra.partial = sh.partial;
+    ra.slot_cap = sh.fixed ? sh.slots : -1;
+    ra.offsets = 1;
+    ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
+    go(offsets_kernel, dim3(1), dim3(RP_NT), 0, L, ra, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_recv_map(const Shape& sh, const Plan& p, const Launch& L)
+{
+    const int64_t pairs = (int64_t)sh.E * sh.N;
+    go(recv_map_kernel, dim3(row_blocks(pairs, 1)), dim3(COPY_THREADS), 0, L, sh, p);
     return hipGetLastError();
 }
 

@@ -45,10 +45,18 @@ def test_byte_model_matches_closed_form(key, transport):
 
 def test_headline_totals():
     """The DeepSeek-R1 decode totals: 4.817 GB staged (602 us at 8 TB/s),
-    2.937 GB with direct push (367 us)."""
+    2.937 GB with direct push (367 us); of them 102 788 bytes are the
+    receiver's map kernel reading the counts and offsets (32 x 256 counts,
+    32 x 257 send offsets, 32 x 256 expert bases, 32 x 33 receive offsets,
+    33 receive bases, 4 bytes each)."""
     c = CONFIGS["C"]
-    assert sum(bench.kernel_bytes(c).values()) == 4_816_804_364
-    assert sum(bench.kernel_bytes(c, "direct").values()) == 2_937_494_028
+    assert bench.kernel_bytes(c)["recv_map"] == 4 * (2 * 32 * 256 + 32 * 257 + 32 * 33 + 33)
+    assert sum(bench.kernel_bytes(c).values()) == 4_816_804_364 + 102_788
+    assert sum(bench.kernel_bytes(c, "direct").values()) == 2_937_494_028 + 102_788
+    # fixed slots with the receiver-side combine: the offsets leave the route
+    # plan for their own kernel, the total is unchanged
+    fx = bench.kernel_bytes(c, layout="fixed")
+    assert sum(fx.values()) == sum(bench.kernel_bytes(c).values()) and fx["offsets"] > 0
 
 
 def test_partial_byte_model_moves_p_rows():

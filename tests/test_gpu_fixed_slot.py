@@ -147,3 +147,61 @@ def test_fixed_slot_capacity_error_writes_nothing():
         assert np.array_equal(gpu["out"], oracle.run_combine(y, inp["w"], d, cfg.H)["out"])
     finally:
         mep.moe_group_destroy(g)
+
+
+@pytest.mark.parametrize("transport", TRANSPORTS)
+def test_fixed_slot_senders_run_before_the_group_offsets(monkeypatch, transport):
+    """Fixed slots with the receiver-side combine: dispatch_send's kernels
+    address every row from its sender's own counts ([EPMC] "Portable
+    kernels": a sender writes to an address it knows without synchronising
+    with the other ranks), and the group offsets are formed at dispatch_recv.
+    In debug mode the offset tables are filled with -1 before dispatch_send;
+    after dispatch_send they still hold -1 (not yet computed) while every
+    slot already holds its row and meta word (the oracle's slot layout);
+    dispatch_recv then forms the offsets and the whole cycle equals the
+    oracle."""
+    from tests.gpu_util import d2h, d2h_rows
+    monkeypatch.setenv("MOE_EP_DEBUG", "1")
+    cfg = CONFIGS["B"]
+    say(f"[gpu] fixed-slot senders before offsets {cfg.describe()} transport={transport}")
+    inp = make_inputs(cfg)
+    N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
+    g = mep.moe_group_create(N, E, K, H, T, mep.MOE_BF16, transport, mep.MOE_COMBINE_RECEIVER,
+                             FIXED)
+    try:
+        x, idx, w = to_dev(torch, inp["x"]), to_dev(torch, inp["idx"]), to_dev(torch, inp["w"])
+        mep.moe_dispatch_send(g, T, x, idx)
+        torch.cuda.synchronize()
+        v = mep.moe_group_view_get(g)
+        assert np.all(d2h(v.recv_base, (N + 1,), np.int32) == -1)
+        assert np.all(d2h(v.recv_off, (N, N + 1), np.int32) == -1)
+        assert np.all(d2h(v.expert_off, (E + 1,), np.int32) == -1)
+        ref = oracle.run_dispatch_fixed(inp["x"], inp["idx"], E, T)
+        named = np.sort(ref["slot"].reshape(-1))
+        got_x = d2h_rows(v.recv_x, named, (H,), np.uint16)
+        assert np.array_equal(got_x, ref["recv_x"][named])
+        got_m = d2h_rows(v.recv_meta, named, (), np.int32)
+        assert np.array_equal(got_m, ref["recv_meta"][named])
+        # the rest of the cycle
+        R = cfg.rows
+        expert_x = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+        offs = torch.empty((E + 1,), dtype=torch.int32, device="cuda")
+        mep.moe_dispatch_recv(g, expert_x, None, offs)
+        torch.cuda.synchronize()
+        assert mep.moe_group_status(g) == mep.MOE_OK
+        assert np.array_equal(d2h(v.recv_base, (N + 1,), np.int32), ref["G"])
+        assert np.array_equal(offs.cpu().numpy(), ref["eoff"])
+        ex = expert_x.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(ex, ref["expert_x"])
+        y = oracle.expert_standin(ref["expert_x"], None, ref["eoff"], H)
+        y_dev = to_dev(torch, y).view(torch.bfloat16)
+        out = torch.empty((N, T, H), dtype=torch.bfloat16, device="cuda")
+        mep.moe_combine_send(g, y_dev)
+        mep.moe_combine_recv(g, w, out)
+        torch.cuda.synchronize()
+        assert mep.moe_group_status(g) == mep.MOE_OK
+        d = oracle.run_dispatch(inp["x"], inp["idx"], E)
+        want = oracle.run_combine(y, inp["w"], d, H)["out"]
+        assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want)
+    finally:
+        mep.moe_group_destroy(g)
