@@ -143,7 +143,7 @@ __device__ int block_exclusive_scan(int v, int* wave_sums, int* total)
 constexpr int RP_NT = 512;
 constexpr int RP_WAVES = RP_NT / WAVE;
 constexpr int BATCH = 32;
-constexpr int HELD_CHUNKS = 32;     // idx chunks kept in registers between the two passes
+constexpr int HELD_CHUNKS = 32;     // most idx chunks kept in registers between the two passes
 
 struct RouteArgs {
     const int32_t* idx;
@@ -195,7 +195,7 @@ __device__ int2 walk_column(const int32_t* __restrict__ lo, const int32_t* __res
 // soff[s][*] over the senders s, because soff[s][e] already sums sender s's
 // counts of the experts before e:
 //   eoff[e]      = sum_s soff[s][e]                 (rows of all experts < e)
-//   ebase[s][e]  = eoff[e] + sum_{s'<s} cnt[s'][e]
+//   ebase[s][e]  = eoff[e] + sum_{s'<s} cnt[s'][e]   (partial combine only)
 //   rbase[d]     = sum_s soff[s][d*L]               (rows received by ranks < d)
 //   roff[d][s]   = sum_{s'<s} (soff[s'][(d+1)L] - soff[s'][dL])
 // and the partial-row tables are the same walks over psoff[s][*] (one bucket
@@ -205,9 +205,10 @@ __device__ int2 walk_column(const int32_t* __restrict__ lo, const int32_t* __res
 //   pbase[s]     = sum_{s'<s} psoff[s'][N]          (partial rows of senders < s)
 // so one thread takes one column (E expert columns, N receiver columns, then
 // N partial columns) and walks the senders; no scan across threads.  The
-// totals need no column of their own: the last expert column's running sum
-// ends at eoff[E] = rbase[N], and the last partial column's upper bounds
-// psoff[s][N] are the per-sender totals whose running sum is pbase.
+// total rows eoff[E] = rbase[N] are the walk of soff[*][E] (or, when the
+// second walk runs, the last expert column's running sum), and the last
+// partial column's upper bounds psoff[s][N] are the per-sender totals whose
+// running sum is pbase.
 __device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* wg_err)
 {
     const int N = ra.N, E = ra.E, L = ra.L;
@@ -215,9 +216,23 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* wg_er
     const int32_t* __restrict__ cnt = p.cnt;
     const int cols = E + N + (ra.partial ? N : 0);
     for (int col = threadIdx.x; col < cols; col += RP_NT) {
-        if (col < E) {
-            // expert column e; its counts are loaded with its offsets and,
-            // for N <= BATCH, kept in registers for the second walk
+        if (col < E && !ra.partial) {
+            // expert column e: its offset alone (the receiver's map kernel
+            // forms each sender's first expert row itself)
+            const int e = col;
+            const int2 br = walk_column(soff + e, soff + e, E + 1, N, nullptr, nullptr);
+            p.eoff[e] = br.x;
+            if (e == E - 1) {
+                // every row of the cycle: the senders' totals, soff[s][E]
+                const int tot = walk_column(soff + E, soff + E, E + 1, N, nullptr, nullptr).x;
+                p.eoff[E] = tot;
+                p.rbase[N] = tot;
+            }
+        } else if (col < E) {
+            // expert column e with the partial combine: its counts are loaded
+            // with its offsets and, for N <= BATCH, kept in registers for the
+            // second walk, which forms each sender's first expert row (the
+            // pack's partial-row records name expert rows)
             const int e = col;
             int base = 0;
             int c[BATCH];
@@ -351,12 +366,12 @@ __device__ inline int pack_keys(int k1, int k2)
 // wave's mask below its lane; the per-key cursor advances by the chunk's
 // total into the other buffer.  With TWO, every item carries two keys (packed,
 // see pack_keys) from disjoint key ranges, ranked in the same pass.  Keys of
-// the first HELD_CHUNKS chunks come from registers, later ones from
+// the first HC chunks come from registers, later ones from
 // key_at(i, mine), which every thread calls.  out1[i] (out2[i]) = the item's
 // position for its first (second) key, -1 for an item without one.
-template <bool TWO, typename KeyAt>
+template <bool TWO, int HC, typename KeyAt>
 __device__ __forceinline__ void stable_ranks(int items, int nkeys, int CW, uint64_t* mask,
-                                             int32_t* cur, const int (&held)[HELD_CHUNKS],
+                                             int32_t* cur, const int (&held)[HC],
                                              KeyAt key_at, int32_t* __restrict__ out1,
                                              int32_t* __restrict__ out2)
 {
@@ -373,10 +388,10 @@ __device__ __forceinline__ void stable_ranks(int items, int nkeys, int CW, uint6
         const bool mine = tid < chunk && i < items;
         int key = TWO ? pack_keys(-1, -1) : -1;
 #pragma unroll
-        for (int h = 0; h < HELD_CHUNKS; ++h)
+        for (int h = 0; h < HC; ++h)
             if (c == h)
                 key = held[h];
-        if (c >= HELD_CHUNKS)
+        if (c >= HC)
             key = key_at(i, mine);
         const int k1 = TWO ? key & 0xFFFF : key;
         const int k2 = TWO ? (key >> 16) & 0xFFFF : NO_KEY;
@@ -446,6 +461,10 @@ __device__ __forceinline__ int rank_of_item(const RouteArgs& ra, const int32_t* 
     return d;
 }
 
+// HC: idx chunks held in registers, the fewest of 1, 2, 4, 8, 32 that cover
+// a rank's items when possible (a decode batch needs 1 or 2; fewer held
+// chunks means fewer loads and shorter unrolled loops).
+template <int HC>
 __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
 {
     extern __shared__ uint64_t lds64[];
@@ -466,7 +485,7 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     int32_t* my_pdst = ra.partial ? p.pdst + (size_t)s * items : nullptr;
     const int tid = threadIdx.x;
     const int chunk = CW * WAVE;
-    const int held_items = min(items, HELD_CHUNKS * chunk);
+    const int held_items = min(items, HC * chunk);
 
     for (int k = tid; k < NK; k += RP_NT)
         cur[k] = 0;
@@ -474,29 +493,29 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
         mask[j] = 0ull;
     if (tid == 0)
         wg_err = 0;
-    // expert ids of the first HELD_CHUNKS chunks stay in registers for both
+    // expert ids of the first HC chunks stay in registers for both
     // the counting and the ranking (thread tid takes item c*chunk + tid of
     // chunk c); all loads are issued before the first use
-    int held_e[HELD_CHUNKS];
+    int held_e[HC];
     if (items > 0) {
         // clamped addresses, so the loads are unconditional and issue together
 #pragma unroll
-        for (int c = 0; c < HELD_CHUNKS; ++c)
+        for (int c = 0; c < HC; ++c)
             held_e[c] = my_idx[min(c * chunk + tid, items - 1)];
 #pragma unroll
-        for (int c = 0; c < HELD_CHUNKS; ++c)
+        for (int c = 0; c < HC; ++c)
             if (!(tid < chunk && c * chunk + tid < items))
                 held_e[c] = -1;
     } else {
 #pragma unroll
-        for (int c = 0; c < HELD_CHUNKS; ++c)
+        for (int c = 0; c < HC; ++c)
             held_e[c] = -1;
     }
     __syncthreads();
     int bad = 0;
     if (!ra.partial) {
 #pragma unroll
-        for (int c = 0; c < HELD_CHUNKS; ++c) {
+        for (int c = 0; c < HC; ++c) {
             const int e = held_e[c];
             if ((unsigned)e < (unsigned)E)
                 atomicAdd(&cur[e], 1);
@@ -515,7 +534,7 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
         // on that rank (one partial row per (token, rank)); the held ids are
         // replaced by the packed key pair.
 #pragma unroll
-        for (int c = 0; c < HELD_CHUNKS; ++c) {
+        for (int c = 0; c < HC; ++c) {
             if (c * chunk >= items)
                 break;
             const int i = c * chunk + tid;
@@ -561,12 +580,12 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     publish_counts(cur, E, p.cnt + (size_t)s * E, p.soff + (size_t)s * (E + 1), wave_sums,
                    ra.slot_cap, &wg_err);
     if (!ra.partial) {
-        stable_ranks<false>(items, NK, CW, mask, cur, held_e,
+        stable_ranks<false, HC>(items, NK, CW, mask, cur, held_e,
                             [&](int i, bool mine) { return mine ? my_idx[i] : -1; },
                             p.pos + (size_t)s * items, nullptr);
     } else {
         publish_counts(cur + E, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums, -1, &wg_err);
-        stable_ranks<true>(items, NK, CW, mask, cur, held_e,
+        stable_ranks<true, HC>(items, NK, CW, mask, cur, held_e,
                            [&](int i, bool mine) {
                                const int e = mine ? my_idx[i] : -1;
                                bool first;
@@ -715,8 +734,12 @@ __device__ inline RowDest row_dest(const Shape& sh, const Plan& p, int s, int e,
     if (!sh.sender_only) {
         const int d = e / sh.L;
         rd.q = p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + pk - so[d * sh.L];
+        ok = ok && (uint64_t)rd.q < (uint64_t)sh.rows;
+    }
+    if (sh.partial) {
+        // the expert row, named by the partial combine's records
         rd.r = p.ebase[(size_t)s * sh.E + e] + i;
-        ok = ok && (uint64_t)rd.q < (uint64_t)sh.rows && (uint64_t)rd.r < (uint64_t)sh.rows;
+        ok = ok && (uint64_t)rd.r < (uint64_t)sh.rows;
     }
     const int64_t slot = ((int64_t)e * sh.slots + i) * sh.N + s;
     rd.qd = sh.fixed ? (int32_t)slot : rd.q;
@@ -1093,7 +1116,7 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p
 // (expert e, sender s) pair, pairs in expert order so consecutive waves
 // write consecutive expert rows; lane i < cnt[s][e] takes the pair's i-th
 // row:
-//   expert row        r    = ebase[s][e] + i
+//   expert row        r    = eoff[e] + sum_{s'<s} cnt[s'][e] + i
 //   packed receive row q    = rbase[d] + roff[d][s] + soff[s][e] - soff[s][d*L] + i
 //   receive-plane row qd   = q, or the slot (e*T_max + i)*N + s
 //   send row          srow = s*T*K + soff[s][e] + i   (its place on the way back)
@@ -1115,7 +1138,15 @@ __global__ __launch_bounds__(COPY_THREADS) void recv_map_kernel(Shape sh, Plan p
     const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
     const int64_t srow0 = (int64_t)s * sh.T * sh.K + so[e];
     const int64_t q0 = (int64_t)p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + so[e] - so[d * sh.L];
-    const int64_t r0 = p.ebase[(size_t)s * sh.E + e];
+    // the pair's first expert row: expert e's offset plus the rows of e from
+    // the senders before s (lane j adds sender j's count, then a wave sum)
+    int before = 0;
+    for (int j = lane_id(); j < s; j += WAVE)
+        before += p.cnt[(size_t)j * sh.E + e];
+#pragma unroll
+    for (int m = WAVE / 2; m >= 1; m >>= 1)
+        before += __shfl_xor(before, m, WAVE);
+    const int64_t r0 = (int64_t)p.eoff[e] + before;
     for (int i = lane_id(); i < c; i += WAVE) {
         const int64_t q = q0 + i, r = r0 + i, srow = srow0 + i;
         const int64_t qd = sh.fixed ? ((int64_t)e * sh.slots + i) * sh.N + s : q;
@@ -1836,7 +1867,18 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
                                                                                    : RP_WAVES / 8;
     const size_t lds = 2 * (size_t)ra.chunk_waves * nk * sizeof(uint64_t) +
                        (size_t)2 * nk * sizeof(int32_t);
-    go(route_plan_kernel, dim3(sh.N), dim3(RP_NT), lds, L, ra, p);
+    const int chunks = (sh.T * sh.K + ra.chunk_waves * WAVE - 1) / (ra.chunk_waves * WAVE);
+    const dim3 grid(sh.N), block(RP_NT);
+    if (chunks <= 1)
+        go(route_plan_kernel<1>, grid, block, lds, L, ra, p);
+    else if (chunks <= 2)
+        go(route_plan_kernel<2>, grid, block, lds, L, ra, p);
+    else if (chunks <= 4)
+        go(route_plan_kernel<4>, grid, block, lds, L, ra, p);
+    else if (chunks <= 8)
+        go(route_plan_kernel<8>, grid, block, lds, L, ra, p);
+    else
+        go(route_plan_kernel<HELD_CHUNKS>, grid, block, lds, L, ra, p);
     return hipGetLastError();
 }
 
