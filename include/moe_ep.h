@@ -351,7 +351,9 @@ typedef enum moe_kernel_mask { MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1 } mo
 int moe_group_timing_enable(moe_group_t g, int kernel_mask);
 int moe_group_timing_read(moe_group_t g, double* total_ms, int64_t* launches);
 
-/* Measurement aid, not part of the method: streaming kernels with the row
+/* MEASUREMENT-ONLY EXPORT, not one of the method's calls (the benchmark uses
+ * it to measure the copy ceiling the row movers are compared against).
+ * Streaming kernels with the row
  * movers' access style (16-byte nontemporal vectors, all loads of a lane in
  * flight before its stores), to measure what HBM delivers for each traffic
  * mix on this device.  kind: MOE_PROBE_COPY (read src, write dst),
