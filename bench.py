@@ -58,8 +58,9 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
     movers (4-8 bytes per row of 7-14 KiB) are an implementation detail and not
     counted.  With the partial combine (P partial rows), the router weights
     travel with the dispatched rows and combine moves P rows instead of R.
-    The receiver's map kernel reads the counts and offsets (its maps, like the
-    pack's, are not counted); with fixed slots and the receiver-side combine
+    The receiver's map kernel reads the counts and offsets and writes its
+    maps, 20 bytes per row (24 with fixed slots): the maps are its whole job,
+    so they are counted there; with fixed slots and the receiver-side combine
     the group offsets move from the route plan to their own kernel."""
     N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
     R = N * T * K
@@ -80,7 +81,8 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
         "combine_pack": 2 * R * hy,
         "transfer_back": 2 * R * hy,
         "combine_reduce": R * hy + R * 8 + tokens * H * 2,
-        "recv_map": N * E * 4 * 2 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4,
+        "recv_map": (N * E * 4 * 2 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4
+                     + R * (20 + (4 if layout == "fixed" else 0))),
     }
     if layout == "fixed" and combine == "receiver":
         offs = (N * E * 4 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4 + (E + 1) * 4
@@ -256,17 +258,27 @@ def _partial_rows_of(cfg, combine: str) -> int:
     return partial_rows(cfg, make_routing(cfg)[0])
 
 
-def trace_summary(cfg, db: str) -> str:
-    """Markdown table of the library's kernels from a rocprofv3 kernel trace."""
+def trace_summary(cfg, db: str, timed=None) -> str:
+    """Markdown table of the library's kernels from a rocprofv3 kernel trace.
+    With timed = (steps, warmup) of the traced bench command, a column with
+    each kernel's average over the launches of its timed region (the
+    MALL-flushed steps): per kernel, launch 1 is the first cycle, then warmup
+    steps, max(10, warmup) all-kernel timing steps, `steps` warm steps, then
+    the `steps` timed ones."""
     import sqlite3
     con = sqlite3.connect(db)
     acc = {}
-    for name, dur in con.execute("select name, duration from kernels"):
+    for name, dur in con.execute("select name, duration from kernels order by start"):
         key = _kernel_key(name)
         if key is not None:
             acc.setdefault(key, []).append(dur / 1000.0)
-    lines = ["| kernel | launches | avg us | min us | max us | algorithmic GB/s |",
-             "|---|---|---|---|---|---|"]
+    first = None if timed is None else 1 + timed[1] + max(10, timed[1]) + timed[0]
+    head = "| kernel | launches | avg us | min us | max us | algorithmic GB/s |"
+    rule = "|---|---|---|---|---|---|"
+    if first is not None:
+        head += " timed-region avg us |"
+        rule += "---|"
+    lines = [head, rule]
     transport = "staged" if "transfer" in acc else "direct"
     combine = "partial" if "partial_send" in acc else "receiver"
     layout = "fixed" if "offsets" in acc else "packed"
@@ -277,9 +289,64 @@ def trace_summary(cfg, db: str) -> str:
         if key in acc:
             v = acc[key]
             avg = sum(v) / len(v)
-            lines.append(f"| {key} | {len(v)} | {avg:.2f} | {min(v):.2f} | {max(v):.2f} | "
-                         f"{kb[key] / (avg * 1e-6) / 1e9:.0f} |")
+            line = (f"| {key} | {len(v)} | {avg:.2f} | {min(v):.2f} | {max(v):.2f} | "
+                    f"{kb[key] / (avg * 1e-6) / 1e9:.0f} |")
+            if first is not None:
+                t = v[first:first + timed[0]]
+                line += f" {sum(t) / len(t):.2f} |" if t else " - |"
+            lines.append(line)
     return "\n".join(lines)
+
+
+def traffic_xcheck(cfg, dram_db, cal_dram_db, req_db, cal_req_db, traffic_json) -> dict:
+    """HBM bytes per launch from two more counter families, each calibrated on
+    the plain copy of CAL_BYTES each way, beside the FETCH_SIZE/WRITE_SIZE
+    figures of traffic_json: (a) requests to DRAM (TCC_EA0_RDREQ_DRAM_sum,
+    TCC_EA0_WRREQ_DRAM_sum) times the bytes per request the copy shows, (b)
+    the raw EA requests (TCC_EA0_RDREQ_sum / _32B_sum, TCC_EA0_WRREQ_sum /
+    _64B_sum) sized 32/64 bytes as FETCH_SIZE's formula does, scaled like it."""
+    def per_kernel(db, ctr):
+        acc = _counter_by_kernel(db, ctr)
+        out = {}
+        for name, vals in acc.items():
+            k = _kernel_key(name)
+            if k:
+                out[k] = sum(vals) / len(vals)
+        cal = max((v for v in acc.values() if len(v) >= 5), key=sum, default=None)
+        return out, (sum(cal) / len(cal) if cal else None)
+    rd = per_kernel(dram_db, "TCC_EA0_RDREQ_DRAM_sum")[0]
+    wr = per_kernel(dram_db, "TCC_EA0_WRREQ_DRAM_sum")[0]
+    b_rd = CAL_BYTES / per_kernel(cal_dram_db, "TCC_EA0_RDREQ_DRAM_sum")[1]
+    b_wr = CAL_BYTES / per_kernel(cal_dram_db, "TCC_EA0_WRREQ_DRAM_sum")[1]
+    names = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_WRREQ_sum",
+             "TCC_EA0_WRREQ_64B_sum")
+    q = {c: per_kernel(req_db, c)[0] for c in names}
+    cq = {c: per_kernel(cal_req_db, c)[1] for c in names}
+
+    def rbytes(r, r32):
+        return 32 * r32 + 64 * (r - r32)
+
+    def wbytes(w, w64):
+        return 64 * w64 + 32 * (w - w64)
+    f_rd = CAL_BYTES / rbytes(cq[names[0]], cq[names[1]])
+    f_wr = CAL_BYTES / wbytes(cq[names[2]], cq[names[3]])
+    with open(traffic_json) as f:
+        tj = json.load(f)
+    rows = {}
+    for k, rec in tj["kernels"].items():
+        if k not in rd:
+            continue
+        dram = rd[k] * b_rd + wr[k] * b_wr
+        ea = (rbytes(q[names[0]][k], q[names[1]][k]) * f_rd
+              + wbytes(q[names[2]][k], q[names[3]][k]) * f_wr)
+        fw = rec["hbm_bytes_per_launch"]
+        rows[k] = {"fetch_write_size": fw, "dram_requests": round(dram), "ea_requests": round(ea),
+                   "dram_over_fetch_write": round(dram / fw, 4),
+                   "ea_over_fetch_write": round(ea / fw, 4)}
+    return {"workload": cfg.describe(), "source_hash": kernel_source_hash(),
+            "bytes_per_dram_read_request": round(b_rd, 3),
+            "bytes_per_dram_write_request": round(b_wr, 3),
+            "ea_read_factor": round(f_rd, 4), "ea_write_factor": round(f_wr, 4), "kernels": rows}
 
 
 def _hip_runtime():
@@ -603,6 +670,13 @@ def main() -> int:
                     help="measure the send/recv split hiding a concurrent GEMM (prints one JSON line)")
     ap.add_argument("--trace-summary", metavar="DB",
                     help="print a table of the library's kernels from a rocprofv3 kernel trace")
+    ap.add_argument("--trace-timed", action="store_true",
+                    help="with --trace-summary: add each kernel's average over the timed region "
+                         "of a traced bench command run with these --steps / --warmup")
+    ap.add_argument("--traffic-xcheck", nargs=5, metavar=("DRAM_DB", "CAL_DRAM_DB", "REQ_DB",
+                                                          "CAL_REQ_DB", "TRAFFIC_JSON"),
+                    help="print the HBM bytes per kernel from the DRAM and EA request counters "
+                         "beside the FETCH_SIZE/WRITE_SIZE figures of TRAFFIC_JSON")
     args = ap.parse_args()
     from workloads import CONFIGS as _configs
     if args.config not in _configs:
@@ -621,11 +695,14 @@ def main() -> int:
         from workloads import CONFIGS
         print(json.dumps(overlap_demo(CONFIGS[args.config], args)), flush=True)
         return 0
-    if args.traffic_from or args.trace_summary:
+    if args.traffic_from or args.trace_summary or args.traffic_xcheck:
         from workloads import CONFIGS
         cfg = CONFIGS[args.config]
         if args.trace_summary:
-            print(trace_summary(cfg, args.trace_summary))
+            print(trace_summary(cfg, args.trace_summary,
+                                (args.steps, args.warmup) if args.trace_timed else None))
+        if args.traffic_xcheck:
+            print(json.dumps(traffic_xcheck(cfg, *args.traffic_xcheck), indent=1))
         if args.traffic_from:
             rec = traffic_from(cfg, *args.traffic_from, transport=args.transport,
                                combine=args.combine)

@@ -3,6 +3,7 @@ closed-form totals of the method (every mandated buffer written once and read
 once by the next stage), the partial-row count against brute force, the
 counter scaling and trace tables on small synthetic profiler databases, the
 source hash's indifference to comments, and the one-GPU guard."""
+import json
 import os
 import sqlite3
 import subprocess
@@ -37,26 +38,29 @@ def test_byte_model_matches_closed_form(key, transport):
     kb = bench.kernel_bytes(cfg, transport)
     total = sum(kb.values())
     main = _closed_form(cfg, transport)
-    # the rest is metadata: a few int32 per row and the per-rank tables
+    # the rest is metadata: a few int32 per row (ids, positions, meta words,
+    # the receiver's 20 bytes of row maps) and the per-rank tables
     R, N, E = cfg.rows, cfg.N, cfg.E
-    small = 64 * R + 64 * N * E + 16 * N * (N + 1) + 64 * E
+    small = 96 * R + 64 * N * E + 16 * N * (N + 1) + 64 * E
     assert main <= total <= main + small, (total, main)
 
 
 def test_headline_totals():
     """The DeepSeek-R1 decode totals: 4.817 GB staged (602 us at 8 TB/s),
-    2.937 GB with direct push (367 us); of them 102 788 bytes are the
-    receiver's map kernel reading the counts and offsets (32 x 256 counts,
+    2.937 GB with direct push (367 us); of them 758 148 bytes are the
+    receiver's map kernel: reading the counts and offsets (32 x 256 counts,
     32 x 257 send offsets, 32 x 256 expert bases, 32 x 33 receive offsets,
-    33 receive bases, 4 bytes each)."""
+    33 receive bases, 4 bytes each) and writing 20 bytes of maps per row."""
     c = CONFIGS["C"]
-    assert bench.kernel_bytes(c)["recv_map"] == 4 * (2 * 32 * 256 + 32 * 257 + 32 * 33 + 33)
-    assert sum(bench.kernel_bytes(c).values()) == 4_816_804_364 + 102_788
-    assert sum(bench.kernel_bytes(c, "direct").values()) == 2_937_494_028 + 102_788
+    maps = 4 * (2 * 32 * 256 + 32 * 257 + 32 * 33 + 33) + 32768 * 20
+    assert bench.kernel_bytes(c)["recv_map"] == maps == 758_148
+    assert sum(bench.kernel_bytes(c).values()) == 4_816_804_364 + maps
+    assert sum(bench.kernel_bytes(c, "direct").values()) == 2_937_494_028 + maps
     # fixed slots with the receiver-side combine: the offsets leave the route
     # plan for their own kernel, the total is unchanged
     fx = bench.kernel_bytes(c, layout="fixed")
-    assert sum(fx.values()) == sum(bench.kernel_bytes(c).values()) and fx["offsets"] > 0
+    assert sum(fx.values()) == sum(bench.kernel_bytes(c).values()) + 32768 * 4
+    assert fx["offsets"] > 0
 
 
 def test_partial_byte_model_moves_p_rows():
@@ -130,12 +134,13 @@ def test_trace_summary_table(tmp_path):
     cfg = CONFIGS["C"]
     db = tmp_path / "trace.db"
     con = sqlite3.connect(db)
-    con.execute("create table kernels (name text, duration integer)")
-    rows = [("void moe::(anonymous namespace)::transfer_kernel<4, 4>(...)", d)
-            for d in (150_000, 160_000, 170_000)]
-    rows += [("void moe::(anonymous namespace)::route_plan_kernel(moe::RouteArgs, moe::Plan)", 12_000)]
-    rows += [("void at::native::vectorized_elementwise_kernel<4>(...)", 5_000)]
-    con.executemany("insert into kernels values (?, ?)", rows)
+    con.execute("create table kernels (name text, start integer, duration integer)")
+    rows = [("void moe::(anonymous namespace)::transfer_kernel<4, 4>(...)", i, d)
+            for i, d in enumerate((150_000, 160_000, 170_000))]
+    rows += [("void moe::(anonymous namespace)::route_plan_kernel(moe::RouteArgs, moe::Plan)", 9,
+              12_000)]
+    rows += [("void at::native::vectorized_elementwise_kernel<4>(...)", 10, 5_000)]
+    con.executemany("insert into kernels values (?, ?, ?)", rows)
     con.commit()
     con.close()
     table = bench.trace_summary(cfg, str(db)).splitlines()
@@ -178,3 +183,58 @@ def test_traffic_summary_names():
     assert key(config="D", transport="staged", combine="receiver", layout="fixed") == "D_fixed"
     h = bench.kernel_source_hash()
     assert bench.measured_traffic("C_fixed", "transfer", h) is None
+
+
+def test_trace_summary_timed_region(tmp_path):
+    """The timed-region column averages each kernel's launches after the
+    first cycle, the warmup, the all-kernel timing pass and the warm leg."""
+    cfg = CONFIGS["C"]
+    db = tmp_path / "trace.db"
+    con = sqlite3.connect(db)
+    con.execute("create table kernels (name text, start integer, duration integer)")
+    steps, warmup = 3, 2
+    first = 1 + warmup + 10 + steps
+    durs = [100_000] * first + [200_000, 210_000, 220_000] + [100_000] * steps
+    name = "void moe::(anonymous namespace)::transfer_kernel<4, 4>(...)"
+    con.executemany("insert into kernels values (?, ?, ?)",
+                    [(name, 1000 - i, d) for i, d in enumerate(reversed(durs))])
+    con.commit()
+    con.close()
+    table = bench.trace_summary(cfg, str(db), (steps, warmup)).splitlines()
+    assert table[0].endswith("timed-region avg us |")
+    cells = [c.strip() for c in table[2].split("|")[1:-1]]
+    assert cells[0] == "transfer" and cells[-1] == "210.00"
+
+
+def test_traffic_cross_check_from_request_counters(tmp_path):
+    """The DRAM-request bytes per request and the EA-request factors come from
+    the calibration copy; a kernel whose requests match the copy's moves the
+    copy's bytes."""
+    cfg = CONFIGS["C"]
+    cal = bench.CAL_BYTES
+    copy_name = "void at::native::elementwise_kernel<128, 4>(int, Func)"
+    tr = "void moe::(anonymous namespace)::transfer_kernel<4, 4>(moe::Shape, ...)"
+    # the copy: 128-byte DRAM reads, 64-byte DRAM writes; EA reads of 128 B
+    # counted as 64 by the formula, 64-byte EA writes
+    _counters_db(tmp_path / "cal_d.db", [(copy_name, "TCC_EA0_RDREQ_DRAM_sum", cal / 128),
+                                         (copy_name, "TCC_EA0_WRREQ_DRAM_sum", cal / 64)] * 5)
+    _counters_db(tmp_path / "cal_q.db", [(copy_name, "TCC_EA0_RDREQ_sum", cal / 128),
+                                         (copy_name, "TCC_EA0_RDREQ_32B_sum", 0),
+                                         (copy_name, "TCC_EA0_WRREQ_sum", cal / 64),
+                                         (copy_name, "TCC_EA0_WRREQ_64B_sum", cal / 64)] * 5)
+    _counters_db(tmp_path / "d.db", [(tr, "TCC_EA0_RDREQ_DRAM_sum", cal / 128),
+                                     (tr, "TCC_EA0_WRREQ_DRAM_sum", cal / 64)] * 3)
+    _counters_db(tmp_path / "q.db", [(tr, "TCC_EA0_RDREQ_sum", cal / 128),
+                                     (tr, "TCC_EA0_RDREQ_32B_sum", 0),
+                                     (tr, "TCC_EA0_WRREQ_sum", cal / 64),
+                                     (tr, "TCC_EA0_WRREQ_64B_sum", cal / 64)] * 3)
+    tj = tmp_path / "traffic.json"
+    tj.write_text(json.dumps({"kernels": {"transfer": {"hbm_bytes_per_launch": 2 * cal}}}))
+    rec = bench.traffic_xcheck(cfg, str(tmp_path / "d.db"), str(tmp_path / "cal_d.db"),
+                               str(tmp_path / "q.db"), str(tmp_path / "cal_q.db"), str(tj))
+    assert rec["bytes_per_dram_read_request"] == 128.0
+    assert rec["bytes_per_dram_write_request"] == 64.0
+    assert rec["ea_read_factor"] == 2.0 and rec["ea_write_factor"] == 1.0
+    t = rec["kernels"]["transfer"]
+    assert t["dram_requests"] == 2 * cal and t["ea_requests"] == 2 * cal
+    assert t["dram_over_fetch_write"] == 1.0 and t["ea_over_fetch_write"] == 1.0
