@@ -50,6 +50,11 @@ def partial_rows(cfg, idx) -> int:
     return int(np.unique(tok * N + d).size)
 
 
+# A sender's tokens up to this size make the staged pack run in send-row order
+# (the library's rule).
+PACK_ROWS_MAX_SENDER_BYTES = 2 << 20
+
+
 def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: int = 0,
                  layout: str = "packed") -> dict:
     """Algorithmic HBM bytes per launch of each kernel: every buffer the method
@@ -61,7 +66,10 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
     The receiver's map kernel reads the counts and offsets and writes its
     maps, 20 bytes per row (24 with fixed slots): the maps are its whole job,
     so they are counted there; with fixed slots and the receiver-side combine
-    the group offsets move from the route plan to their own kernel."""
+    the group offsets move from the route plan to their own kernel.  When the
+    pack runs in send-row order (staged, receiver-side combine, a sender's
+    tokens within 2 MiB) the route plan writes the send rows' meta words and
+    the pack reads them in place of the positions."""
     N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
     R = N * T * K
     fp8 = cfg.dtype == "fp8"
@@ -84,6 +92,9 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
         "recv_map": (N * E * 4 * 2 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4
                      + R * (20 + (4 if layout == "fixed" else 0))),
     }
+    if transport == "staged" and combine == "receiver" and T * H * 2 <= PACK_ROWS_MAX_SENDER_BYTES:
+        kb["route_plan"] += R * 4
+        kb["pack"] -= R * 4
     if layout == "fixed" and combine == "receiver":
         offs = (N * E * 4 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4 + (E + 1) * 4
                 + N * E * 4)

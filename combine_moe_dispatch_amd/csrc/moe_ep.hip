@@ -552,7 +552,7 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const in
     if (g->debug && (rc = poison_dispatch_send(g, stream)))
         return rc;
     if ((rc = timed_launch(g, MOE_KERNEL_ROUTE_PLAN, stream, true, [&](const Launch& L) {
-             return moe::launch_route_plan(sh, topk_idx, g->plan, L);
+             return moe::launch_route_plan(sh, topk_idx, g->plan, rows, L);
          })) ||
         (rc = timed_launch(g, MOE_KERNEL_PACK, stream, any, [&](const Launch& L) {
              return moe::launch_pack(sh, x, topk_idx, partial ? topk_weights : nullptr, g->plan,

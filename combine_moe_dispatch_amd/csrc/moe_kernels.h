@@ -104,7 +104,8 @@ struct Launch {
     hipEvent_t stop;
 };
 
-hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, const Launch& L);
+hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, const Rows& r,
+                             const Launch& L);
 hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const float* w,
                        const Plan& p, const Rows& r, const Launch& L);
 hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, const Launch& L);

@@ -27,7 +27,6 @@ namespace {
 // Native clang vectors (not HIP's struct wrappers) so that a value can be an
 // inline-asm register operand.
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
 constexpr int ROWS_PER_BLOCK = 4;          // waves per 256-thread block
@@ -61,7 +60,6 @@ __device__ inline void hold(v4u (&v)[U])
 // tables (maps, offsets) from the caches.
 __device__ inline v4u ld_nt(const v4u* p) { return __builtin_nontemporal_load(p); }
 __device__ inline void st_nt(const v4u& v, v4u* p) { __builtin_nontemporal_store(v, p); }
-__device__ inline void st_nt(const v2u& v, v2u* p) { __builtin_nontemporal_store(v, p); }
 
 __device__ inline int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
@@ -152,6 +150,7 @@ struct RouteArgs {
     int partial;            // also plan the expert-side partial rows
     int slot_cap;           // fixed-slot layout: most rows per (sender, expert); -1: none
     int offsets;            // the last workgroup computes the group offsets
+    int32_t* send_meta;     // when set: each send row's item t*K+k, written with the positions
     int64_t cap;
 };
 
@@ -368,12 +367,14 @@ __device__ inline int pack_keys(int k1, int k2)
 // see pack_keys) from disjoint key ranges, ranked in the same pass.  Keys of
 // the first HC chunks come from registers, later ones from
 // key_at(i, mine), which every thread calls.  out1[i] (out2[i]) = the item's
-// position for its first (second) key, -1 for an item without one.
+// position for its first (second) key, -1 for an item without one; inv1
+// (when given) the inverse of out1: inv1[position] = i.
 template <bool TWO, int HC, typename KeyAt>
 __device__ __forceinline__ void stable_ranks(int items, int nkeys, int CW, uint64_t* mask,
                                              int32_t* cur, const int (&held)[HC],
                                              KeyAt key_at, int32_t* __restrict__ out1,
-                                             int32_t* __restrict__ out2)
+                                             int32_t* __restrict__ out2,
+                                             int32_t* __restrict__ inv1)
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
     const int chunk = CW * WAVE;
@@ -411,6 +412,8 @@ __device__ __forceinline__ void stable_ranks(int items, int nkeys, int CW, uint6
             for (int w = 0; w < wave; ++w)
                 before += __popcll(mA[(size_t)w * nkeys + k1]);
             out1[i] = before;
+            if (inv1)
+                inv1[before] = i;
         } else if (mine) {
             out1[i] = -1;
         }
@@ -582,7 +585,8 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     if (!ra.partial) {
         stable_ranks<false, HC>(items, NK, CW, mask, cur, held_e,
                             [&](int i, bool mine) { return mine ? my_idx[i] : -1; },
-                            p.pos + (size_t)s * items, nullptr);
+                            p.pos + (size_t)s * items, nullptr,
+                            ra.send_meta ? ra.send_meta + (size_t)s * items : nullptr);
     } else {
         publish_counts(cur + E, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums, -1, &wg_err);
         stable_ranks<true, HC>(items, NK, CW, mask, cur, held_e,
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
                                return pack_keys((unsigned)e < (unsigned)E ? e : -1,
                                                 first ? E + d : -1);
                            },
-                           p.pos + (size_t)s * items, p.ppos + (size_t)s * items);
+                           p.pos + (size_t)s * items, p.ppos + (size_t)s * items, nullptr);
     }
 
     // Publish this rank's counts and error bits and draw a ticket.  Every
@@ -930,6 +934,52 @@ __device__ inline uint32_t e4m3_encode(float v)
     return sign | c;
 }
 
+// Block-scaled e4m3 of a lane's U 16-element groups (two input vectors of
+// bf16 each, va[u] the first 8 elements and vb[u] the next 8): the 16 codes
+// of each group as one vector, and its block's scale.  A 128-element block is
+// 8 consecutive lanes (the same u), which share amax through xor shuffles, so
+// every lane of the wave must call it.
+template <int U>
+__device__ inline void quant_groups(const v4u (&va)[U], const v4u (&vb)[U], v4u (&q)[U],
+                                    float (&sc)[U])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float f[16];
+        const uint32_t bits[8] = {va[u].x, va[u].y, va[u].z, va[u].w,
+                                  vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            f[2 * i] = __uint_as_float(bits[i] << 16);
+            f[2 * i + 1] = __uint_as_float(bits[i] & 0xFFFF0000u);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            amax = fmaxf(amax, fabsf(f[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, WAVE));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, WAVE));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
+        float inv = 0.0f, scale = 1.0f;
+        if (amax >= 0x1.cp-118f) {             // 448 * 2^-126
+            inv = 448.0f / amax;
+            scale = amax / 448.0f;
+        } else if (amax > 0.0f) {
+            inv = 0x1p126f;
+            scale = 0x1p-126f;
+        }
+        uint32_t c[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            c[i] = e4m3_encode(f[i] * inv);
+        q[u].x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        q[u].y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+        q[u].z = c[8] | (c[9] << 8) | (c[10] << 16) | (c[11] << 24);
+        q[u].w = c[12] | (c[13] << 8) | (c[14] << 16) | (c[15] << 24);
+        sc[u] = scale;
+    }
+}
+
 // [EFA] "Dispatch/combine latency": block-scaled fp8 dispatch; the blocks are
 // 128 elements with one fp32 scale each.  Per block: amax = max|x| (exact from
 // bf16); for amax >= 448 * 2^-126, inv = 448/amax and scale = amax/448 as
@@ -983,41 +1033,7 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
         hold(vb);
         v4u q[U];
         float sc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float f[16];
-            const uint32_t bits[8] = {va[u].x, va[u].y, va[u].z, va[u].w,
-                                      vb[u].x, vb[u].y, vb[u].z, vb[u].w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                f[2 * i] = __uint_as_float(bits[i] << 16);
-                f[2 * i + 1] = __uint_as_float(bits[i] & 0xFFFF0000u);
-            }
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                amax = fmaxf(amax, fabsf(f[i]));
-            amax = fmaxf(amax, __shfl_xor(amax, 4, WAVE));
-            amax = fmaxf(amax, __shfl_xor(amax, 2, WAVE));
-            amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
-            float inv = 0.0f, scale = 1.0f;
-            if (amax >= 0x1.cp-118f) {         // 448 * 2^-126
-                inv = 448.0f / amax;
-                scale = amax / 448.0f;
-            } else if (amax > 0.0f) {
-                inv = 0x1p126f;
-                scale = 0x1p-126f;
-            }
-            uint32_t c[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                c[i] = e4m3_encode(f[i] * inv);
-            q[u].x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-            q[u].y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-            q[u].z = c[8] | (c[9] << 8) | (c[10] << 16) | (c[11] << 24);
-            q[u].w = c[12] | (c[13] << 8) | (c[14] << 16) | (c[15] << 24);
-            sc[u] = scale;
-        }
+        quant_groups<U>(va, vb, q, sc);
         for (int k = 0; k < sh.K; ++k) {
             const int row32 = readlane(my_row, k);
             if ((uint64_t)row32 >= (uint64_t)(sh.direct ? sh.recv_rows : sh.rows))
@@ -1034,6 +1050,134 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Pack in send-row order (staged transport, receiver-side combine): the same
+// rows as the token-order kernels above, written as a gather.  The route plan
+// has already written each send row's meta word t*K+k (the item it holds), so
+// send row (s, pk) reads its token's row x[s][t] and writes it (quantised,
+// for e4m3) in place: the writes stream through the send buffer in address
+// order, as the movers' do, and each token is read K times, mostly from cache
+// (a sender's tokens are a few MiB, and one XCD takes a run of its send
+// rows).  The lead wave also records the transfer's map, which needs the
+// item's expert (idx) and the offsets: one more dependent load that no other
+// wave waits for.
+// ---------------------------------------------------------------------------
+__device__ inline void record_send_row(const Shape& sh, const Plan& p,
+                                       const int32_t* __restrict__ idx, int s, int pk, int m)
+{
+    const int64_t TK = (int64_t)sh.T * sh.K;
+    const int e = idx[s * TK + m];
+    if ((unsigned)e >= (unsigned)sh.E) {
+        raise_err(p, ERR_BIT_INTERNAL);
+        return;
+    }
+    const RowDest rd = row_dest(sh, p, s, e, pk);
+    if (rd.ok)
+        record_maps(sh, p, rd);
+    else
+        raise_err(p, ERR_BIT_INTERNAL);
+}
+
+template <int U, int SPLIT>
+__global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, Plan p,
+                                                                      const v4u* __restrict__ x,
+                                                                      const int32_t* __restrict__ idx,
+                                                                      const int32_t* __restrict__ send_meta,
+                                                                      v4u* __restrict__ send_x,
+                                                                      uint32_t xrun)
+{
+    const int lane = lane_id();
+    const int n = sh.payload_vecs;
+    const RowSlot rs = row_slot<SPLIT>(n, xcd_run_block(xrun));
+    const int64_t TK = (int64_t)sh.T * sh.K;
+    const int64_t srow = rs.row;
+    if (srow >= sh.rows)
+        return;
+    const int s = (int)(srow / TK), pk = (int)(srow - s * TK);
+    if (sender_failed(sh, p, s))
+        return;
+    const int m = send_meta[srow];
+    if ((unsigned)m >= (unsigned)TK) {
+        if (rs.lead && lane == 0)
+            raise_err(p, ERR_BIT_INTERNAL);
+        return;
+    }
+    const v4u* src = x + ((int64_t)s * sh.T + m / sh.K) * n + rs.b0;
+    v4u* dst = send_x + srow * n + rs.b0;
+    for (int base = 0; base < rs.len; base += WAVE * U) {
+        // ordinary loads: the token's other K-1 rows read it again
+        v4u v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = src[min(base + u * WAVE + lane, rs.len - 1)];
+        hold(v);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * WAVE + lane;
+            if (j < rs.len)
+                st_nt(v[u], dst + j);
+        }
+    }
+    if (rs.lead && lane == 0)
+        record_send_row(sh, p, idx, s, pk, m);
+}
+
+template <int U, int SPLIT>
+__global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(Shape sh, Plan p,
+                                                                     const v4u* __restrict__ x,
+                                                                     const int32_t* __restrict__ idx,
+                                                                     const int32_t* __restrict__ send_meta,
+                                                                     v4u* __restrict__ send_q,
+                                                                     float* __restrict__ send_scale,
+                                                                     uint32_t xrun)
+{
+    const int lane = lane_id();
+    const int n2 = sh.H / 16;
+    const RowSlot rs = row_slot<SPLIT, 8>(n2, xcd_run_block(xrun));
+    const int64_t TK = (int64_t)sh.T * sh.K;
+    const int64_t srow = rs.row;
+    if (srow >= sh.rows)
+        return;
+    const int s = (int)(srow / TK), pk = (int)(srow - s * TK);
+    if (sender_failed(sh, p, s))
+        return;
+    const int m = send_meta[srow];
+    if ((unsigned)m >= (unsigned)TK) {
+        if (rs.lead && lane == 0)
+            raise_err(p, ERR_BIT_INTERNAL);
+        return;
+    }
+    const int nb = sh.scale_blocks;
+    const v4u* src = x + ((int64_t)s * sh.T + m / sh.K) * (2 * n2);
+    const int end = rs.b0 + rs.len;
+    for (int base = rs.b0; base < end; base += WAVE * U) {
+        // clamped loads; 8-lane groups lie wholly inside or past the part
+        v4u va[U], vb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = min(base + u * WAVE + lane, end - 1);
+            va[u] = src[2 * j];
+            vb[u] = src[2 * j + 1];
+        }
+        hold(va);
+        hold(vb);
+        v4u q[U];
+        float sc[U];
+        quant_groups<U>(va, vb, q, sc);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * WAVE + lane;
+            if (j < end) {
+                st_nt(q[u], send_q + srow * n2 + j);
+                if ((lane & 7) == 0)
+                    send_scale[srow * nb + j / 8] = sc[u];
+            }
+        }
+    }
+    if (rs.lead && lane == 0)
+        record_send_row(sh, p, idx, s, pk, m);
 }
 
 // ---------------------------------------------------------------------------
@@ -1843,12 +1987,30 @@ inline unsigned row_blocks(int64_t rows, int split)
             go((KERNEL<4, 8>), grid_, block_, 0, __VA_ARGS__);                                     \
     } while (0)
 
+// Whether the pack runs in send-row order (its rows' meta words then come
+// from the route plan): the staged transport with the receiver-side combine,
+// when one sender's tokens fit well within an XCD's 4 MiB L2, so that the K
+// reads of each token after the first hit it.  DeepSeek-R1 decode (1.75 MiB
+// per sender, one sender per XCD run): pack 86.9 -> 74.5 us warm, 115 -> 99
+// MALL-flushed; on the prefill (28 MiB per sender) the row order re-reads
+// every token from HBM or the MALL and took 4.9-5.0 ms against 1.87 in token
+// order.  The direct push writes receive rows and the partial combine's
+// records are made per token, so those keep the token-order kernels.
+constexpr int64_t PACK_ROWS_MAX_SENDER_BYTES = 2 << 20;
+
+inline bool pack_in_row_order(const Shape& sh)
+{
+    return !sh.direct && !sh.partial && (int64_t)sh.T * sh.H * 2 <= PACK_ROWS_MAX_SENDER_BYTES;
+}
+
 }  // namespace
 
-hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, const Launch& L)
+hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p, const Rows& r,
+                             const Launch& L)
 {
     RouteArgs ra;
     ra.idx = idx;
+    ra.send_meta = pack_in_row_order(sh) ? r.send_meta : nullptr;
     ra.N = sh.N;
     ra.T = sh.T;
     ra.K = sh.K;
@@ -1934,6 +2096,18 @@ inline uint32_t fixed_run(int64_t blocks, uint32_t run)
     return blocks < XCD_RUN_MIN_BLOCKS ? 1u : run;
 }
 
+// The send-row-order pack takes runs of one sender's rows (T*K rows), so an
+// XCD reads one sender's tokens at a time: 86.9 -> 74.5 us on DeepSeek-R1
+// decode, where runs of 128 blocks (107 us) and plain order (92.5 us) were
+// slower.
+inline uint32_t sender_run(const Shape& sh, const RowShape& rsh)
+{
+    if ((int64_t)row_blocks(sh.rows, rsh.split) < XCD_RUN_MIN_BLOCKS)
+        return 1;
+    const int64_t run = row_blocks((int64_t)sh.T * sh.K, rsh.split);
+    return (uint32_t)std::min<int64_t>(run, (int64_t)1 << 24);
+}
+
 hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const float* w,
                        const Plan& p, const Rows& r, const Launch& L)
 {
@@ -1941,6 +2115,22 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
     const int64_t tokens = (int64_t)sh.N * sh.T;
     if (tokens == 0)
         return hipSuccess;
+    if (pack_in_row_order(sh)) {
+        if (sh.fp8) {
+            RowShape rsh = row_shape(sh.H / 16);
+            if (rsh.u > 4)
+                rsh.u = 4;
+            MOE_DISPATCH_ROW(rsh, pack_rows_fp8_kernel, sh.rows, L, sh, p, (const v4u*)x, idx,
+                             r.send_meta, (v4u*)r.send_x, r.send_scale,
+                             sender_run(sh, rsh));
+        } else {
+            const RowShape rsh = row_shape(sh.payload_vecs);
+            MOE_DISPATCH_ROW(rsh, pack_rows_bf16_kernel, sh.rows, L, sh, p, (const v4u*)x, idx,
+                             r.send_meta, (v4u*)r.send_x,
+                             sender_run(sh, rsh));
+        }
+        return hipGetLastError();
+    }
     if (sh.fp8) {
         // a row is H/16 groups of 16 elements (16 codes out per lane); each
         // lane holds two input vectors per group, so at most 4 groups per
