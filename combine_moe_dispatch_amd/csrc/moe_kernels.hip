@@ -150,6 +150,7 @@ struct RouteArgs {
     int partial;            // also plan the expert-side partial rows
     int slot_cap;           // fixed-slot layout: most rows per (sender, expert); -1: none
     int offsets;            // the last workgroup computes the group offsets
+    int table_lds;          // ... from a copy of soff in the dynamic LDS
     int32_t* send_meta;     // when set: each send row's item t*K+k, written with the positions
     int64_t cap;
 };
@@ -286,15 +287,101 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* wg_er
     }
 }
 
+// The same tables (receiver-side combine) from a copy of soff[N][E+1] in LDS,
+// for small tables: the copy is one round of 16-byte loads (up to TAB_VECS per
+// thread), and the column walks then read LDS only, where each walk above
+// issues its BATCH loads per column (64 for a receiver column, past the 63 a
+// wave can have in flight).  Mixtral decode (72 ints): the last workgroup's
+// part 4.1 -> 2.0 us; DeepSeek-R1 decode (8224 ints) measured 3.8 us either
+// way, the copy's round trip taking what the walks saved.
+constexpr int TAB_VECS = 2;
+constexpr int TAB_MAX_INTS = TAB_VECS * 4 * RP_NT;    // 16 KiB
+
+__device__ void group_offsets_lds(const RouteArgs& ra, const Plan& p, int32_t* wg_err,
+                                  int32_t* tab)
+{
+    const int N = ra.N, E = ra.E, L = ra.L, W = E + 1;
+    const int n = N * W, nv = n / 4;
+    const int4* __restrict__ src = reinterpret_cast<const int4*>(p.soff);
+    const int tid = threadIdx.x;
+    if (nv > 0) {
+        int4 v[TAB_VECS];
+#pragma unroll
+        for (int j = 0; j < TAB_VECS; ++j)
+            v[j] = src[min(tid + j * RP_NT, nv - 1)];
+#pragma unroll
+        for (int j = 0; j < TAB_VECS; ++j)
+            if (tid + j * RP_NT < nv)
+                reinterpret_cast<int4*>(tab)[tid + j * RP_NT] = v[j];
+    }
+    for (int i = nv * 4 + tid; i < n; i += RP_NT)
+        tab[i] = p.soff[i];
+    __syncthreads();
+    // expert columns and the totals column soff[*][E], a thread each, with 8
+    // LDS reads in flight
+    for (int col = tid; col <= E; col += RP_NT) {
+        int sum = 0, s = 0;
+        for (; s + 8 <= N; s += 8) {
+            int v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = tab[(s + j) * W + col];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                sum += v[j];
+        }
+        for (; s < N; ++s)
+            sum += tab[s * W + col];
+        p.eoff[col] = sum;
+        if (col == E)
+            p.rbase[N] = sum;
+    }
+    // receiver columns, a thread each, numbered from the top of the block so
+    // that their waves are not the expert columns' when both fit
+    for (int d = RP_NT - 1 - tid; d < N; d += RP_NT) {
+        int32_t* ro = p.roff + (size_t)d * (N + 1);
+        const int32_t* lo_col = tab + d * L;
+        const int32_t* hi_col = tab + (d + 1) * L;
+        int run = 0, base = 0, s = 0;
+        for (; s + 8 <= N; s += 8) {
+            int lo[8], hi[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                lo[j] = lo_col[(s + j) * W];
+                hi[j] = hi_col[(s + j) * W];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                ro[s + j] = run;
+                run += hi[j] - lo[j];
+                base += lo[j];
+            }
+        }
+        for (; s < N; ++s) {
+            const int lo = lo_col[s * W], hi = hi_col[s * W];
+            ro[s] = run;
+            run += hi - lo;
+            base += lo;
+        }
+        ro[N] = run;
+        p.rbase[d] = base;
+        if ((int64_t)run > ra.cap)
+            atomicOr(wg_err, ERR_BIT_CAPACITY);
+    }
+}
+
 // The end of the plan, once every sender's counts are in view: the group
 // offsets, then the cycle's error word -- every sender's bits and the
 // offsets' checks.  It overwrites the last cycle's word, so an error stops
 // only the kernels of its own cycle; the sticky word keeps it for the status
 // call.  Every thread of the workgroup calls it; wg_err (LDS) holds the
-// workgroup's own bits.
-__device__ void close_plan(const RouteArgs& ra, const Plan& p, int32_t* wg_err)
+// workgroup's own bits; tab, when given, is LDS room for the soff table.
+__device__ void close_plan(const RouteArgs& ra, const Plan& p, int32_t* wg_err, int32_t* tab)
 {
-    group_offsets(ra, p, wg_err);
+    if (tab)
+        group_offsets_lds(ra, p, wg_err, tab);
+    else
+        group_offsets(ra, p, wg_err);
     int e = 0;
     for (int j = threadIdx.x; j < ra.N; j += RP_NT)
         e |= p.err_rank[j];
@@ -470,7 +557,7 @@ __device__ __forceinline__ int rank_of_item(const RouteArgs& ra, const int32_t* 
 template <int HC>
 __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
 {
-    extern __shared__ uint64_t lds64[];
+    extern __shared__ __align__(16) uint64_t lds64[];
     const int E = ra.E, N = ra.N;
     // keys: experts [0, E) and, for the partial combine, destination ranks
     // [E, E + N) for the first item of each (token, rank)
@@ -623,7 +710,8 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     if (ticket != ra.N - 1)
         return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    close_plan(ra, p, &wg_err);
+    // the masks are dead: their LDS takes the soff table
+    close_plan(ra, p, &wg_err, ra.table_lds ? reinterpret_cast<int32_t*>(lds64) : nullptr);
     if (tid == 0)
         atomicExch(p.ticket, 0);
 }
@@ -636,11 +724,12 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
 // counts, after the senders' kernels.
 __global__ __launch_bounds__(RP_NT) void offsets_kernel(RouteArgs ra, Plan p)
 {
+    extern __shared__ __align__(16) uint64_t tab64[];
     __shared__ int32_t wg_err;
     if (threadIdx.x == 0)
         wg_err = 0;
     __syncthreads();
-    close_plan(ra, p, &wg_err);
+    close_plan(ra, p, &wg_err, ra.table_lds ? reinterpret_cast<int32_t*>(tab64) : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1987,6 +2076,19 @@ inline unsigned row_blocks(int64_t rows, int split)
             go((KERNEL<4, 8>), grid_, block_, 0, __VA_ARGS__);                                     \
     } while (0)
 
+// The group offsets are formed from an LDS copy of the send offsets
+// soff[N][E+1] when it fits (receiver-side combine; the partial combine's
+// walks also need the counts and the partial offsets).
+inline size_t table_lds_bytes(const Shape& sh)
+{
+    return (size_t)sh.N * (sh.E + 1) * sizeof(int32_t);
+}
+
+inline int table_in_lds(const Shape& sh)
+{
+    return !sh.partial && (int64_t)sh.N * (sh.E + 1) <= TAB_MAX_INTS;
+}
+
 // Whether the pack runs in send-row order (its rows' meta words then come
 // from the route plan): the staged transport with the receiver-side combine,
 // when one sender's tokens fit well within an XCD's 4 MiB L2, so that the K
@@ -2027,8 +2129,11 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     const int nk = sh.E + (sh.partial ? sh.N : 0);
     ra.chunk_waves = nk <= 481 ? RP_WAVES : nk <= 910 ? RP_WAVES / 2 : nk <= 1638 ? RP_WAVES / 4
                                                                                    : RP_WAVES / 8;
-    const size_t lds = 2 * (size_t)ra.chunk_waves * nk * sizeof(uint64_t) +
-                       (size_t)2 * nk * sizeof(int32_t);
+    size_t lds = 2 * (size_t)ra.chunk_waves * nk * sizeof(uint64_t) +
+                 (size_t)2 * nk * sizeof(int32_t);
+    ra.table_lds = table_in_lds(sh);
+    if (ra.table_lds)
+        lds = std::max(lds, table_lds_bytes(sh));
     const int chunks = (sh.T * sh.K + ra.chunk_waves * WAVE - 1) / (ra.chunk_waves * WAVE);
     const dim3 grid(sh.N), block(RP_NT);
     if (chunks <= 1)
@@ -2056,7 +2161,8 @@ hipError_t launch_offsets(const Shape& sh, const Plan& p, const Launch& L)
     ra.slot_cap = sh.fixed ? sh.slots : -1;
     ra.offsets = 1;
     ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
-    go(offsets_kernel, dim3(1), dim3(RP_NT), 0, L, ra, p);
+    ra.table_lds = table_in_lds(sh);
+    go(offsets_kernel, dim3(1), dim3(RP_NT), ra.table_lds ? table_lds_bytes(sh) : 0, L, ra, p);
     return hipGetLastError();
 }
 
