@@ -266,6 +266,7 @@ int place_buffers(moe_group_s* g, Placer& take)
         (fp8 && staged && (rc = take(&g->send_scale, R * g->scale_blocks))) ||
         (fp8 && (rc = take(&g->recv_scale, RQ * g->scale_blocks))) ||
         (fixed && ((rc = take(&p.slot_of, R)) || (rc = take(&p.send_slot, R)))) ||
+        (!staged && !partial && (rc = take(&p.send_item, R))) ||
         (partial && ((rc = take(&p.pdst, R)) || (rc = take(&p.ppos, R)) ||
                      (rc = take(&p.psoff, (size_t)N * (N + 1))) ||
                      (rc = take(&p.qoff, (size_t)N * (N + 1))) ||
@@ -361,7 +362,7 @@ int poison_dispatch_send(const moe_group_s* g, hipStream_t st)
         (rc = poison(st, p.ebase, N * E * 4)) || (rc = poison(st, p.xfer_src, R * 4)) ||
         (rc = poison(st, p.xfer_dst, R * 8)) || (rc = poison(st, p.shuf_map, R * 8)) ||
         (rc = poison(st, p.shuf_inv, R * 4)) || (rc = poison(st, p.slot_of, R * 4)) ||
-        (rc = poison(st, p.send_slot, R * 4)) ||
+        (rc = poison(st, p.send_slot, R * 4)) || (rc = poison(st, p.send_item, R * 4)) ||
         (rc = poison(st, p.pdst, R * 4)) || (rc = poison(st, p.ppos, R * 4)) ||
         (rc = poison(st, p.psoff, N * (N + 1) * 4)) || (rc = poison(st, p.qoff, N * (N + 1) * 4)) ||
         (rc = poison(st, p.qbase, (N + 1) * 4)) || (rc = poison(st, p.pbase, (N + 1) * 4)) ||

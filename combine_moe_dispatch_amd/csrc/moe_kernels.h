@@ -62,6 +62,8 @@ struct Plan {              // device pointers owned by the group
     int2* xfer_dst;        // [rows]  send row -> (its receive-plane row, its expert row)
     int2* shuf_map;        // [rows]  expert row r <- (receive-plane row, source rank)
     int32_t* shuf_inv;     // [rows]  packed receive row -> its expert row
+    int32_t* send_item;    // [rows]  send row -> its item t*K+k, for the direct transport's
+                           //         send-row-order pack (staged: the send meta words)
     // combine with expert-side partial sums (null unless Shape::partial)
     int32_t* pdst;         // [N][T][K]  destination rank of item (s,t,k)
     int32_t* ppos;         // [N][T][K]  first k of its rank in the token: row among sender

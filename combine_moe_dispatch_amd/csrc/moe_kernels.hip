@@ -152,6 +152,7 @@ struct RouteArgs {
     int offsets;            // the last workgroup computes the group offsets
     int table_lds;          // ... from a copy of soff in the dynamic LDS
     int32_t* send_meta;     // when set: each send row's item t*K+k, written with the positions
+                            // (the send meta words, or the direct transport's send_item)
     int64_t cap;
 };
 
@@ -1142,17 +1143,81 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
 }
 
 // ---------------------------------------------------------------------------
-// Pack in send-row order (staged transport, receiver-side combine): the same
-// rows as the token-order kernels above, written as a gather.  The route plan
-// has already written each send row's meta word t*K+k (the item it holds), so
-// send row (s, pk) reads its token's row x[s][t] and writes it (quantised,
-// for e4m3) in place: the writes stream through the send buffer in address
-// order, as the movers' do, and each token is read K times, mostly from cache
-// (a sender's tokens are a few MiB, and one XCD takes a run of its send
-// rows).  The lead wave also records the transfer's map, which needs the
+// Pack in send-row order (receiver-side combine): the same rows as the
+// token-order kernels above, written as a gather.  The route plan has already
+// written the item t*K+k each send row holds (into the send meta words when
+// staged, into send_item when direct), so send row (s, pk) reads its token's
+// row x[s][t] and writes it (quantised, for e4m3): staged, in place, so the
+// writes stream through the send buffer in address order as the movers' do;
+// direct, to its receive-plane row, so they stream through one (s -> d)
+// segment after another.  Each token is read K times, mostly from cache (a
+// sender's tokens are a few MiB, and one XCD takes a run of its send rows).
+// The staged lead wave also records the transfer's map, which needs the
 // item's expert (idx) and the offsets: one more dependent load that no other
-// wave waits for.
+// wave waits for; the direct lead wave writes the row's meta word.
 // ---------------------------------------------------------------------------
+// The last bucket b in [0, nb) whose start row[b * stride] is <= key, with
+// that start, for non-decreasing starts (the expert or rank parts of a
+// sender's send rows); -1 if none.  Lanes take 64 buckets at a time, and up
+// to C*64 buckets are loaded in one round.  Every lane of the wave must call
+// it with the same arguments.
+template <int C>
+__device__ inline int2 find_bucket(const int32_t* __restrict__ row, int nb, int stride, int key)
+{
+    const int lane = lane_id();
+    int b = -1, start = 0;
+    int v[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+        v[c] = row[(size_t)min(c * WAVE + lane, nb - 1) * stride];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const uint64_t m = __ballot(c * WAVE + lane < nb && v[c] <= key);
+        if (m) {
+            const int top = 63 - __builtin_clzll(m);
+            b = c * WAVE + top;
+            start = readlane(v[c], top);
+        }
+    }
+    for (int b0 = C * WAVE; b0 < nb; b0 += WAVE) {
+        const int j = b0 + lane;
+        const int w = j < nb ? row[(size_t)j * stride] : 0;
+        const uint64_t m = __ballot(j < nb && w <= key);
+        if (m) {
+            const int top = 63 - __builtin_clzll(m);
+            b = b0 + top;
+            start = readlane(w, top);
+        }
+    }
+    return make_int2(b, start);
+}
+
+// The receive-plane row that the direct transport gives send row (s, pk),
+// from the sender's own offsets and the group offsets alone: the rank d whose
+// part of the sender's rows holds pk, then q = rbase[d] + roff[d][s] + pk -
+// soff[s][d*L]; with fixed slots the expert e whose part holds it, then slot
+// i = pk - soff[s][e], row (e*T_max + i)*N + s.  -1 if a check fails.  Every
+// lane of the wave must call it.
+__device__ inline int64_t direct_row(const Shape& sh, const Plan& p, int s, int pk)
+{
+    const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
+    if (sh.fixed) {
+        const int2 b = sh.E <= WAVE ? find_bucket<1>(so, sh.E, 1, pk)
+                                    : find_bucket<4>(so, sh.E, 1, pk);
+        const int i = pk - b.y;
+        if (b.x < 0 || (unsigned)i >= (unsigned)sh.slots)
+            return -1;
+        const int64_t slot = ((int64_t)b.x * sh.slots + i) * sh.N + s;
+        return slot < sh.recv_rows ? slot : -1;
+    }
+    const int2 b = sh.N <= WAVE ? find_bucket<1>(so, sh.N, sh.L, pk)
+                                : find_bucket<4>(so, sh.N, sh.L, pk);
+    if (b.x < 0)
+        return -1;
+    const int64_t q = (int64_t)p.rbase[b.x] + p.roff[(size_t)b.x * (sh.N + 1) + s] + pk - b.y;
+    return (uint64_t)q < (uint64_t)sh.rows ? q : -1;
+}
+
 __device__ inline void record_send_row(const Shape& sh, const Plan& p,
                                        const int32_t* __restrict__ idx, int s, int pk, int m)
 {
@@ -1173,8 +1238,9 @@ template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, Plan p,
                                                                       const v4u* __restrict__ x,
                                                                       const int32_t* __restrict__ idx,
-                                                                      const int32_t* __restrict__ send_meta,
-                                                                      v4u* __restrict__ send_x,
+                                                                      const int32_t* __restrict__ row_item,
+                                                                      v4u* __restrict__ dst_x,
+                                                                      int32_t* __restrict__ dst_meta,
                                                                       uint32_t xrun)
 {
     const int lane = lane_id();
@@ -1187,14 +1253,15 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, 
     const int s = (int)(srow / TK), pk = (int)(srow - s * TK);
     if (sender_failed(sh, p, s))
         return;
-    const int m = send_meta[srow];
-    if ((unsigned)m >= (unsigned)TK) {
+    const int m = row_item[srow];
+    const int64_t drow = sh.direct ? direct_row(sh, p, s, pk) : srow;
+    if ((unsigned)m >= (unsigned)TK || drow < 0) {
         if (rs.lead && lane == 0)
             raise_err(p, ERR_BIT_INTERNAL);
         return;
     }
     const v4u* src = x + ((int64_t)s * sh.T + m / sh.K) * n + rs.b0;
-    v4u* dst = send_x + srow * n + rs.b0;
+    v4u* dst = dst_x + drow * n + rs.b0;
     for (int base = 0; base < rs.len; base += WAVE * U) {
         // ordinary loads: the token's other K-1 rows read it again
         v4u v[U];
@@ -1209,17 +1276,22 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, 
                 st_nt(v[u], dst + j);
         }
     }
-    if (rs.lead && lane == 0)
-        record_send_row(sh, p, idx, s, pk, m);
+    if (rs.lead && lane == 0) {
+        if (sh.direct)
+            dst_meta[drow] = m;
+        else
+            record_send_row(sh, p, idx, s, pk, m);
+    }
 }
 
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(Shape sh, Plan p,
                                                                      const v4u* __restrict__ x,
                                                                      const int32_t* __restrict__ idx,
-                                                                     const int32_t* __restrict__ send_meta,
-                                                                     v4u* __restrict__ send_q,
-                                                                     float* __restrict__ send_scale,
+                                                                     const int32_t* __restrict__ row_item,
+                                                                     v4u* __restrict__ dst_q,
+                                                                     float* __restrict__ dst_scale,
+                                                                     int32_t* __restrict__ dst_meta,
                                                                      uint32_t xrun)
 {
     const int lane = lane_id();
@@ -1232,8 +1304,9 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(Shape sh, P
     const int s = (int)(srow / TK), pk = (int)(srow - s * TK);
     if (sender_failed(sh, p, s))
         return;
-    const int m = send_meta[srow];
-    if ((unsigned)m >= (unsigned)TK) {
+    const int m = row_item[srow];
+    const int64_t drow = sh.direct ? direct_row(sh, p, s, pk) : srow;
+    if ((unsigned)m >= (unsigned)TK || drow < 0) {
         if (rs.lead && lane == 0)
             raise_err(p, ERR_BIT_INTERNAL);
         return;
@@ -1259,14 +1332,18 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(Shape sh, P
         for (int u = 0; u < U; ++u) {
             const int j = base + u * WAVE + lane;
             if (j < end) {
-                st_nt(q[u], send_q + srow * n2 + j);
+                st_nt(q[u], dst_q + drow * n2 + j);
                 if ((lane & 7) == 0)
-                    send_scale[srow * nb + j / 8] = sc[u];
+                    dst_scale[drow * nb + j / 8] = sc[u];
             }
         }
     }
-    if (rs.lead && lane == 0)
-        record_send_row(sh, p, idx, s, pk, m);
+    if (rs.lead && lane == 0) {
+        if (sh.direct)
+            dst_meta[drow] = m;
+        else
+            record_send_row(sh, p, idx, s, pk, m);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -2089,20 +2166,19 @@ inline int table_in_lds(const Shape& sh)
     return !sh.partial && (int64_t)sh.N * (sh.E + 1) <= TAB_MAX_INTS;
 }
 
-// Whether the pack runs in send-row order (its rows' meta words then come
-// from the route plan): the staged transport with the receiver-side combine,
-// when one sender's tokens fit well within an XCD's 4 MiB L2, so that the K
-// reads of each token after the first hit it.  DeepSeek-R1 decode (1.75 MiB
-// per sender, one sender per XCD run): pack 86.9 -> 74.5 us warm, 115 -> 99
-// MALL-flushed; on the prefill (28 MiB per sender) the row order re-reads
-// every token from HBM or the MALL and took 4.9-5.0 ms against 1.87 in token
-// order.  The direct push writes receive rows and the partial combine's
-// records are made per token, so those keep the token-order kernels.
+// Whether the pack runs in send-row order (each row's item then comes from
+// the route plan): the receiver-side combine, when one sender's tokens fit
+// well within an XCD's 4 MiB L2, so that the K reads of each token after the
+// first hit it.  DeepSeek-R1 decode (1.75 MiB per sender, one sender per XCD
+// run), staged: pack 86.9 -> 74.5 us warm, 115 -> 99 MALL-flushed; on the
+// prefill (28 MiB per sender) the row order re-reads every token from HBM or
+// the MALL and took 4.9-5.0 ms against 1.87 in token order.  The partial
+// combine's records are made per token, so it keeps the token-order kernels.
 constexpr int64_t PACK_ROWS_MAX_SENDER_BYTES = 2 << 20;
 
 inline bool pack_in_row_order(const Shape& sh)
 {
-    return !sh.direct && !sh.partial && (int64_t)sh.T * sh.H * 2 <= PACK_ROWS_MAX_SENDER_BYTES;
+    return !sh.partial && (int64_t)sh.T * sh.H * 2 <= PACK_ROWS_MAX_SENDER_BYTES;
 }
 
 }  // namespace
@@ -2112,7 +2188,7 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
 {
     RouteArgs ra;
     ra.idx = idx;
-    ra.send_meta = pack_in_row_order(sh) ? r.send_meta : nullptr;
+    ra.send_meta = !pack_in_row_order(sh) ? nullptr : sh.direct ? p.send_item : r.send_meta;
     ra.N = sh.N;
     ra.T = sh.T;
     ra.K = sh.K;
@@ -2222,18 +2298,20 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
     if (tokens == 0)
         return hipSuccess;
     if (pack_in_row_order(sh)) {
+        const int32_t* item = sh.direct ? p.send_item : r.send_meta;
+        v4u* dx = (v4u*)(sh.direct ? r.recv_x : r.send_x);
+        int32_t* dmeta = sh.direct ? r.recv_meta : nullptr;
         if (sh.fp8) {
             RowShape rsh = row_shape(sh.H / 16);
             if (rsh.u > 4)
                 rsh.u = 4;
             MOE_DISPATCH_ROW(rsh, pack_rows_fp8_kernel, sh.rows, L, sh, p, (const v4u*)x, idx,
-                             r.send_meta, (v4u*)r.send_x, r.send_scale,
+                             item, dx, sh.direct ? r.recv_scale : r.send_scale, dmeta,
                              sender_run(sh, rsh));
         } else {
             const RowShape rsh = row_shape(sh.payload_vecs);
             MOE_DISPATCH_ROW(rsh, pack_rows_bf16_kernel, sh.rows, L, sh, p, (const v4u*)x, idx,
-                             r.send_meta, (v4u*)r.send_x,
-                             sender_run(sh, rsh));
+                             item, dx, dmeta, sender_run(sh, rsh));
         }
         return hipGetLastError();
     }
