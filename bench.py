@@ -50,8 +50,8 @@ def partial_rows(cfg, idx) -> int:
     return int(np.unique(tok * N + d).size)
 
 
-# A sender's tokens up to this size make the pack run in send-row order with
-# the receiver-side combine (the library's rule).
+# A sender's tokens up to this size make the pack run in send-row order (the
+# library's rule).
 PACK_ROWS_MAX_SENDER_BYTES = 2 << 20
 
 
@@ -67,8 +67,8 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
     maps, 20 bytes per row (24 with fixed slots): the maps are its whole job,
     so they are counted there; with fixed slots and the receiver-side combine
     the group offsets move from the route plan to their own kernel.  When the
-    pack runs in send-row order (receiver-side combine, a sender's tokens
-    within 2 MiB) the route plan writes each send row's item and the pack
+    pack runs in send-row order (a sender's tokens within 2 MiB) the route
+    plan writes each send row's item and the pack
     reads it in place of the positions (staged: the send meta words, which the
     pack no longer writes; direct: the pack no longer reads idx)."""
     N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
@@ -93,7 +93,7 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
         "recv_map": (N * E * 4 * 2 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4
                      + R * (20 + (4 if layout == "fixed" else 0))),
     }
-    if combine == "receiver" and T * H * 2 <= PACK_ROWS_MAX_SENDER_BYTES:
+    if T * H * 2 <= PACK_ROWS_MAX_SENDER_BYTES:
         kb["route_plan"] += R * 4
         kb["pack"] -= R * 4
     if layout == "fixed" and combine == "receiver":

@@ -266,7 +266,7 @@ int place_buffers(moe_group_s* g, Placer& take)
         (fp8 && staged && (rc = take(&g->send_scale, R * g->scale_blocks))) ||
         (fp8 && (rc = take(&g->recv_scale, RQ * g->scale_blocks))) ||
         (fixed && ((rc = take(&p.slot_of, R)) || (rc = take(&p.send_slot, R)))) ||
-        (!staged && !partial && (rc = take(&p.send_item, R))) ||
+        (!staged && (rc = take(&p.send_item, R))) ||
         (partial && ((rc = take(&p.pdst, R)) || (rc = take(&p.ppos, R)) ||
                      (rc = take(&p.psoff, (size_t)N * (N + 1))) ||
                      (rc = take(&p.qoff, (size_t)N * (N + 1))) ||

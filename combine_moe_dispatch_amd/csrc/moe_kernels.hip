@@ -685,7 +685,8 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
                                return pack_keys((unsigned)e < (unsigned)E ? e : -1,
                                                 first ? E + d : -1);
                            },
-                           p.pos + (size_t)s * items, p.ppos + (size_t)s * items, nullptr);
+                           p.pos + (size_t)s * items, p.ppos + (size_t)s * items,
+                           ra.send_meta ? ra.send_meta + (size_t)s * items : nullptr);
     }
 
     // Publish this rank's counts and error bits and draw a ticket.  Every
@@ -774,14 +775,14 @@ __device__ inline RowSlot row_slot(int n, int64_t block = blockIdx.x)
 // order.
 constexpr int XCDS = 8;
 
-__device__ inline int64_t xcd_run_block(uint32_t run)
+__device__ inline int64_t xcd_run_block(uint32_t run, uint32_t nblocks = 0)
 {
     const uint32_t b = blockIdx.x;
     if (run <= 1)
         return b;
     const uint32_t tile = XCDS * run;            // the host keeps run below 2^28
     const uint32_t t0 = b / tile * tile;
-    if (t0 + tile > gridDim.x)
+    if (t0 + tile > (nblocks ? nblocks : gridDim.x))   // blocks [0, nblocks) are remapped
         return b;
     const uint32_t r = b - t0;
     return (int64_t)t0 + (r % XCDS) * run + r / XCDS;
@@ -1143,8 +1144,8 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
 }
 
 // ---------------------------------------------------------------------------
-// Pack in send-row order (receiver-side combine): the same rows as the
-// token-order kernels above, written as a gather.  The route plan has already
+// Pack in send-row order: the same rows as the token-order kernels above,
+// written as a gather.  The route plan has already
 // written the item t*K+k each send row holds (into the send meta words when
 // staged, into send_item when direct), so send row (s, pk) reads its token's
 // row x[s][t] and writes it (quantised, for e4m3): staged, in place, so the
@@ -1154,7 +1155,9 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
 // sender's tokens are a few MiB, and one XCD takes a run of its send rows).
 // The staged lead wave also records the transfer's map, which needs the
 // item's expert (idx) and the offsets: one more dependent load that no other
-// wave waits for; the direct lead wave writes the row's meta word.
+// wave waits for; the direct lead wave writes the row's meta word.  With the
+// expert-side partial combine the lead wave also moves the row's router
+// weight, and waves past the rows' write the per-token records.
 // ---------------------------------------------------------------------------
 // The last bucket b in [0, nb) whose start row[b * stride] is <= key, with
 // that start, for non-decreasing starts (the expert or rank parts of a
@@ -1218,6 +1221,30 @@ __device__ inline int64_t direct_row(const Shape& sh, const Plan& p, int s, int 
     return (uint64_t)q < (uint64_t)sh.rows ? q : -1;
 }
 
+// The partial combine's records of token tok (sender s), for the send-row
+// order pack, whose row waves see one item each: lanes k < K find their
+// item's expert and receive-plane rows and the head items write the records
+// (record_partial).  Every lane of the wave must call it.
+__device__ inline void token_records(const Shape& sh, const Plan& p,
+                                     const int32_t* __restrict__ idx, int64_t tok, int s)
+{
+    const int lane = lane_id();
+    int d = -1;
+    RowDest rd{};
+    if (lane < sh.K) {
+        const int64_t i = tok * sh.K + lane;
+        const int e = idx[i];
+        if ((unsigned)e < (unsigned)sh.E) {
+            rd = row_dest(sh, p, s, e, p.pos[i]);
+            if (rd.ok)
+                d = e / sh.L;
+        }
+        if (d < 0)
+            raise_err(p, ERR_BIT_INTERNAL);
+    }
+    record_partial(sh, p, tok, s, d, rd);
+}
+
 __device__ inline void record_send_row(const Shape& sh, const Plan& p,
                                        const int32_t* __restrict__ idx, int s, int pk, int m)
 {
@@ -1234,6 +1261,20 @@ __device__ inline void record_send_row(const Shape& sh, const Plan& p,
         raise_err(p, ERR_BIT_INTERNAL);
 }
 
+// Blocks past the row blocks: one wave per token, for the partial combine's
+// records.
+__device__ inline void pack_token_block(const Shape& sh, const Plan& p,
+                                        const int32_t* __restrict__ idx, uint32_t data_blocks)
+{
+    const int64_t tok = (int64_t)(blockIdx.x - data_blocks) * ROWS_PER_BLOCK + threadIdx.x / WAVE;
+    if (tok >= (int64_t)sh.N * sh.T)
+        return;
+    const int s = (int)(tok / sh.T);
+    if (sender_failed(sh, p, s))
+        return;
+    token_records(sh, p, idx, tok, s);
+}
+
 template <int U, int SPLIT>
 __global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, Plan p,
                                                                       const v4u* __restrict__ x,
@@ -1241,11 +1282,17 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, 
                                                                       const int32_t* __restrict__ row_item,
                                                                       v4u* __restrict__ dst_x,
                                                                       int32_t* __restrict__ dst_meta,
-                                                                      uint32_t xrun)
+                                                                      const float* __restrict__ w,
+                                                                      float* __restrict__ dst_w,
+                                                                      uint32_t xrun, uint32_t data_blocks)
 {
     const int lane = lane_id();
     const int n = sh.payload_vecs;
-    const RowSlot rs = row_slot<SPLIT>(n, xcd_run_block(xrun));
+    if (blockIdx.x >= data_blocks) {
+        pack_token_block(sh, p, idx, data_blocks);
+        return;
+    }
+    const RowSlot rs = row_slot<SPLIT>(n, xcd_run_block(xrun, data_blocks));
     const int64_t TK = (int64_t)sh.T * sh.K;
     const int64_t srow = rs.row;
     if (srow >= sh.rows)
@@ -1281,6 +1328,8 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, 
             dst_meta[drow] = m;
         else
             record_send_row(sh, p, idx, s, pk, m);
+        if (dst_w)
+            dst_w[drow] = w[s * TK + m];
     }
 }
 
@@ -1292,11 +1341,17 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(Shape sh, P
                                                                      v4u* __restrict__ dst_q,
                                                                      float* __restrict__ dst_scale,
                                                                      int32_t* __restrict__ dst_meta,
-                                                                     uint32_t xrun)
+                                                                     const float* __restrict__ w,
+                                                                     float* __restrict__ dst_w,
+                                                                     uint32_t xrun, uint32_t data_blocks)
 {
     const int lane = lane_id();
     const int n2 = sh.H / 16;
-    const RowSlot rs = row_slot<SPLIT, 8>(n2, xcd_run_block(xrun));
+    if (blockIdx.x >= data_blocks) {
+        pack_token_block(sh, p, idx, data_blocks);
+        return;
+    }
+    const RowSlot rs = row_slot<SPLIT, 8>(n2, xcd_run_block(xrun, data_blocks));
     const int64_t TK = (int64_t)sh.T * sh.K;
     const int64_t srow = rs.row;
     if (srow >= sh.rows)
@@ -1343,6 +1398,8 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(Shape sh, P
             dst_meta[drow] = m;
         else
             record_send_row(sh, p, idx, s, pk, m);
+        if (dst_w)
+            dst_w[drow] = w[s * TK + m];
     }
 }
 
@@ -2133,8 +2190,11 @@ inline unsigned row_blocks(int64_t rows, int split)
 }
 
 #define MOE_DISPATCH_ROW(rsh, KERNEL, GRID_ROWS, ...)                                              \
+    MOE_DISPATCH_ROW_BLOCKS(rsh, KERNEL, row_blocks((GRID_ROWS), (rsh).split), __VA_ARGS__)
+
+#define MOE_DISPATCH_ROW_BLOCKS(rsh, KERNEL, GRID_BLOCKS, ...)                                     \
     do {                                                                                           \
-        const dim3 grid_(row_blocks((GRID_ROWS), (rsh).split)), block_(COPY_THREADS);              \
+        const dim3 grid_(GRID_BLOCKS), block_(COPY_THREADS);                                       \
         if ((rsh).split == 1 && (rsh).u == 1)                                                      \
             go((KERNEL<1, 1>), grid_, block_, 0, __VA_ARGS__);                                     \
         else if ((rsh).split == 1)                                                                 \
@@ -2167,18 +2227,19 @@ inline int table_in_lds(const Shape& sh)
 }
 
 // Whether the pack runs in send-row order (each row's item then comes from
-// the route plan): the receiver-side combine, when one sender's tokens fit
+// the route plan): when one sender's tokens fit
 // well within an XCD's 4 MiB L2, so that the K reads of each token after the
 // first hit it.  DeepSeek-R1 decode (1.75 MiB per sender, one sender per XCD
 // run), staged: pack 86.9 -> 74.5 us warm, 115 -> 99 MALL-flushed; on the
 // prefill (28 MiB per sender) the row order re-reads every token from HBM or
-// the MALL and took 4.9-5.0 ms against 1.87 in token order.  The partial
-// combine's records are made per token, so it keeps the token-order kernels.
+// the MALL and took 4.9-5.0 ms against 1.87 in token order.  With the
+// partial combine, whose records are made per token, the same launch runs one
+// wave per token for them after the row blocks.
 constexpr int64_t PACK_ROWS_MAX_SENDER_BYTES = 2 << 20;
 
 inline bool pack_in_row_order(const Shape& sh)
 {
-    return !sh.partial && (int64_t)sh.T * sh.H * 2 <= PACK_ROWS_MAX_SENDER_BYTES;
+    return (int64_t)sh.T * sh.H * 2 <= PACK_ROWS_MAX_SENDER_BYTES;
 }
 
 }  // namespace
@@ -2301,17 +2362,24 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
         const int32_t* item = sh.direct ? p.send_item : r.send_meta;
         v4u* dx = (v4u*)(sh.direct ? r.recv_x : r.send_x);
         int32_t* dmeta = sh.direct ? r.recv_meta : nullptr;
+        // the partial combine's token records take one wave per token, in
+        // blocks after the rows'
+        const unsigned tblocks = sh.partial ? row_blocks(tokens, 1) : 0;
         if (sh.fp8) {
             RowShape rsh = row_shape(sh.H / 16);
             if (rsh.u > 4)
                 rsh.u = 4;
-            MOE_DISPATCH_ROW(rsh, pack_rows_fp8_kernel, sh.rows, L, sh, p, (const v4u*)x, idx,
-                             item, dx, sh.direct ? r.recv_scale : r.send_scale, dmeta,
-                             sender_run(sh, rsh));
+            const unsigned rb = row_blocks(sh.rows, rsh.split);
+            MOE_DISPATCH_ROW_BLOCKS(rsh, pack_rows_fp8_kernel, rb + tblocks, L, sh, p,
+                                    (const v4u*)x, idx, item, dx,
+                                    sh.direct ? r.recv_scale : r.send_scale, dmeta, w, dst_w,
+                                    sender_run(sh, rsh), rb);
         } else {
             const RowShape rsh = row_shape(sh.payload_vecs);
-            MOE_DISPATCH_ROW(rsh, pack_rows_bf16_kernel, sh.rows, L, sh, p, (const v4u*)x, idx,
-                             item, dx, dmeta, sender_run(sh, rsh));
+            const unsigned rb = row_blocks(sh.rows, rsh.split);
+            MOE_DISPATCH_ROW_BLOCKS(rsh, pack_rows_bf16_kernel, rb + tblocks, L, sh, p,
+                                    (const v4u*)x, idx, item, dx, dmeta, w, dst_w,
+                                    sender_run(sh, rsh), rb);
         }
         return hipGetLastError();
     }
