@@ -9,9 +9,11 @@ grid in a partial tile:
   segments of 36 rows, tiles of 576 blocks (114.2); combine reduce 8220
   blocks in tiles of 256 (32.1); partial transfer segments of 72 blocks,
   tiles of 576 (114.2).
-  N=64, T=131, H=7168, E=256, K=8 (fp8): fp8 pack 8384 blocks in tiles of
-  2048 (4.1); shuffle 67 072 blocks in tiles of 1024 (65.5); combine reduce
-  16 768 blocks in tiles of 256 (65.5)."""
+  N=64, T=131, H=7168, E=256, K=8 (fp8): shuffle 67 072 blocks in tiles of
+  1024 (65.5); combine reduce 16 768 blocks in tiles of 256 (65.5).
+The pack runs in send-row order here (a sender's tokens within 2 MiB), in
+runs of one sender: bf16 65 760 blocks in tiles of 17 536 (3.75); its fp8
+grid is 8 whole tiles (ragged sender runs: test_gpu_pack_order.py)."""
 import pytest
 
 from tests.gpu_util import run_cycle, say
