@@ -63,14 +63,17 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
     movers (4-8 bytes per row of 7-14 KiB) are an implementation detail and not
     counted.  With the partial combine (P partial rows), the router weights
     travel with the dispatched rows and combine moves P rows instead of R.
-    The receiver's map kernel reads the counts and offsets and writes its
-    maps, 20 bytes per row (24 with fixed slots): the maps are its whole job,
-    so they are counted there; with fixed slots and the receiver-side combine
-    the group offsets move from the route plan to their own kernel.  When the
-    pack runs in send-row order (a sender's tokens within 2 MiB) the route
-    plan writes each send row's item and the pack
-    reads it in place of the positions (staged: the send meta words, which the
-    pack no longer writes; direct: the pack no longer reads idx)."""
+    The receiver's map kernel forms the group offsets from the exchanged
+    counts and send offsets and writes its maps, 20 bytes per row (24 with
+    fixed slots): tables and maps are its whole job, so they are counted
+    there.  The route plan's last workgroup forms the group offsets too (the
+    same tables in and out) only where a kernel before dispatch_recv needs
+    them: the packed layout's token-order pack and direct push, and the
+    partial combine (the map kernel then reads them instead, counted alike).
+    When the pack runs in send-row order (a sender's tokens within 2 MiB) the
+    route plan writes each send row's item and the pack reads it in place of
+    the positions (staged: the send meta words, which the pack no longer
+    writes; direct: the pack no longer reads idx)."""
     N, T, K, E, H = cfg.N, cfg.T, cfg.K, cfg.E, cfg.H
     R = N * T * K
     fp8 = cfg.dtype == "fp8"
@@ -78,29 +81,26 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
     sb = (H // 128) * 4 if fp8 else 0            # block scales per row
     hy = 2 * H                                   # combine row
     tokens = N * T
+    row_order = T * H * 2 <= PACK_ROWS_MAX_SENDER_BYTES
+    # the group offsets: counts and send offsets in; receive offsets, receive
+    # bases and expert offsets out
+    offs = (N * E * 4 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4 + (E + 1) * 4)
     kb = {
-        # idx in; counts, send offsets, positions out; then the group offsets
-        # (counts and send offsets in; receive/expert offsets and bases out)
-        "route_plan": (R * 4 + N * E * 4 + N * (E + 1) * 4 + R * 4
-                       + N * E * 4 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4
-                       + (E + 1) * 4 + N * E * 4),
+        # idx in; counts, send offsets (both orientations), positions out
+        "route_plan": R * 4 + N * E * 4 + 2 * N * (E + 1) * 4 + R * 4,
         "pack": tokens * H * 2 + R * 4 * 2 + R * (hb + sb + 4),
         "transfer": 2 * R * (hb + sb + 4),
         "shuffle": R * (hb + sb + 4) + R * (hb + sb + 8) + (E + 1) * 4,
         "combine_pack": 2 * R * hy,
         "transfer_back": 2 * R * hy,
         "combine_reduce": R * hy + R * 8 + tokens * H * 2,
-        "recv_map": (N * E * 4 * 2 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4
-                     + R * (20 + (4 if layout == "fixed" else 0))),
+        "recv_map": offs + R * (20 + (4 if layout == "fixed" else 0)),
     }
-    if T * H * 2 <= PACK_ROWS_MAX_SENDER_BYTES:
+    if combine == "partial" or (layout == "packed" and (transport == "direct" or not row_order)):
+        kb["route_plan"] += offs
+    if row_order:
         kb["route_plan"] += R * 4
         kb["pack"] -= R * 4
-    if layout == "fixed" and combine == "receiver":
-        offs = (N * E * 4 + N * (E + 1) * 4 + N * (N + 1) * 4 + (N + 1) * 4 + (E + 1) * 4
-                + N * E * 4)
-        kb["route_plan"] -= offs
-        kb["offsets"] = offs
     if transport == "direct":
         # pack writes the receive rows itself and combine writes the return
         # rows itself: no transfer passes
@@ -108,9 +108,10 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
             del kb[k]
         kb["combine_push"] = 2 * R * hy
     if combine == "partial":
-        # second route-plan pass: rank and position of every item; weights
+        # second route-plan pass: rank and position of every item, each
+        # sender's first expert rows and the partial rows' offsets; weights
         # (4 bytes a row) through pack and transfer
-        kb["route_plan"] += 2 * R * 4 + 3 * N * (N + 1) * 4 + 2 * (N + 1) * 4
+        kb["route_plan"] += 2 * R * 4 + N * E * 4 + 3 * N * (N + 1) * 4 + 2 * (N + 1) * 4
         kb["pack"] += 2 * R * 4
         if "transfer" in kb:
             kb["transfer"] += 2 * R * 4
@@ -197,7 +198,8 @@ KERNEL_OF = [("route_plan_kernel", "route_plan"), ("pack_bf16_kernel", "pack"),
              ("partial_send_kernel", "partial_send"),
              ("partial_transfer_kernel", "partial_transfer"),
              ("partial_reduce_kernel", "partial_reduce"),
-             ("recv_map_kernel", "recv_map"), ("offsets_kernel", "offsets")]
+             ("recv_map_kernel", "recv_map"), ("pack_rows_bf16_kernel", "pack"),
+             ("pack_rows_fp8_kernel", "pack")]
 
 
 def _kernel_key(name: str):
@@ -270,7 +272,7 @@ def _partial_rows_of(cfg, combine: str) -> int:
     return partial_rows(cfg, make_routing(cfg)[0])
 
 
-def trace_summary(cfg, db: str, timed=None) -> str:
+def trace_summary(cfg, db: str, timed=None, layout: str = "packed") -> str:
     """Markdown table of the library's kernels from a rocprofv3 kernel trace.
     With timed = (steps, warmup) of the traced bench command, a column with
     each kernel's average over the launches of its timed region (the
@@ -293,9 +295,8 @@ def trace_summary(cfg, db: str, timed=None) -> str:
     lines = [head, rule]
     transport = "staged" if "transfer" in acc else "direct"
     combine = "partial" if "partial_send" in acc else "receiver"
-    layout = "fixed" if "offsets" in acc else "packed"
     kb = kernel_bytes(cfg, transport, combine, _partial_rows_of(cfg, combine), layout)
-    for key in ["route_plan", "pack", "transfer", "recv_map", "offsets", "shuffle",
+    for key in ["route_plan", "pack", "transfer", "recv_map", "shuffle",
                 "combine_pack", "transfer_back", "combine_push", "combine_reduce",
                 "partial_send", "partial_transfer", "partial_reduce"]:
         if key in acc:
@@ -712,7 +713,8 @@ def main() -> int:
         cfg = CONFIGS[args.config]
         if args.trace_summary:
             print(trace_summary(cfg, args.trace_summary,
-                                (args.steps, args.warmup) if args.trace_timed else None))
+                                (args.steps, args.warmup) if args.trace_timed else None,
+                                args.layout))
         if args.traffic_xcheck:
             print(json.dumps(traffic_xcheck(cfg, *args.traffic_xcheck), indent=1))
         if args.traffic_from:

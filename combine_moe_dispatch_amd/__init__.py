@@ -51,7 +51,7 @@ MOE_PROBE_WRITE = 2
 
 KERNELS = ["route_plan", "pack", "transfer", "shuffle", "combine_pack", "transfer_back",
            "combine_reduce", "combine_push", "partial_send", "partial_transfer",
-           "partial_reduce", "recv_map", "offsets"]
+           "partial_reduce", "recv_map"]
 MOE_KERNEL_COUNT = len(KERNELS)
 MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1
 

@@ -69,6 +69,8 @@ struct moe_group_s {
 
     State state = State::Idle;
     int32_t T = 0;
+    uint32_t cycle = 0;          // dispatch_send calls so far: picks the cycle's error word
+    int32_t* err_words = nullptr;  // the two alternating cycle words
 
     int timing_mask = 0;
     std::vector<EventPair> events;
@@ -85,7 +87,7 @@ const char* const kKernelNames[MOE_KERNEL_COUNT] = {
     "route_plan_kernel",   "pack_kernel",          "transfer_kernel",       "shuffle_kernel",
     "combine_pack_kernel", "transfer_back_kernel", "combine_reduce_kernel", "combine_push_kernel",
     "partial_send_kernel", "partial_transfer_kernel", "partial_reduce_kernel",
-    "recv_map_kernel",     "offsets_kernel",
+    "recv_map_kernel",
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -146,6 +148,7 @@ moe::Shape shape_of(const moe_group_s* g, int T)
     sh.payload_vecs = g->payload_bytes / 16;
     sh.comb_vecs = g->comb_bytes / 16;
     sh.scale_blocks = g->scale_blocks;
+    sh.plan_offsets = moe::plan_offsets_needed(sh);
     return sh;
 }
 
@@ -251,10 +254,11 @@ int place_buffers(moe_group_s* g, Placer& take)
     uint8_t* pool_send = nullptr;
     uint8_t* pool_recv = nullptr;
     int rc;
-    if ((rc = take(&p.err, 1)) || (rc = take(&p.err_sticky, 1)) ||
+    if ((rc = take(&p.err, 2)) || (rc = take(&p.err_sticky, 1)) ||
         (rc = take(&p.err_rank, (size_t)N)) || (rc = take(&p.ticket, 1)) ||
         (rc = take(&p.cnt, (size_t)N * E)) ||
         (rc = take(&p.pos, (size_t)N * T * K)) || (rc = take(&p.soff, (size_t)N * (E + 1))) ||
+        (rc = take(&p.soff_col, (size_t)N * (E + 1))) ||
         (rc = take(&p.roff, (size_t)N * (N + 1))) || (rc = take(&p.rbase, (size_t)N + 1)) ||
         (rc = take(&p.eoff, (size_t)E + 1)) || (rc = take(&p.ebase, (size_t)N * E)) ||
         (rc = take(&p.xfer_src, R)) || (rc = take(&p.xfer_dst, R)) ||
@@ -278,6 +282,8 @@ int place_buffers(moe_group_s* g, Placer& take)
         return rc;
     g->pool_send = pool_send;
     g->pool_recv = pool_recv;
+    g->err_words = p.err;
+    p.err_next = p.err + 1;
     return MOE_OK;
 }
 
@@ -286,7 +292,7 @@ int place_buffers(moe_group_s* g, Placer& take)
 int zero_words(moe_group_s* g)
 {
     const moe::Plan& p = g->plan;
-    if (hipMemset(p.err, 0, sizeof(int32_t)) != hipSuccess ||
+    if (hipMemset(g->err_words, 0, 2 * sizeof(int32_t)) != hipSuccess ||
         hipMemset(p.err_sticky, 0, sizeof(int32_t)) != hipSuccess ||
         hipMemset(p.ticket, 0, sizeof(int32_t)) != hipSuccess ||
         hipMemset(p.eoff, 0, sizeof(int32_t) * (g->desc.num_experts + 1)) != hipSuccess ||
@@ -357,7 +363,7 @@ int poison_dispatch_send(const moe_group_s* g, hipStream_t st)
         (rc = poison(st, g->send_meta, R * 4)) || (rc = poison(st, g->recv_meta, RQ * 4)) ||
         (rc = poison(st, g->send_w, R * 4)) || (rc = poison(st, g->recv_w, RQ * 4)) ||
         (rc = poison(st, p.cnt, N * E * 4)) || (rc = poison(st, p.pos, R * 4)) ||
-        (rc = poison(st, p.soff, N * (E + 1) * 4)) || (rc = poison(st, p.roff, N * (N + 1) * 4)) ||
+        (rc = poison(st, p.soff, N * (E + 1) * 4)) || (rc = poison(st, p.soff_col, N * (E + 1) * 4)) || (rc = poison(st, p.roff, N * (N + 1) * 4)) ||
         (rc = poison(st, p.rbase, (N + 1) * 4)) || (rc = poison(st, p.eoff, (E + 1) * 4)) ||
         (rc = poison(st, p.ebase, N * E * 4)) || (rc = poison(st, p.xfer_src, R * 4)) ||
         (rc = poison(st, p.xfer_dst, R * 8)) || (rc = poison(st, p.shuf_map, R * 8)) ||
@@ -552,6 +558,9 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const in
     using moe::Launch;
     if (g->debug && (rc = poison_dispatch_send(g, stream)))
         return rc;
+    // this cycle's error word, and the next cycle's, which the route plan clears
+    g->plan.err = g->err_words + (g->cycle & 1);
+    g->plan.err_next = g->err_words + ((g->cycle + 1) & 1);
     if ((rc = timed_launch(g, MOE_KERNEL_ROUTE_PLAN, stream, true, [&](const Launch& L) {
              return moe::launch_route_plan(sh, topk_idx, g->plan, rows, L);
          })) ||
@@ -563,6 +572,7 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x, const in
              return moe::launch_transfer(sh, g->plan, rows, L);
          }))))
         return rc;
+    g->cycle++;
     g->T = num_tokens;
     g->state = State::Sent;
     return MOE_OK;
@@ -600,14 +610,10 @@ int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale, int32_
          (rc = poison(stream, expert_scale, (size_t)sh.rows * g->scale_blocks * 4)) ||
          (rc = poison(stream, expert_offsets, (size_t)(sh.E + 1) * 4))))
         return rc;
-    // the receiver's side of the plan: with sender-only addressing (fixed
-    // slots, receiver-side combine) first the group offsets from the exchanged
-    // counts; then the row maps; then the shuffle
-    if ((sh.sender_only &&
-         (rc = timed_launch(g, MOE_KERNEL_OFFSETS, stream, true, [&](const moe::Launch& L) {
-              return moe::launch_offsets(sh, g->plan, L);
-          }))) ||
-        (rc = timed_launch(g, MOE_KERNEL_RECV_MAP, stream, sh.rows > 0, [&](const moe::Launch& L) {
+    // the receiver's side of the plan: the group offsets and row maps from
+    // the exchanged counts (also for an empty cycle, whose offsets are all
+    // zero), then the shuffle
+    if ((rc = timed_launch(g, MOE_KERNEL_RECV_MAP, stream, true, [&](const moe::Launch& L) {
              return moe::launch_recv_map(sh, g->plan, L);
          })) ||
         (rc = timed_launch(g, MOE_KERNEL_SHUFFLE, stream, true, [&](const moe::Launch& L) {

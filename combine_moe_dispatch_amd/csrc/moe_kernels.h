@@ -25,8 +25,9 @@ struct Shape {
     int fixed;            // fixed-slot receive layout: T_max slots per (source, expert),
                           // each expert's area slot-major
     int sender_only;      // fixed slots with the receiver-side combine: dispatch_send's
-                          // kernels use only each sender's own plan, and the group
-                          // offsets are computed in dispatch_recv
+                          // kernels use only each sender's own plan
+    int plan_offsets;     // the route plan's last workgroup forms the group offsets
+                          // (plan_offsets_needed); else the receiver's map kernel does
     int slots;            // T_max (fixed-slot layout)
     int64_t recv_rows;    // rows of the receive planes: rows, or N*E*slots (fixed-slot)
     int64_t rows;         // N*T*K
@@ -35,19 +36,50 @@ struct Shape {
     int scale_blocks;     // H/128 (fp8) or 0
 };
 
+// Whether the pack runs in send-row order (each row's item then comes from
+// the route plan): when one sender's tokens fit well within an XCD's 4 MiB
+// L2, so that the K reads of each token after the first hit it.  DeepSeek-R1 decode (1.75 MiB per sender, one sender per XCD
+// run), staged: pack 86.9 -> 74.5 us warm, 115 -> 99 MALL-flushed; on the
+// prefill (28 MiB per sender) the row order re-reads every token from HBM or
+// the MALL and took 4.9-5.0 ms against 1.87 in token order.  With the
+// partial combine, whose records are made per token, the same launch runs one
+// wave per token for them after the row blocks.
+constexpr int64_t PACK_ROWS_MAX_SENDER_BYTES = 2 << 20;
+
+inline bool pack_in_row_order(const Shape& sh)
+{
+    return (int64_t)sh.T * sh.H * 2 <= PACK_ROWS_MAX_SENDER_BYTES;
+}
+
+// Whether the route plan forms the group offsets in its last workgroup: for
+// the kernels that need them before dispatch_recv -- the packed layout's
+// token-order pack and direct push (their rows' receive rows) and the partial
+// combine (its records).  Otherwise (the staged send-row-order pack, which
+// derives its transfer map from the send offsets, and fixed slots with the
+// receiver-side combine) the route plan ends when its ranks do, and the
+// receiver's map kernel forms them from the exchanged counts: Mixtral decode
+// route plan 7.3 -> 4.2 us, DeepSeek-R1 decode 11.6 -> 5.9 us.
+inline bool plan_offsets_needed(const Shape& sh)
+{
+    return sh.partial || (!sh.fixed && (sh.direct || !pack_in_row_order(sh)));
+}
+
 struct Plan {              // device pointers owned by the group
-    // Errors.  err is the current cycle's word: the route plan's last
-    // workgroup overwrites it with the OR of err_rank[] and its own checks,
-    // and every later kernel of the cycle writes nothing while it is set.
-    // err_sticky collects every cycle's bits until moe_group_status reads and
-    // clears it.
+    // Errors.  err is the current cycle's word and err_next the next cycle's
+    // (the group alternates two words): every route-plan workgroup ORs its
+    // sender's bits into err, and one clears err_next for the next cycle, so
+    // an error stops only the kernels of its own cycle; every later kernel of
+    // the cycle writes nothing while err is set.  err_sticky collects every
+    // cycle's bits until moe_group_status reads and clears it.
     int32_t* err;
+    int32_t* err_next;
     int32_t* err_rank;     // [N]  routing/capacity bits of each sender, this cycle
     int32_t* err_sticky;
     int32_t* ticket;       // arrival counter of the route-plan workgroups (0 between launches)
     int32_t* cnt;          // [N][E]
     int32_t* pos;          // [N][T][K]
     int32_t* soff;         // [N][E+1]
+    int32_t* soff_col;     // [E+1][N]  soff transposed, for sums over the senders
     int32_t* roff;         // [N][N+1]
     int32_t* rbase;        // [N+1]
     int32_t* eoff;         // [E+1]
@@ -111,10 +143,8 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
 hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const float* w,
                        const Plan& p, const Rows& r, const Launch& L);
 hipError_t launch_transfer(const Shape& sh, const Plan& p, const Rows& r, const Launch& L);
-// The group offsets and the cycle's error word alone (one workgroup), for
-// plans whose route plan left them out (Shape::sender_only).
-hipError_t launch_offsets(const Shape& sh, const Plan& p, const Launch& L);
-// The receiver's row maps from the exchanged counts and offsets.
+// The receiver's group offsets and row maps from the exchanged counts and
+// send offsets.
 hipError_t launch_recv_map(const Shape& sh, const Plan& p, const Launch& L);
 hipError_t launch_shuffle(const Shape& sh, const Plan& p, const Rows& r, void* expert_x,
                           float* expert_scale, int32_t* expert_offsets, const Launch& L);

@@ -372,28 +372,23 @@ __device__ void group_offsets_lds(const RouteArgs& ra, const Plan& p, int32_t* w
 }
 
 // The end of the plan, once every sender's counts are in view: the group
-// offsets, then the cycle's error word -- every sender's bits and the
-// offsets' checks.  It overwrites the last cycle's word, so an error stops
-// only the kernels of its own cycle; the sticky word keeps it for the status
-// call.  Every thread of the workgroup calls it; wg_err (LDS) holds the
-// workgroup's own bits; tab, when given, is LDS room for the soff table.
+// offsets, then their checks' bits ORed into the cycle's word (every
+// workgroup has already ORed its sender's bits there) and the sticky word.
+// Every thread of the workgroup calls it; wg_err (LDS) holds the workgroup's
+// bits; tab, when given, is LDS room for the soff table.
 __device__ void close_plan(const RouteArgs& ra, const Plan& p, int32_t* wg_err, int32_t* tab)
 {
     if (tab)
         group_offsets_lds(ra, p, wg_err, tab);
     else
         group_offsets(ra, p, wg_err);
-    int e = 0;
-    for (int j = threadIdx.x; j < ra.N; j += RP_NT)
-        e |= p.err_rank[j];
-    if (e)
-        atomicOr(wg_err, e);
     __syncthreads();
     if (threadIdx.x == 0) {
-        const int32_t cyc = *wg_err;
-        *p.err = cyc;
-        if (cyc)
-            atomicOr(p.err_sticky, cyc);
+        const int32_t bits = *wg_err;
+        if (bits) {
+            atomicOr(p.err, bits);
+            atomicOr(p.err_sticky, bits);
+        }
     }
 }
 
@@ -403,7 +398,9 @@ __device__ void close_plan(const RouteArgs& ra, const Plan& p, int32_t* wg_err, 
 // cap (when cap >= 0) raises the capacity bit.
 __device__ __forceinline__ void publish_counts(int32_t* cur, int nkeys, int32_t* __restrict__ cnt_out,
                                                int32_t* __restrict__ off_out, int* wave_sums,
-                                               int cap, int32_t* err)
+                                               int cap, int32_t* err,
+                                               int32_t* __restrict__ off_col = nullptr,
+                                               int col_stride = 0)
 {
     const int tid = threadIdx.x;
     const int per = (nkeys + RP_NT - 1) / RP_NT;
@@ -427,12 +424,17 @@ __device__ __forceinline__ void publish_counts(int32_t* cur, int nkeys, int32_t*
         if (k < nkeys) {
             const int c = cur[k];
             off_out[k] = run;
+            if (off_col)
+                off_col[(size_t)k * col_stride] = run;
             cur[k] = run;
             run += c;
         }
     }
-    if (tid == 0)
+    if (tid == 0) {
         off_out[nkeys] = total;
+        if (off_col)
+            off_col[(size_t)nkeys * col_stride] = total;
+    }
     __syncthreads();
 }
 
@@ -584,6 +586,8 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
         mask[j] = 0ull;
     if (tid == 0)
         wg_err = 0;
+    if (s == 0 && tid == 0)
+        *p.err_next = 0;             // the next cycle starts with a clean word
     // expert ids of the first HC chunks stay in registers for both
     // the counting and the ranking (thread tid takes item c*chunk + tid of
     // chunk c); all loads are issued before the first use
@@ -669,7 +673,8 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     // item inside its expert's rows (and of every first item of a rank among
     // the sender's partial rows, ordered by rank, then token)
     publish_counts(cur, E, p.cnt + (size_t)s * E, p.soff + (size_t)s * (E + 1), wave_sums,
-                   ra.slot_cap, &wg_err);
+                   ra.slot_cap, &wg_err,
+                   p.soff_col + s, N);
     if (!ra.partial) {
         stable_ranks<false, HC>(items, NK, CW, mask, cur, held_e,
                             [&](int i, bool mine) { return mine ? my_idx[i] : -1; },
@@ -695,10 +700,10 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
     __syncthreads();
     if (tid == 0) {
         p.err_rank[s] = wg_err;
-        // without the offsets tail the cycle word is made in dispatch_recv;
-        // the sticky word gets the sender's bits now
-        if (!ra.offsets && wg_err)
+        if (wg_err) {
+            atomicOr(p.err, wg_err);
             atomicOr(p.err_sticky, wg_err);
+        }
     }
     if (!ra.offsets)
         return;
@@ -718,21 +723,6 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
         atomicExch(p.ticket, 0);
 }
 
-// The group offsets and the cycle's error word in a launch of their own (one
-// workgroup), for the fixed-slot layout with the receiver-side combine: there
-// the senders address their slots from their own counts ([EPMC] "Portable
-// kernels": no synchronisation with other ranks before writing), so the
-// offsets the receivers need are formed at dispatch_recv from the exchanged
-// counts, after the senders' kernels.
-__global__ __launch_bounds__(RP_NT) void offsets_kernel(RouteArgs ra, Plan p)
-{
-    extern __shared__ __align__(16) uint64_t tab64[];
-    __shared__ int32_t wg_err;
-    if (threadIdx.x == 0)
-        wg_err = 0;
-    __syncthreads();
-    close_plan(ra, p, &wg_err, ra.table_lds ? reinterpret_cast<int32_t*>(tab64) : nullptr);
-}
 
 // ---------------------------------------------------------------------------
 // Work split of the row kernels.  SPLIT waves share one row, each moving a
@@ -859,8 +849,8 @@ __device__ inline void record_maps(const Shape& sh, const Plan& p, const RowDest
 }
 
 // Whether sender s's rows are to be dropped this cycle: the cycle's error
-// word, or with Shape::sender_only (where that word is made later, at
-// dispatch_recv) the sender's own bits from this cycle's route plan.
+// word, or with Shape::sender_only (whose senders use nothing from the
+// exchange) the sender's own bits from this cycle's route plan.
 __device__ inline bool sender_failed(const Shape& sh, const Plan& p, int s)
 {
     return sh.sender_only ? p.err_rank[s] != 0 : *p.err != 0;
@@ -1159,6 +1149,54 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_fp8_kernel(Shape sh, Plan p
 // expert-side partial combine the lead wave also moves the row's router
 // weight, and waves past the rows' write the per-token records.
 // ---------------------------------------------------------------------------
+// The sum of one int per lane over the wave (every lane active), as a
+// wave-uniform value: DPP moves within each row of 16 lanes (swap neighbours,
+// swap pairs, mirror within 8, mirror within 16), so every lane holds its
+// row's sum, then the four rows' sums are read out.  Register moves only,
+// where shuffles would go through the LDS crossbar.
+__device__ inline int wave_sum(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);   // row_mirror
+    return readlane(v, 0) + readlane(v, 16) + readlane(v, 32) + readlane(v, 48);
+}
+
+// The first packed receive row of the (s -> d) rows, rbase[d] + roff[d][s],
+// from the senders' offsets alone: what the senders before s send to ranks up
+// to d and what s and the senders after it send to ranks before d, i.e. the
+// sum of soff[j][(d+1)*L] over j < s and of soff[j][d*L] over j >= s.  Lanes
+// take the senders, C*64 of them in one round of loads.  Every lane of the
+// wave must call it.
+template <int C>
+__device__ inline int seg_base_c(const Shape& sh, const Plan& p, int s, int d)
+{
+    const int lane = lane_id();
+    // the two columns, senders consecutive (soff_col is soff transposed)
+    const int32_t* lo = p.soff_col + (size_t)d * sh.L * sh.N;
+    const int32_t* hi = p.soff_col + (size_t)(d + 1) * sh.L * sh.N;
+    int v[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int j = min(c * WAVE + lane, sh.N - 1);
+        v[c] = (j < s ? hi : lo)[j];
+    }
+    int part = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+        if (c * WAVE + lane < sh.N)
+            part += v[c];
+    for (int j = C * WAVE + lane; j < sh.N; j += WAVE)
+        part += (j < s ? hi : lo)[j];
+    return wave_sum(part);
+}
+
+__device__ inline int seg_base(const Shape& sh, const Plan& p, int s, int d)
+{
+    return sh.N <= WAVE ? seg_base_c<1>(sh, p, s, d) : seg_base_c<4>(sh, p, s, d);
+}
+
 // The last bucket b in [0, nb) whose start row[b * stride] is <= key, with
 // that start, for non-decreasing starts (the expert or rank parts of a
 // sender's send rows); -1 if none.  Lanes take 64 buckets at a time, and up
@@ -1195,12 +1233,12 @@ __device__ inline int2 find_bucket(const int32_t* __restrict__ row, int nb, int 
     return make_int2(b, start);
 }
 
-// The receive-plane row that the direct transport gives send row (s, pk),
-// from the sender's own offsets and the group offsets alone: the rank d whose
-// part of the sender's rows holds pk, then q = rbase[d] + roff[d][s] + pk -
-// soff[s][d*L]; with fixed slots the expert e whose part holds it, then slot
-// i = pk - soff[s][e], row (e*T_max + i)*N + s.  -1 if a check fails.  Every
-// lane of the wave must call it.
+// The receive-plane row that the direct transport gives send row (s, pk): the
+// rank d whose part of the sender's rows holds pk, then q = rbase[d] +
+// roff[d][s] + pk - soff[s][d*L] (the route plan formed the group offsets);
+// with fixed slots, from the sender's own offsets alone, the expert e whose
+// part holds it, then slot i = pk - soff[s][e], row (e*T_max + i)*N + s.  -1
+// if a check fails.  Every lane of the wave must call it.
 __device__ inline int64_t direct_row(const Shape& sh, const Plan& p, int s, int pk)
 {
     const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
@@ -1245,20 +1283,42 @@ __device__ inline void token_records(const Shape& sh, const Plan& p,
     record_partial(sh, p, tok, s, d, rd);
 }
 
+// The map the staged transfer follows for send row (s, pk) holding item m,
+// from the senders' offsets alone: the row's packed receive row q (xfer_src[q]
+// = the send row), or with fixed slots its slot (send_slot).  Every lane of
+// the lead wave calls it.
 __device__ inline void record_send_row(const Shape& sh, const Plan& p,
                                        const int32_t* __restrict__ idx, int s, int pk, int m)
 {
+    const int lane = lane_id();
     const int64_t TK = (int64_t)sh.T * sh.K;
+    const int64_t srow = s * TK + pk;
     const int e = idx[s * TK + m];
     if ((unsigned)e >= (unsigned)sh.E) {
-        raise_err(p, ERR_BIT_INTERNAL);
+        if (lane == 0)
+            raise_err(p, ERR_BIT_INTERNAL);
         return;
     }
-    const RowDest rd = row_dest(sh, p, s, e, pk);
-    if (rd.ok)
-        record_maps(sh, p, rd);
-    else
-        raise_err(p, ERR_BIT_INTERNAL);
+    const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
+    if (sh.fixed) {
+        const int i = pk - so[e];
+        const int64_t slot = ((int64_t)e * sh.slots + i) * sh.N + s;
+        if (lane == 0) {
+            if ((unsigned)i < (unsigned)sh.slots && slot < sh.recv_rows)
+                p.send_slot[srow] = (int32_t)slot;
+            else
+                raise_err(p, ERR_BIT_INTERNAL);
+        }
+        return;
+    }
+    const int d = e / sh.L;
+    const int64_t q = (int64_t)seg_base(sh, p, s, d) + pk - so[d * sh.L];
+    if (lane == 0) {
+        if ((uint64_t)q < (uint64_t)sh.rows)
+            p.xfer_src[q] = (int32_t)srow;
+        else
+            raise_err(p, ERR_BIT_INTERNAL);
+    }
 }
 
 // Blocks past the row blocks: one wave per token, for the partial combine's
@@ -1323,13 +1383,15 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, 
                 st_nt(v[u], dst + j);
         }
     }
-    if (rs.lead && lane == 0) {
-        if (sh.direct)
-            dst_meta[drow] = m;
-        else
+    if (rs.lead) {
+        if (!sh.direct)
             record_send_row(sh, p, idx, s, pk, m);
-        if (dst_w)
-            dst_w[drow] = w[s * TK + m];
+        if (lane == 0) {
+            if (sh.direct)
+                dst_meta[drow] = m;
+            if (dst_w)
+                dst_w[drow] = w[s * TK + m];
+        }
     }
 }
 
@@ -1393,13 +1455,15 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(Shape sh, P
             }
         }
     }
-    if (rs.lead && lane == 0) {
-        if (sh.direct)
-            dst_meta[drow] = m;
-        else
+    if (rs.lead) {
+        if (!sh.direct)
             record_send_row(sh, p, idx, s, pk, m);
-        if (dst_w)
-            dst_w[drow] = w[s * TK + m];
+        if (lane == 0) {
+            if (sh.direct)
+                dst_meta[drow] = m;
+            if (dst_w)
+                dst_w[drow] = w[s * TK + m];
+        }
     }
 }
 
@@ -1479,11 +1543,19 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p
 
 // The receiver's row maps, formed at dispatch_recv from the exchanged counts
 // and offsets alone ([EFA] "Send and receive buffers": once the counts are
-// exchanged, each rank knows where its rows come from).  One wave per
-// (expert e, sender s) pair, pairs in expert order so consecutive waves
-// write consecutive expert rows; lane i < cnt[s][e] takes the pair's i-th
-// row:
-//   expert row        r    = eoff[e] + sum_{s'<s} cnt[s'][e] + i
+// exchanged, each rank knows where its rows come from), and -- when the route
+// plan left them out (Shape::plan_offsets unset) -- the group offsets too.
+// One wave per (expert e, sender s) pair, pairs in expert order so
+// consecutive waves write consecutive expert rows.  The sums over senders
+// (lanes take the senders j, 64 at a time, all loaded in one round):
+//   eoff[e]               = sum_j soff[j][e]
+//   rbase[d]              = sum_j soff[j][d*L]                      (d = e / L)
+//   rbase[d] + roff[d][s] = sum_{j<s} soff[j][(d+1)L] + sum_{j>=s} soff[j][d*L]
+//   first expert row r0   = eoff[e] + sum_{j<s} cnt[j][e]
+// The pairs publish the tables they own (eoff by s = 0; roff and rbase by
+// the rank's first expert; the totals by the first pair); then lane i <
+// cnt[s][e] takes the pair's i-th row:
+//   expert row        r    = r0 + i
 //   packed receive row q    = rbase[d] + roff[d][s] + soff[s][e] - soff[s][d*L] + i
 //   receive-plane row qd   = q, or the slot (e*T_max + i)*N + s
 //   send row          srow = s*T*K + soff[s][e] + i   (its place on the way back)
@@ -1497,24 +1569,77 @@ __global__ __launch_bounds__(COPY_THREADS) void recv_map_kernel(Shape sh, Plan p
     const int64_t w = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE;
     if (w >= (int64_t)sh.E * sh.N)
         return;
-    const int e = (int)(w / sh.N), s = (int)(w % sh.N);
+    const int lane = lane_id();
+    const int N = sh.N, L = sh.L;
+    const int e = (int)(w / N), s = (int)(w % N);
+    const int d = e / L;
+    const size_t W = (size_t)sh.E + 1;
+    const int32_t* so = p.soff + (size_t)s * W;
     const int c = p.cnt[(size_t)s * sh.E + e];
+    const bool tables = !sh.plan_offsets;
+    const bool first_pair = tables && e == 0 && s == 0;
+    if (c <= 0 && !(tables && (s == 0 || e == d * L)))
+        return;
+    const int so_e = so[e], so_d = so[d * L];
+    int eo = 0, qb = 0, before = 0;
+    if (!tables) {
+        eo = p.eoff[e];
+        qb = p.rbase[d] + p.roff[(size_t)d * (N + 1) + s];
+        for (int j = lane; j < s; j += WAVE)
+            before += p.cnt[(size_t)j * sh.E + e];
+        before = wave_sum(before);
+    } else {
+        // columns of soff transposed (senders consecutive): coalesced loads
+        const int32_t* col_e = p.soff_col + (size_t)e * N;
+        const int32_t* col_lo = p.soff_col + (size_t)d * L * N;
+        const int32_t* col_hi = p.soff_col + (size_t)(d + 1) * L * N;
+        const int32_t* col_tot = p.soff_col + (size_t)sh.E * N;
+        int rb = 0, tot = 0;
+        for (int j0 = 0; j0 < N; j0 += WAVE) {
+            const int j = j0 + lane;
+            if (j < N) {
+                const int lo = col_lo[j];
+                eo += col_e[j];
+                rb += lo;
+                if (j < s) {
+                    qb += col_hi[j];
+                    before += p.cnt[(size_t)j * sh.E + e];
+                } else {
+                    qb += lo;
+                }
+                if (first_pair)
+                    tot += col_tot[j];
+            }
+        }
+        eo = wave_sum(eo);
+        rb = wave_sum(rb);
+        qb = wave_sum(qb);
+        before = wave_sum(before);
+        if (first_pair)
+            tot = wave_sum(tot);
+        if (lane == 0) {
+            if (s == 0)
+                p.eoff[e] = eo;
+            if (e == d * L) {
+                int32_t* ro = p.roff + (size_t)d * (N + 1);
+                ro[s] = qb - rb;
+                if (s == N - 1)
+                    ro[N] = qb - rb + so[(d + 1) * L] - so_d;
+                if (s == 0)
+                    p.rbase[d] = rb;
+            }
+            if (first_pair) {
+                p.eoff[sh.E] = tot;
+                p.rbase[N] = tot;
+            }
+        }
+    }
     if (c <= 0)
         return;
-    const int d = e / sh.L;
-    const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
-    const int64_t srow0 = (int64_t)s * sh.T * sh.K + so[e];
-    const int64_t q0 = (int64_t)p.rbase[d] + p.roff[(size_t)d * (sh.N + 1) + s] + so[e] - so[d * sh.L];
-    // the pair's first expert row: expert e's offset plus the rows of e from
-    // the senders before s (lane j adds sender j's count, then a wave sum)
-    int before = 0;
-    for (int j = lane_id(); j < s; j += WAVE)
-        before += p.cnt[(size_t)j * sh.E + e];
-#pragma unroll
-    for (int m = WAVE / 2; m >= 1; m >>= 1)
-        before += __shfl_xor(before, m, WAVE);
-    const int64_t r0 = (int64_t)p.eoff[e] + before;
-    for (int i = lane_id(); i < c; i += WAVE) {
+    const int64_t srow0 = (int64_t)s * sh.T * sh.K + so_e;
+    const int64_t q0 = (int64_t)qb + so_e - so_d;
+    const int64_t r0 = (int64_t)eo + before;
+    for (int i = lane; i < c; i += WAVE) {
         const int64_t q = q0 + i, r = r0 + i, srow = srow0 + i;
         const int64_t qd = sh.fixed ? ((int64_t)e * sh.slots + i) * sh.N + s : q;
         if ((uint64_t)q >= (uint64_t)sh.rows || (uint64_t)r >= (uint64_t)sh.rows ||
@@ -2226,21 +2351,6 @@ inline int table_in_lds(const Shape& sh)
     return !sh.partial && (int64_t)sh.N * (sh.E + 1) <= TAB_MAX_INTS;
 }
 
-// Whether the pack runs in send-row order (each row's item then comes from
-// the route plan): when one sender's tokens fit
-// well within an XCD's 4 MiB L2, so that the K reads of each token after the
-// first hit it.  DeepSeek-R1 decode (1.75 MiB per sender, one sender per XCD
-// run), staged: pack 86.9 -> 74.5 us warm, 115 -> 99 MALL-flushed; on the
-// prefill (28 MiB per sender) the row order re-reads every token from HBM or
-// the MALL and took 4.9-5.0 ms against 1.87 in token order.  With the
-// partial combine, whose records are made per token, the same launch runs one
-// wave per token for them after the row blocks.
-constexpr int64_t PACK_ROWS_MAX_SENDER_BYTES = 2 << 20;
-
-inline bool pack_in_row_order(const Shape& sh)
-{
-    return (int64_t)sh.T * sh.H * 2 <= PACK_ROWS_MAX_SENDER_BYTES;
-}
 
 }  // namespace
 
@@ -2257,7 +2367,7 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     ra.L = sh.L;
     ra.partial = sh.partial;
     ra.slot_cap = sh.fixed ? sh.slots : -1;
-    ra.offsets = !sh.sender_only;
+    ra.offsets = sh.plan_offsets;
     ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
     // keys: E experts, plus N ranks for the partial combine.  Two buffers of
     // lane masks take 16 bytes per (wave, key) and the cursors 8 bytes per
@@ -2286,22 +2396,6 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     return hipGetLastError();
 }
 
-hipError_t launch_offsets(const Shape& sh, const Plan& p, const Launch& L)
-{
-    RouteArgs ra{};
-    ra.N = sh.N;
-    ra.T = sh.T;
-    ra.K = sh.K;
-    ra.E = sh.E;
-    ra.L = sh.L;
-    ra.partial = sh.partial;
-    ra.slot_cap = sh.fixed ? sh.slots : -1;
-    ra.offsets = 1;
-    ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
-    ra.table_lds = table_in_lds(sh);
-    go(offsets_kernel, dim3(1), dim3(RP_NT), ra.table_lds ? table_lds_bytes(sh) : 0, L, ra, p);
-    return hipGetLastError();
-}
 
 hipError_t launch_recv_map(const Shape& sh, const Plan& p, const Launch& L)
 {

@@ -341,9 +341,8 @@ typedef enum moe_kernel_id {
     MOE_KERNEL_PARTIAL_SEND = 8,    /* MOE_COMBINE_PARTIAL: the expert-side partial sums */
     MOE_KERNEL_PARTIAL_TRANSFER = 9,
     MOE_KERNEL_PARTIAL_REDUCE = 10,
-    MOE_KERNEL_RECV_MAP = 11,       /* dispatch_recv: the receiver's row maps from the exchanged counts */
-    MOE_KERNEL_OFFSETS = 12,        /* fixed slots, receiver-side combine: the group offsets at dispatch_recv */
-    MOE_KERNEL_COUNT = 13
+    MOE_KERNEL_RECV_MAP = 11,       /* dispatch_recv: the receiver's group offsets and row maps from the exchanged counts */
+    MOE_KERNEL_COUNT = 12
 } moe_kernel_id;
 
 typedef enum moe_kernel_mask { MOE_KERNEL_ALL = (1 << MOE_KERNEL_COUNT) - 1 } moe_kernel_mask;

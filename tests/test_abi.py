@@ -48,8 +48,7 @@ def test_strerror_and_kernel_names(lib):
     assert lib.moe_kernel_name(8) == b"partial_send_kernel"
     assert lib.moe_kernel_name(10) == b"partial_reduce_kernel"
     assert lib.moe_kernel_name(11) == b"recv_map_kernel"
-    assert lib.moe_kernel_name(12) == b"offsets_kernel"
-    assert lib.moe_kernel_name(13) == b""
+    assert lib.moe_kernel_name(12) == b""
 
 
 def test_host_validation_without_gpu(lib):

@@ -47,20 +47,28 @@ def test_byte_model_matches_closed_form(key, transport):
 
 def test_headline_totals():
     """The DeepSeek-R1 decode totals: 4.817 GB staged (602 us at 8 TB/s),
-    2.937 GB with direct push (367 us); of them 758 148 bytes are the
-    receiver's map kernel: reading the counts and offsets (32 x 256 counts,
-    32 x 257 send offsets, 32 x 256 expert bases, 32 x 33 receive offsets,
-    33 receive bases, 4 bytes each) and writing 20 bytes of maps per row."""
+    2.938 GB with direct push (367 us); of them 726 408 bytes are the
+    receiver's map kernel: forming the group offsets (32 x 256 counts and
+    32 x 257 send offsets in; 32 x 33 receive offsets, 33 receive bases and
+    257 expert offsets out, 4 bytes each) and writing 20 bytes of maps per
+    row.  The route plan (no group offsets here: the pack runs in send-row
+    order) reads idx and writes counts, send offsets (row- and column-major),
+    positions and each send row's item."""
     c = CONFIGS["C"]
-    maps = 4 * (2 * 32 * 256 + 32 * 257 + 32 * 33 + 33) + 32768 * 20
-    assert bench.kernel_bytes(c)["recv_map"] == maps == 758_148
-    assert sum(bench.kernel_bytes(c).values()) == 4_816_804_364 + maps
-    assert sum(bench.kernel_bytes(c, "direct").values()) == 2_937_494_028 + maps
-    # fixed slots with the receiver-side combine: the offsets leave the route
-    # plan for their own kernel, the total is unchanged
+    maps = 4 * (32 * 256 + 32 * 257 + 32 * 33 + 33 + 257) + 32768 * 20
+    kb = bench.kernel_bytes(c)
+    assert kb["recv_map"] == maps == 726_408
+    assert kb["route_plan"] == 4 * (3 * 32768 + 32 * 256 + 2 * 32 * 257)
+    assert sum(kb.values()) == 4_817_459_852
+    # the direct push reads the group offsets from the route plan
+    assert sum(bench.kernel_bytes(c, "direct").values()) == 2_938_149_516 + 71_048
+    # fixed slots: 4 more bytes of maps per row (the slot of each receive row)
     fx = bench.kernel_bytes(c, layout="fixed")
-    assert sum(fx.values()) == sum(bench.kernel_bytes(c).values()) + 32768 * 4
-    assert fx["offsets"] > 0
+    assert sum(fx.values()) == sum(kb.values()) + 32768 * 4
+    # the packed layout's token-order pack (a sender's tokens above 2 MiB)
+    # needs the group offsets from the route plan too
+    big = c.with_(T=256)
+    assert bench.kernel_bytes(big)["route_plan"] > bench.kernel_bytes(big, layout="fixed")["route_plan"]
 
 
 def test_partial_byte_model_moves_p_rows():
