@@ -68,8 +68,8 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
     fixed slots): tables and maps are its whole job, so they are counted
     there.  The route plan's last workgroup forms the group offsets too (the
     same tables in and out) only where a kernel before dispatch_recv needs
-    them: the packed layout's token-order pack and direct push, and the
-    partial combine (the map kernel then reads them instead, counted alike).
+    them: the packed layout's token-order pack and the partial combine (the
+    map kernel then reads them instead, counted alike).
     When the pack runs in send-row order (a sender's tokens within 2 MiB) the
     route plan writes each send row's item and the pack reads it in place of
     the positions (staged: the send meta words, which the pack no longer
@@ -96,7 +96,7 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
         "combine_reduce": R * hy + R * 8 + tokens * H * 2,
         "recv_map": offs + R * (20 + (4 if layout == "fixed" else 0)),
     }
-    if combine == "partial" or (layout == "packed" and (transport == "direct" or not row_order)):
+    if combine == "partial" or (layout == "packed" and not row_order):
         kb["route_plan"] += offs
     if row_order:
         kb["route_plan"] += R * 4

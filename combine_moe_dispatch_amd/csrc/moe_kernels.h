@@ -53,15 +53,17 @@ inline bool pack_in_row_order(const Shape& sh)
 
 // Whether the route plan forms the group offsets in its last workgroup: for
 // the kernels that need them before dispatch_recv -- the packed layout's
-// token-order pack and direct push (their rows' receive rows) and the partial
-// combine (its records).  Otherwise (the staged send-row-order pack, which
-// derives its transfer map from the send offsets, and fixed slots with the
+// token-order pack (its rows' receive rows) and the partial combine (its
+// records).  Otherwise (the send-row-order pack, which derives its receive
+// rows or transfer map from the send offsets, and fixed slots with the
 // receiver-side combine) the route plan ends when its ranks do, and the
-// receiver's map kernel forms them from the exchanged counts: Mixtral decode
-// route plan 7.3 -> 4.2 us, DeepSeek-R1 decode 11.6 -> 5.9 us.
+// receiver's map kernel forms them from the exchanged counts.  Route plan,
+// warm: Mixtral decode 7.3 -> 5.1 us (staged) and 8.7 -> 6.6 (direct);
+// DeepSeek-R1 decode 11.2 -> 6.3 and 11.6 -> 6.1; Kimi-K2 decode 15.2 -> 6.6
+// and 15.3 -> 6.8, the pack and the receive map taking back 0.5-7 us of it.
 inline bool plan_offsets_needed(const Shape& sh)
 {
-    return sh.partial || (!sh.fixed && (sh.direct || !pack_in_row_order(sh)));
+    return sh.partial || (!sh.fixed && !pack_in_row_order(sh));
 }
 
 struct Plan {              // device pointers owned by the group

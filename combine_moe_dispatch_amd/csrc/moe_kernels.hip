@@ -1235,10 +1235,11 @@ __device__ inline int2 find_bucket(const int32_t* __restrict__ row, int nb, int 
 
 // The receive-plane row that the direct transport gives send row (s, pk): the
 // rank d whose part of the sender's rows holds pk, then q = rbase[d] +
-// roff[d][s] + pk - soff[s][d*L] (the route plan formed the group offsets);
-// with fixed slots, from the sender's own offsets alone, the expert e whose
-// part holds it, then slot i = pk - soff[s][e], row (e*T_max + i)*N + s.  -1
-// if a check fails.  Every lane of the wave must call it.
+// roff[d][s] + pk - soff[s][d*L] (from the route plan's tables when it formed
+// them, else seg_base); with fixed slots, from the sender's own offsets alone,
+// the expert e whose part holds it, then slot i = pk - soff[s][e], row
+// (e*T_max + i)*N + s.  -1 if a check fails.  Every lane of the wave must
+// call it.
 __device__ inline int64_t direct_row(const Shape& sh, const Plan& p, int s, int pk)
 {
     const int32_t* so = p.soff + (size_t)s * (sh.E + 1);
@@ -1255,7 +1256,9 @@ __device__ inline int64_t direct_row(const Shape& sh, const Plan& p, int s, int 
                                 : find_bucket<4>(so, sh.N, sh.L, pk);
     if (b.x < 0)
         return -1;
-    const int64_t q = (int64_t)p.rbase[b.x] + p.roff[(size_t)b.x * (sh.N + 1) + s] + pk - b.y;
+    const int64_t base = sh.plan_offsets ? (int64_t)p.rbase[b.x] + p.roff[(size_t)b.x * (sh.N + 1) + s]
+                                         : (int64_t)seg_base(sh, p, s, b.x);
+    const int64_t q = base + pk - b.y;
     return (uint64_t)q < (uint64_t)sh.rows ? q : -1;
 }
 

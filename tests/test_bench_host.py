@@ -60,8 +60,7 @@ def test_headline_totals():
     assert kb["recv_map"] == maps == 726_408
     assert kb["route_plan"] == 4 * (3 * 32768 + 32 * 256 + 2 * 32 * 257)
     assert sum(kb.values()) == 4_817_459_852
-    # the direct push reads the group offsets from the route plan
-    assert sum(bench.kernel_bytes(c, "direct").values()) == 2_938_149_516 + 71_048
+    assert sum(bench.kernel_bytes(c, "direct").values()) == 2_938_149_516
     # fixed slots: 4 more bytes of maps per row (the slot of each receive row)
     fx = bench.kernel_bytes(c, layout="fixed")
     assert sum(fx.values()) == sum(kb.values()) + 32768 * 4
