@@ -95,6 +95,46 @@ def test_routing_error_stops_only_its_own_cycle(combine_mode):
         mep.moe_group_destroy(g)
 
 
+@pytest.mark.parametrize("transport", [0, 1])
+def test_routing_errors_in_alternate_cycles(transport):
+    """The group alternates two cycle error words (each route plan clears the
+    next cycle's): failing and valid cycles in the pattern bad, good, bad,
+    bad, good, good on one group with no status read in between -- every
+    valid cycle equals the oracle whichever word it got, every failing cycle
+    leaves the caller's output untouched, and the status afterwards reports
+    the routing error once."""
+    cfg = CONFIGS["A"]
+    say(f"[gpu] alternating routing errors {cfg.describe()} transport={transport}")
+    inp = make_inputs(cfg)
+    bad = inp["idx"].copy()
+    bad[1, 3, 0] = -1
+    g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16, transport, 0)
+    from tests.test_gpu_parity import _compare_all
+    try:
+        R = cfg.rows
+        x, idx, w = to_dev(torch, inp["x"]), to_dev(torch, bad), to_dev(torch, inp["w"])
+        expert_x = torch.empty((R * cfg.H,), dtype=torch.int16, device="cuda")
+        offs = torch.empty((cfg.E + 1,), dtype=torch.int32, device="cuda")
+        y = torch.zeros((R, cfg.H), dtype=torch.bfloat16, device="cuda")
+        for n, good in enumerate([False, True, False, False, True, True]):
+            if good:
+                gpu = run_cycle(torch, mep, cfg, inp, group=g, transport=transport,
+                                check_status=False)
+                _compare_all(cfg, inp, gpu)
+                continue
+            out = torch.full((cfg.N, cfg.T, cfg.H), 0x1234, dtype=torch.int16, device="cuda")
+            mep.moe_dispatch_send(g, cfg.T, x, idx)
+            mep.moe_dispatch_recv(g, expert_x, None, offs)
+            mep.moe_combine_send(g, y)
+            mep.moe_combine_recv(g, w, out)
+            torch.cuda.synchronize()
+            assert torch.all(out == 0x1234).item(), f"cycle {n} wrote its output"
+        assert mep.moe_group_status(g) == mep.MOE_ERR_ROUTING
+        assert mep.moe_group_status(g) == mep.MOE_OK
+    finally:
+        mep.moe_group_destroy(g)
+
+
 def test_call_order_and_arguments():
     cfg = CONFIGS["A"]
     say(f"[gpu] call order {cfg.describe()}")
