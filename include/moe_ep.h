@@ -209,10 +209,11 @@ int moe_group_destroy(moe_group_t g);
  *   topk_weights  device, fp32 [N][T][K] with MOE_COMBINE_PARTIAL (carried
  *                 to the expert owners with the rows); ignored, may be
  *                 NULL, with MOE_COMBINE_RECEIVER
- * Enqueues: route plan (counts, stable positions, offsets; with
- * MOE_COMBINE_PARTIAL also the partial-row plan), pack (+ e4m3 encode) and,
- * with the staged transport, the transfer into the receive buffers.  Reads
- * x, topk_idx and topk_weights only. */
+ * Enqueues: route plan (counts, stable positions, send offsets; the group
+ * offsets too where the pack or the partial combine needs them before
+ * dispatch_recv; with MOE_COMBINE_PARTIAL also the partial-row plan), pack
+ * (+ e4m3 encode) and, with the staged transport, the transfer into the
+ * receive buffers.  Reads x, topk_idx and topk_weights only. */
 int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x,
                       const int32_t* topk_idx, const float* topk_weights,
                       hipStream_t stream);
@@ -227,7 +228,9 @@ int moe_dispatch_send(moe_group_t g, int32_t num_tokens, const void* x,
  *   expert_offsets  device, int32 [E+1]: expert e's rows are
  *                   [expert_offsets[e], expert_offsets[e+1]); rank d's GEMM
  *                   input is rows [expert_offsets[d*L], expert_offsets[(d+1)*L])
- * The back-routing metadata stays in the group. */
+ * Enqueues: the receiver's group offsets and row maps from the exchanged
+ * counts and send offsets, then the shuffle.  The back-routing metadata
+ * stays in the group. */
 int moe_dispatch_recv(moe_group_t g, void* expert_x, float* expert_scale,
                       int32_t* expert_offsets, hipStream_t stream);
 
