@@ -149,7 +149,7 @@ struct RouteArgs {
     int chunk_waves;        // RP_WAVES, or fewer for large E (LDS budget)
     int partial;            // also plan the expert-side partial rows
     int slot_cap;           // fixed-slot layout: most rows per (sender, expert); -1: none
-    int offsets;            // the last workgroup computes the group offsets
+    int offsets;            // the last workgroup computes the group offsets (Shape::plan_offsets)
     int table_lds;          // ... from a copy of soff in the dynamic LDS
     int32_t* send_meta;     // when set: each send row's item t*K+k, written with the positions
                             // (the send meta words, or the direct transport's send_item)
@@ -694,9 +694,11 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
                            ra.send_meta ? ra.send_meta + (size_t)s * items : nullptr);
     }
 
-    // Publish this rank's counts and error bits and draw a ticket.  Every
-    // wave waits for its own stores, then one agent-scope release (an L2
-    // write-back) covers the whole workgroup before the ticket is taken.
+    // Publish this rank's error bits (into the cycle's word too).  Where the
+    // group offsets are formed here, draw a ticket: every wave waits for its
+    // own stores, then one agent-scope release (an L2 write-back) covers the
+    // whole workgroup before the ticket is taken, and the last workgroup
+    // forms them.
     __syncthreads();
     if (tid == 0) {
         p.err_rank[s] = wg_err;
