@@ -70,6 +70,35 @@ def test_headline_totals():
     assert bench.kernel_bytes(big)["route_plan"] > bench.kernel_bytes(big, layout="fixed")["route_plan"]
 
 
+def test_byte_model_follows_the_librarys_rules():
+    """The byte model's pack-order boundary is the library's (read from the
+    kernel interface header), and the group offsets are counted in the route
+    plan exactly where the library forms them there: the token-order pack
+    of the packed layout and the partial combine."""
+    import re
+    hdr = open(os.path.join(ROOT, "combine_moe_dispatch_amd", "csrc", "moe_kernels.h")).read()
+    m = re.search(r"PACK_ROWS_MAX_SENDER_BYTES\s*=\s*(\d+)\s*<<\s*(\d+)", hdr)
+    assert m and bench.PACK_ROWS_MAX_SENDER_BYTES == int(m.group(1)) << int(m.group(2))
+    assert "return sh.partial || (!sh.fixed && !pack_in_row_order(sh));" in hdr
+    c = CONFIGS["C"]
+    small, big = c, c.with_(T=256)           # 1.75 MiB and 3.5 MiB per sender
+    base = bench.kernel_bytes(small, layout="fixed")["route_plan"]
+    for cfg, transport, combine, layout, tail in [
+            (small, "staged", "receiver", "packed", False), (small, "direct", "receiver", "packed", False),
+            (small, "staged", "receiver", "fixed", False), (small, "staged", "partial", "packed", True),
+            (big, "staged", "receiver", "packed", True), (big, "direct", "receiver", "packed", True),
+            (big, "staged", "receiver", "fixed", False)]:
+        kb = bench.kernel_bytes(cfg, transport, combine, 1000 if combine == "partial" else 0, layout)
+        R, N, E = cfg.rows, cfg.N, cfg.E
+        offs = 4 * (N * E + N * (E + 1) + N * (N + 1) + (N + 1) + (E + 1))
+        plain = 4 * (2 * R + N * E + 2 * N * (E + 1)) + (4 * R if cfg is small else 0)
+        extra = kb["route_plan"] - plain
+        if combine == "partial":
+            extra -= 2 * R * 4 + N * E * 4 + 3 * N * (N + 1) * 4 + 2 * (N + 1) * 4
+        assert extra == (offs if tail else 0), (cfg.T, transport, combine, layout)
+    assert base == 4 * (3 * c.rows + c.N * c.E + 2 * c.N * (c.E + 1))
+
+
 def test_partial_byte_model_moves_p_rows():
     """With the partial combine the combine passes carry P rows instead of R."""
     cfg = CONFIGS["C"]
