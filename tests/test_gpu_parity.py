@@ -119,6 +119,25 @@ def test_parity_edge_shapes(transport):
     gpu = run_cycle(torch, mep, cfg, inp, T_max=16, transport=transport)
     assert gpu["cnt"].sum() == 0 and gpu["G"].tolist() == [0] * (cfg.N + 1)
     assert gpu["expert_offsets"].tolist() == [0] * (cfg.E + 1)
+    # an empty cycle after a full one on the same group: the offsets are
+    # formed again (all zero), not left from the full cycle
+    for layout in (mep.MOE_LAYOUT_PACKED, mep.MOE_LAYOUT_FIXED_SLOT):
+        g = mep.moe_group_create(cfg.N, cfg.E, cfg.K, cfg.H, cfg.T, mep.MOE_BF16, transport, 0,
+                                 layout)
+        try:
+            full = make_inputs(cfg)
+            if layout == mep.MOE_LAYOUT_PACKED:
+                _compare_all(cfg, full, run_cycle(torch, mep, cfg, full, group=g,
+                                                  transport=transport))
+            else:
+                run_cycle(torch, mep, cfg, full, group=g, transport=transport, layout=layout,
+                          want_rows=False)
+            gpu = run_cycle(torch, mep, cfg, inp, group=g, transport=transport, layout=layout)
+            assert gpu["cnt"].sum() == 0 and gpu["G"].tolist() == [0] * (cfg.N + 1)
+            assert gpu["expert_offsets"].tolist() == [0] * (cfg.E + 1)
+            assert gpu["eoff"].tolist() == [0] * (cfg.E + 1)
+        finally:
+            mep.moe_group_destroy(g)
 
 
 @pytest.mark.parametrize("key", ["A", "B", "C", "E", "Ep"])
