@@ -288,39 +288,62 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* wg_er
     }
 }
 
-// The same tables (receiver-side combine) from a copy of soff[N][E+1] in LDS,
-// for small tables: the copy is one round of 16-byte loads (up to TAB_VECS per
-// thread), and the column walks then read LDS only, where each walk above
-// issues its BATCH loads per column (64 for a receiver column, past the 63 a
-// wave can have in flight).  Mixtral decode (72 ints): the last workgroup's
-// part 4.1 -> 2.0 us; DeepSeek-R1 decode (8224 ints) measured 3.8 us either
-// way, the copy's round trip taking what the walks saved.
+// The same tables from a copy of soff[N][E+1] (with the partial combine also
+// cnt[N][E] and psoff[N][N+1]) in LDS, for small tables: each copy is one
+// round of 16-byte loads (up to TAB_VECS per thread), and the column walks
+// then read LDS only, where each walk above issues its BATCH loads per column
+// (64 for a receiver column, past the 63 a wave can have in flight).
+// Mixtral decode (72 ints): the last workgroup's part 4.1 -> 2.0 us;
+// DeepSeek-R1 decode (8224 ints) measured 3.8 us either way, the copy's round
+// trip taking what the walks saved.
 constexpr int TAB_VECS = 2;
 constexpr int TAB_MAX_INTS = TAB_VECS * 4 * RP_NT;    // 16 KiB
+
+// One round of 16-byte loads copying n ints (a 16-byte aligned table) into
+// LDS at dst (16-byte aligned); n <= TAB_MAX_INTS.
+__device__ inline void copy_table(const int32_t* __restrict__ src, int n, int32_t* dst)
+{
+    const int tid = threadIdx.x, nv = n / 4;
+    const int4* __restrict__ src4 = reinterpret_cast<const int4*>(src);
+    if (nv > 0) {
+        int4 v[TAB_VECS];
+#pragma unroll
+        for (int j = 0; j < TAB_VECS; ++j)
+            v[j] = src4[min(tid + j * RP_NT, nv - 1)];
+#pragma unroll
+        for (int j = 0; j < TAB_VECS; ++j)
+            if (tid + j * RP_NT < nv)
+                reinterpret_cast<int4*>(dst)[tid + j * RP_NT] = v[j];
+    }
+    for (int i = nv * 4 + tid; i < n; i += RP_NT)
+        dst[i] = src[i];
+}
+
+__host__ __device__ inline int round4(int n)
+{
+    return (n + 3) & ~3;
+}
 
 __device__ void group_offsets_lds(const RouteArgs& ra, const Plan& p, int32_t* wg_err,
                                   int32_t* tab)
 {
     const int N = ra.N, E = ra.E, L = ra.L, W = E + 1;
-    const int n = N * W, nv = n / 4;
-    const int4* __restrict__ src = reinterpret_cast<const int4*>(p.soff);
     const int tid = threadIdx.x;
-    if (nv > 0) {
-        int4 v[TAB_VECS];
-#pragma unroll
-        for (int j = 0; j < TAB_VECS; ++j)
-            v[j] = src[min(tid + j * RP_NT, nv - 1)];
-#pragma unroll
-        for (int j = 0; j < TAB_VECS; ++j)
-            if (tid + j * RP_NT < nv)
-                reinterpret_cast<int4*>(tab)[tid + j * RP_NT] = v[j];
+    // the send offsets; with the partial combine also the counts and the
+    // partial rows' send offsets
+    int32_t* tab_cnt = tab + round4(N * W);
+    int32_t* tab_ps = tab_cnt + round4(N * E);
+    copy_table(p.soff, N * W, tab);
+    if (ra.partial) {
+        copy_table(p.cnt, N * E, tab_cnt);
+        copy_table(p.psoff, N * (N + 1), tab_ps);
     }
-    for (int i = nv * 4 + tid; i < n; i += RP_NT)
-        tab[i] = p.soff[i];
     __syncthreads();
     // expert columns and the totals column soff[*][E], a thread each, with 8
-    // LDS reads in flight
-    for (int col = tid; col <= E; col += RP_NT) {
+    // LDS reads in flight; with the partial combine each expert column also
+    // runs down its counts for each sender's first expert row (ebase), and
+    // the totals are the last column's running sum
+    for (int col = tid; col <= E - (ra.partial ? 1 : 0); col += RP_NT) {
         int sum = 0, s = 0;
         for (; s + 8 <= N; s += 8) {
             int v[8];
@@ -336,6 +359,41 @@ __device__ void group_offsets_lds(const RouteArgs& ra, const Plan& p, int32_t* w
         p.eoff[col] = sum;
         if (col == E)
             p.rbase[N] = sum;
+        if (ra.partial) {
+            int run = sum;
+            for (int s2 = 0; s2 < N; ++s2) {
+                p.ebase[(size_t)s2 * E + col] = run;
+                run += tab_cnt[s2 * E + col];
+            }
+            if (col == E - 1) {
+                p.eoff[E] = run;
+                p.rbase[N] = run;
+            }
+        }
+    }
+    // the partial rows' columns, a thread each: qoff and qbase down the rank
+    // columns of psoff, and down the last one also pbase (the senders' totals)
+    if (ra.partial) {
+        for (int d = (tid + RP_NT - E % RP_NT) % RP_NT; d < N; d += RP_NT) {
+            int32_t* qo = p.qoff + (size_t)d * (N + 1);
+            const bool last = d == N - 1;
+            int base = 0, run = 0, hrun = 0;
+            for (int s2 = 0; s2 < N; ++s2) {
+                const int lo = tab_ps[s2 * (N + 1) + d], hi = tab_ps[s2 * (N + 1) + d + 1];
+                qo[s2] = run;
+                if (last)
+                    p.pbase[s2] = hrun;
+                run += hi - lo;
+                hrun += hi;
+                base += lo;
+            }
+            qo[N] = run;
+            if (last)
+                p.pbase[N] = hrun;
+            p.qbase[d] = base;
+            if (last)
+                p.qbase[N] = base + run;
+        }
     }
     // receiver columns, a thread each, numbered from the top of the block so
     // that their waves are not the expert columns' when both fit
@@ -2348,12 +2406,19 @@ inline unsigned row_blocks(int64_t rows, int split)
 // walks also need the counts and the partial offsets).
 inline size_t table_lds_bytes(const Shape& sh)
 {
-    return (size_t)sh.N * (sh.E + 1) * sizeof(int32_t);
+    int64_t n = round4(sh.N * (sh.E + 1));
+    if (sh.partial)
+        n += round4(sh.N * sh.E) + (int64_t)sh.N * (sh.N + 1);
+    return (size_t)n * sizeof(int32_t);
 }
 
 inline int table_in_lds(const Shape& sh)
 {
-    return !sh.partial && (int64_t)sh.N * (sh.E + 1) <= TAB_MAX_INTS;
+    const int64_t per = std::max<int64_t>((int64_t)sh.N * (sh.E + 1),
+                                          sh.partial ? std::max<int64_t>((int64_t)sh.N * sh.E,
+                                                                         (int64_t)sh.N * (sh.N + 1))
+                                                     : 0);
+    return per <= TAB_MAX_INTS && table_lds_bytes(sh) <= 48 * 1024;
 }
 
 
