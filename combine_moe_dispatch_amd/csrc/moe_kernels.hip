@@ -2538,6 +2538,16 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
                                     (const v4u*)x, idx, item, dx,
                                     sh.direct ? r.recv_scale : r.send_scale, dmeta, w, dst_w,
                                     sender_run(sh, rsh), rb);
+        } else if (sh.payload_vecs == 7 * 2 * WAVE) {
+            // hidden 7168: seven waves of exactly 2 vectors per lane instead of
+            // eight with an eighth of the lanes idle in the second round.
+            // DeepSeek-R1 decode pack, warm / MALL-flushed: direct 84-92 ->
+            // 79-86 / 111 -> 106 us, staged 75-78 -> 74-75 / 99 -> 99 us;
+            // the other movers lost 1-3 us with the same split
+            const RowShape rsh{2, 7};
+            const unsigned rb = row_blocks(sh.rows, rsh.split);
+            go((pack_rows_bf16_kernel<2, 7>), dim3(rb + tblocks), dim3(COPY_THREADS), 0, L, sh, p,
+               (const v4u*)x, idx, item, dx, dmeta, w, dst_w, sender_run(sh, rsh), rb);
         } else {
             const RowShape rsh = row_shape(sh.payload_vecs);
             const unsigned rb = row_blocks(sh.rows, rsh.split);
