@@ -2543,7 +2543,8 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
             // eight with an eighth of the lanes idle in the second round.
             // DeepSeek-R1 decode pack, warm / MALL-flushed: direct 84-92 ->
             // 79-86 / 111 -> 106 us, staged 75-78 -> 74-75 / 99 -> 99 us;
-            // the other movers lost 1-3 us with the same split
+            // the other movers lost 1-3 us with the same split, the combine
+            // and partial reduces 1-2 us
             const RowShape rsh{2, 7};
             const unsigned rb = row_blocks(sh.rows, rsh.split);
             go((pack_rows_bf16_kernel<2, 7>), dim3(rb + tblocks), dim3(COPY_THREADS), 0, L, sh, p,
