@@ -53,6 +53,22 @@ def partial_rows(cfg, idx) -> int:
 # A sender's tokens up to this size make the pack run in send-row order (the
 # library's rule).
 PACK_ROWS_MAX_SENDER_BYTES = 2 << 20
+# With the partial combine and the send-row-order pack, the pack's record
+# blocks form their sender's bases from sums over the senders up to this many
+# terms per block, (E + 2N + 2) * N (the library's rule); past it the route
+# plan forms the group tables.
+RECORD_SUMS_MAX = 1 << 16
+
+
+def plan_forms_offsets(cfg, combine: str = "receiver", layout: str = "packed") -> bool:
+    """Whether the route plan's last workgroup forms the group offsets (the
+    library's rule): for the token-order pack unless its rows go to fixed
+    slots with the receiver-side combine, and for the partial combine's
+    records in the send-row-order pack past RECORD_SUMS_MAX."""
+    partial = combine == "partial"
+    if cfg.T * cfg.H * 2 > PACK_ROWS_MAX_SENDER_BYTES:
+        return partial or layout != "fixed"
+    return partial and (cfg.E + 2 * cfg.N + 2) * cfg.N > RECORD_SUMS_MAX
 
 
 def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: int = 0,
@@ -68,8 +84,8 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
     fixed slots): tables and maps are its whole job, so they are counted
     there.  The route plan's last workgroup forms the group offsets too (the
     same tables in and out) only where a kernel before dispatch_recv needs
-    them: the packed layout's token-order pack and the partial combine (the
-    map kernel then reads them instead, counted alike).
+    them (plan_forms_offsets; the map kernel then reads them instead,
+    counted alike).
     When the pack runs in send-row order (a sender's tokens within 2 MiB) the
     route plan writes each send row's item and the pack reads it in place of
     the positions (staged: the send meta words, which the pack no longer
@@ -96,7 +112,8 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
         "combine_reduce": R * hy + R * 8 + tokens * H * 2,
         "recv_map": offs + R * (20 + (4 if layout == "fixed" else 0)),
     }
-    if combine == "partial" or (layout == "packed" and not row_order):
+    tail = plan_forms_offsets(cfg, combine, layout)
+    if tail:
         kb["route_plan"] += offs
     if row_order:
         kb["route_plan"] += R * 4
@@ -108,10 +125,19 @@ def kernel_bytes(cfg, transport: str = "staged", combine: str = "receiver", P: i
             del kb[k]
         kb["combine_push"] = 2 * R * hy
     if combine == "partial":
-        # second route-plan pass: rank and position of every item, each
-        # sender's first expert rows and the partial rows' offsets; weights
-        # (4 bytes a row) through pack and transfer
-        kb["route_plan"] += 2 * R * 4 + N * E * 4 + 3 * N * (N + 1) * 4 + 2 * (N + 1) * 4
+        # second route-plan pass: rank and position of every item and the
+        # partial rows' send offsets (both orientations); where it forms the
+        # group tables, also the partial rows' owner offsets and bases and
+        # each sender's base row (E + 2N + 2 ints: its first expert rows,
+        # first receive and owner-layout partial rows on each rank, first
+        # token-layout partial row, P), else the map kernel forms the bases
+        # (owner and token layout) from the send offsets; weights (4 bytes a
+        # row) through pack and transfer
+        kb["route_plan"] += 2 * R * 4 + 2 * N * (N + 1) * 4
+        if tail:
+            kb["route_plan"] += N * (E + 2 * N + 2) * 4 + 2 * N * (N + 1) * 4 + 2 * (N + 1) * 4
+        else:
+            kb["recv_map"] += N * (N + 1) * 4 + 2 * (N + 1) * 4
         kb["pack"] += 2 * R * 4
         if "transfer" in kb:
             kb["transfer"] += 2 * R * 4

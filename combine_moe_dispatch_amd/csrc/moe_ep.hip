@@ -260,7 +260,7 @@ int place_buffers(moe_group_s* g, Placer& take)
         (rc = take(&p.pos, (size_t)N * T * K)) || (rc = take(&p.soff, (size_t)N * (E + 1))) ||
         (rc = take(&p.soff_col, (size_t)N * (E + 1))) ||
         (rc = take(&p.roff, (size_t)N * (N + 1))) || (rc = take(&p.rbase, (size_t)N + 1)) ||
-        (rc = take(&p.eoff, (size_t)E + 1)) || (rc = take(&p.ebase, (size_t)N * E)) ||
+        (rc = take(&p.eoff, (size_t)E + 1)) ||
         (rc = take(&p.xfer_src, R)) || (rc = take(&p.xfer_dst, R)) ||
         (rc = take(&p.shuf_map, R)) || (rc = take(&p.shuf_inv, R)) ||
         (staged && (rc = take(&pool_send, R * row_bytes))) ||
@@ -273,6 +273,8 @@ int place_buffers(moe_group_s* g, Placer& take)
         (!staged && (rc = take(&p.send_item, R))) ||
         (partial && ((rc = take(&p.pdst, R)) || (rc = take(&p.ppos, R)) ||
                      (rc = take(&p.psoff, (size_t)N * (N + 1))) ||
+                     (rc = take(&p.psoff_col, (size_t)N * (N + 1))) ||
+                     (rc = take(&p.sbase, (size_t)N * (E + 2 * N + 2))) ||
                      (rc = take(&p.qoff, (size_t)N * (N + 1))) ||
                      (rc = take(&p.qbase, (size_t)N + 1)) ||
                      (rc = take(&p.pbase, (size_t)N + 1)) ||
@@ -365,12 +367,13 @@ int poison_dispatch_send(const moe_group_s* g, hipStream_t st)
         (rc = poison(st, p.cnt, N * E * 4)) || (rc = poison(st, p.pos, R * 4)) ||
         (rc = poison(st, p.soff, N * (E + 1) * 4)) || (rc = poison(st, p.soff_col, N * (E + 1) * 4)) || (rc = poison(st, p.roff, N * (N + 1) * 4)) ||
         (rc = poison(st, p.rbase, (N + 1) * 4)) || (rc = poison(st, p.eoff, (E + 1) * 4)) ||
-        (rc = poison(st, p.ebase, N * E * 4)) || (rc = poison(st, p.xfer_src, R * 4)) ||
+        (rc = poison(st, p.sbase, N * (E + 2 * N + 2) * 4)) || (rc = poison(st, p.xfer_src, R * 4)) ||
         (rc = poison(st, p.xfer_dst, R * 8)) || (rc = poison(st, p.shuf_map, R * 8)) ||
         (rc = poison(st, p.shuf_inv, R * 4)) || (rc = poison(st, p.slot_of, R * 4)) ||
         (rc = poison(st, p.send_slot, R * 4)) || (rc = poison(st, p.send_item, R * 4)) ||
         (rc = poison(st, p.pdst, R * 4)) || (rc = poison(st, p.ppos, R * 4)) ||
-        (rc = poison(st, p.psoff, N * (N + 1) * 4)) || (rc = poison(st, p.qoff, N * (N + 1) * 4)) ||
+        (rc = poison(st, p.psoff, N * (N + 1) * 4)) || (rc = poison(st, p.psoff_col, N * (N + 1) * 4)) ||
+        (rc = poison(st, p.qoff, N * (N + 1) * 4)) ||
         (rc = poison(st, p.qbase, (N + 1) * 4)) || (rc = poison(st, p.pbase, (N + 1) * 4)) ||
         (rc = poison(st, p.pmap, R * 4)) || (rc = poison(st, p.phead, 2 * R * 16)) ||
         (rc = poison(st, p.pitem, R * 8)))

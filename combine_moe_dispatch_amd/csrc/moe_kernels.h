@@ -51,19 +51,43 @@ inline bool pack_in_row_order(const Shape& sh)
     return (int64_t)sh.T * sh.H * 2 <= PACK_ROWS_MAX_SENDER_BYTES;
 }
 
+// With the partial combine and the send-row-order pack, each block of the
+// pack's token records forms its sender's bases itself: E + 2N + 2 sums of N
+// terms over the senders' send offsets (the first expert row of each of its
+// experts, the first receive row and the first owner-layout partial row on
+// each rank, its first token-layout partial row and the total).  Up to this
+// many terms per block; past it the route plan's last workgroup forms the
+// group tables once and the blocks read them.  Partial combine, route plan
+// with the tables -> without, warm: Mixtral decode 11.8 -> 6.6 us, DeepSeek-R1
+// decode 19.7 -> 11.0, Kimi-K2 decode 26.6 -> 11.4; staged step, warm /
+// MALL-flushed: Mixtral 62.6 -> 57.0 / 67.2 -> 62.1 (direct 48.3 -> 43.7 /
+// 52.0 -> 46.0), DeepSeek-R1 754 -> 752 / 779 -> 772, Kimi-K2 1359 -> 1364 /
+// 1407 -> 1394 (the direct pack forms each row's receive base from the send
+// offsets and takes back 5-8 us of the plan's gain there).
+constexpr int64_t RECORD_SUMS_MAX = 1 << 16;
+
+inline bool record_sums(const Shape& sh)
+{
+    return (int64_t)(sh.E + 2 * sh.N + 2) * sh.N <= RECORD_SUMS_MAX;
+}
+
 // Whether the route plan forms the group offsets in its last workgroup: for
 // the kernels that need them before dispatch_recv -- the packed layout's
-// token-order pack (its rows' receive rows) and the partial combine (its
-// records).  Otherwise (the send-row-order pack, which derives its receive
-// rows or transfer map from the send offsets, and fixed slots with the
-// receiver-side combine) the route plan ends when its ranks do, and the
-// receiver's map kernel forms them from the exchanged counts.  Route plan,
-// warm: Mixtral decode 7.3 -> 5.1 us (staged) and 8.7 -> 6.6 (direct);
-// DeepSeek-R1 decode 11.2 -> 6.3 and 11.6 -> 6.1; Kimi-K2 decode 15.2 -> 6.6
-// and 15.3 -> 6.8, the pack and the receive map taking back 0.5-7 us of it.
+// token-order pack (its rows' receive rows), the partial combine's records
+// in the token-order pack, and those of the send-row-order pack past
+// RECORD_SUMS_MAX.  Otherwise (the send-row-order pack, which derives its
+// receive rows or transfer map, and its records, from the send offsets, and
+// fixed slots with the receiver-side combine) the route plan ends when its
+// ranks do, and the receiver's map kernel forms them from the exchanged
+// counts.  Route plan, warm: Mixtral decode 7.3 -> 5.1 us (staged) and
+// 8.7 -> 6.6 (direct); DeepSeek-R1 decode 11.2 -> 6.3 and 11.6 -> 6.1;
+// Kimi-K2 decode 15.2 -> 6.6 and 15.3 -> 6.8, the pack and the receive map
+// taking back 0.5-7 us of it.
 inline bool plan_offsets_needed(const Shape& sh)
 {
-    return sh.partial || (!sh.fixed && !pack_in_row_order(sh));
+    if (!pack_in_row_order(sh))
+        return sh.partial || !sh.fixed;
+    return sh.partial && !record_sums(sh);
 }
 
 struct Plan {              // device pointers owned by the group
@@ -85,7 +109,6 @@ struct Plan {              // device pointers owned by the group
     int32_t* roff;         // [N][N+1]
     int32_t* rbase;        // [N+1]
     int32_t* eoff;         // [E+1]
-    int32_t* ebase;        // [N][E]  first expert-order row of (sender s, expert e)
     // Receive rows are numbered in the packed order q (rank, source, expert,
     // t, k); with the fixed-slot layout a row's place in the receive planes
     // is slot_of[q], otherwise q itself.  The sender's pack writes the maps its
@@ -103,6 +126,12 @@ struct Plan {              // device pointers owned by the group
     int32_t* ppos;         // [N][T][K]  first k of its rank in the token: row among sender
                            //            s's partial rows (rank-major, then t); else -1
     int32_t* psoff;        // [N][N+1]   first partial row of (sender s, rank d) among s's
+    int32_t* psoff_col;    // [N+1][N]   psoff transposed, for sums over the senders
+    int32_t* sbase;        // [N][E+2N+2] each sender's bases, formed by the route plan's
+                           //            last workgroup (Shape::plan_offsets): its first
+                           //            expert row of each expert, first receive row and
+                           //            first owner-layout partial row on each rank, first
+                           //            token-layout partial row, and P
     int32_t* qoff;         // [N][N+1]   first owner-layout row of sender s among rank d's
     int32_t* qbase;        // [N+1]      first owner-layout row of rank d (qbase[N] = P)
     int32_t* pbase;        // [N+1]      first token-layout row of sender s (pbase[N] = P)

@@ -196,7 +196,7 @@ __device__ int2 walk_column(const int32_t* __restrict__ lo, const int32_t* __res
 // soff[s][*] over the senders s, because soff[s][e] already sums sender s's
 // counts of the experts before e:
 //   eoff[e]      = sum_s soff[s][e]                 (rows of all experts < e)
-//   ebase[s][e]  = eoff[e] + sum_{s'<s} cnt[s'][e]   (partial combine only)
+//   sbase[s][e]  = eoff[e] + sum_{s'<s} cnt[s'][e]   (partial combine only)
 //   rbase[d]     = sum_s soff[s][d*L]               (rows received by ranks < d)
 //   roff[d][s]   = sum_{s'<s} (soff[s'][(d+1)L] - soff[s'][dL])
 // and the partial-row tables are the same walks over psoff[s][*] (one bucket
@@ -210,12 +210,23 @@ __device__ int2 walk_column(const int32_t* __restrict__ lo, const int32_t* __res
 // second walk runs, the last expert column's running sum), and the last
 // partial column's upper bounds psoff[s][N] are the per-sender totals whose
 // running sum is pbase.
+// Column `col` of every sender's base row (partial combine): sbase[s][col] =
+// base + off[d][s], the first row from sender s on rank d (off, written by
+// this thread's walk, is read back).
+__device__ inline void sender_rows(const Plan& p, int d, int N, int SB, int col, int base,
+                                   const int32_t* off)
+{
+    for (int s = 0; s < N; ++s)
+        p.sbase[(size_t)s * SB + col] = base + off[(size_t)d * (N + 1) + s];
+}
+
 __device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* wg_err)
 {
     const int N = ra.N, E = ra.E, L = ra.L;
     const int32_t* __restrict__ soff = p.soff;
     const int32_t* __restrict__ cnt = p.cnt;
     const int cols = E + N + (ra.partial ? N : 0);
+    const int SB = E + 2 * N + 2;
     for (int col = threadIdx.x; col < cols; col += RP_NT) {
         if (col < E && !ra.partial) {
             // expert column e: its offset alone (the receiver's map kernel
@@ -261,7 +272,7 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* wg_er
 #pragma unroll
                 for (int b = 0; b < BATCH; ++b)
                     if (s0 + b < N) {
-                        p.ebase[(size_t)(s0 + b) * E + e] = run;
+                        p.sbase[(size_t)(s0 + b) * SB + e] = run;
                         run += c[b];
                     }
             }
@@ -276,14 +287,22 @@ __device__ void group_offsets(const RouteArgs& ra, const Plan& p, int32_t* wg_er
             p.rbase[d] = br.x;
             if ((int64_t)br.y > ra.cap)
                 atomicOr(wg_err, ERR_BIT_CAPACITY);
+            if (ra.partial)
+                sender_rows(p, d, N, SB, E + d, br.x, p.roff);
         } else {
             const int d = col - E - N;
             const bool last = d == N - 1;
             const int2 br = walk_column(p.psoff + d, p.psoff + d + 1, N + 1, N,
                                         p.qoff + (size_t)d * (N + 1), last ? p.pbase : nullptr);
             p.qbase[d] = br.x;
-            if (last)
+            sender_rows(p, d, N, SB, E + N + d, br.x, p.qoff);
+            if (last) {
                 p.qbase[N] = br.x + br.y;
+                for (int s = 0; s < N; ++s) {
+                    p.sbase[(size_t)s * SB + E + 2 * N] = p.pbase[s];
+                    p.sbase[(size_t)s * SB + E + 2 * N + 1] = br.x + br.y;
+                }
+            }
         }
     }
 }
@@ -327,7 +346,7 @@ __host__ __device__ inline int round4(int n)
 __device__ void group_offsets_lds(const RouteArgs& ra, const Plan& p, int32_t* wg_err,
                                   int32_t* tab)
 {
-    const int N = ra.N, E = ra.E, L = ra.L, W = E + 1;
+    const int N = ra.N, E = ra.E, L = ra.L, W = E + 1, SB = E + 2 * N + 2;
     const int tid = threadIdx.x;
     // the send offsets; with the partial combine also the counts and the
     // partial rows' send offsets
@@ -341,7 +360,7 @@ __device__ void group_offsets_lds(const RouteArgs& ra, const Plan& p, int32_t* w
     __syncthreads();
     // expert columns and the totals column soff[*][E], a thread each, with 8
     // LDS reads in flight; with the partial combine each expert column also
-    // runs down its counts for each sender's first expert row (ebase), and
+    // runs down its counts for each sender's first expert row (sbase), and
     // the totals are the last column's running sum
     for (int col = tid; col <= E - (ra.partial ? 1 : 0); col += RP_NT) {
         int sum = 0, s = 0;
@@ -362,7 +381,7 @@ __device__ void group_offsets_lds(const RouteArgs& ra, const Plan& p, int32_t* w
         if (ra.partial) {
             int run = sum;
             for (int s2 = 0; s2 < N; ++s2) {
-                p.ebase[(size_t)s2 * E + col] = run;
+                p.sbase[(size_t)s2 * SB + col] = run;
                 run += tab_cnt[s2 * E + col];
             }
             if (col == E - 1) {
@@ -391,8 +410,14 @@ __device__ void group_offsets_lds(const RouteArgs& ra, const Plan& p, int32_t* w
             if (last)
                 p.pbase[N] = hrun;
             p.qbase[d] = base;
-            if (last)
+            sender_rows(p, d, N, SB, E + N + d, base, p.qoff);
+            if (last) {
                 p.qbase[N] = base + run;
+                for (int s2 = 0; s2 < N; ++s2) {
+                    p.sbase[(size_t)s2 * SB + E + 2 * N] = p.pbase[s2];
+                    p.sbase[(size_t)s2 * SB + E + 2 * N + 1] = base + run;
+                }
+            }
         }
     }
     // receiver columns, a thread each, numbered from the top of the block so
@@ -426,6 +451,8 @@ __device__ void group_offsets_lds(const RouteArgs& ra, const Plan& p, int32_t* w
         p.rbase[d] = base;
         if ((int64_t)run > ra.cap)
             atomicOr(wg_err, ERR_BIT_CAPACITY);
+        if (ra.partial)
+            sender_rows(p, d, N, SB, E + d, base, p.roff);
     }
 }
 
@@ -739,7 +766,8 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
                             p.pos + (size_t)s * items, nullptr,
                             ra.send_meta ? ra.send_meta + (size_t)s * items : nullptr);
     } else {
-        publish_counts(cur + E, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums, -1, &wg_err);
+        publish_counts(cur + E, N, nullptr, p.psoff + (size_t)s * (N + 1), wave_sums, -1, &wg_err,
+                       p.psoff_col + s, N);
         stable_ranks<true, HC>(items, NK, CW, mask, cur, held_e,
                            [&](int i, bool mine) {
                                const int e = mine ? my_idx[i] : -1;
@@ -825,14 +853,16 @@ __device__ inline RowSlot row_slot(int n, int64_t block = blockIdx.x)
 // order.
 constexpr int XCDS = 8;
 
-__device__ inline int64_t xcd_run_block(uint32_t run, uint32_t nblocks = 0)
+// Block b of a part of the grid that starts at a multiple of 8 blocks and
+// has nblocks blocks (the whole grid by default).
+__device__ inline int64_t xcd_run_block(uint32_t run, uint32_t b = blockIdx.x,
+                                        uint32_t nblocks = gridDim.x)
 {
-    const uint32_t b = blockIdx.x;
     if (run <= 1)
         return b;
     const uint32_t tile = XCDS * run;            // the host keeps run below 2^28
     const uint32_t t0 = b / tile * tile;
-    if (t0 + tile > (nblocks ? nblocks : gridDim.x))   // blocks [0, nblocks) are remapped
+    if (t0 + tile > nblocks)
         return b;
     const uint32_t r = b - t0;
     return (int64_t)t0 + (r % XCDS) * run + r / XCDS;
@@ -848,7 +878,7 @@ __device__ inline int64_t xcd_run_block(uint32_t run, uint32_t nblocks = 0)
 // row (s, t, k) lanes k < K work out where it goes:
 //   send row       srow = s*T*K + pos
 //   receive row    q    = rbase[d] + roff[d][s] + pos - soff[s][d*L]   (d = e / L)
-//   expert row     r    = ebase[s][e] + pos - soff[s][e]
+//   expert row     r    = sbase[s][e] + pos - soff[s][e]   (partial combine)
 // and the lead wave records the row maps the movers follow.  With the staged
 // transport the rows go to the send buffer (row srow) and the transfer kernel
 // moves them; with the direct transport they are pushed straight into the
@@ -883,7 +913,7 @@ __device__ inline RowDest row_dest(const Shape& sh, const Plan& p, int s, int e,
     }
     if (sh.partial) {
         // the expert row, named by the partial combine's records
-        rd.r = p.ebase[(size_t)s * sh.E + e] + i;
+        rd.r = p.sbase[(size_t)s * (sh.E + 2 * sh.N + 2) + e] + i;
         ok = ok && (uint64_t)rd.r < (uint64_t)sh.rows;
     }
     const int64_t slot = ((int64_t)e * sh.slots + i) * sh.N + s;
@@ -916,23 +946,27 @@ __device__ inline bool sender_failed(const Shape& sh, const Plan& p, int s)
     return sh.sender_only ? p.err_rank[s] != 0 : *p.err != 0;
 }
 
-// Records of the expert-side partial combine, made by the lead wave of a
-// token (all lanes call it; lane k < K holds item k's expert rank d, or -1
-// if its indices failed, and its receive-plane and expert rows).  Each item
-// gets its (expert row, receive-plane row); each head item (the first of its
-// rank in the token) writes the record of the partial row it heads, in the
-// layout the expert side writes (owner layout when staged, token layout when
-// direct): the (expert row, receive-plane row) of its first two items, the
-// token, the item count and the mask of the token's items on its rank; and,
-// staged, the owner row of its token-layout row for the transfer back.
-__device__ inline void record_partial(const Shape& sh, const Plan& p, int64_t tok, int s, int d,
-                                      const RowDest& rd)
+// Records of the expert-side partial combine, made by waves holding the
+// items of whole tokens, K lanes a token (all lanes call it; a lane holding
+// an item has its index i = tok*K + k, else -1, the first lane of its token
+// `seg`, its expert rank d, or -1 if its indices failed, and its
+// receive-plane and expert rows).  Each item gets its (expert row,
+// receive-plane row); each head item (the first of its rank in the token)
+// writes the record of the partial row it heads, in the layout the expert
+// side writes (owner layout when staged, token layout when direct): the
+// (expert row, receive-plane row) of its first two items, the token, the
+// item count and the mask of the token's items on that rank (by k); and,
+// staged, the owner row of its token-layout row for the transfer back.  The
+// bases: P partial rows in all, pb the sender's first token-layout partial
+// row, and per lane ob, the owner-layout row of the sender's first partial
+// row on rank d less psoff[s][d], so that a head at ppos pp owns token-layout
+// row pb + pp and owner-layout row ob + pp.
+__device__ inline void write_partial_records(const Shape& sh, const Plan& p, int64_t i, int seg,
+                                             int d, const RowDest& rd, int P, int pb, int ob)
 {
     const int lane = lane_id();
-    const int N = sh.N;
     int pp = -1;
-    if (lane < sh.K && d >= 0) {
-        const int64_t i = tok * sh.K + lane;
+    if (i >= 0 && d >= 0) {
         p.pitem[i] = make_int2(rd.r, rd.qd);
         pp = p.ppos[i];
     }
@@ -940,37 +974,51 @@ __device__ inline void record_partial(const Shape& sh, const Plan& p, int64_t to
     int tr = 0, orow = 0;
     bool ok = false;
     if (pp >= 0) {
-        const int P = p.pbase[N];
-        tr = p.pbase[s] + pp;
-        orow = p.qbase[d] + p.qoff[(size_t)d * (N + 1) + s] + pp - p.psoff[(size_t)s * (N + 1) + d];
+        tr = pb + pp;
+        orow = ob + pp;
         ok = (unsigned)tr < (unsigned)P && (unsigned)orow < (unsigned)P;
         if (!ok)
             raise_err(p, ERR_BIT_INTERNAL);
     }
-    // then the masks and second items, head by head (no memory access)
+    // then each lane's mask of its token's items on its rank (bit k: item
+    // k), and the rows of the second of them, by shuffles within the token's
+    // lanes (no memory access)
     uint64_t my_mask = 0;
-    int my_r1 = 0, my_q1 = 0;
-    const uint64_t heads = __ballot(pp >= 0);
-    for (uint64_t hm = heads; hm != 0; hm &= hm - 1) {
-        const int f = __builtin_ctzll(hm);
-        const uint64_t mask = __ballot(d >= 0 && d == readlane(d, f));
-        const uint64_t rest = mask & (mask - 1);
-        const int f1 = rest ? __builtin_ctzll(rest) : f;
-        const int r1 = readlane(rd.r, f1), q1 = readlane(rd.qd, f1);
-        if (lane == f) {
-            my_mask = mask;
-            my_r1 = r1;
-            my_q1 = q1;
-        }
+    for (int j = 0; j < sh.K; ++j) {
+        const int dj = __shfl(d, min(seg + j, WAVE - 1), WAVE);
+        if (d >= 0 && dj == d)
+            my_mask |= 1ull << j;
     }
+    const uint64_t rest = my_mask & (my_mask - 1);
+    const int f1 = seg + (rest ? __builtin_ctzll(rest) : lane - seg);
+    const int my_r1 = __shfl(rd.r, min(f1, WAVE - 1), WAVE);
+    const int my_q1 = __shfl(rd.qd, min(f1, WAVE - 1), WAVE);
     if (ok) {
         int4* rec = p.phead + 2 * (int64_t)(sh.direct ? tr : orow);
         rec[0] = make_int4(rd.r, rd.qd, my_r1, my_q1);
-        rec[1] = make_int4((int)tok, __popcll(my_mask), (int)(uint32_t)my_mask,
+        rec[1] = make_int4((int)(i / sh.K), __popcll(my_mask), (int)(uint32_t)my_mask,
                            (int)(uint32_t)(my_mask >> 32));
         if (!sh.direct)
             p.pmap[tr] = orow;
     }
+}
+
+// One token per wave (lanes k < K), the bases read from the sender's base
+// row that the route plan formed: pb = sbase[s][E+2N], P = sbase[s][E+2N+1],
+// ob = sbase[s][E+N+d] - psoff[s][d].
+__device__ inline void record_partial(const Shape& sh, const Plan& p, int64_t tok, int s, int d,
+                                      const RowDest& rd)
+{
+    const int N = sh.N, E = sh.E;
+    int P = 0, pb = 0, ob = 0;
+    const bool mine = lane_id() < sh.K;
+    if (mine && d >= 0) {
+        const int32_t* sb = p.sbase + (size_t)s * (E + 2 * N + 2);
+        P = sb[E + 2 * N + 1];
+        pb = sb[E + 2 * N];
+        ob = sb[E + N + d] - p.psoff[(size_t)s * (N + 1) + d];
+    }
+    write_partial_records(sh, p, mine ? tok * sh.K + lane_id() : -1, 0, d, rd, P, pb, ob);
 }
 
 // Lanes k < K: the destination row of (token, k) in the buffer pack writes
@@ -1322,30 +1370,6 @@ __device__ inline int64_t direct_row(const Shape& sh, const Plan& p, int s, int 
     return (uint64_t)q < (uint64_t)sh.rows ? q : -1;
 }
 
-// The partial combine's records of token tok (sender s), for the send-row
-// order pack, whose row waves see one item each: lanes k < K find their
-// item's expert and receive-plane rows and the head items write the records
-// (record_partial).  Every lane of the wave must call it.
-__device__ inline void token_records(const Shape& sh, const Plan& p,
-                                     const int32_t* __restrict__ idx, int64_t tok, int s)
-{
-    const int lane = lane_id();
-    int d = -1;
-    RowDest rd{};
-    if (lane < sh.K) {
-        const int64_t i = tok * sh.K + lane;
-        const int e = idx[i];
-        if ((unsigned)e < (unsigned)sh.E) {
-            rd = row_dest(sh, p, s, e, p.pos[i]);
-            if (rd.ok)
-                d = e / sh.L;
-        }
-        if (d < 0)
-            raise_err(p, ERR_BIT_INTERNAL);
-    }
-    record_partial(sh, p, tok, s, d, rd);
-}
-
 // The map the staged transfer follows for send row (s, pk) holding item m,
 // from the senders' offsets alone: the row's packed receive row q (xfer_src[q]
 // = the send row), or with fixed slots its slot (send_slot).  Every lane of
@@ -1384,18 +1408,162 @@ __device__ inline void record_send_row(const Shape& sh, const Plan& p,
     }
 }
 
-// Blocks past the row blocks: one wave per token, for the partial combine's
-// records.
-__device__ inline void pack_token_block(const Shape& sh, const Plan& p,
-                                        const int32_t* __restrict__ idx, uint32_t data_blocks)
+// The partial combine's records in the send-row-order pack, whose row waves
+// see one item each: blocks of one sender s each, ahead of the row blocks, a
+// wave taking 64/K tokens at a time (K lanes a token) and up to REC_PASSES
+// such passes.  A block first puts its sender's bases in LDS (ints:
+// so[E+1], ps[N+1], eb[E], qb[N], ob[N], pb, P):
+//   so[e] = soff[s][e],  ps[d] = psoff[s][d]
+//   eb[e] = first expert row of (s, e) = sum_{j<s} soff[j][e+1] + sum_{j>=s} soff[j][e]
+//   qb[d] = first receive row from s on rank d
+//         = sum_{j<s} soff[j][(d+1)L] + sum_{j>=s} soff[j][dL]
+//   ob[d] = first owner-layout partial row from s on rank d
+//         = sum_{j<s} psoff[j][d+1] + sum_{j>=s} psoff[j][d]
+//   pb    = first token-layout partial row of s = sum_{j<s} psoff[j][N]
+//   P     = partial rows in all = sum_j psoff[j][N]
+// (a thread per sum, walking the senders' rows, so that the threads of a
+// wave read neighbouring entries; with Shape::plan_offsets they are read
+// from the route plan's group tables instead), then each item's lane places
+// it from them:
+//   expert row        r  = eb[e] + pos - so[e]
+//   receive-plane row qd = qb[d] + pos - so[dL], or the slot (e*T_max + pos - so[e])*N + s
+// and the head items write the records (write_partial_records).  Measured on
+// the decode shapes against records one token per wave (many blocks, each
+// summing its sender's bases): those sums cost the pack 4-27 us, and its
+// scalar registers (106, occupancy 7 waves per SIMD for every row block)
+// another 4-10; one block per sender, a wave's tokens' masks by shuffles
+// and 32-bit table indices (94 registers, occupancy 8) brought the staged
+// pack back to its time with the route plan's tables.  One, two or four
+// passes per wave measured the same.
+constexpr int REC_PASSES = 4;
+
+__host__ __device__ inline int rec_lds_ints(const Shape& sh)
 {
-    const int64_t tok = (int64_t)(blockIdx.x - data_blocks) * ROWS_PER_BLOCK + threadIdx.x / WAVE;
-    if (tok >= (int64_t)sh.N * sh.T)
+    return 2 * sh.E + 3 * sh.N + 4;
+}
+
+__host__ __device__ inline int rec_tokens_per_block(const Shape& sh)
+{
+    return ROWS_PER_BLOCK * (WAVE / sh.K) * REC_PASSES;
+}
+
+// sum_{j<s} row_j[hi] + sum_{j>=s} row_j[lo] over the rows j < n of a table
+// with row stride W: 8 loads issued together per round (clamped rows, the
+// ones past n not added).  32-bit indices (the tables hold fewer than 2^21
+// entries).
+__device__ inline int split_sum(const int32_t* __restrict__ t, int W, int lo, int hi, int n, int s)
+{
+    int sum = 0;
+    for (int j = 0; j < n; j += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = min(j + u, n - 1);
+            v[u] = t[r * W + (r < s ? hi : lo)];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j + u < n)
+                sum += v[u];
+    }
+    return sum;
+}
+
+__device__ inline void sender_bases(const Shape& sh, const Plan& p, int s, int32_t* tab)
+{
+    const int E = sh.E, N = sh.N, L = sh.L, tid = threadIdx.x;
+    int32_t* so = tab;
+    int32_t* ps = so + E + 1;
+    int32_t* eb = ps + N + 1;
+    for (int j = tid; j <= E; j += COPY_THREADS)
+        so[j] = p.soff[(size_t)s * (E + 1) + j];
+    for (int j = tid; j <= N; j += COPY_THREADS)
+        ps[j] = p.psoff[(size_t)s * (N + 1) + j];
+    const int nv = E + 2 * N + 2;
+    for (int v = tid; v < nv; v += COPY_THREADS) {
+        int val;
+        if (sh.plan_offsets) {
+            val = p.sbase[(size_t)s * nv + v];
+        } else if (v < E) {
+            val = split_sum(p.soff, E + 1, v, v + 1, N, s);
+        } else if (v < E + N) {
+            const int d = v - E;
+            val = sh.fixed ? 0 : split_sum(p.soff, E + 1, d * L, (d + 1) * L, N, s);
+        } else if (v < E + 2 * N) {
+            const int d = v - E - N;
+            val = split_sum(p.psoff, N + 1, d, d + 1, N, s);
+        } else if (v == E + 2 * N) {
+            val = split_sum(p.psoff, N + 1, N, N, s, s);
+        } else {
+            val = split_sum(p.psoff, N + 1, N, N, N, 0);
+        }
+        eb[v] = val;
+    }
+    __syncthreads();
+}
+
+// One pass of a wave over up to 64/K tokens [t0, t_end) of sender s, K lanes
+// a token, from the sender's bases (every lane of the wave calls it).
+__device__ inline void token_records(const Shape& sh, const Plan& p,
+                                     const int32_t* __restrict__ idx, int s, int t0, int t_end,
+                                     const int32_t* tab)
+{
+    const int lane = lane_id();
+    const int E = sh.E, N = sh.N, K = sh.K;
+    const int32_t* so = tab;
+    const int32_t* ps = so + E + 1;
+    const int32_t* eb = ps + N + 1;
+    const int32_t* qb = eb + E;
+    const int32_t* ob = qb + N;
+    const int tl = lane / K, t = t0 + tl;
+    const bool mine = tl < WAVE / K && t < t_end;
+    const int64_t i = mine ? ((int64_t)s * sh.T + t) * K + lane % K : -1;
+    int d = -1, obase = 0;
+    RowDest rd{};
+    if (mine) {
+        const int e = idx[i];
+        const int pk = p.pos[i];
+        if ((unsigned)e < (unsigned)E && (int64_t)(unsigned)pk < (int64_t)sh.T * K) {
+            const int dd = e / sh.L;
+            const int ii = pk - so[e];
+            const int64_t r = (int64_t)eb[e] + ii;
+            int64_t qd;
+            bool ok = (uint64_t)r < (uint64_t)sh.rows;
+            if (sh.fixed) {
+                qd = ((int64_t)e * sh.slots + ii) * N + s;
+                ok = ok && (unsigned)ii < (unsigned)sh.slots && (uint64_t)qd < (uint64_t)sh.recv_rows;
+            } else {
+                qd = (int64_t)qb[dd] + pk - so[dd * sh.L];
+                ok = ok && (uint64_t)qd < (uint64_t)sh.rows;
+            }
+            if (ok) {
+                d = dd;
+                rd.r = (int32_t)r;
+                rd.qd = (int32_t)qd;
+                obase = ob[dd] - ps[dd];
+            }
+        }
+        if (d < 0)
+            raise_err(p, ERR_BIT_INTERNAL);
+    }
+    write_partial_records(sh, p, i, tl * K, d, rd, ob[N + 1], ob[N], obase);
+}
+
+__device__ inline void pack_record_block(const Shape& sh, const Plan& p,
+                                         const int32_t* __restrict__ idx, int32_t* tab)
+{
+    const int per_block = rec_tokens_per_block(sh);
+    const int bps = (sh.T + per_block - 1) / per_block;
+    const int s = (int)(blockIdx.x / bps);
+    if (s >= sh.N || sender_failed(sh, p, s))     // the same for the whole block
         return;
-    const int s = (int)(tok / sh.T);
-    if (sender_failed(sh, p, s))
-        return;
-    token_records(sh, p, idx, tok, s);
+    sender_bases(sh, p, s, tab);
+    const int per_pass = WAVE / sh.K;
+    const int b0 = (int)(blockIdx.x % bps) * per_block;
+    const int t_end = min(sh.T, b0 + per_block);
+    for (int t0 = b0 + (int)(threadIdx.x / WAVE) * per_pass; t0 < t_end;
+         t0 += ROWS_PER_BLOCK * per_pass)
+        token_records(sh, p, idx, s, t0, t_end, tab);
 }
 
 template <int U, int SPLIT>
@@ -1407,15 +1575,17 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, 
                                                                       int32_t* __restrict__ dst_meta,
                                                                       const float* __restrict__ w,
                                                                       float* __restrict__ dst_w,
-                                                                      uint32_t xrun, uint32_t data_blocks)
+                                                                      uint32_t xrun, uint32_t rec_blocks)
 {
     const int lane = lane_id();
     const int n = sh.payload_vecs;
-    if (blockIdx.x >= data_blocks) {
-        pack_token_block(sh, p, idx, data_blocks);
+    if (blockIdx.x < rec_blocks) {
+        extern __shared__ __align__(16) int32_t rec_tab[];
+        pack_record_block(sh, p, idx, rec_tab);
         return;
     }
-    const RowSlot rs = row_slot<SPLIT>(n, xcd_run_block(xrun, data_blocks));
+    const RowSlot rs = row_slot<SPLIT>(
+        n, xcd_run_block(xrun, blockIdx.x - rec_blocks, gridDim.x - rec_blocks));
     const int64_t TK = (int64_t)sh.T * sh.K;
     const int64_t srow = rs.row;
     if (srow >= sh.rows)
@@ -1468,15 +1638,17 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(Shape sh, P
                                                                      int32_t* __restrict__ dst_meta,
                                                                      const float* __restrict__ w,
                                                                      float* __restrict__ dst_w,
-                                                                     uint32_t xrun, uint32_t data_blocks)
+                                                                     uint32_t xrun, uint32_t rec_blocks)
 {
     const int lane = lane_id();
     const int n2 = sh.H / 16;
-    if (blockIdx.x >= data_blocks) {
-        pack_token_block(sh, p, idx, data_blocks);
+    if (blockIdx.x < rec_blocks) {
+        extern __shared__ __align__(16) int32_t rec_tab[];
+        pack_record_block(sh, p, idx, rec_tab);
         return;
     }
-    const RowSlot rs = row_slot<SPLIT, 8>(n2, xcd_run_block(xrun, data_blocks));
+    const RowSlot rs = row_slot<SPLIT, 8>(
+        n2, xcd_run_block(xrun, blockIdx.x - rec_blocks, gridDim.x - rec_blocks));
     const int64_t TK = (int64_t)sh.T * sh.K;
     const int64_t srow = rs.row;
     if (srow >= sh.rows)
@@ -1616,7 +1788,9 @@ __global__ __launch_bounds__(COPY_THREADS) void transfer_kernel(Shape sh, Plan p
 //   rbase[d] + roff[d][s] = sum_{j<s} soff[j][(d+1)L] + sum_{j>=s} soff[j][d*L]
 //   first expert row r0   = eoff[e] + sum_{j<s} cnt[j][e]
 // The pairs publish the tables they own (eoff by s = 0; roff and rbase by
-// the rank's first expert; the totals by the first pair); then lane i <
+// the rank's first expert; the totals by the first pair; with the partial
+// combine qbase[d] = sum_j psoff[j][d] by (dL, 0), pbase[s] = sum_{j<s}
+// psoff[j][N] by (0, s) and P by the first pair); then lane i <
 // cnt[s][e] takes the pair's i-th row:
 //   expert row        r    = r0 + i
 //   packed receive row q    = rbase[d] + roff[d][s] + soff[s][e] - soff[s][d*L] + i
@@ -1657,7 +1831,14 @@ __global__ __launch_bounds__(COPY_THREADS) void recv_map_kernel(Shape sh, Plan p
         const int32_t* col_lo = p.soff_col + (size_t)d * L * N;
         const int32_t* col_hi = p.soff_col + (size_t)(d + 1) * L * N;
         const int32_t* col_tot = p.soff_col + (size_t)sh.E * N;
-        int rb = 0, tot = 0;
+        // the partial combine's bases too: qbase[d] = sum_j psoff[j][d] (by
+        // the pair (dL, 0)), pbase[s] = sum_{j<s} psoff[j][N] (by (0, s)),
+        // and the total P
+        const bool part = sh.partial != 0;
+        const int32_t* pcol_d = part ? p.psoff_col + (size_t)d * N : nullptr;
+        const int32_t* pcol_tot = part ? p.psoff_col + (size_t)N * N : nullptr;
+        const bool own_qbase = part && s == 0 && e == d * L, own_pbase = part && e == 0;
+        int rb = 0, tot = 0, pq = 0, pbs = 0, ptot = 0;
         for (int j0 = 0; j0 < N; j0 += WAVE) {
             const int j = j0 + lane;
             if (j < N) {
@@ -1672,6 +1853,15 @@ __global__ __launch_bounds__(COPY_THREADS) void recv_map_kernel(Shape sh, Plan p
                 }
                 if (first_pair)
                     tot += col_tot[j];
+                if (own_qbase)
+                    pq += pcol_d[j];
+                if (own_pbase && (j < s || first_pair)) {
+                    const int pt = pcol_tot[j];
+                    if (j < s)
+                        pbs += pt;
+                    if (first_pair)
+                        ptot += pt;
+                }
             }
         }
         eo = wave_sum(eo);
@@ -1680,7 +1870,22 @@ __global__ __launch_bounds__(COPY_THREADS) void recv_map_kernel(Shape sh, Plan p
         before = wave_sum(before);
         if (first_pair)
             tot = wave_sum(tot);
+        if (own_qbase)
+            pq = wave_sum(pq);
+        if (own_pbase) {
+            pbs = wave_sum(pbs);
+            if (first_pair)
+                ptot = wave_sum(ptot);
+        }
         if (lane == 0) {
+            if (own_qbase)
+                p.qbase[d] = pq;
+            if (own_pbase)
+                p.pbase[s] = pbs;
+            if (part && first_pair) {
+                p.qbase[N] = ptot;
+                p.pbase[N] = ptot;
+            }
             if (s == 0)
                 p.eoff[e] = eo;
             if (e == d * L) {
@@ -2381,24 +2586,28 @@ inline unsigned row_blocks(int64_t rows, int split)
     MOE_DISPATCH_ROW_BLOCKS(rsh, KERNEL, row_blocks((GRID_ROWS), (rsh).split), __VA_ARGS__)
 
 #define MOE_DISPATCH_ROW_BLOCKS(rsh, KERNEL, GRID_BLOCKS, ...)                                     \
+    MOE_DISPATCH_ROW_BLOCKS_LDS(rsh, KERNEL, GRID_BLOCKS, 0, __VA_ARGS__)
+
+#define MOE_DISPATCH_ROW_BLOCKS_LDS(rsh, KERNEL, GRID_BLOCKS, LDS, ...)                            \
     do {                                                                                           \
         const dim3 grid_(GRID_BLOCKS), block_(COPY_THREADS);                                       \
+        const size_t lds_ = (LDS);                                                                 \
         if ((rsh).split == 1 && (rsh).u == 1)                                                      \
-            go((KERNEL<1, 1>), grid_, block_, 0, __VA_ARGS__);                                     \
+            go((KERNEL<1, 1>), grid_, block_, lds_, __VA_ARGS__);                                  \
         else if ((rsh).split == 1)                                                                 \
-            go((KERNEL<2, 1>), grid_, block_, 0, __VA_ARGS__);                                     \
+            go((KERNEL<2, 1>), grid_, block_, lds_, __VA_ARGS__);                                  \
         else if ((rsh).split == 2)                                                                 \
-            go((KERNEL<2, 2>), grid_, block_, 0, __VA_ARGS__);                                     \
+            go((KERNEL<2, 2>), grid_, block_, lds_, __VA_ARGS__);                                  \
         else if ((rsh).split == 4 && (rsh).u == 2)                                                 \
-            go((KERNEL<2, 4>), grid_, block_, 0, __VA_ARGS__);                                     \
+            go((KERNEL<2, 4>), grid_, block_, lds_, __VA_ARGS__);                                  \
         else if ((rsh).split == 4 && (rsh).u == 4)                                                 \
-            go((KERNEL<4, 4>), grid_, block_, 0, __VA_ARGS__);                                     \
+            go((KERNEL<4, 4>), grid_, block_, lds_, __VA_ARGS__);                                  \
         else if ((rsh).split == 4)                                                                 \
-            go((KERNEL<16, 4>), grid_, block_, 0, __VA_ARGS__);                                    \
+            go((KERNEL<16, 4>), grid_, block_, lds_, __VA_ARGS__);                                 \
         else if ((rsh).u == 2)                                                                     \
-            go((KERNEL<2, 8>), grid_, block_, 0, __VA_ARGS__);                                     \
+            go((KERNEL<2, 8>), grid_, block_, lds_, __VA_ARGS__);                                  \
         else                                                                                       \
-            go((KERNEL<4, 8>), grid_, block_, 0, __VA_ARGS__);                                     \
+            go((KERNEL<4, 8>), grid_, block_, lds_, __VA_ARGS__);                                  \
     } while (0)
 
 // The group offsets are formed from an LDS copy of the send offsets
@@ -2526,18 +2735,26 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
         const int32_t* item = sh.direct ? p.send_item : r.send_meta;
         v4u* dx = (v4u*)(sh.direct ? r.recv_x : r.send_x);
         int32_t* dmeta = sh.direct ? r.recv_meta : nullptr;
-        // the partial combine's token records take one wave per token, in
-        // blocks after the rows'
-        const unsigned tblocks = sh.partial ? row_blocks(tokens, 1) : 0;
+        // the partial combine's token records: blocks of one sender each,
+        // ahead of the row blocks (so that their latency overlaps the rows),
+        // padded to a multiple of 8 blocks (the row blocks keep their XCDs)
+        unsigned tblocks = 0;
+        size_t lds = 0;
+        if (sh.partial) {
+            const int per_block = rec_tokens_per_block(sh);
+            const int64_t nb = (int64_t)sh.N * ((sh.T + per_block - 1) / per_block);
+            tblocks = (unsigned)((nb + XCDS - 1) / XCDS * XCDS);
+            lds = (size_t)rec_lds_ints(sh) * sizeof(int32_t);
+        }
         if (sh.fp8) {
             RowShape rsh = row_shape(sh.H / 16);
             if (rsh.u > 4)
                 rsh.u = 4;
             const unsigned rb = row_blocks(sh.rows, rsh.split);
-            MOE_DISPATCH_ROW_BLOCKS(rsh, pack_rows_fp8_kernel, rb + tblocks, L, sh, p,
-                                    (const v4u*)x, idx, item, dx,
-                                    sh.direct ? r.recv_scale : r.send_scale, dmeta, w, dst_w,
-                                    sender_run(sh, rsh), rb);
+            MOE_DISPATCH_ROW_BLOCKS_LDS(rsh, pack_rows_fp8_kernel, rb + tblocks, lds, L, sh, p,
+                                        (const v4u*)x, idx, item, dx,
+                                        sh.direct ? r.recv_scale : r.send_scale, dmeta, w, dst_w,
+                                        sender_run(sh, rsh), tblocks);
         } else if (sh.payload_vecs == 7 * 2 * WAVE) {
             // hidden 7168: seven waves of exactly 2 vectors per lane instead of
             // eight with an eighth of the lanes idle in the second round.
@@ -2547,14 +2764,14 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
             // and partial reduces 1-2 us
             const RowShape rsh{2, 7};
             const unsigned rb = row_blocks(sh.rows, rsh.split);
-            go((pack_rows_bf16_kernel<2, 7>), dim3(rb + tblocks), dim3(COPY_THREADS), 0, L, sh, p,
-               (const v4u*)x, idx, item, dx, dmeta, w, dst_w, sender_run(sh, rsh), rb);
+            go((pack_rows_bf16_kernel<2, 7>), dim3(rb + tblocks), dim3(COPY_THREADS), lds, L, sh,
+               p, (const v4u*)x, idx, item, dx, dmeta, w, dst_w, sender_run(sh, rsh), tblocks);
         } else {
             const RowShape rsh = row_shape(sh.payload_vecs);
             const unsigned rb = row_blocks(sh.rows, rsh.split);
-            MOE_DISPATCH_ROW_BLOCKS(rsh, pack_rows_bf16_kernel, rb + tblocks, L, sh, p,
-                                    (const v4u*)x, idx, item, dx, dmeta, w, dst_w,
-                                    sender_run(sh, rsh), rb);
+            MOE_DISPATCH_ROW_BLOCKS_LDS(rsh, pack_rows_bf16_kernel, rb + tblocks, lds, L, sh, p,
+                                        (const v4u*)x, idx, item, dx, dmeta, w, dst_w,
+                                        sender_run(sh, rsh), tblocks);
         }
         return hipGetLastError();
     }

@@ -71,31 +71,49 @@ def test_headline_totals():
 
 
 def test_byte_model_follows_the_librarys_rules():
-    """The byte model's pack-order boundary is the library's (read from the
-    kernel interface header), and the group offsets are counted in the route
-    plan exactly where the library forms them there: the token-order pack
-    of the packed layout and the partial combine."""
+    """The byte model's pack-order boundary and record-sum limit are the
+    library's (read from the kernel interface header), and the group offsets
+    are counted in the route plan exactly where the library forms them there:
+    the token-order pack (unless its rows go to fixed slots with the
+    receiver-side combine), and the partial combine's records in the
+    send-row-order pack past the record-sum limit."""
     import re
     hdr = open(os.path.join(ROOT, "combine_moe_dispatch_amd", "csrc", "moe_kernels.h")).read()
     m = re.search(r"PACK_ROWS_MAX_SENDER_BYTES\s*=\s*(\d+)\s*<<\s*(\d+)", hdr)
     assert m and bench.PACK_ROWS_MAX_SENDER_BYTES == int(m.group(1)) << int(m.group(2))
-    assert "return sh.partial || (!sh.fixed && !pack_in_row_order(sh));" in hdr
+    m = re.search(r"RECORD_SUMS_MAX\s*=\s*(\d+)\s*<<\s*(\d+)", hdr)
+    assert m and bench.RECORD_SUMS_MAX == int(m.group(1)) << int(m.group(2))
+    assert "return (int64_t)(sh.E + 2 * sh.N + 2) * sh.N <= RECORD_SUMS_MAX;" in hdr
+    assert "if (!pack_in_row_order(sh))\n        return sh.partial || !sh.fixed;" in hdr
+    assert "return sh.partial && !record_sums(sh);" in hdr
     c = CONFIGS["C"]
     small, big = c, c.with_(T=256)           # 1.75 MiB and 3.5 MiB per sender
+    # 128 ranks x 256 experts: (256 + 2*128 + 2) * 128 = 65 792 terms per
+    # record block, past the limit (DeepSeek-R1 decode: 10 304)
+    wide = c.with_(N=128, T=8)
     base = bench.kernel_bytes(small, layout="fixed")["route_plan"]
     for cfg, transport, combine, layout, tail in [
             (small, "staged", "receiver", "packed", False), (small, "direct", "receiver", "packed", False),
-            (small, "staged", "receiver", "fixed", False), (small, "staged", "partial", "packed", True),
+            (small, "staged", "receiver", "fixed", False), (small, "staged", "partial", "packed", False),
+            (small, "direct", "partial", "fixed", False), (wide, "staged", "partial", "packed", True),
+            (wide, "staged", "receiver", "packed", False),
             (big, "staged", "receiver", "packed", True), (big, "direct", "receiver", "packed", True),
-            (big, "staged", "receiver", "fixed", False)]:
+            (big, "staged", "receiver", "fixed", False), (big, "staged", "partial", "fixed", True)]:
+        assert bench.plan_forms_offsets(cfg, combine, layout) == tail
         kb = bench.kernel_bytes(cfg, transport, combine, 1000 if combine == "partial" else 0, layout)
         R, N, E = cfg.rows, cfg.N, cfg.E
         offs = 4 * (N * E + N * (E + 1) + N * (N + 1) + (N + 1) + (E + 1))
-        plain = 4 * (2 * R + N * E + 2 * N * (E + 1)) + (4 * R if cfg is small else 0)
+        plain = 4 * (2 * R + N * E + 2 * N * (E + 1)) + (4 * R if cfg is not big else 0)
         extra = kb["route_plan"] - plain
+        maps = kb["recv_map"] - offs - R * (24 if layout == "fixed" else 20)
         if combine == "partial":
-            extra -= 2 * R * 4 + N * E * 4 + 3 * N * (N + 1) * 4 + 2 * (N + 1) * 4
-        assert extra == (offs if tail else 0), (cfg.T, transport, combine, layout)
+            extra -= 2 * R * 4 + 2 * N * (N + 1) * 4
+            if tail:
+                extra -= N * (E + 2 * N + 2) * 4 + 2 * N * (N + 1) * 4 + 2 * (N + 1) * 4
+            else:
+                maps -= N * (N + 1) * 4 + 2 * (N + 1) * 4
+        assert extra == (offs if tail else 0), (cfg.N, cfg.T, transport, combine, layout)
+        assert maps == 0, (cfg.N, cfg.T, transport, combine, layout)
     assert base == 4 * (3 * c.rows + c.N * c.E + 2 * c.N * (c.E + 1))
 
 

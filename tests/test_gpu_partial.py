@@ -121,6 +121,28 @@ def test_partial_edge_shapes(transport):
     assert gpu["P"] == 0 and gpu["part_base"].tolist() == [0] * (cfg.N + 1)
 
 
+# Each block of the send-row-order pack's partial records forms its sender's
+# bases from (E + 2N + 2) * N terms of the senders' send offsets up to 65 536
+# terms, else reads the route plan's group tables: 126 ranks x 252 experts
+# (63 756 terms) and 128 x 256 (65 792), packed and fixed-slot layouts.
+RECORD_SIDES = {"sums": (126, 252), "tables": (128, 256)}
+
+
+@pytest.mark.parametrize("layout", ["packed", "fixed"])
+@pytest.mark.parametrize("transport", TRANSPORTS)
+@pytest.mark.parametrize("side", list(RECORD_SIDES))
+def test_partial_record_bases(side, transport, layout):
+    from tests.test_gpu_fixed_slot import _check as check_fixed
+    N, E = RECORD_SIDES[side]
+    cfg = Config("Q", f"records-{side}", N, 5, 136, E, 6, "bf16", "softmax", 23)
+    say(f"[gpu] partial record bases {cfg.describe()} transport={transport} layout={layout}")
+    inp = make_inputs(cfg)
+    if layout == "fixed":
+        check_fixed(cfg, inp, cfg.T, transport, PARTIAL)
+    else:
+        _check(cfg, inp, run_cycle(torch, mep, cfg, inp, transport=transport, combine_mode=PARTIAL))
+
+
 @pytest.mark.parametrize("transport", TRANSPORTS)
 def test_partial_same_rank_identity(transport):
     """Identity experts, weights summing to one, every expert of a token on
