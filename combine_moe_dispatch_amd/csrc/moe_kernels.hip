@@ -1819,15 +1819,17 @@ __global__ __launch_bounds__(COPY_THREADS) void recv_map_kernel(Shape sh, Plan p
         return;
     const int so_e = so[e], so_d = so[d * L];
     int eo = 0, qb = 0, before = 0;
+    // columns of soff transposed (senders consecutive): coalesced loads; a
+    // sender's count of e is the difference of its columns e+1 and e
+    const int32_t* col_e = p.soff_col + (size_t)e * N;
+    const int32_t* col_e1 = col_e + N;
     if (!tables) {
         eo = p.eoff[e];
         qb = p.rbase[d] + p.roff[(size_t)d * (N + 1) + s];
         for (int j = lane; j < s; j += WAVE)
-            before += p.cnt[(size_t)j * sh.E + e];
+            before += col_e1[j] - col_e[j];
         before = wave_sum(before);
     } else {
-        // columns of soff transposed (senders consecutive): coalesced loads
-        const int32_t* col_e = p.soff_col + (size_t)e * N;
         const int32_t* col_lo = p.soff_col + (size_t)d * L * N;
         const int32_t* col_hi = p.soff_col + (size_t)(d + 1) * L * N;
         const int32_t* col_tot = p.soff_col + (size_t)sh.E * N;
@@ -1842,12 +1844,12 @@ __global__ __launch_bounds__(COPY_THREADS) void recv_map_kernel(Shape sh, Plan p
         for (int j0 = 0; j0 < N; j0 += WAVE) {
             const int j = j0 + lane;
             if (j < N) {
-                const int lo = col_lo[j];
-                eo += col_e[j];
+                const int lo = col_lo[j], ce = col_e[j];
+                eo += ce;
                 rb += lo;
                 if (j < s) {
                     qb += col_hi[j];
-                    before += p.cnt[(size_t)j * sh.E + e];
+                    before += col_e1[j] - ce;
                 } else {
                     qb += lo;
                 }
