@@ -225,7 +225,8 @@ KERNEL_OF = [("route_plan_kernel", "route_plan"), ("pack_bf16_kernel", "pack"),
              ("partial_transfer_kernel", "partial_transfer"),
              ("partial_reduce_kernel", "partial_reduce"),
              ("recv_map_kernel", "recv_map"), ("pack_rows_bf16_kernel", "pack"),
-             ("pack_rows_fp8_kernel", "pack")]
+             ("pack_rows_fp8_kernel", "pack"), ("pack_rows_rec_bf16_kernel", "pack"),
+             ("pack_rows_rec_fp8_kernel", "pack")]
 
 
 def _kernel_key(name: str):

@@ -1566,20 +1566,24 @@ __device__ inline void pack_record_block(const Shape& sh, const Plan& p,
         token_records(sh, p, idx, s, t0, t_end, tab);
 }
 
-template <int U, int SPLIT>
-__global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, Plan p,
-                                                                      const v4u* __restrict__ x,
-                                                                      const int32_t* __restrict__ idx,
-                                                                      const int32_t* __restrict__ row_item,
-                                                                      v4u* __restrict__ dst_x,
-                                                                      int32_t* __restrict__ dst_meta,
-                                                                      const float* __restrict__ w,
-                                                                      float* __restrict__ dst_w,
-                                                                      uint32_t xrun, uint32_t rec_blocks)
+// REC: the grid starts with the partial combine's record blocks (a separate
+// instance, so that the row blocks of the other modes keep their registers:
+// the record path took the kernel's scalar registers from 71 to 94 and the
+// receiver-side combine's direct pack from 89 to 93 us on DeepSeek-R1 decode).
+template <int U, int SPLIT, bool REC>
+__device__ __forceinline__ void pack_rows_bf16(const Shape& sh, const Plan& p,
+                                               const v4u* __restrict__ x,
+                                               const int32_t* __restrict__ idx,
+                                               const int32_t* __restrict__ row_item,
+                                               v4u* __restrict__ dst_x,
+                                               int32_t* __restrict__ dst_meta,
+                                               const float* __restrict__ w,
+                                               float* __restrict__ dst_w, uint32_t xrun,
+                                               uint32_t rec_blocks)
 {
     const int lane = lane_id();
     const int n = sh.payload_vecs;
-    if (blockIdx.x < rec_blocks) {
+    if (REC && blockIdx.x < rec_blocks) {
         extern __shared__ __align__(16) int32_t rec_tab[];
         pack_record_block(sh, p, idx, rec_tab);
         return;
@@ -1628,21 +1632,21 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(Shape sh, 
     }
 }
 
-template <int U, int SPLIT>
-__global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(Shape sh, Plan p,
-                                                                     const v4u* __restrict__ x,
-                                                                     const int32_t* __restrict__ idx,
-                                                                     const int32_t* __restrict__ row_item,
-                                                                     v4u* __restrict__ dst_q,
-                                                                     float* __restrict__ dst_scale,
-                                                                     int32_t* __restrict__ dst_meta,
-                                                                     const float* __restrict__ w,
-                                                                     float* __restrict__ dst_w,
-                                                                     uint32_t xrun, uint32_t rec_blocks)
+template <int U, int SPLIT, bool REC>
+__device__ __forceinline__ void pack_rows_fp8(const Shape& sh, const Plan& p,
+                                              const v4u* __restrict__ x,
+                                              const int32_t* __restrict__ idx,
+                                              const int32_t* __restrict__ row_item,
+                                              v4u* __restrict__ dst_q,
+                                              float* __restrict__ dst_scale,
+                                              int32_t* __restrict__ dst_meta,
+                                              const float* __restrict__ w,
+                                              float* __restrict__ dst_w, uint32_t xrun,
+                                              uint32_t rec_blocks)
 {
     const int lane = lane_id();
     const int n2 = sh.H / 16;
-    if (blockIdx.x < rec_blocks) {
+    if (REC && blockIdx.x < rec_blocks) {
         extern __shared__ __align__(16) int32_t rec_tab[];
         pack_record_block(sh, p, idx, rec_tab);
         return;
@@ -1700,6 +1704,48 @@ __global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(Shape sh, P
                 dst_w[drow] = w[s * TK + m];
         }
     }
+}
+
+template <int U, int SPLIT>
+__global__ __launch_bounds__(COPY_THREADS) void pack_rows_bf16_kernel(
+    Shape sh, Plan p, const v4u* __restrict__ x, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ row_item, v4u* __restrict__ dst_x, int32_t* __restrict__ dst_meta,
+    const float* __restrict__ w, float* __restrict__ dst_w, uint32_t xrun, uint32_t rec_blocks)
+{
+    pack_rows_bf16<U, SPLIT, false>(sh, p, x, idx, row_item, dst_x, dst_meta, w, dst_w, xrun,
+                                    rec_blocks);
+}
+
+template <int U, int SPLIT>
+__global__ __launch_bounds__(COPY_THREADS) void pack_rows_rec_bf16_kernel(
+    Shape sh, Plan p, const v4u* __restrict__ x, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ row_item, v4u* __restrict__ dst_x, int32_t* __restrict__ dst_meta,
+    const float* __restrict__ w, float* __restrict__ dst_w, uint32_t xrun, uint32_t rec_blocks)
+{
+    pack_rows_bf16<U, SPLIT, true>(sh, p, x, idx, row_item, dst_x, dst_meta, w, dst_w, xrun,
+                                   rec_blocks);
+}
+
+template <int U, int SPLIT>
+__global__ __launch_bounds__(COPY_THREADS) void pack_rows_fp8_kernel(
+    Shape sh, Plan p, const v4u* __restrict__ x, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ row_item, v4u* __restrict__ dst_q, float* __restrict__ dst_scale,
+    int32_t* __restrict__ dst_meta, const float* __restrict__ w, float* __restrict__ dst_w,
+    uint32_t xrun, uint32_t rec_blocks)
+{
+    pack_rows_fp8<U, SPLIT, false>(sh, p, x, idx, row_item, dst_q, dst_scale, dst_meta, w, dst_w,
+                                   xrun, rec_blocks);
+}
+
+template <int U, int SPLIT>
+__global__ __launch_bounds__(COPY_THREADS) void pack_rows_rec_fp8_kernel(
+    Shape sh, Plan p, const v4u* __restrict__ x, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ row_item, v4u* __restrict__ dst_q, float* __restrict__ dst_scale,
+    int32_t* __restrict__ dst_meta, const float* __restrict__ w, float* __restrict__ dst_w,
+    uint32_t xrun, uint32_t rec_blocks)
+{
+    pack_rows_fp8<U, SPLIT, true>(sh, p, x, idx, row_item, dst_q, dst_scale, dst_meta, w, dst_w,
+                                  xrun, rec_blocks);
 }
 
 // ---------------------------------------------------------------------------
@@ -2753,10 +2799,15 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
             if (rsh.u > 4)
                 rsh.u = 4;
             const unsigned rb = row_blocks(sh.rows, rsh.split);
-            MOE_DISPATCH_ROW_BLOCKS_LDS(rsh, pack_rows_fp8_kernel, rb + tblocks, lds, L, sh, p,
-                                        (const v4u*)x, idx, item, dx,
-                                        sh.direct ? r.recv_scale : r.send_scale, dmeta, w, dst_w,
-                                        sender_run(sh, rsh), tblocks);
+            float* dscale = sh.direct ? r.recv_scale : r.send_scale;
+            if (sh.partial)
+                MOE_DISPATCH_ROW_BLOCKS_LDS(rsh, pack_rows_rec_fp8_kernel, rb + tblocks, lds, L, sh,
+                                            p, (const v4u*)x, idx, item, dx, dscale, dmeta, w,
+                                            dst_w, sender_run(sh, rsh), tblocks);
+            else
+                MOE_DISPATCH_ROW_BLOCKS(rsh, pack_rows_fp8_kernel, rb, L, sh, p, (const v4u*)x,
+                                        idx, item, dx, dscale, dmeta, w, dst_w,
+                                        sender_run(sh, rsh), 0u);
         } else if (sh.payload_vecs == 7 * 2 * WAVE) {
             // hidden 7168: seven waves of exactly 2 vectors per lane instead of
             // eight with an eighth of the lanes idle in the second round.
@@ -2766,14 +2817,23 @@ hipError_t launch_pack(const Shape& sh, const void* x, const int32_t* idx, const
             // and partial reduces 1-2 us
             const RowShape rsh{2, 7};
             const unsigned rb = row_blocks(sh.rows, rsh.split);
-            go((pack_rows_bf16_kernel<2, 7>), dim3(rb + tblocks), dim3(COPY_THREADS), lds, L, sh,
-               p, (const v4u*)x, idx, item, dx, dmeta, w, dst_w, sender_run(sh, rsh), tblocks);
+            if (sh.partial)
+                go((pack_rows_rec_bf16_kernel<2, 7>), dim3(rb + tblocks), dim3(COPY_THREADS), lds,
+                   L, sh, p, (const v4u*)x, idx, item, dx, dmeta, w, dst_w, sender_run(sh, rsh),
+                   tblocks);
+            else
+                go((pack_rows_bf16_kernel<2, 7>), dim3(rb), dim3(COPY_THREADS), 0, L, sh, p,
+                   (const v4u*)x, idx, item, dx, dmeta, w, dst_w, sender_run(sh, rsh), 0u);
         } else {
             const RowShape rsh = row_shape(sh.payload_vecs);
             const unsigned rb = row_blocks(sh.rows, rsh.split);
-            MOE_DISPATCH_ROW_BLOCKS_LDS(rsh, pack_rows_bf16_kernel, rb + tblocks, lds, L, sh, p,
-                                        (const v4u*)x, idx, item, dx, dmeta, w, dst_w,
-                                        sender_run(sh, rsh), tblocks);
+            if (sh.partial)
+                MOE_DISPATCH_ROW_BLOCKS_LDS(rsh, pack_rows_rec_bf16_kernel, rb + tblocks, lds, L,
+                                            sh, p, (const v4u*)x, idx, item, dx, dmeta, w, dst_w,
+                                            sender_run(sh, rsh), tblocks);
+            else
+                MOE_DISPATCH_ROW_BLOCKS(rsh, pack_rows_bf16_kernel, rb, L, sh, p, (const v4u*)x,
+                                        idx, item, dx, dmeta, w, dst_w, sender_run(sh, rsh), 0u);
         }
         return hipGetLastError();
     }
