@@ -149,8 +149,7 @@ struct RouteArgs {
     int chunk_waves;        // RP_WAVES, or fewer for large E (LDS budget)
     int partial;            // also plan the expert-side partial rows
     int slot_cap;           // fixed-slot layout: most rows per (sender, expert); -1: none
-    int offsets;            // the last workgroup computes the group offsets (Shape::plan_offsets)
-    int table_lds;          // ... from a copy of soff in the dynamic LDS
+    int table_lds;          // the tail forms the group offsets from a copy of soff in LDS
     int32_t* send_meta;     // when set: each send row's item t*K+k, written with the positions
                             // (the send meta words, or the direct transport's send_item)
     int64_t cap;
@@ -642,13 +641,14 @@ __device__ __forceinline__ int rank_of_item(const RouteArgs& ra, const int32_t* 
 // HC: idx chunks held in registers, the fewest of 1, 2, 4, 8, 32 that cover
 // a rank's items when possible (a decode batch needs 1 or 2; fewer held
 // chunks means fewer loads and shorter unrolled loops).
-// FULL: the instance with the partial combine's second key and the group
-// offsets' tail; the plain one (neither) keeps 72 scalar and 36 vector
-// registers with no spills, against 106 (163 spilled) and 133.
-template <int HC, bool FULL>
+// Instances: PARTIAL, the partial combine's second key; TAIL, the group
+// offsets' tail.  Without the tail the kernel keeps 72 scalar and 36 vector
+// registers (94 and 46 with the partial key) and spills none; the tail takes
+// it to 106 (149-163 spilled) and 133.
+template <int HC, bool PARTIAL, bool TAIL>
 __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
 {
-    const bool partial = FULL && ra.partial;
+    const bool partial = PARTIAL;
     extern __shared__ __align__(16) uint64_t lds64[];
     const int E = ra.E, N = ra.N;
     // keys: experts [0, E) and, for the partial combine, destination ranks
@@ -797,7 +797,7 @@ __global__ __launch_bounds__(RP_NT) void route_plan_kernel(RouteArgs ra, Plan p)
             atomicOr(p.err_sticky, wg_err);
         }
     }
-    if (!FULL || !ra.offsets)
+    if (!TAIL)
         return;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -2698,7 +2698,6 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
     ra.L = sh.L;
     ra.partial = sh.partial;
     ra.slot_cap = sh.fixed ? sh.slots : -1;
-    ra.offsets = sh.plan_offsets;
     ra.cap = (int64_t)sh.N * sh.T * (sh.K > sh.L ? sh.K : sh.L);
     // keys: E experts, plus N ranks for the partial combine.  Two buffers of
     // lane masks take 16 bytes per (wave, key) and the cursors 8 bytes per
@@ -2714,10 +2713,11 @@ hipError_t launch_route_plan(const Shape& sh, const int32_t* idx, const Plan& p,
         lds = std::max(lds, table_lds_bytes(sh));
     const int chunks = (sh.T * sh.K + ra.chunk_waves * WAVE - 1) / (ra.chunk_waves * WAVE);
     const dim3 grid(sh.N), block(RP_NT);
-    const bool full = sh.partial || sh.plan_offsets;
 #define MOE_ROUTE_PLAN(HC)                                                                         \
-    (full ? go(route_plan_kernel<HC, true>, grid, block, lds, L, ra, p)                            \
-          : go(route_plan_kernel<HC, false>, grid, block, lds, L, ra, p))
+    (sh.partial ? (sh.plan_offsets ? go(route_plan_kernel<HC, true, true>, grid, block, lds, L, ra, p)  \
+                                   : go(route_plan_kernel<HC, true, false>, grid, block, lds, L, ra, p)) \
+                : (sh.plan_offsets ? go(route_plan_kernel<HC, false, true>, grid, block, lds, L, ra, p) \
+                                   : go(route_plan_kernel<HC, false, false>, grid, block, lds, L, ra, p)))
     if (chunks <= 1)
         MOE_ROUTE_PLAN(1);
     else if (chunks <= 2)
