@@ -42,8 +42,8 @@ struct Shape {
 // run), staged: pack 86.9 -> 74.5 us warm, 115 -> 99 MALL-flushed; on the
 // prefill (28 MiB per sender) the row order re-reads every token from HBM or
 // the MALL and took 4.9-5.0 ms against 1.87 in token order.  With the
-// partial combine, whose records are made per token, the same launch runs one
-// wave per token for them after the row blocks.
+// partial combine, whose records are made per token, the same launch runs a
+// block per sender for them ahead of the row blocks.
 constexpr int64_t PACK_ROWS_MAX_SENDER_BYTES = 2 << 20;
 
 inline bool pack_in_row_order(const Shape& sh)
