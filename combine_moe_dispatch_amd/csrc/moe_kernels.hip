@@ -851,7 +851,9 @@ __device__ inline RowSlot row_slot(int n, int64_t block = blockIdx.x)
 // segments of contiguous source rows, take one average segment per run:
 // DeepSeek-R1 decode (64 blocks a segment) 155 -> 148-150 us; fp8 prefill (256
 // and 512) 2610 -> 2460 and 5284 -> 4760 us, where round-robin placement took
-// one UTCL1 translation miss per row.  The shuffle, the combine pack, the
+// one UTCL1 translation miss per row; the transfer back, against runs of 1,
+// 32, 128, 256 and 2048 blocks, was fastest or equal with its segment runs
+// (DeepSeek-R1 decode 149.7 us against 151.3-156.5).  The shuffle, the combine pack, the
 // combine push and the combine reduce take fixed runs (host side,
 // RUN_ROWS_BLOCKS and RUN_TOKEN_BLOCKS).  A ragged last tile keeps its order; run = 1 is plain
 // order.
