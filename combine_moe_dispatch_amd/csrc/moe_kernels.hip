@@ -1561,7 +1561,13 @@ __device__ inline void pack_record_block(const Shape& sh, const Plan& p,
     const int per_block = rec_tokens_per_block(sh);
     const int bps = (sh.T + per_block - 1) / per_block;
     const int s = (int)(blockIdx.x / bps);
-    if (s >= sh.N || sender_failed(sh, p, s))     // the same for the whole block
+    if (s >= sh.N)
+        return;
+    // one decision for the whole block, before its barrier: another block's
+    // error can land while this one's threads read the word, and a block
+    // that went on with part of its threads would place records from bases
+    // it never formed
+    if (__syncthreads_or(sender_failed(sh, p, s)))
         return;
     sender_bases(sh, p, s, tab);
     const int per_pass = WAVE / sh.K;
