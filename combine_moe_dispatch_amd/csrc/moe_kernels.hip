@@ -2962,7 +2962,9 @@ hipError_t launch_combine_push(const Shape& sh, const Plan& p, const Rows& r, co
 // of a token at once: with the movers' split and 2 vectors per lane per row,
 // K = 8 rows take 64 VGPRs of data (94 in all, 5 waves per SIMD); at 4
 // vectors per lane over 4 waves such kernels took 160-180 VGPRs and ran at 2
-// (an earlier per-token partial send: 172 -> 165 us on DeepSeek-R1 decode).
+// (an earlier per-token partial send: 172 -> 165 us on DeepSeek-R1 decode);
+// at 1 vector per lane (56 VGPRs, 8 waves per SIMD, two rounds a wave) the
+// combine reduce took 91.8 us against 87.0 (Kimi-K2 decode 183.6 against 172.4).
 #define MOE_DISPATCH_TOKEN(sh, KERNEL, UK, tokens, L, ...)                                         \
     do {                                                                                           \
         const int split_ = row_shape((sh).comb_vecs).split;                                        \
